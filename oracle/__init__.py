@@ -1,0 +1,268 @@
+"""CPU oracle of the MoE-layer forward (route, dispatch, expert FFN, combine,
+selection-bias update).
+
+TEST INFRASTRUCTURE ONLY.  Only the tests, ``__graft_entry__.smoke()`` and the
+CPU-baseline leg of ``bench.py`` may import this package.  It shares no code
+with the HIP library and the HIP library never calls it.
+
+The arithmetic lives in ``oracle.c`` (plain per-token loops, fp64); this module
+only marshals numpy arrays through ctypes.  bf16 tensors travel as ``uint16``
+arrays of their bit patterns.
+
+Workload dictionaries use the keys ``N d E k R cf G kg score dtype`` (and
+``h act`` for the FFN); ``score`` is ``softmax_topk``, ``softmax_all`` or
+``sigmoid_norm``; ``act`` is ``relu``, ``gelu`` or ``swiglu``; ``dtype`` is
+``fp32`` or ``bf16``.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "liboracle.so")
+SRC_PATH = os.path.join(_HERE, "oracle.c")
+
+SCORE_CODES = {"softmax_topk": 0, "softmax_all": 1, "sigmoid_norm": 2}
+ACT_CODES = {"relu": 0, "gelu": 1, "swiglu": 2}
+DTYPE_CODES = {"fp32": 0, "bf16": 1}
+
+
+def build() -> str:
+    """Compile ``liboracle.so`` with gcc (strict IEEE: no contraction, no fast-math)."""
+    cmd = [
+        "gcc", "-O2", "-std=c11", "-Wall", "-Wextra", "-fPIC", "-shared", "-fopenmp",
+        "-ffp-contract=off", "-fno-fast-math", "-o", LIB_PATH, SRC_PATH, "-lm",
+    ]
+    subprocess.run(cmd, check=True)
+    return LIB_PATH
+
+
+class _Desc(ctypes.Structure):
+    _fields_ = [
+        ("num_tokens", ctypes.c_int32),
+        ("hidden", ctypes.c_int32),
+        ("num_experts", ctypes.c_int32),
+        ("top_k", ctypes.c_int32),
+        ("num_ranks", ctypes.c_int32),
+        ("capacity_factor", ctypes.c_float),
+        ("num_groups", ctypes.c_int32),
+        ("topk_groups", ctypes.c_int32),
+        ("score_fn", ctypes.c_int32),
+        ("dtype", ctypes.c_int32),
+    ]
+
+
+_lib = None
+
+
+def lib():
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            build()
+        L = ctypes.CDLL(LIB_PATH)
+        P, I32, F32 = ctypes.c_void_p, ctypes.c_int32, ctypes.c_float
+        D = ctypes.POINTER(_Desc)
+        sig = {
+            "oracle_logits": [D, P, P, P, P],
+            "oracle_select": [D, P, P, P, P, P, P],
+            "oracle_dispatch": [D, P, P, P, P, P, P, P, P],
+            "oracle_permute": [I32, I32, I32, P, P, P],
+            "oracle_ffn_row": [I32, I32, I32, I32, P, P, P, P, P],
+            "oracle_expert_ffn": [I32, I32, I32, I32, I32, P, P, P, P, P, P],
+            "oracle_combine": [I32, I32, I32, I32, P, P, P, P, P, P],
+            "oracle_bias_update": [I32, I32, I32, P, F32, P],
+        }
+        for name, args in sig.items():
+            fn = getattr(L, name)
+            fn.argtypes = args
+            fn.restype = I32
+        L.oracle_capacity.argtypes = [D]
+        L.oracle_capacity.restype = ctypes.c_int64
+        L.oracle_set_threads.argtypes = [I32]
+        L.oracle_set_threads.restype = None
+        L.oracle_get_threads.argtypes = []
+        L.oracle_get_threads.restype = I32
+        _lib = L
+    return _lib
+
+
+def _desc(cfg: dict, N: int | None = None) -> _Desc:
+    return _Desc(
+        int(cfg["N"] if N is None else N), int(cfg["d"]), int(cfg["E"]), int(cfg["k"]),
+        int(cfg.get("R", 1)), float(cfg.get("cf", 0.0) or 0.0), int(cfg.get("G", 1)),
+        int(cfg.get("kg", 1)), SCORE_CODES[cfg["score"]], DTYPE_CODES[cfg["dtype"]],
+    )
+
+
+def _ptr(a):
+    return None if a is None else a.ctypes.data_as(ctypes.c_void_p)
+
+
+def _c(a, dtype):
+    return None if a is None else np.ascontiguousarray(a, dtype=dtype)
+
+
+def _elem_dtype(dtype: str):
+    return np.float32 if dtype == "fp32" else np.uint16
+
+
+def _check(rc: int, name: str):
+    if rc != 0:
+        raise ValueError(f"{name}: invalid arguments")
+
+
+def set_threads(n: int) -> None:
+    lib().oracle_set_threads(int(n))
+
+
+def get_threads() -> int:
+    return int(lib().oracle_get_threads())
+
+
+def capacity(cfg: dict) -> int:
+    d = _desc(cfg)
+    return int(lib().oracle_capacity(ctypes.byref(d)))
+
+
+def logits(cfg: dict, x, w_router, router_bias=None) -> np.ndarray:
+    ed = _elem_dtype(cfg["dtype"])
+    x, w_router = _c(x, ed), _c(w_router, ed)
+    router_bias = _c(router_bias, np.float32)
+    N = x.shape[0]
+    z = np.empty((N, cfg["E"]), np.float32)
+    d = _desc(cfg, N)
+    _check(lib().oracle_logits(ctypes.byref(d), _ptr(x), _ptr(w_router), _ptr(router_bias),
+                               _ptr(z)), "oracle_logits")
+    return z
+
+
+def select(cfg: dict, z, sel_bias=None) -> dict:
+    z = _c(z, np.float32)
+    sel_bias = _c(sel_bias, np.float32)
+    N, k, E = z.shape[0], cfg["k"], cfg["E"]
+    idx = np.empty((N, k), np.int32)
+    w = np.empty((N, k), np.float32)
+    counts = np.empty(E, np.int32)
+    aff = np.empty((N, E), np.float32)
+    d = _desc(cfg, N)
+    _check(lib().oracle_select(ctypes.byref(d), _ptr(z), _ptr(sel_bias), _ptr(idx), _ptr(w),
+                               _ptr(counts), _ptr(aff)), "oracle_select")
+    return {"topk_idx": idx, "topk_w": w, "counts": counts, "affinity": aff}
+
+
+def route(cfg: dict, x, w_router, router_bias=None, sel_bias=None) -> dict:
+    z = logits(cfg, x, w_router, router_bias)
+    out = select(cfg, z, sel_bias)
+    out["logits"] = z
+    return out
+
+
+def dispatch(cfg: dict, topk_idx) -> dict:
+    topk_idx = _c(topk_idx, np.int32)
+    N, k, E, R = topk_idx.shape[0], cfg["k"], cfg["E"], cfg.get("R", 1)
+    S = N * k
+    out = {
+        "row_of_slot": np.empty((N, k), np.int32),
+        "token_of_row": np.empty(S, np.int32),
+        "slot_of_row": np.empty(S, np.int8),
+        "expert_offsets": np.empty(E + 1, np.int32),
+        "admitted": np.empty(E, np.int32),
+        "rank_offsets": np.empty(R + 1, np.int32),
+        "rank_counts": np.empty(R, np.int32),
+    }
+    d = _desc(cfg, N)
+    _check(lib().oracle_dispatch(
+        ctypes.byref(d), _ptr(topk_idx), _ptr(out["row_of_slot"]), _ptr(out["token_of_row"]),
+        _ptr(out["slot_of_row"]), _ptr(out["expert_offsets"]), _ptr(out["admitted"]),
+        _ptr(out["rank_offsets"]), _ptr(out["rank_counts"])), "oracle_dispatch")
+    out["num_rows"] = int(out["expert_offsets"][E])
+    return out
+
+
+def permute(dtype: str, x, token_of_row, num_rows: int) -> np.ndarray:
+    ed = _elem_dtype(dtype)
+    x = _c(x, ed)
+    token_of_row = _c(token_of_row, np.int32)
+    out = np.empty((max(num_rows, 0), x.shape[1]), ed)
+    _check(lib().oracle_permute(int(num_rows), int(x.shape[1]), DTYPE_CODES[dtype], _ptr(x),
+                                _ptr(token_of_row), _ptr(out)), "oracle_permute")
+    return out
+
+
+def ffn_row(dtype: str, act: str, x_row, w1, w3, w2) -> np.ndarray:
+    """One row through one expert: w1/w3 are [h,d], w2 is [d,h]."""
+    ed = _elem_dtype(dtype)
+    x_row, w1, w2 = _c(x_row, ed), _c(w1, ed), _c(w2, ed)
+    w3 = _c(w3, ed)
+    h, d = w1.shape
+    y = np.empty(d, ed)
+    _check(lib().oracle_ffn_row(d, h, ACT_CODES[act], DTYPE_CODES[dtype], _ptr(x_row), _ptr(w1),
+                                _ptr(w3), _ptr(w2), _ptr(y)), "oracle_ffn_row")
+    return y
+
+
+def expert_ffn(dtype: str, act: str, x_rows, offsets, w1, w3, w2) -> np.ndarray:
+    """Grouped FFN over rows [offsets[e], offsets[e+1]) with expert e's weights."""
+    ed = _elem_dtype(dtype)
+    x_rows, w1, w2 = _c(x_rows, ed), _c(w1, ed), _c(w2, ed)
+    w3 = _c(w3, ed)
+    offsets = _c(offsets, np.int32)
+    E, h, d = w1.shape
+    y = np.zeros((x_rows.shape[0], d), ed)
+    _check(lib().oracle_expert_ffn(E, d, h, ACT_CODES[act], DTYPE_CODES[dtype], _ptr(x_rows),
+                                   _ptr(offsets), _ptr(w1), _ptr(w3), _ptr(w2), _ptr(y)),
+           "oracle_expert_ffn")
+    return y
+
+
+def combine(dtype: str, y_perm, row_of_slot, topk_w, residual=None, shared_out=None):
+    ed = _elem_dtype(dtype)
+    row_of_slot = _c(row_of_slot, np.int32)
+    topk_w = _c(topk_w, np.float32)
+    y_perm = _c(y_perm, ed)
+    residual, shared_out = _c(residual, ed), _c(shared_out, ed)
+    N, k = row_of_slot.shape
+    d = (residual if residual is not None else y_perm).shape[1]
+    y = np.empty((N, d), ed)
+    _check(lib().oracle_combine(N, d, k, DTYPE_CODES[dtype], _ptr(y_perm), _ptr(row_of_slot),
+                                _ptr(topk_w), _ptr(residual), _ptr(shared_out), _ptr(y)),
+           "oracle_combine")
+    return y
+
+
+def bias_update(num_tokens: int, top_k: int, counts, sel_bias, step: float = 1e-3):
+    counts = _c(counts, np.int32)
+    b = np.array(sel_bias, dtype=np.float32, copy=True)
+    _check(lib().oracle_bias_update(counts.shape[0], int(num_tokens), int(top_k), _ptr(counts),
+                                    float(step), _ptr(b)), "oracle_bias_update")
+    return b
+
+
+def forward(cfg: dict, x, w_router, router_bias, sel_bias, w1, w3, w2,
+            shared=None, residual=True) -> dict:
+    """The whole layer: route -> dispatch -> permute -> FFN -> combine.
+    ``shared`` is an optional (w1, w3, w2) triple of one always-on expert."""
+    r = route(cfg, x, w_router, router_bias, sel_bias)
+    dsp = dispatch(cfg, r["topk_idx"])
+    M = dsp["num_rows"]
+    x_perm = permute(cfg["dtype"], x, dsp["token_of_row"], M)
+    y_perm = expert_ffn(cfg["dtype"], cfg["act"], x_perm, dsp["expert_offsets"], w1, w3, w2)
+    shared_out = None
+    if shared is not None:
+        sw1, sw3, sw2 = shared
+        N = np.asarray(x).shape[0]
+        shared_out = expert_ffn(cfg["dtype"], cfg["act"], x, np.array([0, N], np.int32),
+                                np.asarray(sw1)[None], None if sw3 is None else np.asarray(sw3)[None],
+                                np.asarray(sw2)[None])
+    y = combine(cfg["dtype"], y_perm, dsp["row_of_slot"], r["topk_w"],
+                np.asarray(x) if residual else None, shared_out)
+    out = dict(r)
+    out.update(dsp)
+    out.update({"x_perm": x_perm, "y_perm": y_perm, "shared_out": shared_out, "y": y})
+    return out

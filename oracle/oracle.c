@@ -1,0 +1,487 @@
+/*
+ * oracle.c -- plain CPU reference of the MoE-layer forward.  See oracle.h.
+ *
+ * TEST INFRASTRUCTURE ONLY: loaded by the tests, the smoke entry point and the
+ * benchmark's CPU-baseline leg; never by the HIP library.
+ *
+ * Readings of the pages adopted here (the pages are silent on these points):
+ *  - logits: fp64 accumulation left to right over the hidden index, router bias
+ *    added last in fp64, one rounding to fp32;
+ *  - ties in any ranking go to the lower expert (or group) index;
+ *  - capacity = ceil(cf * N * k / E) (the mean load times the factor), and
+ *    slots are admitted in token order;
+ *  - a dropped slot contributes nothing and the remaining weights are not
+ *    renormalised; the layer output includes the residual;
+ *  - the group score is the maximum biased selection score in the group;
+ *  - H, O and y round to the layer dtype (bf16: round-to-nearest-even).
+ */
+#include "oracle.h"
+
+#include <float.h>
+#include <limits.h>
+#include <math.h>
+#include <stdlib.h>
+#include <string.h>
+#ifdef _OPENMP
+#include <omp.h>
+#endif
+
+static int32_t g_threads = 1;
+
+void oracle_set_threads(int32_t n) { g_threads = n < 1 ? 1 : n; }
+int32_t oracle_get_threads(void) { return g_threads; }
+
+/* ---------------------------------------------------------------- dtypes -- */
+
+static double bf16_bits_to_double(uint16_t b) {
+  uint32_t u = (uint32_t)b << 16;
+  float f;
+  memcpy(&f, &u, sizeof f);
+  return (double)f;
+}
+
+static double elem(const void* p, int32_t dtype, size_t i) {
+  if (dtype == 0) return (double)((const float*)p)[i];
+  return bf16_bits_to_double(((const uint16_t*)p)[i]);
+}
+
+/* Round an fp64 value to bf16 with a single round-to-nearest-even step.
+ * bf16 carries 8 significant bits and fp32's exponent range; below 2^-126 the
+ * spacing stays 2^-133 (subnormals). */
+static uint16_t double_to_bf16_bits(double v) {
+  if (isnan(v)) return (uint16_t)0x7fc0;
+  if (v == 0.0) return signbit(v) ? (uint16_t)0x8000 : (uint16_t)0x0000;
+  int ex;
+  (void)frexp(fabs(v), &ex);      /* |v| = m * 2^ex with m in [0.5, 1) */
+  int q_exp = ex - 8;             /* spacing of 8-bit significands */
+  if (q_exp < -133) q_exp = -133;
+  double q = rint(ldexp(fabs(v), -q_exp)); /* default rounding: ties to even */
+  double r = ldexp(q, q_exp);
+  const double bf16_max = ldexp(255.0, 120); /* (2 - 2^-7) * 2^127 */
+  float f = r > bf16_max ? INFINITY : (float)r; /* exact: r is a bf16 value */
+  if (signbit(v)) f = -f;
+  uint32_t u;
+  memcpy(&u, &f, sizeof u);
+  return (uint16_t)(u >> 16);
+}
+
+static void store(void* p, int32_t dtype, size_t i, double v) {
+  if (dtype == 0)
+    ((float*)p)[i] = (float)v;
+  else
+    ((uint16_t*)p)[i] = double_to_bf16_bits(v);
+}
+
+static int dtype_ok(int32_t dtype) { return dtype == 0 || dtype == 1; }
+
+static int desc_ok(const oracle_desc* d) {
+  if (!d) return 0;
+  if (d->num_tokens < 0 || d->hidden < 1 || d->num_experts < 1) return 0;
+  if (d->top_k < 1 || d->top_k > d->num_experts) return 0;
+  if (d->num_ranks < 1 || d->num_experts % d->num_ranks != 0) return 0;
+  if (d->num_groups < 1 || d->num_experts % d->num_groups != 0) return 0;
+  if (d->topk_groups < 1 || d->topk_groups > d->num_groups) return 0;
+  if ((int64_t)d->topk_groups * (d->num_experts / d->num_groups) < d->top_k) return 0;
+  if (d->score_fn < 0 || d->score_fn > 2) return 0;
+  if (!dtype_ok(d->dtype)) return 0;
+  return 1;
+}
+
+/* ---------------------------------------------------------------- route --- */
+
+/* Router scores: the router is a linear layer over the hidden state
+ * ([EP-glossary] "How tokens travel between GPUs", step 1 and the routing
+ * snippet, where the router is a Linear(hidden, num_experts)).
+ * Fixed summation: acc starts at 0 and adds x[t,i]*w[e,i] for i = 0..d-1 in
+ * order, in fp64.  Each product of two fp32 (or bf16) values is exact in fp64,
+ * so each step is the same as a fused multiply-add.  The bias is added last,
+ * then the sum is rounded once to fp32. */
+int oracle_logits(const oracle_desc* desc, const void* x, const void* w,
+                  const float* router_bias, float* z) {
+  if (!desc_ok(desc) || (desc->num_tokens > 0 && (!x || !w || !z))) return -1;
+  const int32_t N = desc->num_tokens, d = desc->hidden, E = desc->num_experts;
+  double* wd = (double*)malloc(sizeof(double) * (size_t)E * d);
+  if (!wd) return -1;
+  for (size_t i = 0; i < (size_t)E * d; ++i) wd[i] = elem(w, desc->dtype, i);
+
+  int failed = 0;
+#pragma omp parallel num_threads(g_threads)
+  {
+    double* xd = (double*)malloc(sizeof(double) * (size_t)d);
+    if (!xd) {
+#pragma omp atomic write
+      failed = 1;
+    }
+#pragma omp for schedule(static)
+    for (int32_t t = 0; t < N; ++t) {
+      if (!xd) continue;
+      for (int32_t i = 0; i < d; ++i) xd[i] = elem(x, desc->dtype, (size_t)t * d + i);
+      for (int32_t e = 0; e < E; ++e) {
+        const double* we = wd + (size_t)e * d;
+        double acc = 0.0;
+        for (int32_t i = 0; i < d; ++i) acc = acc + xd[i] * we[i];
+        if (router_bias) acc = acc + (double)router_bias[e];
+        z[(size_t)t * E + e] = (float)acc;
+      }
+    }
+    free(xd);
+  }
+  free(wd);
+  return failed ? -1 : 0;
+}
+
+/* DeepSeek-V3-style affinity: the logistic function of the logit, evaluated in
+ * fp64 and rounded once to fp32. */
+static float sigmoid_affinity(float z) { return (float)(1.0 / (1.0 + exp(-(double)z))); }
+
+/* Is (sa, a) ranked before (sb, b)?  Higher score first, lower index on ties. */
+static int ranks_before(float sa, int32_t a, float sb, int32_t b) {
+  return sa > sb || (sa == sb && a < b);
+}
+
+/* Selection and weights for one token.
+ *  - selection score: the router score plus the per-expert selection bias,
+ *    which only affects which experts are chosen ([EP-glossary] "Load
+ *    balancing and capacity", bias-based balancing bullet);
+ *  - score function: softmax over the selected logits (top-2 GShard / Mixtral
+ *    style), softmax over all experts (top-1 Switch, [MLSys-ch10] 10.5), or
+ *    sigmoid affinities renormalised over the selected (DeepSeek-V3 style);
+ *  - group limit: experts are split into G groups of consecutive indices, only
+ *    the kg groups with the highest group score stay eligible (each token
+ *    reaches experts on a bounded number of nodes, [EP-glossary] "Load
+ *    balancing and capacity", last paragraph);
+ *  - top-k: the k eligible experts with the highest selection scores
+ *    ([EP-glossary] step 1 "keep the k highest-scoring experts");
+ *  - weights: from the unbiased scores of the selected experts; the outputs
+ *    are later weighted by them and summed ([EP-glossary] step 4). */
+static void select_token(const oracle_desc* desc, const float* zt, const float* sel_bias,
+                         int32_t* idx, float* wout, float* aff, float* s,
+                         unsigned char* eligible, float* gscore, unsigned char* gkeep) {
+  const int32_t E = desc->num_experts, k = desc->top_k;
+  const int32_t G = desc->num_groups, kg = desc->topk_groups, per = E / G;
+
+  for (int32_t e = 0; e < E; ++e) {
+    const float a = desc->score_fn == 2 ? sigmoid_affinity(zt[e]) : zt[e];
+    if (aff) aff[e] = a;
+    s[e] = sel_bias ? a + sel_bias[e] : a; /* fp32 add */
+    eligible[e] = 1;
+  }
+
+  if (G > 1) {
+    for (int32_t g = 0; g < G; ++g) {
+      float m = s[g * per];
+      for (int32_t e = g * per + 1; e < (g + 1) * per; ++e)
+        if (s[e] > m) m = s[e];
+      gscore[g] = m;
+      gkeep[g] = 0;
+    }
+    for (int32_t j = 0; j < kg; ++j) {
+      int32_t best = -1;
+      for (int32_t g = 0; g < G; ++g)
+        if (!gkeep[g] && (best < 0 || ranks_before(gscore[g], g, gscore[best], best))) best = g;
+      gkeep[best] = 1;
+    }
+    for (int32_t e = 0; e < E; ++e) eligible[e] = gkeep[e / per];
+  }
+
+  for (int32_t j = 0; j < k; ++j) {
+    int32_t best = -1;
+    for (int32_t e = 0; e < E; ++e)
+      if (eligible[e] && (best < 0 || ranks_before(s[e], e, s[best], best))) best = e;
+    idx[j] = best;
+    eligible[best] = 0; /* taken */
+  }
+
+  if (desc->score_fn == 0) {
+    double zmax = -INFINITY;
+    for (int32_t j = 0; j < k; ++j) zmax = fmax(zmax, (double)zt[idx[j]]);
+    double sum = 0.0;
+    for (int32_t j = 0; j < k; ++j) sum += exp((double)zt[idx[j]] - zmax);
+    for (int32_t j = 0; j < k; ++j) wout[j] = (float)(exp((double)zt[idx[j]] - zmax) / sum);
+  } else if (desc->score_fn == 1) {
+    double zmax = -INFINITY;
+    for (int32_t e = 0; e < E; ++e) zmax = fmax(zmax, (double)zt[e]);
+    double sum = 0.0;
+    for (int32_t e = 0; e < E; ++e) sum += exp((double)zt[e] - zmax);
+    for (int32_t j = 0; j < k; ++j) wout[j] = (float)(exp((double)zt[idx[j]] - zmax) / sum);
+  } else {
+    double sum = 0.0;
+    for (int32_t j = 0; j < k; ++j) sum += (double)sigmoid_affinity(zt[idx[j]]);
+    for (int32_t j = 0; j < k; ++j) wout[j] = (float)((double)sigmoid_affinity(zt[idx[j]]) / sum);
+  }
+}
+
+int oracle_select(const oracle_desc* desc, const float* z, const float* sel_bias,
+                  int32_t* topk_idx, float* topk_w, int32_t* counts, float* affinity) {
+  if (!desc_ok(desc) || !counts || (desc->num_tokens > 0 && (!z || !topk_idx || !topk_w)))
+    return -1;
+  const int32_t N = desc->num_tokens, E = desc->num_experts, k = desc->top_k;
+  const int32_t G = desc->num_groups;
+  int failed = 0;
+#pragma omp parallel num_threads(g_threads)
+  {
+    float* s = (float*)malloc(sizeof(float) * E);
+    unsigned char* elig = (unsigned char*)malloc((size_t)E);
+    float* gs = (float*)malloc(sizeof(float) * G);
+    unsigned char* gk = (unsigned char*)malloc((size_t)G);
+    if (!s || !elig || !gs || !gk) {
+#pragma omp atomic write
+      failed = 1;
+    }
+#pragma omp for schedule(static)
+    for (int32_t t = 0; t < N; ++t) {
+      if (!s || !elig || !gs || !gk) continue;
+      select_token(desc, z + (size_t)t * E, sel_bias, topk_idx + (size_t)t * k,
+                   topk_w + (size_t)t * k, affinity ? affinity + (size_t)t * E : NULL, s, elig,
+                   gs, gk);
+    }
+    free(s);
+    free(elig);
+    free(gs);
+    free(gk);
+  }
+  if (failed) return -1;
+  /* Per-expert assignment counts (the snippet's bincount over the chosen
+   * experts, [EP-glossary] routing snippet). */
+  for (int32_t e = 0; e < E; ++e) counts[e] = 0;
+  for (size_t i = 0; i < (size_t)N * k; ++i) counts[topk_idx[i]] += 1;
+  return 0;
+}
+
+/* -------------------------------------------------------------- dispatch -- */
+
+/* Capacity: each expert takes at most a fixed number of token-expert
+ * assignments per batch, the factor times its uniform share N*k/E
+ * ([EP-glossary] "Load balancing and capacity", capacity-factor bullet;
+ * [EP-notes] answer 2: per-expert buffer = mean x 1.25). */
+int64_t oracle_capacity(const oracle_desc* desc) {
+  if (!desc || desc->capacity_factor <= 0.0f) return INT32_MAX;
+  double c = ceil((double)desc->capacity_factor * ((double)desc->num_tokens * desc->top_k) /
+                  (double)desc->num_experts);
+  return c > (double)INT32_MAX ? INT32_MAX : (int64_t)c;
+}
+
+/* Dispatch layout.  Tokens are taken in order; a slot whose expert is already
+ * full is dropped (it "skips that expert").  Rows are grouped by expert, and
+ * experts are placed on ranks in blocks, rank = e / (E/R) (the snippet's
+ * `experts // (num_experts // num_gpus)`), so the same buffer is contiguous per
+ * rank: it is the send buffer of the dispatch all-to-all and rank_counts are
+ * its send counts ([EP-glossary] step 2; [EP-notes] dispatch). */
+int oracle_dispatch(const oracle_desc* desc, const int32_t* topk_idx,
+                    int32_t* row_of_slot, int32_t* token_of_row, int8_t* slot_of_row,
+                    int32_t* expert_offsets, int32_t* admitted,
+                    int32_t* rank_offsets, int32_t* rank_counts) {
+  if (!desc_ok(desc) || !expert_offsets || !admitted || !rank_offsets || !rank_counts) return -1;
+  const int32_t N = desc->num_tokens, E = desc->num_experts, k = desc->top_k;
+  const int32_t R = desc->num_ranks;
+  const size_t S = (size_t)N * k;
+  if (S > 0 && (!topk_idx || !row_of_slot || !token_of_row || !slot_of_row)) return -1;
+  for (size_t i = 0; i < S; ++i)
+    if (topk_idx[i] < 0 || topk_idx[i] >= E) return -1;
+  const int64_t cap = oracle_capacity(desc);
+
+  int32_t* seen = (int32_t*)calloc((size_t)E, sizeof(int32_t));
+  int32_t* rank_in_expert = (int32_t*)malloc(sizeof(int32_t) * (S ? S : 1));
+  int32_t* counts = (int32_t*)calloc((size_t)E, sizeof(int32_t));
+  if (!seen || !rank_in_expert || !counts) {
+    free(seen);
+    free(rank_in_expert);
+    free(counts);
+    return -1;
+  }
+  for (size_t i = 0; i < S; ++i) counts[topk_idx[i]] += 1;
+
+  /* Admission in token order (t outer, slot inner). */
+  for (int32_t t = 0; t < N; ++t) {
+    for (int32_t j = 0; j < k; ++j) {
+      const size_t slot = (size_t)t * k + j;
+      const int32_t e = topk_idx[slot];
+      if (seen[e] < cap) {
+        rank_in_expert[slot] = seen[e];
+        seen[e] += 1;
+      } else {
+        rank_in_expert[slot] = -1; /* dropped */
+      }
+    }
+  }
+
+  int32_t run = 0;
+  for (int32_t e = 0; e < E; ++e) {
+    admitted[e] = counts[e] < cap ? counts[e] : (int32_t)cap;
+    expert_offsets[e] = run;
+    run += admitted[e];
+  }
+  expert_offsets[E] = run;
+
+  for (size_t i = 0; i < S; ++i) {
+    token_of_row[i] = -1;
+    slot_of_row[i] = -1;
+  }
+  for (int32_t t = 0; t < N; ++t) {
+    for (int32_t j = 0; j < k; ++j) {
+      const size_t slot = (size_t)t * k + j;
+      if (rank_in_expert[slot] < 0) {
+        row_of_slot[slot] = -1;
+        continue;
+      }
+      const int32_t row = expert_offsets[topk_idx[slot]] + rank_in_expert[slot];
+      row_of_slot[slot] = row;
+      token_of_row[row] = t;
+      slot_of_row[row] = (int8_t)j;
+    }
+  }
+
+  const int32_t per = E / R;
+  for (int32_t r = 0; r <= R; ++r) rank_offsets[r] = expert_offsets[r * per];
+  for (int32_t r = 0; r < R; ++r) rank_counts[r] = rank_offsets[r + 1] - rank_offsets[r];
+
+  free(seen);
+  free(rank_in_expert);
+  free(counts);
+  return 0;
+}
+
+/* The dispatch payload: each admitted row carries its token's hidden state
+ * unchanged ([EP-glossary] step 2). */
+int oracle_permute(int32_t num_rows, int32_t hidden, int32_t dtype, const void* x,
+                   const int32_t* token_of_row, void* x_perm) {
+  if (num_rows < 0 || hidden < 1 || !dtype_ok(dtype)) return -1;
+  if (num_rows > 0 && (!x || !token_of_row || !x_perm)) return -1;
+  const size_t es = dtype == 0 ? 4 : 2, rb = es * (size_t)hidden;
+  for (int32_t i = 0; i < num_rows; ++i)
+    memcpy((char*)x_perm + (size_t)i * rb, (const char*)x + (size_t)token_of_row[i] * rb, rb);
+  return 0;
+}
+
+/* ------------------------------------------------------------ expert FFN -- */
+
+static double act_relu(double u) { return u > 0.0 ? u : 0.0; }
+static double act_gelu(double u) { return 0.5 * u * (1.0 + erf(u / sqrt(2.0))); }
+static double act_silu(double g) { return g / (1.0 + exp(-g)); }
+
+/* Each expert is an ordinary feed-forward block ([EP-glossary] intro: the MoE
+ * layer replaces one large feed-forward block by many small expert networks;
+ * [EP-notes] "为何不用 TP 切专家": a single expert is an ordinary FFN).
+ * H = act(x W1^T) (SwiGLU: silu(x W1^T) * (x W3^T)), rounded to the dtype;
+ * y = H W2^T, rounded to the dtype.  Sums in fp64. */
+int oracle_ffn_row(int32_t hidden, int32_t ffn_hidden, int32_t act, int32_t dtype,
+                   const void* x_row, const void* w1, const void* w3, const void* w2,
+                   void* y_row) {
+  if (hidden < 1 || ffn_hidden < 1 || act < 0 || act > 2 || !dtype_ok(dtype)) return -1;
+  if (!x_row || !w1 || !w2 || !y_row || (act == 2 && !w3)) return -1;
+  const int32_t d = hidden, h = ffn_hidden;
+  double* xd = (double*)malloc(sizeof(double) * d);
+  double* hd = (double*)malloc(sizeof(double) * h);
+  if (!xd || !hd) {
+    free(xd);
+    free(hd);
+    return -1;
+  }
+  for (int32_t i = 0; i < d; ++i) xd[i] = elem(x_row, dtype, i);
+  for (int32_t j = 0; j < h; ++j) {
+    double u = 0.0;
+    for (int32_t i = 0; i < d; ++i) u += xd[i] * elem(w1, dtype, (size_t)j * d + i);
+    double a;
+    if (act == 0) {
+      a = act_relu(u);
+    } else if (act == 1) {
+      a = act_gelu(u);
+    } else {
+      double v = 0.0;
+      for (int32_t i = 0; i < d; ++i) v += xd[i] * elem(w3, dtype, (size_t)j * d + i);
+      a = act_silu(u) * v;
+    }
+    /* H is stored in the layer dtype before the second projection. */
+    hd[j] = dtype == 0 ? (double)(float)a : bf16_bits_to_double(double_to_bf16_bits(a));
+  }
+  for (int32_t i = 0; i < d; ++i) {
+    double o = 0.0;
+    for (int32_t j = 0; j < h; ++j) o += hd[j] * elem(w2, dtype, (size_t)i * h + j);
+    store(y_row, dtype, (size_t)i, o);
+  }
+  free(xd);
+  free(hd);
+  return 0;
+}
+
+int oracle_expert_ffn(int32_t num_experts, int32_t hidden, int32_t ffn_hidden,
+                      int32_t act, int32_t dtype, const void* x_rows,
+                      const int32_t* offsets, const void* w1, const void* w3,
+                      const void* w2, void* y_rows) {
+  if (num_experts < 1 || hidden < 1 || ffn_hidden < 1 || !dtype_ok(dtype) || !offsets)
+    return -1;
+  if (act < 0 || act > 2) return -1;
+  const size_t es = dtype == 0 ? 4 : 2;
+  const size_t wsz = (size_t)hidden * ffn_hidden * es;
+  const size_t rb = (size_t)hidden * es;
+  for (int32_t e = 0; e < num_experts; ++e)
+    if (offsets[e + 1] < offsets[e] || offsets[e] < 0) return -1;
+  int failed = 0;
+  for (int32_t e = 0; e < num_experts; ++e) {
+    const int32_t lo = offsets[e], hi = offsets[e + 1];
+    const char* w1e = (const char*)w1 + (size_t)e * wsz;
+    const char* w3e = w3 ? (const char*)w3 + (size_t)e * wsz : NULL;
+    const char* w2e = (const char*)w2 + (size_t)e * wsz;
+#pragma omp parallel for num_threads(g_threads) schedule(dynamic, 1)
+    for (int32_t r = lo; r < hi; ++r) {
+      if (oracle_ffn_row(hidden, ffn_hidden, act, dtype, (const char*)x_rows + (size_t)r * rb,
+                         w1e, w3e, w2e, (char*)y_rows + (size_t)r * rb) != 0) {
+#pragma omp atomic write
+        failed = 1;
+      }
+    }
+  }
+  return failed ? -1 : 0;
+}
+
+/* --------------------------------------------------------------- combine -- */
+
+/* Combine: each token's expert outputs come back to it, weighted by the router
+ * scores and summed ([EP-glossary] step 4; [EP-notes] combine).  The layer
+ * output carries the residual, so a token whose every slot was dropped leaves
+ * the layer unchanged ([EP-glossary] "Load balancing and capacity", the
+ * paragraph after the capacity list).  A DeepSeek-style shared expert output
+ * is added with weight 1.  One rounding to the dtype at the end. */
+int oracle_combine(int32_t num_tokens, int32_t hidden, int32_t top_k, int32_t dtype,
+                   const void* y_perm, const int32_t* row_of_slot, const float* topk_w,
+                   const void* residual, const void* shared_out, void* y) {
+  if (num_tokens < 0 || hidden < 1 || top_k < 1 || !dtype_ok(dtype)) return -1;
+  if (num_tokens > 0 && (!row_of_slot || !topk_w || !y)) return -1;
+  for (int32_t t = 0; t < num_tokens; ++t) {
+    for (int32_t i = 0; i < hidden; ++i) {
+      const size_t ti = (size_t)t * hidden + i;
+      double acc = residual ? elem(residual, dtype, ti) : 0.0;
+      if (shared_out) acc += elem(shared_out, dtype, ti);
+      for (int32_t j = 0; j < top_k; ++j) {
+        const int32_t row = row_of_slot[(size_t)t * top_k + j];
+        if (row < 0) continue;
+        if (!y_perm) return -1;
+        acc += (double)topk_w[(size_t)t * top_k + j] *
+               elem(y_perm, dtype, (size_t)row * hidden + i);
+      }
+      store(y, dtype, ti, acc);
+    }
+  }
+  return 0;
+}
+
+/* ------------------------------------------------------------ bias update -- */
+
+/* Bias-based balancing: after each step the bias of overloaded experts goes
+ * down and that of idle experts goes up ([EP-glossary] "Load balancing and
+ * capacity", bias-based balancing bullet).  Load = pre-capacity assignment
+ * count, compared with the mean N*k/E in integers (count*E vs N*k); equal
+ * load leaves the bias as it is.  The step is applied in fp32. */
+int oracle_bias_update(int32_t num_experts, int32_t num_tokens, int32_t top_k,
+                       const int32_t* counts, float step, float* sel_bias) {
+  if (num_experts < 1 || num_tokens < 0 || top_k < 1 || !counts || !sel_bias) return -1;
+  const int64_t mean_times_e = (int64_t)num_tokens * top_k;
+  for (int32_t e = 0; e < num_experts; ++e) {
+    const int64_t load_times_e = (int64_t)counts[e] * num_experts;
+    if (load_times_e > mean_times_e)
+      sel_bias[e] = sel_bias[e] - step;
+    else if (load_times_e < mean_times_e)
+      sel_bias[e] = sel_bias[e] + step;
+  }
+  return 0;
+}

@@ -1,0 +1,110 @@
+/*
+ * oracle.h -- CPU reference for the single-GPU forward of a Mixture-of-Experts
+ * layer (route -> dispatch -> expert FFN -> combine, plus the selection-bias
+ * update).
+ *
+ * TEST INFRASTRUCTURE ONLY.  This library is the correctness oracle for the
+ * HIP path.  Only the tests, the smoke entry point and the CPU-baseline leg of
+ * the benchmark may load it.  It shares no code, header, table or helper with
+ * the HIP library, and the HIP library never calls it.
+ *
+ * Everything is plain per-token / per-row loops in fp64 except where a
+ * rounding point is part of the definition (logits to fp32; hidden activations,
+ * expert outputs and layer outputs to the layer dtype, round-to-nearest-even).
+ *
+ * Sources (web pages; each function cites the passage it follows):
+ *  [EP-glossary]  "Expert Parallelism", Ultralytics glossary (zh/de/ja
+ *                 editions say the same): sections "How tokens travel between
+ *                 GPUs" (four steps + routing snippet), "Load balancing and
+ *                 capacity" (capacity factor, selection-only bias, drops pass
+ *                 through the residual, node-limited routing).
+ *  [EP-notes]     "专家并行" (bowenzhou.top): "MoE 的账先算清楚" (256 routed +
+ *                 1 shared expert, 8 active), "机制：all-to-all 两轮"
+ *                 (dispatch/combine), answer 2 of "参考答案" (per-expert buffer
+ *                 = mean x capacity factor).
+ *  [MLSys-ch10]   "第 10 章 模型并行与专家并行", section 10.5 (top-1 Switch,
+ *                 top-2 GShard, DeepSeekMoE shared + fine-grained experts).
+ *
+ * Dtype codes: 0 = fp32, 1 = bf16 (raw uint16 bit patterns).
+ * Score codes: 0 = softmax over the k selected logits, 1 = softmax over all E
+ *              logits (not renormalised), 2 = sigmoid affinities renormalised
+ *              over the k selected.
+ * Activation codes: 0 = ReLU, 1 = GELU (erf), 2 = SwiGLU.
+ * Return value of every int function: 0 on success, -1 on invalid arguments.
+ */
+#ifndef MOE_ORACLE_H
+#define MOE_ORACLE_H
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef struct {
+  int32_t num_tokens;      /* N */
+  int32_t hidden;          /* d */
+  int32_t num_experts;     /* E */
+  int32_t top_k;           /* k */
+  int32_t num_ranks;       /* R, E % R == 0 */
+  float   capacity_factor; /* <= 0: no capacity limit */
+  int32_t num_groups;      /* G, 1 = no group limit */
+  int32_t topk_groups;     /* kg */
+  int32_t score_fn;        /* 0/1/2, see above */
+  int32_t dtype;           /* 0 fp32, 1 bf16 */
+} oracle_desc;
+
+/* Router logits z[N,E] (fp32) of x[N,d] against w[E,d], plus bias[E] (nullable). */
+int oracle_logits(const oracle_desc* desc, const void* x, const void* w,
+                  const float* router_bias, float* z);
+
+/* Selection from given logits: topk_idx[N,k], topk_w[N,k], counts[E].
+ * sel_bias[E] is nullable. affinity[N,E] (nullable) receives the fp32 score
+ * f(z) before the bias (z itself for the softmax modes). */
+int oracle_select(const oracle_desc* desc, const float* z, const float* sel_bias,
+                  int32_t* topk_idx, float* topk_w, int32_t* counts, float* affinity);
+
+/* Capacity, token-order admission and the expert/rank-contiguous layout.
+ * token_of_row / slot_of_row have N*k entries; entries from M on are set to -1. */
+int oracle_dispatch(const oracle_desc* desc, const int32_t* topk_idx,
+                    int32_t* row_of_slot, int32_t* token_of_row, int8_t* slot_of_row,
+                    int32_t* expert_offsets, int32_t* admitted,
+                    int32_t* rank_offsets, int32_t* rank_counts);
+
+/* x_perm[i] = x[token_of_row[i]] for i < num_rows (a byte copy). */
+int oracle_permute(int32_t num_rows, int32_t hidden, int32_t dtype, const void* x,
+                   const int32_t* token_of_row, void* x_perm);
+
+/* One row of one expert's FFN: y = W2 act(W1 x [, W3 x]).  w1/w3 are [h,d],
+ * w2 is [d,h] (row-major, out x in); w3 only for SwiGLU (gate = w1, up = w3). */
+int oracle_ffn_row(int32_t hidden, int32_t ffn_hidden, int32_t act, int32_t dtype,
+                   const void* x_row, const void* w1, const void* w3, const void* w2,
+                   void* y_row);
+
+/* Grouped FFN: rows [offsets[e], offsets[e+1]) of x_rows use expert e's
+ * weights w1[e], w3[e], w2[e] ([E,h,d], [E,h,d], [E,d,h]). */
+int oracle_expert_ffn(int32_t num_experts, int32_t hidden, int32_t ffn_hidden,
+                      int32_t act, int32_t dtype, const void* x_rows,
+                      const int32_t* offsets, const void* w1, const void* w3,
+                      const void* w2, void* y_rows);
+
+/* y[t] = residual[t] + shared[t] + sum_j w[t,j] y_perm[row_of_slot[t,j]]
+ * (residual, shared nullable; dropped slots, row < 0, contribute nothing). */
+int oracle_combine(int32_t num_tokens, int32_t hidden, int32_t top_k, int32_t dtype,
+                   const void* y_perm, const int32_t* row_of_slot, const float* topk_w,
+                   const void* residual, const void* shared_out, void* y);
+
+/* Selection-bias update from pre-capacity counts. */
+int oracle_bias_update(int32_t num_experts, int32_t num_tokens, int32_t top_k,
+                       const int32_t* counts, float step, float* sel_bias);
+
+/* Capacity for a descriptor (INT32_MAX when unlimited). */
+int64_t oracle_capacity(const oracle_desc* desc);
+
+/* Threads the route loop may use (OpenMP over tokens; 1 = sequential). */
+void oracle_set_threads(int32_t n);
+int32_t oracle_get_threads(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif

@@ -1,0 +1,194 @@
+"""Pins of the oracle's dispatch step (capacity, token-order admission,
+expert/rank-contiguous layout, permute) and the selection-bias update.  CPU only.
+"""
+
+import numpy as np
+import pytest
+from hypothesis import given, settings, strategies as st
+
+import oracle
+
+
+def _cfg(**kw):
+    base = dict(name="t", N=0, d=4, h=4, E=8, k=2, R=1, cf=0.0, G=1, kg=1,
+                score="softmax_topk", act="relu", dtype="fp32")
+    base.update(kw)
+    return base
+
+
+def _random_topk(rng, N, E, k, skew=0.0):
+    """k distinct experts per token, optionally skewed toward low indices."""
+    p = np.arange(1, E + 1, dtype=np.float64) ** (-skew)
+    p /= p.sum()
+    out = np.empty((N, k), np.int32)
+    for t in range(N):
+        out[t] = rng.choice(E, size=k, replace=False, p=p)
+    return out
+
+
+def _check_invariants(cfg, idx, dsp):
+    N, k, E, R = idx.shape[0], cfg["k"], cfg["E"], cfg["R"]
+    cap = oracle.capacity(cfg)
+    counts = np.bincount(idx.ravel(), minlength=E)
+    adm = dsp["admitted"]
+    assert np.array_equal(adm, np.minimum(counts, cap))
+    M = dsp["num_rows"]
+    ros = dsp["row_of_slot"]
+    dropped = (ros < 0).sum()
+    assert adm.sum() == N * k - dropped == M
+    off = dsp["expert_offsets"]
+    assert off[0] == 0 and np.array_equal(np.diff(off), adm)
+    # Bijection: admitted slots <-> rows [0, M)
+    t_idx, j_idx = np.nonzero(ros >= 0)
+    rows = ros[t_idx, j_idx]
+    assert np.array_equal(np.sort(rows), np.arange(M))
+    assert np.array_equal(dsp["token_of_row"][rows], t_idx)
+    assert np.array_equal(dsp["slot_of_row"][rows], j_idx)
+    # Each row sits in its expert's segment; tokens increase inside a segment.
+    e_of_row = np.repeat(np.arange(E), adm)
+    assert np.array_equal(idx[t_idx, j_idx], e_of_row[rows])
+    tor = dsp["token_of_row"][:M]
+    for e in range(E):
+        seg = tor[off[e]:off[e + 1]]
+        assert np.all(np.diff(seg) > 0)
+    # Ranks: blocks of E/R experts, counts are sums over the block.
+    per = E // R
+    assert np.array_equal(dsp["rank_counts"], adm.reshape(R, per).sum(1))
+    assert np.array_equal(dsp["rank_offsets"], off[::per])
+    return counts
+
+
+def test_no_capacity_equals_stable_argsort():
+    """Without a capacity limit the rows are the flattened (token, slot) list
+    stably sorted by expert: numpy.argsort(kind='stable')."""
+    rng = np.random.default_rng(20)
+    for N, E, k in [(1000, 8, 2), (777, 64, 1), (300, 256, 8)]:
+        idx = _random_topk(rng, N, E, k)
+        dsp = oracle.dispatch(_cfg(N=N, E=E, k=k, R=E // 4 if E >= 4 else 1), idx)
+        order = np.argsort(idx.ravel(), kind="stable")
+        assert np.array_equal(dsp["token_of_row"], order // k)
+        assert np.array_equal(dsp["slot_of_row"], (order % k).astype(np.int8))
+        assert dsp["num_rows"] == N * k
+
+
+def test_capacity_fifo_brute_force():
+    """Capacity admission equals an explicit per-expert FIFO filled in token
+    order that turns away arrivals once it holds `cap` entries."""
+    rng = np.random.default_rng(21)
+    for trial in range(40):
+        E = int(rng.choice([2, 4, 8, 16]))
+        k = int(rng.integers(1, min(3, E) + 1))
+        N = int(rng.integers(1, 200))
+        cf = float(rng.choice([0.25, 0.5, 1.0, 1.25, 2.0]))
+        idx = _random_topk(rng, N, E, k, skew=float(rng.choice([0.0, 1.5])))
+        cfg = _cfg(N=N, E=E, k=k, cf=cf)
+        dsp = oracle.dispatch(cfg, idx)
+        cap = int(np.ceil(np.float64(np.float32(cf)) * N * k / E))
+        assert oracle.capacity(cfg) == cap
+        queues = {e: [] for e in range(E)}
+        for t in range(N):
+            for j in range(k):
+                e = idx[t, j]
+                if len(queues[e]) < cap:
+                    queues[e].append((t, j))
+        expect_rows = [ts for e in range(E) for ts in queues[e]]
+        M = dsp["num_rows"]
+        assert M == len(expect_rows)
+        got = list(zip(dsp["token_of_row"][:M].tolist(), dsp["slot_of_row"][:M].tolist()))
+        assert got == expect_rows
+        _check_invariants(cfg, idx, dsp)
+
+
+def test_capacity_one_admits_first_token_per_expert():
+    rng = np.random.default_rng(22)
+    N, E, k = 64, 8, 2
+    idx = _random_topk(rng, N, E, k)
+    cfg = _cfg(N=N, E=E, k=k, cf=E / (N * k))  # cap = ceil(1) = 1
+    assert oracle.capacity(cfg) == 1
+    dsp = oracle.dispatch(cfg, idx)
+    for e in range(E):
+        first = np.argwhere(idx == e)
+        if len(first):
+            t, j = first[0]
+            assert dsp["row_of_slot"][t, j] == dsp["expert_offsets"][e]
+    assert np.array_equal(dsp["admitted"], (np.bincount(idx.ravel(), minlength=E) > 0).astype(int))
+
+
+def test_uniform_routing_no_drops_at_cf_one():
+    """Forced round-robin routing gives every expert exactly N*k/E slots, so a
+    capacity factor of 1 drops nothing."""
+    N, E, k = 512, 16, 2
+    idx = np.stack([(np.arange(N) * k + j) % E for j in range(k)], 1).astype(np.int32)
+    cfg = _cfg(N=N, E=E, k=k, cf=1.0, R=4)
+    dsp = oracle.dispatch(cfg, idx)
+    assert np.all(dsp["admitted"] == N * k // E)
+    assert np.all(dsp["row_of_slot"] >= 0)
+
+
+def test_tiny_capacity_drops_nearly_everything():
+    rng = np.random.default_rng(23)
+    N, E, k = 1000, 8, 2
+    idx = _random_topk(rng, N, E, k)
+    cfg = _cfg(N=N, E=E, k=k, cf=1e-6)
+    dsp = oracle.dispatch(cfg, idx)
+    assert dsp["num_rows"] == E  # cap rounds up to 1
+    _check_invariants(cfg, idx, dsp)
+
+
+def test_empty_batch():
+    cfg = _cfg(N=0, E=8, k=2, R=4, cf=1.25)
+    dsp = oracle.dispatch(cfg, np.zeros((0, 2), np.int32))
+    assert dsp["num_rows"] == 0
+    assert np.all(dsp["expert_offsets"] == 0) and np.all(dsp["rank_counts"] == 0)
+
+
+def test_out_of_range_expert_rejected():
+    with pytest.raises(ValueError):
+        oracle.dispatch(_cfg(N=1, E=4, k=1), np.array([[4]], np.int32))
+
+
+@settings(max_examples=60, deadline=None)
+@given(N=st.integers(0, 300), E_pow=st.integers(0, 8), k=st.integers(1, 8),
+       R_pow=st.integers(0, 6), cf=st.sampled_from([0.0, 0.5, 1.0, 1.25, 2.0]),
+       skew=st.sampled_from([0.0, 1.1, 3.0]), seed=st.integers(0, 2 ** 31 - 1))
+def test_dispatch_invariants_property(N, E_pow, k, R_pow, cf, skew, seed):
+    E = 2 ** E_pow
+    k = min(k, E)
+    R = 2 ** min(R_pow, E_pow)
+    rng = np.random.default_rng(seed)
+    idx = _random_topk(rng, N, E, k, skew)
+    cfg = _cfg(N=N, E=E, k=k, R=R, cf=cf)
+    dsp = oracle.dispatch(cfg, idx)
+    _check_invariants(cfg, idx, dsp)
+
+
+def test_permute_is_bitwise_row_copy():
+    rng = np.random.default_rng(24)
+    N, d, E, k = 100, 32, 4, 2
+    idx = _random_topk(rng, N, E, k)
+    dsp = oracle.dispatch(_cfg(N=N, E=E, k=k, d=d), idx)
+    x = rng.integers(0, 65535, (N, d)).astype(np.uint16)  # arbitrary bit patterns
+    xp = oracle.permute("bf16", x, dsp["token_of_row"], dsp["num_rows"])
+    assert np.array_equal(xp, x[dsp["token_of_row"][:dsp["num_rows"]]])
+
+
+# ----------------------------------------------------------- bias update ----
+
+def test_bias_update_closed_form():
+    """Mean load N*k/E = 4: load 5 lowers the bias by the step, 3 raises it,
+    4 leaves it bitwise unchanged."""
+    counts = np.array([5, 3, 4, 4, 0, 8], np.int32)  # N*k = 24, E = 6
+    b0 = np.array([0.0, 0.0, 0.25, -1.5, 1.0, 1e-3], np.float32)
+    b = oracle.bias_update(12, 2, counts, b0, 1e-3)
+    step = np.float32(1e-3)
+    expect = np.array([b0[0] - step, b0[1] + step, b0[2], b0[3], b0[4] + step, b0[5] - step],
+                      np.float32)
+    assert np.array_equal(b.view(np.uint32), expect.view(np.uint32))
+    assert b[5] == 0.0
+
+
+def test_bias_update_non_integer_mean():
+    """Mean 7/3 is not an integer: loads 2 and 3 fall strictly below/above."""
+    counts = np.array([2, 3, 2], np.int32)  # N*k = 7
+    b = oracle.bias_update(7, 1, counts, np.zeros(3, np.float32), 0.5)
+    assert b.tolist() == [0.5, -0.5, 0.5]
