@@ -1,0 +1,241 @@
+"""Python binding of the MI355X MoE-layer forward library (``include/moe.h``).
+
+Argument marshalling only: every function here checks the torch tensors it is
+given (device, dtype, shape, contiguity), passes their device pointers and the
+current HIP stream to the C ABI of ``libmoe_mi355x.so``, and raises
+``MoeError`` on a non-zero status.  All computation happens in the library's
+gfx950 kernels; there is no fallback path.  PyTorch only provides device
+memory and streams.
+
+Entry points (same names and argument order as the C ABI):
+``moe_route``, ``moe_dispatch``, ``moe_expert_ffn``, ``moe_combine``,
+``moe_bias_update``, plus the ``*_workspace_size`` queries.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+PKG_DIR = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(PKG_DIR, "libmoe_mi355x.so")
+
+MOE_OK, MOE_ERR_INVALID_ARG, MOE_ERR_UNSUPPORTED, MOE_ERR_HIP, MOE_ERR_WORKSPACE = range(5)
+MOE_F32, MOE_BF16 = 0, 1
+MOE_SOFTMAX_TOPK, MOE_SOFTMAX_ALL, MOE_SIGMOID_NORM = 0, 1, 2
+MOE_RELU, MOE_GELU, MOE_SWIGLU = 0, 1, 2
+
+SCORE = {"softmax_topk": MOE_SOFTMAX_TOPK, "softmax_all": MOE_SOFTMAX_ALL,
+         "sigmoid_norm": MOE_SIGMOID_NORM}
+ACT = {"relu": MOE_RELU, "gelu": MOE_GELU, "swiglu": MOE_SWIGLU}
+DTYPE = {"fp32": MOE_F32, "bf16": MOE_BF16}
+TORCH_DTYPE = {MOE_F32: torch.float32, MOE_BF16: torch.bfloat16}
+
+EXPORTS = [
+    "moe_route_workspace_size", "moe_route", "moe_dispatch_workspace_size", "moe_dispatch",
+    "moe_expert_ffn_workspace_size", "moe_expert_ffn", "moe_combine", "moe_bias_update",
+    "moe_status_string",
+]
+
+
+class MoeError(RuntimeError):
+    def __init__(self, fn: str, status: int, msg: str):
+        super().__init__(f"{fn}: {msg} (status {status})")
+        self.status = status
+
+
+class RouteDesc(ctypes.Structure):
+    """Mirror of ``moe_route_desc``."""
+
+    _fields_ = [
+        ("num_tokens", ctypes.c_int32),
+        ("hidden", ctypes.c_int32),
+        ("num_experts", ctypes.c_int32),
+        ("top_k", ctypes.c_int32),
+        ("num_ranks", ctypes.c_int32),
+        ("capacity_factor", ctypes.c_float),
+        ("num_groups", ctypes.c_int32),
+        ("topk_groups", ctypes.c_int32),
+        ("score_fn", ctypes.c_int32),
+        ("dtype", ctypes.c_int32),
+    ]
+
+
+def route_desc(N, d, E, k, R=1, cf=0.0, G=1, kg=1, score="softmax_topk", dtype="bf16"):
+    return RouteDesc(int(N), int(d), int(E), int(k), int(R), float(cf or 0.0), int(G), int(kg),
+                     SCORE[score] if isinstance(score, str) else int(score),
+                     DTYPE[dtype] if isinstance(dtype, str) else int(dtype))
+
+
+def desc_from_workload(cfg: dict, N: int | None = None, cf: float | None = None) -> RouteDesc:
+    """Descriptor from a workload dictionary (keys N d E k R cf G kg score dtype)."""
+    return route_desc(cfg["N"] if N is None else N, cfg["d"], cfg["E"], cfg["k"],
+                      cfg.get("R", 1), cfg.get("cf", 0.0) if cf is None else cf,
+                      cfg.get("G", 1), cfg.get("kg", 1), cfg["score"], cfg["dtype"])
+
+
+_lib = None
+
+
+def lib() -> ctypes.CDLL:
+    """Load the HIP library; fails loudly if it has not been built."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is missing: build it with __graft_entry__.build()")
+        L = ctypes.CDLL(LIB_PATH)
+        P, I32, SZ, F32 = ctypes.c_void_p, ctypes.c_int32, ctypes.c_size_t, ctypes.c_float
+        D = ctypes.POINTER(RouteDesc)
+        sigs = {
+            "moe_route_workspace_size": ([D], SZ),
+            "moe_route": ([D, P, P, P, P, P, P, P, P, P, SZ, P], I32),
+            "moe_dispatch_workspace_size": ([D], SZ),
+            "moe_dispatch": ([D, P, P, P, P, P, P, P, P, P, P, P, SZ, P], I32),
+            "moe_expert_ffn_workspace_size": ([I32, I32, I32, I32, I32, I32], SZ),
+            "moe_expert_ffn": ([I32, I32, I32, I32, I32, I32, P, P, P, P, P, P, P, SZ, P], I32),
+            "moe_combine": ([D, P, P, P, P, P, P, P], I32),
+            "moe_bias_update": ([I32, I32, I32, P, F32, P, P], I32),
+            "moe_status_string": ([I32], ctypes.c_char_p),
+        }
+        for name, (args, res) in sigs.items():
+            fn = getattr(L, name)
+            fn.argtypes = args
+            fn.restype = res
+        _lib = L
+    return _lib
+
+
+def status_string(status: int) -> str:
+    return lib().moe_status_string(int(status)).decode()
+
+
+def _raise(fn: str, status: int):
+    if status != MOE_OK:
+        raise MoeError(fn, status, status_string(status))
+
+
+def _stream(stream):
+    if stream is None:
+        return ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+    if isinstance(stream, torch.cuda.Stream):
+        return ctypes.c_void_p(stream.cuda_stream)
+    return ctypes.c_void_p(int(stream))
+
+
+def _ptr(t, name, dtype=None, numel=None, required=True):
+    """Device pointer of a contiguous CUDA tensor (None -> NULL)."""
+    if t is None:
+        if required:
+            raise ValueError(f"{name} is required")
+        return None
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if t.device.type != "cuda":
+        raise ValueError(f"{name} must be on a HIP device, got {t.device}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if dtype is not None and t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if numel is not None and t.numel() < numel:
+        raise ValueError(f"{name} holds {t.numel()} elements, needs {numel}")
+    return ctypes.c_void_p(t.data_ptr())
+
+
+def moe_route_workspace_size(desc: RouteDesc) -> int:
+    return int(lib().moe_route_workspace_size(ctypes.byref(desc)))
+
+
+def moe_dispatch_workspace_size(desc: RouteDesc) -> int:
+    return int(lib().moe_dispatch_workspace_size(ctypes.byref(desc)))
+
+
+def moe_expert_ffn_workspace_size(num_experts, max_rows, hidden, ffn_hidden, act, dtype) -> int:
+    act = ACT[act] if isinstance(act, str) else int(act)
+    dtype = DTYPE[dtype] if isinstance(dtype, str) else int(dtype)
+    return int(lib().moe_expert_ffn_workspace_size(num_experts, max_rows, hidden, ffn_hidden,
+                                                   act, dtype))
+
+
+def workspace(nbytes: int, device="cuda") -> torch.Tensor:
+    """Caller-owned scratch buffer (256-byte aligned by the caching allocator)."""
+    return torch.empty(max(int(nbytes), 256), dtype=torch.uint8, device=device)
+
+
+def moe_route(desc, x, w_router, router_bias, sel_bias, logits, topk_idx, topk_w, counts,
+              ws, stream=None):
+    N, d, E, k = desc.num_tokens, desc.hidden, desc.num_experts, desc.top_k
+    dt = TORCH_DTYPE.get(desc.dtype)
+    st = lib().moe_route(
+        ctypes.byref(desc), _ptr(x, "x", dt, N * d, N > 0), _ptr(w_router, "w_router", dt, E * d, N > 0),
+        _ptr(router_bias, "router_bias", torch.float32, E, False),
+        _ptr(sel_bias, "sel_bias", torch.float32, E, False),
+        _ptr(logits, "logits", torch.float32, N * E, N > 0),
+        _ptr(topk_idx, "topk_idx", torch.int32, N * k, N > 0),
+        _ptr(topk_w, "topk_w", torch.float32, N * k, N > 0),
+        _ptr(counts, "counts", torch.int32, E),
+        _ptr(ws, "ws", None, None, False), 0 if ws is None else ws.numel() * ws.element_size(),
+        _stream(stream))
+    _raise("moe_route", st)
+
+
+def moe_dispatch(desc, x, topk_idx, x_perm, row_of_slot, token_of_row, slot_of_row,
+                 expert_offsets, admitted, rank_offsets, rank_counts, ws, stream=None):
+    N, d, E, k, R = desc.num_tokens, desc.hidden, desc.num_experts, desc.top_k, desc.num_ranks
+    dt = TORCH_DTYPE.get(desc.dtype)
+    S = N * k
+    st = lib().moe_dispatch(
+        ctypes.byref(desc), _ptr(x, "x", dt, N * d, N > 0),
+        _ptr(topk_idx, "topk_idx", torch.int32, S, N > 0),
+        _ptr(x_perm, "x_perm", dt, S * d, N > 0),
+        _ptr(row_of_slot, "row_of_slot", torch.int32, S, N > 0),
+        _ptr(token_of_row, "token_of_row", torch.int32, S, N > 0),
+        _ptr(slot_of_row, "slot_of_row", torch.int8, S, N > 0),
+        _ptr(expert_offsets, "expert_offsets", torch.int32, E + 1),
+        _ptr(admitted, "admitted", torch.int32, E),
+        _ptr(rank_offsets, "rank_offsets", torch.int32, R + 1),
+        _ptr(rank_counts, "rank_counts", torch.int32, R),
+        _ptr(ws, "ws", None, None, False), 0 if ws is None else ws.numel() * ws.element_size(),
+        _stream(stream))
+    _raise("moe_dispatch", st)
+
+
+def moe_expert_ffn(num_experts, max_rows, hidden, ffn_hidden, act, dtype, x_rows,
+                   group_offsets, w1, w3, w2, y_rows, ws, stream=None):
+    act = ACT[act] if isinstance(act, str) else int(act)
+    dtype = DTYPE[dtype] if isinstance(dtype, str) else int(dtype)
+    dt = TORCH_DTYPE.get(dtype)
+    E, M, d, h = num_experts, max_rows, hidden, ffn_hidden
+    st = lib().moe_expert_ffn(
+        E, M, d, h, act, dtype, _ptr(x_rows, "x_rows", dt, M * d, M > 0),
+        _ptr(group_offsets, "group_offsets", torch.int32, E + 1),
+        _ptr(w1, "w1", dt, E * h * d), _ptr(w3, "w3", dt, E * h * d, act == MOE_SWIGLU),
+        _ptr(w2, "w2", dt, E * d * h), _ptr(y_rows, "y_rows", dt, M * d, M > 0),
+        _ptr(ws, "ws", None, None, False), 0 if ws is None else ws.numel() * ws.element_size(),
+        _stream(stream))
+    _raise("moe_expert_ffn", st)
+
+
+def moe_combine(desc, y_perm, row_of_slot, topk_w, residual, shared_out, y, stream=None):
+    N, d, k = desc.num_tokens, desc.hidden, desc.top_k
+    dt = TORCH_DTYPE.get(desc.dtype)
+    st = lib().moe_combine(
+        ctypes.byref(desc), _ptr(y_perm, "y_perm", dt, None, N > 0),
+        _ptr(row_of_slot, "row_of_slot", torch.int32, N * k, N > 0),
+        _ptr(topk_w, "topk_w", torch.float32, N * k, N > 0),
+        _ptr(residual, "residual", dt, N * d, False),
+        _ptr(shared_out, "shared_out", dt, N * d, False),
+        _ptr(y, "y", dt, N * d, N > 0), _stream(stream))
+    _raise("moe_combine", st)
+
+
+def moe_bias_update(num_experts, num_tokens, top_k, counts, step, sel_bias, stream=None):
+    st = lib().moe_bias_update(
+        int(num_experts), int(num_tokens), int(top_k),
+        _ptr(counts, "counts", torch.int32, num_experts),
+        float(step), _ptr(sel_bias, "sel_bias", torch.float32, num_experts), _stream(stream))
+    _raise("moe_bias_update", st)
+
+
+from .layer import MoeBuffers, moe_forward  # noqa: E402,F401  (composition of the calls above)

@@ -1,0 +1,176 @@
+// api.hip -- the C ABI declared in include/moe.h: host-side validation, then
+// the launches.  Nothing here allocates device memory or synchronises.
+#include <math.h>
+
+#include "../../include/moe.h"
+#include "kernels.h"
+
+namespace {
+
+constexpr int kMaxExperts = 256;   // routing kernels: <= 4 experts per lane
+constexpr int kMaxTopK = 8;        // per-token register arrays; int8 slot ids
+constexpr int kMaxGroups = 64;     // group mask fits one 64-bit word
+constexpr int kMaxFfnExperts = 1024;
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+// Returns MOE_OK or the status describing what is wrong with desc.
+int check_desc(const moe_route_desc* d) {
+  if (!d) return MOE_ERR_INVALID_ARG;
+  if (d->num_tokens < 0 || d->hidden < 1 || d->num_experts < 1 || d->top_k < 1)
+    return MOE_ERR_INVALID_ARG;
+  if (d->top_k > d->num_experts) return MOE_ERR_INVALID_ARG;
+  if (d->num_ranks < 1 || d->num_experts % d->num_ranks != 0) return MOE_ERR_INVALID_ARG;
+  if (d->num_groups < 1 || d->num_experts % d->num_groups != 0) return MOE_ERR_INVALID_ARG;
+  if (d->topk_groups < 1 || d->topk_groups > d->num_groups) return MOE_ERR_INVALID_ARG;
+  if ((long long)d->topk_groups * (d->num_experts / d->num_groups) < d->top_k)
+    return MOE_ERR_INVALID_ARG;
+  if (d->score_fn < MOE_SOFTMAX_TOPK || d->score_fn > MOE_SIGMOID_NORM) return MOE_ERR_INVALID_ARG;
+  if (d->dtype != MOE_F32 && d->dtype != MOE_BF16) return MOE_ERR_INVALID_ARG;
+  if (isnan(d->capacity_factor)) return MOE_ERR_INVALID_ARG;
+  if ((long long)d->num_tokens * d->top_k > 0x7fffffffLL) return MOE_ERR_INVALID_ARG;
+  if (d->hidden % 8 != 0) return MOE_ERR_UNSUPPORTED;
+  if (d->num_experts > kMaxExperts || d->top_k > kMaxTopK || d->num_groups > kMaxGroups)
+    return MOE_ERR_UNSUPPORTED;
+  return MOE_OK;
+}
+
+int32_t capacity_of(const moe_route_desc* d) {
+  if (!(d->capacity_factor > 0.0f)) return 0x7fffffff;
+  const double c = ceil((double)d->capacity_factor * ((double)d->num_tokens * d->top_k) /
+                        (double)d->num_experts);
+  return c > 2147483647.0 ? 0x7fffffff : (int32_t)c;
+}
+
+int status_of(hipError_t e) { return e == hipSuccess ? MOE_OK : MOE_ERR_HIP; }
+
+}  // namespace
+
+extern "C" {
+
+const char* moe_status_string(int status) {
+  switch (status) {
+    case MOE_OK: return "ok";
+    case MOE_ERR_INVALID_ARG: return "invalid argument";
+    case MOE_ERR_UNSUPPORTED: return "unsupported configuration";
+    case MOE_ERR_HIP: return "HIP launch error";
+    case MOE_ERR_WORKSPACE: return "workspace missing or too small";
+    default: return "unknown status";
+  }
+}
+
+size_t moe_route_workspace_size(const moe_route_desc* desc) {
+  if (check_desc(desc) != MOE_OK) return 0;
+  return moe::route_workspace_bytes(desc->num_tokens, desc->hidden, desc->num_experts);
+}
+
+int moe_route(const moe_route_desc* desc, const void* x, const void* w_router,
+              const float* router_bias, const float* sel_bias, float* logits,
+              int32_t* topk_idx, float* topk_w, int32_t* counts, void* ws, size_t ws_bytes,
+              void* stream) {
+  int st = check_desc(desc);
+  if (st != MOE_OK) return st;
+  if (!counts) return MOE_ERR_INVALID_ARG;
+  const int N = desc->num_tokens;
+  if (N > 0) {
+    if (!x || !w_router || !logits || !topk_idx || !topk_w) return MOE_ERR_INVALID_ARG;
+    if (!aligned16(x)) return MOE_ERR_INVALID_ARG;
+    const size_t need = moe::route_workspace_bytes(N, desc->hidden, desc->num_experts);
+    if (!ws || ws_bytes < need || (reinterpret_cast<uintptr_t>(ws) & 15u)) return MOE_ERR_WORKSPACE;
+  }
+  moe::RouteArgs a{N, desc->hidden, desc->num_experts, desc->top_k, desc->num_groups,
+                   desc->topk_groups, desc->score_fn, desc->dtype, x, w_router, router_bias,
+                   sel_bias, logits, topk_idx, topk_w, counts, ws};
+  return status_of(moe::launch_route(a, static_cast<hipStream_t>(stream)));
+}
+
+size_t moe_dispatch_workspace_size(const moe_route_desc* desc) {
+  if (check_desc(desc) != MOE_OK) return 0;
+  return moe::dispatch_workspace_bytes(desc->num_tokens, desc->top_k, desc->num_experts);
+}
+
+int moe_dispatch(const moe_route_desc* desc, const void* x, const int32_t* topk_idx,
+                 void* x_perm, int32_t* row_of_slot, int32_t* token_of_row,
+                 int8_t* slot_of_row, int32_t* expert_offsets, int32_t* admitted,
+                 int32_t* rank_offsets, int32_t* rank_counts, void* ws, size_t ws_bytes,
+                 void* stream) {
+  int st = check_desc(desc);
+  if (st != MOE_OK) return st;
+  if (!expert_offsets || !admitted || !rank_offsets || !rank_counts) return MOE_ERR_INVALID_ARG;
+  const int N = desc->num_tokens;
+  if (N > 0) {
+    if (!x || !topk_idx || !x_perm || !row_of_slot || !token_of_row || !slot_of_row)
+      return MOE_ERR_INVALID_ARG;
+    if (!aligned16(x) || !aligned16(x_perm)) return MOE_ERR_INVALID_ARG;
+  }
+  const size_t need = moe::dispatch_workspace_bytes(N, desc->top_k, desc->num_experts);
+  if (!ws || ws_bytes < need || (reinterpret_cast<uintptr_t>(ws) & 15u)) return MOE_ERR_WORKSPACE;
+  moe::DispatchArgs a{N, desc->hidden, desc->num_experts, desc->top_k, desc->num_ranks,
+                      desc->dtype, capacity_of(desc), x, topk_idx, x_perm, row_of_slot,
+                      token_of_row, slot_of_row, expert_offsets, admitted, rank_offsets,
+                      rank_counts, ws};
+  return status_of(moe::launch_dispatch(a, static_cast<hipStream_t>(stream)));
+}
+
+static int check_ffn(int32_t E, int32_t max_rows, int32_t d, int32_t h, int32_t act,
+                     int32_t dtype) {
+  if (E < 1 || max_rows < 0 || d < 1 || h < 1) return MOE_ERR_INVALID_ARG;
+  if (act < MOE_RELU || act > MOE_SWIGLU) return MOE_ERR_INVALID_ARG;
+  if (dtype != MOE_F32 && dtype != MOE_BF16) return MOE_ERR_INVALID_ARG;
+  if (E > kMaxFfnExperts || d % 64 != 0 || h % 64 != 0) return MOE_ERR_UNSUPPORTED;
+  return MOE_OK;
+}
+
+size_t moe_expert_ffn_workspace_size(int32_t num_experts, int32_t max_rows, int32_t hidden,
+                                     int32_t ffn_hidden, int32_t act, int32_t dtype) {
+  if (check_ffn(num_experts, max_rows, hidden, ffn_hidden, act, dtype) != MOE_OK) return 0;
+  return moe::ffn_workspace_bytes(num_experts, max_rows, hidden, ffn_hidden, act, dtype);
+}
+
+int moe_expert_ffn(int32_t num_experts, int32_t max_rows, int32_t hidden, int32_t ffn_hidden,
+                   int32_t act, int32_t dtype, const void* x_rows,
+                   const int32_t* group_offsets, const void* w1, const void* w3,
+                   const void* w2, void* y_rows, void* ws, size_t ws_bytes, void* stream) {
+  int st = check_ffn(num_experts, max_rows, hidden, ffn_hidden, act, dtype);
+  if (st != MOE_OK) return st;
+  if (!group_offsets || !w1 || !w2) return MOE_ERR_INVALID_ARG;
+  if ((act == MOE_SWIGLU) != (w3 != nullptr)) return MOE_ERR_INVALID_ARG;
+  if (max_rows == 0) return MOE_OK;
+  if (!x_rows || !y_rows) return MOE_ERR_INVALID_ARG;
+  if (!aligned16(x_rows) || !aligned16(y_rows) || !aligned16(w1) || !aligned16(w2) ||
+      (w3 && !aligned16(w3)))
+    return MOE_ERR_INVALID_ARG;
+  const size_t need =
+      moe::ffn_workspace_bytes(num_experts, max_rows, hidden, ffn_hidden, act, dtype);
+  if (!ws || ws_bytes < need || (reinterpret_cast<uintptr_t>(ws) & 255u)) return MOE_ERR_WORKSPACE;
+  moe::FfnArgs a{num_experts, max_rows, hidden, ffn_hidden, act, dtype, x_rows,
+                 group_offsets, w1, w3, w2, y_rows, ws};
+  return status_of(moe::launch_ffn(a, static_cast<hipStream_t>(stream)));
+}
+
+int moe_combine(const moe_route_desc* desc, const void* y_perm, const int32_t* row_of_slot,
+                const float* topk_w, const void* residual, const void* shared_out, void* y,
+                void* stream) {
+  int st = check_desc(desc);
+  if (st != MOE_OK) return st;
+  const int N = desc->num_tokens;
+  if (N == 0) return MOE_OK;
+  if (!y_perm || !row_of_slot || !topk_w || !y) return MOE_ERR_INVALID_ARG;
+  if (!aligned16(y_perm) || !aligned16(y) || (residual && !aligned16(residual)) ||
+      (shared_out && !aligned16(shared_out)))
+    return MOE_ERR_INVALID_ARG;
+  moe::CombineArgs a{N, desc->hidden, desc->top_k, desc->dtype, y_perm, row_of_slot, topk_w,
+                     residual, shared_out, y};
+  return status_of(moe::launch_combine(a, static_cast<hipStream_t>(stream)));
+}
+
+int moe_bias_update(int32_t num_experts, int32_t num_tokens, int32_t top_k,
+                    const int32_t* counts, float step, float* sel_bias, void* stream) {
+  if (num_experts < 1 || num_tokens < 0 || top_k < 1 || !counts || !sel_bias)
+    return MOE_ERR_INVALID_ARG;
+  if (!isfinite(step)) return MOE_ERR_INVALID_ARG;
+  return status_of(moe::launch_bias_update(num_experts, num_tokens, top_k, counts, step,
+                                           sel_bias, static_cast<hipStream_t>(stream)));
+}
+
+}  // extern "C"

@@ -1,0 +1,71 @@
+// device.h -- small device helpers shared by the gfx950 kernels of the MoE
+// forward library (element conversion, wave reductions, vector types).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace moe {
+
+constexpr int kWave = 64;  // CDNA wavefront width
+
+typedef uint16_t bf16_t;  // raw bf16 bits
+
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));  // one 16-byte vector
+
+__device__ __forceinline__ float bf16_to_f32(uint32_t bits16) {
+  return __uint_as_float(bits16 << 16);
+}
+
+// fp32 -> bf16, round to nearest, ties to even; NaN stays a quiet NaN.
+__device__ __forceinline__ uint32_t f32_to_bf16(float f) {
+  uint32_t u = __float_as_uint(f);
+  if ((u & 0x7fffffffu) > 0x7f800000u) return ((u >> 16) | 0x40u) & 0xffffu;
+  u += 0x7fffu + ((u >> 16) & 1u);
+  return u >> 16;
+}
+
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  return f32_to_bf16(lo) | (f32_to_bf16(hi) << 16);
+}
+
+// Load element i of a dtype-tagged buffer as fp32 (dtype 0 fp32, 1 bf16).
+__device__ __forceinline__ float load_elem(const void* p, int dtype, size_t i) {
+  if (dtype == 0) return static_cast<const float*>(p)[i];
+  return bf16_to_f32(static_cast<const bf16_t*>(p)[i]);
+}
+
+__device__ __forceinline__ int lane_id() { return __lane_id(); }
+
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, kWave);
+  return v;
+}
+
+__device__ __forceinline__ double wave_sum(double v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, kWave);
+  return v;
+}
+
+__device__ __forceinline__ float wave_max(float v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, kWave));
+  return v;
+}
+
+// (score, index) pair ordered by score descending, index ascending.  Returns
+// the best pair over the wave in every lane.  Index -1 marks "no candidate".
+__device__ __forceinline__ void wave_argmax(float& s, int& idx) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) {
+    float so = __shfl_xor(s, o, kWave);
+    int io = __shfl_xor(idx, o, kWave);
+    bool take = (io >= 0) && (idx < 0 || so > s || (so == s && io < idx));
+    s = take ? so : s;
+    idx = take ? io : idx;
+  }
+}
+
+}  // namespace moe

@@ -1,0 +1,241 @@
+// dispatch.hip -- capacity, token-order admission and the expert/rank-
+// contiguous send-buffer layout, for gfx950.
+//
+// Glossary "Expert Parallelism": step 2 of "How tokens travel between GPUs"
+// (each token's hidden state goes to the rank holding its experts; experts sit
+// on ranks in blocks, e / (E/R), as in the routing snippet) and the capacity
+// bullet of "Load balancing and capacity" (an expert takes at most cap
+// assignments per batch, the rest skip it).  Admission is in token order, so
+// the rank of slot (t, j) inside expert e is the number of earlier slots (in
+// t-major, j-minor order) that chose e -- a stable counting sort.
+//
+// Kernels (slots are the N*k flattened (t, j) pairs, in tiles of 1024):
+//  tile_hist   per-tile, per-expert histogram (LDS atomics).
+//  scan        one block: per expert, exclusive prefix of the tile histograms
+//              (in place), admitted = min(count, cap), exclusive scan over
+//              experts -> expert offsets, rank offsets and counts.
+//  assign      per tile: per-wave histograms and their prefix give each wave
+//              its base; inside a wave, slots of one 64-slot chunk that chose
+//              the same expert are found with one ballot per expert-id bit,
+//              and a slot's rank is the popcount of the matching lanes below
+//              it.  Writes row_of_slot / token_of_row / slot_of_row.
+//  permute     token-major copy: one wave reads x[t] once (16-byte vectors)
+//              and writes it to each of its admitted rows.
+#include "device.h"
+#include "kernels.h"
+
+namespace moe {
+
+constexpr int kTileSlots = 1024;  // 4 waves x 4 chunks x 64 slots
+
+__global__ __launch_bounds__(256) void dispatch_tile_hist(const int32_t* __restrict__ topk_idx,
+                                                          int S, int E,
+                                                          int32_t* __restrict__ tile_counts) {
+  __shared__ int32_t hist[256];
+  for (int e = threadIdx.x; e < E; e += 256) hist[e] = 0;
+  __syncthreads();
+  const int s0 = blockIdx.x * kTileSlots;
+  const int s1 = min(S, s0 + kTileSlots);
+  for (int s = s0 + threadIdx.x; s < s1; s += 256) {
+    const int e = topk_idx[s];
+    if ((unsigned)e < (unsigned)E) atomicAdd(&hist[e], 1);  // ids out of range are ignored
+  }
+  __syncthreads();
+  for (int e = threadIdx.x; e < E; e += 256)
+    tile_counts[(size_t)blockIdx.x * E + e] = hist[e];
+}
+
+// One block of 256 threads; thread e owns expert e.
+__global__ __launch_bounds__(256) void dispatch_scan(int32_t* __restrict__ tile_counts,
+                                                     int num_tiles, int E, int R, int32_t cap,
+                                                     int32_t* __restrict__ expert_offsets,
+                                                     int32_t* __restrict__ admitted,
+                                                     int32_t* __restrict__ rank_offsets,
+                                                     int32_t* __restrict__ rank_counts) {
+  __shared__ int32_t scan[256];
+  __shared__ int32_t offs[257];
+  const int e = threadIdx.x;
+  int32_t run = 0;
+  if (e < E) {
+    for (int t = 0; t < num_tiles; ++t) {
+      const size_t q = (size_t)t * E + e;
+      const int32_t c = tile_counts[q];
+      tile_counts[q] = run;  // becomes the tile's base rank for expert e
+      run += c;
+    }
+  }
+  const int32_t adm = e < E ? min(run, cap) : 0;
+  if (e < E) admitted[e] = adm;
+  // Block-wide exclusive scan of adm (Hillis-Steele in LDS; 256 entries).
+  scan[e] = adm;
+  __syncthreads();
+  for (int o = 1; o < 256; o <<= 1) {
+    const int32_t v = e >= o ? scan[e - o] : 0;
+    __syncthreads();
+    scan[e] += v;
+    __syncthreads();
+  }
+  const int32_t excl = scan[e] - adm;
+  if (e < E) {
+    expert_offsets[e] = excl;
+    offs[e] = excl;
+  }
+  if (e == E - 1) {
+    expert_offsets[E] = scan[e];
+    offs[E] = scan[e];
+  }
+  __syncthreads();
+  const int per = E / R;
+  for (int r = threadIdx.x; r <= R; r += 256) rank_offsets[r] = offs[r * per];
+  for (int r = threadIdx.x; r < R; r += 256) rank_counts[r] = offs[(r + 1) * per] - offs[r * per];
+}
+
+__device__ __forceinline__ uint64_t lanemask_lt(int lane) {
+  return lane == 0 ? 0ull : (~0ull >> (64 - lane));
+}
+
+__global__ __launch_bounds__(256) void dispatch_assign(
+    const int32_t* __restrict__ topk_idx, int S, int k, int E, int32_t cap,
+    const int32_t* __restrict__ tile_base, const int32_t* __restrict__ expert_offsets,
+    int32_t* __restrict__ row_of_slot, int32_t* __restrict__ token_of_row,
+    int8_t* __restrict__ slot_of_row) {
+  __shared__ int32_t wcount[4][256];  // per-wave histogram, then per-wave running rank
+  __shared__ int32_t eoff[257];
+  const int wave = threadIdx.x / 64, lane = threadIdx.x % 64;
+  const int s0 = blockIdx.x * kTileSlots;
+
+  for (int q = threadIdx.x; q < 4 * 256; q += 256) (&wcount[0][0])[q] = 0;
+  for (int e = threadIdx.x; e <= E; e += 256) eoff[e] = expert_offsets[e];
+  __syncthreads();
+
+  const int ws0 = s0 + wave * 256;  // this wave's 256 slots
+  int my_e[4];
+#pragma unroll
+  for (int c = 0; c < 4; ++c) {
+    const int s = ws0 + c * 64 + lane;
+    int e = s < S ? topk_idx[s] : E;  // E = "no slot"
+    if ((unsigned)e >= (unsigned)E) e = E;  // an out-of-range id is treated as dropped
+    my_e[c] = e;
+    if (e < E) atomicAdd(&wcount[wave][e], 1);
+  }
+  __syncthreads();
+  // Turn per-wave counts into per-wave base ranks: tile base + earlier waves.
+  for (int e = threadIdx.x; e < E; e += 256) {
+    int32_t run = tile_base[(size_t)blockIdx.x * E + e];
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+      const int32_t c = wcount[w][e];
+      wcount[w][e] = run;
+      run += c;
+    }
+  }
+  __syncthreads();
+
+  // Bits needed to tell apart expert ids 0..E (E is the "no slot" id).
+  const int nbits = 32 - __clz(E);
+  const int32_t M = eoff[E];
+#pragma unroll
+  for (int c = 0; c < 4; ++c) {
+    const int s = ws0 + c * 64 + lane;
+    const int e = my_e[c];
+    uint64_t same = ~0ull;
+    for (int b = 0; b < nbits; ++b) {
+      const uint64_t bal = __ballot((e >> b) & 1);
+      same &= ((e >> b) & 1) ? bal : ~bal;
+    }
+    const int below = __popcll(same & lanemask_lt(lane));
+    const int leader = 63 - __clzll(same);  // highest lane with this expert
+    int32_t rank = 0;
+    if (e < E) rank = wcount[wave][e] + below;
+    __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    if (e < E && lane == leader) wcount[wave][e] += __popcll(same);
+    __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    if (e < E) {
+      if (rank < cap) {
+        const int32_t row = eoff[e] + rank;
+        row_of_slot[s] = row;
+        token_of_row[row] = s / k;
+        slot_of_row[row] = (int8_t)(s % k);
+      } else {
+        row_of_slot[s] = -1;
+      }
+    } else if (s < S) {
+      row_of_slot[s] = -1;
+    }
+  }
+  // Rows >= M (dropped capacity) are marked unused.
+  for (int r = s0 + threadIdx.x; r < min(S, s0 + kTileSlots); r += 256) {
+    if (r >= M) {
+      token_of_row[r] = -1;
+      slot_of_row[r] = -1;
+    }
+  }
+}
+
+// Token-major permute: one wave per token (grid-stride), 16-byte vectors.
+__global__ __launch_bounds__(256) void dispatch_permute(const u32x4* __restrict__ x, int N,
+                                                        int vec_per_row, int k,
+                                                        const int32_t* __restrict__ row_of_slot,
+                                                        u32x4* __restrict__ x_perm) {
+  const int lane = threadIdx.x % 64;
+  const int gw = blockIdx.x * 4 + threadIdx.x / 64;
+  const int nw = gridDim.x * 4;
+  for (int t = gw; t < N; t += nw) {
+    int my_row = lane < k ? row_of_slot[(size_t)t * k + lane] : -1;
+    int rows[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) rows[j] = __shfl(my_row, j, 64);
+    const u32x4* src = x + (size_t)t * vec_per_row;
+    for (int v0 = 0; v0 < vec_per_row; v0 += 64 * 4) {
+      u32x4 buf[4];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const int v = v0 + u * 64 + lane;
+        if (v < vec_per_row) buf[u] = src[v];
+      }
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        if (j < k && rows[j] >= 0) {
+          u32x4* dst = x_perm + (size_t)rows[j] * vec_per_row;
+#pragma unroll
+          for (int u = 0; u < 4; ++u) {
+            const int v = v0 + u * 64 + lane;
+            if (v < vec_per_row) dst[v] = buf[u];
+          }
+        }
+      }
+    }
+  }
+}
+
+size_t dispatch_workspace_bytes(int N, int k, int E) {
+  const size_t S = (size_t)N * k;
+  const size_t tiles = (S + kTileSlots - 1) / kTileSlots;
+  return std::max<size_t>(tiles, 1) * (size_t)E * sizeof(int32_t);
+}
+
+hipError_t launch_dispatch(const DispatchArgs& a, hipStream_t st) {
+  const int S = a.N * a.k;
+  const int tiles = (S + kTileSlots - 1) / kTileSlots;
+  int32_t* tile_counts = static_cast<int32_t*>(a.ws);
+  if (tiles > 0) {
+    dispatch_tile_hist<<<tiles, 256, 0, st>>>(a.topk_idx, S, a.E, tile_counts);
+  }
+  dispatch_scan<<<1, 256, 0, st>>>(tile_counts, tiles, a.E, a.R, a.cap, a.expert_offsets,
+                                   a.admitted, a.rank_offsets, a.rank_counts);
+  if (tiles == 0) return hipGetLastError();
+  dispatch_assign<<<tiles, 256, 0, st>>>(a.topk_idx, S, a.k, a.E, a.cap, tile_counts,
+                                         a.expert_offsets, a.row_of_slot, a.token_of_row,
+                                         a.slot_of_row);
+  const int elem = a.dtype == 0 ? 4 : 2;
+  const int vec_per_row = a.d * elem / 16;
+  const int waves_needed = a.N;
+  const int blocks = std::max(1, std::min((waves_needed + 3) / 4, 8192));
+  dispatch_permute<<<blocks, 256, 0, st>>>(static_cast<const u32x4*>(a.x), a.N, vec_per_row, a.k,
+                                           a.row_of_slot, static_cast<u32x4*>(a.x_perm));
+  return hipGetLastError();
+}
+
+}  // namespace moe

@@ -1,0 +1,78 @@
+// kernels.h -- launch interface between the C ABI (api.hip) and the kernels.
+// Host-side validation happens in api.hip; these functions assume valid,
+// already-checked arguments.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include <algorithm>
+
+namespace moe {
+
+struct RouteArgs {
+  int N, d, E, k, G, kg, score_fn, dtype;
+  const void* x;
+  const void* w_router;
+  const float* router_bias;
+  const float* sel_bias;
+  float* logits;
+  int32_t* topk_idx;
+  float* topk_w;
+  int32_t* counts;
+  void* ws;
+};
+
+size_t route_workspace_bytes(int N, int d, int E);
+hipError_t launch_route(const RouteArgs& a, hipStream_t st);
+
+struct DispatchArgs {
+  int N, d, E, k, R, dtype;
+  int32_t cap;  // INT32_MAX when unlimited
+  const void* x;
+  const int32_t* topk_idx;
+  void* x_perm;
+  int32_t* row_of_slot;
+  int32_t* token_of_row;
+  int8_t* slot_of_row;
+  int32_t* expert_offsets;
+  int32_t* admitted;
+  int32_t* rank_offsets;
+  int32_t* rank_counts;
+  void* ws;
+};
+
+size_t dispatch_workspace_bytes(int N, int k, int E);
+hipError_t launch_dispatch(const DispatchArgs& a, hipStream_t st);
+
+struct FfnArgs {
+  int E, max_rows, d, h, act, dtype;
+  const void* x_rows;
+  const int32_t* offsets;
+  const void* w1;
+  const void* w3;
+  const void* w2;
+  void* y_rows;
+  void* ws;
+};
+
+size_t ffn_workspace_bytes(int E, int max_rows, int d, int h, int act, int dtype);
+hipError_t launch_ffn(const FfnArgs& a, hipStream_t st);
+
+struct CombineArgs {
+  int N, d, k, dtype;
+  const void* y_perm;
+  const int32_t* row_of_slot;
+  const float* topk_w;
+  const void* residual;
+  const void* shared_out;
+  void* y;
+};
+
+hipError_t launch_combine(const CombineArgs& a, hipStream_t st);
+
+hipError_t launch_bias_update(int E, int N, int k, const int32_t* counts, float step,
+                              float* sel_bias, hipStream_t st);
+
+}  // namespace moe

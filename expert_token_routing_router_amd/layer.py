@@ -1,0 +1,96 @@
+"""The whole MoE-layer forward as a sequence of library calls.
+
+``MoeBuffers`` allocates (with torch) every output and workspace the five
+entry points need for one workload; ``moe_forward`` enqueues route ->
+dispatch -> expert FFN (+ shared expert) -> combine on one stream, with no
+host synchronisation.  No arithmetic happens here.
+"""
+
+from __future__ import annotations
+
+import torch
+
+from . import (ACT, DTYPE, TORCH_DTYPE, desc_from_workload, moe_bias_update, moe_combine,
+               moe_dispatch, moe_dispatch_workspace_size, moe_expert_ffn,
+               moe_expert_ffn_workspace_size, moe_route, moe_route_workspace_size, workspace)
+
+
+class MoeBuffers:
+    """Device buffers for one workload (N tokens, k slots, E experts, R ranks)."""
+
+    def __init__(self, cfg: dict, device="cuda", N: int | None = None, cf: float | None = None):
+        self.cfg = cfg
+        self.desc = desc_from_workload(cfg, N=N, cf=cf)
+        d = self.desc
+        N, E, k, R, dim = d.num_tokens, d.num_experts, d.top_k, d.num_ranks, d.hidden
+        S = N * k
+        dt = TORCH_DTYPE[d.dtype]
+        i32 = dict(dtype=torch.int32, device=device)
+        self.logits = torch.empty(N, E, dtype=torch.float32, device=device)
+        self.topk_idx = torch.empty(N, k, **i32)
+        self.topk_w = torch.empty(N, k, dtype=torch.float32, device=device)
+        self.counts = torch.empty(E, **i32)
+        self.ws_route = workspace(moe_route_workspace_size(d), device)
+        self.x_perm = torch.empty(max(S, 1), dim, dtype=dt, device=device)
+        self.row_of_slot = torch.empty(N, k, **i32)
+        self.token_of_row = torch.empty(max(S, 1), **i32)
+        self.slot_of_row = torch.empty(max(S, 1), dtype=torch.int8, device=device)
+        self.expert_offsets = torch.empty(E + 1, **i32)
+        self.admitted = torch.empty(E, **i32)
+        self.rank_offsets = torch.empty(R + 1, **i32)
+        self.rank_counts = torch.empty(R, **i32)
+        self.ws_dispatch = workspace(moe_dispatch_workspace_size(d), device)
+        self.y_perm = torch.empty(max(S, 1), dim, dtype=dt, device=device)
+        h = cfg["h"]
+        self.ws_ffn = workspace(moe_expert_ffn_workspace_size(E, S, dim, h, cfg["act"],
+                                                              cfg["dtype"]), device)
+        self.shared_out = None
+        if cfg.get("shared"):
+            self.shared_out = torch.empty(N, dim, dtype=dt, device=device)
+            self.shared_offsets = torch.tensor([0, N], **i32)
+            self.ws_shared = workspace(moe_expert_ffn_workspace_size(1, N, dim, h, cfg["act"],
+                                                                     cfg["dtype"]), device)
+        self.y = torch.empty(N, dim, dtype=dt, device=device)
+
+
+def route(buf: MoeBuffers, inp: dict, sel_bias=None, stream=None):
+    moe_route(buf.desc, inp["x"], inp["w_router"], inp.get("router_bias"),
+              inp.get("sel_bias") if sel_bias is None else sel_bias, buf.logits, buf.topk_idx,
+              buf.topk_w, buf.counts, buf.ws_route, stream)
+
+
+def dispatch(buf: MoeBuffers, inp: dict, stream=None):
+    moe_dispatch(buf.desc, inp["x"], buf.topk_idx, buf.x_perm, buf.row_of_slot,
+                 buf.token_of_row, buf.slot_of_row, buf.expert_offsets, buf.admitted,
+                 buf.rank_offsets, buf.rank_counts, buf.ws_dispatch, stream)
+
+
+def expert_ffn(buf: MoeBuffers, inp: dict, stream=None):
+    d, cfg = buf.desc, buf.cfg
+    S = d.num_tokens * d.top_k
+    moe_expert_ffn(d.num_experts, S, d.hidden, cfg["h"], cfg["act"], cfg["dtype"], buf.x_perm,
+                   buf.expert_offsets, inp["w1"], inp.get("w3"), inp["w2"], buf.y_perm,
+                   buf.ws_ffn, stream)
+    if buf.shared_out is not None and inp.get("shared") is not None:
+        sw1, sw3, sw2 = inp["shared"]
+        moe_expert_ffn(1, d.num_tokens, d.hidden, cfg["h"], cfg["act"], cfg["dtype"], inp["x"],
+                       buf.shared_offsets, sw1, sw3, sw2, buf.shared_out, buf.ws_shared, stream)
+
+
+def combine(buf: MoeBuffers, inp: dict, residual=True, stream=None):
+    moe_combine(buf.desc, buf.y_perm, buf.row_of_slot, buf.topk_w,
+                inp["x"] if residual else None, buf.shared_out, buf.y, stream)
+
+
+def bias_update(buf: MoeBuffers, sel_bias: torch.Tensor, step: float, stream=None):
+    d = buf.desc
+    moe_bias_update(d.num_experts, d.num_tokens, d.top_k, buf.counts, step, sel_bias, stream)
+
+
+def moe_forward(buf: MoeBuffers, inp: dict, residual=True, stream=None):
+    """route -> dispatch -> expert FFN (+ shared) -> combine, all enqueued."""
+    route(buf, inp, stream=stream)
+    dispatch(buf, inp, stream)
+    expert_ffn(buf, inp, stream)
+    combine(buf, inp, residual, stream)
+    return buf.y

@@ -1,0 +1,222 @@
+/*
+ * moe.h -- C ABI of the MI355X (gfx950) MoE-layer forward library.
+ *
+ * The single-GPU forward of a Mixture-of-Experts layer in the four steps the
+ * "Expert Parallelism" glossary page (Ultralytics; section "How tokens travel
+ * between GPUs") lists -- route, dispatch, compute, combine -- plus the
+ * selection-bias update of its "Load balancing and capacity" section:
+ *
+ *   moe_route        router logits, top-k selection (optional group limit and
+ *                    selection-only bias), combine weights, per-expert counts
+ *   moe_dispatch     capacity, token-order admission, expert- and
+ *                    rank-contiguous row layout, permuted hidden states
+ *   moe_expert_ffn   every expert's FFN over its rows as one grouped GEMM pair
+ *   moe_combine      weighted sum back to token order, plus residual and an
+ *                    optional shared-expert output
+ *   moe_bias_update  lower the selection bias of overloaded experts, raise it
+ *                    for underloaded ones
+ *
+ * Conventions (all entry points):
+ *  - Every tensor pointer is a DEVICE pointer owned by the caller; the library
+ *    never allocates device memory.  Scratch memory comes in through `ws`
+ *    (size from the matching *_workspace_size query, 256-byte aligned).
+ *  - `stream` is a hipStream_t (NULL = the null stream).  Work is enqueued
+ *    asynchronously; nothing synchronises the host.
+ *  - Arguments are validated on the host before any launch.  A call that
+ *    returns an error has enqueued nothing and written nothing.
+ *  - Layouts are row-major and dense.  Hidden-state buffers must be 16-byte
+ *    aligned.  dtype MOE_BF16 buffers hold bf16, MOE_F32 buffers fp32; routing
+ *    tensors (logits, weights, biases) are fp32 in both cases.
+ *  - Every call fully overwrites its outputs (counts included), so calls are
+ *    idempotent; calls on different streams with distinct buffers are
+ *    independent.
+ *  - Asynchronous device faults surface at the caller's next synchronisation.
+ *  - No C++ exception crosses this interface.
+ */
+#ifndef MOE_MI355X_H
+#define MOE_MI355X_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Status codes. */
+enum {
+  MOE_OK = 0,
+  MOE_ERR_INVALID_ARG = 1,    /* a size, pointer or enum is out of range */
+  MOE_ERR_UNSUPPORTED = 2,    /* valid, but outside what the kernels handle */
+  MOE_ERR_HIP = 3,            /* a HIP launch failed */
+  MOE_ERR_WORKSPACE = 4       /* ws is NULL or smaller than the query said */
+};
+
+/* Element types of hidden states and expert weights. */
+enum { MOE_F32 = 0, MOE_BF16 = 1 };
+
+/* How combine weights come from the router logits z (selection never uses
+ * these weights; it ranks z, or the sigmoid of z, plus the selection bias):
+ *  MOE_SOFTMAX_TOPK  softmax over the k selected logits (GShard/Mixtral top-2)
+ *  MOE_SOFTMAX_ALL   softmax over all E logits, taken at the selected experts,
+ *                    not renormalised (Switch top-1)
+ *  MOE_SIGMOID_NORM  sigmoid affinities, renormalised over the k selected
+ *                    (DeepSeek-V3); selection ranks sigmoid(z) + bias */
+enum { MOE_SOFTMAX_TOPK = 0, MOE_SOFTMAX_ALL = 1, MOE_SIGMOID_NORM = 2 };
+
+/* Expert activation: ReLU and GELU (exact erf) FFNs are act(x W1^T) W2^T;
+ * SwiGLU is (silu(x W1^T) * (x W3^T)) W2^T with W1 the gate, W3 the up. */
+enum { MOE_RELU = 0, MOE_GELU = 1, MOE_SWIGLU = 2 };
+
+/* The routing problem as the pages state it: tokens and their hidden states,
+ * number of experts, number of GPUs (here simulated EP ranks, expert e on rank
+ * e / (E/R), as in the glossary snippet), top-k, capacity factor (glossary
+ * "Load balancing and capacity"), and the node-limited group restriction
+ * (DeepSeek-V3: each token reaches experts on a bounded number of nodes). */
+typedef struct {
+  int32_t num_tokens;       /* N >= 0 */
+  int32_t hidden;           /* d >= 1, multiple of 8 */
+  int32_t num_experts;      /* E in [1, 256] */
+  int32_t top_k;            /* k in [1, min(E, 8)] */
+  int32_t num_ranks;        /* R >= 1, E % R == 0 */
+  float   capacity_factor;  /* <= 0: unlimited; else cap = ceil(cf * N * k / E) */
+  int32_t num_groups;       /* G >= 1, E % G == 0; 1 = no group limit */
+  int32_t topk_groups;      /* kg in [1, G], kg * (E/G) >= k */
+  int32_t score_fn;         /* MOE_SOFTMAX_TOPK / MOE_SOFTMAX_ALL / MOE_SIGMOID_NORM */
+  int32_t dtype;            /* MOE_F32 / MOE_BF16 */
+} moe_route_desc;
+
+/* ------------------------------------------------------------------ route -- */
+
+/* Workspace bytes moe_route needs (0 when N == 0). */
+size_t moe_route_workspace_size(const moe_route_desc* desc);
+
+/* Route.  Glossary "How tokens travel between GPUs", step 1: the router scores
+ * each token against each expert and keeps the k highest; "Load balancing and
+ * capacity": a per-expert bias added to the scores steers selection only.
+ *
+ *  x           [N, d]  dtype       hidden states
+ *  w_router    [E, d]  dtype       router weight (Linear(d, E).weight)
+ *  router_bias [E]     fp32        Linear bias, nullable
+ *  sel_bias    [E]     fp32        selection-only bias, nullable
+ *  logits      [N, E]  fp32  out   z[t,e] = fp32( fp64 sum over i = 0..d-1, in
+ *                                  order, of x[t,i]*w[e,i]; then + router_bias[e]
+ *                                  in fp64 ), rounded once to nearest-even
+ *  topk_idx    [N, k]  int32 out   chosen experts, best first; a token's
+ *                                  selection score is sigmoid(z) (SIGMOID_NORM,
+ *                                  fp64 then rounded to fp32) or z, plus
+ *                                  sel_bias in fp32; ties go to the lower index;
+ *                                  with G > 1 only experts in the kg groups with
+ *                                  the highest group score (max selection score
+ *                                  in the group; ties to the lower group) are
+ *                                  eligible
+ *  topk_w      [N, k]  fp32  out   combine weights (score_fn), from unbiased z
+ *  counts      [E]     int32 out   assignments per expert before capacity
+ *                                  (sum = N*k)
+ *  ws, ws_bytes                    workspace, >= moe_route_workspace_size */
+int moe_route(const moe_route_desc* desc, const void* x, const void* w_router,
+              const float* router_bias, const float* sel_bias, float* logits,
+              int32_t* topk_idx, float* topk_w, int32_t* counts,
+              void* ws, size_t ws_bytes, void* stream);
+
+/* --------------------------------------------------------------- dispatch -- */
+
+/* Workspace bytes moe_dispatch needs. */
+size_t moe_dispatch_workspace_size(const moe_route_desc* desc);
+
+/* Dispatch.  Glossary step 2 (the dispatch all-to-all sends each token's hidden
+ * state to the rank that holds its experts) and the capacity-factor bullet
+ * (each expert takes at most cap = ceil(cf*N*k/E) assignments per batch; the
+ * rest skip that expert).  Single-GPU form: the send buffer and its counts.
+ *
+ *  x              [N, d]    dtype  hidden states
+ *  topk_idx       [N, k]    int32  from moe_route (values in [0, E))
+ *  x_perm         [N*k, d]  dtype  out: rows 0..M-1 are the admitted
+ *                                  assignments grouped by expert in increasing
+ *                                  expert order, token order inside an expert;
+ *                                  x_perm[r] = x[token_of_row[r]] bit for bit.
+ *                                  Since rank = e / (E/R) is non-decreasing in
+ *                                  e, the buffer is also rank-contiguous.
+ *                                  Rows >= M are left untouched.
+ *  row_of_slot    [N, k]    int32  out: row of slot (t,j), -1 if dropped;
+ *                                  admission walks tokens in order
+ *  token_of_row   [N*k]     int32  out: token of each row (entries >= M: -1)
+ *  slot_of_row    [N*k]     int8   out: slot j of each row (entries >= M: -1)
+ *  expert_offsets [E+1]     int32  out: exclusive scan of admitted; [E] = M
+ *  admitted       [E]       int32  out: min(count_e, cap)
+ *  rank_offsets   [R+1]     int32  out: expert_offsets[r * E/R]
+ *  rank_counts    [R]       int32  out: rows per rank (the all-to-all's send
+ *                                  counts)
+ * Returns MOE_ERR_INVALID_ARG for bad sizes; out-of-range expert ids in
+ * topk_idx are a caller error the kernels do not detect. */
+int moe_dispatch(const moe_route_desc* desc, const void* x, const int32_t* topk_idx,
+                 void* x_perm, int32_t* row_of_slot, int32_t* token_of_row,
+                 int8_t* slot_of_row, int32_t* expert_offsets, int32_t* admitted,
+                 int32_t* rank_offsets, int32_t* rank_counts,
+                 void* ws, size_t ws_bytes, void* stream);
+
+/* ------------------------------------------------------------- expert FFN -- */
+
+/* Workspace bytes moe_expert_ffn needs for up to max_rows rows. */
+size_t moe_expert_ffn_workspace_size(int32_t num_experts, int32_t max_rows, int32_t hidden,
+                                     int32_t ffn_hidden, int32_t act, int32_t dtype);
+
+/* Expert FFN.  Glossary step 3 (each GPU runs its local experts on the tokens
+ * it received); each expert is an ordinary FFN.  Rows [offsets[e],
+ * offsets[e+1]) of x_rows go through expert e:
+ *   H = act(X W1_e^T) (SwiGLU: silu(X W1_e^T) * (X W3_e^T)), stored in dtype;
+ *   Y = H W2_e^T, stored in dtype.  fp32 accumulation.
+ *
+ *  num_experts   E >= 1 (1 with offsets {0, N} runs a shared expert)
+ *  max_rows      rows allocated in x_rows / y_rows (offsets[E] <= max_rows)
+ *  hidden        d, multiple of 64;  ffn_hidden  h, multiple of 64
+ *  x_rows        [max_rows, d]  dtype
+ *  group_offsets [E+1]  int32  DEVICE array, non-decreasing, [0] = 0
+ *  w1            [E, h, d]  dtype  (gate for SwiGLU)
+ *  w3            [E, h, d]  dtype  (up; SwiGLU only, else NULL)
+ *  w2            [E, d, h]  dtype
+ *  y_rows        [max_rows, d]  dtype out (rows >= offsets[E] untouched)
+ *  ws, ws_bytes  workspace >= moe_expert_ffn_workspace_size(...) */
+int moe_expert_ffn(int32_t num_experts, int32_t max_rows, int32_t hidden, int32_t ffn_hidden,
+                   int32_t act, int32_t dtype, const void* x_rows,
+                   const int32_t* group_offsets, const void* w1, const void* w3,
+                   const void* w2, void* y_rows, void* ws, size_t ws_bytes, void* stream);
+
+/* ---------------------------------------------------------------- combine -- */
+
+/* Combine.  Glossary step 4 (outputs return to each token and are weighted by
+ * the router scores and summed) and "Load balancing and capacity" (a skipped
+ * token passes through the residual connection unchanged):
+ *   y[t] = residual[t] + shared_out[t] + sum_j [row_of_slot[t,j] >= 0] *
+ *          topk_w[t,j] * y_perm[row_of_slot[t,j]]
+ * accumulated in fp32 in that order and rounded once to dtype.
+ *
+ *  y_perm      [>=M, d]  dtype   expert outputs by row
+ *  row_of_slot [N, k]    int32   from moe_dispatch
+ *  topk_w      [N, k]    fp32    from moe_route
+ *  residual    [N, d]    dtype   nullable (normally x)
+ *  shared_out  [N, d]    dtype   nullable (always-on shared expert output)
+ *  y           [N, d]    dtype   out */
+int moe_combine(const moe_route_desc* desc, const void* y_perm, const int32_t* row_of_slot,
+                const float* topk_w, const void* residual, const void* shared_out,
+                void* y, void* stream);
+
+/* ------------------------------------------------------------ bias update -- */
+
+/* Selection-bias update.  Glossary "Load balancing and capacity", bias-based
+ * balancing: after each step the bias of overloaded experts goes down and that
+ * of idle ones goes up.  In place, for each e:
+ *   counts[e]*E > N*k  ->  sel_bias[e] -= step   (fp32)
+ *   counts[e]*E < N*k  ->  sel_bias[e] += step
+ *   equal              ->  unchanged
+ *  counts [E] int32 (pre-capacity, from moe_route), sel_bias [E] fp32. */
+int moe_bias_update(int32_t num_experts, int32_t num_tokens, int32_t top_k,
+                    const int32_t* counts, float step, float* sel_bias, void* stream);
+
+/* Human-readable name of a status code (static storage). */
+const char* moe_status_string(int status);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* MOE_MI355X_H */

@@ -1,0 +1,154 @@
+"""The C-ABI library loads on the CPU, exports every entry point include/moe.h
+declares, and rejects invalid arguments before touching a device.  No compute
+call is made here (there is no GPU in this environment)."""
+
+import ctypes
+import os
+import re
+
+import pytest
+
+import expert_token_routing_router_amd as moe
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "moe.h")
+
+FAKE = ctypes.c_void_p(0x10000)  # aligned, never dereferenced (validation fails first)
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(moe_[a-z_]+)\s*\(", text)))
+
+
+def test_header_declares_the_boundary():
+    names = declared_functions()
+    for want in ["moe_route", "moe_dispatch", "moe_expert_ffn", "moe_combine",
+                 "moe_bias_update"]:
+        assert want in names
+
+
+def test_library_exports_every_declared_symbol():
+    lib = moe.lib()
+    missing = [n for n in declared_functions() if not hasattr(lib, n)]
+    assert not missing, missing
+    assert sorted(moe.EXPORTS) == declared_functions()
+
+
+def test_status_strings():
+    assert moe.status_string(moe.MOE_OK) == "ok"
+    assert "invalid" in moe.status_string(moe.MOE_ERR_INVALID_ARG)
+    assert "workspace" in moe.status_string(moe.MOE_ERR_WORKSPACE)
+    assert moe.status_string(99) == "unknown status"
+
+
+def _route(desc, ws_bytes=0, ptrs=True, counts=True):
+    lib = moe.lib()
+    p = FAKE if ptrs else None
+    return lib.moe_route(ctypes.byref(desc), p, p, None, None, p, p, p, FAKE if counts else None,
+                         FAKE if ws_bytes else None, ws_bytes, None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(k=9), moe.MOE_ERR_INVALID_ARG),               # k > E
+    (dict(R=3), moe.MOE_ERR_INVALID_ARG),               # E % R != 0
+    (dict(G=3), moe.MOE_ERR_INVALID_ARG),               # E % G != 0
+    (dict(G=2, kg=3), moe.MOE_ERR_INVALID_ARG),         # kg > G
+    (dict(E=16, G=8, kg=1, k=3), moe.MOE_ERR_INVALID_ARG),  # kg * E/G < k
+    (dict(N=-1), moe.MOE_ERR_INVALID_ARG),
+    (dict(d=0), moe.MOE_ERR_INVALID_ARG),
+    (dict(d=12), moe.MOE_ERR_UNSUPPORTED),              # hidden not a multiple of 8
+    (dict(E=512, k=2), moe.MOE_ERR_UNSUPPORTED),        # more than 256 experts
+    (dict(E=16, k=9), moe.MOE_ERR_UNSUPPORTED),         # k > 8
+    (dict(E=128, G=128, kg=2), moe.MOE_ERR_UNSUPPORTED),      # more than 64 groups
+    (dict(cf=float("nan")), moe.MOE_ERR_INVALID_ARG),
+])
+def test_route_rejects_bad_descriptors(kw, status):
+    base = dict(N=64, d=64, E=8, k=2, R=4, cf=0.0, G=1, kg=1)
+    base.update(kw)
+    desc = moe.route_desc(base["N"], base["d"], base["E"], base["k"], base["R"], base["cf"],
+                          base["G"], base["kg"])
+    assert _route(desc, ws_bytes=1 << 20) == status
+
+
+def test_route_bad_score_and_dtype():
+    d = moe.route_desc(64, 64, 8, 2)
+    d.score_fn = 7
+    assert _route(d, 1 << 20) == moe.MOE_ERR_INVALID_ARG
+    d = moe.route_desc(64, 64, 8, 2)
+    d.dtype = 5
+    assert _route(d, 1 << 20) == moe.MOE_ERR_INVALID_ARG
+
+
+def test_route_null_pointers_and_workspace():
+    d = moe.route_desc(64, 64, 8, 2)
+    assert _route(d, 1 << 20, ptrs=False) == moe.MOE_ERR_INVALID_ARG
+    assert _route(d, 1 << 20, counts=False) == moe.MOE_ERR_INVALID_ARG
+    need = moe.moe_route_workspace_size(d)
+    assert need > 0
+    assert _route(d, 0) == moe.MOE_ERR_WORKSPACE
+    assert _route(d, need - 8) == moe.MOE_ERR_WORKSPACE
+
+
+def test_route_misaligned_hidden_states():
+    lib = moe.lib()
+    d = moe.route_desc(64, 64, 8, 2)
+    odd = ctypes.c_void_p(0x10002)
+    st = lib.moe_route(ctypes.byref(d), odd, FAKE, None, None, FAKE, FAKE, FAKE, FAKE, FAKE,
+                       1 << 20, None)
+    assert st == moe.MOE_ERR_INVALID_ARG
+
+
+def test_dispatch_validation():
+    lib = moe.lib()
+    d = moe.route_desc(64, 64, 8, 2, R=4, cf=1.25)
+    need = moe.moe_dispatch_workspace_size(d)
+    assert need >= 8 * 4
+    args = [FAKE] * 10
+    assert lib.moe_dispatch(ctypes.byref(d), *args, None, 0, None) == moe.MOE_ERR_WORKSPACE
+    assert lib.moe_dispatch(ctypes.byref(d), *args, FAKE, need - 4, None) == moe.MOE_ERR_WORKSPACE
+    args2 = list(args)
+    args2[2] = None  # x_perm
+    assert lib.moe_dispatch(ctypes.byref(d), *args2, FAKE, need, None) == moe.MOE_ERR_INVALID_ARG
+    bad = moe.route_desc(64, 64, 8, 2, R=3)
+    assert lib.moe_dispatch(ctypes.byref(bad), *args, FAKE, need, None) == moe.MOE_ERR_INVALID_ARG
+
+
+def test_expert_ffn_validation():
+    lib = moe.lib()
+    F = FAKE
+    call = lambda E, M, d, h, act, dt, w3=None, ws=F, wsb=1 << 30: lib.moe_expert_ffn(  # noqa: E731
+        E, M, d, h, act, dt, F, F, F, w3, F, F, ws, wsb, None)
+    assert call(0, 100, 64, 64, moe.MOE_RELU, moe.MOE_BF16) == moe.MOE_ERR_INVALID_ARG
+    assert call(8, -1, 64, 64, moe.MOE_RELU, moe.MOE_BF16) == moe.MOE_ERR_INVALID_ARG
+    assert call(8, 100, 96, 64, moe.MOE_RELU, moe.MOE_BF16) == moe.MOE_ERR_UNSUPPORTED
+    assert call(8, 100, 64, 100, moe.MOE_RELU, moe.MOE_BF16) == moe.MOE_ERR_UNSUPPORTED
+    assert call(8, 100, 64, 64, 5, moe.MOE_BF16) == moe.MOE_ERR_INVALID_ARG
+    assert call(8, 100, 64, 64, moe.MOE_SWIGLU, moe.MOE_BF16) == moe.MOE_ERR_INVALID_ARG  # no w3
+    assert call(8, 100, 64, 64, moe.MOE_RELU, moe.MOE_BF16, w3=F) == moe.MOE_ERR_INVALID_ARG
+    assert call(8, 100, 64, 64, moe.MOE_RELU, moe.MOE_BF16, ws=None) == moe.MOE_ERR_WORKSPACE
+    need = moe.moe_expert_ffn_workspace_size(8, 100, 64, 64, "relu", "bf16")
+    assert call(8, 100, 64, 64, moe.MOE_RELU, moe.MOE_BF16, wsb=need - 1) == moe.MOE_ERR_WORKSPACE
+    assert call(8, 0, 64, 64, moe.MOE_RELU, moe.MOE_BF16) == moe.MOE_OK  # nothing to do
+
+
+def test_combine_and_bias_validation():
+    lib = moe.lib()
+    d = moe.route_desc(64, 64, 8, 2)
+    assert lib.moe_combine(ctypes.byref(d), None, FAKE, FAKE, None, None, FAKE, None) == \
+        moe.MOE_ERR_INVALID_ARG
+    assert lib.moe_combine(ctypes.byref(moe.route_desc(0, 64, 8, 2)), None, None, None, None,
+                           None, None, None) == moe.MOE_OK
+    assert lib.moe_bias_update(0, 10, 1, FAKE, 1e-3, FAKE, None) == moe.MOE_ERR_INVALID_ARG
+    assert lib.moe_bias_update(8, 10, 1, None, 1e-3, FAKE, None) == moe.MOE_ERR_INVALID_ARG
+    assert lib.moe_bias_update(8, 10, 1, FAKE, float("inf"), FAKE, None) == \
+        moe.MOE_ERR_INVALID_ARG
+
+
+def test_binding_requires_device_tensors():
+    import torch
+    desc = moe.route_desc(4, 64, 8, 2)
+    x = torch.zeros(4, 64, dtype=torch.bfloat16)
+    with pytest.raises(ValueError):
+        moe.moe_route(desc, x, x, None, None, None, None, None, None, None)

@@ -1,0 +1,268 @@
+"""GPU parity: every entry point of the HIP library against the CPU oracle on
+the same seeded inputs.  Integer outputs, logits and the permuted rows are
+compared bit for bit; floating outputs with the per-tensor max relative error
+(fp32 1e-4, bf16 2e-2; combine weights 1e-5 absolute).
+
+Workloads: the reduced version of every workload family (ragged N, several
+tiles per expert, N tiles not a multiple of the GEMM tile), the glossary
+snippet's own fp32 workload at full size, and edge cases.
+"""
+
+import numpy as np
+import pytest
+import torch
+
+import expert_token_routing_router_amd as moe
+from expert_token_routing_router_amd import layer
+import moe_workloads as W
+import oracle
+
+from gpu_util import TOL, TOPK_W_TOL, as_tensor, bits, n, oracle_reference, rel_err, to_dev
+
+pytestmark = pytest.mark.gpu
+
+CASES = {
+    "toy-full": W.full("toy"),
+    "toy-small": W.small("toy"),
+    "switch-small": W.small("switch"),
+    "mixtral-small": W.small("mixtral"),
+    "deepseek-small": W.small("deepseek"),
+    "zipf-small-cf1.0": W.with_(W.small("zipf"), cf=1.0),
+    "zipf-small-cf1.25": W.with_(W.small("zipf"), cf=1.25),
+    "zipf-small-cf2.0": W.with_(W.small("zipf"), cf=2.0),
+}
+
+_cache = {}
+
+
+def run_case(name):
+    if name in _cache:
+        return _cache[name]
+    cfg = CASES[name]
+    print(f"[case {name}] N={cfg['N']} d={cfg['d']} h={cfg['h']} E={cfg['E']} k={cfg['k']}",
+          flush=True)
+    inp_cpu = W.make_inputs(cfg)
+    inp = to_dev(inp_cpu)
+    buf = moe.MoeBuffers(cfg)
+    layer.route(buf, inp)
+    layer.dispatch(buf, inp)
+    layer.expert_ffn(buf, inp)
+    layer.combine(buf, inp, residual=True)
+    torch.cuda.synchronize()
+    gpu = {k: getattr(buf, k).detach().cpu().clone() for k in
+           ["logits", "topk_idx", "topk_w", "counts", "row_of_slot", "token_of_row",
+            "slot_of_row", "expert_offsets", "admitted", "rank_offsets", "rank_counts",
+            "x_perm", "y_perm", "y"]}
+    if buf.shared_out is not None:
+        gpu["shared_out"] = buf.shared_out.cpu().clone()
+    # Branch alone (no residual): the residual cannot hide FFN error.
+    layer.combine(buf, inp, residual=False)
+    torch.cuda.synchronize()
+    gpu["y_branch"] = buf.y.cpu().clone()
+    ref = oracle_reference(cfg, inp_cpu)
+    shared_ref = ref["shared_out"]
+    ref["y_branch"] = oracle.combine(cfg["dtype"], ref["y_perm"], ref["row_of_slot"],
+                                     ref["topk_w"], None, shared_ref)
+    _cache[name] = (cfg, inp_cpu, gpu, ref)
+    return _cache[name]
+
+
+@pytest.mark.parametrize("name", list(CASES))
+def test_route_bit_exact(name):
+    cfg, _, gpu, ref = run_case(name)
+    assert np.array_equal(bits(gpu["logits"]), ref["logits"].view(np.int32)), "logits differ"
+    assert np.array_equal(gpu["topk_idx"].numpy(), ref["topk_idx"])
+    assert np.array_equal(gpu["counts"].numpy(), ref["counts"])
+    assert gpu["counts"].sum().item() == cfg["N"] * cfg["k"]
+    assert np.abs(gpu["topk_w"].numpy() - ref["topk_w"]).max() <= TOPK_W_TOL
+
+
+@pytest.mark.parametrize("name", list(CASES))
+def test_dispatch_bit_exact(name):
+    cfg, inp_cpu, gpu, ref = run_case(name)
+    M = ref["num_rows"]
+    for key in ["row_of_slot", "expert_offsets", "admitted", "rank_offsets", "rank_counts"]:
+        assert np.array_equal(gpu[key].numpy(), ref[key]), key
+    assert np.array_equal(gpu["token_of_row"].numpy(), ref["token_of_row"])
+    assert np.array_equal(gpu["slot_of_row"].numpy(), ref["slot_of_row"])
+    assert np.array_equal(bits(gpu["x_perm"][:M]), bits(as_tensor(ref["x_perm"], cfg["dtype"])))
+
+
+@pytest.mark.parametrize("name", list(CASES))
+def test_expert_ffn_within_tolerance(name):
+    cfg, _, gpu, ref = run_case(name)
+    M = ref["num_rows"]
+    err = rel_err(gpu["y_perm"][:M], as_tensor(ref["y_perm"], cfg["dtype"]))
+    assert err <= TOL[cfg["dtype"]], f"y_perm max rel err {err:.3e}"
+    if ref["shared_out"] is not None:
+        err = rel_err(gpu["shared_out"], as_tensor(ref["shared_out"], cfg["dtype"]))
+        assert err <= TOL[cfg["dtype"]], f"shared_out max rel err {err:.3e}"
+
+
+@pytest.mark.parametrize("name", list(CASES))
+def test_combine_within_tolerance(name):
+    cfg, inp_cpu, gpu, ref = run_case(name)
+    err = rel_err(gpu["y_branch"], as_tensor(ref["y_branch"], cfg["dtype"]))
+    assert err <= TOL[cfg["dtype"]], f"branch-only y max rel err {err:.3e}"
+    err = rel_err(gpu["y"], as_tensor(ref["y"], cfg["dtype"]))
+    assert err <= TOL[cfg["dtype"]], f"y max rel err {err:.3e}"
+    dropped = np.all(ref["row_of_slot"] < 0, axis=1)
+    if dropped.any() and ref["shared_out"] is None:
+        d = torch.from_numpy(dropped)
+        assert torch.equal(gpu["y"][d], inp_cpu["x"][d]), "dropped tokens must pass unchanged"
+
+
+def test_zipf_bias_update_and_reroute():
+    """route -> bias update -> route: updated bias bitwise equal to the oracle's,
+    and the second routing (with the new bias) bit-exact; the update changes
+    some selections."""
+    cfg = W.small("zipf")
+    inp_cpu = W.make_inputs(cfg, weights=False)
+    inp = to_dev(inp_cpu)
+    buf = moe.MoeBuffers(cfg)
+    layer.route(buf, inp)
+    sel = inp["sel_bias"].clone()
+    layer.bias_update(buf, sel, cfg["bias_step"])
+    first = buf.topk_idx.cpu().clone()
+    layer.route(buf, inp, sel_bias=sel)
+    torch.cuda.synchronize()
+    oracle.set_threads(16)
+    r1 = oracle.route(cfg, n(inp_cpu["x"]), n(inp_cpu["w_router"]), n(inp_cpu["router_bias"]),
+                      n(inp_cpu["sel_bias"]))
+    b = oracle.bias_update(cfg["N"], cfg["k"], r1["counts"], n(inp_cpu["sel_bias"]), cfg["bias_step"])
+    assert np.array_equal(bits(sel.cpu()), b.view(np.int32))
+    r2 = oracle.select(cfg, r1["logits"], b)
+    assert np.array_equal(buf.topk_idx.cpu().numpy(), r2["topk_idx"])
+    assert np.array_equal(buf.counts.cpu().numpy(), r2["counts"])
+    assert not torch.equal(first, buf.topk_idx.cpu())
+
+
+def test_integer_outputs_deterministic():
+    """Two runs of route + dispatch give bitwise identical integer outputs."""
+    cfg = W.small("zipf")
+    inp = to_dev(W.make_inputs(cfg, weights=False))
+    outs = []
+    for _ in range(2):
+        buf = moe.MoeBuffers(cfg)
+        layer.route(buf, inp)
+        layer.dispatch(buf, inp)
+        torch.cuda.synchronize()
+        outs.append([getattr(buf, k).cpu() for k in
+                     ["topk_idx", "counts", "row_of_slot", "token_of_row", "slot_of_row",
+                      "expert_offsets"]])
+    for a, b in zip(*outs):
+        assert torch.equal(a, b)
+
+
+# ------------------------------------------------------------------ edges ---
+
+def _route_dispatch(cfg, inp_cpu, sel_bias=None):
+    inp = to_dev(inp_cpu)
+    buf = moe.MoeBuffers(cfg)
+    sb = None if sel_bias is None else sel_bias.cuda()
+    layer.route(buf, inp, sel_bias=sb)
+    layer.dispatch(buf, inp)
+    torch.cuda.synchronize()
+    return buf
+
+
+def test_empty_batch():
+    cfg = W.with_(W.small("switch"), N=0)
+    inp_cpu = W.make_inputs(W.small("switch"), weights=False)
+    inp_cpu["x"] = inp_cpu["x"][:0]
+    buf = _route_dispatch(cfg, inp_cpu)
+    assert buf.counts.sum().item() == 0
+    assert buf.expert_offsets.abs().sum().item() == 0
+    assert buf.rank_counts.abs().sum().item() == 0
+
+
+@pytest.mark.parametrize("N", [1, 63, 64, 65, 1023, 1025])
+def test_ragged_token_counts(N):
+    base = W.small("deepseek")
+    cfg = W.with_(base, N=N)
+    inp_cpu = W.make_inputs(cfg, weights=False)
+    buf = _route_dispatch(cfg, inp_cpu)
+    r = oracle.route(cfg, n(inp_cpu["x"]), n(inp_cpu["w_router"]), None, n(inp_cpu["sel_bias"]))
+    dsp = oracle.dispatch(cfg, r["topk_idx"])
+    assert np.array_equal(buf.topk_idx.cpu().numpy(), r["topk_idx"])
+    assert np.array_equal(buf.row_of_slot.cpu().numpy(), dsp["row_of_slot"])
+    assert np.array_equal(buf.token_of_row.cpu().numpy(), dsp["token_of_row"])
+
+
+def test_all_tokens_to_one_expert_with_capacity():
+    """A huge selection bias sends every token to expert 3; capacity 1.25
+    admits the first cap tokens; every other token leaves the layer unchanged."""
+    cfg = W.small("switch")
+    inp_cpu = W.make_inputs(cfg)
+    sb = torch.zeros(cfg["E"], dtype=torch.float32)
+    sb[3] = 1e4
+    inp_cpu["sel_bias"] = sb
+    inp = to_dev(inp_cpu)
+    buf = moe.MoeBuffers(cfg)
+    moe.moe_forward(buf, inp)
+    torch.cuda.synchronize()
+    cap = oracle.capacity(cfg)
+    assert buf.counts[3].item() == cfg["N"]
+    assert buf.admitted[3].item() == cap
+    ros = buf.row_of_slot.cpu().numpy()[:, 0]
+    assert np.array_equal(ros[:cap], np.arange(cap)) and np.all(ros[cap:] == -1)
+    assert torch.equal(buf.y.cpu()[cap:], inp_cpu["x"][cap:])
+    ref = oracle_reference(cfg, inp_cpu)
+    assert rel_err(buf.y, as_tensor(ref["y"], "bf16")) <= TOL["bf16"]
+
+
+def test_capacity_one():
+    cfg = W.with_(W.small("zipf"), cf=1e-9)
+    inp_cpu = W.make_inputs(cfg, weights=False)
+    buf = _route_dispatch(cfg, inp_cpu)
+    r = oracle.route(cfg, n(inp_cpu["x"]), n(inp_cpu["w_router"]), n(inp_cpu["router_bias"]),
+                     n(inp_cpu["sel_bias"]))
+    dsp = oracle.dispatch(cfg, r["topk_idx"])
+    assert oracle.capacity(cfg) == 1
+    assert np.array_equal(buf.row_of_slot.cpu().numpy(), dsp["row_of_slot"])
+    assert np.array_equal(buf.admitted.cpu().numpy(), dsp["admitted"])
+
+
+def test_single_expert_layer():
+    """E = 1, k = 1: y = x + FFN(x)."""
+    cfg = dict(name="single", size="small", N=300, d=128, h=192, E=1, k=1, R=1, cf=0.0, G=1,
+               kg=1, score="softmax_topk", act="swiglu", dtype="bf16", router_bias=None,
+               sel_bias=None, shared=False, zipf=None)
+    inp_cpu = W.make_inputs(cfg)
+    inp = to_dev(inp_cpu)
+    buf = moe.MoeBuffers(cfg)
+    moe.moe_forward(buf, inp)
+    torch.cuda.synchronize()
+    ref = oracle_reference(cfg, inp_cpu)
+    assert np.all(buf.topk_w.cpu().numpy() == 1.0)
+    assert rel_err(buf.y, as_tensor(ref["y"], "bf16")) <= TOL["bf16"]
+
+
+def test_topk_equals_num_experts():
+    cfg = W.with_(W.small("mixtral"), k=8, N=257)
+    inp_cpu = W.make_inputs(cfg)
+    inp = to_dev(inp_cpu)
+    buf = moe.MoeBuffers(cfg)
+    moe.moe_forward(buf, inp)
+    torch.cuda.synchronize()
+    ref = oracle_reference(cfg, inp_cpu)
+    assert np.array_equal(buf.topk_idx.cpu().numpy(), ref["topk_idx"])
+    assert rel_err(buf.y, as_tensor(ref["y"], "bf16")) <= TOL["bf16"]
+
+
+def test_invalid_arguments_enqueue_nothing():
+    cfg = W.small("switch")
+    inp = to_dev(W.make_inputs(cfg, weights=False))
+    buf = moe.MoeBuffers(cfg)
+    buf.counts.fill_(-7)
+    bad = moe.route_desc(cfg["N"], cfg["d"], cfg["E"], cfg["E"] + 1)
+    with pytest.raises(moe.MoeError) as ei:
+        moe.moe_route(bad, inp["x"], inp["w_router"], None, None, buf.logits, buf.topk_idx,
+                      buf.topk_w, buf.counts, buf.ws_route)
+    assert ei.value.status == moe.MOE_ERR_INVALID_ARG
+    with pytest.raises(moe.MoeError) as ei:
+        moe.moe_route(buf.desc, inp["x"], inp["w_router"], None, None, buf.logits, buf.topk_idx,
+                      buf.topk_w, buf.counts, buf.ws_route[:16])
+    assert ei.value.status == moe.MOE_ERR_WORKSPACE
+    torch.cuda.synchronize()
+    assert torch.all(buf.counts.cpu() == -7)
