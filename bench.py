@@ -1,0 +1,322 @@
+#!/usr/bin/env python3
+"""MoE-layer forward throughput on one MI355X.
+
+One step is one pass of the whole hot path over one batch of synthetic input,
+already resident in HBM: route -> dispatch -> expert FFN (plan, up, down; plus
+the shared expert where the workload has one) -> combine -> selection-bias
+update.  Default workload: Switch-style top-1, N=16384 tokens, d=1024, 64
+experts, softmax over all 64, capacity factor 1.25 (cap 320, token-order
+admission), GELU experts 1024->4096->1024, 8 simulated EP ranks, bf16.
+
+Prints one JSON line.  Every library call inside the timed region is bracketed
+by HIP events on the stream it is launched on; the per-call averages give the
+roofline of the dominant kernel and the per-step breakdown.  The CPU oracle is
+timed on a bounded sample of the same workload (``cpu_baseline``).
+"""
+
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "MoE layer tokens/sec at 1 GPU; grouped-GEMM % MFMA peak; permute % HBM BW"
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, published
+MFMA_PEAK_TFLOPS = {"bf16": 2500.0, "fp32": 157.3}  # dense, published
+PROFILE_DIR = os.path.join(ROOT, "profiles")
+
+
+def parse_args():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="switch",
+                    choices=["toy", "switch", "mixtral", "deepseek", "zipf"])
+    ap.add_argument("--cf", type=float, default=None, help="override the capacity factor")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=15.0,
+                    help="target length of the oracle's timed sample")
+    ap.add_argument("--copy-calibration-mib", type=int, default=0,
+                    help="also run one device copy of this size (counter calibration)")
+    return ap.parse_args()
+
+
+def kernel_sources_digest() -> str:
+    """Digest of the HIP sources the measured kernels are built from."""
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "expert_token_routing_router_amd", "csrc")
+    for name in sorted(os.listdir(csrc)):
+        with open(os.path.join(csrc, name), "rb") as f:
+            h.update(name.encode())
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def read_traffic(kernel: str, workload: str, digest: str):
+    """HBM bytes per launch from the committed counter summary, or None if it is
+    missing or was taken from different kernel sources."""
+    path = os.path.join(PROFILE_DIR, f"{kernel}_{workload}_pmc.txt")
+    if not os.path.exists(path):
+        return None
+    vals = {}
+    with open(path) as f:
+        for line in f:
+            if ":" in line and not line.startswith("#"):
+                k, v = line.split(":", 1)
+                vals[k.strip()] = v.strip()
+    if vals.get("kernel_sources_digest") != digest:
+        return None
+    try:
+        return float(vals["hbm_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
+
+
+def describe(cfg) -> str:
+    s = (f"{cfg['name']} N={cfg['N']} d={cfg['d']} h={cfg['h']} E={cfg['E']} k={cfg['k']} "
+         f"score={cfg['score']} act={cfg['act']} R={cfg['R']}")
+    if cfg.get("cf"):
+        s += f" cf={cfg['cf']}"
+    if cfg.get("G", 1) > 1:
+        s += f" groups={cfg['G']}/keep{cfg['kg']}"
+    if cfg.get("shared"):
+        s += " +shared"
+    return s
+
+
+def cpu_baseline(cfg, inp, target_s: float) -> dict:
+    """Time the oracle (as it stands) on the first T tokens of the workload,
+    taken as a batch of T (capacity recomputed for T): route, dispatch, FFN,
+    combine and bias update.  T is chosen so the run lasts about target_s."""
+    import numpy as np
+
+    import moe_workloads as W
+    import oracle
+
+    threads = max(1, min(16, os.cpu_count() or 1))
+    oracle.set_threads(threads)
+    n = W.to_numpy
+    wr, rb = n(inp["w_router"]), n(inp["router_bias"])
+    sb = n(inp["sel_bias"])
+    bias_state = sb if sb is not None else np.zeros(cfg["E"], np.float32)
+    w1, w3, w2 = n(inp["w1"]), n(inp["w3"]), n(inp["w2"])
+    shared = None
+    if inp.get("shared") is not None:
+        shared = tuple(None if t is None else n(t[0]) for t in inp["shared"])
+    x_all = inp["x"]
+
+    def run(T):
+        c = dict(cfg)
+        c["N"] = T
+        x = n(x_all[:T])
+        t0 = time.perf_counter()
+        out = oracle.forward(c, x, wr, rb, sb, w1, w3, w2, shared=shared)
+        oracle.bias_update(T, c["k"], out["counts"], bias_state, cfg.get("bias_step", 1e-3))
+        return time.perf_counter() - t0
+
+    T0 = min(cfg["N"], 64)
+    t0 = run(T0)
+    T = int(min(cfg["N"], max(T0, T0 * target_s / max(t0, 1e-6))))
+    elapsed = run(T) if T != T0 else t0
+    return {"value": T / elapsed, "unit": "tokens/s", "cores": threads, "kind": "oracle",
+            "sample": f"first {T} of {cfg['N']} tokens as one batch (capacity for {T}); "
+                      f"route+dispatch+FFN+combine+bias update; {elapsed:.1f} s"}
+
+
+def main():
+    args = parse_args()
+    if args.gpus != 1:
+        print(json.dumps({"error": "this build runs on one GPU only; --gpus must be 1",
+                          "n_gpus": args.gpus}))
+        sys.exit(2)
+
+    import torch
+
+    import expert_token_routing_router_amd as moe
+    from expert_token_routing_router_amd import layer
+    import moe_workloads as W
+
+    dev = torch.device("cuda:0")
+    cfg = W.full(args.workload)
+    if args.cf is not None:
+        cfg["cf"] = args.cf
+    # Inputs: the glossary snippet's stream for the toy workload (CPU), else
+    # drawn on the device.
+    gen_dev = "cpu" if args.workload == "toy" else "cuda"
+    inp_src = W.make_inputs(cfg, device=gen_dev)
+    inp = {k: (tuple(None if t is None else t.to(dev) for t in v) if isinstance(v, tuple)
+               else (v.to(dev) if isinstance(v, torch.Tensor) else v))
+           for k, v in inp_src.items()}
+    buf = moe.MoeBuffers(cfg, dev)
+    d = buf.desc
+    N, E, k, dim, h = d.num_tokens, d.num_experts, d.top_k, d.hidden, cfg["h"]
+    S = N * k
+    bias_state = (inp["sel_bias"].clone() if inp.get("sel_bias") is not None
+                  else torch.zeros(E, dtype=torch.float32, device=dev))
+    step_bias = cfg.get("bias_step", 1e-3)
+
+    calls = ["route", "dispatch", "ffn_plan", "ffn_up", "ffn_down"]
+    if buf.shared_out is not None:
+        calls.append("shared_ffn")
+    calls += ["combine", "bias_update"]
+
+    def step(events=None):
+        def mark(i):
+            if events is not None:
+                events[i].record()
+        mark(0)
+        layer.route(buf, inp)
+        mark(1)
+        layer.dispatch(buf, inp)
+        mark(2)
+        moe.moe_expert_ffn_plan(E, S, dim, h, cfg["act"], cfg["dtype"], buf.expert_offsets,
+                                buf.ws_ffn)
+        mark(3)
+        moe.moe_expert_ffn_up(E, S, dim, h, cfg["act"], cfg["dtype"], buf.x_perm,
+                              buf.expert_offsets, inp["w1"], inp.get("w3"), buf.ws_ffn)
+        mark(4)
+        moe.moe_expert_ffn_down(E, S, dim, h, cfg["act"], cfg["dtype"], buf.expert_offsets,
+                                inp["w2"], buf.y_perm, buf.ws_ffn)
+        i = 5
+        mark(i)
+        if buf.shared_out is not None:
+            sw1, sw3, sw2 = inp["shared"]
+            moe.moe_expert_ffn(1, N, dim, h, cfg["act"], cfg["dtype"], inp["x"],
+                               buf.shared_offsets, sw1, sw3, sw2, buf.shared_out, buf.ws_shared)
+            i += 1
+            mark(i)
+        layer.combine(buf, inp, residual=True)
+        i += 1
+        mark(i)
+        layer.bias_update(buf, bias_state, step_bias)
+        mark(i + 1)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+
+    nev = len(calls) + 1
+    events = [[torch.cuda.Event(enable_timing=True) for _ in range(nev)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for s in range(args.steps):
+        step(events[s])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+
+    per_call = {c: 0.0 for c in calls}
+    for ev in events:
+        for i, c in enumerate(calls):
+            per_call[c] += ev[i].elapsed_time(ev[i + 1])
+    per_call = {c: v / args.steps * 1e3 for c, v in per_call.items()}  # microseconds
+    step_ms = sum(events[s][0].elapsed_time(events[s][-1]) for s in range(args.steps)) / args.steps
+    ms_per_step = max(step_ms, wall * 1e3 / args.steps)
+    value = N / (ms_per_step * 1e-3)
+
+    if args.copy_calibration_mib > 0:
+        nbytes = args.copy_calibration_mib << 20
+        a = torch.empty(nbytes // 4, dtype=torch.float32, device=dev).fill_(1.0)
+        b = torch.empty_like(a)
+        torch.cuda.synchronize()
+        b.copy_(a)
+        torch.cuda.synchronize()
+
+    # Algorithmic work of this batch (rows actually admitted).
+    M = int(buf.expert_offsets[E].item())
+    counts = buf.admitted.cpu()
+    active = int((counts > 0).sum().item())
+    es = 2 if cfg["dtype"] == "bf16" else 4
+    mats_up = 2 if cfg["act"] == "swiglu" else 1
+    up_flops = 2.0 * M * dim * h * mats_up
+    up_bytes = (active * mats_up * h * dim + M * dim + M * h) * es
+    down_flops = 2.0 * M * h * dim
+    down_bytes = (active * dim * h + M * h + M * dim) * es
+    dispatch_bytes = S * 4 + N * dim * es + M * dim * es + S * 4 + 2 * S * 4 + S
+    combine_bytes = M * dim * es + N * dim * es + N * dim * es + S * 8
+    route_bytes = N * dim * es + E * dim * es + N * E * 4 + S * 8
+    peak = MFMA_PEAK_TFLOPS[cfg["dtype"]]
+
+    def roof(name, flops, nbytes):
+        t = per_call[name] * 1e-6
+        t_f, t_b = flops / (peak * 1e12), nbytes / (HBM_PEAK_GBS * 1e9)
+        return {"us": round(per_call[name], 2), "tflops": round(flops / t / 1e12, 2),
+                "gbs": round(nbytes / t / 1e9, 1), "mfma_frac": round(flops / t / (peak * 1e12), 4),
+                "hbm_frac": round(nbytes / t / (HBM_PEAK_GBS * 1e9), 4),
+                "bound": "mfma" if t_f >= t_b else "hbm"}
+
+    kern = {
+        "ffn_up": roof("ffn_up", up_flops, up_bytes),
+        "ffn_down": roof("ffn_down", down_flops, down_bytes),
+    }
+    for name, nbytes in [("route", route_bytes), ("dispatch", dispatch_bytes),
+                         ("combine", combine_bytes)]:
+        t = per_call[name] * 1e-6
+        kern[name] = {"us": round(per_call[name], 2), "gbs": round(nbytes / t / 1e9, 1),
+                      "hbm_frac": round(nbytes / t / (HBM_PEAK_GBS * 1e9), 4)}
+    for name in calls:
+        kern.setdefault(name, {"us": round(per_call[name], 2)})
+
+    dom = "ffn_up" if per_call["ffn_up"] >= per_call["ffn_down"] else "ffn_down"
+    dk = kern[dom]
+    kernel_name = {"ffn_up": "grouped_gemm_up", "ffn_down": "grouped_gemm_down"}[dom]
+    digest = kernel_sources_digest()
+    traffic = read_traffic(kernel_name, args.workload, digest)
+    if dk["bound"] == "mfma":
+        roofline = {"bound": "mfma", "achieved": dk["tflops"], "peak": peak, "unit": "TFLOP/s",
+                    "frac": dk["mfma_frac"], "traffic": traffic}
+    else:
+        roofline = {"bound": "hbm", "achieved": dk["gbs"], "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                    "frac": dk["hbm_frac"], "traffic": traffic}
+    roofline["kernel"] = f"{kernel_name} ({dom})"
+    roofline["mfma_frac"] = dk["mfma_frac"]
+
+    out = {
+        "metric": METRIC,
+        "value": round(value, 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": cfg["dtype"],
+        "data": "synthetic",
+        "config": {"workload": describe(cfg), "global_batch": N, "rows_admitted": M,
+                   "dropped_slots": S - M, "active_experts": active},
+        "roofline": roofline,
+        "grouped_gemm_mfma_frac": {"up": kern["ffn_up"]["mfma_frac"],
+                                   "down": kern["ffn_down"]["mfma_frac"]},
+        "permute_hbm_frac": kern["dispatch"]["hbm_frac"],
+        "kernels": kern,
+        "kernel_sources_digest": digest,
+    }
+    if not args.no_cpu_baseline:
+        host = {}
+        for key, v in inp.items():
+            if isinstance(v, tuple):
+                host[key] = tuple(None if t is None else t.cpu() for t in v)
+            elif isinstance(v, torch.Tensor):
+                host[key] = v.cpu()
+            else:
+                host[key] = v
+        cb = cpu_baseline(cfg, host, args.cpu_seconds)
+        cb["gpu_speedup"] = round(value / cb["value"], 1)
+        out["cpu_baseline"] = cb
+    else:
+        out["cpu_baseline"] = None
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

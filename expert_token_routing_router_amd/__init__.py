@@ -35,7 +35,8 @@ TORCH_DTYPE = {MOE_F32: torch.float32, MOE_BF16: torch.bfloat16}
 
 EXPORTS = [
     "moe_route_workspace_size", "moe_route", "moe_dispatch_workspace_size", "moe_dispatch",
-    "moe_expert_ffn_workspace_size", "moe_expert_ffn", "moe_combine", "moe_bias_update",
+    "moe_expert_ffn_workspace_size", "moe_expert_ffn", "moe_expert_ffn_plan",
+    "moe_expert_ffn_up", "moe_expert_ffn_down", "moe_combine", "moe_bias_update",
     "moe_status_string",
 ]
 
@@ -95,6 +96,9 @@ def lib() -> ctypes.CDLL:
             "moe_dispatch": ([D, P, P, P, P, P, P, P, P, P, P, P, SZ, P], I32),
             "moe_expert_ffn_workspace_size": ([I32, I32, I32, I32, I32, I32], SZ),
             "moe_expert_ffn": ([I32, I32, I32, I32, I32, I32, P, P, P, P, P, P, P, SZ, P], I32),
+            "moe_expert_ffn_plan": ([I32, I32, I32, I32, I32, I32, P, P, SZ, P], I32),
+            "moe_expert_ffn_up": ([I32, I32, I32, I32, I32, I32, P, P, P, P, P, SZ, P], I32),
+            "moe_expert_ffn_down": ([I32, I32, I32, I32, I32, I32, P, P, P, P, SZ, P], I32),
             "moe_combine": ([D, P, P, P, P, P, P, P], I32),
             "moe_bias_update": ([I32, I32, I32, P, F32, P, P], I32),
             "moe_status_string": ([I32], ctypes.c_char_p),
@@ -215,6 +219,49 @@ def moe_expert_ffn(num_experts, max_rows, hidden, ffn_hidden, act, dtype, x_rows
         _ptr(ws, "ws", None, None, False), 0 if ws is None else ws.numel() * ws.element_size(),
         _stream(stream))
     _raise("moe_expert_ffn", st)
+
+
+def _ws(ws):
+    return (_ptr(ws, "ws", None, None, False),
+            0 if ws is None else ws.numel() * ws.element_size())
+
+
+def moe_expert_ffn_plan(num_experts, max_rows, hidden, ffn_hidden, act, dtype, group_offsets,
+                        ws, stream=None):
+    act = ACT[act] if isinstance(act, str) else int(act)
+    dtype = DTYPE[dtype] if isinstance(dtype, str) else int(dtype)
+    st = lib().moe_expert_ffn_plan(
+        num_experts, max_rows, hidden, ffn_hidden, act, dtype,
+        _ptr(group_offsets, "group_offsets", torch.int32, num_experts + 1), *_ws(ws),
+        _stream(stream))
+    _raise("moe_expert_ffn_plan", st)
+
+
+def moe_expert_ffn_up(num_experts, max_rows, hidden, ffn_hidden, act, dtype, x_rows,
+                      group_offsets, w1, w3, ws, stream=None):
+    act = ACT[act] if isinstance(act, str) else int(act)
+    dtype = DTYPE[dtype] if isinstance(dtype, str) else int(dtype)
+    dt = TORCH_DTYPE.get(dtype)
+    E, M, d, h = num_experts, max_rows, hidden, ffn_hidden
+    st = lib().moe_expert_ffn_up(
+        E, M, d, h, act, dtype, _ptr(x_rows, "x_rows", dt, M * d, M > 0),
+        _ptr(group_offsets, "group_offsets", torch.int32, E + 1),
+        _ptr(w1, "w1", dt, E * h * d), _ptr(w3, "w3", dt, E * h * d, act == MOE_SWIGLU),
+        *_ws(ws), _stream(stream))
+    _raise("moe_expert_ffn_up", st)
+
+
+def moe_expert_ffn_down(num_experts, max_rows, hidden, ffn_hidden, act, dtype, group_offsets,
+                        w2, y_rows, ws, stream=None):
+    act = ACT[act] if isinstance(act, str) else int(act)
+    dtype = DTYPE[dtype] if isinstance(dtype, str) else int(dtype)
+    dt = TORCH_DTYPE.get(dtype)
+    E, M, d, h = num_experts, max_rows, hidden, ffn_hidden
+    st = lib().moe_expert_ffn_down(
+        E, M, d, h, act, dtype, _ptr(group_offsets, "group_offsets", torch.int32, E + 1),
+        _ptr(w2, "w2", dt, E * d * h), _ptr(y_rows, "y_rows", dt, M * d, M > 0),
+        *_ws(ws), _stream(stream))
+    _raise("moe_expert_ffn_down", st)
 
 
 def moe_combine(desc, y_perm, row_of_slot, topk_w, residual, shared_out, y, stream=None):

@@ -127,25 +127,76 @@ size_t moe_expert_ffn_workspace_size(int32_t num_experts, int32_t max_rows, int3
   return moe::ffn_workspace_bytes(num_experts, max_rows, hidden, ffn_hidden, act, dtype);
 }
 
+// Validation shared by moe_expert_ffn and its stages.  stage: 0 = all,
+// 1 = plan, 2 = up, 3 = down.
+static int check_ffn_call(int stage, int32_t E, int32_t max_rows, int32_t d, int32_t h,
+                          int32_t act, int32_t dtype, const void* x_rows,
+                          const int32_t* offsets, const void* w1, const void* w3,
+                          const void* w2, const void* y_rows, const void* ws, size_t ws_bytes) {
+  int st = check_ffn(E, max_rows, d, h, act, dtype);
+  if (st != MOE_OK) return st;
+  if (!offsets) return MOE_ERR_INVALID_ARG;
+  const bool up = stage == 0 || stage == 2, down = stage == 0 || stage == 3;
+  if (up && (!w1 || (act == MOE_SWIGLU) != (w3 != nullptr))) return MOE_ERR_INVALID_ARG;
+  if (down && !w2) return MOE_ERR_INVALID_ARG;
+  if (max_rows == 0) return MOE_OK;
+  if (up && (!x_rows || !aligned16(x_rows) || !aligned16(w1) || (w3 && !aligned16(w3))))
+    return MOE_ERR_INVALID_ARG;
+  if (down && (!y_rows || !aligned16(y_rows) || !aligned16(w2))) return MOE_ERR_INVALID_ARG;
+  const size_t need = moe::ffn_workspace_bytes(E, max_rows, d, h, act, dtype);
+  if (!ws || ws_bytes < need || (reinterpret_cast<uintptr_t>(ws) & 255u)) return MOE_ERR_WORKSPACE;
+  return MOE_OK;
+}
+
 int moe_expert_ffn(int32_t num_experts, int32_t max_rows, int32_t hidden, int32_t ffn_hidden,
                    int32_t act, int32_t dtype, const void* x_rows,
                    const int32_t* group_offsets, const void* w1, const void* w3,
                    const void* w2, void* y_rows, void* ws, size_t ws_bytes, void* stream) {
-  int st = check_ffn(num_experts, max_rows, hidden, ffn_hidden, act, dtype);
-  if (st != MOE_OK) return st;
-  if (!group_offsets || !w1 || !w2) return MOE_ERR_INVALID_ARG;
-  if ((act == MOE_SWIGLU) != (w3 != nullptr)) return MOE_ERR_INVALID_ARG;
-  if (max_rows == 0) return MOE_OK;
-  if (!x_rows || !y_rows) return MOE_ERR_INVALID_ARG;
-  if (!aligned16(x_rows) || !aligned16(y_rows) || !aligned16(w1) || !aligned16(w2) ||
-      (w3 && !aligned16(w3)))
-    return MOE_ERR_INVALID_ARG;
-  const size_t need =
-      moe::ffn_workspace_bytes(num_experts, max_rows, hidden, ffn_hidden, act, dtype);
-  if (!ws || ws_bytes < need || (reinterpret_cast<uintptr_t>(ws) & 255u)) return MOE_ERR_WORKSPACE;
+  int st = check_ffn_call(0, num_experts, max_rows, hidden, ffn_hidden, act, dtype, x_rows,
+                          group_offsets, w1, w3, w2, y_rows, ws, ws_bytes);
+  if (st != MOE_OK || max_rows == 0) return st;
   moe::FfnArgs a{num_experts, max_rows, hidden, ffn_hidden, act, dtype, x_rows,
                  group_offsets, w1, w3, w2, y_rows, ws};
-  return status_of(moe::launch_ffn(a, static_cast<hipStream_t>(stream)));
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  hipError_t e = moe::launch_ffn_plan(a, s);
+  if (e == hipSuccess) e = moe::launch_ffn_up(a, s);
+  if (e == hipSuccess) e = moe::launch_ffn_down(a, s);
+  return status_of(e);
+}
+
+int moe_expert_ffn_plan(int32_t num_experts, int32_t max_rows, int32_t hidden,
+                        int32_t ffn_hidden, int32_t act, int32_t dtype,
+                        const int32_t* group_offsets, void* ws, size_t ws_bytes, void* stream) {
+  int st = check_ffn_call(1, num_experts, max_rows, hidden, ffn_hidden, act, dtype, nullptr,
+                          group_offsets, nullptr, nullptr, nullptr, nullptr, ws, ws_bytes);
+  if (st != MOE_OK || max_rows == 0) return st;
+  moe::FfnArgs a{num_experts, max_rows, hidden, ffn_hidden, act, dtype, nullptr,
+                 group_offsets, nullptr, nullptr, nullptr, nullptr, ws};
+  return status_of(moe::launch_ffn_plan(a, static_cast<hipStream_t>(stream)));
+}
+
+int moe_expert_ffn_up(int32_t num_experts, int32_t max_rows, int32_t hidden, int32_t ffn_hidden,
+                      int32_t act, int32_t dtype, const void* x_rows,
+                      const int32_t* group_offsets, const void* w1, const void* w3,
+                      void* ws, size_t ws_bytes, void* stream) {
+  int st = check_ffn_call(2, num_experts, max_rows, hidden, ffn_hidden, act, dtype, x_rows,
+                          group_offsets, w1, w3, nullptr, nullptr, ws, ws_bytes);
+  if (st != MOE_OK || max_rows == 0) return st;
+  moe::FfnArgs a{num_experts, max_rows, hidden, ffn_hidden, act, dtype, x_rows,
+                 group_offsets, w1, w3, nullptr, nullptr, ws};
+  return status_of(moe::launch_ffn_up(a, static_cast<hipStream_t>(stream)));
+}
+
+int moe_expert_ffn_down(int32_t num_experts, int32_t max_rows, int32_t hidden,
+                        int32_t ffn_hidden, int32_t act, int32_t dtype,
+                        const int32_t* group_offsets, const void* w2, void* y_rows,
+                        void* ws, size_t ws_bytes, void* stream) {
+  int st = check_ffn_call(3, num_experts, max_rows, hidden, ffn_hidden, act, dtype, nullptr,
+                          group_offsets, nullptr, nullptr, w2, y_rows, ws, ws_bytes);
+  if (st != MOE_OK || max_rows == 0) return st;
+  moe::FfnArgs a{num_experts, max_rows, hidden, ffn_hidden, act, dtype, nullptr,
+                 group_offsets, nullptr, nullptr, w2, y_rows, ws};
+  return status_of(moe::launch_ffn_down(a, static_cast<hipStream_t>(stream)));
 }
 
 int moe_combine(const moe_route_desc* desc, const void* y_perm, const int32_t* row_of_slot,

@@ -328,49 +328,68 @@ static int grid_for(int max_rows, int BM, int E, int n_tiles) {
   return (int)g;
 }
 
-hipError_t launch_ffn(const FfnArgs& a, hipStream_t st) {
-  int32_t* tile_start = static_cast<int32_t*>(a.ws);
-  void* H = static_cast<char*>(a.ws) + align256((size_t)(a.E + 1) * sizeof(int32_t));
-  const int BM = a.dtype == 0 ? kF32BM : kBf16BM;
-  const int BN = a.dtype == 0 ? kF32BN : kBf16BN;
-  ffn_tile_prefix<<<1, 1024, 0, st>>>(a.offsets, a.E, BM, tile_start);
-  const int nt1 = (a.h + BN - 1) / BN, nt2 = (a.d + BN - 1) / BN;
-  const int g1 = grid_for(a.max_rows, BM, a.E, nt1), g2 = grid_for(a.max_rows, BM, a.E, nt2);
+static int32_t* ffn_tile_start(const FfnArgs& a) { return static_cast<int32_t*>(a.ws); }
+static void* ffn_hidden_buf(const FfnArgs& a) {
+  return static_cast<char*>(a.ws) + align256((size_t)(a.E + 1) * sizeof(int32_t));
+}
+static int ffn_bm(int dtype) { return dtype == 0 ? kF32BM : kBf16BM; }
+static int ffn_bn(int dtype) { return dtype == 0 ? kF32BN : kBf16BN; }
+
+hipError_t launch_ffn_plan(const FfnArgs& a, hipStream_t st) {
+  ffn_tile_prefix<<<1, 1024, 0, st>>>(a.offsets, a.E, ffn_bm(a.dtype), ffn_tile_start(a));
+  return hipGetLastError();
+}
+
+hipError_t launch_ffn_up(const FfnArgs& a, hipStream_t st) {
+  const int BM = ffn_bm(a.dtype), BN = ffn_bn(a.dtype);
+  const int nt = (a.h + BN - 1) / BN;
+  const int g = grid_for(a.max_rows, BM, a.E, nt);
+  int32_t* ts = ffn_tile_start(a);
   if (a.dtype == 0) {
     const float* X = static_cast<const float*>(a.x_rows);
     const float* W1 = static_cast<const float*>(a.w1);
     const float* W3 = static_cast<const float*>(a.w3);
-    const float* W2 = static_cast<const float*>(a.w2);
-    float* Hf = static_cast<float*>(H);
+    float* Hf = static_cast<float*>(ffn_hidden_buf(a));
     if (a.act == ACT_RELU)
-      grouped_gemm_f32<ACT_RELU><<<g1, 256, 0, st>>>(X, W1, nullptr, Hf, a.d, a.h, a.offsets,
-                                                     tile_start, a.E, nt1, a.max_rows);
+      grouped_gemm_f32<ACT_RELU><<<g, 256, 0, st>>>(X, W1, nullptr, Hf, a.d, a.h, a.offsets, ts,
+                                                    a.E, nt, a.max_rows);
     else if (a.act == ACT_GELU)
-      grouped_gemm_f32<ACT_GELU><<<g1, 256, 0, st>>>(X, W1, nullptr, Hf, a.d, a.h, a.offsets,
-                                                     tile_start, a.E, nt1, a.max_rows);
+      grouped_gemm_f32<ACT_GELU><<<g, 256, 0, st>>>(X, W1, nullptr, Hf, a.d, a.h, a.offsets, ts,
+                                                    a.E, nt, a.max_rows);
     else
-      grouped_gemm_f32<ACT_SWIGLU><<<g1, 256, 0, st>>>(X, W1, W3, Hf, a.d, a.h, a.offsets,
-                                                       tile_start, a.E, nt1, a.max_rows);
-    grouped_gemm_f32<ACT_NONE><<<g2, 256, 0, st>>>(Hf, W2, nullptr, static_cast<float*>(a.y_rows),
-                                                   a.h, a.d, a.offsets, tile_start, a.E, nt2, a.max_rows);
+      grouped_gemm_f32<ACT_SWIGLU><<<g, 256, 0, st>>>(X, W1, W3, Hf, a.d, a.h, a.offsets, ts,
+                                                      a.E, nt, a.max_rows);
   } else {
     const bf16_t* X = static_cast<const bf16_t*>(a.x_rows);
     const bf16_t* W1 = static_cast<const bf16_t*>(a.w1);
     const bf16_t* W3 = static_cast<const bf16_t*>(a.w3);
-    const bf16_t* W2 = static_cast<const bf16_t*>(a.w2);
-    bf16_t* Hb = static_cast<bf16_t*>(H);
+    bf16_t* Hb = static_cast<bf16_t*>(ffn_hidden_buf(a));
     if (a.act == ACT_RELU)
-      grouped_gemm_bf16<kBf16BM, kBf16BN, ACT_RELU><<<g1, 256, 0, st>>>(
-          X, W1, nullptr, Hb, a.d, a.h, a.offsets, tile_start, a.E, nt1, a.max_rows);
+      grouped_gemm_bf16<kBf16BM, kBf16BN, ACT_RELU><<<g, 256, 0, st>>>(
+          X, W1, nullptr, Hb, a.d, a.h, a.offsets, ts, a.E, nt, a.max_rows);
     else if (a.act == ACT_GELU)
-      grouped_gemm_bf16<kBf16BM, kBf16BN, ACT_GELU><<<g1, 256, 0, st>>>(
-          X, W1, nullptr, Hb, a.d, a.h, a.offsets, tile_start, a.E, nt1, a.max_rows);
+      grouped_gemm_bf16<kBf16BM, kBf16BN, ACT_GELU><<<g, 256, 0, st>>>(
+          X, W1, nullptr, Hb, a.d, a.h, a.offsets, ts, a.E, nt, a.max_rows);
     else
-      grouped_gemm_bf16<kBf16BM, kBf16BN, ACT_SWIGLU><<<g1, 256, 0, st>>>(
-          X, W1, W3, Hb, a.d, a.h, a.offsets, tile_start, a.E, nt1, a.max_rows);
-    grouped_gemm_bf16<kBf16BM, kBf16BN, ACT_NONE><<<g2, 256, 0, st>>>(
-        Hb, W2, nullptr, static_cast<bf16_t*>(a.y_rows), a.h, a.d, a.offsets, tile_start, a.E,
-        nt2, a.max_rows);
+      grouped_gemm_bf16<kBf16BM, kBf16BN, ACT_SWIGLU><<<g, 256, 0, st>>>(
+          X, W1, W3, Hb, a.d, a.h, a.offsets, ts, a.E, nt, a.max_rows);
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_ffn_down(const FfnArgs& a, hipStream_t st) {
+  const int BM = ffn_bm(a.dtype), BN = ffn_bn(a.dtype);
+  const int nt = (a.d + BN - 1) / BN;
+  const int g = grid_for(a.max_rows, BM, a.E, nt);
+  int32_t* ts = ffn_tile_start(a);
+  if (a.dtype == 0) {
+    grouped_gemm_f32<ACT_NONE><<<g, 256, 0, st>>>(
+        static_cast<const float*>(ffn_hidden_buf(a)), static_cast<const float*>(a.w2), nullptr,
+        static_cast<float*>(a.y_rows), a.h, a.d, a.offsets, ts, a.E, nt, a.max_rows);
+  } else {
+    grouped_gemm_bf16<kBf16BM, kBf16BN, ACT_NONE><<<g, 256, 0, st>>>(
+        static_cast<const bf16_t*>(ffn_hidden_buf(a)), static_cast<const bf16_t*>(a.w2),
+        nullptr, static_cast<bf16_t*>(a.y_rows), a.h, a.d, a.offsets, ts, a.E, nt, a.max_rows);
   }
   return hipGetLastError();
 }

@@ -182,6 +182,26 @@ int moe_expert_ffn(int32_t num_experts, int32_t max_rows, int32_t hidden, int32_
                    const int32_t* group_offsets, const void* w1, const void* w3,
                    const void* w2, void* y_rows, void* ws, size_t ws_bytes, void* stream);
 
+/* The three stages of moe_expert_ffn, for callers that time or overlap them.
+ * They share one workspace (same size query) and must run in this order on
+ * one stream with the same num_experts, max_rows, group_offsets and ws:
+ *  moe_expert_ffn_plan  per-expert row-tile schedule from group_offsets
+ *  moe_expert_ffn_up    H = act(X W1_e^T) (SwiGLU: silu(X W1_e^T)*(X W3_e^T)),
+ *                       H kept in ws, one kernel launch
+ *  moe_expert_ffn_down  Y = H W2_e^T, one kernel launch
+ * Arguments mean what they mean for moe_expert_ffn; errors likewise. */
+int moe_expert_ffn_plan(int32_t num_experts, int32_t max_rows, int32_t hidden,
+                        int32_t ffn_hidden, int32_t act, int32_t dtype,
+                        const int32_t* group_offsets, void* ws, size_t ws_bytes, void* stream);
+int moe_expert_ffn_up(int32_t num_experts, int32_t max_rows, int32_t hidden, int32_t ffn_hidden,
+                      int32_t act, int32_t dtype, const void* x_rows,
+                      const int32_t* group_offsets, const void* w1, const void* w3,
+                      void* ws, size_t ws_bytes, void* stream);
+int moe_expert_ffn_down(int32_t num_experts, int32_t max_rows, int32_t hidden,
+                        int32_t ffn_hidden, int32_t act, int32_t dtype,
+                        const int32_t* group_offsets, const void* w2, void* y_rows,
+                        void* ws, size_t ws_bytes, void* stream);
+
 /* ---------------------------------------------------------------- combine -- */
 
 /* Combine.  Glossary step 4 (outputs return to each token and are weighted by
