@@ -34,7 +34,8 @@ DTYPE = {"fp32": MOE_F32, "bf16": MOE_BF16}
 TORCH_DTYPE = {MOE_F32: torch.float32, MOE_BF16: torch.bfloat16}
 
 EXPORTS = [
-    "moe_route_workspace_size", "moe_route", "moe_dispatch_workspace_size", "moe_dispatch",
+    "moe_route_workspace_size", "moe_route", "moe_router_logits",
+    "moe_dispatch_workspace_size", "moe_dispatch",
     "moe_expert_ffn_workspace_size", "moe_expert_ffn", "moe_expert_ffn_plan",
     "moe_expert_ffn_up", "moe_expert_ffn_down", "moe_combine", "moe_bias_update",
     "moe_status_string",
@@ -92,6 +93,7 @@ def lib() -> ctypes.CDLL:
         sigs = {
             "moe_route_workspace_size": ([D], SZ),
             "moe_route": ([D, P, P, P, P, P, P, P, P, P, SZ, P], I32),
+            "moe_router_logits": ([D, P, P, P, P, P, SZ, P], I32),
             "moe_dispatch_workspace_size": ([D], SZ),
             "moe_dispatch": ([D, P, P, P, P, P, P, P, P, P, P, P, SZ, P], I32),
             "moe_expert_ffn_workspace_size": ([I32, I32, I32, I32, I32, I32], SZ),
@@ -182,6 +184,19 @@ def moe_route(desc, x, w_router, router_bias, sel_bias, logits, topk_idx, topk_w
         _ptr(ws, "ws", None, None, False), 0 if ws is None else ws.numel() * ws.element_size(),
         _stream(stream))
     _raise("moe_route", st)
+
+
+def moe_router_logits(desc, x, w_router, router_bias, logits, ws, stream=None):
+    N, d, E = desc.num_tokens, desc.hidden, desc.num_experts
+    dt = TORCH_DTYPE.get(desc.dtype)
+    st = lib().moe_router_logits(
+        ctypes.byref(desc), _ptr(x, "x", dt, N * d, N > 0),
+        _ptr(w_router, "w_router", dt, E * d, N > 0),
+        _ptr(router_bias, "router_bias", torch.float32, E, False),
+        _ptr(logits, "logits", torch.float32, N * E, N > 0),
+        _ptr(ws, "ws", None, None, False), 0 if ws is None else ws.numel() * ws.element_size(),
+        _stream(stream))
+    _raise("moe_router_logits", st)
 
 
 def moe_dispatch(desc, x, topk_idx, x_perm, row_of_slot, token_of_row, slot_of_row,

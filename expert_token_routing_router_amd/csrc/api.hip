@@ -61,7 +61,8 @@ const char* moe_status_string(int status) {
 
 size_t moe_route_workspace_size(const moe_route_desc* desc) {
   if (check_desc(desc) != MOE_OK) return 0;
-  return moe::route_workspace_bytes(desc->num_tokens, desc->hidden, desc->num_experts);
+  return moe::route_workspace_bytes(desc->num_tokens, desc->hidden, desc->num_experts,
+                                    desc->dtype);
 }
 
 int moe_route(const moe_route_desc* desc, const void* x, const void* w_router,
@@ -75,13 +76,31 @@ int moe_route(const moe_route_desc* desc, const void* x, const void* w_router,
   if (N > 0) {
     if (!x || !w_router || !logits || !topk_idx || !topk_w) return MOE_ERR_INVALID_ARG;
     if (!aligned16(x)) return MOE_ERR_INVALID_ARG;
-    const size_t need = moe::route_workspace_bytes(N, desc->hidden, desc->num_experts);
-    if (!ws || ws_bytes < need || (reinterpret_cast<uintptr_t>(ws) & 15u)) return MOE_ERR_WORKSPACE;
+    const size_t need =
+        moe::route_workspace_bytes(N, desc->hidden, desc->num_experts, desc->dtype);
+    if (!ws || ws_bytes < need || (reinterpret_cast<uintptr_t>(ws) & 255u)) return MOE_ERR_WORKSPACE;
   }
   moe::RouteArgs a{N, desc->hidden, desc->num_experts, desc->top_k, desc->num_groups,
                    desc->topk_groups, desc->score_fn, desc->dtype, x, w_router, router_bias,
                    sel_bias, logits, topk_idx, topk_w, counts, ws};
   return status_of(moe::launch_route(a, static_cast<hipStream_t>(stream)));
+}
+
+int moe_router_logits(const moe_route_desc* desc, const void* x, const void* w_router,
+                      const float* router_bias, float* logits, void* ws, size_t ws_bytes,
+                      void* stream) {
+  int st = check_desc(desc);
+  if (st != MOE_OK) return st;
+  const int N = desc->num_tokens;
+  if (N == 0) return MOE_OK;
+  if (!x || !w_router || !logits) return MOE_ERR_INVALID_ARG;
+  if (!aligned16(x)) return MOE_ERR_INVALID_ARG;
+  const size_t need = moe::route_workspace_bytes(N, desc->hidden, desc->num_experts, desc->dtype);
+  if (!ws || ws_bytes < need || (reinterpret_cast<uintptr_t>(ws) & 255u)) return MOE_ERR_WORKSPACE;
+  moe::RouteArgs a{N, desc->hidden, desc->num_experts, desc->top_k, desc->num_groups,
+                   desc->topk_groups, desc->score_fn, desc->dtype, x, w_router, router_bias,
+                   nullptr, logits, nullptr, nullptr, nullptr, ws};
+  return status_of(moe::launch_router_logits(a, static_cast<hipStream_t>(stream)));
 }
 
 size_t moe_dispatch_workspace_size(const moe_route_desc* desc) {

@@ -24,8 +24,14 @@ struct RouteArgs {
   void* ws;
 };
 
-size_t route_workspace_bytes(int N, int d, int E);
+size_t route_workspace_bytes(int N, int d, int E, int dtype);
 hipError_t launch_route(const RouteArgs& a, hipStream_t st);
+// Exact logits for every (token, expert) pair (the fp64 definition), no selection.
+hipError_t launch_router_logits(const RouteArgs& a, hipStream_t st);
+// Certified path for bf16 inputs (route_mfma.hip).
+size_t route_certified_workspace_bytes(int N, int E);
+hipError_t launch_route_certified(const RouteArgs& a, hipStream_t st);
+constexpr int kCertifiedMaxTokens = 1 << 23;  // (token << 8 | expert) pair encoding
 
 struct DispatchArgs {
   int N, d, E, k, R, dtype;

@@ -113,16 +113,17 @@ __device__ __forceinline__ float sigmoid_affinity(float z) {
 // One wave per token; a block of 4 waves walks TPB tokens.  Lane l holds
 // experts l, l+64, l+128, l+192.
 constexpr int kSelectTokensPerBlock = 64;
+constexpr int kSelectWaves = 16;  // 4 tokens per wave
 
-__global__ __launch_bounds__(256) void select_topk(const float* __restrict__ logits,
+__global__ __launch_bounds__(kSelectWaves * 64) void select_topk(const float* __restrict__ logits,
                                                    const float* __restrict__ sel_bias, int N,
                                                    int E, int k, int G, int kg, int score_fn,
                                                    int32_t* __restrict__ topk_idx,
                                                    float* __restrict__ topk_w,
                                                    int32_t* __restrict__ counts) {
   __shared__ int32_t hist[256];
-  __shared__ float sbuf[4][256];
-  for (int e = threadIdx.x; e < E; e += 256) hist[e] = 0;
+  __shared__ float sbuf[kSelectWaves][256];
+  for (int e = threadIdx.x; e < E; e += blockDim.x) hist[e] = 0;
   __syncthreads();
 
   const int wave = threadIdx.x / 64, lane = threadIdx.x % 64;
@@ -130,7 +131,7 @@ __global__ __launch_bounds__(256) void select_topk(const float* __restrict__ log
   const int t_begin = blockIdx.x * kSelectTokensPerBlock;
   const int t_end = min(N, t_begin + kSelectTokensPerBlock);
 
-  for (int t = t_begin + wave; t < t_end; t += 4) {
+  for (int t = t_begin + wave; t < t_end; t += kSelectWaves) {
     float z[4], s[4];
     bool ok[4];
 #pragma unroll
@@ -253,7 +254,7 @@ __global__ __launch_bounds__(256) void select_topk(const float* __restrict__ log
     }
   }
   __syncthreads();
-  for (int e = threadIdx.x; e < E; e += 256)
+  for (int e = threadIdx.x; e < E; e += blockDim.x)
     if (hist[e]) atomicAdd(&counts[e], hist[e]);
 }
 
@@ -266,16 +267,23 @@ static int route_padded_experts(int E) {
   return (E + ec - 1) / ec * ec;
 }
 
-size_t route_workspace_bytes(int N, int d, int E) {
+static size_t exact_logits_bytes(int N, int d, int E) {
   if (N <= 0) return 0;
   return (size_t)route_padded_experts(E) * d * sizeof(double);
 }
 
-hipError_t launch_route(const RouteArgs& a, hipStream_t st) {
-  if (a.N == 0) {
-    zero_i32<<<1, 256, 0, st>>>(a.counts, a.E);
-    return hipGetLastError();
-  }
+static bool use_certified(const RouteArgs& a) {
+  return a.dtype == 1 && a.N < kCertifiedMaxTokens;
+}
+
+size_t route_workspace_bytes(int N, int d, int E, int dtype) {
+  const size_t exact = exact_logits_bytes(N, d, E);
+  const size_t cert = dtype == 1 ? route_certified_workspace_bytes(N, E) : 0;
+  return exact > cert ? exact : cert;
+}
+
+// Exact fp64 logits of every pair; zeroes `counts` on the way (may be null).
+static hipError_t launch_exact_logits(const RouteArgs& a, hipStream_t st) {
   const int EC = route_chunk(a.E);
   const int Ep = route_padded_experts(a.E);
   double* wt = static_cast<double*>(a.ws);
@@ -284,7 +292,6 @@ hipError_t launch_route(const RouteArgs& a, hipStream_t st) {
     const int blocks = (int)std::min<size_t>((total + 255) / 256, 4096);
     router_weight_to_f64<<<blocks, 256, 0, st>>>(a.w_router, a.dtype, a.E, a.d, Ep, wt);
   }
-  // Token tiles per block: enough expert chunks to keep 4 waves busy.
   const int chunks = (Ep + EC - 1) / EC;
   if (EC == 8) {
     // A single chunk of 8 experts: 4 token tiles per block.
@@ -304,10 +311,24 @@ hipError_t launch_route(const RouteArgs& a, hipStream_t st) {
     logits_f64<16, 4><<<grid, 256, 0, st>>>(a.x, a.dtype, a.N, a.d, a.E, Ep, wt, a.router_bias,
                                              a.logits, a.counts);
   }
-  hipError_t err = hipGetLastError();
+  return hipGetLastError();
+}
+
+hipError_t launch_router_logits(const RouteArgs& a, hipStream_t st) {
+  if (a.N == 0) return hipSuccess;
+  return launch_exact_logits(a, st);
+}
+
+hipError_t launch_route(const RouteArgs& a, hipStream_t st) {
+  if (a.N == 0) {
+    zero_i32<<<1, 256, 0, st>>>(a.counts, a.E);
+    return hipGetLastError();
+  }
+  if (use_certified(a)) return launch_route_certified(a, st);
+  hipError_t err = launch_exact_logits(a, st);
   if (err != hipSuccess) return err;
   const int blocks = (a.N + kSelectTokensPerBlock - 1) / kSelectTokensPerBlock;
-  select_topk<<<blocks, 256, 0, st>>>(a.logits, a.sel_bias, a.N, a.E, a.k, a.G, a.kg,
+  select_topk<<<blocks, kSelectWaves * 64, 0, st>>>(a.logits, a.sel_bias, a.N, a.E, a.k, a.G, a.kg,
                                       a.score_fn, a.topk_idx, a.topk_w, a.counts);
   return hipGetLastError();
 }

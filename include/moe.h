@@ -99,9 +99,16 @@ size_t moe_route_workspace_size(const moe_route_desc* desc);
  *  w_router    [E, d]  dtype       router weight (Linear(d, E).weight)
  *  router_bias [E]     fp32        Linear bias, nullable
  *  sel_bias    [E]     fp32        selection-only bias, nullable
- *  logits      [N, E]  fp32  out   z[t,e] = fp32( fp64 sum over i = 0..d-1, in
+ *  logits      [N, E]  fp32  out   the router logit, defined as
+ *                                  z[t,e] = fp32( fp64 sum over i = 0..d-1, in
  *                                  order, of x[t,i]*w[e,i]; then + router_bias[e]
- *                                  in fp64 ), rounded once to nearest-even
+ *                                  in fp64 ), rounded once to nearest-even.
+ *                                  MOE_F32: every entry is that value.
+ *                                  MOE_BF16: entries of the selected experts (and
+ *                                  of any expert whose rank the selection had to
+ *                                  resolve exactly) are that value; the others
+ *                                  are within 2^-16 |x_t| |w_e| + 2^-22 |z| of it
+ *                                  (selection is decided only on exact values)
  *  topk_idx    [N, k]  int32 out   chosen experts, best first; a token's
  *                                  selection score is sigmoid(z) (SIGMOID_NORM,
  *                                  fp64 then rounded to fp32) or z, plus
@@ -118,6 +125,16 @@ int moe_route(const moe_route_desc* desc, const void* x, const void* w_router,
               const float* router_bias, const float* sel_bias, float* logits,
               int32_t* topk_idx, float* topk_w, int32_t* counts,
               void* ws, size_t ws_bytes, void* stream);
+
+/* Exact router logits of every (token, expert) pair, as defined for moe_route,
+ * with no selection (glossary "How tokens travel between GPUs": the router is
+ * a Linear(d, E) over the hidden state).  x, w_router, router_bias (nullable)
+ * and logits [N, E] fp32 as for moe_route; only num_tokens, hidden,
+ * num_experts and dtype of desc are used beyond validation; ws as for
+ * moe_route (same size query). */
+int moe_router_logits(const moe_route_desc* desc, const void* x, const void* w_router,
+                      const float* router_bias, float* logits, void* ws, size_t ws_bytes,
+                      void* stream);
 
 /* --------------------------------------------------------------- dispatch -- */
 
