@@ -8,8 +8,9 @@ gfx950 kernels; there is no fallback path.  PyTorch only provides device
 memory and streams.
 
 Entry points (same names and argument order as the C ABI):
-``moe_route``, ``moe_dispatch``, ``moe_expert_ffn``, ``moe_combine``,
-``moe_bias_update``, plus the ``*_workspace_size`` queries.
+``moe_route``, ``moe_dispatch``, ``moe_expert_ffn`` (and its stages),
+``moe_expert_ffn_pack_weights``, ``moe_combine``, ``moe_bias_update``, plus the
+``*_workspace_size`` queries.
 """
 
 from __future__ import annotations
@@ -37,8 +38,8 @@ EXPORTS = [
     "moe_route_workspace_size", "moe_route", "moe_router_logits",
     "moe_dispatch_workspace_size", "moe_dispatch",
     "moe_expert_ffn_workspace_size", "moe_expert_ffn", "moe_expert_ffn_plan",
-    "moe_expert_ffn_up", "moe_expert_ffn_down", "moe_combine", "moe_bias_update",
-    "moe_status_string",
+    "moe_expert_ffn_up", "moe_expert_ffn_down", "moe_expert_ffn_pack_weights", "moe_combine",
+    "moe_bias_update", "moe_status_string",
 ]
 
 
@@ -101,6 +102,7 @@ def lib() -> ctypes.CDLL:
             "moe_expert_ffn_plan": ([I32, I32, I32, I32, I32, I32, P, P, SZ, P], I32),
             "moe_expert_ffn_up": ([I32, I32, I32, I32, I32, I32, P, P, P, P, P, SZ, P], I32),
             "moe_expert_ffn_down": ([I32, I32, I32, I32, I32, I32, P, P, P, P, SZ, P], I32),
+            "moe_expert_ffn_pack_weights": ([I32, I32, I32, I32, P, P, P], I32),
             "moe_combine": ([D, P, P, P, P, P, P, P], I32),
             "moe_bias_update": ([I32, I32, I32, P, F32, P, P], I32),
             "moe_status_string": ([I32], ctypes.c_char_p),
@@ -236,6 +238,17 @@ def moe_expert_ffn(num_experts, max_rows, hidden, ffn_hidden, act, dtype, x_rows
     _raise("moe_expert_ffn", st)
 
 
+def moe_expert_ffn_pack_weights(num_experts, rows, cols, dtype, w, w_packed, stream=None):
+    """Pack a bf16 [E, rows, cols] expert weight tensor into ``w_packed``
+    (same size) in the layout the bf16 expert FFN reads (``include/moe.h``)."""
+    dtype = DTYPE[dtype] if isinstance(dtype, str) else int(dtype)
+    dt = TORCH_DTYPE.get(dtype)
+    n = num_experts * rows * cols
+    st = lib().moe_expert_ffn_pack_weights(num_experts, rows, cols, dtype, _ptr(w, "w", dt, n),
+                                           _ptr(w_packed, "w_packed", dt, n), _stream(stream))
+    _raise("moe_expert_ffn_pack_weights", st)
+
+
 def _ws(ws):
     return (_ptr(ws, "ws", None, None, False),
             0 if ws is None else ws.numel() * ws.element_size())
@@ -300,4 +313,4 @@ def moe_bias_update(num_experts, num_tokens, top_k, counts, step, sel_bias, stre
     _raise("moe_bias_update", st)
 
 
-from .layer import MoeBuffers, moe_forward  # noqa: E402,F401  (composition of the calls above)
+from .layer import MoeBuffers, moe_forward, prepare_weights  # noqa: E402,F401  (composition of the calls above)

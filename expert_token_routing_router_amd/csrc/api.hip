@@ -218,6 +218,20 @@ int moe_expert_ffn_down(int32_t num_experts, int32_t max_rows, int32_t hidden,
   return status_of(moe::launch_ffn_down(a, static_cast<hipStream_t>(stream)));
 }
 
+int moe_expert_ffn_pack_weights(int32_t num_experts, int32_t rows, int32_t cols, int32_t dtype,
+                                const void* w, void* w_packed, void* stream) {
+  if (num_experts < 1 || rows < 1 || cols < 1) return MOE_ERR_INVALID_ARG;
+  if (dtype != MOE_F32 && dtype != MOE_BF16) return MOE_ERR_INVALID_ARG;
+  if (dtype != MOE_BF16 || rows % 64 != 0 || cols % 64 != 0) return MOE_ERR_UNSUPPORTED;
+  if (!w || !w_packed || !aligned16(w) || !aligned16(w_packed)) return MOE_ERR_INVALID_ARG;
+  const size_t bytes = (size_t)num_experts * rows * cols * 2;
+  const char* a0 = static_cast<const char*>(w);
+  const char* b0 = static_cast<const char*>(w_packed);
+  if (a0 < b0 + bytes && b0 < a0 + bytes) return MOE_ERR_INVALID_ARG;  // must not overlap
+  return status_of(moe::launch_pack_weights(num_experts, rows, cols, w, w_packed,
+                                            static_cast<hipStream_t>(stream)));
+}
+
 int moe_combine(const moe_route_desc* desc, const void* y_perm, const int32_t* row_of_slot,
                 const float* topk_w, const void* residual, const void* shared_out, void* y,
                 void* stream) {

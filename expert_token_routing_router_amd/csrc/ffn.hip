@@ -12,22 +12,23 @@
 // Both are "A row-major [M,K], B row-major [N,K]" products, K contiguous in
 // both operands, which is the natural operand order of the MFMA units.
 //
-// Scheduling: a prologue kernel turns the per-expert row counts into a prefix
-// of M tiles.  The GEMM grid is sized for the worst case (max_rows/BM + E
-// tiles); block b is remapped so that consecutive logical tiles run on the
-// same XCD (the hardware deals blocks round-robin over the 8 XCDs), logical
-// tiles walk the N tiles of one M tile first (A tile reused from that XCD's
-// L2), and blocks past the real tile count exit at once.
+// Scheduling: a prologue kernel turns the per-expert row counts into a list
+// of row tiles (each expert split into equal tiles of at most BM rows).  The
+// GEMM grid is sized for the worst case (max_rows/BM + E tiles); block b is
+// remapped so that consecutive logical tiles run on the same XCD (the
+// hardware deals blocks round-robin over the 8 XCDs), logical tiles walk the N
+// tiles of one row tile first (A rows reused from that XCD's L2), and blocks
+// past the real tile count exit at once.
 //
-// bf16 kernel: 256 threads (2x2 waves), tile BM x BN x 64, each wave owns
-// (BM/2) x (BN/2) as 32x32 MFMA blocks (v_mfma_f32_32x32x16_bf16).  Tiles go
-// global -> registers -> LDS (double buffered), the next K tile's global loads
-// in flight while the current one is multiplied.  LDS rows are 64 bf16 = eight
-// 16-byte chunks; chunk c of row r is stored at c ^ (r & 7) so the 16-byte
-// fragment reads of 8 consecutive rows hit 8 different bank groups.
+// bf16 kernel (grouped_gemm_bf16): 8 waves, tiles of up to 320 rows, operands
+// streamed global -> LDS by direct DMA into a multi-stage ring, MFMA
+// v_mfma_f32_32x32x16_bf16, epilogue straight from registers.  Details at the
+// kernel.
 //
-// fp32 kernel (fp32 workloads): same schedule, v_mfma_f32_16x16x4_f32, 64x64
-// tiles, K step 16; plain padded LDS rows.
+// fp32 kernel (fp32 workloads): v_mfma_f32_16x16x4_f32, 64x64 tiles, K step
+// 16, plain padded LDS rows.
+#include <algorithm>
+
 #include "device.h"
 #include "kernels.h"
 
@@ -41,12 +42,13 @@ enum { ACT_RELU = 0, ACT_GELU = 1, ACT_SWIGLU = 2, ACT_NONE = 3 };
 
 // erf(x) by Abramowitz & Stegun, Handbook of Mathematical Functions, formula
 // 7.1.26: for x >= 0, erf(x) = 1 - (a1 t + a2 t^2 + a3 t^3 + a4 t^4 + a5 t^5)
-// exp(-x^2) with t = 1 / (1 + p x); absolute error <= 1.5e-7 (the fp32
-// evaluation adds a few ulp), far below the bf16 rounding H goes through.
+// exp(-x^2) with t = 1 / (1 + p x); absolute error <= 1.5e-7.  t comes from
+// v_rcp_f32 (within 2 ulp on gfx950) and the fp32 evaluation adds a few ulp:
+// all far below the bf16 rounding H goes through.
 // erf is odd, so the sign is restored at the end.
 __device__ __forceinline__ float erf_as7126(float x) {
   const float ax = fabsf(x);
-  const float t = __frcp_rn(fmaf(0.3275911f, ax, 1.0f));
+  const float t = __builtin_amdgcn_rcpf(fmaf(0.3275911f, ax, 1.0f));
   float poly = fmaf(1.061405429f, t, -1.453152027f);
   poly = fmaf(poly, t, 1.421413741f);
   poly = fmaf(poly, t, -0.284496736f);
@@ -62,24 +64,29 @@ __device__ __forceinline__ float apply_act(float u, int act) {
   return u;
 }
 
-__device__ __forceinline__ float silu(float g) { return g / (1.f + __expf(-g)); }
+// g sigmoid(g); v_rcp_f32 (within 2 ulp) in place of an IEEE divide.
+__device__ __forceinline__ float silu(float g) { return g * __builtin_amdgcn_rcpf(1.f + __expf(-g)); }
 
 // ------------------------------------------------------------- tile plan ---
 
-// One block of 1024 threads (E <= 1024): expert e owns ceil(rows_e / BM) row
-// tiles; tile q of the batch is tiles[q] = {e, first row, row end, 0}, and
-// *count = number of tiles.  Rows are clamped to max_rows.
+// One block of 1024 threads (E <= 1024): expert e owns n_e = ceil(rows_e / BM)
+// row tiles of equal height, rounded up to whole 32-row MFMA fragments
+// (chunk_e = 32 ceil(ceil(rows_e / n_e) / 32) <= BM; since (n_e - 1) BM <
+// rows_e, no tile is empty).  Tile q of the batch is tiles[q] = {e, first
+// row, row end, 0}, and *count = number of tiles.  Rows are clamped to
+// max_rows.
 __global__ __launch_bounds__(1024) void ffn_plan_tiles(const int32_t* __restrict__ offsets,
                                                        int E, int BM, int max_rows,
                                                        int4* __restrict__ tiles,
                                                        int32_t* __restrict__ count) {
   __shared__ int32_t s[1024];
   const int e = threadIdx.x;
-  int32_t lo = 0, hi = 0, n = 0;
+  int32_t lo = 0, hi = 0, n = 0, chunk = BM;
   if (e < E) {
     lo = min(offsets[e], max_rows);
     hi = min(offsets[e + 1], max_rows);
     n = hi > lo ? (hi - lo + BM - 1) / BM : 0;
+    if (n > 0) chunk = ((hi - lo + n - 1) / n + 31) / 32 * 32;
   }
   s[e] = n;
   __syncthreads();
@@ -91,8 +98,8 @@ __global__ __launch_bounds__(1024) void ffn_plan_tiles(const int32_t* __restrict
   }
   const int32_t start = s[e] - n;
   for (int q = 0; q < n; ++q) {
-    const int32_t r0 = lo + q * BM;
-    tiles[start + q] = make_int4(e, r0, min(hi, r0 + BM), 0);
+    const int32_t r0 = lo + q * chunk;
+    tiles[start + q] = make_int4(e, r0, min(hi, r0 + chunk), 0);
   }
   if (e == E - 1) *count = s[e];
 }
@@ -113,15 +120,15 @@ __device__ __forceinline__ int xcd_logical(int b, int total) {
 
 // ------------------------------------------------------------- bf16 MFMA ---
 
-// LDS rows hold BK bf16 (BK = 32: 64 bytes = four 16-byte chunks).  Chunk c of row r
-// lives at c ^ swz(r): consecutive rows reading the same logical chunk then hit
-// distinct bank groups for 8- and for 16-lane LDS phases.
+// LDS rows hold 32 bf16 (64 bytes = four 16-byte chunks).  Chunk c of row r
+// lives at c ^ swz4(r): consecutive rows reading the same logical chunk then
+// hit distinct bank groups for 8- and for 16-lane LDS phases.  The pattern
+// depends on row bits 1-3 only, so rows 16 or 32 apart share it.
 __device__ __forceinline__ int swz4(int r) { return ((r >> 1) ^ (r >> 2)) & 3; }
-// Same for 128-byte rows (64 bf16, eight chunks).  Both depend on the low four
-// row bits only, so rows 16 or 32 apart share the pattern.
-__device__ __forceinline__ int swz8(int r) { return (r ^ ((r >> 3) & 1)) & 7; }
-template <int BK>
-__device__ __forceinline__ int swz(int r) { return BK == 32 ? swz4(r) : swz8(r); }
+
+// Rows per slab of packed weights (rows = N of the GEMM, a multiple of 64): a
+// slab's K stage is one contiguous run of SR * 64 bytes.
+__host__ __device__ __forceinline__ int packed_slab_rows(int N) { return N % 256 == 0 ? 256 : 64; }
 
 typedef __attribute__((address_space(3))) void* lds_ptr_t;
 
@@ -149,42 +156,60 @@ __device__ __forceinline__ void ring_barrier() {
 }
 
 // Grouped GEMM C[rows, N] = act(A[rows, K] B_e[N, K]^T) for bf16.
-// Block tile 256 (rows) x BN (columns), K step 32, 4 waves as 2 x 2, wave tile
-// 128 x BN/2.  DUAL (SwiGLU): the B stage holds BN rows of W1 (gate) and BN
-// rows of W3 (up); the wave keeps both accumulators and combines them in the
-// epilogue.  MFMA v_mfma_f32_32x32x16_bf16 with the weight fragment as the
-// first operand, so a lane's accumulator holds 4 consecutive output columns of
-// one row.  Stages arrive by global_load_lds_dwordx4 (16 bytes per lane,
-// straight into LDS) into a 4-deep ring; the XOR swizzle is applied by the
-// choice of source address.
-template <int BM, int BN, int BK, int WAVES, int ACT>
-__global__ __launch_bounds__(WAVES * 64, 1) __attribute__((amdgpu_waves_per_eu(WAVES / 4, WAVES / 4)))
+//
+// Block: 8 waves, tile of up to BM = 320 rows x BN columns, K step 32.  The
+// waves form 2 (along M) x 4 (along N); wave (wm, wn) owns the 32-row
+// fragments f = 2i + wm (i < 5) of the tile -- alternate fragments, so a
+// short tile leaves the two M waves (which share a SIMD) equally loaded -- and
+// the output columns [wn*BN/4, (wn+1)*BN/4).  Fragments holding no row of the
+// tile are skipped: each number of live fragments has its own copy of the
+// accumulators, K loop and epilogue, and the wave runs the copy that matches
+// its share.  320-row tiles take a whole expert of up to 320 rows (one tile
+// per expert at capacity factor 1.25 of 256 rows per expert); 160 x 64 wave
+// tiles (160 accumulators) leave room for two waves per SIMD.
+//
+// MFMA v_mfma_f32_32x32x16_bf16 with the weight fragment as the first operand,
+// so a lane's accumulator holds 4 consecutive output columns of one row.
+// DUAL (SwiGLU): the B stage holds BN rows of W1 (gate) and BN rows of W3
+// (up); the wave keeps both accumulators and combines them in the epilogue.
+//
+// Operands reach LDS by global_load_lds_dwordx4 (16 bytes per lane, 1 KB =
+// 16 rows of 64 bytes per instruction) into a ring of NS stages; waves 0-3
+// fetch the A rows (XOR swizzle applied through the choice of source address),
+// waves 4-7 the weight rows.  Weights come packed (moe_expert_ffn_pack_weights)
+// so that one stage of a slab of 64 or 256 weight rows is one contiguous run
+// already in LDS order: the weight stream reads long sequential runs of HBM.
+// The epilogue converts to bf16 in registers (v_cvt_pk_bf16_f32), swaps
+// half-rows between lanes l and l+32 (v_permlane32_swap) so each lane owns 8
+// consecutive columns, and stores 16 bytes per lane straight to global memory.
+constexpr int kGemmBM = 320, kGemmWaves = 8;
+
+template <int BN, int ACT>
+__global__ __launch_bounds__(kGemmWaves * 64, 1) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void grouped_gemm_bf16(
     const bf16_t* __restrict__ A, const bf16_t* __restrict__ B, const bf16_t* __restrict__ B2,
     bf16_t* __restrict__ C, int K, int N, const int4* __restrict__ tiles,
     const int32_t* __restrict__ tile_count, int n_tiles) {
   constexpr bool DUAL = ACT == ACT_SWIGLU;
-  constexpr int RB = BK * 2;                          // bytes per staged row
-  constexpr int CH = BK / 8;                          // 16-byte chunks per row
-  constexpr int RPL = 1024 / RB;                      // rows per 1-KB load
-  constexpr int KK = BK / 16;                         // MFMA K steps per stage
-  constexpr int BROWS = DUAL ? 2 * BN : BN;           // weight rows per stage
-  constexpr int ROWS = BM + BROWS;                    // rows per stage
-  constexpr int STAGE = ROWS * RB;                    // bytes per stage
+  constexpr int BM = kGemmBM, BK = 32, RB = BK * 2;  // RB: bytes per staged row
+  constexpr int CH = BK / 8;                         // 16-byte chunks per row
+  constexpr int RPL = 1024 / RB;                     // rows per 1-KB load
+  constexpr int KK = BK / 16;                        // MFMA K steps per stage
+  constexpr int BROWS = DUAL ? 2 * BN : BN;          // weight rows per stage
+  constexpr int STAGE = (BM + BROWS) * RB;           // bytes per stage
   constexpr int NS = kLdsBytes / STAGE < 6 ? kLdsBytes / STAGE : 6;  // ring depth
-  constexpr int LOADS = ROWS / RPL / WAVES;           // 1 KB loads per wave per stage
-  static_assert(NS >= 3, "the ring needs three stages");
-  static_assert(KK % 2 == 0, "register sets alternate per K step");
-  constexpr int WGN = WAVES / 2;                      // waves along N (2 along M)
-  constexpr int WM = BM / 2, WN = BN / WGN;           // wave tile (rows x output cols)
-  constexpr int FM = WM / 32, FN = WN / 32;
+  constexpr int LA = BM / RPL / 4;                   // loads per stage, A waves (0-3)
+  constexpr int LB = BROWS / RPL / 4;                // loads per stage, B waves (4-7)
+  constexpr int LMAX = LA > LB ? LA : LB;
+  constexpr int WN = BN / 4;                         // output columns per wave
+  constexpr int FM = BM / 64, FN = WN / 32;          // fragments per wave
   constexpr int FN2 = DUAL ? FN : 1;
-  constexpr int EPI_ROW = WN * 2 + 16;                // epilogue LDS row bytes (padded)
-  constexpr int EPI = WAVES * WM * EPI_ROW;
-  constexpr int SMEM = NS * STAGE > EPI ? NS * STAGE : EPI;
-  static_assert(ROWS % (WAVES * RPL) == 0, "stage rows must split evenly over the waves");
+  static_assert(NS >= 3, "the ring needs three stages");
+  static_assert(KK == 2, "register sets alternate per K step");
+  static_assert(BM % (4 * RPL) == 0 && BROWS % (4 * RPL) == 0, "loads split over 4 waves");
   static_assert(WN % 32 == 0, "wave tile must be whole 32-column MFMA blocks");
-  __shared__ __attribute__((aligned(1024))) char smem[SMEM];
+  static_assert((NS - 1) * LMAX < 64, "loads in flight must fit the 6-bit vmcnt");
+  __shared__ __attribute__((aligned(1024))) char smem[NS * STAGE];
 
   const int logical = xcd_logical(blockIdx.x, *tile_count * n_tiles);
   if (logical < 0) return;
@@ -193,61 +218,89 @@ void grouped_gemm_bf16(
   const int e = tile.x, r0 = tile.y, r1 = tile.z;
   const int n0 = nt * BN;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int wm = wave / WGN, wn = wave % WGN;
+  const int wm = wave / 4, wn = wave % 4;
+  const bool a_wave = wave < 4;
+  const int grp = wave % 4;
 
-  // Per-lane source pointers of this wave's LOADS 1-KB loads (16 rows each).
-  const bf16_t* src[LOADS];
+  // Per-lane source pointers of this wave's loads (16 stage rows each) and the
+  // element step from one K stage to the next: BK along an A row, one slab
+  // stage (SR * BK elements) in the packed weights.
+  const bf16_t* src[LMAX];
+  int ldst;  // LDS byte offset (within a stage) of this wave's first load
+  size_t kstep;
+  if (a_wave) {
+    ldst = grp * LA * 1024;
+    kstep = BK;
 #pragma unroll
-  for (int i = 0; i < LOADS; ++i) {
-    const int q = wave * LOADS + i;           // load index within the stage
-    const int sr = q * RPL + lane / CH;       // stage row
-    const int c = (lane % CH) ^ swz<BK>(sr);  // logical chunk this lane fetches
-    if (sr < BM) {
-      const int row = min(r0 + sr, r1 - 1);   // rows past the tile: computed, never stored
+    for (int i = 0; i < LMAX; ++i) {
+      const int sr = (grp * LA + (i < LA ? i : 0)) * RPL + lane / CH;  // stage row
+      const int c = (lane % CH) ^ swz4(sr);                             // logical chunk
+      const int row = min(r0 + sr, r1 - 1);  // rows past the tile: fetched, never used
       src[i] = A + (size_t)row * K + c * 8;
-    } else {
-      const int br = sr - BM;
+    }
+  } else {
+    ldst = BM * RB + grp * LB * 1024;
+    const int SR = packed_slab_rows(N);
+    kstep = (size_t)SR * BK;
+#pragma unroll
+    for (int i = 0; i < LMAX; ++i) {
+      const int br = (grp * LB + (i < LB ? i : 0)) * RPL;  // first weight row in the stage
       const bf16_t* W = (DUAL && br >= BN) ? B2 : B;
-      const int n = min(n0 + (DUAL ? br % BN : br), N - 1);
-      src[i] = W + ((size_t)e * N + n) * K + c * 8;
+      const int n = min(n0 + (DUAL ? br % BN : br), N - RPL);  // 16-row group, clamped
+      src[i] = W + ((size_t)e * (N / SR) + n / SR) * (size_t)(K / BK) * SR * BK +
+               (n % SR) / RPL * 512 + lane * 8;
     }
   }
+  const int nl = a_wave ? LA : LB;
+
   // LDS byte offsets (within a stage) of this lane's MFMA fragments; the
   // chunk index of K step kk is (kk * 2 + lane / 32) ^ swizzle(row).
   int xoff[FM], woff[FN], woff2[FN2];
 #pragma unroll
-  for (int i = 0; i < FM; ++i) xoff[i] = (wm * WM + i * 32 + (lane & 31)) * RB;
+  for (int i = 0; i < FM; ++i) xoff[i] = ((2 * i + wm) * 32 + (lane & 31)) * RB;
 #pragma unroll
   for (int j = 0; j < FN; ++j) {
     woff[j] = (BM + wn * WN + j * 32 + (lane & 31)) * RB;
     if constexpr (DUAL) woff2[j] = (BM + BN + wn * WN + j * 32 + (lane & 31)) * RB;
   }
-  // Fragment rows differ from lane&31 by multiples of 32 (BM and BN are), and
+  // Fragment rows differ from lane&31 by multiples of 32 (BM is one too), and
   // the swizzle only looks at the low four row bits.
-  const int sw = swz<BK>(lane & 31);
+  const int sw = swz4(lane & 31);
+
+  // Live fragments of this wave: the tile has ceil(rows / 32) fragments,
+  // numbered so that this wave owns wm, wm + 2, ...
+  const int nf = (r1 - r0 + 31) / 32;
+  const int fa = min(FM, max(0, (nf - wm + 1) / 2));
+
+  // Two register sets, one K step (16) each: set 0 holds step 0 of a stage,
+  // set 1 step 1.  Each set is refilled while the other one feeds the MFMAs.
+  bf16x8_t xf0[FM], wf0[FN], vf0[FN2];
+  bf16x8_t xf1[FM], wf1[FN], vf1[FN2];
+  const int ktiles = K / BK;
 
   // Issue the global->LDS loads of K tile kt_ into ring slot slot_.
 #define MOE_RING_ISSUE(kt_, slot_)                                                         \
   do {                                                                                     \
-    char* base_ = smem + (slot_) * STAGE + wave * LOADS * 1024;                            \
-    _Pragma("unroll") for (int i = 0; i < LOADS; ++i)                                      \
-        __builtin_amdgcn_global_load_lds((void*)(src[i] + (kt_) * BK),                     \
+    char* base_ = smem + (slot_) * STAGE + ldst;                                           \
+    _Pragma("unroll") for (int i = 0; i < LMAX; ++i) if (LA == LB || i < nl)               \
+        __builtin_amdgcn_global_load_lds((void*)(src[i] + (size_t)(kt_) * kstep),          \
                                          (lds_ptr_t)(base_ + i * 1024), 16, 0, 0);         \
   } while (0)
-  // Read the fragments of K step kk_ of ring slot slot_ into set S.
-#define MOE_LOAD_KK(slot_, kk_, S)                                                         \
+  // Read the fragments of K step kk_ of ring slot slot_ into set S (FA_ live
+  // row fragments).
+#define MOE_LOAD_KK(FA_, slot_, kk_, S)                                                    \
   do {                                                                                     \
     const char* st_ = smem + (slot_) * STAGE + ((((kk_) * 2 + (lane >> 5)) ^ sw) << 4);     \
-    _Pragma("unroll") for (int i = 0; i < FM; ++i)                                         \
+    _Pragma("unroll") for (int i = 0; i < (FA_); ++i)                                      \
         xf##S[i] = *reinterpret_cast<const bf16x8_t*>(st_ + xoff[i]);                      \
     _Pragma("unroll") for (int j = 0; j < FN; ++j) {                                       \
       wf##S[j] = *reinterpret_cast<const bf16x8_t*>(st_ + woff[j]);                        \
       if constexpr (DUAL) vf##S[j] = *reinterpret_cast<const bf16x8_t*>(st_ + woff2[j]);   \
     }                                                                                      \
   } while (0)
-#define MOE_MFMA_KK(S)                                                                     \
+#define MOE_MFMA_KK(FA_, S)                                                                \
   do {                                                                                     \
-    _Pragma("unroll") for (int i = 0; i < FM; ++i)                                         \
+    _Pragma("unroll") for (int i = 0; i < (FA_); ++i)                                      \
     _Pragma("unroll") for (int j = 0; j < FN; ++j) {                                       \
       acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(wf##S[j], xf##S[i], acc[i][j],   \
                                                           0, 0, 0);                        \
@@ -257,99 +310,141 @@ void grouped_gemm_bf16(
     }                                                                                      \
   } while (0)
   // Wait until the next stage's loads have landed in every wave: at most
-  // `later` younger stages may still be in flight (vmcnt counts 1-KB loads).
+  // `later_` younger stages of this wave may still be in flight (vmcnt counts
+  // this wave's 1-KB loads, nl per stage).
 #define MOE_WAIT_STAGE(later_)                                                             \
   do {                                                                                     \
-    switch (later_) {                                                                      \
-      case 0: wait_vmcnt<0>(); break;                                                      \
-      case 1: wait_vmcnt<LOADS>(); break;                                                  \
-      case 2: wait_vmcnt<2 * LOADS>(); break;                                              \
-      case 3: wait_vmcnt<3 * LOADS>(); break;                                              \
-      default: wait_vmcnt<4 * LOADS>(); break;                                             \
+    if (a_wave) {                                                                          \
+      switch (later_) {                                                                    \
+        case 0: wait_vmcnt<0>(); break;                                                    \
+        case 1: wait_vmcnt<LA>(); break;                                                   \
+        case 2: wait_vmcnt<2 * LA>(); break;                                               \
+        default: wait_vmcnt<3 * LA>(); break;                                              \
+      }                                                                                    \
+    } else {                                                                               \
+      switch (later_) {                                                                    \
+        case 0: wait_vmcnt<0>(); break;                                                    \
+        case 1: wait_vmcnt<LB>(); break;                                                   \
+        case 2: wait_vmcnt<2 * LB>(); break;                                               \
+        default: wait_vmcnt<3 * LB>(); break;                                              \
+      }                                                                                    \
     }                                                                                      \
     ring_barrier();                                                                        \
   } while (0)
+  // The whole K loop for FA_ live row fragments.  Every copy issues the same
+  // loads and barriers; only the LDS reads and MFMAs differ.
+#define MOE_K_LOOP(FA_)                                                                    \
+  do {                                                                                     \
+    _Pragma("unroll") for (int i = 0; i < (FA_); ++i)                                      \
+    _Pragma("unroll") for (int j = 0; j < FN; ++j) {                                       \
+      acc[i][j] = floatx16{};                                                              \
+      if constexpr (DUAL) acc2[i][j] = floatx16{};                                         \
+    }                                                                                      \
+    _Pragma("unroll") for (int s = 0; s < NS - 1; ++s) if (s < ktiles) MOE_RING_ISSUE(s, s); \
+    MOE_WAIT_STAGE(min(NS - 2, ktiles - 1));                                               \
+    MOE_LOAD_KK(FA_, 0, 0, 0);                                                             \
+    for (int kt = 0; kt < ktiles; ++kt) {                                                  \
+      const int slot = kt % NS;                                                            \
+      MOE_LOAD_KK(FA_, slot, 1, 1);                                                        \
+      MOE_MFMA_KK(FA_, 0);                                                                 \
+      if (kt + 1 < ktiles) {                                                               \
+        /* Stage kt+1 visible to all waves; every wave is past its reads of  */            \
+        /* stage kt-1, so that slot can be refilled.                          */            \
+        MOE_WAIT_STAGE(min(NS - 3, ktiles - kt - 2));                                      \
+        if (kt + NS - 1 < ktiles) MOE_RING_ISSUE(kt + NS - 1, (kt + NS - 1) % NS);         \
+        MOE_LOAD_KK(FA_, (kt + 1) % NS, 0, 0);                                             \
+      }                                                                                    \
+      MOE_MFMA_KK(FA_, 1);                                                                 \
+    }                                                                                      \
+  } while (0)
 
-  floatx16 acc[FM][FN];
-  floatx16 acc2[DUAL ? FM : 1][FN2];
-#pragma unroll
-  for (int i = 0; i < FM; ++i)
-#pragma unroll
-    for (int j = 0; j < FN; ++j) {
-      acc[i][j] = floatx16{};
-      if constexpr (DUAL) acc2[i][j] = floatx16{};
-    }
-  // Two register sets, one K step (16) each: set 0 holds step 0 of a tile,
-  // set 1 step 1.  Each set is refilled while the other one feeds the MFMAs.
-  bf16x8_t xf0[FM], wf0[FN], vf0[FN2];
-  bf16x8_t xf1[FM], wf1[FN], vf1[FN2];
+  // Epilogue: activation, bf16 pairs, then a half-row swap between lanes l
+  // and l+32.  Before it, lane l (row l&31) holds columns 8g + 4(l>>5) + 0..3
+  // for g = 0..3; after swapping g = 2p+1 of lane l with g = 2p of lane l+32,
+  // lane l holds columns 16p + 0..7 and lane l+32 columns 16p + 8..15.
+#define MOE_EPILOGUE(FA_)                                                                  \
+  do {                                                                                     \
+    _Pragma("unroll") for (int i = 0; i < (FA_); ++i) {                                    \
+      const int row = r0 + (2 * i + wm) * 32 + (lane & 31);                                \
+      _Pragma("unroll") for (int j = 0; j < FN; ++j)                                       \
+      _Pragma("unroll") for (int p = 0; p < 2; ++p) {                                      \
+        float o[8];                                                                        \
+        _Pragma("unroll") for (int u = 0; u < 8; ++u) {                                    \
+          const int q = 8 * p + u; /* accumulator element: g = 2p + u/4 */                 \
+          if constexpr (DUAL) o[u] = silu(acc[i][j][q]) * acc2[i][j][q];                   \
+          else o[u] = apply_act(acc[i][j][q], ACT);                                        \
+        }                                                                                  \
+        const uint32_t lo0 = pack_bf16x2(o[0], o[1]), lo1 = pack_bf16x2(o[2], o[3]);        \
+        const uint32_t hi0 = pack_bf16x2(o[4], o[5]), hi1 = pack_bf16x2(o[6], o[7]);        \
+        const auto s0 = __builtin_amdgcn_permlane32_swap(lo0, hi0, false, false);          \
+        const auto s1 = __builtin_amdgcn_permlane32_swap(lo1, hi1, false, false);          \
+        const int col = n0 + wn * WN + j * 32 + 16 * p + 8 * (lane >> 5);                  \
+        if (row < r1 && col < N) {                                                         \
+          const u32x4 v = {s0[0], s1[0], s0[1], s1[1]};                                    \
+          *reinterpret_cast<u32x4*>(C + (size_t)row * N + col) = v;                        \
+        }                                                                                  \
+      }                                                                                    \
+    }                                                                                      \
+  } while (0)
+  // One self-contained copy (accumulators, K loop, epilogue) per number of
+  // live fragments, so no accumulator value crosses from one copy to another.
+#define MOE_TILE(FA_)                                                                      \
+  do {                                                                                     \
+    floatx16 acc[(FA_) > 0 ? (FA_) : 1][FN];                                               \
+    floatx16 acc2[DUAL && (FA_) > 0 ? (FA_) : 1][FN2];                                     \
+    MOE_K_LOOP(FA_);                                                                       \
+    MOE_EPILOGUE(FA_);                                                                     \
+  } while (0)
 
-  const int ktiles = K / BK;
-#pragma unroll
-  for (int s = 0; s < NS - 1; ++s)
-    if (s < ktiles) MOE_RING_ISSUE(s, s);
-  MOE_WAIT_STAGE(min(NS - 2, ktiles - 1));
-  MOE_LOAD_KK(0, 0, 0);
-  for (int kt = 0; kt < ktiles; ++kt) {
-    const int slot = kt % NS;
-#pragma unroll
-    for (int kk = 0; kk < KK; kk += 2) {
-      MOE_LOAD_KK(slot, kk + 1, 1);
-      MOE_MFMA_KK(0);
-      if (kk + 2 < KK) {
-        MOE_LOAD_KK(slot, kk + 2, 0);
-      } else if (kt + 1 < ktiles) {
-        // Tile kt+1 visible to all waves; every wave is past its reads of
-        // tile kt-1, so that slot can be refilled.
-        MOE_WAIT_STAGE(min(NS - 3, ktiles - kt - 2));
-        if (kt + NS - 1 < ktiles) MOE_RING_ISSUE(kt + NS - 1, (kt + NS - 1) % NS);
-        MOE_LOAD_KK((kt + 1) % NS, 0, 0);
-      }
-      MOE_MFMA_KK(1);
-    }
+  static_assert(FM == 5, "one copy per live-fragment count 0..5");
+  switch (fa) {
+    case 0: MOE_TILE(0); break;
+    case 1: MOE_TILE(1); break;
+    case 2: MOE_TILE(2); break;
+    case 3: MOE_TILE(3); break;
+    case 4: MOE_TILE(4); break;
+    default: MOE_TILE(5); break;
   }
+#undef MOE_TILE
+#undef MOE_EPILOGUE
+#undef MOE_K_LOOP
 #undef MOE_LOAD_KK
 #undef MOE_MFMA_KK
 #undef MOE_WAIT_STAGE
 #undef MOE_RING_ISSUE
+}
 
-  // Epilogue: activation, bf16, through LDS to 16-byte row stores.
-  ring_barrier();
-  char* ep = smem + wave * WM * EPI_ROW;
-#pragma unroll
-  for (int i = 0; i < FM; ++i)
-#pragma unroll
-    for (int j = 0; j < FN; ++j)
-#pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        float o[4];
-#pragma unroll
-        for (int u = 0; u < 4; ++u) {
-          const float a = acc[i][j][4 * g + u];
-          if constexpr (DUAL) o[u] = silu(a) * acc2[i][j][4 * g + u];
-          else o[u] = apply_act(a, ACT);
-        }
-        const int m = i * 32 + (lane & 31);
-        const int n = j * 32 + 8 * g + 4 * (lane >> 5);
-        uint2 packed = make_uint2(pack_bf16x2(o[0], o[1]), pack_bf16x2(o[2], o[3]));
-        *reinterpret_cast<uint2*>(ep + m * EPI_ROW + n * 2) = packed;
-      }
-  __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): this wave's LDS writes are done
-  __builtin_amdgcn_wave_barrier();
-  constexpr int CPR = WN / 8;          // 16-byte chunks per output row
-  constexpr int RPI = 64 / CPR;        // rows per wave instruction
-  const int row_base = r0 + wm * WM;
-  const int col_base = n0 + wn * WN;
-#pragma unroll 4
-  for (int it = 0; it < WM / RPI; ++it) {
-    const int m = it * RPI + lane / CPR;
-    const int ch = lane % CPR;
-    const int row = row_base + m, col = col_base + ch * 8;
-    if (row < r1 && col < N) {
-      const u32x4 v = *reinterpret_cast<const u32x4*>(ep + m * EPI_ROW + ch * 16);
-      *reinterpret_cast<u32x4*>(C + (size_t)row * N + col) = v;
-    }
+// Weight packing for the bf16 kernel: W [E, N, K] row-major -> slabs of SR
+// rows (SR = packed_slab_rows(N)); slab (e, s) holds K/32 stages of SR*32
+// elements, each stage SR/16 blocks of 1 KB laid out exactly as
+// grouped_gemm_bf16 stages 16 weight rows in LDS: 16-byte position L of block
+// g holds row 16g + L/4 of the slab, logical chunk (L % 4) ^ swz4(L / 4).  One
+// thread per 16-byte output chunk, so the writes are contiguous.
+__global__ __launch_bounds__(256) void pack_weights_bf16(const bf16_t* __restrict__ w,
+                                                         bf16_t* __restrict__ wp, int N, int K,
+                                                         size_t chunks) {
+  const int SR = packed_slab_rows(N), kts = K / 32;
+  const size_t stride = (size_t)gridDim.x * blockDim.x;
+  for (size_t q = (size_t)blockIdx.x * blockDim.x + threadIdx.x; q < chunks; q += stride) {
+    const int L = (int)(q % 64);
+    const size_t blk = q / 64;                 // 1-KB block index
+    const int g = (int)(blk % (SR / 16));      // 16-row group in the slab stage
+    const size_t st = blk / (SR / 16);         // slab stage: (e * N/SR + s) * kts + kt
+    const int kt = (int)(st % kts);
+    const size_t es = st / kts;                // e * (N / SR) + s: slabs are contiguous rows
+    const int r = L / 4, c = (L % 4) ^ swz4(r);
+    const size_t row = es * SR + g * 16 + r;
+    *reinterpret_cast<u32x4*>(wp + q * 8) =
+        *reinterpret_cast<const u32x4*>(w + row * K + kt * 32 + c * 8);
   }
+}
+
+hipError_t launch_pack_weights(int E, int N, int K, const void* w, void* wp, hipStream_t st) {
+  const size_t chunks = (size_t)E * N * K / 8;
+  const int blocks = (int)std::min<size_t>((chunks + 255) / 256, 8192);
+  pack_weights_bf16<<<blocks, 256, 0, st>>>(static_cast<const bf16_t*>(w),
+                                            static_cast<bf16_t*>(wp), N, K, chunks);
+  return hipGetLastError();
 }
 
 // ------------------------------------------------------------- fp32 MFMA ---
@@ -426,11 +521,11 @@ __global__ __launch_bounds__(256) void grouped_gemm_f32(
 
 // ---------------------------------------------------------------- launch ---
 
-constexpr int kBf16BM = 256, kBf16Waves = 8, kF32BM = 64, kF32BN = 64;
+constexpr int kF32BM = 64, kF32BN = 64;
 
 static size_t align256(size_t x) { return (x + 255) / 256 * 256; }
 
-static int ffn_bm(int dtype) { return dtype == 0 ? kF32BM : kBf16BM; }
+static int ffn_bm(int dtype) { return dtype == 0 ? kF32BM : kGemmBM; }
 
 // Upper bound of row tiles: every expert may end in a partial tile.
 static int max_m_tiles(int max_rows, int BM, int E) { return (max_rows + BM - 1) / BM + E; }
@@ -466,12 +561,13 @@ hipError_t launch_ffn_plan(const FfnArgs& a, hipStream_t st) {
   return hipGetLastError();
 }
 
-template <int BN, int BK, int ACT>
+template <int BN, int ACT>
 static void launch_bf16(const bf16_t* A, const bf16_t* B, const bf16_t* B2, bf16_t* C, int K,
                         int N, const FfnArgs& a, hipStream_t st) {
   const int nt = (N + BN - 1) / BN;
-  const int g = grid_of(max_m_tiles(a.max_rows, kBf16BM, a.E), nt);
-  grouped_gemm_bf16<kBf16BM, BN, BK, kBf16Waves, ACT><<<g, kBf16Waves * 64, 0, st>>>(A, B, B2, C, K, N, ffn_tiles(a), ffn_count(a), nt);
+  const int g = grid_of(max_m_tiles(a.max_rows, kGemmBM, a.E), nt);
+  grouped_gemm_bf16<BN, ACT><<<g, kGemmWaves * 64, 0, st>>>(A, B, B2, C, K, N, ffn_tiles(a),
+                                                             ffn_count(a), nt);
 }
 
 template <int ACT>
@@ -496,13 +592,13 @@ hipError_t launch_ffn_up(const FfnArgs& a, hipStream_t st) {
     auto W1 = static_cast<const bf16_t*>(a.w1);
     auto W3 = static_cast<const bf16_t*>(a.w3);
     auto H = static_cast<bf16_t*>(ffn_hidden_buf(a));
-    if (a.act == ACT_SWIGLU) launch_bf16<128, 32, ACT_SWIGLU>(X, W1, W3, H, a.d, a.h, a, st);
+    if (a.act == ACT_SWIGLU) launch_bf16<128, ACT_SWIGLU>(X, W1, W3, H, a.d, a.h, a, st);
     else if (a.h >= 2048) {
-      if (a.act == ACT_RELU) launch_bf16<256, 32, ACT_RELU>(X, W1, nullptr, H, a.d, a.h, a, st);
-      else launch_bf16<256, 32, ACT_GELU>(X, W1, nullptr, H, a.d, a.h, a, st);
+      if (a.act == ACT_RELU) launch_bf16<256, ACT_RELU>(X, W1, nullptr, H, a.d, a.h, a, st);
+      else launch_bf16<256, ACT_GELU>(X, W1, nullptr, H, a.d, a.h, a, st);
     } else {
-      if (a.act == ACT_RELU) launch_bf16<128, 32, ACT_RELU>(X, W1, nullptr, H, a.d, a.h, a, st);
-      else launch_bf16<128, 32, ACT_GELU>(X, W1, nullptr, H, a.d, a.h, a, st);
+      if (a.act == ACT_RELU) launch_bf16<128, ACT_RELU>(X, W1, nullptr, H, a.d, a.h, a, st);
+      else launch_bf16<128, ACT_GELU>(X, W1, nullptr, H, a.d, a.h, a, st);
     }
   }
   return hipGetLastError();
@@ -517,8 +613,8 @@ hipError_t launch_ffn_down(const FfnArgs& a, hipStream_t st) {
     auto H = static_cast<const bf16_t*>(ffn_hidden_buf(a));
     auto W2 = static_cast<const bf16_t*>(a.w2);
     auto Y = static_cast<bf16_t*>(a.y_rows);
-    if (a.d >= 1024) launch_bf16<256, 32, ACT_NONE>(H, W2, nullptr, Y, a.h, a.d, a, st);
-    else launch_bf16<128, 32, ACT_NONE>(H, W2, nullptr, Y, a.h, a.d, a, st);
+    if (a.d >= 1024) launch_bf16<256, ACT_NONE>(H, W2, nullptr, Y, a.h, a.d, a, st);
+    else launch_bf16<128, ACT_NONE>(H, W2, nullptr, Y, a.h, a.d, a, st);
   }
   return hipGetLastError();
 }

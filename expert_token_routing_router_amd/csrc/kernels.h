@@ -67,6 +67,7 @@ size_t ffn_workspace_bytes(int E, int max_rows, int d, int h, int act, int dtype
 hipError_t launch_ffn_plan(const FfnArgs& a, hipStream_t st);
 hipError_t launch_ffn_up(const FfnArgs& a, hipStream_t st);
 hipError_t launch_ffn_down(const FfnArgs& a, hipStream_t st);
+hipError_t launch_pack_weights(int E, int N, int K, const void* w, void* wp, hipStream_t st);
 
 struct CombineArgs {
   int N, d, k, dtype;

@@ -1,9 +1,10 @@
 """The whole MoE-layer forward as a sequence of library calls.
 
 ``MoeBuffers`` allocates (with torch) every output and workspace the five
-entry points need for one workload; ``moe_forward`` enqueues route ->
-dispatch -> expert FFN (+ shared expert) -> combine on one stream, with no
-host synchronisation.  No arithmetic happens here.
+entry points need for one workload; ``prepare_weights`` packs bf16 expert
+weights once into the layout the expert FFN reads; ``moe_forward`` enqueues
+route -> dispatch -> expert FFN (+ shared expert) -> combine on one stream,
+with no host synchronisation.  No arithmetic happens here.
 """
 
 from __future__ import annotations
@@ -12,7 +13,34 @@ import torch
 
 from . import (ACT, DTYPE, TORCH_DTYPE, desc_from_workload, moe_bias_update, moe_combine,
                moe_dispatch, moe_dispatch_workspace_size, moe_expert_ffn,
-               moe_expert_ffn_workspace_size, moe_route, moe_route_workspace_size, workspace)
+               moe_expert_ffn_pack_weights, moe_expert_ffn_workspace_size, moe_route,
+               moe_route_workspace_size, workspace)
+
+
+def prepare_weights(cfg: dict, inp: dict, stream=None) -> dict:
+    """A shallow copy of the device inputs ``inp`` whose expert weights (w1,
+    w3, w2 and the shared expert's) are in the layout ``moe_expert_ffn``
+    reads: packed by ``moe_expert_ffn_pack_weights`` for bf16, unchanged for
+    fp32.  Done once per set of weights; the layer functions take the result."""
+    out = dict(inp)
+    out["weights_packed"] = True
+    if cfg["dtype"] != "bf16":
+        return out
+
+    def pack(w, rows, cols):
+        if w is None:
+            return None
+        wp = torch.empty_like(w)
+        moe_expert_ffn_pack_weights(w.shape[0], rows, cols, "bf16", w, wp, stream)
+        return wp
+
+    d, h = cfg["d"], cfg["h"]
+    out["w1"], out["w3"], out["w2"] = (pack(inp["w1"], h, d), pack(inp.get("w3"), h, d),
+                                       pack(inp["w2"], d, h))
+    if inp.get("shared") is not None:
+        sw1, sw3, sw2 = inp["shared"]
+        out["shared"] = (pack(sw1, h, d), pack(sw3, h, d), pack(sw2, d, h))
+    return out
 
 
 class MoeBuffers:
@@ -66,7 +94,10 @@ def dispatch(buf: MoeBuffers, inp: dict, stream=None):
 
 
 def expert_ffn(buf: MoeBuffers, inp: dict, stream=None):
+    """``inp`` must come from ``prepare_weights`` (packed bf16 weights)."""
     d, cfg = buf.desc, buf.cfg
+    if not inp.get("weights_packed"):
+        raise ValueError("expert_ffn needs the weights from prepare_weights(cfg, inp)")
     S = d.num_tokens * d.top_k
     moe_expert_ffn(d.num_experts, S, d.hidden, cfg["h"], cfg["act"], cfg["dtype"], buf.x_perm,
                    buf.expert_offsets, inp["w1"], inp.get("w3"), inp["w2"], buf.y_perm,

@@ -11,6 +11,7 @@
  *   moe_dispatch     capacity, token-order admission, expert- and
  *                    rank-contiguous row layout, permuted hidden states
  *   moe_expert_ffn   every expert's FFN over its rows as one grouped GEMM pair
+ *                    (bf16 weights packed once by moe_expert_ffn_pack_weights)
  *   moe_combine      weighted sum back to token order, plus residual and an
  *                    optional shared-expert output
  *   moe_bias_update  lower the selection bias of overloaded experts, raise it
@@ -24,7 +25,8 @@
  *    asynchronously; nothing synchronises the host.
  *  - Arguments are validated on the host before any launch.  A call that
  *    returns an error has enqueued nothing and written nothing.
- *  - Layouts are row-major and dense.  Hidden-state buffers must be 16-byte
+ *  - Layouts are row-major and dense (bf16 expert weights excepted: packed,
+ *    see moe_expert_ffn_pack_weights).  Hidden-state buffers must be 16-byte
  *    aligned.  dtype MOE_BF16 buffers hold bf16, MOE_F32 buffers fp32; routing
  *    tensors (logits, weights, biases) are fp32 in both cases.
  *  - Every call fully overwrites its outputs (counts included), so calls are
@@ -192,6 +194,10 @@ size_t moe_expert_ffn_workspace_size(int32_t num_experts, int32_t max_rows, int3
  *  w1            [E, h, d]  dtype  (gate for SwiGLU)
  *  w3            [E, h, d]  dtype  (up; SwiGLU only, else NULL)
  *  w2            [E, d, h]  dtype
+ *                fp32: row-major as shown.  bf16: in the packed layout that
+ *                moe_expert_ffn_pack_weights writes (done once, when the
+ *                weights are loaded); row-major bf16 weights give wrong
+ *                results, which the library cannot detect.
  *  y_rows        [max_rows, d]  dtype out (rows >= offsets[E] untouched)
  *  ws, ws_bytes  workspace >= moe_expert_ffn_workspace_size(...) */
 int moe_expert_ffn(int32_t num_experts, int32_t max_rows, int32_t hidden, int32_t ffn_hidden,
@@ -218,6 +224,31 @@ int moe_expert_ffn_down(int32_t num_experts, int32_t max_rows, int32_t hidden,
                         int32_t ffn_hidden, int32_t act, int32_t dtype,
                         const int32_t* group_offsets, const void* w2, void* y_rows,
                         void* ws, size_t ws_bytes, void* stream);
+
+/* Pack one bf16 expert weight tensor for the bf16 expert FFN.
+ *
+ *  num_experts  E >= 1
+ *  rows, cols   the tensor is [E, rows, cols] row-major bf16: rows = output
+ *               features of its GEMM, cols = input features (W1, W3: rows = h,
+ *               cols = d; W2: rows = d, cols = h); both multiples of 64
+ *  dtype        MOE_BF16 (fp32 weights are used row-major: MOE_ERR_UNSUPPORTED)
+ *  w            source, device, 16-byte aligned; not modified
+ *  w_packed     destination, device, E*rows*cols bf16, 16-byte aligned, must
+ *               not overlap w; owned by the caller
+ *
+ * Layout: rows are grouped in slabs of S rows, S = 256 if rows % 256 == 0,
+ * else 64.  Element (e, n, k), with s = n / S, g = (n % S) / 16, r = n % 16,
+ * t = k / 32, c = (k % 32) / 8 and L = 4r + (c XOR sw(r)),
+ * sw(r) = ((r >> 1) XOR (r >> 2)) & 3, is stored at element offset
+ *   ((e*(rows/S) + s)*(cols/32) + t)*S*32 + g*512 + 8*L + k % 8.
+ * So each slab is cols/32 consecutive stages of S x 32 elements, and each
+ * stage is S/16 blocks of 1 KB in the order the GEMM kernel stages weight
+ * rows in LDS: every K step of a slab is one contiguous run of S * 64 bytes.
+ * A pure permutation: the packed tensor holds the same values bit for bit.
+ * Errors: MOE_ERR_INVALID_ARG (sizes, null/misaligned/overlapping pointers),
+ * MOE_ERR_UNSUPPORTED (fp32, rows or cols not a multiple of 64), MOE_ERR_HIP. */
+int moe_expert_ffn_pack_weights(int32_t num_experts, int32_t rows, int32_t cols, int32_t dtype,
+                                const void* w, void* w_packed, void* stream);
 
 /* ---------------------------------------------------------------- combine -- */
 

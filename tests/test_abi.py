@@ -133,6 +133,22 @@ def test_expert_ffn_validation():
     assert call(8, 0, 64, 64, moe.MOE_RELU, moe.MOE_BF16) == moe.MOE_OK  # nothing to do
 
 
+def test_pack_weights_validation():
+    lib = moe.lib()
+    pack = lib.moe_expert_ffn_pack_weights
+    A, B = ctypes.c_void_p(0x10000), ctypes.c_void_p(0x10000 + (1 << 30))
+    assert pack(0, 64, 64, moe.MOE_BF16, A, B, None) == moe.MOE_ERR_INVALID_ARG
+    assert pack(2, 64, 64, 7, A, B, None) == moe.MOE_ERR_INVALID_ARG
+    assert pack(2, 64, 64, moe.MOE_F32, A, B, None) == moe.MOE_ERR_UNSUPPORTED
+    assert pack(2, 96, 64, moe.MOE_BF16, A, B, None) == moe.MOE_ERR_UNSUPPORTED
+    assert pack(2, 64, 32, moe.MOE_BF16, A, B, None) == moe.MOE_ERR_UNSUPPORTED
+    assert pack(2, 64, 64, moe.MOE_BF16, None, B, None) == moe.MOE_ERR_INVALID_ARG
+    assert pack(2, 64, 64, moe.MOE_BF16, A, ctypes.c_void_p(0x10008), None) == \
+        moe.MOE_ERR_INVALID_ARG  # misaligned
+    assert pack(2, 64, 64, moe.MOE_BF16, A, ctypes.c_void_p(0x10000 + 4096), None) == \
+        moe.MOE_ERR_INVALID_ARG  # overlaps the source
+
+
 def test_combine_and_bias_validation():
     lib = moe.lib()
     d = moe.route_desc(64, 64, 8, 2)

@@ -43,7 +43,7 @@ def test_fullsize(name):
           flush=True)
     inp = inputs_on_device(cfg)
     buf = moe.MoeBuffers(cfg)
-    moe.moe_forward(buf, inp)
+    moe.moe_forward(buf, moe.prepare_weights(cfg, inp))
     torch.cuda.synchronize()
     dt = cfg["dtype"]
 

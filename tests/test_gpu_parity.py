@@ -42,7 +42,7 @@ def run_case(name):
     print(f"[case {name}] N={cfg['N']} d={cfg['d']} h={cfg['h']} E={cfg['E']} k={cfg['k']}",
           flush=True)
     inp_cpu = W.make_inputs(cfg)
-    inp = to_dev(inp_cpu)
+    inp = moe.prepare_weights(cfg, to_dev(inp_cpu))
     buf = moe.MoeBuffers(cfg)
     layer.route(buf, inp)
     layer.dispatch(buf, inp)
@@ -225,7 +225,7 @@ def test_all_tokens_to_one_expert_with_capacity():
     sb = torch.zeros(cfg["E"], dtype=torch.float32)
     sb[3] = 1e4
     inp_cpu["sel_bias"] = sb
-    inp = to_dev(inp_cpu)
+    inp = moe.prepare_weights(cfg, to_dev(inp_cpu))
     buf = moe.MoeBuffers(cfg)
     moe.moe_forward(buf, inp)
     torch.cuda.synchronize()
@@ -257,7 +257,7 @@ def test_single_expert_layer():
                kg=1, score="softmax_topk", act="swiglu", dtype="bf16", router_bias=None,
                sel_bias=None, shared=False, zipf=None)
     inp_cpu = W.make_inputs(cfg)
-    inp = to_dev(inp_cpu)
+    inp = moe.prepare_weights(cfg, to_dev(inp_cpu))
     buf = moe.MoeBuffers(cfg)
     moe.moe_forward(buf, inp)
     torch.cuda.synchronize()
@@ -269,7 +269,7 @@ def test_single_expert_layer():
 def test_topk_equals_num_experts():
     cfg = W.with_(W.small("mixtral"), k=8, N=257)
     inp_cpu = W.make_inputs(cfg)
-    inp = to_dev(inp_cpu)
+    inp = moe.prepare_weights(cfg, to_dev(inp_cpu))
     buf = moe.MoeBuffers(cfg)
     moe.moe_forward(buf, inp)
     torch.cuda.synchronize()
@@ -303,7 +303,7 @@ def test_invalid_arguments_enqueue_nothing():
 def test_ffn_stages_equal_single_call():
     """plan + up + down gives bitwise the same rows as moe_expert_ffn."""
     cfg = W.small("mixtral")
-    inp = to_dev(W.make_inputs(cfg))
+    inp = moe.prepare_weights(cfg, to_dev(W.make_inputs(cfg)))
     buf = moe.MoeBuffers(cfg)
     moe.moe_forward(buf, inp)
     torch.cuda.synchronize()
