@@ -120,40 +120,9 @@ __device__ __forceinline__ int xcd_logical(int b, int total) {
 
 // ------------------------------------------------------------- bf16 MFMA ---
 
-// LDS rows hold 32 bf16 (64 bytes = four 16-byte chunks).  Chunk c of row r
-// lives at c ^ swz4(r): consecutive rows reading the same logical chunk then
-// hit distinct bank groups for 8- and for 16-lane LDS phases.  The pattern
-// depends on row bits 1-3 only, so rows 16 or 32 apart share it.
-__device__ __forceinline__ int swz4(int r) { return ((r >> 1) ^ (r >> 2)) & 3; }
-
 // Rows per slab of packed weights (rows = N of the GEMM, a multiple of 64): a
 // slab's K stage is one contiguous run of SR * 64 bytes.
 __host__ __device__ __forceinline__ int packed_slab_rows(int N) { return N % 256 == 0 ? 256 : 64; }
-
-typedef __attribute__((address_space(3))) void* lds_ptr_t;
-
-// s_waitcnt vmcnt(N), other counters untouched (gfx9 encoding: vmcnt[3:0] in
-// bits 3:0 and vmcnt[5:4] in bits 15:14; expcnt 7 and lgkmcnt 15 mean "no wait").
-template <int N>
-__device__ __forceinline__ void wait_vmcnt() {
-  static_assert(N >= 0 && N < 64, "vmcnt is 6 bits");
-  __builtin_amdgcn_s_waitcnt(0x0F70 | (N & 15) | (((N >> 4) & 3) << 14));
-}
-
-constexpr int kLdsBytes = 160 * 1024;  // LDS per CU (and per workgroup) on gfx950
-
-// Workgroup barrier for the LDS ring.  Before it, each wave has waited for
-// its own global->LDS loads of the stage about to be read (explicit
-// s_waitcnt vmcnt) and has consumed every LDS read of the stage about to be
-// overwritten; the barrier then makes both true for the whole block.  A
-// __syncthreads() would also drain the loads of the stages still in flight,
-// which is exactly the latency the ring is there to hide, so only compiler
-// reordering is fenced here.
-__device__ __forceinline__ void ring_barrier() {
-  __atomic_signal_fence(__ATOMIC_SEQ_CST);
-  __builtin_amdgcn_s_barrier();
-  __atomic_signal_fence(__ATOMIC_SEQ_CST);
-}
 
 // Grouped GEMM C[rows, N] = act(A[rows, K] B_e[N, K]^T) for bf16.
 //

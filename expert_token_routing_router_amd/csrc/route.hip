@@ -272,8 +272,9 @@ static size_t exact_logits_bytes(int N, int d, int E) {
   return (size_t)route_padded_experts(E) * d * sizeof(double);
 }
 
+// The certified path (bf16 inputs) streams rows in 32-element chunks.
 static bool use_certified(const RouteArgs& a) {
-  return a.dtype == 1 && a.N < kCertifiedMaxTokens;
+  return a.dtype == 1 && a.N < kCertifiedMaxTokens && a.d % 32 == 0;
 }
 
 size_t route_workspace_bytes(int N, int d, int E, int dtype) {

@@ -388,54 +388,94 @@ __global__ __launch_bounds__(kCertWaves * 64) void route_certify(
 
 // ------------------------------------------------------------- 3. exact ---
 
-// Every lane of the grid takes listed pairs (grid-stride, consecutive pairs in
-// one wave so their loads overlap) and evaluates the definition: fp64 sum left
-// to right of exact products, + bias, one rounding.
-__global__ __launch_bounds__(256) void route_exact(const bf16_t* __restrict__ x,
-                                                   const bf16_t* __restrict__ w, int d, int E,
-                                                   const float* __restrict__ router_bias,
-                                                   const int32_t* __restrict__ pairs,
-                                                   const int32_t* __restrict__ pair_count,
-                                                   float* __restrict__ logits) {
-  const long long n = *pair_count;
-  for (long long p = (long long)blockIdx.x * blockDim.x + threadIdx.x; p < n;
-       p += (long long)gridDim.x * blockDim.x) {
-    const int v = pairs[p];
+// The definition for every listed pair: fp64 sum, left to right, of the exact
+// products x_ti w_ei, + bias, one rounding to fp32.  The sum is one
+// sequential chain per pair (its rounding order is part of the definition),
+// so a lane owns a pair; what the 64 lanes of a wave share is the memory
+// traffic.  A one-wave block takes groups of 64 consecutive list entries and
+// streams their x and w rows through LDS in chunks of 32 elements (64 bytes
+// of each row, 8 KB per chunk for the group) with global_load_lds_dwordx4,
+// up to kExactRing - 1 chunks ahead of the chains.  Load i of a chunk covers
+// the rows of pairs 16(i%4) .. 16(i%4)+15 (x for i < 4, w after); lane L
+// fetches row L/4 of those, logical 16-byte chunk (L % 4) ^ swz4(L / 4), so
+// the chains' 16-byte LDS reads of one chunk spread over the banks.  Needs
+// d % 32 == 0 (the launcher checks).
+constexpr int kExactRing = 8;    // LDS chunk slots per wave, 8 KB each
+constexpr int kExactBlocks = 2048;
+
+__global__ __launch_bounds__(64) void route_exact(const bf16_t* __restrict__ x,
+                                                  const bf16_t* __restrict__ w, int d, int E,
+                                                  const float* __restrict__ router_bias,
+                                                  const int32_t* __restrict__ pairs,
+                                                  const int32_t* __restrict__ pair_count,
+                                                  float* __restrict__ logits) {
+  __shared__ __attribute__((aligned(1024))) char ring[kExactRing][8192];
+  const int lane = threadIdx.x;
+  const int n = *pair_count;
+  const int nch = d / 32;
+  const int mine = (lane & 15) * 4;  // this lane's row inside its 1-KB block: byte offset / 16
+  const int msw = swz4(lane & 15);
+  for (int g0 = blockIdx.x * 64; g0 < n; g0 += gridDim.x * 64) {
+    const bool live = g0 + lane < n;
+    const int v = pairs[live ? g0 + lane : g0];  // idle lanes shadow a listed pair
     const int t = v >> 8, e = v & 255;
-    const u32x4* xr = reinterpret_cast<const u32x4*>(x + (size_t)t * d);
-    const u32x4* wr = reinterpret_cast<const u32x4*>(w + (size_t)e * d);
-    // Loads run 4 vectors (32 elements) ahead of the sequential fp64 chain.
-    constexpr int AHEAD = 4;
-    const int nv = d / 8;
-    u32x4 xa[AHEAD], wa[AHEAD];
+    const u32x4* src[8];
 #pragma unroll
-    for (int u = 0; u < AHEAD; ++u) {
-      xa[u] = u < nv ? xr[u] : u32x4{0u, 0u, 0u, 0u};
-      wa[u] = u < nv ? wr[u] : u32x4{0u, 0u, 0u, 0u};
+    for (int i = 0; i < 4; ++i) {
+      const int q = 16 * i + lane / 4;  // pair whose rows this lane fetches
+      const int tq = __shfl(t, q, 64), eq = __shfl(e, q, 64);
+      const int c = (lane % 4) ^ swz4(lane / 4);
+      src[i] = reinterpret_cast<const u32x4*>(x + (size_t)tq * d) + c;
+      src[4 + i] = reinterpret_cast<const u32x4*>(w + (size_t)eq * d) + c;
     }
+#define MOE_EXACT_ISSUE(ch_)                                                                \
+  do {                                                                                      \
+    char* slot_ = ring[(ch_) % kExactRing];                                                 \
+    _Pragma("unroll") for (int i = 0; i < 8; ++i)                                           \
+        __builtin_amdgcn_global_load_lds((void*)(src[i] + (size_t)(ch_) * 4),               \
+                                         (lds_ptr_t)(slot_ + i * 1024), 16, 0, 0);          \
+  } while (0)
+#pragma unroll
+    for (int c = 0; c < kExactRing - 1; ++c)
+      if (c < nch) MOE_EXACT_ISSUE(c);
     double acc = 0.0;
-    for (int i0 = 0; i0 < nv; i0 += AHEAD) {
+    for (int ch = 0; ch < nch; ++ch) {
+      // Chunk ch has landed once at most `later` younger chunks (8 loads
+      // each) are still in flight.
+      switch (min(kExactRing - 2, nch - 1 - ch)) {
+        case 0: wait_vmcnt<0>(); break;
+        case 1: wait_vmcnt<8>(); break;
+        case 2: wait_vmcnt<16>(); break;
+        case 3: wait_vmcnt<24>(); break;
+        case 4: wait_vmcnt<32>(); break;
+        case 5: wait_vmcnt<40>(); break;
+        default: wait_vmcnt<48>(); break;
+      }
+      __atomic_signal_fence(__ATOMIC_SEQ_CST);
+      // The slot of chunk ch-1 was consumed by the previous iteration.
+      if (ch + kExactRing - 1 < nch) MOE_EXACT_ISSUE(ch + kExactRing - 1);
+      const char* slot = ring[ch % kExactRing];
+      const char* xb = slot + (lane >> 4) * 1024;
+      const char* wb = slot + 4096 + (lane >> 4) * 1024;
 #pragma unroll
-      for (int u = 0; u < AHEAD; ++u) {
-        const u32x4 a = xa[u], b = wa[u];
-        const int nxt = i0 + AHEAD + u;
-        if (nxt < nv) {
-          xa[u] = xr[nxt];
-          wa[u] = wr[nxt];
-        }
-        if (i0 + u < nv) {
+      for (int qq = 0; qq < 4; ++qq) {
+        const int pos = (mine + (qq ^ msw)) * 16;
+        const u32x4 a = *reinterpret_cast<const u32x4*>(xb + pos);
+        const u32x4 b = *reinterpret_cast<const u32x4*>(wb + pos);
 #pragma unroll
-          for (int q = 0; q < 4; ++q) {
-            acc = __fma_rn((double)bf16_to_f32(a[q] & 0xffffu),
-                           (double)bf16_to_f32(b[q] & 0xffffu), acc);
-            acc = __fma_rn((double)bf16_to_f32(a[q] >> 16), (double)bf16_to_f32(b[q] >> 16),
-                           acc);
-          }
+        for (int q = 0; q < 4; ++q) {
+          acc = __fma_rn((double)bf16_to_f32(a[q] & 0xffffu), (double)bf16_to_f32(b[q] & 0xffffu),
+                         acc);
+          acc = __fma_rn((double)bf16_to_f32(a[q] >> 16), (double)bf16_to_f32(b[q] >> 16), acc);
         }
       }
+      __atomic_signal_fence(__ATOMIC_SEQ_CST);
     }
-    if (router_bias) acc = acc + (double)router_bias[e];
-    logits[(size_t)t * E + e] = __double2float_rn(acc);
+#undef MOE_EXACT_ISSUE
+    if (live) {
+      if (router_bias) acc = acc + (double)router_bias[e];
+      logits[(size_t)t * E + e] = __double2float_rn(acc);
+    }
   }
 }
 
@@ -631,8 +671,8 @@ hipError_t launch_route_certified(const RouteArgs& a, hipStream_t st) {
   route_certify<<<blocks, kCertWaves * 64, 0, st>>>(a.logits, c.sumsq_x, c.sumsq_w, a.sel_bias, a.N, a.E,
                                         a.k, a.G, a.kg, a.score_fn, c.cand, c.gmask, c.pairs,
                                         c.pair_count);
-  route_exact<<<1024, 256, 0, st>>>(x, w, a.d, a.E, a.router_bias, c.pairs, c.pair_count,
-                                    a.logits);
+  route_exact<<<kExactBlocks, 64, 0, st>>>(x, w, a.d, a.E, a.router_bias, c.pairs,
+                                           c.pair_count, a.logits);
   route_finalize<<<blocks, kCertWaves * 64, 0, st>>>(a.logits, a.sel_bias, c.cand, c.gmask, a.N, a.E, a.k,
                                          a.G, a.kg, a.score_fn, a.topk_idx, a.topk_w, a.counts);
   return hipGetLastError();
