@@ -35,35 +35,90 @@ __device__ __forceinline__ float load_elem(const void* p, int dtype, size_t i) {
 
 __device__ __forceinline__ int lane_id() { return __lane_id(); }
 
+// Wave reductions through DPP lane exchanges (gfx9 encodings), no LDS
+// crossbar: a butterfly inside each row of 16 lanes (quad xor 1, quad xor 2,
+// half-row mirror, row mirror), then row broadcasts (lane 15 into rows 1 and
+// 3, lane 31 into rows 2 and 3) leave the reduction of all 64 lanes in lane
+// 63, which v_readlane hands to every lane.
+enum : int {
+  kDppXor1 = 0xB1, kDppXor2 = 0x4E, kDppHalfMirror = 0x141, kDppMirror = 0x140,
+  kDppBcast15 = 0x142, kDppBcast31 = 0x143
+};
+
+template <int CTRL, int ROWS = 0xF>
+__device__ __forceinline__ int dpp_i(int old, int v) {
+  return __builtin_amdgcn_update_dpp(old, v, CTRL, ROWS, 0xF, false);
+}
+template <int CTRL, int ROWS = 0xF>
+__device__ __forceinline__ float dpp_f(float old, float v) {
+  return __int_as_float(dpp_i<CTRL, ROWS>(__float_as_int(old), __float_as_int(v)));
+}
+template <int CTRL, int ROWS = 0xF>
+__device__ __forceinline__ double dpp_d(double old, double v) {
+  const long long o = __double_as_longlong(old), x = __double_as_longlong(v);
+  const int lo = dpp_i<CTRL, ROWS>((int)o, (int)x);
+  const int hi = dpp_i<CTRL, ROWS>((int)(o >> 32), (int)(x >> 32));
+  return __longlong_as_double(((long long)hi << 32) | (unsigned)lo);
+}
+__device__ __forceinline__ float lane63(float v) {
+  return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 63));
+}
+__device__ __forceinline__ double lane63(double v) {
+  const long long b = __double_as_longlong(v);
+  const int lo = __builtin_amdgcn_readlane((int)b, 63);
+  const int hi = __builtin_amdgcn_readlane((int)(b >> 32), 63);
+  return __longlong_as_double(((long long)hi << 32) | (unsigned)lo);
+}
+
 __device__ __forceinline__ float wave_sum(float v) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, kWave);
-  return v;
+  v += dpp_f<kDppXor1>(0.f, v);
+  v += dpp_f<kDppXor2>(0.f, v);
+  v += dpp_f<kDppHalfMirror>(0.f, v);
+  v += dpp_f<kDppMirror>(0.f, v);
+  v += dpp_f<kDppBcast15, 0xA>(0.f, v);
+  v += dpp_f<kDppBcast31, 0xC>(0.f, v);
+  return lane63(v);
 }
 
 __device__ __forceinline__ double wave_sum(double v) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, kWave);
-  return v;
+  v += dpp_d<kDppXor1>(0.0, v);
+  v += dpp_d<kDppXor2>(0.0, v);
+  v += dpp_d<kDppHalfMirror>(0.0, v);
+  v += dpp_d<kDppMirror>(0.0, v);
+  v += dpp_d<kDppBcast15, 0xA>(0.0, v);
+  v += dpp_d<kDppBcast31, 0xC>(0.0, v);
+  return lane63(v);
 }
 
 __device__ __forceinline__ float wave_max(float v) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, kWave));
-  return v;
+  v = fmaxf(v, dpp_f<kDppXor1>(v, v));
+  v = fmaxf(v, dpp_f<kDppXor2>(v, v));
+  v = fmaxf(v, dpp_f<kDppHalfMirror>(v, v));
+  v = fmaxf(v, dpp_f<kDppMirror>(v, v));
+  v = fmaxf(v, dpp_f<kDppBcast15, 0xA>(v, v));
+  v = fmaxf(v, dpp_f<kDppBcast31, 0xC>(v, v));
+  return lane63(v);
 }
 
 // (score, index) pair ordered by score descending, index ascending.  Returns
 // the best pair over the wave in every lane.  Index -1 marks "no candidate".
+template <int CTRL, int ROWS>
+__device__ __forceinline__ void argmax_step(float& s, int& idx) {
+  const float so = dpp_f<CTRL, ROWS>(0.f, s);
+  const int io = dpp_i<CTRL, ROWS>(-1, idx);
+  const bool take = (io >= 0) && (idx < 0 || so > s || (so == s && io < idx));
+  s = take ? so : s;
+  idx = take ? io : idx;
+}
 __device__ __forceinline__ void wave_argmax(float& s, int& idx) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) {
-    float so = __shfl_xor(s, o, kWave);
-    int io = __shfl_xor(idx, o, kWave);
-    bool take = (io >= 0) && (idx < 0 || so > s || (so == s && io < idx));
-    s = take ? so : s;
-    idx = take ? io : idx;
-  }
+  argmax_step<kDppXor1, 0xF>(s, idx);
+  argmax_step<kDppXor2, 0xF>(s, idx);
+  argmax_step<kDppHalfMirror, 0xF>(s, idx);
+  argmax_step<kDppMirror, 0xF>(s, idx);
+  argmax_step<kDppBcast15, 0xA>(s, idx);
+  argmax_step<kDppBcast31, 0xC>(s, idx);
+  s = lane63(s);
+  idx = __builtin_amdgcn_readlane(idx, 63);
 }
 
 // ------------------------------------------- direct global->LDS streaming ---

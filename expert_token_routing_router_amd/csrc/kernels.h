@@ -31,7 +31,7 @@ hipError_t launch_router_logits(const RouteArgs& a, hipStream_t st);
 // Certified path for bf16 inputs (route_mfma.hip).
 size_t route_certified_workspace_bytes(int N, int E);
 hipError_t launch_route_certified(const RouteArgs& a, hipStream_t st);
-constexpr int kCertifiedMaxTokens = 1 << 23;  // (token << 8 | expert) pair encoding
+void launch_zero_i32(int32_t* p, int n, hipStream_t st);
 
 struct DispatchArgs {
   int N, d, E, k, R, dtype;

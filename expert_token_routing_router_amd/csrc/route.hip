@@ -41,6 +41,8 @@ __global__ void zero_i32(int32_t* __restrict__ p, int n) {
   for (int i = blockIdx.x * blockDim.x + threadIdx.x; i < n; i += gridDim.x * blockDim.x) p[i] = 0;
 }
 
+void launch_zero_i32(int32_t* p, int n, hipStream_t st) { zero_i32<<<1, 256, 0, st>>>(p, n); }
+
 // Block: 256 threads = 4 waves.  The block covers TT token tiles of 64 and
 // EG = 4 / TT expert chunks of EC.  Grid: (ceil(N / (64*TT)), ceil(Ep / (EC*EG))).
 template <int EC, int TT>
@@ -197,7 +199,7 @@ __global__ __launch_bounds__(kSelectWaves * 64) void select_topk(const float* __
 #pragma unroll
         for (int j = 1; j < 4; ++j)
           if (jj == j) zv = z[j];
-        zsel[r] = __shfl(zv, owner, 64);
+        zsel[r] = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(zv), owner));
         if (lane == owner) {
 #pragma unroll
           for (int j = 0; j < 4; ++j)
@@ -274,7 +276,7 @@ static size_t exact_logits_bytes(int N, int d, int E) {
 
 // The certified path (bf16 inputs) streams rows in 32-element chunks.
 static bool use_certified(const RouteArgs& a) {
-  return a.dtype == 1 && a.N < kCertifiedMaxTokens && a.d % 32 == 0;
+  return a.dtype == 1 && a.d % 32 == 0 && a.E <= 256;
 }
 
 size_t route_workspace_bytes(int N, int d, int E, int dtype) {

@@ -2,37 +2,12 @@
 //
 // The router logit is defined exactly (fp64 sum left to right of exact
 // products, bias added in fp64, one rounding to fp32).  Computing that for
-// every (token, expert) costs 2*N*d*E fp64 operations, which is far above the
-// memory time of reading x once when E >= 64.  Selection only needs exact
-// values where they decide something, so:
-//
-//  1. logits_mfma      z~ = sum over K chunks of 64 of the bf16 MFMA chunk sum
-//                      (fp32 accumulation, exact products), added up in fp64,
-//                      plus the bias; also sum_i x_ti^2 and sum_i w_ei^2 in fp64.
-//                      Error bound: each fp32 rounding in a chunk of 64 exact
-//                      products is at most 2^-23 of a partial sum bounded by
-//                      S_c = sum over the chunk of |x_i w_i|; with at most 64
-//                      roundings per chunk the chunk error is <= 2^-17 S_c, so
-//                      |z~ - exact| <= 2^-17 S with S <= |x_t| |w_e| (Cauchy-
-//                      Schwarz).  The definition's own fp64 summation and fp32
-//                      rounding add at most 2^-40 S + 2^-24 |z|.  The margin
-//                      used is m = 2^-16 |x_t| |w_e| + 2^-22 |z~| + 2^-90.
-//  2. route_certify    one wave per token: selection-score intervals (the score
-//                      map -- identity or sigmoid, then + selection bias in
-//                      fp32 -- is monotone, so the interval ends map through
-//                      it); groups that are certainly kept / certainly dropped
-//                      / undecided; the experts that can still be selected or
-//                      can still be the maximum of an undecided group.  Those
-//                      (token, expert) pairs go to a list.
-//  3. route_exact      the exact definition for every listed pair (one lane,
-//                      one sequential fp64 chain), overwriting z~.
-//  4. route_finalize   one wave per token: group and top-k selection from exact
-//                      values (every expert left out of the list is certainly
-//                      not selected), combine weights, per-expert counts.
-//
-// Passages: glossary "Expert Parallelism", "How tokens travel between GPUs"
-// (step 1 and the snippet's Linear router) and "Load balancing and capacity"
-// (selection-only bias; node-limited routing as the group limit).
+// every (token, expert) costs 2*N*d*E fp64 operations, far above the memory
+// time of reading x once when E >= 64.  Selection only needs exact values
+// where they decide something, so the scores come from bf16 MFMAs with a
+// proven error bound, and only the (token, expert) pairs the bound cannot
+// settle are recomputed by the definition.  One kernel does all of it per
+// tile of tokens (see route_fused).
 #include "device.h"
 #include "kernels.h"
 
@@ -41,136 +16,47 @@ namespace moe {
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef float floatx4 __attribute__((ext_vector_type(4)));
 
-constexpr int kRouteTokTile = 64;   // tokens per block in logits_mfma
-constexpr int kRouteExpTile = 64;   // experts per block (4 waves x 16)
-constexpr int kRouteKChunk = 64;    // K chunk accumulated in fp32
-
-// ------------------------------------------------------------ 1. scores ---
-
-// Grid (ceil(N/64), ceil(E/64)); 256 threads.  Wave w covers the block's 64
-// tokens x experts [16w, 16w+16) with four 16x16 MFMA blocks
-// (v_mfma_f32_16x16x32_bf16, tokens as rows).  LDS rows are 64 bf16 = eight
-// 16-byte chunks, chunk c of row r stored at c ^ (r & 7).
-__global__ __launch_bounds__(256) void logits_mfma(const bf16_t* __restrict__ x,
-                                                   const bf16_t* __restrict__ w, int N, int d,
-                                                   int E, const float* __restrict__ router_bias,
-                                                   float* __restrict__ logits,
-                                                   double* __restrict__ sumsq_x,
-                                                   double* __restrict__ sumsq_w,
-                                                   int32_t* __restrict__ zero_counts,
-                                                   int32_t* __restrict__ zero_pairs) {
-  __shared__ u32x4 xs[kRouteTokTile * 8];
-  __shared__ u32x4 ws[kRouteExpTile * 8];
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int t0 = blockIdx.x * kRouteTokTile, e0 = blockIdx.y * kRouteExpTile;
-  if (blockIdx.x == 0 && blockIdx.y == 0) {
-    for (int e = tid; e < E; e += 256) zero_counts[e] = 0;
-    if (tid == 0) *zero_pairs = 0;
-  }
-
-  // Each thread stages 2 x-chunks and 2 w-chunks per K chunk: rows tid/8 and
-  // tid/8 + 32, chunk tid % 8.  It also accumulates their squares.
-  const int cr = tid >> 3, cc = tid & 7;
-  double sx[2] = {0.0, 0.0}, sw[2] = {0.0, 0.0};
-  floatx4 acc32[4];
-  double acc[4][4];
-#pragma unroll
-  for (int b = 0; b < 4; ++b)
-#pragma unroll
-    for (int v = 0; v < 4; ++v) acc[b][v] = 0.0;
-
-  const u32x4 zero4 = {0u, 0u, 0u, 0u};
-  // The next chunk's global loads are issued before the current chunk's
-  // MFMAs (two register sets, loop unrolled by two).
-  u32x4 rx0[2], rw0[2], rx1[2], rw1[2];
-#define MOE_LOGITS_LOAD(k0_, RX, RW)                                                        \
-  do {                                                                                      \
-    _Pragma("unroll") for (int h = 0; h < 2; ++h) {                                         \
-      const int r = cr + 32 * h, kc = (k0_) + cc * 8;                                       \
-      RX[h] = (t0 + r < N && kc < d) ? *reinterpret_cast<const u32x4*>(x + (size_t)(t0 + r) * d + kc) \
-                                     : zero4;                                              \
-      RW[h] = (e0 + r < E && kc < d) ? *reinterpret_cast<const u32x4*>(w + (size_t)(e0 + r) * d + kc) \
-                                     : zero4;                                              \
-    }                                                                                       \
-  } while (0)
-#define MOE_LOGITS_CHUNK(RX, RW)                                                            \
-  do {                                                                                      \
-    __syncthreads();                                                                        \
-    _Pragma("unroll") for (int h = 0; h < 2; ++h) {                                         \
-      const int r = cr + 32 * h;                                                            \
-      xs[r * 8 + (cc ^ (r & 7))] = RX[h];                                                   \
-      ws[r * 8 + (cc ^ (r & 7))] = RW[h];                                                   \
-      _Pragma("unroll") for (int q = 0; q < 4; ++q) {                                       \
-        const uint32_t a_ = RX[h][q], b_ = RW[h][q];                                        \
-        const double a0 = bf16_to_f32(a_ & 0xffffu), a1 = bf16_to_f32(a_ >> 16);            \
-        const double b0 = bf16_to_f32(b_ & 0xffffu), b1 = bf16_to_f32(b_ >> 16);            \
-        sx[h] = fma(a0, a0, fma(a1, a1, sx[h]));                                            \
-        sw[h] = fma(b0, b0, fma(b1, b1, sw[h]));                                            \
-      }                                                                                     \
-    }                                                                                       \
-    __syncthreads();                                                                        \
-  } while (0)
-#define MOE_LOGITS_MFMA()                                                                   \
-  do {                                                                                      \
-    _Pragma("unroll") for (int b = 0; b < 4; ++b) acc32[b] = floatx4{0.f, 0.f, 0.f, 0.f};   \
-    _Pragma("unroll") for (int ks = 0; ks < kRouteKChunk / 32; ++ks) {                      \
-      const int c = ks * 4 + (lane >> 4);                                                   \
-      const int er = wave * 16 + (lane & 15);                                               \
-      const bf16x8_t bw = __builtin_bit_cast(bf16x8_t, ws[er * 8 + (c ^ (er & 7))]);        \
-      _Pragma("unroll") for (int b = 0; b < 4; ++b) {                                       \
-        const int tr = b * 16 + (lane & 15);                                                \
-        const bf16x8_t ax = __builtin_bit_cast(bf16x8_t, xs[tr * 8 + (c ^ (tr & 7))]);      \
-        acc32[b] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ax, bw, acc32[b], 0, 0, 0);      \
-      }                                                                                     \
-    }                                                                                       \
-    _Pragma("unroll") for (int b = 0; b < 4; ++b)                                           \
-        _Pragma("unroll") for (int v = 0; v < 4; ++v) acc[b][v] += (double)acc32[b][v];     \
-  } while (0)
-
-  MOE_LOGITS_LOAD(0, rx0, rw0);
-  for (int k0 = 0; k0 < d; k0 += 2 * kRouteKChunk) {
-    MOE_LOGITS_CHUNK(rx0, rw0);
-    if (k0 + kRouteKChunk < d) MOE_LOGITS_LOAD(k0 + kRouteKChunk, rx1, rw1);
-    MOE_LOGITS_MFMA();
-    if (k0 + kRouteKChunk >= d) break;
-    MOE_LOGITS_CHUNK(rx1, rw1);
-    if (k0 + 2 * kRouteKChunk < d) MOE_LOGITS_LOAD(k0 + 2 * kRouteKChunk, rx0, rw0);
-    MOE_LOGITS_MFMA();
-  }
-#undef MOE_LOGITS_LOAD
-#undef MOE_LOGITS_CHUNK
-#undef MOE_LOGITS_MFMA
-
-  // Sums of squares: the 8 threads of a row (consecutive lanes) combine.
-#pragma unroll
-  for (int h = 0; h < 2; ++h) {
-#pragma unroll
-    for (int o = 1; o < 8; o <<= 1) {
-      sx[h] += __shfl_xor(sx[h], o, 64);
-      sw[h] += __shfl_xor(sw[h], o, 64);
-    }
-    const int r = cr + 32 * h;
-    if (cc == 0) {
-      if (blockIdx.y == 0 && t0 + r < N) sumsq_x[t0 + r] = sx[h];
-      if (blockIdx.x == 0 && e0 + r < E) sumsq_w[e0 + r] = sw[h];
-    }
-  }
-
-  // C block b: lane holds expert (lane & 15) of this wave, tokens 4*(lane>>4)+v.
-  const int e = e0 + wave * 16 + (lane & 15);
-  if (e < E) {
-    const double bias = router_bias ? (double)router_bias[e] : 0.0;
-#pragma unroll
-    for (int b = 0; b < 4; ++b)
-#pragma unroll
-      for (int v = 0; v < 4; ++v) {
-        const int t = t0 + b * 16 + 4 * (lane >> 4) + v;
-        if (t < N) logits[(size_t)t * E + e] = (float)(acc[b][v] + bias);
-      }
-  }
-}
-
-// ----------------------------------------------------------- 2. certify ---
+// Fused per-tile routing.  One block of 8 waves owns kFuseTok consecutive
+// tokens and runs every step for them, so the approximate logits, the
+// candidate sets and the exact values never leave LDS:
+//
+//  1. scores     for each tile of 64 experts, stream the tokens' x rows and
+//                the experts' w rows through an LDS ring in chunks of 32
+//                elements (global_load_lds_dwordx4); wave w multiplies tokens
+//                16(w/4).. by experts 16(w%4).. of the tile with
+//                v_mfma_f32_16x16x32_bf16 (fp32 within 64-element chunks, fp64
+//                across), and the block accumulates sum x_ti^2 and sum w_ei^2
+//                in fp64 from the same LDS data.  z~ = that sum + bias, kept
+//                as fp32.  Error bound: each fp32 rounding in a chunk of at
+//                most 64 exact products is at most 2^-23 of a partial sum
+//                bounded by S_c = sum over the chunk of |x_i w_i|, so the
+//                chunk error is <= 2^-17 S_c and |z~ - exact| <= 2^-17 S with
+//                S <= |x_t| |w_e| (Cauchy-Schwarz); the definition's own fp64
+//                summation and fp32 rounding add at most 2^-40 S + 2^-24 |z|.
+//                Margin used: m = 2^-16 |x_t| |w_e| + 2^-22 |z~| + 1e-27.
+//  2. certify    one wave per token: selection-score intervals (the score map
+//                -- identity or sigmoid, then + selection bias in fp32 -- is
+//                monotone, so the interval ends map through it); groups that
+//                are certainly kept / certainly dropped / undecided; the
+//                experts that can still be selected or can still be the
+//                maximum of an undecided group become (token, expert) pairs.
+//  3. exact      the definition for every pair -- fp64 sum left to right of
+//                exact products, + bias, one rounding -- one sequential chain
+//                per lane, pairs packed densely into as few waves as possible;
+//                the rows were streamed in step 1, so they come from L2.
+//  4. finalize   one wave per token: group and top-k selection from exact
+//                values (every expert outside the candidate set is certainly
+//                not selected), combine weights; then the tile's logits, its
+//                top-k rows and its per-expert counts go out.
+//
+// Passages: glossary "Expert Parallelism", "How tokens travel between GPUs"
+// (step 1 and the snippet's Linear router) and "Load balancing and capacity"
+// (selection-only bias; node-limited routing as the group limit).
+constexpr int kFuseTok = 32;                     // tokens per block
+constexpr int kFuseWaves = 8;
+constexpr int kFuseRing = 6;                     // LDS chunk slots in step 1
+constexpr int kFuseSlot = (kFuseTok + 64) * 64;  // bytes: 32 x rows + 64 w rows of 64 B
+constexpr int kFuseMaxE = 256;
 
 __device__ __forceinline__ float sigmoid_affinity_v2(float z) {
   return __double2float_rn(1.0 / (1.0 + exp(-(double)z)));
@@ -188,34 +74,147 @@ __device__ __forceinline__ bool certainly_before(float lo_a, int a, float hi_b, 
   return lo_a > hi_b || (lo_a == hi_b && a < b);
 }
 
-constexpr int kCertTokensPerBlock = 64;
-constexpr int kCertWaves = 16;  // 4 tokens per wave; occupancy hides per-token latency
+__global__ __launch_bounds__(kFuseWaves * 64, 2) void route_fused(
+    const bf16_t* __restrict__ x, const bf16_t* __restrict__ w, int N, int d, int E, int k,
+    int G, int kg, int score_fn, const float* __restrict__ router_bias,
+    const float* __restrict__ sel_bias, float* __restrict__ logits,
+    int32_t* __restrict__ topk_idx, float* __restrict__ topk_w, int32_t* __restrict__ counts) {
+  __shared__ float zs[kFuseTok][kFuseMaxE];  // z~, then exact values for candidates
+  __shared__ __attribute__((aligned(1024))) char ring[kFuseRing][kFuseSlot];  // step 1; then pairs
+  __shared__ double sx[kFuseTok], sw[kFuseMaxE];
+  __shared__ uint64_t cand_s[kFuseTok][4], gm_s[kFuseTok][2];
+  __shared__ int32_t cnt_s[kFuseTok];
+  __shared__ int32_t hist[kFuseMaxE];
+  __shared__ int32_t npairs_s;
+  // After step 1 the ring holds, at different times, the per-wave scratch of
+  // the group limit (steps 2 and 4) and the pair list (end of 2, step 3).
+  uint16_t* plist = reinterpret_cast<uint16_t*>(&ring[0][0]);  // (t_local << 8) | e
+  typedef float ExpRow[kFuseMaxE];
+  typedef float GroupRows[2][64];
+  ExpRow* wsc = reinterpret_cast<ExpRow*>(&ring[0][0]);                       // [8][E]: lower ends / scores
+  ExpRow* wsc2 = reinterpret_cast<ExpRow*>(&ring[0][0] + kFuseWaves * 1024);  // [8][E]: upper ends
+  GroupRows* gsc = reinterpret_cast<GroupRows*>(&ring[0][0] + 2 * kFuseWaves * 1024);
+  static_assert(kFuseTok * kFuseMaxE * 2 <= kFuseRing * kFuseSlot, "pair list fits the ring");
+  static_assert(2 * kFuseWaves * 1024 + kFuseWaves * 512 <= kFuseRing * kFuseSlot,
+                "group-limit scratch fits the ring");
+  static_assert(kFuseTok <= 64 && kFuseMaxE <= 256, "pair encoding and one-wave token scan");
 
-// One wave per token.  Lane l holds experts l, l+64, l+128, l+192.
-// Outputs per token: cand[t][4] (bit e set: e needs its exact logit),
-// gmask[t][2] = {certainly kept groups, undecided groups}; pairs appended.
-__global__ __launch_bounds__(kCertWaves * 64) void route_certify(
-    const float* __restrict__ logits, const double* __restrict__ sumsq_x,
-    const double* __restrict__ sumsq_w, const float* __restrict__ sel_bias, int N, int E, int k,
-    int G, int kg, int score_fn, uint64_t* __restrict__ cand, uint64_t* __restrict__ gmask,
-    int32_t* __restrict__ pairs, int32_t* __restrict__ pair_count) {
-  static_assert(kCertTokensPerBlock == 64, "the pair scan is one wave wide");
-  __shared__ float glo_s[kCertWaves][64], ghi_s[kCertWaves][64];
-  __shared__ float lo_s[kCertWaves][256], hi_s[kCertWaves][256];
-  __shared__ uint64_t cand_s[kCertTokensPerBlock][4];  // this block's candidate masks
-  __shared__ int32_t cnt_s[kCertTokensPerBlock];       // candidates per token, then offsets
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int t0 = blockIdx.x * kFuseTok;
+  const int nt = min(kFuseTok, N - t0);
+  const int nch = d / 32;
+  for (int e = tid; e < E; e += kFuseWaves * 64) hist[e] = 0;
+
+  // ---- 1. scores --------------------------------------------------------
+  // Six 1-KB loads per chunk: 0-1 x rows 16j.., 2-5 w rows 16(j-2).. of the
+  // expert tile; wave w < 6 issues load w.  Lane L fetches row L/4 of its
+  // load, logical 16-byte chunk (L % 4) ^ swz4(L / 4).
+  const bool loader = wave < 6;
+  double sxp = 0.0;  // this thread's part of sum x^2 (row tid/16, 2 elements per chunk)
+  for (int et = 0; et < E; et += 64) {
+    const u32x4* src;
+    {
+      const int j = min(wave, 5);
+      const int r = lane / 4, c = (lane % 4) ^ swz4(r);
+      if (j < 2) {
+        const int t = min(t0 + 16 * j + r, N - 1);
+        src = reinterpret_cast<const u32x4*>(x + (size_t)t * d) + c;
+      } else {
+        const int e = min(et + 16 * (j - 2) + r, E - 1);
+        src = reinterpret_cast<const u32x4*>(w + (size_t)e * d) + c;
+      }
+    }
+#define MOE_FUSE_ISSUE(ch_)                                                                 \
+  do {                                                                                      \
+    if (loader)                                                                             \
+      __builtin_amdgcn_global_load_lds((void*)(src + (size_t)(ch_) * 4),                    \
+                                       (lds_ptr_t)(ring[(ch_) % kFuseRing] + wave * 1024),  \
+                                       16, 0, 0);                                           \
+  } while (0)
+#pragma unroll
+    for (int c = 0; c < kFuseRing - 1; ++c)
+      if (c < nch) MOE_FUSE_ISSUE(c);
+    double swp = 0.0;  // sum w^2 part: expert row tid/8 of the tile, 4 elements per chunk
+    floatx4 acc32 = floatx4{0.f, 0.f, 0.f, 0.f};
+    double acc[4] = {0.0, 0.0, 0.0, 0.0};
+    for (int ch = 0; ch < nch; ++ch) {
+      // One load per chunk per loading wave: chunk ch has landed once at most
+      // `later` younger chunks are in flight.
+      switch (min(kFuseRing - 2, nch - 1 - ch)) {
+        case 0: wait_vmcnt<0>(); break;
+        case 1: wait_vmcnt<1>(); break;
+        case 2: wait_vmcnt<2>(); break;
+        case 3: wait_vmcnt<3>(); break;
+        default: wait_vmcnt<4>(); break;
+      }
+      // Chunk ch visible to all waves; all waves are done with chunk ch-1.
+      ring_barrier();
+      if (ch + kFuseRing - 1 < nch) MOE_FUSE_ISSUE(ch + kFuseRing - 1);
+      const char* slot = ring[ch % kFuseRing];
+      // Squares: x once (first expert tile), w for every tile.
+      if (et == 0) {  // x: row tid/16, elements 2(tid%16), +1 of the chunk
+        const int r = tid / 16, pq = tid % 16, c = pq / 4;
+        const uint32_t v = *reinterpret_cast<const uint32_t*>(
+            slot + (r / 16) * 1024 + ((r % 16) * 4 + (c ^ swz4(r % 16))) * 16 + (pq % 4) * 4);
+        const double a0 = bf16_to_f32(v & 0xffffu), a1 = bf16_to_f32(v >> 16);
+        sxp = fma(a0, a0, fma(a1, a1, sxp));
+      }
+      {  // w: expert row tid/8, elements 4(tid%8)..+3 of the chunk
+        const int r = tid / 8, pq = tid % 8, c = pq / 2;
+        const uint2 v = *reinterpret_cast<const uint2*>(
+            slot + 2048 + (r / 16) * 1024 + ((r % 16) * 4 + (c ^ swz4(r % 16))) * 16 + (pq % 2) * 8);
+        const double b0 = bf16_to_f32(v.x & 0xffffu), b1 = bf16_to_f32(v.x >> 16);
+        const double b2 = bf16_to_f32(v.y & 0xffffu), b3 = bf16_to_f32(v.y >> 16);
+        swp = fma(b0, b0, fma(b1, b1, fma(b2, b2, fma(b3, b3, swp))));
+      }
+      // MFMA: wave w takes token block w/4 (A = tokens 16(w/4) + (lane & 15))
+      // and expert block w%4 of the tile (B).
+      {
+        const int er = 16 * (wave % 4) + (lane & 15), cc = lane >> 4;
+        const bf16x8_t bw = *reinterpret_cast<const bf16x8_t*>(
+            slot + 2048 + (er / 16) * 1024 + ((er % 16) * 4 + (cc ^ swz4(er % 16))) * 16);
+        const int tr = lane & 15;
+        const bf16x8_t ax = *reinterpret_cast<const bf16x8_t*>(
+            slot + (wave / 4) * 1024 + (tr * 4 + (cc ^ swz4(tr))) * 16);
+        acc32 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ax, bw, acc32, 0, 0, 0);
+      }
+      if ((ch & 1) || ch == nch - 1) {  // fp32 chunks of at most 64 products
+#pragma unroll
+        for (int v = 0; v < 4; ++v) acc[v] += (double)acc32[v];
+        acc32 = floatx4{0.f, 0.f, 0.f, 0.f};
+      }
+    }
+#undef MOE_FUSE_ISSUE
+    // z~: lane holds expert (lane & 15) of block w%4, tokens 16(w/4) + 4*(lane>>4)+v.
+    const int e = et + 16 * (wave % 4) + (lane & 15);
+    if (e < E) {
+      const double bias = router_bias ? (double)router_bias[e] : 0.0;
+#pragma unroll
+      for (int v = 0; v < 4; ++v) zs[16 * (wave / 4) + 4 * (lane >> 4) + v][e] = (float)(acc[v] + bias);
+    }
+    // sum w^2: the 8 threads of an expert row are consecutive lanes.
+#pragma unroll
+    for (int o = 1; o < 8; o <<= 1) swp += __shfl_xor(swp, o, 64);
+    if (tid % 8 == 0 && et + tid / 8 < E) sw[et + tid / 8] = swp;
+    __syncthreads();  // ring slots are reused by the next expert tile
+  }
+#pragma unroll
+  for (int o = 1; o < 16; o <<= 1) sxp += __shfl_xor(sxp, o, 64);
+  if (tid % 16 == 0) sx[tid / 16] = sxp;
+  __syncthreads();
+
+  // ---- 2. certify -------------------------------------------------------
   const int per = E / G;
-  const int t_begin = blockIdx.x * kCertTokensPerBlock;
-  const int t_end = min(N, t_begin + kCertTokensPerBlock);
   double nw[4];
+  float sb[4];  // this lane's selection biases, read once per block
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
     const int e = lane + 64 * j;
-    nw[j] = e < E ? sqrt(sumsq_w[e]) : 0.0;
+    nw[j] = e < E ? sqrt(sw[e]) : 0.0;
+    sb[j] = (sel_bias && e < E) ? sel_bias[e] : 0.f;
   }
-  for (int t = t_begin + wave; t < t_end; t += kCertWaves) {
-    const double nx = sqrt(sumsq_x[t]);
+  for (int tl = wave; tl < nt; tl += kFuseWaves) {
+    const double nx = sqrt(sx[tl]);
     float lo[4], hi[4];
     bool ok[4];
 #pragma unroll
@@ -225,37 +224,37 @@ __global__ __launch_bounds__(kCertWaves * 64) void route_certify(
       lo[j] = -INFINITY;
       hi[j] = -INFINITY;
       if (ok[j]) {
-        const double zt = (double)logits[(size_t)t * E + e];
+        const double zt = (double)zs[tl][e];
         // 2^-16 |x||w| (with a relative pad for the rounded norms), 2^-22 |z|.
         const double m = 1.52587890625e-05 * (nx * nw[j]) * (1.0 + 1e-12) +
                          2.384185791015625e-07 * fabs(zt) + 1e-27;
-        const float zlo = __double2float_rd(zt - m), zhi = __double2float_ru(zt + m);
-        const float b = sel_bias ? sel_bias[e] : 0.f;
+        // Outward by one ulp after rounding to nearest: still an enclosure.
+        const float zlo = nextafterf(__double2float_rn(zt - m), -INFINITY);
+        const float zhi = nextafterf(__double2float_rn(zt + m), INFINITY);
+        const float b = sb[j];
         lo[j] = sel_score(zlo, score_fn, b);
         hi[j] = sel_score(zhi, score_fn, b);
       }
     }
-
     // Groups: certainly kept, undecided (bit masks over G <= 64 groups).
     uint64_t kept_c = ~0ull, undecided = 0ull;
     if (G > 1) {
-      // Group maxima of the lower and upper ends: lane g < G scans group g.
       float gl = -INFINITY, gh = -INFINITY;
 #pragma unroll
       for (int j = 0; j < 4; ++j)
         if (ok[j]) {
-          lo_s[wave][lane + 64 * j] = lo[j];
-          hi_s[wave][lane + 64 * j] = hi[j];
+          wsc[wave][lane + 64 * j] = lo[j];
+          wsc2[wave][lane + 64 * j] = hi[j];
         }
       __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
       __builtin_amdgcn_wave_barrier();
       if (lane < G) {
         for (int e = lane * per; e < (lane + 1) * per; ++e) {
-          gl = fmaxf(gl, lo_s[wave][e]);
-          gh = fmaxf(gh, hi_s[wave][e]);
+          gl = fmaxf(gl, wsc[wave][e]);
+          gh = fmaxf(gh, wsc2[wave][e]);
         }
-        glo_s[wave][lane] = gl;
-        ghi_s[wave][lane] = gh;
+        gsc[wave][0][lane] = gl;
+        gsc[wave][1][lane] = gh;
       }
       __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
       __builtin_amdgcn_wave_barrier();
@@ -264,7 +263,7 @@ __global__ __launch_bounds__(kCertWaves * 64) void route_certify(
         int could_beat = 0, beaten = 0;
         for (int h = 0; h < G; ++h) {
           if (h == lane) continue;
-          const float glh = glo_s[wave][h], ghh = ghi_s[wave][h];
+          const float glh = gsc[wave][0][h], ghh = gsc[wave][1][h];
           if (!certainly_before(gl, lane, ghh, h)) ++could_beat;
           if (certainly_before(glh, h, gh, lane)) ++beaten;
         }
@@ -275,7 +274,6 @@ __global__ __launch_bounds__(kCertWaves * 64) void route_certify(
       undecided = __ballot(lane < G && !keep && !drop);
       __builtin_amdgcn_wave_barrier();
     }
-
     // k-th largest lower end among experts of certainly kept groups.
     bool comp[4], elig[4];
 #pragma unroll
@@ -315,199 +313,120 @@ __global__ __launch_bounds__(kCertWaves * 64) void route_certify(
       }
       thr = ti < 0 ? -INFINITY : tv;
     }
-
     // Candidates: eligible experts that are not certainly out, plus possible
     // maxima of undecided groups.
     uint64_t cw[4];
+    int n = 0;
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       const int e = lane + 64 * j;
       bool c = elig[j] && hi[j] >= thr;
       if (ok[j] && G > 1) {
         const int g = e / per;
-        if ((undecided >> g) & 1ull) c = c || hi[j] >= glo_s[wave][g];
+        if ((undecided >> g) & 1ull) c = c || hi[j] >= gsc[wave][0][g];
       }
       cw[j] = __ballot(c);
+      n += __popcll(cw[j]);
     }
     if (lane < 4) {
       uint64_t v = cw[0];
 #pragma unroll
       for (int j = 1; j < 4; ++j)
         if (lane == j) v = cw[j];
-      cand[(size_t)t * 4 + lane] = v;
+      cand_s[tl][lane] = v;
     }
     if (lane == 0) {
-      gmask[(size_t)t * 2 + 0] = kept_c;
-      gmask[(size_t)t * 2 + 1] = undecided;
+      gm_s[tl][0] = kept_c;
+      gm_s[tl][1] = undecided;
+      cnt_s[tl] = n;
     }
-    int n = 0;
-#pragma unroll
-    for (int j = 0; j < 4; ++j) n += __popcll(cw[j]);
-    if (lane < 4) {
-      uint64_t v = cw[0];
-#pragma unroll
-      for (int j = 1; j < 4; ++j)
-        if (lane == j) v = cw[j];
-      cand_s[t - t_begin][lane] = v;
-    }
-    if (lane == 0) cnt_s[t - t_begin] = n;
   }
-
-  // Append this block's (t, e) pairs with one global atomic: an exclusive
-  // scan of the per-token counts (64 entries, one wave), then each wave
-  // writes the pairs of its tokens.
   __syncthreads();
-  const int nt = t_end - t_begin;
+  // Pair list in LDS: exclusive scan of the per-token counts, then each wave
+  // writes the pairs of its tokens.
   if (wave == 0) {
-    int c = lane < nt ? cnt_s[lane] : 0;
+    const int c = lane < nt ? cnt_s[lane] : 0;
     int incl = c;
 #pragma unroll
     for (int o = 1; o < 64; o <<= 1) {
       const int v = __shfl_up(incl, o, 64);
       if (lane >= o) incl += v;
     }
-    const int total = __shfl(incl, 63, 64);
-    int base = 0;
-    if (lane == 0) base = atomicAdd(pair_count, total);
-    base = __shfl(base, 0, 64);
-    if (lane < nt) cnt_s[lane] = base + incl - c;
+    if (lane < nt) cnt_s[lane] = incl - c;
+    if (lane == 63) npairs_s = incl;
   }
   __syncthreads();
-  for (int tl = wave; tl < nt; tl += kCertWaves) {
-    const int t = t_begin + tl;
+  for (int tl = wave; tl < nt; tl += kFuseWaves) {
     int base = cnt_s[tl];
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       const uint64_t m = cand_s[tl][j];
       const uint64_t below = lane == 0 ? 0ull : (m << (64 - lane));
-      if ((m >> lane) & 1ull) pairs[base + __popcll(below)] = (t << 8) | (lane + 64 * j);
+      if ((m >> lane) & 1ull) plist[base + __popcll(below)] = (uint16_t)((tl << 8) | (lane + 64 * j));
       base += __popcll(m);
     }
   }
-}
+  __syncthreads();
 
-// ------------------------------------------------------------- 3. exact ---
-
-// The definition for every listed pair: fp64 sum, left to right, of the exact
-// products x_ti w_ei, + bias, one rounding to fp32.  The sum is one
-// sequential chain per pair (its rounding order is part of the definition),
-// so a lane owns a pair; what the 64 lanes of a wave share is the memory
-// traffic.  A one-wave block takes groups of 64 consecutive list entries and
-// streams their x and w rows through LDS in chunks of 32 elements (64 bytes
-// of each row, 8 KB per chunk for the group) with global_load_lds_dwordx4,
-// up to kExactRing - 1 chunks ahead of the chains.  Load i of a chunk covers
-// the rows of pairs 16(i%4) .. 16(i%4)+15 (x for i < 4, w after); lane L
-// fetches row L/4 of those, logical 16-byte chunk (L % 4) ^ swz4(L / 4), so
-// the chains' 16-byte LDS reads of one chunk spread over the banks.  Needs
-// d % 32 == 0 (the launcher checks).
-constexpr int kExactRing = 8;    // LDS chunk slots per wave, 8 KB each
-constexpr int kExactBlocks = 2048;
-
-__global__ __launch_bounds__(64) void route_exact(const bf16_t* __restrict__ x,
-                                                  const bf16_t* __restrict__ w, int d, int E,
-                                                  const float* __restrict__ router_bias,
-                                                  const int32_t* __restrict__ pairs,
-                                                  const int32_t* __restrict__ pair_count,
-                                                  float* __restrict__ logits) {
-  __shared__ __attribute__((aligned(1024))) char ring[kExactRing][8192];
-  const int lane = threadIdx.x;
-  const int n = *pair_count;
-  const int nch = d / 32;
-  const int mine = (lane & 15) * 4;  // this lane's row inside its 1-KB block: byte offset / 16
-  const int msw = swz4(lane & 15);
-  for (int g0 = blockIdx.x * 64; g0 < n; g0 += gridDim.x * 64) {
-    const bool live = g0 + lane < n;
-    const int v = pairs[live ? g0 + lane : g0];  // idle lanes shadow a listed pair
-    const int t = v >> 8, e = v & 255;
-    const u32x4* src[8];
+  // ---- 3. exact ---------------------------------------------------------
+  // Pairs go to waves in groups of 64 (wave 0 first), one chain per lane;
+  // loads run 8 vectors (64 elements) ahead of the chain.
+  const int np = npairs_s;
+  for (int p = tid; p < np; p += kFuseWaves * 64) {
+    const int v = plist[p];
+    const int tl = v >> 8, e = v & 255;
+    const u32x4* xr = reinterpret_cast<const u32x4*>(x + (size_t)(t0 + tl) * d);
+    const u32x4* wr = reinterpret_cast<const u32x4*>(w + (size_t)e * d);
+    constexpr int AHEAD = 8;
+    const int nv = d / 8;  // a multiple of 4 (d % 32 == 0)
+    u32x4 xa[AHEAD], wa[AHEAD];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int q = 16 * i + lane / 4;  // pair whose rows this lane fetches
-      const int tq = __shfl(t, q, 64), eq = __shfl(e, q, 64);
-      const int c = (lane % 4) ^ swz4(lane / 4);
-      src[i] = reinterpret_cast<const u32x4*>(x + (size_t)tq * d) + c;
-      src[4 + i] = reinterpret_cast<const u32x4*>(w + (size_t)eq * d) + c;
+    for (int u = 0; u < AHEAD; ++u) {
+      xa[u] = u < nv ? xr[u] : u32x4{0u, 0u, 0u, 0u};
+      wa[u] = u < nv ? wr[u] : u32x4{0u, 0u, 0u, 0u};
     }
-#define MOE_EXACT_ISSUE(ch_)                                                                \
-  do {                                                                                      \
-    char* slot_ = ring[(ch_) % kExactRing];                                                 \
-    _Pragma("unroll") for (int i = 0; i < 8; ++i)                                           \
-        __builtin_amdgcn_global_load_lds((void*)(src[i] + (size_t)(ch_) * 4),               \
-                                         (lds_ptr_t)(slot_ + i * 1024), 16, 0, 0);          \
-  } while (0)
-#pragma unroll
-    for (int c = 0; c < kExactRing - 1; ++c)
-      if (c < nch) MOE_EXACT_ISSUE(c);
     double acc = 0.0;
-    for (int ch = 0; ch < nch; ++ch) {
-      // Chunk ch has landed once at most `later` younger chunks (8 loads
-      // each) are still in flight.
-      switch (min(kExactRing - 2, nch - 1 - ch)) {
-        case 0: wait_vmcnt<0>(); break;
-        case 1: wait_vmcnt<8>(); break;
-        case 2: wait_vmcnt<16>(); break;
-        case 3: wait_vmcnt<24>(); break;
-        case 4: wait_vmcnt<32>(); break;
-        case 5: wait_vmcnt<40>(); break;
-        default: wait_vmcnt<48>(); break;
-      }
-      __atomic_signal_fence(__ATOMIC_SEQ_CST);
-      // The slot of chunk ch-1 was consumed by the previous iteration.
-      if (ch + kExactRing - 1 < nch) MOE_EXACT_ISSUE(ch + kExactRing - 1);
-      const char* slot = ring[ch % kExactRing];
-      const char* xb = slot + (lane >> 4) * 1024;
-      const char* wb = slot + 4096 + (lane >> 4) * 1024;
+    for (int i0 = 0; i0 < nv; i0 += AHEAD) {
 #pragma unroll
-      for (int qq = 0; qq < 4; ++qq) {
-        const int pos = (mine + (qq ^ msw)) * 16;
-        const u32x4 a = *reinterpret_cast<const u32x4*>(xb + pos);
-        const u32x4 b = *reinterpret_cast<const u32x4*>(wb + pos);
+      for (int u = 0; u < AHEAD; ++u) {
+        const u32x4 a = xa[u], b = wa[u];
+        const int nxt = i0 + AHEAD + u;
+        if (nxt < nv) {
+          xa[u] = xr[nxt];
+          wa[u] = wr[nxt];
+        }
+        if (i0 + u < nv) {
 #pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          acc = __fma_rn((double)bf16_to_f32(a[q] & 0xffffu), (double)bf16_to_f32(b[q] & 0xffffu),
-                         acc);
-          acc = __fma_rn((double)bf16_to_f32(a[q] >> 16), (double)bf16_to_f32(b[q] >> 16), acc);
+          for (int q = 0; q < 4; ++q) {
+            acc = __fma_rn((double)bf16_to_f32(a[q] & 0xffffu),
+                           (double)bf16_to_f32(b[q] & 0xffffu), acc);
+            acc = __fma_rn((double)bf16_to_f32(a[q] >> 16), (double)bf16_to_f32(b[q] >> 16),
+                           acc);
+          }
         }
       }
-      __atomic_signal_fence(__ATOMIC_SEQ_CST);
     }
-#undef MOE_EXACT_ISSUE
-    if (live) {
-      if (router_bias) acc = acc + (double)router_bias[e];
-      logits[(size_t)t * E + e] = __double2float_rn(acc);
-    }
+    if (router_bias) acc = acc + (double)router_bias[e];
+    zs[tl][e] = __double2float_rn(acc);
   }
-}
-
-// ---------------------------------------------------------- 4. finalize ---
-
-__global__ __launch_bounds__(kCertWaves * 64) void route_finalize(
-    const float* __restrict__ logits, const float* __restrict__ sel_bias,
-    const uint64_t* __restrict__ cand, const uint64_t* __restrict__ gmask, int N, int E, int k,
-    int G, int kg, int score_fn, int32_t* __restrict__ topk_idx, float* __restrict__ topk_w,
-    int32_t* __restrict__ counts) {
-  __shared__ int32_t hist[256];
-  __shared__ float s_s[kCertWaves][256];
-  for (int e = threadIdx.x; e < E; e += blockDim.x) hist[e] = 0;
   __syncthreads();
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  const int per = E / G;
-  const int t_begin = blockIdx.x * kCertTokensPerBlock;
-  const int t_end = min(N, t_begin + kCertTokensPerBlock);
-  for (int t = t_begin + wave; t < t_end; t += kCertWaves) {
+
+  // ---- 4. finalize ------------------------------------------------------
+  for (int tl = wave; tl < nt; tl += kFuseWaves) {
+    const int t = t0 + tl;
     float z[4], s[4];
     bool is_c[4];
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       const int e = lane + 64 * j;
       const bool okj = e < E;
-      z[j] = okj ? logits[(size_t)t * E + e] : 0.f;
-      is_c[j] = okj && ((cand[(size_t)t * 4 + j] >> lane) & 1ull);
-      s[j] = is_c[j] ? sel_score(z[j], score_fn, sel_bias ? sel_bias[e] : 0.f) : -INFINITY;
+      z[j] = okj ? zs[tl][e] : 0.f;
+      is_c[j] = okj && ((cand_s[tl][j] >> lane) & 1ull);
+      s[j] = is_c[j] ? sel_score(z[j], score_fn, sb[j]) : -INFINITY;
     }
     uint64_t kept = ~0ull;
     if (G > 1) {
-      const uint64_t kept_c = gmask[(size_t)t * 2 + 0], undecided = gmask[(size_t)t * 2 + 1];
+      const uint64_t kept_c = gm_s[tl][0], undecided = gm_s[tl][1];
       kept = kept_c;
       const int need = kg - __popcll(kept_c);
       if (need > 0 && undecided) {
@@ -515,14 +434,14 @@ __global__ __launch_bounds__(kCertWaves * 64) void route_finalize(
         // candidates, so the maximum over candidates is the group score).
 #pragma unroll
         for (int j = 0; j < 4; ++j)
-          if (lane + 64 * j < E) s_s[wave][lane + 64 * j] = s[j];
+          if (lane + 64 * j < E) wsc[wave][lane + 64 * j] = s[j];
         __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
         __builtin_amdgcn_wave_barrier();
         float gs = 0.f;
         int gi = -1;
         if (lane < G && ((undecided >> lane) & 1ull)) {
           float m = -INFINITY;
-          for (int e = lane * per; e < (lane + 1) * per; ++e) m = fmaxf(m, s_s[wave][e]);
+          for (int e = lane * per; e < (lane + 1) * per; ++e) m = fmaxf(m, wsc[wave][e]);
           gs = m;
           gi = lane;
         }
@@ -565,7 +484,7 @@ __global__ __launch_bounds__(kCertWaves * 64) void route_finalize(
 #pragma unroll
         for (int j = 1; j < 4; ++j)
           if (jj == j) zv = z[j];
-        zsel[r] = __shfl(zv, owner, 64);
+        zsel[r] = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(zv), owner));
         if (lane == owner) {
 #pragma unroll
           for (int j = 0; j < 4; ++j)
@@ -619,62 +538,28 @@ __global__ __launch_bounds__(kCertWaves * 64) void route_finalize(
       if (my_e >= 0) atomicAdd(&hist[my_e], 1);
     }
   }
+  // The tile's logits (exact for candidates, z~ elsewhere) and counts.
+  for (int i = tid; i < nt * E; i += kFuseWaves * 64) logits[(size_t)t0 * E + i] = zs[i / E][i % E];
   __syncthreads();
-  for (int e = threadIdx.x; e < E; e += blockDim.x)
+  for (int e = tid; e < E; e += kFuseWaves * 64)
     if (hist[e]) atomicAdd(&counts[e], hist[e]);
 }
 
 // ---------------------------------------------------------------- launch ---
 
-static size_t a256(size_t v) { return (v + 255) / 256 * 256; }
-
-struct CertWs {
-  double* sumsq_x;
-  double* sumsq_w;
-  uint64_t* cand;
-  uint64_t* gmask;
-  int32_t* pairs;
-  int32_t* pair_count;
-};
-
-static CertWs cert_layout(void* ws, int N, int E) {
-  char* p = static_cast<char*>(ws);
-  CertWs c;
-  c.sumsq_x = reinterpret_cast<double*>(p);
-  p += a256((size_t)N * 8);
-  c.sumsq_w = reinterpret_cast<double*>(p);
-  p += a256((size_t)E * 8);
-  c.cand = reinterpret_cast<uint64_t*>(p);
-  p += a256((size_t)N * 4 * 8);
-  c.gmask = reinterpret_cast<uint64_t*>(p);
-  p += a256((size_t)N * 2 * 8);
-  c.pairs = reinterpret_cast<int32_t*>(p);
-  p += a256((size_t)N * E * 4);
-  c.pair_count = reinterpret_cast<int32_t*>(p);
-  return c;
-}
-
 size_t route_certified_workspace_bytes(int N, int E) {
-  if (N <= 0) return 0;
-  return a256((size_t)N * 8) + a256((size_t)E * 8) + a256((size_t)N * 32) + a256((size_t)N * 16) +
-         a256((size_t)N * E * 4) + 256;
+  (void)N;
+  (void)E;
+  return 0;  // everything lives in LDS
 }
 
 hipError_t launch_route_certified(const RouteArgs& a, hipStream_t st) {
-  const CertWs c = cert_layout(a.ws, a.N, a.E);
-  const bf16_t* x = static_cast<const bf16_t*>(a.x);
-  const bf16_t* w = static_cast<const bf16_t*>(a.w_router);
-  dim3 g1((a.N + kRouteTokTile - 1) / kRouteTokTile, (a.E + kRouteExpTile - 1) / kRouteExpTile);
-  logits_mfma<<<g1, 256, 0, st>>>(x, w, a.N, a.d, a.E, a.router_bias, a.logits, c.sumsq_x,
-                                   c.sumsq_w, a.counts, c.pair_count);
-  const int blocks = (a.N + kCertTokensPerBlock - 1) / kCertTokensPerBlock;
-  route_certify<<<blocks, kCertWaves * 64, 0, st>>>(a.logits, c.sumsq_x, c.sumsq_w, a.sel_bias, a.N, a.E,
-                                        a.k, a.G, a.kg, a.score_fn, c.cand, c.gmask, c.pairs,
-                                        c.pair_count);
-  route_exact<<<kExactBlocks, 64, 0, st>>>(x, w, a.d, a.E, a.router_bias, c.pairs,
-                                           c.pair_count, a.logits);
-  route_finalize<<<blocks, kCertWaves * 64, 0, st>>>(a.logits, a.sel_bias, c.cand, c.gmask, a.N, a.E, a.k,
-                                         a.G, a.kg, a.score_fn, a.topk_idx, a.topk_w, a.counts);
+  launch_zero_i32(a.counts, a.E, st);
+  const int blocks = (a.N + kFuseTok - 1) / kFuseTok;
+  route_fused<<<blocks, kFuseWaves * 64, 0, st>>>(static_cast<const bf16_t*>(a.x),
+                                      static_cast<const bf16_t*>(a.w_router), a.N, a.d, a.E, a.k,
+                                      a.G, a.kg, a.score_fn, a.router_bias, a.sel_bias, a.logits,
+                                      a.topk_idx, a.topk_w, a.counts);
   return hipGetLastError();
 }
 
