@@ -73,8 +73,10 @@ __device__ __forceinline__ float silu(float g) { return g * __builtin_amdgcn_rcp
 // row tiles of equal height, rounded up to whole 32-row MFMA fragments
 // (chunk_e = 32 ceil(ceil(rows_e / n_e) / 32) <= BM; since (n_e - 1) BM <
 // rows_e, no tile is empty).  Tile q of the batch is tiles[q] = {e, first
-// row, row end, 0}, and *count = number of tiles.  Rows are clamped to
-// max_rows.
+// row, row end, first 16-row group}, and *count = number of tiles.  The group
+// numbering gives every tile ceil(rows / 16) groups of its own, in tile order:
+// the packed hidden buffer of the bf16 FFN stores a tile's rows there.  Rows
+// are clamped to max_rows.
 __global__ __launch_bounds__(1024) void ffn_plan_tiles(const int32_t* __restrict__ offsets,
                                                        int E, int BM, int max_rows,
                                                        int4* __restrict__ tiles,
@@ -97,11 +99,27 @@ __global__ __launch_bounds__(1024) void ffn_plan_tiles(const int32_t* __restrict
     __syncthreads();
   }
   const int32_t start = s[e] - n;
-  for (int q = 0; q < n; ++q) {
-    const int32_t r0 = lo + q * chunk;
-    tiles[start + q] = make_int4(e, r0, min(hi, r0 + chunk), 0);
+  // 16-row groups of this expert's tiles, then their exclusive prefix.
+  int32_t ng = 0;
+  for (int q = 0; q < n; ++q) ng += (min(hi, lo + (q + 1) * chunk) - (lo + q * chunk) + 15) / 16;
+  __syncthreads();
+  const int32_t total_tiles = s[E - 1];
+  __syncthreads();
+  s[e] = ng;
+  __syncthreads();
+  for (int o = 1; o < 1024; o <<= 1) {
+    const int32_t v = e >= o ? s[e - o] : 0;
+    __syncthreads();
+    s[e] += v;
+    __syncthreads();
   }
-  if (e == E - 1) *count = s[e];
+  int32_t g0 = s[e] - ng;
+  for (int q = 0; q < n; ++q) {
+    const int32_t r0 = lo + q * chunk, r1 = min(hi, r0 + chunk);
+    tiles[start + q] = make_int4(e, r0, r1, g0);
+    g0 += (r1 - r0 + 15) / 16;
+  }
+  if (e == 0) *count = total_tiles;
 }
 
 // XCD-aware block order.  The hardware deals blocks round-robin over the 8
@@ -153,12 +171,21 @@ __host__ __device__ __forceinline__ int packed_slab_rows(int N) { return N % 256
 // consecutive columns, and stores 16 bytes per lane straight to global memory.
 constexpr int kGemmBM = 320, kGemmWaves = 8;
 
-template <int BN, int ACT>
+// MODE kUpGemm: A = the permuted rows (row-major [rows, K]), C = the packed
+// hidden buffer.  MODE kDownGemm: A = the packed hidden buffer, C = row-major
+// [rows, N].  The packed hidden buffer holds, for K stage t (32 columns) and
+// 16-row group g (tiles[q].w numbers a tile's groups), one 1-KB block at
+// element offset (t * ldg + g) * 512, laid out as the A stage rows sit in LDS
+// (16-byte position L: row L/4 of the group, logical chunk (L % 4) ^ swz4(L/4)),
+// so a down tile's K stage is one contiguous run.
+enum { kUpGemm = 0, kDownGemm = 1 };
+
+template <int BN, int ACT, int MODE>
 __global__ __launch_bounds__(kGemmWaves * 64, 1) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void grouped_gemm_bf16(
     const bf16_t* __restrict__ A, const bf16_t* __restrict__ B, const bf16_t* __restrict__ B2,
     bf16_t* __restrict__ C, int K, int N, const int4* __restrict__ tiles,
-    const int32_t* __restrict__ tile_count, int n_tiles) {
+    const int32_t* __restrict__ tile_count, int n_tiles, int ldg) {
   constexpr bool DUAL = ACT == ACT_SWIGLU;
   constexpr int BM = kGemmBM, BK = 32, RB = BK * 2;  // RB: bytes per staged row
   constexpr int CH = BK / 8;                         // 16-byte chunks per row
@@ -184,7 +211,7 @@ void grouped_gemm_bf16(
   if (logical < 0) return;
   const int mt = logical / n_tiles, nt = logical % n_tiles;
   const int4 tile = tiles[mt];
-  const int e = tile.x, r0 = tile.y, r1 = tile.z;
+  const int e = tile.x, r0 = tile.y, r1 = tile.z, g0 = tile.w;
   const int n0 = nt * BN;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wm = wave / 4, wn = wave % 4;
@@ -197,7 +224,16 @@ void grouped_gemm_bf16(
   const bf16_t* src[LMAX];
   int ldst;  // LDS byte offset (within a stage) of this wave's first load
   size_t kstep;
-  if (a_wave) {
+  if (a_wave && MODE == kDownGemm) {
+    ldst = grp * LA * 1024;
+    kstep = (size_t)ldg * 512;
+    const int last = (r1 - r0 - 1) / RPL;  // the tile's last 16-row group
+#pragma unroll
+    for (int i = 0; i < LMAX; ++i) {
+      const int g = min(grp * LA + (i < LA ? i : 0), last);  // groups past the tile: fetched, never used
+      src[i] = A + (size_t)(g0 + g) * 512 + lane * 8;
+    }
+  } else if (a_wave) {
     ldst = grp * LA * 1024;
     kstep = BK;
 #pragma unroll
@@ -334,7 +370,8 @@ void grouped_gemm_bf16(
 #define MOE_EPILOGUE(FA_)                                                                  \
   do {                                                                                     \
     _Pragma("unroll") for (int i = 0; i < (FA_); ++i) {                                    \
-      const int row = r0 + (2 * i + wm) * 32 + (lane & 31);                                \
+      const int lr = (2 * i + wm) * 32 + (lane & 31); /* row within the tile */            \
+      const int row = r0 + lr;                                                             \
       _Pragma("unroll") for (int j = 0; j < FN; ++j)                                       \
       _Pragma("unroll") for (int p = 0; p < 2; ++p) {                                      \
         float o[8];                                                                        \
@@ -350,7 +387,13 @@ void grouped_gemm_bf16(
         const int col = n0 + wn * WN + j * 32 + 16 * p + 8 * (lane >> 5);                  \
         if (row < r1 && col < N) {                                                         \
           const u32x4 v = {s0[0], s1[0], s0[1], s1[1]};                                    \
-          *reinterpret_cast<u32x4*>(C + (size_t)row * N + col) = v;                        \
+          if (MODE == kUpGemm) {                                                           \
+            const int r16 = lr % 16, pos = 4 * r16 + (((col % 32) / 8) ^ swz4(r16));        \
+            *reinterpret_cast<u32x4*>(C + ((size_t)(col / 32) * ldg + g0 + lr / 16) * 512 + \
+                                      pos * 8) = v;                                        \
+          } else {                                                                         \
+            *reinterpret_cast<u32x4*>(C + (size_t)row * N + col) = v;                      \
+          }                                                                                \
         }                                                                                  \
       }                                                                                    \
     }                                                                                      \
@@ -504,11 +547,18 @@ static size_t ffn_plan_bytes(int E, int max_rows, int dtype) {
          align256((size_t)max_m_tiles(max_rows, ffn_bm(dtype), E) * sizeof(int4));
 }
 
+// 16-row groups of the packed bf16 hidden buffer: each tile rounds its rows up
+// to whole groups, so at most one partial group per tile.
+static int ffn_groups(int E, int max_rows) {
+  return (max_rows + 15) / 16 + max_m_tiles(max_rows, kGemmBM, E);
+}
+
 size_t ffn_workspace_bytes(int E, int max_rows, int d, int h, int act, int dtype) {
   (void)d;
   (void)act;
-  const size_t elem = dtype == 0 ? 4 : 2;
-  return ffn_plan_bytes(E, max_rows, dtype) + align256((size_t)max_rows * h * elem);
+  const size_t hidden = dtype == 0 ? (size_t)max_rows * h * 4
+                                   : (size_t)ffn_groups(E, max_rows) * 16 * h * 2;
+  return ffn_plan_bytes(E, max_rows, dtype) + align256(hidden);
 }
 
 static int32_t* ffn_count(const FfnArgs& a) { return static_cast<int32_t*>(a.ws); }
@@ -530,13 +580,13 @@ hipError_t launch_ffn_plan(const FfnArgs& a, hipStream_t st) {
   return hipGetLastError();
 }
 
-template <int BN, int ACT>
+template <int BN, int ACT, int MODE>
 static void launch_bf16(const bf16_t* A, const bf16_t* B, const bf16_t* B2, bf16_t* C, int K,
                         int N, const FfnArgs& a, hipStream_t st) {
   const int nt = (N + BN - 1) / BN;
   const int g = grid_of(max_m_tiles(a.max_rows, kGemmBM, a.E), nt);
-  grouped_gemm_bf16<BN, ACT><<<g, kGemmWaves * 64, 0, st>>>(A, B, B2, C, K, N, ffn_tiles(a),
-                                                             ffn_count(a), nt);
+  grouped_gemm_bf16<BN, ACT, MODE><<<g, kGemmWaves * 64, 0, st>>>(
+      A, B, B2, C, K, N, ffn_tiles(a), ffn_count(a), nt, ffn_groups(a.E, a.max_rows));
 }
 
 template <int ACT>
@@ -561,13 +611,13 @@ hipError_t launch_ffn_up(const FfnArgs& a, hipStream_t st) {
     auto W1 = static_cast<const bf16_t*>(a.w1);
     auto W3 = static_cast<const bf16_t*>(a.w3);
     auto H = static_cast<bf16_t*>(ffn_hidden_buf(a));
-    if (a.act == ACT_SWIGLU) launch_bf16<128, ACT_SWIGLU>(X, W1, W3, H, a.d, a.h, a, st);
+    if (a.act == ACT_SWIGLU) launch_bf16<128, ACT_SWIGLU, kUpGemm>(X, W1, W3, H, a.d, a.h, a, st);
     else if (a.h >= 2048) {
-      if (a.act == ACT_RELU) launch_bf16<256, ACT_RELU>(X, W1, nullptr, H, a.d, a.h, a, st);
-      else launch_bf16<256, ACT_GELU>(X, W1, nullptr, H, a.d, a.h, a, st);
+      if (a.act == ACT_RELU) launch_bf16<256, ACT_RELU, kUpGemm>(X, W1, nullptr, H, a.d, a.h, a, st);
+      else launch_bf16<256, ACT_GELU, kUpGemm>(X, W1, nullptr, H, a.d, a.h, a, st);
     } else {
-      if (a.act == ACT_RELU) launch_bf16<128, ACT_RELU>(X, W1, nullptr, H, a.d, a.h, a, st);
-      else launch_bf16<128, ACT_GELU>(X, W1, nullptr, H, a.d, a.h, a, st);
+      if (a.act == ACT_RELU) launch_bf16<128, ACT_RELU, kUpGemm>(X, W1, nullptr, H, a.d, a.h, a, st);
+      else launch_bf16<128, ACT_GELU, kUpGemm>(X, W1, nullptr, H, a.d, a.h, a, st);
     }
   }
   return hipGetLastError();
@@ -582,8 +632,8 @@ hipError_t launch_ffn_down(const FfnArgs& a, hipStream_t st) {
     auto H = static_cast<const bf16_t*>(ffn_hidden_buf(a));
     auto W2 = static_cast<const bf16_t*>(a.w2);
     auto Y = static_cast<bf16_t*>(a.y_rows);
-    if (a.d >= 1024) launch_bf16<256, ACT_NONE>(H, W2, nullptr, Y, a.h, a.d, a, st);
-    else launch_bf16<128, ACT_NONE>(H, W2, nullptr, Y, a.h, a.d, a, st);
+    if (a.d >= 1024) launch_bf16<256, ACT_NONE, kDownGemm>(H, W2, nullptr, Y, a.h, a.d, a, st);
+    else launch_bf16<128, ACT_NONE, kDownGemm>(H, W2, nullptr, Y, a.h, a.d, a, st);
   }
   return hipGetLastError();
 }
