@@ -10,6 +10,8 @@
 // t-major, j-minor order) that chose e -- a stable counting sort.
 //
 // Kernels (slots are the N*k flattened (t, j) pairs, in tiles of 1024):
+//  count       one block: per-tile, per-expert histogram in LDS and the scan
+//              below, when tiles * E fits in LDS (else tile_hist + scan).
 //  tile_hist   per-tile, per-expert histogram (LDS atomics).
 //  scan        one block: per expert, exclusive prefix of the tile histograms
 //              (in place), admitted = min(count, cap), exclusive scan over
@@ -88,6 +90,66 @@ __global__ __launch_bounds__(256) void dispatch_scan(int32_t* __restrict__ tile_
   const int per = E / R;
   for (int r = threadIdx.x; r <= R; r += 256) rank_offsets[r] = offs[r * per];
   for (int r = threadIdx.x; r < R; r += 256) rank_counts[r] = offs[(r + 1) * per] - offs[r * per];
+}
+
+// Histogram and scan in one block of 1024 threads, for batches whose per-tile
+// histograms fit in LDS (tiles * E <= kCountLds): the per-tile, per-expert
+// counts are taken with LDS atomics over every slot, then thread e turns
+// expert e's column into exclusive tile bases (written for dispatch_assign)
+// and the same per-expert / per-rank offsets as dispatch_scan follow.
+constexpr int kCountLds = 16384;  // ints
+
+__global__ __launch_bounds__(1024) void dispatch_count(const int32_t* __restrict__ topk_idx,
+                                                       int S, int num_tiles, int E, int R,
+                                                       int32_t cap,
+                                                       int32_t* __restrict__ tile_base,
+                                                       int32_t* __restrict__ expert_offsets,
+                                                       int32_t* __restrict__ admitted,
+                                                       int32_t* __restrict__ rank_offsets,
+                                                       int32_t* __restrict__ rank_counts) {
+  __shared__ int32_t h[kCountLds];
+  __shared__ int32_t scan[1024];
+  __shared__ int32_t offs[1025];
+  const int tid = threadIdx.x;
+  const int cells = num_tiles * E;
+  for (int q = tid; q < cells; q += 1024) h[q] = 0;
+  __syncthreads();
+  for (int s = tid; s < S; s += 1024) {
+    const int e = topk_idx[s];
+    if ((unsigned)e < (unsigned)E) atomicAdd(&h[(s / kTileSlots) * E + e], 1);  // ids out of range are ignored
+  }
+  __syncthreads();
+  int32_t run = 0;
+  if (tid < E) {
+    for (int t = 0; t < num_tiles; ++t) {
+      const int32_t c = h[t * E + tid];
+      tile_base[(size_t)t * E + tid] = run;
+      run += c;
+    }
+  }
+  const int32_t adm = tid < E ? min(run, cap) : 0;
+  if (tid < E) admitted[tid] = adm;
+  scan[tid] = adm;
+  __syncthreads();
+  for (int o = 1; o < 1024; o <<= 1) {
+    const int32_t v = tid >= o ? scan[tid - o] : 0;
+    __syncthreads();
+    scan[tid] += v;
+    __syncthreads();
+  }
+  const int32_t excl = scan[tid] - adm;
+  if (tid < E) {
+    expert_offsets[tid] = excl;
+    offs[tid] = excl;
+  }
+  if (tid == E - 1) {
+    expert_offsets[E] = scan[tid];
+    offs[E] = scan[tid];
+  }
+  __syncthreads();
+  const int per = E / R;
+  for (int r = tid; r <= R; r += 1024) rank_offsets[r] = offs[r * per];
+  for (int r = tid; r < R; r += 1024) rank_counts[r] = offs[(r + 1) * per] - offs[r * per];
 }
 
 __device__ __forceinline__ uint64_t lanemask_lt(int lane) {
@@ -220,11 +282,15 @@ hipError_t launch_dispatch(const DispatchArgs& a, hipStream_t st) {
   const int S = a.N * a.k;
   const int tiles = (S + kTileSlots - 1) / kTileSlots;
   int32_t* tile_counts = static_cast<int32_t*>(a.ws);
-  if (tiles > 0) {
-    dispatch_tile_hist<<<tiles, 256, 0, st>>>(a.topk_idx, S, a.E, tile_counts);
+  if (tiles > 0 && (long long)tiles * a.E <= kCountLds && a.E <= 1024) {
+    dispatch_count<<<1, 1024, 0, st>>>(a.topk_idx, S, tiles, a.E, a.R, a.cap, tile_counts,
+                                       a.expert_offsets, a.admitted, a.rank_offsets,
+                                       a.rank_counts);
+  } else {
+    if (tiles > 0) dispatch_tile_hist<<<tiles, 256, 0, st>>>(a.topk_idx, S, a.E, tile_counts);
+    dispatch_scan<<<1, 256, 0, st>>>(tile_counts, tiles, a.E, a.R, a.cap, a.expert_offsets,
+                                     a.admitted, a.rank_offsets, a.rank_counts);
   }
-  dispatch_scan<<<1, 256, 0, st>>>(tile_counts, tiles, a.E, a.R, a.cap, a.expert_offsets,
-                                   a.admitted, a.rank_offsets, a.rank_counts);
   if (tiles == 0) return hipGetLastError();
   dispatch_assign<<<tiles, 256, 0, st>>>(a.topk_idx, S, a.k, a.E, a.cap, tile_counts,
                                          a.expert_offsets, a.row_of_slot, a.token_of_row,
