@@ -131,59 +131,68 @@ __global__ __launch_bounds__(kFuseWaves * 64, 2) void route_fused(
                                        (lds_ptr_t)(ring[(ch_) % kFuseRing] + wave * 1024),  \
                                        16, 0, 0);                                           \
   } while (0)
-#pragma unroll
-    for (int c = 0; c < kFuseRing - 1; ++c)
-      if (c < nch) MOE_FUSE_ISSUE(c);
+    // Chunks are consumed in pairs: one wait and one barrier per pair, and the
+    // two chunks' LDS reads and arithmetic overlap.  The prologue issues
+    // kFuseRing - 2 chunks; each pair step refills the two slots the previous
+    // pair used.
+    static_assert(kFuseRing >= 4, "two slots refilled per pair step");
+    for (int c = 0; c < kFuseRing - 2 && c < nch; ++c) MOE_FUSE_ISSUE(c);
     double swp = 0.0;  // sum w^2 part: expert row tid/8 of the tile, 4 elements per chunk
     floatx4 acc32 = floatx4{0.f, 0.f, 0.f, 0.f};
     double acc[4] = {0.0, 0.0, 0.0, 0.0};
-    for (int ch = 0; ch < nch; ++ch) {
-      // One load per chunk per loading wave: chunk ch has landed once at most
-      // `later` younger chunks are in flight.
-      switch (min(kFuseRing - 2, nch - 1 - ch)) {
+#define MOE_FUSE_CHUNK(ch_)                                                                 \
+  do {                                                                                      \
+    const char* slot = ring[(ch_) % kFuseRing];                                             \
+    /* Squares: x once (first expert tile), w for every tile. */                           \
+    if (et == 0) { /* x: row tid/16, elements 2(tid%16), +1 of the chunk */                \
+      const int r = tid / 16, pq = tid % 16, c = pq / 4;                                    \
+      const uint32_t v = *reinterpret_cast<const uint32_t*>(                                \
+          slot + (r / 16) * 1024 + ((r % 16) * 4 + (c ^ swz4(r % 16))) * 16 + (pq % 4) * 4);  \
+      const double a0 = bf16_to_f32(v & 0xffffu), a1 = bf16_to_f32(v >> 16);                \
+      sxp = fma(a0, a0, fma(a1, a1, sxp));                                                  \
+    }                                                                                       \
+    { /* w: expert row tid/8, elements 4(tid%8)..+3 of the chunk */                        \
+      const int r = tid / 8, pq = tid % 8, c = pq / 2;                                      \
+      const uint2 v = *reinterpret_cast<const uint2*>(                                      \
+          slot + 2048 + (r / 16) * 1024 + ((r % 16) * 4 + (c ^ swz4(r % 16))) * 16 + (pq % 2) * 8); \
+      const double b0 = bf16_to_f32(v.x & 0xffffu), b1 = bf16_to_f32(v.x >> 16);            \
+      const double b2 = bf16_to_f32(v.y & 0xffffu), b3 = bf16_to_f32(v.y >> 16);            \
+      swp = fma(b0, b0, fma(b1, b1, fma(b2, b2, fma(b3, b3, swp))));                        \
+    }                                                                                       \
+    /* MFMA: wave w takes token block w/4 (A = tokens 16(w/4) + (lane & 15)) */            \
+    /* and expert block w%4 of the tile (B). */                                             \
+    {                                                                                       \
+      const int er = 16 * (wave % 4) + (lane & 15), cc = lane >> 4;                         \
+      const bf16x8_t bw = *reinterpret_cast<const bf16x8_t*>(                               \
+          slot + 2048 + (er / 16) * 1024 + ((er % 16) * 4 + (cc ^ swz4(er % 16))) * 16);    \
+      const int tr = lane & 15;                                                             \
+      const bf16x8_t ax = *reinterpret_cast<const bf16x8_t*>(                               \
+          slot + (wave / 4) * 1024 + (tr * 4 + (cc ^ swz4(tr))) * 16);                      \
+      acc32 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ax, bw, acc32, 0, 0, 0);              \
+    }                                                                                       \
+  } while (0)
+    for (int ch = 0; ch < nch; ch += 2) {
+      const bool two = ch + 1 < nch;
+      // The pair's last chunk has landed once at most `later` younger chunks
+      // (one load each per loading wave) are in flight.
+      switch (two ? min(kFuseRing - 4, nch - 2 - ch) : 0) {
         case 0: wait_vmcnt<0>(); break;
         case 1: wait_vmcnt<1>(); break;
-        case 2: wait_vmcnt<2>(); break;
-        case 3: wait_vmcnt<3>(); break;
-        default: wait_vmcnt<4>(); break;
+        default: wait_vmcnt<2>(); break;
       }
-      // Chunk ch visible to all waves; all waves are done with chunk ch-1.
+      // The pair is visible to all waves; all waves are done with the previous
+      // pair, whose two slots are refilled now.
       ring_barrier();
+      if (ch + kFuseRing - 2 < nch) MOE_FUSE_ISSUE(ch + kFuseRing - 2);
       if (ch + kFuseRing - 1 < nch) MOE_FUSE_ISSUE(ch + kFuseRing - 1);
-      const char* slot = ring[ch % kFuseRing];
-      // Squares: x once (first expert tile), w for every tile.
-      if (et == 0) {  // x: row tid/16, elements 2(tid%16), +1 of the chunk
-        const int r = tid / 16, pq = tid % 16, c = pq / 4;
-        const uint32_t v = *reinterpret_cast<const uint32_t*>(
-            slot + (r / 16) * 1024 + ((r % 16) * 4 + (c ^ swz4(r % 16))) * 16 + (pq % 4) * 4);
-        const double a0 = bf16_to_f32(v & 0xffffu), a1 = bf16_to_f32(v >> 16);
-        sxp = fma(a0, a0, fma(a1, a1, sxp));
-      }
-      {  // w: expert row tid/8, elements 4(tid%8)..+3 of the chunk
-        const int r = tid / 8, pq = tid % 8, c = pq / 2;
-        const uint2 v = *reinterpret_cast<const uint2*>(
-            slot + 2048 + (r / 16) * 1024 + ((r % 16) * 4 + (c ^ swz4(r % 16))) * 16 + (pq % 2) * 8);
-        const double b0 = bf16_to_f32(v.x & 0xffffu), b1 = bf16_to_f32(v.x >> 16);
-        const double b2 = bf16_to_f32(v.y & 0xffffu), b3 = bf16_to_f32(v.y >> 16);
-        swp = fma(b0, b0, fma(b1, b1, fma(b2, b2, fma(b3, b3, swp))));
-      }
-      // MFMA: wave w takes token block w/4 (A = tokens 16(w/4) + (lane & 15))
-      // and expert block w%4 of the tile (B).
-      {
-        const int er = 16 * (wave % 4) + (lane & 15), cc = lane >> 4;
-        const bf16x8_t bw = *reinterpret_cast<const bf16x8_t*>(
-            slot + 2048 + (er / 16) * 1024 + ((er % 16) * 4 + (cc ^ swz4(er % 16))) * 16);
-        const int tr = lane & 15;
-        const bf16x8_t ax = *reinterpret_cast<const bf16x8_t*>(
-            slot + (wave / 4) * 1024 + (tr * 4 + (cc ^ swz4(tr))) * 16);
-        acc32 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ax, bw, acc32, 0, 0, 0);
-      }
-      if ((ch & 1) || ch == nch - 1) {  // fp32 chunks of at most 64 products
+      MOE_FUSE_CHUNK(ch);
+      if (two) MOE_FUSE_CHUNK(ch + 1);
+      // fp32 chunks of at most 64 products, summed in fp64.
 #pragma unroll
-        for (int v = 0; v < 4; ++v) acc[v] += (double)acc32[v];
-        acc32 = floatx4{0.f, 0.f, 0.f, 0.f};
-      }
+      for (int v = 0; v < 4; ++v) acc[v] += (double)acc32[v];
+      acc32 = floatx4{0.f, 0.f, 0.f, 0.f};
     }
+#undef MOE_FUSE_CHUNK
 #undef MOE_FUSE_ISSUE
     // z~: lane holds expert (lane & 15) of block w%4, tokens 16(w/4) + 4*(lane>>4)+v.
     const int e = et + 16 * (wave % 4) + (lane & 15);
