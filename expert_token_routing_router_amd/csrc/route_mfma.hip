@@ -41,8 +41,10 @@ typedef float floatx4 __attribute__((ext_vector_type(4)));
 //                experts that can still be selected or can still be the
 //                maximum of an undecided group become (token, expert) pairs.
 //  3. exact      the definition for every pair -- fp64 sum left to right of
-//                exact products, + bias, one rounding -- one sequential chain
-//                per lane, pairs packed densely into as few waves as possible;
+//                exact products, + bias, one rounding.  Where a test on the
+//                products' exponents proves that chain rounds nowhere, 16
+//                lanes sum the pair's products in any order (same bits);
+//                otherwise one lane runs the chain itself;
 //                the rows were streamed in step 1, so they come from L2.
 //  4. finalize   one wave per token: group and top-k selection from exact
 //                values (every expert outside the candidate set is certainly
@@ -85,7 +87,7 @@ __global__ __launch_bounds__(kFuseWaves * 64, 2) void route_fused(
   __shared__ uint64_t cand_s[kFuseTok][4], gm_s[kFuseTok][2];
   __shared__ int32_t cnt_s[kFuseTok];
   __shared__ int32_t hist[kFuseMaxE];
-  __shared__ int32_t npairs_s;
+  __shared__ int32_t npairs_s, nfb_s;
   // After step 1 the ring holds, at different times, the per-wave scratch of
   // the group limit (steps 2 and 4) and the pair list (end of 2, step 3).
   uint16_t* plist = reinterpret_cast<uint16_t*>(&ring[0][0]);  // (t_local << 8) | e
@@ -94,7 +96,8 @@ __global__ __launch_bounds__(kFuseWaves * 64, 2) void route_fused(
   ExpRow* wsc = reinterpret_cast<ExpRow*>(&ring[0][0]);                       // [8][E]: lower ends / scores
   ExpRow* wsc2 = reinterpret_cast<ExpRow*>(&ring[0][0] + kFuseWaves * 1024);  // [8][E]: upper ends
   GroupRows* gsc = reinterpret_cast<GroupRows*>(&ring[0][0] + 2 * kFuseWaves * 1024);
-  static_assert(kFuseTok * kFuseMaxE * 2 <= kFuseRing * kFuseSlot, "pair list fits the ring");
+  static_assert(2 * kFuseTok * kFuseMaxE * 2 <= kFuseRing * kFuseSlot,
+                "pair list and fallback list fit the ring");
   static_assert(2 * kFuseWaves * 1024 + kFuseWaves * 512 <= kFuseRing * kFuseSlot,
                 "group-limit scratch fits the ring");
   static_assert(kFuseTok <= 64 && kFuseMaxE <= 256, "pair encoding and one-wave token scan");
@@ -362,7 +365,10 @@ __global__ __launch_bounds__(kFuseWaves * 64, 2) void route_fused(
       if (lane >= o) incl += v;
     }
     if (lane < nt) cnt_s[lane] = incl - c;
-    if (lane == 63) npairs_s = incl;
+    if (lane == 63) {
+      npairs_s = incl;
+      nfb_s = 0;
+    }
   }
   __syncthreads();
   for (int tl = wave; tl < nt; tl += kFuseWaves) {
@@ -378,11 +384,91 @@ __global__ __launch_bounds__(kFuseWaves * 64, 2) void route_fused(
   __syncthreads();
 
   // ---- 3. exact ---------------------------------------------------------
-  // Pairs go to waves in groups of 64 (wave 0 first), one chain per lane;
-  // loads run 8 vectors (64 elements) ahead of the chain.
+  // The definition sums exact products left to right in fp64.  Every
+  // partial sum of that chain is exact when all products are multiples of
+  // 2^m and sum |x_i w_i| < 2^(m+53): then the fp64 result is the exact dot
+  // product, and any order of summation gives the same bits.  A product p of
+  // two bf16 values is a multiple of 2^(frexp_exp(p) - 16) (8-bit
+  // significands, so its lowest bit sits at most 16 places below its top
+  // bit, which is frexp_exp(p) - 1); a zero product reports exponent 0,
+  // which can only lower the minimum.  Cauchy-Schwarz bounds sum |x_i w_i|
+  // by sqrt(sum x^2 * sum w^2), both already summed in step 1 (their fp64
+  // rounding is covered by the 2^-20 pad).  So: 16 lanes per pair, each
+  // summing a strided share of the products; the pair's lanes reduce the
+  // sum and the minimum exponent; pairs that pass the test are done, the
+  // others go to a list and run the chain one lane each below.
   const int np = npairs_s;
-  for (int p = tid; p < np; p += kFuseWaves * 64) {
-    const int v = plist[p];
+  uint16_t* fb = plist + kFuseTok * kFuseMaxE;  // pairs that need the chain
+  {
+    const int q = tid >> 4, s16 = tid & 15;
+    const int nv = d / 8;  // 16-byte vectors per row
+    for (int p = q; p - q < np; p += kFuseWaves * 4) {
+      // Four partial sums (exact, so they may be split and regrouped freely)
+      // keep the fp64 adds off one dependency chain; loads run 4 vectors
+      // ahead of the arithmetic.
+      constexpr int AHEAD = 4;
+      double acc4[4] = {0.0, 0.0, 0.0, 0.0};
+      int emin = 0x7fffffff;
+      int tl = 0, e = 0;
+      if (p < np) {
+        const int v = plist[p];
+        tl = v >> 8;
+        e = v & 255;
+        const u32x4* xr = reinterpret_cast<const u32x4*>(x + (size_t)(t0 + tl) * d);
+        const u32x4* wr = reinterpret_cast<const u32x4*>(w + (size_t)e * d);
+        u32x4 xa[AHEAD], wa[AHEAD];
+#pragma unroll
+        for (int u = 0; u < AHEAD; ++u) {
+          const int i = s16 + 16 * u;
+          xa[u] = i < nv ? xr[i] : u32x4{0u, 0u, 0u, 0u};
+          wa[u] = i < nv ? wr[i] : u32x4{0u, 0u, 0u, 0u};
+        }
+        for (int i0 = s16; i0 < nv; i0 += 16 * AHEAD) {
+#pragma unroll
+          for (int u = 0; u < AHEAD; ++u) {
+            const u32x4 a = xa[u], b = wa[u];
+            const int nxt = i0 + 16 * (AHEAD + u);
+            if (nxt < nv) {
+              xa[u] = xr[nxt];
+              wa[u] = wr[nxt];
+            }
+            if (i0 + 16 * u < nv) {
+#pragma unroll
+              for (int h = 0; h < 4; ++h) {
+                const double p0 =
+                    (double)bf16_to_f32(a[h] & 0xffffu) * (double)bf16_to_f32(b[h] & 0xffffu);
+                const double p1 = (double)bf16_to_f32(a[h] >> 16) * (double)bf16_to_f32(b[h] >> 16);
+                acc4[h] += p0;
+                acc4[h] += p1;
+                emin = min(emin, min(__builtin_amdgcn_frexp_exp(p0), __builtin_amdgcn_frexp_exp(p1)));
+              }
+            }
+          }
+        }
+      }
+      double acc = (acc4[0] + acc4[1]) + (acc4[2] + acc4[3]);
+#pragma unroll
+      for (int o = 8; o >= 1; o >>= 1) {
+        acc += __shfl_xor(acc, o, 64);
+        emin = min(emin, __shfl_xor(emin, o, 64));
+      }
+      if (p < np && s16 == 0) {
+        const double bound = sqrt(sx[tl] * sw[e]) * (1.0 + 0x1p-20);
+        if (bound < ldexp(1.0, min(emin, 1000) - 16 + 53)) {
+          if (router_bias) acc = acc + (double)router_bias[e];
+          zs[tl][e] = __double2float_rn(acc);
+        } else {
+          fb[atomicAdd(&nfb_s, 1)] = (uint16_t)((tl << 8) | e);
+        }
+      }
+    }
+  }
+  __syncthreads();
+  // The chain itself for the pairs the test did not settle, one per lane;
+  // loads run 8 vectors (64 elements) ahead of it.
+  const int nfb = nfb_s;
+  for (int p = tid; p < nfb; p += kFuseWaves * 64) {
+    const int v = fb[p];
     const int tl = v >> 8, e = v & 255;
     const u32x4* xr = reinterpret_cast<const u32x4*>(x + (size_t)(t0 + tl) * d);
     const u32x4* wr = reinterpret_cast<const u32x4*>(w + (size_t)e * d);

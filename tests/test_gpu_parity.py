@@ -93,6 +93,44 @@ def test_route_bit_exact(name):
     assert np.abs(gpu["topk_w"].numpy() - ref["topk_w"]).max() <= TOPK_W_TOL
 
 
+def test_route_exact_where_the_chain_rounds():
+    """Rows whose fp64 chain rounds cannot be summed in another order.  In
+    every fourth token the first and last elements are +2^60 and -2^60 and
+    the router's first and last columns are equal: left to right, the small
+    products in between vanish against 2^60 w_e0 and the logit is the bias
+    alone, while the exact dot product is their sum (every one of those
+    logits differs).  Every fourth token, offset by one, has elements 2^-100
+    times smaller (products over too many binades for any order but the
+    chain).  Mixed in one tile with ordinary rows, every selected logit must
+    be the definition's left-to-right fp64 value, bit for bit (glossary
+    "Expert Parallelism", step 1: the Linear router)."""
+    cfg = W.small("switch")
+    d = cfg["d"]
+    inp_cpu = W.make_inputs(cfg, weights=False)
+    x = inp_cpu["x"].float()
+    w = inp_cpu["w_router"].float()
+    w[:, d - 1] = w[:, 0]
+    t = torch.arange(cfg["N"])
+    big = t % 4 == 0
+    x[big, 0] = 2.0 ** 60
+    x[big, d - 1] = -2.0 ** 60
+    tiny = t % 4 == 1
+    x[tiny, ::5] *= 2.0 ** -100
+    inp_cpu["x"] = x.bfloat16()
+    inp_cpu["w_router"] = w.bfloat16()
+    print(f"[chain rounds] N={cfg['N']} d={cfg['d']} E={cfg['E']}", flush=True)
+    buf = _route_dispatch(cfg, inp_cpu)
+    r = oracle.route(cfg, n(inp_cpu["x"]), n(inp_cpu["w_router"]), n(inp_cpu["router_bias"]),
+                     n(inp_cpu["sel_bias"]))
+    zr = torch.from_numpy(r["logits"])
+    sel = torch.from_numpy(r["topk_idx"]).long()
+    assert torch.equal(bits_t(buf.logits.cpu().gather(1, sel)), bits_t(zr.gather(1, sel)))
+    m = certified_margin(inp_cpu["x"], inp_cpu["w_router"], zr)
+    assert bool(((buf.logits.cpu().double() - zr.double()).abs() <= m).all())
+    assert np.array_equal(buf.topk_idx.cpu().numpy(), r["topk_idx"])
+    assert np.array_equal(buf.counts.cpu().numpy(), r["counts"])
+
+
 @pytest.mark.parametrize("name", list(CASES))
 def test_router_logits_exact_everywhere(name):
     """moe_router_logits gives the defined logit of every pair, bit for bit."""
