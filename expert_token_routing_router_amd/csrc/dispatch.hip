@@ -114,9 +114,21 @@ __global__ __launch_bounds__(1024) void dispatch_count(const int32_t* __restrict
   const int cells = num_tiles * E;
   for (int q = tid; q < cells; q += 1024) h[q] = 0;
   __syncthreads();
-  for (int s = tid; s < S; s += 1024) {
-    const int e = topk_idx[s];
-    if ((unsigned)e < (unsigned)E) atomicAdd(&h[(s / kTileSlots) * E + e], 1);  // ids out of range are ignored
+  // Eight loads in flight per thread before their atomics (a block-strided
+  // loop would wait for each load in turn).
+  for (int s0 = 0; s0 < S; s0 += 8 * 1024) {
+    int ids[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const int s = s0 + u * 1024 + tid;
+      ids[u] = s < S ? topk_idx[s] : -1;
+    }
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const int s = s0 + u * 1024 + tid;
+      if ((unsigned)ids[u] < (unsigned)E)  // ids out of range are ignored
+        atomicAdd(&h[(s / kTileSlots) * E + ids[u]], 1);
+    }
   }
   __syncthreads();
   int32_t run = 0;
