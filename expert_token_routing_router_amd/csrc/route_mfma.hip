@@ -76,6 +76,8 @@ __device__ __forceinline__ bool certainly_before(float lo_a, int a, float hi_b, 
   return lo_a > hi_b || (lo_a == hi_b && a < b);
 }
 
+// NJ = ceil(E / 64) expert slots per lane in steps 2 and 4.
+template <int NJ>
 __global__ __launch_bounds__(kFuseWaves * 64, 2) void route_fused(
     const bf16_t* __restrict__ x, const bf16_t* __restrict__ w, int N, int d, int E, int k,
     int G, int kg, int score_fn, const float* __restrict__ router_bias,
@@ -217,20 +219,20 @@ __global__ __launch_bounds__(kFuseWaves * 64, 2) void route_fused(
 
   // ---- 2. certify -------------------------------------------------------
   const int per = E / G;
-  double nw[4];
-  float sb[4];  // this lane's selection biases, read once per block
+  double nw[NJ];
+  float sb[NJ];  // this lane's selection biases, read once per block
 #pragma unroll
-  for (int j = 0; j < 4; ++j) {
+  for (int j = 0; j < NJ; ++j) {
     const int e = lane + 64 * j;
     nw[j] = e < E ? sqrt(sw[e]) : 0.0;
     sb[j] = (sel_bias && e < E) ? sel_bias[e] : 0.f;
   }
   for (int tl = wave; tl < nt; tl += kFuseWaves) {
     const double nx = sqrt(sx[tl]);
-    float lo[4], hi[4];
-    bool ok[4];
+    float lo[NJ], hi[NJ];
+    bool ok[NJ];
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
+    for (int j = 0; j < NJ; ++j) {
       const int e = lane + 64 * j;
       ok[j] = e < E;
       lo[j] = -INFINITY;
@@ -253,7 +255,7 @@ __global__ __launch_bounds__(kFuseWaves * 64, 2) void route_fused(
     if (G > 1) {
       float gl = -INFINITY, gh = -INFINITY;
 #pragma unroll
-      for (int j = 0; j < 4; ++j)
+      for (int j = 0; j < NJ; ++j)
         if (ok[j]) {
           wsc[wave][lane + 64 * j] = lo[j];
           wsc2[wave][lane + 64 * j] = hi[j];
@@ -287,23 +289,23 @@ __global__ __launch_bounds__(kFuseWaves * 64, 2) void route_fused(
       __builtin_amdgcn_wave_barrier();
     }
     // k-th largest lower end among experts of certainly kept groups.
-    bool comp[4], elig[4];
+    bool comp[NJ], elig[NJ];
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
+    for (int j = 0; j < NJ; ++j) {
       const int g = (lane + 64 * j) / per;
       comp[j] = ok[j] && ((kept_c >> g) & 1ull);
       elig[j] = ok[j] && (((kept_c | undecided) >> g) & 1ull);
     }
     float thr = -INFINITY;
     {
-      bool used[4] = {false, false, false, false};
+      bool used[NJ] = {};
       float tv = -INFINITY;
       int ti = -1;
       for (int r = 0; r < k; ++r) {
         float bs = 0.f;
         int bi = -1;
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
+        for (int j = 0; j < NJ; ++j) {
           const int e = lane + 64 * j;
           if (comp[j] && !used[j] && (bi < 0 || lo[j] > bs)) {
             bs = lo[j];
@@ -319,7 +321,7 @@ __global__ __launch_bounds__(kFuseWaves * 64, 2) void route_fused(
         ti = bi;
         if (lane == (bi & 63)) {
 #pragma unroll
-          for (int j = 0; j < 4; ++j)
+          for (int j = 0; j < NJ; ++j)
             if (bi == lane + 64 * j) used[j] = true;
         }
       }
@@ -327,10 +329,10 @@ __global__ __launch_bounds__(kFuseWaves * 64, 2) void route_fused(
     }
     // Candidates: eligible experts that are not certainly out, plus possible
     // maxima of undecided groups.
-    uint64_t cw[4];
+    uint64_t cw[NJ];
     int n = 0;
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
+    for (int j = 0; j < NJ; ++j) {
       const int e = lane + 64 * j;
       bool c = elig[j] && hi[j] >= thr;
       if (ok[j] && G > 1) {
@@ -340,10 +342,10 @@ __global__ __launch_bounds__(kFuseWaves * 64, 2) void route_fused(
       cw[j] = __ballot(c);
       n += __popcll(cw[j]);
     }
-    if (lane < 4) {
+    if (lane < NJ) {
       uint64_t v = cw[0];
 #pragma unroll
-      for (int j = 1; j < 4; ++j)
+      for (int j = 1; j < NJ; ++j)
         if (lane == j) v = cw[j];
       cand_s[tl][lane] = v;
     }
@@ -374,7 +376,7 @@ __global__ __launch_bounds__(kFuseWaves * 64, 2) void route_fused(
   for (int tl = wave; tl < nt; tl += kFuseWaves) {
     int base = cnt_s[tl];
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
+    for (int j = 0; j < NJ; ++j) {
       const uint64_t m = cand_s[tl][j];
       const uint64_t below = lane == 0 ? 0ull : (m << (64 - lane));
       if ((m >> lane) & 1ull) plist[base + __popcll(below)] = (uint16_t)((tl << 8) | (lane + 64 * j));
@@ -509,10 +511,10 @@ __global__ __launch_bounds__(kFuseWaves * 64, 2) void route_fused(
   // ---- 4. finalize ------------------------------------------------------
   for (int tl = wave; tl < nt; tl += kFuseWaves) {
     const int t = t0 + tl;
-    float z[4], s[4];
-    bool is_c[4];
+    float z[NJ], s[NJ];
+    bool is_c[NJ];
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
+    for (int j = 0; j < NJ; ++j) {
       const int e = lane + 64 * j;
       const bool okj = e < E;
       z[j] = okj ? zs[tl][e] : 0.f;
@@ -528,7 +530,7 @@ __global__ __launch_bounds__(kFuseWaves * 64, 2) void route_fused(
         // Exact maxima of undecided groups (all their possible maxima are
         // candidates, so the maximum over candidates is the group score).
 #pragma unroll
-        for (int j = 0; j < 4; ++j)
+        for (int j = 0; j < NJ; ++j)
           if (lane + 64 * j < E) wsc[wave][lane + 64 * j] = s[j];
         __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
         __builtin_amdgcn_wave_barrier();
@@ -551,9 +553,9 @@ __global__ __launch_bounds__(kFuseWaves * 64, 2) void route_fused(
         __builtin_amdgcn_wave_barrier();
       }
     }
-    bool elig[4];
+    bool elig[NJ];
 #pragma unroll
-    for (int j = 0; j < 4; ++j) elig[j] = is_c[j] && ((kept >> ((lane + 64 * j) / per)) & 1ull);
+    for (int j = 0; j < NJ; ++j) elig[j] = is_c[j] && ((kept >> ((lane + 64 * j) / per)) & 1ull);
 
     int sel[8];
     float zsel[8];
@@ -565,7 +567,7 @@ __global__ __launch_bounds__(kFuseWaves * 64, 2) void route_fused(
         float bs = 0.f;
         int bi = -1;
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
+        for (int j = 0; j < NJ; ++j) {
           const int e = lane + 64 * j;
           if (elig[j] && (bi < 0 || s[j] > bs)) {
             bs = s[j];
@@ -577,12 +579,12 @@ __global__ __launch_bounds__(kFuseWaves * 64, 2) void route_fused(
         const int owner = bi & 63, jj = bi >> 6;
         float zv = z[0];
 #pragma unroll
-        for (int j = 1; j < 4; ++j)
+        for (int j = 1; j < NJ; ++j)
           if (jj == j) zv = z[j];
         zsel[r] = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(zv), owner));
         if (lane == owner) {
 #pragma unroll
-          for (int j = 0; j < 4; ++j)
+          for (int j = 0; j < NJ; ++j)
             if (jj == j) elig[j] = false;
         }
       }
@@ -602,12 +604,12 @@ __global__ __launch_bounds__(kFuseWaves * 64, 2) void route_fused(
     } else if (score_fn == 1) {
       float m = -INFINITY;
 #pragma unroll
-      for (int j = 0; j < 4; ++j)
+      for (int j = 0; j < NJ; ++j)
         if (lane + 64 * j < E) m = fmaxf(m, z[j]);
       const double zmax = (double)wave_max(m);
       double part = 0.0;
 #pragma unroll
-      for (int j = 0; j < 4; ++j)
+      for (int j = 0; j < NJ; ++j)
         if (lane + 64 * j < E) part += exp((double)z[j] - zmax);
       wsum = wave_sum(part);
 #pragma unroll
@@ -651,10 +653,18 @@ size_t route_certified_workspace_bytes(int N, int E) {
 hipError_t launch_route_certified(const RouteArgs& a, hipStream_t st) {
   launch_zero_i32(a.counts, a.E, st);
   const int blocks = (a.N + kFuseTok - 1) / kFuseTok;
-  route_fused<<<blocks, kFuseWaves * 64, 0, st>>>(static_cast<const bf16_t*>(a.x),
-                                      static_cast<const bf16_t*>(a.w_router), a.N, a.d, a.E, a.k,
-                                      a.G, a.kg, a.score_fn, a.router_bias, a.sel_bias, a.logits,
-                                      a.topk_idx, a.topk_w, a.counts);
+  auto launch = [&](auto kernel) {
+    kernel<<<blocks, kFuseWaves * 64, 0, st>>>(
+        static_cast<const bf16_t*>(a.x), static_cast<const bf16_t*>(a.w_router), a.N, a.d, a.E,
+        a.k, a.G, a.kg, a.score_fn, a.router_bias, a.sel_bias, a.logits, a.topk_idx, a.topk_w,
+        a.counts);
+  };
+  switch ((a.E + 63) / 64) {
+    case 1: launch(route_fused<1>); break;
+    case 2: launch(route_fused<2>); break;
+    case 3: launch(route_fused<3>); break;
+    default: launch(route_fused<4>); break;
+  }
   return hipGetLastError();
 }
 
