@@ -56,9 +56,8 @@ typedef float floatx4 __attribute__((ext_vector_type(4)));
 // (selection-only bias; node-limited routing as the group limit).
 constexpr int kFuseTok = 32;                     // tokens per block
 constexpr int kFuseWaves = 8;
-constexpr int kFuseRing = 6;                     // LDS chunk slots in step 1
+constexpr int kFuseRing = 6;  // LDS chunk slots in step 1 (11 measured slower)
 constexpr int kFuseSlot = (kFuseTok + 64) * 64;  // bytes: 32 x rows + 64 w rows of 64 B
-constexpr int kFuseMaxE = 256;
 
 __device__ __forceinline__ float sigmoid_affinity_v2(float z) {
   return __double2float_rn(1.0 / (1.0 + exp(-(double)z)));
@@ -76,147 +75,29 @@ __device__ __forceinline__ bool certainly_before(float lo_a, int a, float hi_b, 
   return lo_a > hi_b || (lo_a == hi_b && a < b);
 }
 
-// NJ = ceil(E / 64) expert slots per lane in steps 2 and 4.
-template <int NJ>
-__global__ __launch_bounds__(kFuseWaves * 64, 2) void route_fused(
-    const bf16_t* __restrict__ x, const bf16_t* __restrict__ w, int N, int d, int E, int k,
-    int G, int kg, int score_fn, const float* __restrict__ router_bias,
+// Steps 2-4 of one tile of nt <= kFuseTok tokens starting at t0, given the
+// approximate logits in zs and the squared norms sx (tokens) and sw (experts):
+// certify, exact values for the candidate pairs, selection and weights, the
+// tile's logits, and per-expert counts added to hist.  scratch (LDS) holds
+// the pair lists and the group-limit scratch: at least
+// max(4 * kFuseTok * ZW, 8 * kFuseWaves * ZW + 512 * kFuseWaves) bytes.
+template <int NJ, int ZW>
+__device__ __forceinline__ void route_tile_tail(
+    const bf16_t* __restrict__ x, const bf16_t* __restrict__ w, int d, int E, int k, int G,
+    int kg, int score_fn, const float* __restrict__ router_bias,
     const float* __restrict__ sel_bias, float* __restrict__ logits,
-    int32_t* __restrict__ topk_idx, float* __restrict__ topk_w, int32_t* __restrict__ counts) {
-  __shared__ float zs[kFuseTok][kFuseMaxE];  // z~, then exact values for candidates
-  __shared__ __attribute__((aligned(1024))) char ring[kFuseRing][kFuseSlot];  // step 1; then pairs
-  __shared__ double sx[kFuseTok], sw[kFuseMaxE];
-  __shared__ uint64_t cand_s[kFuseTok][4], gm_s[kFuseTok][2];
-  __shared__ int32_t cnt_s[kFuseTok];
-  __shared__ int32_t hist[kFuseMaxE];
-  __shared__ int32_t npairs_s, nfb_s;
-  // After step 1 the ring holds, at different times, the per-wave scratch of
-  // the group limit (steps 2 and 4) and the pair list (end of 2, step 3).
-  uint16_t* plist = reinterpret_cast<uint16_t*>(&ring[0][0]);  // (t_local << 8) | e
-  typedef float ExpRow[kFuseMaxE];
-  typedef float GroupRows[2][64];
-  ExpRow* wsc = reinterpret_cast<ExpRow*>(&ring[0][0]);                       // [8][E]: lower ends / scores
-  ExpRow* wsc2 = reinterpret_cast<ExpRow*>(&ring[0][0] + kFuseWaves * 1024);  // [8][E]: upper ends
-  GroupRows* gsc = reinterpret_cast<GroupRows*>(&ring[0][0] + 2 * kFuseWaves * 1024);
-  static_assert(2 * kFuseTok * kFuseMaxE * 2 <= kFuseRing * kFuseSlot,
-                "pair list and fallback list fit the ring");
-  static_assert(2 * kFuseWaves * 1024 + kFuseWaves * 512 <= kFuseRing * kFuseSlot,
-                "group-limit scratch fits the ring");
-  static_assert(kFuseTok <= 64 && kFuseMaxE <= 256, "pair encoding and one-wave token scan");
-
+    int32_t* __restrict__ topk_idx, float* __restrict__ topk_w, int t0, int nt,
+    float (*zs)[ZW], char* scratch, const double* sx, const double* sw,
+    uint64_t (*cand_s)[4], uint64_t (*gm_s)[2], int32_t* cnt_s, int32_t* hist,
+    int32_t& npairs_s, int32_t& nfb_s) {
+  static_assert(ZW >= 64 * NJ, "a zs row holds every expert");
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int t0 = blockIdx.x * kFuseTok;
-  const int nt = min(kFuseTok, N - t0);
-  const int nch = d / 32;
-  for (int e = tid; e < E; e += kFuseWaves * 64) hist[e] = 0;
-
-  // ---- 1. scores --------------------------------------------------------
-  // Six 1-KB loads per chunk: 0-1 x rows 16j.., 2-5 w rows 16(j-2).. of the
-  // expert tile; wave w < 6 issues load w.  Lane L fetches row L/4 of its
-  // load, logical 16-byte chunk (L % 4) ^ swz4(L / 4).
-  const bool loader = wave < 6;
-  double sxp = 0.0;  // this thread's part of sum x^2 (row tid/16, 2 elements per chunk)
-  for (int et = 0; et < E; et += 64) {
-    const u32x4* src;
-    {
-      const int j = min(wave, 5);
-      const int r = lane / 4, c = (lane % 4) ^ swz4(r);
-      if (j < 2) {
-        const int t = min(t0 + 16 * j + r, N - 1);
-        src = reinterpret_cast<const u32x4*>(x + (size_t)t * d) + c;
-      } else {
-        const int e = min(et + 16 * (j - 2) + r, E - 1);
-        src = reinterpret_cast<const u32x4*>(w + (size_t)e * d) + c;
-      }
-    }
-#define MOE_FUSE_ISSUE(ch_)                                                                 \
-  do {                                                                                      \
-    if (loader)                                                                             \
-      __builtin_amdgcn_global_load_lds((void*)(src + (size_t)(ch_) * 4),                    \
-                                       (lds_ptr_t)(ring[(ch_) % kFuseRing] + wave * 1024),  \
-                                       16, 0, 0);                                           \
-  } while (0)
-    // Chunks are consumed in pairs: one wait and one barrier per pair, and the
-    // two chunks' LDS reads and arithmetic overlap.  The prologue issues
-    // kFuseRing - 2 chunks; each pair step refills the two slots the previous
-    // pair used.
-    static_assert(kFuseRing >= 4, "two slots refilled per pair step");
-    for (int c = 0; c < kFuseRing - 2 && c < nch; ++c) MOE_FUSE_ISSUE(c);
-    double swp = 0.0;  // sum w^2 part: expert row tid/8 of the tile, 4 elements per chunk
-    floatx4 acc32 = floatx4{0.f, 0.f, 0.f, 0.f};
-    double acc[4] = {0.0, 0.0, 0.0, 0.0};
-#define MOE_FUSE_CHUNK(ch_)                                                                 \
-  do {                                                                                      \
-    const char* slot = ring[(ch_) % kFuseRing];                                             \
-    /* Squares: x once (first expert tile), w for every tile. */                           \
-    if (et == 0) { /* x: row tid/16, elements 2(tid%16), +1 of the chunk */                \
-      const int r = tid / 16, pq = tid % 16, c = pq / 4;                                    \
-      const uint32_t v = *reinterpret_cast<const uint32_t*>(                                \
-          slot + (r / 16) * 1024 + ((r % 16) * 4 + (c ^ swz4(r % 16))) * 16 + (pq % 4) * 4);  \
-      const double a0 = bf16_to_f32(v & 0xffffu), a1 = bf16_to_f32(v >> 16);                \
-      sxp = fma(a0, a0, fma(a1, a1, sxp));                                                  \
-    }                                                                                       \
-    { /* w: expert row tid/8, elements 4(tid%8)..+3 of the chunk */                        \
-      const int r = tid / 8, pq = tid % 8, c = pq / 2;                                      \
-      const uint2 v = *reinterpret_cast<const uint2*>(                                      \
-          slot + 2048 + (r / 16) * 1024 + ((r % 16) * 4 + (c ^ swz4(r % 16))) * 16 + (pq % 2) * 8); \
-      const double b0 = bf16_to_f32(v.x & 0xffffu), b1 = bf16_to_f32(v.x >> 16);            \
-      const double b2 = bf16_to_f32(v.y & 0xffffu), b3 = bf16_to_f32(v.y >> 16);            \
-      swp = fma(b0, b0, fma(b1, b1, fma(b2, b2, fma(b3, b3, swp))));                        \
-    }                                                                                       \
-    /* MFMA: wave w takes token block w/4 (A = tokens 16(w/4) + (lane & 15)) */            \
-    /* and expert block w%4 of the tile (B). */                                             \
-    {                                                                                       \
-      const int er = 16 * (wave % 4) + (lane & 15), cc = lane >> 4;                         \
-      const bf16x8_t bw = *reinterpret_cast<const bf16x8_t*>(                               \
-          slot + 2048 + (er / 16) * 1024 + ((er % 16) * 4 + (cc ^ swz4(er % 16))) * 16);    \
-      const int tr = lane & 15;                                                             \
-      const bf16x8_t ax = *reinterpret_cast<const bf16x8_t*>(                               \
-          slot + (wave / 4) * 1024 + (tr * 4 + (cc ^ swz4(tr))) * 16);                      \
-      acc32 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ax, bw, acc32, 0, 0, 0);              \
-    }                                                                                       \
-  } while (0)
-    for (int ch = 0; ch < nch; ch += 2) {
-      const bool two = ch + 1 < nch;
-      // The pair's last chunk has landed once at most `later` younger chunks
-      // (one load each per loading wave) are in flight.
-      switch (two ? min(kFuseRing - 4, nch - 2 - ch) : 0) {
-        case 0: wait_vmcnt<0>(); break;
-        case 1: wait_vmcnt<1>(); break;
-        default: wait_vmcnt<2>(); break;
-      }
-      // The pair is visible to all waves; all waves are done with the previous
-      // pair, whose two slots are refilled now.
-      ring_barrier();
-      if (ch + kFuseRing - 2 < nch) MOE_FUSE_ISSUE(ch + kFuseRing - 2);
-      if (ch + kFuseRing - 1 < nch) MOE_FUSE_ISSUE(ch + kFuseRing - 1);
-      MOE_FUSE_CHUNK(ch);
-      if (two) MOE_FUSE_CHUNK(ch + 1);
-      // fp32 chunks of at most 64 products, summed in fp64.
-#pragma unroll
-      for (int v = 0; v < 4; ++v) acc[v] += (double)acc32[v];
-      acc32 = floatx4{0.f, 0.f, 0.f, 0.f};
-    }
-#undef MOE_FUSE_CHUNK
-#undef MOE_FUSE_ISSUE
-    // z~: lane holds expert (lane & 15) of block w%4, tokens 16(w/4) + 4*(lane>>4)+v.
-    const int e = et + 16 * (wave % 4) + (lane & 15);
-    if (e < E) {
-      const double bias = router_bias ? (double)router_bias[e] : 0.0;
-#pragma unroll
-      for (int v = 0; v < 4; ++v) zs[16 * (wave / 4) + 4 * (lane >> 4) + v][e] = (float)(acc[v] + bias);
-    }
-    // sum w^2: the 8 threads of an expert row are consecutive lanes.
-#pragma unroll
-    for (int o = 1; o < 8; o <<= 1) swp += __shfl_xor(swp, o, 64);
-    if (tid % 8 == 0 && et + tid / 8 < E) sw[et + tid / 8] = swp;
-    __syncthreads();  // ring slots are reused by the next expert tile
-  }
-#pragma unroll
-  for (int o = 1; o < 16; o <<= 1) sxp += __shfl_xor(sxp, o, 64);
-  if (tid % 16 == 0) sx[tid / 16] = sxp;
-  __syncthreads();
-
+  uint16_t* plist = reinterpret_cast<uint16_t*>(scratch);  // (t_local << 8) | e
+  typedef float ExpRow[ZW];
+  typedef float GroupRows[2][64];
+  ExpRow* wsc = reinterpret_cast<ExpRow*>(scratch);                            // [8][E]: lower ends / scores
+  ExpRow* wsc2 = reinterpret_cast<ExpRow*>(scratch + kFuseWaves * ZW * 4);     // [8][E]: upper ends
+  GroupRows* gsc = reinterpret_cast<GroupRows*>(scratch + 2 * kFuseWaves * ZW * 4);
   // ---- 2. certify -------------------------------------------------------
   const int per = E / G;
   double nw[NJ];
@@ -400,7 +281,7 @@ __global__ __launch_bounds__(kFuseWaves * 64, 2) void route_fused(
   // sum and the minimum exponent; pairs that pass the test are done, the
   // others go to a list and run the chain one lane each below.
   const int np = npairs_s;
-  uint16_t* fb = plist + kFuseTok * kFuseMaxE;  // pairs that need the chain
+  uint16_t* fb = plist + kFuseTok * ZW;  // pairs that need the chain
   {
     const int q = tid >> 4, s16 = tid & 15;
     const int nv = d / 8;  // 16-byte vectors per row
@@ -637,6 +518,162 @@ __global__ __launch_bounds__(kFuseWaves * 64, 2) void route_fused(
   }
   // The tile's logits (exact for candidates, z~ elsewhere) and counts.
   for (int i = tid; i < nt * E; i += kFuseWaves * 64) logits[(size_t)t0 * E + i] = zs[i / E][i % E];
+}
+
+// NJ = ceil(E / 64) expert slots per lane in steps 2 and 4.
+template <int NJ>
+__global__ __launch_bounds__(kFuseWaves * 64, 2) void route_fused(
+    const bf16_t* __restrict__ x, const bf16_t* __restrict__ w, int N, int d, int E, int k,
+    int G, int kg, int score_fn, const float* __restrict__ router_bias,
+    const float* __restrict__ sel_bias, float* __restrict__ logits,
+    int32_t* __restrict__ topk_idx, float* __restrict__ topk_w, int32_t* __restrict__ counts) {
+  constexpr int ZW = 64 * NJ;
+  __shared__ float zs[kFuseTok][ZW];  // z~, then exact values for candidates
+  __shared__ __attribute__((aligned(1024))) char ring[kFuseRing][kFuseSlot];  // step 1; then pairs
+  __shared__ double sx[kFuseTok], sw[ZW];
+  __shared__ uint64_t cand_s[kFuseTok][4], gm_s[kFuseTok][2];
+  __shared__ int32_t cnt_s[kFuseTok];
+  __shared__ int32_t hist[ZW];
+  __shared__ int32_t npairs_s, nfb_s;
+  // After step 1 the ring holds, at different times, the per-wave scratch of
+  // the group limit (steps 2 and 4) and the pair lists (end of 2, step 3).
+  static_assert(2 * kFuseTok * ZW * 2 <= kFuseRing * kFuseSlot,
+                "pair list and fallback list fit the ring");
+  static_assert(2 * kFuseWaves * ZW * 4 + kFuseWaves * 512 <= kFuseRing * kFuseSlot,
+                "group-limit scratch fits the ring");
+  static_assert(kFuseTok <= 64 && ZW <= 256, "pair encoding and one-wave token scan");
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int t0 = blockIdx.x * kFuseTok;
+  const int nt = min(kFuseTok, N - t0);
+  const int nch = d / 32;
+  for (int e = tid; e < E; e += kFuseWaves * 64) hist[e] = 0;
+
+  // ---- 1. scores --------------------------------------------------------
+  // Six 1-KB loads per chunk: 0-1 x rows 16j.., 2-5 w rows 16(j-2).. of the
+  // expert tile; wave w < 6 issues load w.  Lane L fetches row L/4 of its
+  // load, logical 16-byte chunk (L % 4) ^ swz4(L / 4).
+  const bool loader = wave < 6;
+  double sxp = 0.0;  // this thread's part of sum x^2 (row tid/16, 2 elements per chunk)
+  for (int et = 0; et < E; et += 64) {
+    const u32x4* src;
+    {
+      const int j = min(wave, 5);
+      const int r = lane / 4, c = (lane % 4) ^ swz4(r);
+      if (j < 2) {
+        const int t = min(t0 + 16 * j + r, N - 1);
+        src = reinterpret_cast<const u32x4*>(x + (size_t)t * d) + c;
+      } else {
+        const int e = min(et + 16 * (j - 2) + r, E - 1);
+        src = reinterpret_cast<const u32x4*>(w + (size_t)e * d) + c;
+      }
+    }
+#define MOE_FUSE_ISSUE(ch_)                                                                 \
+  do {                                                                                      \
+    if (loader)                                                                             \
+      __builtin_amdgcn_global_load_lds((void*)(src + (size_t)(ch_) * 4),                    \
+                                       (lds_ptr_t)(ring[(ch_) % kFuseRing] + wave * 1024),  \
+                                       16, 0, 0);                                           \
+  } while (0)
+    // Chunks are consumed in pairs: one wait and one barrier per pair, and the
+    // two chunks' LDS reads and arithmetic overlap.  The prologue issues
+    // kFuseRing - 2 chunks; each pair step refills the two slots the previous
+    // pair used.
+    static_assert(kFuseRing >= 4, "two slots refilled per pair step");
+    for (int c = 0; c < kFuseRing - 2 && c < nch; ++c) MOE_FUSE_ISSUE(c);
+    double swp = 0.0;  // sum w^2 part: expert row tid/8 of the tile, 4 elements per chunk
+    floatx4 acc32 = floatx4{0.f, 0.f, 0.f, 0.f};
+    double acc[4] = {0.0, 0.0, 0.0, 0.0};
+#define MOE_FUSE_CHUNK(ch_)                                                                 \
+  do {                                                                                      \
+    const char* slot = ring[(ch_) % kFuseRing];                                             \
+    /* Squares: x once (first expert tile), w for every tile. */                           \
+    if (et == 0) { /* x: row tid/16, elements 2(tid%16), +1 of the chunk */                \
+      const int r = tid / 16, pq = tid % 16, c = pq / 4;                                    \
+      const uint32_t v = *reinterpret_cast<const uint32_t*>(                                \
+          slot + (r / 16) * 1024 + ((r % 16) * 4 + (c ^ swz4(r % 16))) * 16 + (pq % 4) * 4);  \
+      const double a0 = bf16_to_f32(v & 0xffffu), a1 = bf16_to_f32(v >> 16);                \
+      sxp = fma(a0, a0, fma(a1, a1, sxp));                                                  \
+    }                                                                                       \
+    { /* w: expert row tid/8, elements 4(tid%8)..+3 of the chunk */                        \
+      const int r = tid / 8, pq = tid % 8, c = pq / 2;                                      \
+      const uint2 v = *reinterpret_cast<const uint2*>(                                      \
+          slot + 2048 + (r / 16) * 1024 + ((r % 16) * 4 + (c ^ swz4(r % 16))) * 16 + (pq % 2) * 8); \
+      const double b0 = bf16_to_f32(v.x & 0xffffu), b1 = bf16_to_f32(v.x >> 16);            \
+      const double b2 = bf16_to_f32(v.y & 0xffffu), b3 = bf16_to_f32(v.y >> 16);            \
+      swp = fma(b0, b0, fma(b1, b1, fma(b2, b2, fma(b3, b3, swp))));                        \
+    }                                                                                       \
+    /* MFMA: wave w takes token block w/4 (A = tokens 16(w/4) + (lane & 15)) */            \
+    /* and expert block w%4 of the tile (B). */                                             \
+    {                                                                                       \
+      const int er = 16 * (wave % 4) + (lane & 15), cc = lane >> 4;                         \
+      const bf16x8_t bw = *reinterpret_cast<const bf16x8_t*>(                               \
+          slot + 2048 + (er / 16) * 1024 + ((er % 16) * 4 + (cc ^ swz4(er % 16))) * 16);    \
+      const int tr = lane & 15;                                                             \
+      const bf16x8_t ax = *reinterpret_cast<const bf16x8_t*>(                               \
+          slot + (wave / 4) * 1024 + (tr * 4 + (cc ^ swz4(tr))) * 16);                      \
+      acc32 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ax, bw, acc32, 0, 0, 0);              \
+    }                                                                                       \
+  } while (0)
+    // Steady state: both refills of the step are in range, so the wait count
+    // is a constant and the loop body has no branches.
+    int ch = 0;
+    for (; ch + kFuseRing - 1 < nch; ch += 2) {
+      // The pair's last chunk has landed once at most kFuseRing - 4 younger
+      // chunks (one load each per loading wave) are in flight.
+      wait_vmcnt<kFuseRing - 4>();
+      // The pair is visible to all waves; all waves are done with the previous
+      // pair, whose two slots are refilled now.
+      ring_barrier();
+      MOE_FUSE_ISSUE(ch + kFuseRing - 2);
+      MOE_FUSE_ISSUE(ch + kFuseRing - 1);
+      MOE_FUSE_CHUNK(ch);
+      MOE_FUSE_CHUNK(ch + 1);
+      // fp32 chunks of at most 64 products, summed in fp64.
+#pragma unroll
+      for (int v = 0; v < 4; ++v) acc[v] += (double)acc32[v];
+      acc32 = floatx4{0.f, 0.f, 0.f, 0.f};
+    }
+    // The last pairs: fewer younger chunks in flight, at most one refill.
+    for (; ch < nch; ch += 2) {
+      const bool two = ch + 1 < nch;
+      switch (two ? min(kFuseRing - 4, nch - 2 - ch) : 0) {
+        case 0: wait_vmcnt<0>(); break;
+        case 1: wait_vmcnt<1>(); break;
+        default: wait_vmcnt<2>(); break;
+      }
+      static_assert(kFuseRing - 4 <= 2, "wait counts above cover the ring");
+      ring_barrier();
+      if (ch + kFuseRing - 2 < nch) MOE_FUSE_ISSUE(ch + kFuseRing - 2);
+      MOE_FUSE_CHUNK(ch);
+      if (two) MOE_FUSE_CHUNK(ch + 1);
+#pragma unroll
+      for (int v = 0; v < 4; ++v) acc[v] += (double)acc32[v];
+      acc32 = floatx4{0.f, 0.f, 0.f, 0.f};
+    }
+#undef MOE_FUSE_CHUNK
+#undef MOE_FUSE_ISSUE
+    // z~: lane holds expert (lane & 15) of block w%4, tokens 16(w/4) + 4*(lane>>4)+v.
+    const int e = et + 16 * (wave % 4) + (lane & 15);
+    if (e < E) {
+      const double bias = router_bias ? (double)router_bias[e] : 0.0;
+#pragma unroll
+      for (int v = 0; v < 4; ++v) zs[16 * (wave / 4) + 4 * (lane >> 4) + v][e] = (float)(acc[v] + bias);
+    }
+    // sum w^2: the 8 threads of an expert row are consecutive lanes.
+#pragma unroll
+    for (int o = 1; o < 8; o <<= 1) swp += __shfl_xor(swp, o, 64);
+    if (tid % 8 == 0 && et + tid / 8 < E) sw[et + tid / 8] = swp;
+    __syncthreads();  // ring slots are reused by the next expert tile
+  }
+#pragma unroll
+  for (int o = 1; o < 16; o <<= 1) sxp += __shfl_xor(sxp, o, 64);
+  if (tid % 16 == 0) sx[tid / 16] = sxp;
+  __syncthreads();
+
+  route_tile_tail<NJ, ZW>(x, w, d, E, k, G, kg, score_fn, router_bias, sel_bias, logits,
+                                 topk_idx, topk_w, t0, nt, zs, &ring[0][0], sx, sw, cand_s, gm_s,
+                                 cnt_s, hist, npairs_s, nfb_s);
   __syncthreads();
   for (int e = tid; e < E; e += kFuseWaves * 64)
     if (hist[e]) atomicAdd(&counts[e], hist[e]);
