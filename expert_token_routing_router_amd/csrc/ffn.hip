@@ -358,7 +358,20 @@ void grouped_gemm_bf16(
     _Pragma("unroll") for (int s = 0; s < NS - 1; ++s) if (s < ktiles) MOE_RING_ISSUE(s, s); \
     MOE_WAIT_STAGE(min(NS - 2, ktiles - 1));                                               \
     MOE_LOAD_KK(FA_, 0, 0, 0);                                                             \
-    for (int kt = 0; kt < ktiles; ++kt) {                                                  \
+    /* Steady state: the refill is always in range and the wait count is  */            \
+    /* fixed, so the loop body has no branches besides the wave role.     */            \
+    int kt = 0;                                                                            \
+    for (; kt + NS - 1 < ktiles; ++kt) {                                                   \
+      MOE_LOAD_KK(FA_, kt % NS, 1, 1);                                                     \
+      MOE_MFMA_KK(FA_, 0);                                                                 \
+      if (a_wave) wait_vmcnt<(NS - 3) * LA>(); else wait_vmcnt<(NS - 3) * LB>();           \
+      ring_barrier();                                                                      \
+      MOE_RING_ISSUE(kt + NS - 1, (kt + NS - 1) % NS);                                     \
+      MOE_LOAD_KK(FA_, (kt + 1) % NS, 0, 0);                                               \
+      MOE_MFMA_KK(FA_, 1);                                                                 \
+    }                                                                                      \
+    /* The last NS - 1 stages: nothing left to issue.                     */            \
+    for (; kt < ktiles; ++kt) {                                                            \
       const int slot = kt % NS;                                                            \
       MOE_LOAD_KK(FA_, slot, 1, 1);                                                        \
       MOE_MFMA_KK(FA_, 0);                                                                 \
