@@ -54,7 +54,8 @@ __global__ __launch_bounds__(256) void logits_f64(const void* __restrict__ x, in
                                                   int32_t* __restrict__ counts_to_zero) {
   constexpr int EG = 4 / TT;
   constexpr int BK = 64;
-  __shared__ float xs[BK][TT * 64];  // [hidden index][token], fp32 (exact)
+  __shared__ float xs[BK][TT * 64 + 1];  // [hidden index][token], fp32 (exact); +1: no bank conflicts on the transposed store
+  __shared__ double wsm[BK][EG * EC];    // the block's weight columns of this K block
 
   if (counts_to_zero && blockIdx.x == 0 && blockIdx.y == 0) {
     for (int e = threadIdx.x; e < E; e += blockDim.x) counts_to_zero[e] = 0;
@@ -73,25 +74,60 @@ __global__ __launch_bounds__(256) void logits_f64(const void* __restrict__ x, in
 #pragma unroll
   for (int c = 0; c < EC; ++c) acc[c] = 0.0;
 
+  // K blocks of BK hidden indices; the next block's x and w values are
+  // loaded into registers while the current one is multiplied.
+  constexpr int XPT = TT * 64 * BK / 256;  // x values per thread per K block
+  constexpr int WPT = (BK * EG * EC + 255) / 256;
+  const int eb = blockIdx.y * EG * EC;
+  float xr[XPT];
+  double wr[WPT];
+  auto fetch = [&](int k0) {
+    const int kw = min(BK, d - k0);
+#pragma unroll
+    for (int u = 0; u < XPT; ++u) {
+      const int q = threadIdx.x + 256 * u;
+      const int r = q / BK, kk = q % BK, tr = t0 + r;
+      xr[u] = (tr < N && kk < kw) ? load_elem(x, dtype, (size_t)tr * d + k0 + kk) : 0.f;
+    }
+#pragma unroll
+    for (int u = 0; u < WPT; ++u) {
+      const int q = threadIdx.x + 256 * u;
+      const int kk = q / (EG * EC), j = q % (EG * EC);
+      wr[u] = (q < BK * EG * EC && kk < kw && eb + j < Ep) ? wt[(size_t)(k0 + kk) * Ep + eb + j] : 0.0;
+    }
+  };
+  fetch(0);
   for (int k0 = 0; k0 < d; k0 += BK) {
     const int kw = min(BK, d - k0);
-    __syncthreads();
-    // Cooperative load of x[t0 : t0+64*TT, k0 : k0+kw] into xs (transposed).
-    for (int q = threadIdx.x; q < TT * 64 * BK; q += 256) {
-      const int r = q / BK, kk = q % BK;
-      const int tr = t0 + r;
-      float v = 0.f;
-      if (tr < N && kk < kw) v = load_elem(x, dtype, (size_t)tr * d + k0 + kk);
-      xs[kk][r] = v;
+    __syncthreads();  // every wave is done with the previous block
+#pragma unroll
+    for (int u = 0; u < XPT; ++u) {
+      const int q = threadIdx.x + 256 * u;
+      xs[q % BK][q / BK] = xr[u];  // transposed: [hidden index][token]
+    }
+#pragma unroll
+    for (int u = 0; u < WPT; ++u) {
+      const int q = threadIdx.x + 256 * u;
+      if (q < BK * EG * EC) wsm[q / (EG * EC)][q % (EG * EC)] = wr[u];
     }
     __syncthreads();
+    if (k0 + BK < d) fetch(k0 + BK);
     if (active_chunk) {
-      const double* wrow = wt + (size_t)k0 * Ep + e0;
-      for (int kk = 0; kk < kw; ++kk) {
-        const double xv = (double)xs[kk][tt * 64 + lane];
+      // Unrolled so that the LDS reads run ahead of the fp64 chains; the
+      // chains themselves keep their order (k ascending).
+      if (kw == BK) {
+#pragma unroll 16
+        for (int kk = 0; kk < BK; ++kk) {
+          const double xv = (double)xs[kk][tt * 64 + lane];
 #pragma unroll
-        for (int c = 0; c < EC; ++c) acc[c] = __fma_rn(xv, wrow[c], acc[c]);
-        wrow += Ep;
+          for (int c = 0; c < EC; ++c) acc[c] = __fma_rn(xv, wsm[kk][eg * EC + c], acc[c]);
+        }
+      } else {
+        for (int kk = 0; kk < kw; ++kk) {
+          const double xv = (double)xs[kk][tt * 64 + lane];
+#pragma unroll
+          for (int c = 0; c < EC; ++c) acc[c] = __fma_rn(xv, wsm[kk][eg * EC + c], acc[c]);
+        }
       }
     }
   }
@@ -117,6 +153,7 @@ __device__ __forceinline__ float sigmoid_affinity(float z) {
 constexpr int kSelectTokensPerBlock = 64;
 constexpr int kSelectWaves = 16;  // 4 tokens per wave
 
+template <int NJ>  // ceil(E / 64) experts per lane
 __global__ __launch_bounds__(kSelectWaves * 64) void select_topk(const float* __restrict__ logits,
                                                    const float* __restrict__ sel_bias, int N,
                                                    int E, int k, int G, int kg, int score_fn,
@@ -133,14 +170,30 @@ __global__ __launch_bounds__(kSelectWaves * 64) void select_topk(const float* __
   const int t_begin = blockIdx.x * kSelectTokensPerBlock;
   const int t_end = min(N, t_begin + kSelectTokensPerBlock);
 
-  for (int t = t_begin + wave; t < t_end; t += kSelectWaves) {
-    float z[4], s[4];
-    bool ok[4];
+  // The wave's tokens' logits are loaded up front, so their latency is paid
+  // once per wave rather than once per token.
+  constexpr int kTPW = kSelectTokensPerBlock / kSelectWaves;
+  float zpre[kTPW][NJ];
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
+  for (int i = 0; i < kTPW; ++i) {
+    const int t = t_begin + wave + i * kSelectWaves;
+#pragma unroll
+    for (int j = 0; j < NJ; ++j) {
+      const int e = lane + 64 * j;
+      zpre[i][j] = (t < t_end && e < E) ? logits[(size_t)t * E + e] : 0.f;
+    }
+  }
+#pragma unroll
+  for (int i = 0; i < kTPW; ++i) {
+    const int t = t_begin + wave + i * kSelectWaves;
+    if (t >= t_end) break;
+    float z[NJ], s[NJ];
+    bool ok[NJ];
+#pragma unroll
+    for (int j = 0; j < NJ; ++j) {
       const int e = lane + 64 * j;
       ok[j] = e < E;
-      z[j] = ok[j] ? logits[(size_t)t * E + e] : 0.f;
+      z[j] = zpre[i][j];
       const float a = score_fn == 2 ? sigmoid_affinity(z[j]) : z[j];
       s[j] = (ok[j] && sel_bias) ? a + sel_bias[e] : a;
     }
@@ -148,7 +201,7 @@ __global__ __launch_bounds__(kSelectWaves * 64) void select_topk(const float* __
     // Group limit: only experts of the kg best groups stay eligible.
     if (G > 1) {
 #pragma unroll
-      for (int j = 0; j < 4; ++j)
+      for (int j = 0; j < NJ; ++j)
         if (ok[j]) sbuf[wave][lane + 64 * j] = s[j];
       __builtin_amdgcn_wave_barrier();
       __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
@@ -168,7 +221,7 @@ __global__ __launch_bounds__(kSelectWaves * 64) void select_topk(const float* __
         if (lane == bi) gi = -1;  // taken
       }
 #pragma unroll
-      for (int j = 0; j < 4; ++j)
+      for (int j = 0; j < NJ; ++j)
         if (ok[j]) ok[j] = (keep >> ((lane + 64 * j) / per)) & 1ull;
       __builtin_amdgcn_wave_barrier();
     }
@@ -185,7 +238,7 @@ __global__ __launch_bounds__(kSelectWaves * 64) void select_topk(const float* __
         float bs = 0.f;
         int bi = -1;
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
+        for (int j = 0; j < NJ; ++j) {
           const int e = lane + 64 * j;
           if (ok[j] && (bi < 0 || s[j] > bs)) {  // increasing e: ties keep the lower index
             bs = s[j];
@@ -197,12 +250,12 @@ __global__ __launch_bounds__(kSelectWaves * 64) void select_topk(const float* __
         const int owner = bi % 64, jj = bi / 64;
         float zv = z[0];
 #pragma unroll
-        for (int j = 1; j < 4; ++j)
+        for (int j = 1; j < NJ; ++j)
           if (jj == j) zv = z[j];
         zsel[r] = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(zv), owner));
         if (lane == owner) {
 #pragma unroll
-          for (int j = 0; j < 4; ++j)
+          for (int j = 0; j < NJ; ++j)
             if (jj == j) ok[j] = false;
         }
       }
@@ -223,12 +276,12 @@ __global__ __launch_bounds__(kSelectWaves * 64) void select_topk(const float* __
     } else if (score_fn == 1) {
       float m = -INFINITY;
 #pragma unroll
-      for (int j = 0; j < 4; ++j)
+      for (int j = 0; j < NJ; ++j)
         if (lane + 64 * j < E) m = fmaxf(m, z[j]);
       const double zmax = (double)wave_max(m);
       double part = 0.0;
 #pragma unroll
-      for (int j = 0; j < 4; ++j)
+      for (int j = 0; j < NJ; ++j)
         if (lane + 64 * j < E) part += exp((double)z[j] - zmax);
       wsum = wave_sum(part);
 #pragma unroll
@@ -297,9 +350,10 @@ static hipError_t launch_exact_logits(const RouteArgs& a, hipStream_t st) {
   }
   const int chunks = (Ep + EC - 1) / EC;
   if (EC == 8) {
-    // A single chunk of 8 experts: 4 token tiles per block.
-    dim3 grid((a.N + 255) / 256, 1);
-    logits_f64<8, 4><<<grid, 256, 0, st>>>(a.x, a.dtype, a.N, a.d, a.E, Ep, wt, a.router_bias,
+    // At most 8 experts: four waves of 2 experts each per 64-token tile, so
+    // the grid has one block per 64 tokens.
+    dim3 grid((a.N + 63) / 64, 1);
+    logits_f64<2, 1><<<grid, 256, 0, st>>>(a.x, a.dtype, a.N, a.d, a.E, Ep, wt, a.router_bias,
                                             a.logits, a.counts);
   } else if (chunks >= 4) {
     dim3 grid((a.N + 63) / 64, (chunks + 3) / 4);
@@ -331,8 +385,16 @@ hipError_t launch_route(const RouteArgs& a, hipStream_t st) {
   hipError_t err = launch_exact_logits(a, st);
   if (err != hipSuccess) return err;
   const int blocks = (a.N + kSelectTokensPerBlock - 1) / kSelectTokensPerBlock;
-  select_topk<<<blocks, kSelectWaves * 64, 0, st>>>(a.logits, a.sel_bias, a.N, a.E, a.k, a.G, a.kg,
-                                      a.score_fn, a.topk_idx, a.topk_w, a.counts);
+  auto select = [&](auto kernel) {
+    kernel<<<blocks, kSelectWaves * 64, 0, st>>>(a.logits, a.sel_bias, a.N, a.E, a.k, a.G, a.kg,
+                                                 a.score_fn, a.topk_idx, a.topk_w, a.counts);
+  };
+  switch ((a.E + 63) / 64) {
+    case 1: select(select_topk<1>); break;
+    case 2: select(select_topk<2>); break;
+    case 3: select(select_topk<3>); break;
+    default: select(select_topk<4>); break;
+  }
   return hipGetLastError();
 }
 
