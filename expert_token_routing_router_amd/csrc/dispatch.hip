@@ -108,7 +108,7 @@ __global__ __launch_bounds__(1024) void dispatch_count(const int32_t* __restrict
                                                        int32_t* __restrict__ rank_offsets,
                                                        int32_t* __restrict__ rank_counts) {
   __shared__ int32_t h[kCountLds];
-  __shared__ int32_t scan[1024];
+  __shared__ int32_t scan[16];  // wave totals of the expert scan
   __shared__ int32_t offs[1025];
   const int tid = threadIdx.x;
   const int cells = num_tiles * E;
@@ -141,22 +141,26 @@ __global__ __launch_bounds__(1024) void dispatch_count(const int32_t* __restrict
   }
   const int32_t adm = tid < E ? min(run, cap) : 0;
   if (tid < E) admitted[tid] = adm;
-  scan[tid] = adm;
-  __syncthreads();
-  for (int o = 1; o < 1024; o <<= 1) {
-    const int32_t v = tid >= o ? scan[tid - o] : 0;
-    __syncthreads();
-    scan[tid] += v;
-    __syncthreads();
+  // Exclusive scan of adm over experts: inclusive scan inside each wave,
+  // then the wave totals (E <= 1024: at most 16 waves).
+  const int lane = tid & 63, wv = tid >> 6;
+  int32_t incl = adm;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const int32_t v = __shfl_up(incl, o, 64);
+    if (lane >= o) incl += v;
   }
-  const int32_t excl = scan[tid] - adm;
+  if (lane == 63) scan[wv] = incl;
+  __syncthreads();
+  for (int w = 0; w < wv; ++w) incl += scan[w];
+  const int32_t excl = incl - adm;
   if (tid < E) {
     expert_offsets[tid] = excl;
     offs[tid] = excl;
   }
   if (tid == E - 1) {
-    expert_offsets[E] = scan[tid];
-    offs[E] = scan[tid];
+    expert_offsets[E] = incl;
+    offs[E] = incl;
   }
   __syncthreads();
   const int per = E / R;
@@ -178,6 +182,10 @@ __global__ __launch_bounds__(256) void dispatch_assign(
   const int wave = threadIdx.x / 64, lane = threadIdx.x % 64;
   const int s0 = blockIdx.x * kTileSlots;
 
+  // The tile's base ranks are loaded now, with the ids below, rather than
+  // after the per-wave counts.
+  // Descriptors allow at most 256 experts: thread e owns expert e.
+  const int32_t base = threadIdx.x < E ? tile_base[(size_t)blockIdx.x * E + threadIdx.x] : 0;
   for (int q = threadIdx.x; q < 4 * 256; q += 256) (&wcount[0][0])[q] = 0;
   for (int e = threadIdx.x; e <= E; e += 256) eoff[e] = expert_offsets[e];
   __syncthreads();
@@ -194,8 +202,9 @@ __global__ __launch_bounds__(256) void dispatch_assign(
   }
   __syncthreads();
   // Turn per-wave counts into per-wave base ranks: tile base + earlier waves.
-  for (int e = threadIdx.x; e < E; e += 256) {
-    int32_t run = tile_base[(size_t)blockIdx.x * E + e];
+  if (threadIdx.x < E) {
+    const int e = threadIdx.x;
+    int32_t run = base;
 #pragma unroll
     for (int w = 0; w < 4; ++w) {
       const int32_t c = wcount[w][e];
