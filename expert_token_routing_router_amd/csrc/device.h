@@ -128,6 +128,10 @@ __device__ __forceinline__ void wave_argmax(float& s, int& idx) {
 // hit distinct bank groups for 8- and for 16-lane LDS phases.  The pattern
 // depends on row bits 1-3 only, so rows 16 or 32 apart share it.
 __device__ __forceinline__ int swz4(int r) { return ((r >> 1) ^ (r >> 2)) & 3; }
+// The same for rows of eight 16-byte chunks (128 bytes): for each row parity,
+// the eight rows of a 16-row group map one logical chunk to eight distinct
+// physical chunks.
+__device__ __forceinline__ int swz8(int r) { return (r ^ (r >> 3)) & 7; }
 
 typedef __attribute__((address_space(3))) void* lds_ptr_t;
 

@@ -204,12 +204,24 @@ void grouped_gemm_bf16(
   constexpr int WN = BN / 4;                         // output columns per wave
   constexpr int FM = BM / 64, FN = WN / 32;          // fragments per wave
   constexpr int FN2 = DUAL ? FN : 1;
+  // Up GEMM (AP): the A rows are fetched as 128-byte pieces covering two K
+  // stages (full cache lines, half the requests of 64-byte pieces) into two
+  // pair slots; the weights keep their own ring of NW single stages.
+  constexpr bool AP = MODE == kUpGemm;
+  constexpr int ASLOT = BM * 2 * RB;                   // bytes of one A pair slot
+  constexpr int WST = BROWS * RB;                      // bytes of one weight stage
+  constexpr int NW_ = (kLdsBytes - 2 * ASLOT) / WST;
+  constexpr int NW = AP ? (NW_ < 6 ? NW_ : 6) : NS;    // weight ring depth
+  constexpr int LA2 = BM / 8 / 4;                      // A loads per pair, A waves (0-3)
+  constexpr int LDSB = AP ? 2 * ASLOT + NW * WST : NS * STAGE;
+  static_assert(!AP || (NW >= 4 && NW - 2 <= 4 && (NW - 1) * LB < 64 && 2 * LA2 < 64),
+                "pair ring: A pairs two stages ahead, weight waits covered below");
   static_assert(NS >= 3, "the ring needs three stages");
   static_assert(KK == 2, "register sets alternate per K step");
   static_assert(BM % (4 * RPL) == 0 && BROWS % (4 * RPL) == 0, "loads split over 4 waves");
   static_assert(WN % 32 == 0, "wave tile must be whole 32-column MFMA blocks");
   static_assert((NS - 1) * LMAX < 64, "loads in flight must fit the 6-bit vmcnt");
-  __shared__ __attribute__((aligned(1024))) char smem[NS * STAGE];
+  __shared__ __attribute__((aligned(1024))) char smem[LDSB];
 
   const int logical = xcd_logical(blockIdx.x, *tile_count * n_tiles);
   if (logical < 0) return;
@@ -217,7 +229,8 @@ void grouped_gemm_bf16(
   const int4 tile = tiles[mt];
   const int e = tile.x, r0 = tile.y, r1 = tile.z, g0 = tile.w;
   const int n0 = nt * BN;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  // wave is uniform: readfirstlane lets every per-wave index live in SGPRs.
+  const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wm = wave / 4, wn = wave % 4;
   const bool a_wave = wave < 4;
   const int grp = wave % 4;
@@ -228,6 +241,7 @@ void grouped_gemm_bf16(
   const bf16_t* src[LMAX];
   int ldst;  // LDS byte offset (within a stage) of this wave's first load
   size_t kstep;
+  int arow = 0, ach0 = 0, ach1 = 0;  // AP A waves: first row, logical chunk offsets
   if (a_wave && MODE == kDownGemm) {
     ldst = grp * LA * 1024;
     kstep = (size_t)ldg * 512;
@@ -238,17 +252,16 @@ void grouped_gemm_bf16(
       src[i] = A + (size_t)(g0 + g) * 512 + lane * 8;
     }
   } else if (a_wave) {
-    ldst = grp * LA * 1024;
-    kstep = BK;
-#pragma unroll
-    for (int i = 0; i < LMAX; ++i) {
-      const int sr = (grp * LA + (i < LA ? i : 0)) * RPL + lane / CH;  // stage row
-      const int c = (lane % CH) ^ swz4(sr);                             // logical chunk
-      const int row = min(r0 + sr, r1 - 1);  // rows past the tile: fetched, never used
-      src[i] = A + (size_t)row * K + c * 8;
-    }
+    // Load i of a pair: tile rows (grp * LA2 + i) * 8 + lane / 8, physical
+    // 16-byte chunk lane % 8 of the row's 128 bytes, which holds logical chunk
+    // (lane % 8) ^ swz8(row % 16); row % 16 = 8 (i % 2) + lane / 8.
+    ldst = 0;
+    kstep = 0;
+    arow = r0 + grp * LA2 * 8 + lane / 8;
+    ach0 = ((lane & 7) ^ swz8(lane >> 3)) * 8;
+    ach1 = ((lane & 7) ^ swz8(8 + (lane >> 3))) * 8;
   } else {
-    ldst = BM * RB + grp * LB * 1024;
+    ldst = (AP ? 0 : BM * RB) + grp * LB * 1024;
     const int SR = packed_slab_rows(N);
     kstep = (size_t)SR * BK;
 #pragma unroll
@@ -264,17 +277,21 @@ void grouped_gemm_bf16(
 
   // LDS byte offsets (within a stage) of this lane's MFMA fragments; the
   // chunk index of K step kk is (kk * 2 + lane / 32) ^ swizzle(row).
+  // (AP: A rows are 128 bytes in their pair slot, weight rows are offsets
+  // within their own stage.)
   int xoff[FM], woff[FN], woff2[FN2];
+  constexpr int WBASE = AP ? 0 : BM;
 #pragma unroll
-  for (int i = 0; i < FM; ++i) xoff[i] = ((2 * i + wm) * 32 + (lane & 31)) * RB;
+  for (int i = 0; i < FM; ++i) xoff[i] = ((2 * i + wm) * 32 + (lane & 31)) * (AP ? 2 * RB : RB);
 #pragma unroll
   for (int j = 0; j < FN; ++j) {
-    woff[j] = (BM + wn * WN + j * 32 + (lane & 31)) * RB;
-    if constexpr (DUAL) woff2[j] = (BM + BN + wn * WN + j * 32 + (lane & 31)) * RB;
+    woff[j] = (WBASE + wn * WN + j * 32 + (lane & 31)) * RB;
+    if constexpr (DUAL) woff2[j] = (WBASE + BN + wn * WN + j * 32 + (lane & 31)) * RB;
   }
   // Fragment rows differ from lane&31 by multiples of 32 (BM is one too), and
-  // the swizzle only looks at the low four row bits.
+  // the swizzles only look at the low four row bits.
   const int sw = swz4(lane & 31);
+  const int sw8 = swz8(lane & 15);
 
   // Live fragments of this wave: the tile has ceil(rows / 32) fragments,
   // numbered so that this wave owns wm, wm + 2, ...
@@ -301,16 +318,44 @@ void grouped_gemm_bf16(
                                            (lds_ptr_t)(base_ + i * 1024), 16, 0, kWeightCpol); \
     }                                                                                      \
   } while (0)
-  // Read the fragments of K step kk_ of ring slot slot_ into set S (FA_ live
-  // row fragments).
-#define MOE_LOAD_KK(FA_, slot_, kk_, S)                                                    \
+  // AP: weight stage kt_ into its ring slot (weight waves), A pair p_ into
+  // pair slot p_ & 1 (A waves).
+#define MOE_ISSUE_W(kt_)                                                                   \
   do {                                                                                     \
-    const char* st_ = smem + (slot_) * STAGE + ((((kk_) * 2 + (lane >> 5)) ^ sw) << 4);     \
+    char* base_ = smem + 2 * ASLOT + ((kt_) % NW) * WST + ldst;                            \
+    _Pragma("unroll") for (int i = 0; i < LB; ++i)                                         \
+        __builtin_amdgcn_global_load_lds((void*)(src[i] + (size_t)(kt_) * kstep),          \
+                                         (lds_ptr_t)(base_ + i * 1024), 16, 0, kWeightCpol); \
+  } while (0)
+#define MOE_ISSUE_A(p_)                                                                    \
+  do {                                                                                     \
+    char* base_ = smem + ((p_) & 1) * ASLOT + grp * LA2 * 1024;                            \
+    _Pragma("unroll") for (int i = 0; i < LA2; ++i) {                                      \
+      const int row_ = min(arow + 8 * i, r1 - 1); /* rows past the tile: never used */     \
+      __builtin_amdgcn_global_load_lds(                                                    \
+          (void*)(A + (size_t)row_ * K + ((i & 1) ? ach1 : ach0) + (size_t)(p_) * 2 * BK), \
+          (lds_ptr_t)(base_ + i * 1024), 16, 0, 0);                                        \
+    }                                                                                      \
+  } while (0)
+  // Read the fragments of K step kk_ of stage kt_ into set S (FA_ live row
+  // fragments).
+#define MOE_LOAD_KK(FA_, kt_, kk_, S)                                                      \
+  do {                                                                                     \
+    const char* xs_;                                                                       \
+    const char* ws_;                                                                       \
+    if constexpr (AP) {                                                                    \
+      xs_ = smem + (((kt_) >> 1) & 1) * ASLOT +                                            \
+            (((((kt_) & 1) * 4 + (kk_) * 2 + (lane >> 5)) ^ sw8) << 4);                    \
+      ws_ = smem + 2 * ASLOT + ((kt_) % NW) * WST + ((((kk_) * 2 + (lane >> 5)) ^ sw) << 4); \
+    } else {                                                                               \
+      xs_ = smem + ((kt_) % NS) * STAGE + ((((kk_) * 2 + (lane >> 5)) ^ sw) << 4);          \
+      ws_ = xs_;                                                                           \
+    }                                                                                      \
     _Pragma("unroll") for (int i = 0; i < (FA_); ++i)                                      \
-        xf##S[i] = *reinterpret_cast<const bf16x8_t*>(st_ + xoff[i]);                      \
+        xf##S[i] = *reinterpret_cast<const bf16x8_t*>(xs_ + xoff[i]);                      \
     _Pragma("unroll") for (int j = 0; j < FN; ++j) {                                       \
-      wf##S[j] = *reinterpret_cast<const bf16x8_t*>(st_ + woff[j]);                        \
-      if constexpr (DUAL) vf##S[j] = *reinterpret_cast<const bf16x8_t*>(st_ + woff2[j]);   \
+      wf##S[j] = *reinterpret_cast<const bf16x8_t*>(ws_ + woff[j]);                        \
+      if constexpr (DUAL) vf##S[j] = *reinterpret_cast<const bf16x8_t*>(ws_ + woff2[j]);   \
     }                                                                                      \
   } while (0)
 #define MOE_MFMA_KK(FA_, S)                                                                \
@@ -346,6 +391,17 @@ void grouped_gemm_bf16(
     }                                                                                      \
     ring_barrier();                                                                        \
   } while (0)
+  // AP weight waits: at most later_ younger weight stages of this wave in flight.
+#define MOE_WAIT_W(later_)                                                                 \
+  do {                                                                                     \
+    switch (later_) {                                                                      \
+      case 0: wait_vmcnt<0>(); break;                                                      \
+      case 1: wait_vmcnt<LB>(); break;                                                     \
+      case 2: wait_vmcnt<2 * LB>(); break;                                                 \
+      case 3: wait_vmcnt<3 * LB>(); break;                                                 \
+      default: wait_vmcnt<4 * LB>(); break;                                                \
+    }                                                                                      \
+  } while (0)
   // The whole K loop for FA_ live row fragments.  Every copy issues the same
   // loads and barriers; only the LDS reads and MFMAs differ.
 #define MOE_K_LOOP(FA_)                                                                    \
@@ -355,34 +411,91 @@ void grouped_gemm_bf16(
       acc[i][j] = floatx16{};                                                              \
       if constexpr (DUAL) acc2[i][j] = floatx16{};                                         \
     }                                                                                      \
-    _Pragma("unroll") for (int s = 0; s < NS - 1; ++s) if (s < ktiles) MOE_RING_ISSUE(s, s); \
-    MOE_WAIT_STAGE(min(NS - 2, ktiles - 1));                                               \
-    MOE_LOAD_KK(FA_, 0, 0, 0);                                                             \
-    /* Steady state: the refill is always in range and the wait count is  */            \
-    /* fixed, so the loop body has no branches besides the wave role.     */            \
     int kt = 0;                                                                            \
-    for (; kt + NS - 1 < ktiles; ++kt) {                                                   \
-      MOE_LOAD_KK(FA_, kt % NS, 1, 1);                                                     \
-      MOE_MFMA_KK(FA_, 0);                                                                 \
-      if (a_wave) wait_vmcnt<(NS - 3) * LA>(); else wait_vmcnt<(NS - 3) * LB>();           \
-      ring_barrier();                                                                      \
-      MOE_RING_ISSUE(kt + NS - 1, (kt + NS - 1) % NS);                                     \
-      MOE_LOAD_KK(FA_, (kt + 1) % NS, 0, 0);                                               \
-      MOE_MFMA_KK(FA_, 1);                                                                 \
-    }                                                                                      \
-    /* The last NS - 1 stages: nothing left to issue.                     */            \
-    for (; kt < ktiles; ++kt) {                                                            \
-      const int slot = kt % NS;                                                            \
-      MOE_LOAD_KK(FA_, slot, 1, 1);                                                        \
-      MOE_MFMA_KK(FA_, 0);                                                                 \
-      if (kt + 1 < ktiles) {                                                               \
-        /* Stage kt+1 visible to all waves; every wave is past its reads of  */            \
-        /* stage kt-1, so that slot can be refilled.                          */            \
-        MOE_WAIT_STAGE(min(NS - 3, ktiles - kt - 2));                                      \
-        if (kt + NS - 1 < ktiles) MOE_RING_ISSUE(kt + NS - 1, (kt + NS - 1) % NS);         \
-        MOE_LOAD_KK(FA_, (kt + 1) % NS, 0, 0);                                             \
+    if constexpr (AP) {                                                                    \
+      /* A pairs 0 and 1, weight stages 0 .. NW-2; stage 0 landed.          */            \
+      if (a_wave) {                                                                        \
+        MOE_ISSUE_A(0);                                                                    \
+        if (ktiles > 2) {                                                                  \
+          MOE_ISSUE_A(1);                                                                  \
+          wait_vmcnt<LA2>();                                                               \
+        } else {                                                                           \
+          wait_vmcnt<0>();                                                                 \
+        }                                                                                  \
+      } else {                                                                             \
+        _Pragma("unroll") for (int s = 0; s < NW - 1; ++s) if (s < ktiles) MOE_ISSUE_W(s); \
+        MOE_WAIT_W(min(NW - 2, ktiles - 1));                                               \
       }                                                                                    \
-      MOE_MFMA_KK(FA_, 1);                                                                 \
+      ring_barrier();                                                                      \
+      MOE_LOAD_KK(FA_, 0, 0, 0);                                                           \
+      /* Steady state: the weight refill and the next A pair are in range.  */            \
+      /* The wait at stage kt is for stage kt+1: for the A waves a new pair  */            \
+      /* when kt is odd (issued two stages ago, the only A loads in flight), */            \
+      /* after which pair (kt+3)/2 goes into the slot of stages kt-1 and kt. */            \
+      for (; kt + NW - 1 < ktiles; ++kt) {                                                 \
+        MOE_LOAD_KK(FA_, kt, 1, 1);                                                        \
+        MOE_MFMA_KK(FA_, 0);                                                               \
+        if (a_wave) {                                                                      \
+          if (kt & 1) wait_vmcnt<0>();                                                     \
+        } else {                                                                           \
+          wait_vmcnt<(NW - 3) * LB>();                                                     \
+        }                                                                                  \
+        ring_barrier();                                                                    \
+        if (a_wave) {                                                                      \
+          if (kt & 1) MOE_ISSUE_A((kt + 3) >> 1);                                          \
+        } else {                                                                           \
+          MOE_ISSUE_W(kt + NW - 1);                                                        \
+        }                                                                                  \
+        MOE_LOAD_KK(FA_, kt + 1, 0, 0);                                                    \
+        MOE_MFMA_KK(FA_, 1);                                                               \
+      }                                                                                    \
+      for (; kt < ktiles; ++kt) {                                                          \
+        MOE_LOAD_KK(FA_, kt, 1, 1);                                                        \
+        MOE_MFMA_KK(FA_, 0);                                                               \
+        if (kt + 1 < ktiles) {                                                             \
+          if (a_wave) {                                                                    \
+            if (kt & 1) wait_vmcnt<0>();                                                   \
+          } else {                                                                         \
+            MOE_WAIT_W(min(NW - 3, ktiles - kt - 2));                                      \
+          }                                                                                \
+          ring_barrier();                                                                  \
+          if (a_wave) {                                                                    \
+            if ((kt & 1) && kt + 3 < ktiles) MOE_ISSUE_A((kt + 3) >> 1);                   \
+          } else if (kt + NW - 1 < ktiles) {                                               \
+            MOE_ISSUE_W(kt + NW - 1);                                                      \
+          }                                                                                \
+          MOE_LOAD_KK(FA_, kt + 1, 0, 0);                                                  \
+        }                                                                                  \
+        MOE_MFMA_KK(FA_, 1);                                                               \
+      }                                                                                    \
+    } else {                                                                               \
+      _Pragma("unroll") for (int s = 0; s < NS - 1; ++s) if (s < ktiles) MOE_RING_ISSUE(s, s); \
+      MOE_WAIT_STAGE(min(NS - 2, ktiles - 1));                                             \
+      MOE_LOAD_KK(FA_, 0, 0, 0);                                                           \
+      /* Steady state: the refill is always in range and the wait count is  */            \
+      /* fixed, so the loop body has no branches besides the wave role.     */            \
+      for (; kt + NS - 1 < ktiles; ++kt) {                                                 \
+        MOE_LOAD_KK(FA_, kt, 1, 1);                                                        \
+        MOE_MFMA_KK(FA_, 0);                                                               \
+        if (a_wave) wait_vmcnt<(NS - 3) * LA>(); else wait_vmcnt<(NS - 3) * LB>();         \
+        ring_barrier();                                                                    \
+        MOE_RING_ISSUE(kt + NS - 1, (kt + NS - 1) % NS);                                   \
+        MOE_LOAD_KK(FA_, kt + 1, 0, 0);                                                    \
+        MOE_MFMA_KK(FA_, 1);                                                               \
+      }                                                                                    \
+      /* The last NS - 1 stages: nothing left to issue.                     */            \
+      for (; kt < ktiles; ++kt) {                                                          \
+        MOE_LOAD_KK(FA_, kt, 1, 1);                                                        \
+        MOE_MFMA_KK(FA_, 0);                                                               \
+        if (kt + 1 < ktiles) {                                                             \
+          /* Stage kt+1 visible to all waves; every wave is past its reads of */          \
+          /* stage kt-1, so that slot can be refilled.                         */          \
+          MOE_WAIT_STAGE(min(NS - 3, ktiles - kt - 2));                                    \
+          if (kt + NS - 1 < ktiles) MOE_RING_ISSUE(kt + NS - 1, (kt + NS - 1) % NS);       \
+          MOE_LOAD_KK(FA_, kt + 1, 0, 0);                                                  \
+        }                                                                                  \
+        MOE_MFMA_KK(FA_, 1);                                                               \
+      }                                                                                    \
     }                                                                                      \
   } while (0)
 
@@ -447,6 +560,9 @@ void grouped_gemm_bf16(
 #undef MOE_MFMA_KK
 #undef MOE_WAIT_STAGE
 #undef MOE_RING_ISSUE
+#undef MOE_ISSUE_W
+#undef MOE_ISSUE_A
+#undef MOE_WAIT_W
 }
 
 // Weight packing for the bf16 kernel: W [E, N, K] row-major -> slabs of SR
