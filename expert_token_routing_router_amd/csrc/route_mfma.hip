@@ -25,8 +25,10 @@ typedef float floatx4 __attribute__((ext_vector_type(4)));
 //                elements (global_load_lds_dwordx4); wave w multiplies tokens
 //                16(w/4).. by experts 16(w%4).. of the tile with
 //                v_mfma_f32_16x16x32_bf16 (fp32 within 64-element chunks, fp64
-//                across), and the block accumulates sum x_ti^2 and sum w_ei^2
-//                in fp64 from the same LDS data.  z~ = that sum + bias, kept
+//                across); upper bounds of sum x_ti^2 and sum w_ei^2 come from
+//                the diagonals of X X^T and W W^T by the same MFMA on the same
+//                operands (fp32 per 64 elements, padded by 2^-17 relative and
+//                2^-120 absolute, summed in fp64).  z~ = that sum + bias, kept
 //                as fp32.  Error bound: each fp32 rounding in a chunk of at
 //                most 64 exact products is at most 2^-23 of a partial sum
 //                bounded by S_c = sum over the chunk of |x_i w_i|, so the
@@ -91,7 +93,7 @@ __device__ __forceinline__ void route_tile_tail(
     uint64_t (*cand_s)[4], uint64_t (*gm_s)[2], int32_t* cnt_s, int32_t* hist,
     int32_t& npairs_s, int32_t& nfb_s) {
   static_assert(ZW >= 64 * NJ, "a zs row holds every expert");
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   uint16_t* plist = reinterpret_cast<uint16_t*>(scratch);  // (t_local << 8) | e
   typedef float ExpRow[ZW];
   typedef float GroupRows[2][64];
@@ -543,7 +545,7 @@ __global__ __launch_bounds__(kFuseWaves * 64, 2) void route_fused(
                 "group-limit scratch fits the ring");
   static_assert(kFuseTok <= 64 && ZW <= 256, "pair encoding and one-wave token scan");
 
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int t0 = blockIdx.x * kFuseTok;
   const int nt = min(kFuseTok, N - t0);
   const int nch = d / 32;
@@ -554,7 +556,15 @@ __global__ __launch_bounds__(kFuseWaves * 64, 2) void route_fused(
   // expert tile; wave w < 6 issues load w.  Lane L fetches row L/4 of its
   // load, logical 16-byte chunk (L % 4) ^ swz4(L / 4).
   const bool loader = wave < 6;
-  double sxp = 0.0;  // this thread's part of sum x^2 (row tid/16, 2 elements per chunk)
+  // Squared norms from the diagonal of X X^T and W W^T, one extra MFMA per
+  // chunk on the operands already in registers (waves 0 and 4 for the two
+  // token blocks, waves 0-3 for the expert blocks).  In the 16x16 output lane
+  // l holds rows 4(l/16) + v of column l % 16, so the diagonal element of row
+  // i = l % 16 is in lanes with l / 16 = i / 4, at v = i % 4.
+  const bool diag_lane = (lane >> 4) == ((lane & 15) >> 2);
+  const int diag_v = lane & 3;
+  double sxp = 0.0;  // waves 0 and 4, diagonal lanes: sum x^2 of token 16(wave/4) + lane%16
+  floatx4 sq32x = floatx4{0.f, 0.f, 0.f, 0.f};
   for (int et = 0; et < E; et += 64) {
     const u32x4* src;
     {
@@ -581,28 +591,13 @@ __global__ __launch_bounds__(kFuseWaves * 64, 2) void route_fused(
     // pair used.
     static_assert(kFuseRing >= 4, "two slots refilled per pair step");
     for (int c = 0; c < kFuseRing - 2 && c < nch; ++c) MOE_FUSE_ISSUE(c);
-    double swp = 0.0;  // sum w^2 part: expert row tid/8 of the tile, 4 elements per chunk
+    double swp = 0.0;  // waves 0-3, diagonal lanes: sum w^2 of expert 16 wave + lane%16
+    floatx4 sq32w = floatx4{0.f, 0.f, 0.f, 0.f};
     floatx4 acc32 = floatx4{0.f, 0.f, 0.f, 0.f};
     double acc[4] = {0.0, 0.0, 0.0, 0.0};
 #define MOE_FUSE_CHUNK(ch_)                                                                 \
   do {                                                                                      \
     const char* slot = ring[(ch_) % kFuseRing];                                             \
-    /* Squares: x once (first expert tile), w for every tile. */                           \
-    if (et == 0) { /* x: row tid/16, elements 2(tid%16), +1 of the chunk */                \
-      const int r = tid / 16, pq = tid % 16, c = pq / 4;                                    \
-      const uint32_t v = *reinterpret_cast<const uint32_t*>(                                \
-          slot + (r / 16) * 1024 + ((r % 16) * 4 + (c ^ swz4(r % 16))) * 16 + (pq % 4) * 4);  \
-      const double a0 = bf16_to_f32(v & 0xffffu), a1 = bf16_to_f32(v >> 16);                \
-      sxp = fma(a0, a0, fma(a1, a1, sxp));                                                  \
-    }                                                                                       \
-    { /* w: expert row tid/8, elements 4(tid%8)..+3 of the chunk */                        \
-      const int r = tid / 8, pq = tid % 8, c = pq / 2;                                      \
-      const uint2 v = *reinterpret_cast<const uint2*>(                                      \
-          slot + 2048 + (r / 16) * 1024 + ((r % 16) * 4 + (c ^ swz4(r % 16))) * 16 + (pq % 2) * 8); \
-      const double b0 = bf16_to_f32(v.x & 0xffffu), b1 = bf16_to_f32(v.x >> 16);            \
-      const double b2 = bf16_to_f32(v.y & 0xffffu), b3 = bf16_to_f32(v.y >> 16);            \
-      swp = fma(b0, b0, fma(b1, b1, fma(b2, b2, fma(b3, b3, swp))));                        \
-    }                                                                                       \
     /* MFMA: wave w takes token block w/4 (A = tokens 16(w/4) + (lane & 15)) */            \
     /* and expert block w%4 of the tile (B). */                                             \
     {                                                                                       \
@@ -613,6 +608,25 @@ __global__ __launch_bounds__(kFuseWaves * 64, 2) void route_fused(
       const bf16x8_t ax = *reinterpret_cast<const bf16x8_t*>(                               \
           slot + (wave / 4) * 1024 + (tr * 4 + (cc ^ swz4(tr))) * 16);                      \
       acc32 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ax, bw, acc32, 0, 0, 0);              \
+      if (wave < 4) sq32w = __builtin_amdgcn_mfma_f32_16x16x32_bf16(bw, bw, sq32w, 0, 0, 0); \
+      if (et == 0 && (wave & 3) == 0)                                                        \
+        sq32x = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ax, ax, sq32x, 0, 0, 0);             \
+    }                                                                                       \
+  } while (0)
+    // A pair's fp32 sums of at most 64 exact squares, as upper bounds in fp64:
+    // the rounded sum is at least (1 - 2^-18) of the exact one, and squares
+    // below 2^-126 that the MFMA may flush add at most 64 * 2^-126.
+#define MOE_FUSE_FOLD_SQ()                                                                  \
+  do {                                                                                      \
+    if (wave < 4) {                                                                         \
+      const float q = diag_v == 0 ? sq32w[0] : diag_v == 1 ? sq32w[1] : diag_v == 2 ? sq32w[2] : sq32w[3]; \
+      if (diag_lane) swp += (double)q * (1.0 + 0x1p-17) + 0x1p-120;                         \
+      sq32w = floatx4{0.f, 0.f, 0.f, 0.f};                                                  \
+    }                                                                                       \
+    if (et == 0 && (wave & 3) == 0) {                                                       \
+      const float q = diag_v == 0 ? sq32x[0] : diag_v == 1 ? sq32x[1] : diag_v == 2 ? sq32x[2] : sq32x[3]; \
+      if (diag_lane) sxp += (double)q * (1.0 + 0x1p-17) + 0x1p-120;                         \
+      sq32x = floatx4{0.f, 0.f, 0.f, 0.f};                                                  \
     }                                                                                       \
   } while (0)
     // Steady state: both refills of the step are in range, so the wait count
@@ -633,6 +647,7 @@ __global__ __launch_bounds__(kFuseWaves * 64, 2) void route_fused(
 #pragma unroll
       for (int v = 0; v < 4; ++v) acc[v] += (double)acc32[v];
       acc32 = floatx4{0.f, 0.f, 0.f, 0.f};
+      MOE_FUSE_FOLD_SQ();
     }
     // The last pairs: fewer younger chunks in flight, at most one refill.
     for (; ch < nch; ch += 2) {
@@ -650,8 +665,10 @@ __global__ __launch_bounds__(kFuseWaves * 64, 2) void route_fused(
 #pragma unroll
       for (int v = 0; v < 4; ++v) acc[v] += (double)acc32[v];
       acc32 = floatx4{0.f, 0.f, 0.f, 0.f};
+      MOE_FUSE_FOLD_SQ();
     }
 #undef MOE_FUSE_CHUNK
+#undef MOE_FUSE_FOLD_SQ
 #undef MOE_FUSE_ISSUE
     // z~: lane holds expert (lane & 15) of block w%4, tokens 16(w/4) + 4*(lane>>4)+v.
     const int e = et + 16 * (wave % 4) + (lane & 15);
@@ -660,15 +677,11 @@ __global__ __launch_bounds__(kFuseWaves * 64, 2) void route_fused(
 #pragma unroll
       for (int v = 0; v < 4; ++v) zs[16 * (wave / 4) + 4 * (lane >> 4) + v][e] = (float)(acc[v] + bias);
     }
-    // sum w^2: the 8 threads of an expert row are consecutive lanes.
-#pragma unroll
-    for (int o = 1; o < 8; o <<= 1) swp += __shfl_xor(swp, o, 64);
-    if (tid % 8 == 0 && et + tid / 8 < E) sw[et + tid / 8] = swp;
+    // sum w^2: from the diagonal lanes of waves 0-3.
+    if (wave < 4 && diag_lane && et + 16 * wave + (lane & 15) < E) sw[et + 16 * wave + (lane & 15)] = swp;
     __syncthreads();  // ring slots are reused by the next expert tile
   }
-#pragma unroll
-  for (int o = 1; o < 16; o <<= 1) sxp += __shfl_xor(sxp, o, 64);
-  if (tid % 16 == 0) sx[tid / 16] = sxp;
+  if ((wave & 3) == 0 && diag_lane) sx[16 * (wave >> 2) + (lane & 15)] = sxp;
   __syncthreads();
 
   route_tile_tail<NJ, ZW>(x, w, d, E, k, G, kg, score_fn, router_bias, sel_bias, logits,
