@@ -77,11 +77,28 @@ __device__ __forceinline__ float silu(float g) { return g * __builtin_amdgcn_rcp
 // numbering gives every tile ceil(rows / 16) groups of its own, in tile order:
 // the packed hidden buffer of the bf16 FFN stores a tile's rows there.  Rows
 // are clamped to max_rows.
+// Inclusive scan over the 1024 threads of a block: shuffles inside each wave,
+// then the 16 wave totals (two barriers instead of a Hillis-Steele loop).
+__device__ __forceinline__ int32_t block_scan_1024(int32_t v, int32_t* wsum) {
+  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const int32_t u = __shfl_up(v, o, 64);
+    if (lane >= o) v += u;
+  }
+  __syncthreads();  // wsum is free (a previous scan may still be reading it)
+  if (lane == 63) wsum[wv] = v;
+  __syncthreads();
+  for (int w = 0; w < wv; ++w) v += wsum[w];
+  return v;
+}
+
 __global__ __launch_bounds__(1024) void ffn_plan_tiles(const int32_t* __restrict__ offsets,
                                                        int E, int BM, int max_rows,
                                                        int4* __restrict__ tiles,
                                                        int32_t* __restrict__ count) {
-  __shared__ int32_t s[1024];
+  __shared__ int32_t wsum[16];
+  __shared__ int32_t total_s;
   const int e = threadIdx.x;
   int32_t lo = 0, hi = 0, n = 0, chunk = BM;
   if (e < E) {
@@ -90,36 +107,19 @@ __global__ __launch_bounds__(1024) void ffn_plan_tiles(const int32_t* __restrict
     n = hi > lo ? (hi - lo + BM - 1) / BM : 0;
     if (n > 0) chunk = ((hi - lo + n - 1) / n + 31) / 32 * 32;
   }
-  s[e] = n;
-  __syncthreads();
-  for (int o = 1; o < 1024; o <<= 1) {
-    const int32_t v = e >= o ? s[e - o] : 0;
-    __syncthreads();
-    s[e] += v;
-    __syncthreads();
-  }
-  const int32_t start = s[e] - n;
+  const int32_t n_incl = block_scan_1024(n, wsum);
+  const int32_t start = n_incl - n;
+  if (e == E - 1) total_s = n_incl;
   // 16-row groups of this expert's tiles, then their exclusive prefix.
   int32_t ng = 0;
   for (int q = 0; q < n; ++q) ng += (min(hi, lo + (q + 1) * chunk) - (lo + q * chunk) + 15) / 16;
-  __syncthreads();
-  const int32_t total_tiles = s[E - 1];
-  __syncthreads();
-  s[e] = ng;
-  __syncthreads();
-  for (int o = 1; o < 1024; o <<= 1) {
-    const int32_t v = e >= o ? s[e - o] : 0;
-    __syncthreads();
-    s[e] += v;
-    __syncthreads();
-  }
-  int32_t g0 = s[e] - ng;
+  int32_t g0 = block_scan_1024(ng, wsum) - ng;
   for (int q = 0; q < n; ++q) {
     const int32_t r0 = lo + q * chunk, r1 = min(hi, r0 + chunk);
     tiles[start + q] = make_int4(e, r0, r1, g0);
     g0 += (r1 - r0 + 15) / 16;
   }
-  if (e == 0) *count = total_tiles;
+  if (e == 0) *count = total_s;  // written by thread E-1 before the second scan's barriers
 }
 
 // XCD-aware block order.  The hardware deals blocks round-robin over the 8
