@@ -522,13 +522,18 @@ __device__ __forceinline__ void route_tile_tail(
   for (int i = tid; i < nt * E; i += kFuseWaves * 64) logits[(size_t)t0 * E + i] = zs[i / E][i % E];
 }
 
-// NJ = ceil(E / 64) expert slots per lane in steps 2 and 4.
-template <int NJ>
+// NJ = ceil(E / 64) expert slots per lane in steps 2 and 4.  SPLIT 0 runs
+// every step; with few token tiles and several expert tiles the work is split
+// in two launches so that step 1 runs on every CU: SPLIT 1 is step 1 for one
+// expert tile (blockIdx.y) per block, writing z~ to `logits` and the squared
+// norms to ws_sx / ws_sw; SPLIT 2 reads them back and runs steps 2-4.
+template <int NJ, int SPLIT>
 __global__ __launch_bounds__(kFuseWaves * 64, 2) void route_fused(
     const bf16_t* __restrict__ x, const bf16_t* __restrict__ w, int N, int d, int E, int k,
     int G, int kg, int score_fn, const float* __restrict__ router_bias,
     const float* __restrict__ sel_bias, float* __restrict__ logits,
-    int32_t* __restrict__ topk_idx, float* __restrict__ topk_w, int32_t* __restrict__ counts) {
+    int32_t* __restrict__ topk_idx, float* __restrict__ topk_w, int32_t* __restrict__ counts,
+    double* __restrict__ ws_sx, double* __restrict__ ws_sw) {
   constexpr int ZW = 64 * NJ;
   __shared__ float zs[kFuseTok][ZW];  // z~, then exact values for candidates
   __shared__ __attribute__((aligned(1024))) char ring[kFuseRing][kFuseSlot];  // step 1; then pairs
@@ -546,8 +551,11 @@ __global__ __launch_bounds__(kFuseWaves * 64, 2) void route_fused(
   static_assert(kFuseTok <= 64 && ZW <= 256, "pair encoding and one-wave token scan");
 
   const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int t0 = blockIdx.x * kFuseTok;
-  const int nt = min(kFuseTok, N - t0);
+  // The tail launch takes 16 tokens per block, so that the few token tiles
+  // of a split launch still cover every CU.
+  constexpr int TPB = SPLIT == 2 ? kFuseTok / 2 : kFuseTok;
+  const int t0 = blockIdx.x * TPB;
+  const int nt = min(TPB, N - t0);
   const int nch = d / 32;
   for (int e = tid; e < E; e += kFuseWaves * 64) hist[e] = 0;
 
@@ -565,7 +573,9 @@ __global__ __launch_bounds__(kFuseWaves * 64, 2) void route_fused(
   const int diag_v = lane & 3;
   double sxp = 0.0;  // waves 0 and 4, diagonal lanes: sum x^2 of token 16(wave/4) + lane%16
   floatx4 sq32x = floatx4{0.f, 0.f, 0.f, 0.f};
-  for (int et = 0; et < E; et += 64) {
+  const int et_begin = SPLIT == 1 ? 64 * (int)blockIdx.y : 0;
+  const int et_end = SPLIT == 1 ? et_begin + 64 : (SPLIT == 2 ? 0 : E);
+  for (int et = et_begin; et < et_end; et += 64) {
     const u32x4* src;
     {
       const int j = min(wave, 5);
@@ -675,13 +685,38 @@ __global__ __launch_bounds__(kFuseWaves * 64, 2) void route_fused(
     if (e < E) {
       const double bias = router_bias ? (double)router_bias[e] : 0.0;
 #pragma unroll
-      for (int v = 0; v < 4; ++v) zs[16 * (wave / 4) + 4 * (lane >> 4) + v][e] = (float)(acc[v] + bias);
+      for (int v = 0; v < 4; ++v) {
+        const int tl = 16 * (wave / 4) + 4 * (lane >> 4) + v;
+        if constexpr (SPLIT == 1) {
+          if (tl < nt) logits[(size_t)(t0 + tl) * E + e] = (float)(acc[v] + bias);
+        } else {
+          zs[tl][e] = (float)(acc[v] + bias);
+        }
+      }
     }
     // sum w^2: from the diagonal lanes of waves 0-3.
-    if (wave < 4 && diag_lane && et + 16 * wave + (lane & 15) < E) sw[et + 16 * wave + (lane & 15)] = swp;
+    if (wave < 4 && diag_lane && et + 16 * wave + (lane & 15) < E) {
+      if constexpr (SPLIT == 1) {
+        if (blockIdx.x == 0) ws_sw[et + 16 * wave + (lane & 15)] = swp;
+      } else {
+        sw[et + 16 * wave + (lane & 15)] = swp;
+      }
+    }
     __syncthreads();  // ring slots are reused by the next expert tile
   }
-  if ((wave & 3) == 0 && diag_lane) sx[16 * (wave >> 2) + (lane & 15)] = sxp;
+  if constexpr (SPLIT == 1) {
+    const int tl = 16 * (wave >> 2) + (lane & 15);
+    if (blockIdx.y == 0 && (wave & 3) == 0 && diag_lane && tl < nt) ws_sx[t0 + tl] = sxp;
+    return;
+  }
+  if constexpr (SPLIT == 2) {
+    // The tile's z~ and norms from the scoring launch.
+    for (int i = tid; i < nt * E; i += kFuseWaves * 64) zs[i / E][i % E] = logits[(size_t)t0 * E + i];
+    for (int tl = tid; tl < nt; tl += kFuseWaves * 64) sx[tl] = ws_sx[t0 + tl];
+    for (int e = tid; e < E; e += kFuseWaves * 64) sw[e] = ws_sw[e];
+  } else {
+    if ((wave & 3) == 0 && diag_lane) sx[16 * (wave >> 2) + (lane & 15)] = sxp;
+  }
   __syncthreads();
 
   route_tile_tail<NJ, ZW>(x, w, d, E, k, G, kg, score_fn, router_bias, sel_bias, logits,
@@ -694,26 +729,58 @@ __global__ __launch_bounds__(kFuseWaves * 64, 2) void route_fused(
 
 // ---------------------------------------------------------------- launch ---
 
+// Split launches (see route_fused) when there are several expert tiles but
+// fewer token tiles than two per CU.
+static bool route_split(int N, int E) {
+  return E > 64 && (N + kFuseTok - 1) / kFuseTok < 512;
+}
+
 size_t route_certified_workspace_bytes(int N, int E) {
-  (void)N;
-  (void)E;
-  return 0;  // everything lives in LDS
+  // The fused kernel keeps everything in LDS; the split one passes the
+  // squared norms between its two launches.
+  return route_split(N, E) ? (size_t)(N + E) * sizeof(double) : 0;
 }
 
 hipError_t launch_route_certified(const RouteArgs& a, hipStream_t st) {
   launch_zero_i32(a.counts, a.E, st);
   const int blocks = (a.N + kFuseTok - 1) / kFuseTok;
-  auto launch = [&](auto kernel) {
-    kernel<<<blocks, kFuseWaves * 64, 0, st>>>(
+  const bool split = route_split(a.N, a.E);
+  double* ws_sx = split ? static_cast<double*>(a.ws) : nullptr;
+  double* ws_sw = split ? ws_sx + a.N : nullptr;
+  auto launch = [&](auto kernel, dim3 grid) {
+    kernel<<<grid, kFuseWaves * 64, 0, st>>>(
         static_cast<const bf16_t*>(a.x), static_cast<const bf16_t*>(a.w_router), a.N, a.d, a.E,
         a.k, a.G, a.kg, a.score_fn, a.router_bias, a.sel_bias, a.logits, a.topk_idx, a.topk_w,
-        a.counts);
+        a.counts, ws_sx, ws_sw);
   };
+  const dim3 scores_grid(blocks, (a.E + 63) / 64);
+  const dim3 tail_grid((a.N + kFuseTok / 2 - 1) / (kFuseTok / 2));
   switch ((a.E + 63) / 64) {
-    case 1: launch(route_fused<1>); break;
-    case 2: launch(route_fused<2>); break;
-    case 3: launch(route_fused<3>); break;
-    default: launch(route_fused<4>); break;
+    case 1: launch(route_fused<1, 0>, dim3(blocks)); break;
+    case 2:
+      if (split) {
+        launch(route_fused<2, 1>, scores_grid);
+        launch(route_fused<2, 2>, tail_grid);
+      } else {
+        launch(route_fused<2, 0>, dim3(blocks));
+      }
+      break;
+    case 3:
+      if (split) {
+        launch(route_fused<3, 1>, scores_grid);
+        launch(route_fused<3, 2>, tail_grid);
+      } else {
+        launch(route_fused<3, 0>, dim3(blocks));
+      }
+      break;
+    default:
+      if (split) {
+        launch(route_fused<4, 1>, scores_grid);
+        launch(route_fused<4, 2>, tail_grid);
+      } else {
+        launch(route_fused<4, 0>, dim3(blocks));
+      }
+      break;
   }
   return hipGetLastError();
 }
