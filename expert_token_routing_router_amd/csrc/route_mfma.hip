@@ -523,8 +523,8 @@ __device__ __forceinline__ void route_tile_tail(
 }
 
 // NJ = ceil(E / 64) expert slots per lane in steps 2 and 4.  SPLIT 0 runs
-// every step; with few token tiles and several expert tiles the work is split
-// in two launches so that step 1 runs on every CU: SPLIT 1 is step 1 for one
+// every step; with several expert tiles the work is split in two launches so
+// that the expert tiles of step 1 run in parallel: SPLIT 1 is step 1 for one
 // expert tile (blockIdx.y) per block, writing z~ to `logits` and the squared
 // norms to ws_sx / ws_sw; SPLIT 2 reads them back and runs steps 2-4.
 template <int NJ, int SPLIT>
@@ -729,10 +729,12 @@ __global__ __launch_bounds__(kFuseWaves * 64, 2) void route_fused(
 
 // ---------------------------------------------------------------- launch ---
 
-// Split launches (see route_fused) when there are several expert tiles but
-// fewer token tiles than two per CU.
+// Split launches (see route_fused) whenever there are several expert tiles
+// (measured: Zipf-like 32768 tokens x 128 experts 210 -> 178 us; with one
+// expert tile the extra launch costs more than it gains, 42 -> 55 us).
 static bool route_split(int N, int E) {
-  return E > 64 && (N + kFuseTok - 1) / kFuseTok < 512;
+  (void)N;
+  return E > 64;
 }
 
 size_t route_certified_workspace_bytes(int N, int E) {
