@@ -349,45 +349,57 @@ __device__ __forceinline__ void route_tile_tail(
     }
   }
   __syncthreads();
-  // The chain itself for the pairs the test did not settle, one per lane;
-  // loads run 8 vectors (64 elements) ahead of it.
+  // The chain itself for the pairs the test did not settle, one wave per pair:
+  // for each 256 elements the lanes form the exact products (4 each) and store
+  // them to a 2-KB staging buffer of the wave, after the fallback list in the
+  // scratch; then every lane runs the same running fp64 sum over them in
+  // order (broadcast LDS reads), one rounded add each -- the definition's
+  // fma(x, w, acc) with an exact product is the same add.  Conversions,
+  // products and loads stay off the dependency chain.
+  constexpr int kStageBytes = 2048;
+  constexpr int kFbEnd = 2 * kFuseTok * ZW * 2;  // end of the pair and fallback lists
+  constexpr int kStagers = (kFuseRing * kFuseSlot - kFbEnd) / kStageBytes < kFuseWaves
+                               ? (kFuseRing * kFuseSlot - kFbEnd) / kStageBytes
+                               : kFuseWaves;
+  static_assert(kStagers >= 1, "room for one staging buffer");
   const int nfb = nfb_s;
-  for (int p = tid; p < nfb; p += kFuseWaves * 64) {
-    const int v = fb[p];
-    const int tl = v >> 8, e = v & 255;
-    const u32x4* xr = reinterpret_cast<const u32x4*>(x + (size_t)(t0 + tl) * d);
-    const u32x4* wr = reinterpret_cast<const u32x4*>(w + (size_t)e * d);
-    constexpr int AHEAD = 8;
-    const int nv = d / 8;  // a multiple of 4 (d % 32 == 0)
-    u32x4 xa[AHEAD], wa[AHEAD];
-#pragma unroll
-    for (int u = 0; u < AHEAD; ++u) {
-      xa[u] = u < nv ? xr[u] : u32x4{0u, 0u, 0u, 0u};
-      wa[u] = u < nv ? wr[u] : u32x4{0u, 0u, 0u, 0u};
-    }
-    double acc = 0.0;
-    for (int i0 = 0; i0 < nv; i0 += AHEAD) {
-#pragma unroll
-      for (int u = 0; u < AHEAD; ++u) {
-        const u32x4 a = xa[u], b = wa[u];
-        const int nxt = i0 + AHEAD + u;
-        if (nxt < nv) {
-          xa[u] = xr[nxt];
-          wa[u] = wr[nxt];
+  if (wave < kStagers) {
+    double* stage = reinterpret_cast<double*>(scratch + kFbEnd + wave * kStageBytes);
+    for (int p = wave; p < nfb; p += kStagers) {
+      const int v = fb[p];
+      const int tl = v >> 8, e = v & 255;
+      const uint2* xr = reinterpret_cast<const uint2*>(x + (size_t)(t0 + tl) * d);
+      const uint2* wr = reinterpret_cast<const uint2*>(w + (size_t)e * d);
+      const int nq = d / 4;  // 4-element pieces per row (d % 32 == 0)
+      double acc = 0.0;
+      uint2 xa = lane < nq ? xr[lane] : uint2{0u, 0u};
+      uint2 wa = lane < nq ? wr[lane] : uint2{0u, 0u};
+      for (int q0 = 0; q0 < nq; q0 += 64) {
+        const double p0 = (double)bf16_to_f32(xa.x & 0xffffu) * (double)bf16_to_f32(wa.x & 0xffffu);
+        const double p1 = (double)bf16_to_f32(xa.x >> 16) * (double)bf16_to_f32(wa.x >> 16);
+        const double p2 = (double)bf16_to_f32(xa.y & 0xffffu) * (double)bf16_to_f32(wa.y & 0xffffu);
+        const double p3 = (double)bf16_to_f32(xa.y >> 16) * (double)bf16_to_f32(wa.y >> 16);
+        if (q0 + 64 + lane < nq) {  // next 256 elements, while these are summed
+          xa = xr[q0 + 64 + lane];
+          wa = wr[q0 + 64 + lane];
         }
-        if (i0 + u < nv) {
-#pragma unroll
-          for (int q = 0; q < 4; ++q) {
-            acc = __fma_rn((double)bf16_to_f32(a[q] & 0xffffu),
-                           (double)bf16_to_f32(b[q] & 0xffffu), acc);
-            acc = __fma_rn((double)bf16_to_f32(a[q] >> 16), (double)bf16_to_f32(b[q] >> 16),
-                           acc);
-          }
-        }
+        stage[4 * lane] = p0;
+        stage[4 * lane + 1] = p1;
+        stage[4 * lane + 2] = p2;
+        stage[4 * lane + 3] = p3;
+        __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+        __builtin_amdgcn_wave_barrier();
+        const int n = 4 * min(64, nq - q0);
+#pragma unroll 16
+        for (int i = 0; i < n; ++i) acc = acc + stage[i];
+        __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+        __builtin_amdgcn_wave_barrier();
+      }
+      if (lane == 0) {
+        if (router_bias) acc = acc + (double)router_bias[e];
+        zs[tl][e] = __double2float_rn(acc);
       }
     }
-    if (router_bias) acc = acc + (double)router_bias[e];
-    zs[tl][e] = __double2float_rn(acc);
   }
   __syncthreads();
 
