@@ -40,27 +40,29 @@ typedef float floatx4 __attribute__((ext_vector_type(4)));
 
 enum { ACT_RELU = 0, ACT_GELU = 1, ACT_SWIGLU = 2, ACT_NONE = 3 };
 
-// erf(x) by Abramowitz & Stegun, Handbook of Mathematical Functions, formula
-// 7.1.26: for x >= 0, erf(x) = 1 - (a1 t + a2 t^2 + a3 t^3 + a4 t^4 + a5 t^5)
-// exp(-x^2) with t = 1 / (1 + p x); absolute error <= 1.5e-7.  t comes from
-// v_rcp_f32 (within 2 ulp on gfx950) and the fp32 evaluation adds a few ulp:
-// all far below the bf16 rounding H goes through.
-// erf is odd, so the sign is restored at the end.
-__device__ __forceinline__ float erf_as7126(float x) {
-  const float ax = fabsf(x);
-  const float t = __builtin_amdgcn_rcpf(fmaf(0.3275911f, ax, 1.0f));
-  float poly = fmaf(1.061405429f, t, -1.453152027f);
-  poly = fmaf(poly, t, 1.421413741f);
-  poly = fmaf(poly, t, -0.284496736f);
-  poly = fmaf(poly, t, 0.254829592f);
-  poly *= t;
-  const float r = 1.0f - poly * __expf(-ax * ax);
-  return copysignf(r, x);
+// GELU(u) = 0.5 u (1 + erf(u / sqrt 2)) with erf from Abramowitz & Stegun,
+// Handbook of Mathematical Functions, formula 7.1.26: for x >= 0,
+// erf(x) = 1 - P(t) exp(-x^2), P(t) = a1 t + a2 t^2 + a3 t^3 + a4 t^4 + a5 t^5,
+// t = 1 / (1 + p x), absolute error <= 1.5e-7.  erf is odd, so with x = |u|/sqrt 2
+// the factor 1 + erf is 2 - P e for u >= 0 and P e for u < 0 (e = exp(-u^2/2)),
+// and both cases are GELU(u) = max(u, 0) - 0.5 |u| P e.  The code folds 1/sqrt 2
+// into p and the 0.5 into the a_i, and takes e as 2^(-u^2 log2(e) / 2) on
+// v_exp_f32.  t comes from v_rcp_f32 (within 2 ulp on gfx950); the fp32
+// evaluation adds a few ulp, all far below the bf16 rounding H goes through.
+__device__ __forceinline__ float gelu_as7126(float u) {
+  const float a = fabsf(u);
+  const float t = __builtin_amdgcn_rcpf(fmaf(0.3275911f * 0.70710678118654752440f, a, 1.0f));
+  float q = fmaf(0.5f * 1.061405429f, t, 0.5f * -1.453152027f);
+  q = fmaf(q, t, 0.5f * 1.421413741f);
+  q = fmaf(q, t, 0.5f * -0.284496736f);
+  q = fmaf(q, t, 0.5f * 0.254829592f);
+  const float e = __builtin_amdgcn_exp2f(u * u * -0.72134752044448170368f);
+  return fmaf(-(a * t), q * e, fmaxf(u, 0.f));
 }
 
 __device__ __forceinline__ float apply_act(float u, int act) {
   if (act == ACT_RELU) return fmaxf(u, 0.f);
-  if (act == ACT_GELU) return 0.5f * u * (1.f + erf_as7126(u * 0.70710678118654752440f));
+  if (act == ACT_GELU) return gelu_as7126(u);
   return u;
 }
 
