@@ -10,7 +10,9 @@ admission), GELU experts 1024->4096->1024, 8 simulated EP ranks, bf16.
 
 Prints one JSON line.  Every library call inside the timed region is bracketed
 by HIP events on the stream it is launched on; the per-call averages give the
-roofline of the dominant kernel and the per-step breakdown.  The CPU oracle is
+roofline of the dominant kernel and the per-step breakdown.  Two more passes
+give the step-time percentiles (one event per step) and the cold-cache per-call
+times (a 512 MiB write before each step evicts the Infinity Cache and the L2s).  The CPU oracle is
 timed on a bounded sample of the same workload (``cpu_baseline``).
 """
 
@@ -45,6 +47,9 @@ def parse_args():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0,
                     help="target length of the oracle's timed sample")
+    ap.add_argument("--rank-share", action="store_true",
+                    help="also time the expert FFN on one rank's share of the experts at "
+                         "its real shape (rows from all R source ranks)")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="also run one device copy of this size (counter calibration)")
     return ap.parse_args()
@@ -79,6 +84,79 @@ def read_traffic(kernel: str, workload: str, digest: str):
         return float(vals["hbm_bytes_per_launch"])
     except (KeyError, ValueError):
         return None
+
+
+def read_clocks() -> dict:
+    """Current clocks from rocm-smi, if it answers within a few seconds.  Runs
+    before this process initialises the GPU."""
+    info = {}
+    try:
+        import subprocess
+        r = subprocess.run(["rocm-smi", "--showclocks", "--json"], capture_output=True,
+                           text=True, timeout=20)
+        card = next(iter(json.loads(r.stdout).values()))
+        for key, val in card.items():
+            kl = key.lower()
+            if "sclk" in kl or "mclk" in kl:
+                info[key] = val
+    except Exception as exc:  # clocks are context, never a reason to fail
+        info["clocks"] = f"unavailable ({type(exc).__name__})"
+    return info
+
+
+def rank_share(moe, torch, cfg, buf, wts, steps: int) -> dict:
+    """The expert FFN on one rank's share at its real shape: rank 0's E/R local
+    experts, each receiving rows from all R source ranks.  The receive buffer is
+    this batch's rows for those experts repeated R times (each source rank sends
+    its own tokens' rows; the repeat gives the same row count and shapes)."""
+    d = buf.desc
+    E, R, dim, h = d.num_experts, d.num_ranks, d.hidden, cfg["h"]
+    El = E // R
+    dev = buf.x_perm.device
+    off = buf.expert_offsets.cpu().tolist()
+    chunks = [buf.x_perm[off[e]:off[e + 1]].repeat(R, 1) for e in range(El)]
+    rows = [c.shape[0] for c in chunks]
+    recv = torch.cat(chunks)
+    M = recv.shape[0]
+    goff = torch.zeros(El + 1, dtype=torch.int32)
+    goff[1:] = torch.cumsum(torch.tensor(rows, dtype=torch.int32), 0)
+    goff = goff.to(dev)
+    w1 = wts["w1"][:El]
+    w3 = wts["w3"][:El] if wts.get("w3") is not None else None
+    w2 = wts["w2"][:El]
+    y = torch.empty_like(recv)
+    ws = moe.workspace(moe.moe_expert_ffn_workspace_size(El, M, dim, h, cfg["act"], cfg["dtype"]),
+                       device=dev)
+
+    def run():
+        moe.moe_expert_ffn(El, M, dim, h, cfg["act"], cfg["dtype"], recv, goff, w1, w3, w2, y, ws)
+
+    for _ in range(3):
+        run()
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+    torch.cuda.synchronize()
+    ev[0].record()
+    for _ in range(steps):
+        run()
+    ev[1].record()
+    torch.cuda.synchronize()
+    us = ev[0].elapsed_time(ev[1]) / steps * 1e3
+    es = 2 if cfg["dtype"] == "bf16" else 4
+    mats_up = 2 if cfg["act"] == "swiglu" else 1
+    flops = 2.0 * M * dim * h * (mats_up + 1)
+    nbytes = (El * (mats_up + 1) * h * dim + 2 * M * dim) * es
+    peak = MFMA_PEAK_TFLOPS[cfg["dtype"]]
+    # Each output row depends only on its input row and the expert's weights,
+    # so every copy must equal the layer step's own output for that row.
+    same = all(torch.equal(y[int(goff[e]) + c * (rows[e] // R):int(goff[e]) + (c + 1) * (rows[e] // R)],
+                           buf.y_perm[off[e]:off[e + 1]])
+               for e in range(El) for c in range(R))
+    return {"local_experts": El, "rows": M, "rows_per_expert": rows, "us": round(us, 1),
+            "rows_equal_layer_output": bool(same),
+            "tflops": round(flops / (us * 1e-6) / 1e12, 1),
+            "mfma_frac": round(flops / (us * 1e-6) / (peak * 1e12), 4),
+            "hbm_frac": round(nbytes / (us * 1e-6) / (HBM_PEAK_GBS * 1e9), 4),
+            "bound": "mfma" if flops / (peak * 1e12) >= nbytes / (HBM_PEAK_GBS * 1e9) else "hbm"}
 
 
 def describe(cfg) -> str:
@@ -132,9 +210,23 @@ def cpu_baseline(cfg, inp, target_s: float) -> dict:
             break
         T = int(min(cfg["N"], max(2 * T, T * target_s / max(elapsed, 1e-6))))
         elapsed = run(T)
-    return {"value": T / elapsed, "unit": "tokens/s", "cores": threads, "kind": "oracle",
-            "sample": f"first {T} of {cfg['N']} tokens as one batch (capacity for {T}); "
-                      f"route+dispatch+FFN+combine+bias update; {elapsed:.1f} s"}
+    out = {"value": T / elapsed, "unit": "tokens/s", "cores": threads, "kind": "oracle",
+           "sample": f"first {T} of {cfg['N']} tokens as one batch (capacity for {T}); "
+                     f"route+dispatch+FFN+combine+bias update; {elapsed:.1f} s"}
+
+    # The same on one thread, the plain loops as written, on a smaller sample.
+    oracle.set_threads(1)
+    T1 = min(cfg["N"], 16)
+    e1 = run(T1)
+    for _ in range(4):
+        if e1 >= target_s / 4 or T1 >= cfg["N"]:
+            break
+        T1 = int(min(cfg["N"], max(2 * T1, T1 * (target_s / 2) / max(e1, 1e-6))))
+        e1 = run(T1)
+    oracle.set_threads(threads)
+    out["single_thread"] = {"value": T1 / e1, "unit": "tokens/s", "cores": 1,
+                            "sample": f"first {T1} of {cfg['N']} tokens as one batch; {e1:.1f} s"}
+    return out
 
 
 def main():
@@ -144,6 +236,7 @@ def main():
                           "n_gpus": args.gpus}))
         sys.exit(2)
 
+    clocks = read_clocks()
     import torch
 
     import expert_token_routing_router_amd as moe
@@ -245,6 +338,35 @@ def main():
     instrumented_ms = sum(events[s][0].elapsed_time(events[s][-1])
                           for s in range(args.steps)) / args.steps
 
+    # Step-time distribution: the same K steps with one event per step
+    # boundary only.
+    marks = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
+    torch.cuda.synchronize()
+    marks[0].record()
+    for s in range(args.steps):
+        step()
+        marks[s + 1].record()
+    torch.cuda.synchronize()
+    step_ms = sorted(marks[s].elapsed_time(marks[s + 1]) for s in range(args.steps))
+
+    def pct(v, q):
+        return v[min(len(v) - 1, int(q * (len(v) - 1) + 0.5))]
+
+    # Cold pass: before each step a 512 MiB write evicts the 256 MB Infinity
+    # Cache and every XCD's L2, then the step runs with per-call events.
+    n_cold = min(args.steps, 20)
+    flush = torch.empty(512 << 18, dtype=torch.float32, device=dev)
+    cold_ev = [[torch.cuda.Event(enable_timing=True) for _ in range(nev)] for _ in range(n_cold)]
+    torch.cuda.synchronize()
+    for s in range(n_cold):
+        flush.fill_(float(s))
+        step(cold_ev[s])
+    torch.cuda.synchronize()
+    cold_call = {c: sum(ev[i].elapsed_time(ev[i + 1]) for ev in cold_ev) / n_cold * 1e3
+                 for i, c in enumerate(calls)}
+    cold_step_ms = sum(ev[0].elapsed_time(ev[-1]) for ev in cold_ev) / n_cold
+    del flush
+
     if args.copy_calibration_mib > 0:
         # A plain elementwise copy kernel (reads and writes nbytes each), whose
         # counters scale the HBM byte counters of the kernels above.
@@ -270,10 +392,10 @@ def main():
     route_bytes = N * dim * es + E * dim * es + N * E * 4 + S * 8
     peak = MFMA_PEAK_TFLOPS[cfg["dtype"]]
 
-    def roof(name, flops, nbytes):
-        t = per_call[name] * 1e-6
+    def roof(name, flops, nbytes, table=per_call):
+        t = table[name] * 1e-6
         t_f, t_b = flops / (peak * 1e12), nbytes / (HBM_PEAK_GBS * 1e9)
-        return {"us": round(per_call[name], 2), "tflops": round(flops / t / 1e12, 2),
+        return {"us": round(table[name], 2), "tflops": round(flops / t / 1e12, 2),
                 "gbs": round(nbytes / t / 1e9, 1), "mfma_frac": round(flops / t / (peak * 1e12), 4),
                 "hbm_frac": round(nbytes / t / (HBM_PEAK_GBS * 1e9), 4),
                 "bound": "mfma" if t_f >= t_b else "hbm"}
@@ -289,6 +411,15 @@ def main():
                       "hbm_frac": round(nbytes / t / (HBM_PEAK_GBS * 1e9), 4)}
     for name in calls:
         kern.setdefault(name, {"us": round(per_call[name], 2)})
+    cold = {"ms_per_step_with_per_call_events": round(cold_step_ms, 4), "steps": n_cold,
+            "ffn_up": roof("ffn_up", up_flops, up_bytes, cold_call),
+            "ffn_down": roof("ffn_down", down_flops, down_bytes, cold_call)}
+    for name, nbytes in [("route", route_bytes), ("dispatch", dispatch_bytes),
+                         ("combine", combine_bytes)]:
+        cold[name] = {"us": round(cold_call[name], 2),
+                      "hbm_frac": round(nbytes / (cold_call[name] * 1e-6) / (HBM_PEAK_GBS * 1e9), 4)}
+    for name in calls:
+        cold.setdefault(name, {"us": round(cold_call[name], 2)})
 
     dom = "ffn_up" if per_call["ffn_up"] >= per_call["ffn_down"] else "ffn_down"
     dk = kern[dom]
@@ -325,9 +456,15 @@ def main():
         "permute_hbm_frac": kern["dispatch"]["hbm_frac"],
         "kernels": kern,
         "ms_per_step_with_per_call_events": round(instrumented_ms, 4),
+        "step_ms_p10_p50_p90": [round(pct(step_ms, q), 4) for q in (0.1, 0.5, 0.9)],
+        "cold": cold,
+        "platform": {"hip": torch.version.hip, "torch": torch.__version__,
+                     "device": torch.cuda.get_device_name(0), **clocks},
         "timed_region": {"gpu_events_ms": round(gpu_ms, 3), "host_wall_ms": round(wall * 1e3, 3)},
         "kernel_sources_digest": digest,
     }
+    if args.rank_share:
+        out["rank_share"] = rank_share(moe, torch, cfg, buf, wts, max(5, min(args.steps, 30)))
     if not args.no_cpu_baseline:
         host = {}
         for key, v in inp.items():
@@ -339,6 +476,7 @@ def main():
                 host[key] = v
         cb = cpu_baseline(cfg, host, args.cpu_seconds)
         cb["gpu_speedup"] = round(value / cb["value"], 1)
+        cb["single_thread"]["gpu_speedup"] = round(value / cb["single_thread"]["value"], 1)
         out["cpu_baseline"] = cb
     else:
         out["cpu_baseline"] = None
