@@ -138,6 +138,25 @@ __device__ __forceinline__ int xcd_logical(int b, int total) {
   return logical < total ? logical : -1;
 }
 
+// Logical tile -> (row tile, column tile).  gm == 1: row-major (the column
+// tiles of one row tile are consecutive).  gm > 1: groups of gm consecutive row
+// tiles walk their column tiles together, so the blocks an XCD runs at once
+// (32 consecutive logical tiles) cover gm row tiles x 32/gm column tiles and
+// share both the A rows and the weight slabs in that XCD's L2.  The last group
+// may hold fewer row tiles.
+__device__ __forceinline__ void tile_of(int logical, int n_tiles, int m_tiles, int gm, int& mt,
+                                        int& nt) {
+  if (gm <= 1) {
+    mt = logical / n_tiles;
+    nt = logical % n_tiles;
+    return;
+  }
+  const int g = logical / (gm * n_tiles), idx = logical % (gm * n_tiles);
+  const int rows = min(gm, m_tiles - g * gm);
+  mt = g * gm + idx % rows;
+  nt = idx / rows;
+}
+
 // ------------------------------------------------------------- bf16 MFMA ---
 
 // Rows per slab of packed weights (rows = N of the GEMM, a multiple of 64): a
@@ -191,7 +210,7 @@ __global__ __launch_bounds__(kGemmWaves * 64, 1) __attribute__((amdgpu_waves_per
 void grouped_gemm_bf16(
     const bf16_t* __restrict__ A, const bf16_t* __restrict__ B, const bf16_t* __restrict__ B2,
     bf16_t* __restrict__ C, int K, int N, const int4* __restrict__ tiles,
-    const int32_t* __restrict__ tile_count, int n_tiles, int ldg) {
+    const int32_t* __restrict__ tile_count, int n_tiles, int ldg, int gm) {
   constexpr bool DUAL = ACT == ACT_SWIGLU;
   constexpr int BM = kGemmBM, BK = 32, RB = BK * 2;  // RB: bytes per staged row
   constexpr int CH = BK / 8;                         // 16-byte chunks per row
@@ -225,9 +244,11 @@ void grouped_gemm_bf16(
   static_assert((NS - 1) * LMAX < 64, "loads in flight must fit the 6-bit vmcnt");
   __shared__ __attribute__((aligned(1024))) char smem[LDSB];
 
-  const int logical = xcd_logical(blockIdx.x, *tile_count * n_tiles);
+  const int m_tiles = *tile_count;
+  const int logical = xcd_logical(blockIdx.x, m_tiles * n_tiles);
   if (logical < 0) return;
-  const int mt = logical / n_tiles, nt = logical % n_tiles;
+  int mt, nt;
+  tile_of(logical, n_tiles, m_tiles, gm, mt, nt);
   const int4 tile = tiles[mt];
   const int e = tile.x, r0 = tile.y, r1 = tile.z, g0 = tile.w;
   const int n0 = nt * BN;
@@ -726,8 +747,12 @@ static void launch_bf16(const bf16_t* A, const bf16_t* B, const bf16_t* B2, bf16
                         int N, const FfnArgs& a, hipStream_t st) {
   const int nt = (N + BN - 1) / BN;
   const int g = grid_of(max_m_tiles(a.max_rows, kGemmBM, a.E), nt);
+  // Groups of 4 row tiles once experts average two or more row tiles: an XCD's
+  // 32 concurrent blocks then cover 4 x 8 tiles, and its L2 misses per K stage
+  // fall from 1 A tile + 32 weight slabs to 4 A tiles + 8 weight slabs.
+  const int gm = a.max_rows / a.E >= 2 * kGemmBM ? 4 : 1;
   grouped_gemm_bf16<BN, ACT, MODE><<<g, kGemmWaves * 64, 0, st>>>(
-      A, B, B2, C, K, N, ffn_tiles(a), ffn_count(a), nt, ffn_groups(a.E, a.max_rows));
+      A, B, B2, C, K, N, ffn_tiles(a), ffn_count(a), nt, ffn_groups(a.E, a.max_rows), gm);
 }
 
 template <int ACT>

@@ -5,7 +5,9 @@ Row tiles hold up to 320 rows in 32-row fragments, experts longer than that
 are split into equal tiles, and fragments without rows are skipped: the
 per-expert row counts below sit on every one of those edges (0, 1, 31/32/33,
 160/161, 319/320/321, 641), with output widths that are and are not a
-multiple of the column tile.  Reference: the oracle's grouped FFN on the same
+multiple of the column tile.  Experts of many row tiles take the grouped
+block order (4 row tiles walk their column tiles together), with a short last
+group.  Reference: the oracle's grouped FFN on the same
 rows (glossary "Expert Parallelism", step 3), per-tensor max relative error
 within 2e-2 (bf16) / 1e-4 (fp32).
 """
@@ -57,15 +59,15 @@ def test_pack_weights_is_the_documented_permutation(E, R, C):
     assert torch.equal(wd.cpu().view(torch.int16), w.view(torch.int16))  # source untouched
 
 
-def _inputs(d, h, act, dtype, seed):
+def _inputs(d, h, act, dtype, seed, counts=COUNTS):
     g = torch.Generator().manual_seed(seed)
-    E, M = len(COUNTS), sum(COUNTS)
+    E, M = len(counts), sum(counts)
     tdt = torch.bfloat16 if dtype == "bf16" else torch.float32
     x = torch.randn(M + 7, d, generator=g).to(tdt)
     w1 = (torch.randn(E, h, d, generator=g) / d ** 0.5).to(tdt)
     w3 = (torch.randn(E, h, d, generator=g) / d ** 0.5).to(tdt) if act == "swiglu" else None
     w2 = (torch.randn(E, d, h, generator=g) / h ** 0.5).to(tdt)
-    offs = torch.tensor(np.concatenate([[0], np.cumsum(COUNTS)]), dtype=torch.int32)
+    offs = torch.tensor(np.concatenate([[0], np.cumsum(counts)]), dtype=torch.int32)
     return x, w1, w3, w2, offs
 
 
@@ -77,9 +79,21 @@ def _inputs(d, h, act, dtype, seed):
     (128, 256, "gelu", "fp32"),
 ])
 def test_ffn_row_tile_edges(d, h, act, dtype):
-    print(f"[ffn tiles] d={d} h={h} act={act} dtype={dtype} counts={COUNTS}", flush=True)
-    x, w1, w3, w2, offs = _inputs(d, h, act, dtype, seed=d + h)
-    E, M = len(COUNTS), x.shape[0]
+    _check_ffn(d, h, act, dtype, COUNTS, seed=d + h)
+
+
+# Experts of several row tiles each (5, 0, 3 and 7 tiles: 15 in all): the bf16
+# GEMMs then walk groups of 4 row tiles column tile by column tile, and the
+# last group holds 3.  Several column tiles in both GEMMs.
+@pytest.mark.parametrize("act", ["gelu", "swiglu"])
+def test_ffn_grouped_row_tiles(act):
+    _check_ffn(512, 1024, act, "bf16", [1500, 0, 700, 2100], seed=77)
+
+
+def _check_ffn(d, h, act, dtype, counts, seed):
+    print(f"[ffn tiles] d={d} h={h} act={act} dtype={dtype} counts={counts}", flush=True)
+    x, w1, w3, w2, offs = _inputs(d, h, act, dtype, seed=seed, counts=counts)
+    E, M = len(counts), x.shape[0]
     cfg = {"dtype": dtype, "d": d, "h": h}
     wts = moe.prepare_weights(cfg, {"w1": w1.cuda(), "w3": None if w3 is None else w3.cuda(),
                                     "w2": w2.cuda()})
