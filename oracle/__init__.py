@@ -72,6 +72,7 @@ def lib():
             "oracle_logits": [D, P, P, P, P],
             "oracle_select": [D, P, P, P, P, P, P],
             "oracle_dispatch": [D, P, P, P, P, P, P, P, P],
+            "oracle_dispatch_ex": [D, I32, P, P, P, P, P, P, P, P],
             "oracle_permute": [I32, I32, I32, P, P, P],
             "oracle_ffn_row": [I32, I32, I32, I32, P, P, P, P, P],
             "oracle_expert_ffn": [I32, I32, I32, I32, I32, P, P, P, P, P, P],
@@ -163,7 +164,14 @@ def route(cfg: dict, x, w_router, router_bias=None, sel_bias=None) -> dict:
     return out
 
 
-def dispatch(cfg: dict, topk_idx) -> dict:
+ADMISSION = {"token": 0, "first_choice": 1}
+
+
+def dispatch(cfg: dict, topk_idx, admission: str | None = None) -> dict:
+    """Capacity, admission and layout.  admission: "token" (default; token
+    order) or "first_choice" (every token's first choice before any second
+    choice); defaults to cfg.get("admission", "token")."""
+    adm = ADMISSION[admission or cfg.get("admission", "token")]
     topk_idx = _c(topk_idx, np.int32)
     N, k, E, R = topk_idx.shape[0], cfg["k"], cfg["E"], cfg.get("R", 1)
     S = N * k
@@ -177,10 +185,10 @@ def dispatch(cfg: dict, topk_idx) -> dict:
         "rank_counts": np.empty(R, np.int32),
     }
     d = _desc(cfg, N)
-    _check(lib().oracle_dispatch(
-        ctypes.byref(d), _ptr(topk_idx), _ptr(out["row_of_slot"]), _ptr(out["token_of_row"]),
+    _check(lib().oracle_dispatch_ex(
+        ctypes.byref(d), adm, _ptr(topk_idx), _ptr(out["row_of_slot"]), _ptr(out["token_of_row"]),
         _ptr(out["slot_of_row"]), _ptr(out["expert_offsets"]), _ptr(out["admitted"]),
-        _ptr(out["rank_offsets"]), _ptr(out["rank_counts"])), "oracle_dispatch")
+        _ptr(out["rank_offsets"]), _ptr(out["rank_counts"])), "oracle_dispatch_ex")
     out["num_rows"] = int(out["expert_offsets"][E])
     return out
 

@@ -9,7 +9,8 @@
  *    added last in fp64, one rounding to fp32;
  *  - ties in any ranking go to the lower expert (or group) index;
  *  - capacity = ceil(cf * N * k / E) (the mean load times the factor), and
- *    slots are admitted in token order;
+ *    slots are admitted in token order (or, on request, first choices of all
+ *    tokens before any second choice: the top-2 router of GShard);
  *  - a dropped slot contributes nothing and the remaining weights are not
  *    renormalised; the layer output includes the residual;
  *  - the group score is the maximum biased selection score in the group;
@@ -271,7 +272,16 @@ int oracle_dispatch(const oracle_desc* desc, const int32_t* topk_idx,
                     int32_t* row_of_slot, int32_t* token_of_row, int8_t* slot_of_row,
                     int32_t* expert_offsets, int32_t* admitted,
                     int32_t* rank_offsets, int32_t* rank_counts) {
+  return oracle_dispatch_ex(desc, 0, topk_idx, row_of_slot, token_of_row, slot_of_row,
+                            expert_offsets, admitted, rank_offsets, rank_counts);
+}
+
+int oracle_dispatch_ex(const oracle_desc* desc, int32_t admission, const int32_t* topk_idx,
+                       int32_t* row_of_slot, int32_t* token_of_row, int8_t* slot_of_row,
+                       int32_t* expert_offsets, int32_t* admitted,
+                       int32_t* rank_offsets, int32_t* rank_counts) {
   if (!desc_ok(desc) || !expert_offsets || !admitted || !rank_offsets || !rank_counts) return -1;
+  if (admission != 0 && admission != 1) return -1;
   const int32_t N = desc->num_tokens, E = desc->num_experts, k = desc->top_k;
   const int32_t R = desc->num_ranks;
   const size_t S = (size_t)N * k;
@@ -291,16 +301,33 @@ int oracle_dispatch(const oracle_desc* desc, const int32_t* topk_idx,
   }
   for (size_t i = 0; i < S; ++i) counts[topk_idx[i]] += 1;
 
-  /* Admission in token order (t outer, slot inner). */
-  for (int32_t t = 0; t < N; ++t) {
+  if (admission == 0) {
+    /* Admission in token order (t outer, slot inner). */
+    for (int32_t t = 0; t < N; ++t) {
+      for (int32_t j = 0; j < k; ++j) {
+        const size_t slot = (size_t)t * k + j;
+        const int32_t e = topk_idx[slot];
+        if (seen[e] < cap) {
+          rank_in_expert[slot] = seen[e];
+          seen[e] += 1;
+        } else {
+          rank_in_expert[slot] = -1; /* dropped */
+        }
+      }
+    }
+  } else {
+    /* First choice first: every token's slot 0 (in token order), then every
+     * token's slot 1, and so on (slot outer, token inner). */
     for (int32_t j = 0; j < k; ++j) {
-      const size_t slot = (size_t)t * k + j;
-      const int32_t e = topk_idx[slot];
-      if (seen[e] < cap) {
-        rank_in_expert[slot] = seen[e];
-        seen[e] += 1;
-      } else {
-        rank_in_expert[slot] = -1; /* dropped */
+      for (int32_t t = 0; t < N; ++t) {
+        const size_t slot = (size_t)t * k + j;
+        const int32_t e = topk_idx[slot];
+        if (seen[e] < cap) {
+          rank_in_expert[slot] = seen[e];
+          seen[e] += 1;
+        } else {
+          rank_in_expert[slot] = -1; /* dropped */
+        }
       }
     }
   }

@@ -70,6 +70,18 @@ int oracle_dispatch(const oracle_desc* desc, const int32_t* topk_idx,
                     int32_t* expert_offsets, int32_t* admitted,
                     int32_t* rank_offsets, int32_t* rank_counts);
 
+/* The same with a choice of admission order.  admission 0: token order (as
+ * oracle_dispatch).  admission 1: first choice first -- slot j = 0 of every
+ * token in token order, then j = 1 of every token, and so on; rows inside an
+ * expert follow that order.  MLSys ch.10, section 10.5 names GShard's top-2
+ * router; the pages fix no admission priority, and this is the plainest
+ * reading of a router that ranks first choices above second ones.
+ * Returns -1 for any other admission value. */
+int oracle_dispatch_ex(const oracle_desc* desc, int32_t admission, const int32_t* topk_idx,
+                       int32_t* row_of_slot, int32_t* token_of_row, int8_t* slot_of_row,
+                       int32_t* expert_offsets, int32_t* admitted,
+                       int32_t* rank_offsets, int32_t* rank_counts);
+
 /* x_perm[i] = x[token_of_row[i]] for i < num_rows (a byte copy). */
 int oracle_permute(int32_t num_rows, int32_t hidden, int32_t dtype, const void* x,
                    const int32_t* token_of_row, void* x_perm);

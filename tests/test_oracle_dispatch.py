@@ -1,5 +1,6 @@
-"""Pins of the oracle's dispatch step (capacity, token-order admission,
-expert/rank-contiguous layout, permute) and the selection-bias update.  CPU only.
+"""Pins of the oracle's dispatch step (capacity, token-order and first-choice-
+first admission, expert/rank-contiguous layout, permute) and the selection-bias
+update.  CPU only.
 """
 
 import numpy as np
@@ -26,7 +27,7 @@ def _random_topk(rng, N, E, k, skew=0.0):
     return out
 
 
-def _check_invariants(cfg, idx, dsp):
+def _check_invariants(cfg, idx, dsp, admission="token"):
     N, k, E, R = idx.shape[0], cfg["k"], cfg["E"], cfg["R"]
     cap = oracle.capacity(cfg)
     counts = np.bincount(idx.ravel(), minlength=E)
@@ -44,12 +45,15 @@ def _check_invariants(cfg, idx, dsp):
     assert np.array_equal(np.sort(rows), np.arange(M))
     assert np.array_equal(dsp["token_of_row"][rows], t_idx)
     assert np.array_equal(dsp["slot_of_row"][rows], j_idx)
-    # Each row sits in its expert's segment; tokens increase inside a segment.
+    # Each row sits in its expert's segment; inside a segment tokens increase
+    # (token order) or (slot, token) pairs increase (first choice first).
     e_of_row = np.repeat(np.arange(E), adm)
     assert np.array_equal(idx[t_idx, j_idx], e_of_row[rows])
-    tor = dsp["token_of_row"][:M]
+    tor = dsp["token_of_row"][:M].astype(np.int64)
+    sor = dsp["slot_of_row"][:M].astype(np.int64)
+    key = tor if admission == "token" else sor * (N + 1) + tor
     for e in range(E):
-        seg = tor[off[e]:off[e + 1]]
+        seg = key[off[e]:off[e + 1]]
         assert np.all(np.diff(seg) > 0)
     # Ranks: blocks of E/R experts, counts are sums over the block.
     per = E // R
@@ -160,6 +164,108 @@ def test_dispatch_invariants_property(N, E_pow, k, R_pow, cf, skew, seed):
     cfg = _cfg(N=N, E=E, k=k, R=R, cf=cf)
     dsp = oracle.dispatch(cfg, idx)
     _check_invariants(cfg, idx, dsp)
+
+
+# ---- first choice first (GShard's top-2 router; admission = "first_choice") --
+
+
+def test_first_choice_equals_token_order_for_top1():
+    """With one slot per token both admission orders are the same walk."""
+    rng = np.random.default_rng(30)
+    for N, E, cf in [(500, 8, 1.0), (777, 64, 1.25), (64, 4, 0.25)]:
+        idx = _random_topk(rng, N, E, 1, skew=1.5)
+        cfg = _cfg(N=N, E=E, k=1, cf=cf, R=2)
+        a, b = oracle.dispatch(cfg, idx, "token"), oracle.dispatch(cfg, idx, "first_choice")
+        for key in a:
+            assert np.array_equal(np.asarray(a[key]), np.asarray(b[key])), key
+
+
+def _lexsort_rows(idx):
+    """(t, j) of every slot, sorted by (expert, slot, token) with numpy.lexsort."""
+    N, k = idx.shape
+    t = np.repeat(np.arange(N), k)
+    j = np.tile(np.arange(k), N)
+    e = idx.ravel()
+    order = np.lexsort((t, j, e))
+    return e[order], t[order], j[order]
+
+
+def test_first_choice_no_capacity_is_lexsort():
+    """Without a capacity limit the rows are every slot sorted by (expert,
+    slot, token): numpy.lexsort."""
+    rng = np.random.default_rng(31)
+    for N, E, k in [(1000, 8, 2), (300, 256, 8), (129, 16, 3)]:
+        idx = _random_topk(rng, N, E, k, skew=1.1)
+        cfg = _cfg(N=N, E=E, k=k, R=E // 4)
+        dsp = oracle.dispatch(cfg, idx, "first_choice")
+        _, t, j = _lexsort_rows(idx)
+        assert np.array_equal(dsp["token_of_row"], t)
+        assert np.array_equal(dsp["slot_of_row"], j.astype(np.int8))
+        _check_invariants(cfg, idx, dsp, "first_choice")
+
+
+def test_first_choice_capacity_is_lexsort_prefix():
+    """With a capacity, each expert keeps the first cap entries of its
+    (slot, token)-sorted list (numpy.lexsort, then a per-expert prefix)."""
+    rng = np.random.default_rng(32)
+    for trial in range(40):
+        E = int(rng.choice([2, 4, 8, 16]))
+        k = int(rng.integers(1, min(4, E) + 1))
+        N = int(rng.integers(1, 300))
+        cf = float(rng.choice([0.25, 0.5, 1.0, 1.25, 2.0]))
+        idx = _random_topk(rng, N, E, k, skew=float(rng.choice([0.0, 1.5, 3.0])))
+        cfg = _cfg(N=N, E=E, k=k, cf=cf)
+        cap = oracle.capacity(cfg)
+        dsp = oracle.dispatch(cfg, idx, "first_choice")
+        e, t, j = _lexsort_rows(idx)
+        first = np.searchsorted(e, np.arange(E))  # start of each expert's run
+        keep = np.arange(e.size) - first[e] < cap
+        M = dsp["num_rows"]
+        assert M == int(keep.sum())
+        assert np.array_equal(dsp["token_of_row"][:M], t[keep])
+        assert np.array_equal(dsp["slot_of_row"][:M], j[keep].astype(np.int8))
+        _check_invariants(cfg, idx, dsp, "first_choice")
+
+
+def test_first_choice_priority_over_token_order():
+    """No expert admits a later choice while turning away an earlier one, and
+    no admission order admits more first choices."""
+    rng = np.random.default_rng(33)
+    for trial in range(30):
+        E, k = 8, int(rng.integers(2, 5))
+        N = int(rng.integers(50, 400))
+        idx = _random_topk(rng, N, E, k, skew=2.0)
+        cfg = _cfg(N=N, E=E, k=k, cf=float(rng.choice([0.5, 1.0])))
+        fc = oracle.dispatch(cfg, idx, "first_choice")["row_of_slot"]
+        to = oracle.dispatch(cfg, idx, "token")["row_of_slot"]
+        for ex in range(E):
+            for j in range(1, k):
+                if np.any(fc[:, j][idx[:, j] == ex] >= 0):
+                    for jj in range(j):
+                        assert np.all(fc[:, jj][idx[:, jj] == ex] >= 0)
+        assert (fc[:, 0] >= 0).sum() >= (to[:, 0] >= 0).sum()
+        # the same number of rows either way: min(count, cap) per expert
+        assert (fc >= 0).sum() == (to >= 0).sum()
+
+
+def test_unknown_admission_rejected():
+    with pytest.raises(KeyError):
+        oracle.dispatch(_cfg(N=1, E=4, k=1), np.array([[0]], np.int32), "slot")
+
+
+@settings(max_examples=40, deadline=None)
+@given(N=st.integers(0, 300), E_pow=st.integers(0, 8), k=st.integers(1, 8),
+       R_pow=st.integers(0, 6), cf=st.sampled_from([0.0, 0.5, 1.0, 1.25, 2.0]),
+       skew=st.sampled_from([0.0, 1.1, 3.0]), seed=st.integers(0, 2 ** 31 - 1))
+def test_first_choice_invariants_property(N, E_pow, k, R_pow, cf, skew, seed):
+    E = 2 ** E_pow
+    k = min(k, E)
+    R = 2 ** min(R_pow, E_pow)
+    rng = np.random.default_rng(seed)
+    idx = _random_topk(rng, N, E, k, skew)
+    cfg = _cfg(N=N, E=E, k=k, R=R, cf=cf)
+    dsp = oracle.dispatch(cfg, idx, "first_choice")
+    _check_invariants(cfg, idx, dsp, "first_choice")
 
 
 def test_permute_is_bitwise_row_copy():
