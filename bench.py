@@ -44,6 +44,9 @@ def parse_args():
     ap.add_argument("--workload", default="switch",
                     choices=["toy", "switch", "mixtral", "deepseek", "zipf"])
     ap.add_argument("--cf", type=float, default=None, help="override the capacity factor")
+    ap.add_argument("--admission", default="token", choices=["token", "first_choice"],
+                    help="capacity admission order: token order, or every token's first "
+                         "choice before any second choice")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0,
                     help="target length of the oracle's timed sample")
@@ -168,6 +171,8 @@ def describe(cfg) -> str:
         s += f" groups={cfg['G']}/keep{cfg['kg']}"
     if cfg.get("shared"):
         s += " +shared"
+    if cfg.get("admission", "token") != "token":
+        s += f" admission={cfg['admission']}"
     return s
 
 
@@ -247,6 +252,8 @@ def main():
     cfg = W.full(args.workload)
     if args.cf is not None:
         cfg["cf"] = args.cf
+    if args.admission != "token":
+        cfg["admission"] = args.admission
     # Inputs: the glossary snippet's stream for the toy workload (CPU), else
     # drawn on the device.
     gen_dev = "cpu" if args.workload == "toy" else "cuda"

@@ -27,16 +27,18 @@ MOE_OK, MOE_ERR_INVALID_ARG, MOE_ERR_UNSUPPORTED, MOE_ERR_HIP, MOE_ERR_WORKSPACE
 MOE_F32, MOE_BF16 = 0, 1
 MOE_SOFTMAX_TOPK, MOE_SOFTMAX_ALL, MOE_SIGMOID_NORM = 0, 1, 2
 MOE_RELU, MOE_GELU, MOE_SWIGLU = 0, 1, 2
+MOE_ADMIT_TOKEN_ORDER, MOE_ADMIT_FIRST_CHOICE = 0, 1
 
 SCORE = {"softmax_topk": MOE_SOFTMAX_TOPK, "softmax_all": MOE_SOFTMAX_ALL,
          "sigmoid_norm": MOE_SIGMOID_NORM}
 ACT = {"relu": MOE_RELU, "gelu": MOE_GELU, "swiglu": MOE_SWIGLU}
 DTYPE = {"fp32": MOE_F32, "bf16": MOE_BF16}
+ADMISSION = {"token": MOE_ADMIT_TOKEN_ORDER, "first_choice": MOE_ADMIT_FIRST_CHOICE}
 TORCH_DTYPE = {MOE_F32: torch.float32, MOE_BF16: torch.bfloat16}
 
 EXPORTS = [
     "moe_route_workspace_size", "moe_route", "moe_router_logits",
-    "moe_dispatch_workspace_size", "moe_dispatch",
+    "moe_dispatch_workspace_size", "moe_dispatch", "moe_dispatch_ex",
     "moe_expert_ffn_workspace_size", "moe_expert_ffn", "moe_expert_ffn_plan",
     "moe_expert_ffn_up", "moe_expert_ffn_down", "moe_expert_ffn_pack_weights", "moe_combine",
     "moe_bias_update", "moe_status_string",
@@ -97,6 +99,7 @@ def lib() -> ctypes.CDLL:
             "moe_router_logits": ([D, P, P, P, P, P, SZ, P], I32),
             "moe_dispatch_workspace_size": ([D], SZ),
             "moe_dispatch": ([D, P, P, P, P, P, P, P, P, P, P, P, SZ, P], I32),
+            "moe_dispatch_ex": ([D, I32, P, P, P, P, P, P, P, P, P, P, P, SZ, P], I32),
             "moe_expert_ffn_workspace_size": ([I32, I32, I32, I32, I32, I32], SZ),
             "moe_expert_ffn": ([I32, I32, I32, I32, I32, I32, P, P, P, P, P, P, P, SZ, P], I32),
             "moe_expert_ffn_plan": ([I32, I32, I32, I32, I32, I32, P, P, SZ, P], I32),
@@ -203,11 +206,29 @@ def moe_router_logits(desc, x, w_router, router_bias, logits, ws, stream=None):
 
 def moe_dispatch(desc, x, topk_idx, x_perm, row_of_slot, token_of_row, slot_of_row,
                  expert_offsets, admitted, rank_offsets, rank_counts, ws, stream=None):
+    _dispatch("moe_dispatch", desc, None, x, topk_idx, x_perm, row_of_slot, token_of_row,
+              slot_of_row, expert_offsets, admitted, rank_offsets, rank_counts, ws, stream)
+
+
+def moe_dispatch_ex(desc, admission, x, topk_idx, x_perm, row_of_slot, token_of_row,
+                    slot_of_row, expert_offsets, admitted, rank_offsets, rank_counts, ws,
+                    stream=None):
+    """admission: "token" / MOE_ADMIT_TOKEN_ORDER or "first_choice" /
+    MOE_ADMIT_FIRST_CHOICE."""
+    adm = ADMISSION[admission] if isinstance(admission, str) else int(admission)
+    _dispatch("moe_dispatch_ex", desc, adm, x, topk_idx, x_perm, row_of_slot, token_of_row,
+              slot_of_row, expert_offsets, admitted, rank_offsets, rank_counts, ws, stream)
+
+
+def _dispatch(name, desc, admission, x, topk_idx, x_perm, row_of_slot, token_of_row,
+              slot_of_row, expert_offsets, admitted, rank_offsets, rank_counts, ws, stream):
     N, d, E, k, R = desc.num_tokens, desc.hidden, desc.num_experts, desc.top_k, desc.num_ranks
     dt = TORCH_DTYPE.get(desc.dtype)
     S = N * k
-    st = lib().moe_dispatch(
-        ctypes.byref(desc), _ptr(x, "x", dt, N * d, N > 0),
+    fn = getattr(lib(), name)
+    head = (ctypes.byref(desc),) if admission is None else (ctypes.byref(desc), admission)
+    st = fn(
+        *head, _ptr(x, "x", dt, N * d, N > 0),
         _ptr(topk_idx, "topk_idx", torch.int32, S, N > 0),
         _ptr(x_perm, "x_perm", dt, S * d, N > 0),
         _ptr(row_of_slot, "row_of_slot", torch.int32, S, N > 0),
@@ -219,7 +240,7 @@ def moe_dispatch(desc, x, topk_idx, x_perm, row_of_slot, token_of_row, slot_of_r
         _ptr(rank_counts, "rank_counts", torch.int32, R),
         _ptr(ws, "ws", None, None, False), 0 if ws is None else ws.numel() * ws.element_size(),
         _stream(stream))
-    _raise("moe_dispatch", st)
+    _raise(name, st)
 
 
 def moe_expert_ffn(num_experts, max_rows, hidden, ffn_hidden, act, dtype, x_rows,

@@ -113,8 +113,20 @@ int moe_dispatch(const moe_route_desc* desc, const void* x, const int32_t* topk_
                  int8_t* slot_of_row, int32_t* expert_offsets, int32_t* admitted,
                  int32_t* rank_offsets, int32_t* rank_counts, void* ws, size_t ws_bytes,
                  void* stream) {
+  return moe_dispatch_ex(desc, MOE_ADMIT_TOKEN_ORDER, x, topk_idx, x_perm, row_of_slot,
+                         token_of_row, slot_of_row, expert_offsets, admitted, rank_offsets,
+                         rank_counts, ws, ws_bytes, stream);
+}
+
+int moe_dispatch_ex(const moe_route_desc* desc, int32_t admission, const void* x,
+                    const int32_t* topk_idx, void* x_perm, int32_t* row_of_slot,
+                    int32_t* token_of_row, int8_t* slot_of_row, int32_t* expert_offsets,
+                    int32_t* admitted, int32_t* rank_offsets, int32_t* rank_counts, void* ws,
+                    size_t ws_bytes, void* stream) {
   int st = check_desc(desc);
   if (st != MOE_OK) return st;
+  if (admission != MOE_ADMIT_TOKEN_ORDER && admission != MOE_ADMIT_FIRST_CHOICE)
+    return MOE_ERR_INVALID_ARG;
   if (!expert_offsets || !admitted || !rank_offsets || !rank_counts) return MOE_ERR_INVALID_ARG;
   const int N = desc->num_tokens;
   if (N > 0) {
@@ -127,7 +139,7 @@ int moe_dispatch(const moe_route_desc* desc, const void* x, const int32_t* topk_
   moe::DispatchArgs a{N, desc->hidden, desc->num_experts, desc->top_k, desc->num_ranks,
                       desc->dtype, capacity_of(desc), x, topk_idx, x_perm, row_of_slot,
                       token_of_row, slot_of_row, expert_offsets, admitted, rank_offsets,
-                      rank_counts, ws};
+                      rank_counts, ws, admission == MOE_ADMIT_FIRST_CHOICE ? 1 : 0};
   return status_of(moe::launch_dispatch(a, static_cast<hipStream_t>(stream)));
 }
 

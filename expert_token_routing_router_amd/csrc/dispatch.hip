@@ -1,5 +1,5 @@
-// dispatch.hip -- capacity, token-order admission and the expert/rank-
-// contiguous send-buffer layout, for gfx950.
+// dispatch.hip -- capacity, admission (token order, or first choice first)
+// and the expert/rank-contiguous send-buffer layout, for gfx950.
 //
 // Glossary "Expert Parallelism": step 2 of "How tokens travel between GPUs"
 // (each token's hidden state goes to the rank holding its experts; experts sit
@@ -7,9 +7,11 @@
 // bullet of "Load balancing and capacity" (an expert takes at most cap
 // assignments per batch, the rest skip it).  Admission is in token order, so
 // the rank of slot (t, j) inside expert e is the number of earlier slots (in
-// t-major, j-minor order) that chose e -- a stable counting sort.
+// t-major, j-minor order) that chose e -- a stable counting sort.  On request
+// the walk is first choice first (MLSys ch.10, section 10.5: GShard's top-2
+// router): j-major, t-minor, the same counting sort over that order.
 //
-// Kernels (slots are the N*k flattened (t, j) pairs, in tiles of 1024):
+// Kernels (over the N*k positions of the admission walk, in tiles of 1024):
 //  count       one block: per-tile, per-expert histogram in LDS and the scan
 //              below, when tiles * E fits in LDS (else tile_hist + scan).
 //  tile_hist   per-tile, per-expert histogram (LDS atomics).
@@ -30,16 +32,29 @@ namespace moe {
 
 constexpr int kTileSlots = 1024;  // 4 waves x 4 chunks x 64 slots
 
+// The admission walk: position q of the walk visits slot walk_slot(q).  Token
+// order visits slots in storage order (t-major, j-minor); first choice first
+// visits slot j of every token, in token order, before slot j + 1 of any
+// (q = j N + t).  Tiles, histograms and ranks are all taken over q, so a
+// slot's rank inside its expert is the number of earlier positions of the
+// walk that chose the same expert, whichever walk it is.
+__device__ __forceinline__ int walk_slot(int q, int N, int k, int first_choice) {
+  if (!first_choice) return q;
+  const int j = q / N;
+  return (q - j * N) * k + j;
+}
+
 __global__ __launch_bounds__(256) void dispatch_tile_hist(const int32_t* __restrict__ topk_idx,
-                                                          int S, int E,
+                                                          int S, int k, int E, int first_choice,
                                                           int32_t* __restrict__ tile_counts) {
   __shared__ int32_t hist[256];
   for (int e = threadIdx.x; e < E; e += 256) hist[e] = 0;
   __syncthreads();
   const int s0 = blockIdx.x * kTileSlots;
   const int s1 = min(S, s0 + kTileSlots);
-  for (int s = s0 + threadIdx.x; s < s1; s += 256) {
-    const int e = topk_idx[s];
+  const int N = S / k;
+  for (int q = s0 + threadIdx.x; q < s1; q += 256) {
+    const int e = topk_idx[walk_slot(q, N, k, first_choice)];
     if ((unsigned)e < (unsigned)E) atomicAdd(&hist[e], 1);  // ids out of range are ignored
   }
   __syncthreads();
@@ -100,7 +115,8 @@ __global__ __launch_bounds__(256) void dispatch_scan(int32_t* __restrict__ tile_
 constexpr int kCountLds = 16384;  // ints
 
 __global__ __launch_bounds__(1024) void dispatch_count(const int32_t* __restrict__ topk_idx,
-                                                       int S, int num_tiles, int E, int R,
+                                                       int S, int k, int first_choice,
+                                                       int num_tiles, int E, int R,
                                                        int32_t cap,
                                                        int32_t* __restrict__ tile_base,
                                                        int32_t* __restrict__ expert_offsets,
@@ -115,13 +131,14 @@ __global__ __launch_bounds__(1024) void dispatch_count(const int32_t* __restrict
   for (int q = tid; q < cells; q += 1024) h[q] = 0;
   __syncthreads();
   // Eight loads in flight per thread before their atomics (a block-strided
-  // loop would wait for each load in turn).
+  // loop would wait for each load in turn).  s is the position in the walk.
+  const int N = S / k;
   for (int s0 = 0; s0 < S; s0 += 8 * 1024) {
     int ids[8];
 #pragma unroll
     for (int u = 0; u < 8; ++u) {
       const int s = s0 + u * 1024 + tid;
-      ids[u] = s < S ? topk_idx[s] : -1;
+      ids[u] = s < S ? topk_idx[walk_slot(s, N, k, first_choice)] : -1;
     }
 #pragma unroll
     for (int u = 0; u < 8; ++u) {
@@ -173,7 +190,7 @@ __device__ __forceinline__ uint64_t lanemask_lt(int lane) {
 }
 
 __global__ __launch_bounds__(256) void dispatch_assign(
-    const int32_t* __restrict__ topk_idx, int S, int k, int E, int32_t cap,
+    const int32_t* __restrict__ topk_idx, int S, int k, int first_choice, int E, int32_t cap,
     const int32_t* __restrict__ tile_base, const int32_t* __restrict__ expert_offsets,
     int32_t* __restrict__ row_of_slot, int32_t* __restrict__ token_of_row,
     int8_t* __restrict__ slot_of_row) {
@@ -190,12 +207,13 @@ __global__ __launch_bounds__(256) void dispatch_assign(
   for (int e = threadIdx.x; e <= E; e += 256) eoff[e] = expert_offsets[e];
   __syncthreads();
 
-  const int ws0 = s0 + wave * 256;  // this wave's 256 slots
+  const int ws0 = s0 + wave * 256;  // this wave's 256 positions of the walk
+  const int N = S / k;
   int my_e[4];
 #pragma unroll
   for (int c = 0; c < 4; ++c) {
-    const int s = ws0 + c * 64 + lane;
-    int e = s < S ? topk_idx[s] : E;  // E = "no slot"
+    const int q = ws0 + c * 64 + lane;
+    int e = q < S ? topk_idx[walk_slot(q, N, k, first_choice)] : E;  // E = "no slot"
     if ((unsigned)e >= (unsigned)E) e = E;  // an out-of-range id is treated as dropped
     my_e[c] = e;
     if (e < E) atomicAdd(&wcount[wave][e], 1);
@@ -219,7 +237,8 @@ __global__ __launch_bounds__(256) void dispatch_assign(
   const int32_t M = eoff[E];
 #pragma unroll
   for (int c = 0; c < 4; ++c) {
-    const int s = ws0 + c * 64 + lane;
+    const int q = ws0 + c * 64 + lane;
+    const int s = q < S ? walk_slot(q, N, k, first_choice) : q;  // the slot itself
     const int e = my_e[c];
     uint64_t same = ~0ull;
     for (int b = 0; b < nbits; ++b) {
@@ -244,7 +263,7 @@ __global__ __launch_bounds__(256) void dispatch_assign(
       } else {
         row_of_slot[s] = -1;
       }
-    } else if (s < S) {
+    } else if (q < S) {
       row_of_slot[s] = -1;
     }
   }
@@ -304,16 +323,20 @@ hipError_t launch_dispatch(const DispatchArgs& a, hipStream_t st) {
   const int tiles = (S + kTileSlots - 1) / kTileSlots;
   int32_t* tile_counts = static_cast<int32_t*>(a.ws);
   if (tiles > 0 && (long long)tiles * a.E <= kCountLds && a.E <= 1024) {
-    dispatch_count<<<1, 1024, 0, st>>>(a.topk_idx, S, tiles, a.E, a.R, a.cap, tile_counts,
+    dispatch_count<<<1, 1024, 0, st>>>(a.topk_idx, S, a.k, a.first_choice, tiles, a.E, a.R,
+                                       a.cap, tile_counts,
                                        a.expert_offsets, a.admitted, a.rank_offsets,
                                        a.rank_counts);
   } else {
-    if (tiles > 0) dispatch_tile_hist<<<tiles, 256, 0, st>>>(a.topk_idx, S, a.E, tile_counts);
+    if (tiles > 0)
+      dispatch_tile_hist<<<tiles, 256, 0, st>>>(a.topk_idx, S, a.k, a.E, a.first_choice,
+                                                tile_counts);
     dispatch_scan<<<1, 256, 0, st>>>(tile_counts, tiles, a.E, a.R, a.cap, a.expert_offsets,
                                      a.admitted, a.rank_offsets, a.rank_counts);
   }
   if (tiles == 0) return hipGetLastError();
-  dispatch_assign<<<tiles, 256, 0, st>>>(a.topk_idx, S, a.k, a.E, a.cap, tile_counts,
+  dispatch_assign<<<tiles, 256, 0, st>>>(a.topk_idx, S, a.k, a.first_choice, a.E, a.cap,
+                                         tile_counts,
                                          a.expert_offsets, a.row_of_slot, a.token_of_row,
                                          a.slot_of_row);
   const int elem = a.dtype == 0 ? 4 : 2;

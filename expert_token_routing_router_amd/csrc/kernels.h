@@ -47,6 +47,7 @@ struct DispatchArgs {
   int32_t* rank_offsets;
   int32_t* rank_counts;
   void* ws;
+  int first_choice;  // 0: token order; 1: every token's slot j before any slot j + 1
 };
 
 size_t dispatch_workspace_bytes(int N, int k, int E);

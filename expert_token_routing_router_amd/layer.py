@@ -12,7 +12,7 @@ from __future__ import annotations
 import torch
 
 from . import (ACT, DTYPE, TORCH_DTYPE, desc_from_workload, moe_bias_update, moe_combine,
-               moe_dispatch, moe_dispatch_workspace_size, moe_expert_ffn,
+               moe_dispatch, moe_dispatch_ex, moe_dispatch_workspace_size, moe_expert_ffn,
                moe_expert_ffn_pack_weights, moe_expert_ffn_workspace_size, moe_route,
                moe_route_workspace_size, workspace)
 
@@ -88,9 +88,17 @@ def route(buf: MoeBuffers, inp: dict, sel_bias=None, stream=None):
 
 
 def dispatch(buf: MoeBuffers, inp: dict, stream=None):
-    moe_dispatch(buf.desc, inp["x"], buf.topk_idx, buf.x_perm, buf.row_of_slot,
-                 buf.token_of_row, buf.slot_of_row, buf.expert_offsets, buf.admitted,
-                 buf.rank_offsets, buf.rank_counts, buf.ws_dispatch, stream)
+    """Admission in token order unless the workload sets ``admission`` to
+    ``"first_choice"``."""
+    adm = buf.cfg.get("admission", "token")
+    if adm == "token":
+        moe_dispatch(buf.desc, inp["x"], buf.topk_idx, buf.x_perm, buf.row_of_slot,
+                     buf.token_of_row, buf.slot_of_row, buf.expert_offsets, buf.admitted,
+                     buf.rank_offsets, buf.rank_counts, buf.ws_dispatch, stream)
+    else:
+        moe_dispatch_ex(buf.desc, adm, inp["x"], buf.topk_idx, buf.x_perm, buf.row_of_slot,
+                        buf.token_of_row, buf.slot_of_row, buf.expert_offsets, buf.admitted,
+                        buf.rank_offsets, buf.rank_counts, buf.ws_dispatch, stream)
 
 
 def expert_ffn(buf: MoeBuffers, inp: dict, stream=None):

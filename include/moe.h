@@ -10,6 +10,7 @@
  *                    selection-only bias), combine weights, per-expert counts
  *   moe_dispatch     capacity, token-order admission, expert- and
  *                    rank-contiguous row layout, permuted hidden states
+ *                    (moe_dispatch_ex: also first-choice-first admission)
  *   moe_expert_ffn   every expert's FFN over its rows as one grouped GEMM pair
  *                    (bf16 weights packed once by moe_expert_ffn_pack_weights)
  *   moe_combine      weighted sum back to token order, plus residual and an
@@ -173,6 +174,31 @@ int moe_dispatch(const moe_route_desc* desc, const void* x, const int32_t* topk_
                  int8_t* slot_of_row, int32_t* expert_offsets, int32_t* admitted,
                  int32_t* rank_offsets, int32_t* rank_counts,
                  void* ws, size_t ws_bytes, void* stream);
+
+/* Admission orders of moe_dispatch_ex. */
+typedef enum {
+  MOE_ADMIT_TOKEN_ORDER = 0,  /* tokens in order, a token's slots j = 0..k-1 in turn */
+  MOE_ADMIT_FIRST_CHOICE = 1  /* slot 0 of every token (in token order), then slot 1
+                                 of every token, and so on */
+} moe_admission;
+
+/* Dispatch with a choice of admission order.  MLSys ch.10, section 10.5 names
+ * GShard's top-2 router, whose first choices outrank second choices when an
+ * expert fills up; the pages fix no admission priority, and
+ * MOE_ADMIT_FIRST_CHOICE is the plainest reading of such a router: the
+ * capacity is filled by walking every token's first choice (token order),
+ * then every second choice, and so on.  Rows inside an expert follow the same
+ * walk: by (slot, token) for MOE_ADMIT_FIRST_CHOICE, so token_of_row is not
+ * monotonic inside an expert there.  Everything else -- arguments, layout,
+ * admitted = min(count_e, cap), rank offsets, workspace size, errors -- is as
+ * for moe_dispatch, which is moe_dispatch_ex with MOE_ADMIT_TOKEN_ORDER.  With
+ * k = 1, or with no capacity limit, both orders admit the same slots.
+ * Returns MOE_ERR_INVALID_ARG for any other admission value. */
+int moe_dispatch_ex(const moe_route_desc* desc, int32_t admission, const void* x,
+                    const int32_t* topk_idx, void* x_perm, int32_t* row_of_slot,
+                    int32_t* token_of_row, int8_t* slot_of_row, int32_t* expert_offsets,
+                    int32_t* admitted, int32_t* rank_offsets, int32_t* rank_counts,
+                    void* ws, size_t ws_bytes, void* stream);
 
 /* ------------------------------------------------------------- expert FFN -- */
 

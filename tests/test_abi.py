@@ -115,6 +115,24 @@ def test_dispatch_validation():
     assert lib.moe_dispatch(ctypes.byref(bad), *args, FAKE, need, None) == moe.MOE_ERR_INVALID_ARG
 
 
+def test_dispatch_ex_validation():
+    """moe_dispatch_ex checks what moe_dispatch checks, plus the admission."""
+    lib = moe.lib()
+    d = moe.route_desc(64, 64, 8, 2, R=4, cf=1.25)
+    need = moe.moe_dispatch_workspace_size(d)
+    args = [FAKE] * 10
+    for adm in (-1, 2, 7):
+        assert lib.moe_dispatch_ex(ctypes.byref(d), adm, *args, FAKE, need,
+                                   None) == moe.MOE_ERR_INVALID_ARG
+    for adm in (moe.MOE_ADMIT_TOKEN_ORDER, moe.MOE_ADMIT_FIRST_CHOICE):
+        assert lib.moe_dispatch_ex(ctypes.byref(d), adm, *args, FAKE, need - 4,
+                                   None) == moe.MOE_ERR_WORKSPACE
+        args2 = list(args)
+        args2[2] = None  # x_perm
+        assert lib.moe_dispatch_ex(ctypes.byref(d), adm, *args2, FAKE, need,
+                                   None) == moe.MOE_ERR_INVALID_ARG
+
+
 def test_expert_ffn_validation():
     lib = moe.lib()
     F = FAKE

@@ -30,6 +30,8 @@ CASES = {
     "zipf-small-cf1.0": W.with_(W.small("zipf"), cf=1.0),
     "zipf-small-cf1.25": W.with_(W.small("zipf"), cf=1.25),
     "zipf-small-cf2.0": W.with_(W.small("zipf"), cf=2.0),
+    # GShard's top-2 router: first choices fill the capacity before second ones.
+    "zipf-small-cf1.0-first-choice": W.with_(W.small("zipf"), cf=1.0, admission="first_choice"),
 }
 
 _cache = {}
@@ -285,6 +287,49 @@ def test_dispatch_batch_size_paths(N, E):
     assert M < N * cfg["k"], "capacity should drop some assignments"
     tor = torch.from_numpy(dsp["token_of_row"][:M]).long()
     assert torch.equal(buf.x_perm[:M].cpu(), x[tor])
+
+
+@pytest.mark.parametrize("N,E,k,cf", [
+    (4096, 8, 2, 1.0),       # top-2 over 8 experts, tight capacity
+    (3000, 64, 1, 1.25),     # top-1: the same walk as token order
+    (32768, 128, 2, 1.25),   # one-block index pass at its largest batch
+    (32769, 128, 2, 1.0),    # per-tile histograms in one block, then assign
+    (100000, 128, 2, 1.25),  # tile_hist + scan + assign
+    (4096, 256, 8, 0.5),     # k = 8 over the most experts a descriptor allows
+    (777, 16, 3, 0.0),       # no capacity: same rows as token order, other order
+])
+def test_dispatch_first_choice_bit_exact(N, E, k, cf):
+    """moe_dispatch_ex with first-choice-first admission on Zipf-skewed, distinct
+    per-token expert ids: every integer output bit-exact against the oracle's
+    slot-major walk, x_perm row r equal to x[token_of_row[r]]; with no
+    capacity the admitted set equals token order's."""
+    cfg = W.with_(W.small("zipf"), N=N, E=E, k=k, R=min(E, 16), cf=cf,
+                  admission="first_choice")
+    print(f"[dispatch first choice] N={N} k={k} E={E} cf={cf}", flush=True)
+    g = np.random.default_rng(N + E + k)
+    logp = -1.1 * np.log(np.arange(1, E + 1))
+    keys = logp + g.gumbel(size=(N, E))  # Gumbel top-k: k distinct Zipf draws
+    ids = np.argsort(-keys, axis=1)[:, :k].astype(np.int32)
+    x = torch.randn(N, cfg["d"], generator=torch.Generator().manual_seed(N + k)).bfloat16()
+    buf = moe.MoeBuffers(cfg)
+    buf.topk_idx.copy_(torch.from_numpy(ids))
+    layer.dispatch(buf, {"x": x.cuda()})
+    torch.cuda.synchronize()
+    dsp = oracle.dispatch(cfg, ids)
+    for key in ("row_of_slot", "token_of_row", "slot_of_row", "expert_offsets", "admitted",
+                "rank_offsets", "rank_counts"):
+        assert np.array_equal(getattr(buf, key).cpu().numpy(), dsp[key]), key
+    M = dsp["num_rows"]
+    tor = torch.from_numpy(dsp["token_of_row"][:M]).long()
+    assert torch.equal(buf.x_perm[:M].cpu(), x[tor])
+    tok = oracle.dispatch(cfg, ids, "token")
+    if cf > 0:
+        assert (dsp["row_of_slot"][:, 0] >= 0).sum() >= (tok["row_of_slot"][:, 0] >= 0).sum()
+    else:
+        assert np.array_equal(dsp["row_of_slot"] >= 0, tok["row_of_slot"] >= 0)
+    if k > 1 and cf > 0:
+        assert not np.array_equal(dsp["row_of_slot"], tok["row_of_slot"]), \
+            "the case should tell the two walks apart"
 
 
 def test_all_tokens_to_one_expert_with_capacity():
