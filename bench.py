@@ -42,7 +42,7 @@ def parse_args():
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=50)
     ap.add_argument("--workload", default="switch",
-                    choices=["toy", "switch", "mixtral", "deepseek", "zipf"])
+                    choices=["toy", "switch", "mixtral", "deepseek", "zipf", "decode"])
     ap.add_argument("--cf", type=float, default=None, help="override the capacity factor")
     ap.add_argument("--admission", default="token", choices=["token", "first_choice"],
                     help="capacity admission order: token order, or every token's first "
@@ -272,15 +272,25 @@ def main():
                   else torch.zeros(E, dtype=torch.float32, device=dev))
     step_bias = cfg.get("bias_step", 1e-3)
 
-    calls = ["route", "dispatch", "ffn_plan", "ffn_up", "ffn_down"]
-    if buf.shared_out is not None:
-        calls.append("shared_ffn")
-    calls += ["combine", "bias_update"]
+    # Calls on the main stream, in order.  A shared expert (needs only x) is
+    # forked onto a side stream at the start of the step and joined before
+    # the combine, as the layer's forward does; it is timed by its own pair
+    # of events on that stream.
+    calls = ["route", "dispatch", "ffn_plan", "ffn_up", "ffn_down", "combine", "bias_update"]
+    fork = layer.has_shared(buf, wts)
+    main = torch.cuda.current_stream()
 
-    def step(events=None):
+    def step(events=None, shared_events=None):
         def mark(i):
             if events is not None:
-                events[i].record()
+                events[i].record(main)
+        if fork:
+            buf.side_stream.wait_stream(main)
+            if shared_events is not None:
+                shared_events[0].record(buf.side_stream)
+            layer.shared_ffn(buf, wts, buf.side_stream)
+            if shared_events is not None:
+                shared_events[1].record(buf.side_stream)
         mark(0)
         layer.route(buf, inp)
         mark(1)
@@ -294,19 +304,13 @@ def main():
         mark(4)
         moe.moe_expert_ffn_down(E, S, dim, h, cfg["act"], cfg["dtype"], buf.expert_offsets,
                                 wts["w2"], buf.y_perm, buf.ws_ffn)
-        i = 5
-        mark(i)
-        if buf.shared_out is not None:
-            sw1, sw3, sw2 = wts["shared"]
-            moe.moe_expert_ffn(1, N, dim, h, cfg["act"], cfg["dtype"], inp["x"],
-                               buf.shared_offsets, sw1, sw3, sw2, buf.shared_out, buf.ws_shared)
-            i += 1
-            mark(i)
+        mark(5)
+        if fork:
+            main.wait_stream(buf.side_stream)
         layer.combine(buf, inp, residual=True)
-        i += 1
-        mark(i)
+        mark(6)
         layer.bias_update(buf, bias_state, step_bias)
-        mark(i + 1)
+        mark(7)
 
     for _ in range(args.warmup):
         step()
@@ -333,15 +337,19 @@ def main():
     # the per-kernel durations and the roofline, not the step time.
     nev = len(calls) + 1
     events = [[torch.cuda.Event(enable_timing=True) for _ in range(nev)] for _ in range(args.steps)]
+    sh_events = [[torch.cuda.Event(enable_timing=True) for _ in range(2)]
+                 for _ in range(args.steps)]
     torch.cuda.synchronize()
     for s in range(args.steps):
-        step(events[s])
+        step(events[s], sh_events[s])
     torch.cuda.synchronize()
     per_call = {c: 0.0 for c in calls}
     for ev in events:
         for i, c in enumerate(calls):
             per_call[c] += ev[i].elapsed_time(ev[i + 1])
     per_call = {c: v / args.steps * 1e3 for c, v in per_call.items()}  # microseconds
+    if fork:
+        per_call["shared_ffn"] = sum(a.elapsed_time(b) for a, b in sh_events) / args.steps * 1e3
     instrumented_ms = sum(events[s][0].elapsed_time(events[s][-1])
                           for s in range(args.steps)) / args.steps
 
@@ -364,13 +372,16 @@ def main():
     n_cold = min(args.steps, 20)
     flush = torch.empty(512 << 18, dtype=torch.float32, device=dev)
     cold_ev = [[torch.cuda.Event(enable_timing=True) for _ in range(nev)] for _ in range(n_cold)]
+    cold_sh = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(n_cold)]
     torch.cuda.synchronize()
     for s in range(n_cold):
         flush.fill_(float(s))
-        step(cold_ev[s])
+        step(cold_ev[s], cold_sh[s])
     torch.cuda.synchronize()
     cold_call = {c: sum(ev[i].elapsed_time(ev[i + 1]) for ev in cold_ev) / n_cold * 1e3
                  for i, c in enumerate(calls)}
+    if fork:
+        cold_call["shared_ffn"] = sum(a.elapsed_time(b) for a, b in cold_sh) / n_cold * 1e3
     cold_step_ms = sum(ev[0].elapsed_time(ev[-1]) for ev in cold_ev) / n_cold
     del flush
 
@@ -416,7 +427,7 @@ def main():
         t = per_call[name] * 1e-6
         kern[name] = {"us": round(per_call[name], 2), "gbs": round(nbytes / t / 1e9, 1),
                       "hbm_frac": round(nbytes / t / (HBM_PEAK_GBS * 1e9), 4)}
-    for name in calls:
+    for name in per_call:
         kern.setdefault(name, {"us": round(per_call[name], 2)})
     cold = {"ms_per_step_with_per_call_events": round(cold_step_ms, 4), "steps": n_cold,
             "ffn_up": roof("ffn_up", up_flops, up_bytes, cold_call),
@@ -425,7 +436,7 @@ def main():
                          ("combine", combine_bytes)]:
         cold[name] = {"us": round(cold_call[name], 2),
                       "hbm_frac": round(nbytes / (cold_call[name] * 1e-6) / (HBM_PEAK_GBS * 1e9), 4)}
-    for name in calls:
+    for name in cold_call:
         cold.setdefault(name, {"us": round(cold_call[name], 2)})
 
     dom = "ffn_up" if per_call["ffn_up"] >= per_call["ffn_down"] else "ffn_down"

@@ -76,6 +76,9 @@ class MoeBuffers:
         if cfg.get("shared"):
             self.shared_out = torch.empty(N, dim, dtype=dt, device=device)
             self.shared_offsets = torch.tensor([0, N], **i32)
+            # The shared expert needs only x: moe_forward runs it on this
+            # stream (default priority) beside the routed path.
+            self.side_stream = torch.cuda.Stream(device=device)
             self.ws_shared = workspace(moe_expert_ffn_workspace_size(1, N, dim, h, cfg["act"],
                                                                      cfg["dtype"]), device)
         self.y = torch.empty(N, dim, dtype=dt, device=device)
@@ -101,8 +104,9 @@ def dispatch(buf: MoeBuffers, inp: dict, stream=None):
                         buf.rank_offsets, buf.rank_counts, buf.ws_dispatch, stream)
 
 
-def expert_ffn(buf: MoeBuffers, inp: dict, stream=None):
-    """``inp`` must come from ``prepare_weights`` (packed bf16 weights)."""
+def routed_ffn(buf: MoeBuffers, inp: dict, stream=None):
+    """Every routed expert over its rows.  ``inp`` must come from
+    ``prepare_weights`` (packed bf16 weights)."""
     d, cfg = buf.desc, buf.cfg
     if not inp.get("weights_packed"):
         raise ValueError("expert_ffn needs the weights from prepare_weights(cfg, inp)")
@@ -110,10 +114,27 @@ def expert_ffn(buf: MoeBuffers, inp: dict, stream=None):
     moe_expert_ffn(d.num_experts, S, d.hidden, cfg["h"], cfg["act"], cfg["dtype"], buf.x_perm,
                    buf.expert_offsets, inp["w1"], inp.get("w3"), inp["w2"], buf.y_perm,
                    buf.ws_ffn, stream)
-    if buf.shared_out is not None and inp.get("shared") is not None:
-        sw1, sw3, sw2 = inp["shared"]
-        moe_expert_ffn(1, d.num_tokens, d.hidden, cfg["h"], cfg["act"], cfg["dtype"], inp["x"],
-                       buf.shared_offsets, sw1, sw3, sw2, buf.shared_out, buf.ws_shared, stream)
+
+
+def has_shared(buf: MoeBuffers, inp: dict) -> bool:
+    return buf.shared_out is not None and inp.get("shared") is not None
+
+
+def shared_ffn(buf: MoeBuffers, inp: dict, stream=None):
+    """The shared expert over every token, in token order (x itself)."""
+    d, cfg = buf.desc, buf.cfg
+    if not inp.get("weights_packed"):
+        raise ValueError("expert_ffn needs the weights from prepare_weights(cfg, inp)")
+    sw1, sw3, sw2 = inp["shared"]
+    moe_expert_ffn(1, d.num_tokens, d.hidden, cfg["h"], cfg["act"], cfg["dtype"], inp["x"],
+                   buf.shared_offsets, sw1, sw3, sw2, buf.shared_out, buf.ws_shared, stream)
+
+
+def expert_ffn(buf: MoeBuffers, inp: dict, stream=None):
+    """Routed experts, then the shared expert where there is one, on one stream."""
+    routed_ffn(buf, inp, stream)
+    if has_shared(buf, inp):
+        shared_ffn(buf, inp, stream)
 
 
 def combine(buf: MoeBuffers, inp: dict, residual=True, stream=None):
@@ -127,9 +148,21 @@ def bias_update(buf: MoeBuffers, sel_bias: torch.Tensor, step: float, stream=Non
 
 
 def moe_forward(buf: MoeBuffers, inp: dict, residual=True, stream=None):
-    """route -> dispatch -> expert FFN (+ shared) -> combine, all enqueued."""
-    route(buf, inp, stream=stream)
-    dispatch(buf, inp, stream)
-    expert_ffn(buf, inp, stream)
-    combine(buf, inp, residual, stream)
+    """route -> dispatch -> routed expert FFN -> combine, all enqueued on
+    ``stream`` (default: torch's current stream).  A shared expert needs only
+    x, so it is forked onto the buffers' side stream before the route and
+    joined before the combine: it runs while the route and dispatch leave most
+    of the GPU idle.  The fork and join are stream waits on events, which a
+    HIP graph capture follows."""
+    main = stream if stream is not None else torch.cuda.current_stream()
+    fork = has_shared(buf, inp)
+    if fork:
+        buf.side_stream.wait_stream(main)
+        shared_ffn(buf, inp, buf.side_stream)
+    route(buf, inp, stream=main)
+    dispatch(buf, inp, main)
+    routed_ffn(buf, inp, main)
+    if fork:
+        main.wait_stream(buf.side_stream)
+    combine(buf, inp, residual, main)
     return buf.y

@@ -4,7 +4,7 @@ This module only describes shapes and draws seeded random tensors; it holds
 none of the layer's arithmetic.  Both the CPU oracle's tests and the HIP path's
 tests and benchmark feed it the same tensors.
 
-Five workload families (full sizes), after the configurations the pages'
+Six workload families (full sizes), after the configurations the pages'
 examples and the systems they name suggest:
 
 * ``toy``      -- the routing snippet of the "Expert Parallelism" glossary page
@@ -25,6 +25,12 @@ examples and the systems they name suggest:
                   offsets that make expert popularity roughly Zipf(1.1),
                   SwiGLU 2048->1408->2048, 16 ranks, capacity factor in
                   {1.0, 1.25, 2.0}, one selection-bias update then re-routing.
+* ``decode``   -- one decode step of the ``deepseek`` layer: 256 tokens (one
+                  per sequence), every other parameter as ``deepseek`` but 32
+                  ranks of 8 experts (DeepSeek-V3 decodes with EP = 40 over
+                  320 expert slots, 8 per GPU; without redundant experts 256
+                  experts make 32 such ranks).  About 8 rows per expert: the
+                  expert FFN streams every weight for a few rows each.
 
 ``small(name)`` gives a reduced version of each (same routing structure,
 smaller N/d/h with ragged sizes) that the oracle finishes in seconds.
@@ -59,6 +65,9 @@ FULL = {
                  score="softmax_topk", act="swiglu", dtype="bf16",
                  router_bias="zipf", sel_bias="zeros", shared=False, zipf=1.1,
                  cf_sweep=(1.0, 1.25, 2.0), bias_step=1e-3),
+    "decode": dict(N=256, d=7168, h=2048, E=256, k=8, R=32, cf=0.0, G=8, kg=4,
+                   score="sigmoid_norm", act="swiglu", dtype="bf16",
+                   router_bias=None, sel_bias=0.01, shared=True, zipf=None),
 }
 
 _SMALL = {
@@ -67,9 +76,10 @@ _SMALL = {
     "mixtral": dict(N=1531, d=512, h=448),
     "deepseek": dict(N=517, d=384, h=192),
     "zipf": dict(N=3001, d=256, h=192),
+    "decode": dict(N=67, d=384, h=192),
 }
 
-ORDER = ["toy", "switch", "mixtral", "deepseek", "zipf"]
+ORDER = ["toy", "switch", "mixtral", "deepseek", "zipf", "decode"]
 
 
 def full(name: str) -> dict:

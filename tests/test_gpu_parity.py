@@ -27,6 +27,7 @@ CASES = {
     "switch-small": W.small("switch"),
     "mixtral-small": W.small("mixtral"),
     "deepseek-small": W.small("deepseek"),
+    "decode-small": W.small("decode"),
     "zipf-small-cf1.0": W.with_(W.small("zipf"), cf=1.0),
     "zipf-small-cf1.25": W.with_(W.small("zipf"), cf=1.25),
     "zipf-small-cf2.0": W.with_(W.small("zipf"), cf=2.0),
