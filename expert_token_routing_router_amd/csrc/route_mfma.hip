@@ -545,7 +545,7 @@ __global__ __launch_bounds__(kFuseWaves * 64, 2) void route_fused(
     int G, int kg, int score_fn, const float* __restrict__ router_bias,
     const float* __restrict__ sel_bias, float* __restrict__ logits,
     int32_t* __restrict__ topk_idx, float* __restrict__ topk_w, int32_t* __restrict__ counts,
-    double* __restrict__ ws_sx, double* __restrict__ ws_sw) {
+    double* __restrict__ ws_sx, double* __restrict__ ws_sw, int tail_tpb) {
   constexpr int ZW = 64 * NJ;
   __shared__ float zs[kFuseTok][ZW];  // z~, then exact values for candidates
   __shared__ __attribute__((aligned(1024))) char ring[kFuseRing][kFuseSlot];  // step 1; then pairs
@@ -563,9 +563,9 @@ __global__ __launch_bounds__(kFuseWaves * 64, 2) void route_fused(
   static_assert(kFuseTok <= 64 && ZW <= 256, "pair encoding and one-wave token scan");
 
   const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  // The tail launch takes 16 tokens per block, so that the few token tiles
-  // of a split launch still cover every CU.
-  constexpr int TPB = SPLIT == 2 ? kFuseTok / 2 : kFuseTok;
+  // The tail launch takes tail_tpb (1..16) tokens per block, so that the few
+  // token tiles of a split launch still cover every CU.
+  const int TPB = SPLIT == 2 ? tail_tpb : kFuseTok;
   const int t0 = blockIdx.x * TPB;
   const int nt = min(TPB, N - t0);
   const int nch = d / 32;
@@ -761,14 +761,19 @@ hipError_t launch_route_certified(const RouteArgs& a, hipStream_t st) {
   const bool split = route_split(a.N, a.E);
   double* ws_sx = split ? static_cast<double*>(a.ws) : nullptr;
   double* ws_sw = split ? ws_sx + a.N : nullptr;
+  // Tail blocks take 16 tokens while that still gives about one block per
+  // CU, fewer for small batches (decode-sized): there the exact sums of a
+  // block's candidate pairs stream each pair's x and w rows from L2, and 16
+  // tokens per block would put all of that on N/16 CUs.
+  const int tail_tpb = std::min(kFuseTok / 2, std::max(1, (a.N + 255) / 256));
   auto launch = [&](auto kernel, dim3 grid) {
     kernel<<<grid, kFuseWaves * 64, 0, st>>>(
         static_cast<const bf16_t*>(a.x), static_cast<const bf16_t*>(a.w_router), a.N, a.d, a.E,
         a.k, a.G, a.kg, a.score_fn, a.router_bias, a.sel_bias, a.logits, a.topk_idx, a.topk_w,
-        a.counts, ws_sx, ws_sw);
+        a.counts, ws_sx, ws_sw, tail_tpb);
   };
   const dim3 scores_grid(blocks, (a.E + 63) / 64);
-  const dim3 tail_grid((a.N + kFuseTok / 2 - 1) / (kFuseTok / 2));
+  const dim3 tail_grid((a.N + tail_tpb - 1) / tail_tpb);
   switch ((a.E + 63) / 64) {
     case 1: launch(route_fused<1, 0>, dim3(blocks)); break;
     case 2:
