@@ -29,7 +29,7 @@ hipError_t launch_route(const RouteArgs& a, hipStream_t st);
 // Exact logits for every (token, expert) pair (the fp64 definition), no selection.
 hipError_t launch_router_logits(const RouteArgs& a, hipStream_t st);
 // Certified path for bf16 inputs (route_mfma.hip).
-size_t route_certified_workspace_bytes(int N, int E);
+size_t route_certified_workspace_bytes(int N, int d, int E);
 hipError_t launch_route_certified(const RouteArgs& a, hipStream_t st);
 void launch_zero_i32(int32_t* p, int n, hipStream_t st);
 

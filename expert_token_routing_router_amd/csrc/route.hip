@@ -334,7 +334,7 @@ static bool use_certified(const RouteArgs& a) {
 
 size_t route_workspace_bytes(int N, int d, int E, int dtype) {
   const size_t exact = exact_logits_bytes(N, d, E);
-  const size_t cert = dtype == 1 ? route_certified_workspace_bytes(N, E) : 0;
+  const size_t cert = dtype == 1 ? route_certified_workspace_bytes(N, d, E) : 0;
   return exact > cert ? exact : cert;
 }
 

@@ -545,7 +545,8 @@ __global__ __launch_bounds__(kFuseWaves * 64, 2) void route_fused(
     int G, int kg, int score_fn, const float* __restrict__ router_bias,
     const float* __restrict__ sel_bias, float* __restrict__ logits,
     int32_t* __restrict__ topk_idx, float* __restrict__ topk_w, int32_t* __restrict__ counts,
-    double* __restrict__ ws_sx, double* __restrict__ ws_sw, int tail_tpb) {
+    double* __restrict__ ws_sx, double* __restrict__ ws_sw, double* __restrict__ ws_part,
+    int ksplit, int tail_tpb) {
   constexpr int ZW = 64 * NJ;
   __shared__ float zs[kFuseTok][ZW];  // z~, then exact values for candidates
   __shared__ __attribute__((aligned(1024))) char ring[kFuseRing][kFuseSlot];  // step 1; then pairs
@@ -568,7 +569,16 @@ __global__ __launch_bounds__(kFuseWaves * 64, 2) void route_fused(
   const int TPB = SPLIT == 2 ? tail_tpb : kFuseTok;
   const int t0 = blockIdx.x * TPB;
   const int nt = min(TPB, N - t0);
-  const int nch = d / 32;
+  // Chunks of 32 elements this block sums.  A K-split scoring launch
+  // (ksplit > 1, grid.z = split) gives split z the even-aligned chunk range
+  // [c0, c0 + nch); its fp64 partial sums go to ws_part.
+  int c0 = 0, nch = d / 32;
+  if (SPLIT == 1 && ksplit > 1) {
+    const int z = blockIdx.z, pairs = nch / 2;
+    c0 = 2 * (pairs * z / ksplit);
+    const int c1 = z + 1 == ksplit ? nch : 2 * (pairs * (z + 1) / ksplit);
+    nch = c1 - c0;
+  }
   for (int e = tid; e < E; e += kFuseWaves * 64) hist[e] = 0;
 
   // ---- 1. scores --------------------------------------------------------
@@ -594,10 +604,10 @@ __global__ __launch_bounds__(kFuseWaves * 64, 2) void route_fused(
       const int r = lane / 4, c = (lane % 4) ^ swz4(r);
       if (j < 2) {
         const int t = min(t0 + 16 * j + r, N - 1);
-        src = reinterpret_cast<const u32x4*>(x + (size_t)t * d) + c;
+        src = reinterpret_cast<const u32x4*>(x + (size_t)t * d) + c + 4 * c0;
       } else {
         const int e = min(et + 16 * (j - 2) + r, E - 1);
-        src = reinterpret_cast<const u32x4*>(w + (size_t)e * d) + c;
+        src = reinterpret_cast<const u32x4*>(w + (size_t)e * d) + c + 4 * c0;
       }
     }
 #define MOE_FUSE_ISSUE(ch_)                                                                 \
@@ -700,7 +710,12 @@ __global__ __launch_bounds__(kFuseWaves * 64, 2) void route_fused(
       for (int v = 0; v < 4; ++v) {
         const int tl = 16 * (wave / 4) + 4 * (lane >> 4) + v;
         if constexpr (SPLIT == 1) {
-          if (tl < nt) logits[(size_t)(t0 + tl) * E + e] = (float)(acc[v] + bias);
+          if (tl < nt) {
+            if (ksplit > 1)
+              ws_part[((size_t)blockIdx.z * N + t0 + tl) * E + e] = acc[v];
+            else
+              logits[(size_t)(t0 + tl) * E + e] = (float)(acc[v] + bias);
+          }
         } else {
           zs[tl][e] = (float)(acc[v] + bias);
         }
@@ -709,7 +724,7 @@ __global__ __launch_bounds__(kFuseWaves * 64, 2) void route_fused(
     // sum w^2: from the diagonal lanes of waves 0-3.
     if (wave < 4 && diag_lane && et + 16 * wave + (lane & 15) < E) {
       if constexpr (SPLIT == 1) {
-        if (blockIdx.x == 0) ws_sw[et + 16 * wave + (lane & 15)] = swp;
+        if (blockIdx.x == 0) ws_sw[(size_t)blockIdx.z * E + et + 16 * wave + (lane & 15)] = swp;
       } else {
         sw[et + 16 * wave + (lane & 15)] = swp;
       }
@@ -718,14 +733,39 @@ __global__ __launch_bounds__(kFuseWaves * 64, 2) void route_fused(
   }
   if constexpr (SPLIT == 1) {
     const int tl = 16 * (wave >> 2) + (lane & 15);
-    if (blockIdx.y == 0 && (wave & 3) == 0 && diag_lane && tl < nt) ws_sx[t0 + tl] = sxp;
+    if (blockIdx.y == 0 && (wave & 3) == 0 && diag_lane && tl < nt)
+      ws_sx[(size_t)blockIdx.z * N + t0 + tl] = sxp;
     return;
   }
   if constexpr (SPLIT == 2) {
-    // The tile's z~ and norms from the scoring launch.
-    for (int i = tid; i < nt * E; i += kFuseWaves * 64) zs[i / E][i % E] = logits[(size_t)t0 * E + i];
-    for (int tl = tid; tl < nt; tl += kFuseWaves * 64) sx[tl] = ws_sx[t0 + tl];
-    for (int e = tid; e < E; e += kFuseWaves * 64) sw[e] = ws_sw[e];
+    // The tile's z~ and norms from the scoring launch; after a K split, the
+    // sum of the splits' fp64 partials in split order (each partial obeys the
+    // chunk bound, and the few fp64 additions are far inside the margin's
+    // slack), plus the bias, rounded once.  Sums of the partial squared-norm
+    // bounds are bounds.
+    if (ksplit > 1) {
+      for (int i = tid; i < nt * E; i += kFuseWaves * 64) {
+        const int e = i % E;
+        double z = 0.0;
+        for (int q = 0; q < ksplit; ++q) z += ws_part[((size_t)q * N + t0) * E + i];
+        zs[i / E][e] = (float)(z + (router_bias ? (double)router_bias[e] : 0.0));
+      }
+      for (int tl = tid; tl < nt; tl += kFuseWaves * 64) {
+        double q2 = 0.0;
+        for (int q = 0; q < ksplit; ++q) q2 += ws_sx[(size_t)q * N + t0 + tl];
+        sx[tl] = q2;
+      }
+      for (int e = tid; e < E; e += kFuseWaves * 64) {
+        double q2 = 0.0;
+        for (int q = 0; q < ksplit; ++q) q2 += ws_sw[(size_t)q * E + e];
+        sw[e] = q2;
+      }
+    } else {
+      for (int i = tid; i < nt * E; i += kFuseWaves * 64)
+        zs[i / E][i % E] = logits[(size_t)t0 * E + i];
+      for (int tl = tid; tl < nt; tl += kFuseWaves * 64) sx[tl] = ws_sx[t0 + tl];
+      for (int e = tid; e < E; e += kFuseWaves * 64) sw[e] = ws_sw[e];
+    }
   } else {
     if ((wave & 3) == 0 && diag_lane) sx[16 * (wave >> 2) + (lane & 15)] = sxp;
   }
@@ -749,18 +789,34 @@ static bool route_split(int N, int E) {
   return E > 64;
 }
 
-size_t route_certified_workspace_bytes(int N, int E) {
+// K splits of the scoring launch: when its token tiles x expert tiles give
+// fewer blocks than CUs (decode-sized batches), each block sums 1/ks of the
+// hidden dimension, up to 8 ways and at least one chunk pair each.
+static int route_ksplit(int N, int d, int E) {
+  if (!route_split(N, E)) return 1;
+  const int base = ((N + kFuseTok - 1) / kFuseTok) * ((E + 63) / 64);
+  if (base >= 256) return 1;
+  return std::max(1, std::min(std::min(8, 256 / std::max(base, 1)), d / 64));
+}
+
+size_t route_certified_workspace_bytes(int N, int d, int E) {
   // The fused kernel keeps everything in LDS; the split one passes the
-  // squared norms between its two launches.
-  return route_split(N, E) ? (size_t)(N + E) * sizeof(double) : 0;
+  // squared norms (per K split) and, when K is split, the fp64 partial
+  // logits between its two launches.
+  if (!route_split(N, E)) return 0;
+  const size_t ks = route_ksplit(N, d, E);
+  return ks * (size_t)(N + E) * sizeof(double) +
+         (ks > 1 ? ks * (size_t)N * E * sizeof(double) : 0);
 }
 
 hipError_t launch_route_certified(const RouteArgs& a, hipStream_t st) {
   launch_zero_i32(a.counts, a.E, st);
   const int blocks = (a.N + kFuseTok - 1) / kFuseTok;
   const bool split = route_split(a.N, a.E);
+  const int ks = route_ksplit(a.N, a.d, a.E);
   double* ws_sx = split ? static_cast<double*>(a.ws) : nullptr;
-  double* ws_sw = split ? ws_sx + a.N : nullptr;
+  double* ws_sw = split ? ws_sx + (size_t)ks * a.N : nullptr;
+  double* ws_part = ks > 1 ? ws_sw + (size_t)ks * a.E : nullptr;
   // Tail blocks take 16 tokens while that still gives about one block per
   // CU, fewer for small batches (decode-sized): there the exact sums of a
   // block's candidate pairs stream each pair's x and w rows from L2, and 16
@@ -770,9 +826,9 @@ hipError_t launch_route_certified(const RouteArgs& a, hipStream_t st) {
     kernel<<<grid, kFuseWaves * 64, 0, st>>>(
         static_cast<const bf16_t*>(a.x), static_cast<const bf16_t*>(a.w_router), a.N, a.d, a.E,
         a.k, a.G, a.kg, a.score_fn, a.router_bias, a.sel_bias, a.logits, a.topk_idx, a.topk_w,
-        a.counts, ws_sx, ws_sw, tail_tpb);
+        a.counts, ws_sx, ws_sw, ws_part, ks, tail_tpb);
   };
-  const dim3 scores_grid(blocks, (a.E + 63) / 64);
+  const dim3 scores_grid(blocks, (a.E + 63) / 64, ks);
   const dim3 tail_grid((a.N + tail_tpb - 1) / tail_tpb);
   switch ((a.E + 63) / 64) {
     case 1: launch(route_fused<1, 0>, dim3(blocks)); break;
