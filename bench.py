@@ -50,6 +50,9 @@ def parse_args():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0,
                     help="target length of the oracle's timed sample")
+    ap.add_argument("--no-clocks", action="store_true",
+                    help="skip reading the clocks with rocm-smi (a child process; under a "
+                         "profiler that has already initialised the GPU, leave it out)")
     ap.add_argument("--rank-share", action="store_true",
                     help="also time the expert FFN on one rank's share of the experts at "
                          "its real shape (rows from all R source ranks)")
@@ -241,7 +244,7 @@ def main():
                           "n_gpus": args.gpus}))
         sys.exit(2)
 
-    clocks = read_clocks()
+    clocks = {} if args.no_clocks else read_clocks()
     import torch
 
     import expert_token_routing_router_amd as moe
