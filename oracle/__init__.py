@@ -74,6 +74,8 @@ def lib():
             "oracle_dispatch": [D, P, P, P, P, P, P, P, P],
             "oracle_dispatch_ex": [D, I32, P, P, P, P, P, P, P, P],
             "oracle_permute": [I32, I32, I32, P, P, P],
+            "oracle_quantize_rows_q8": [I32, I32, I32, P, P, P],
+            "oracle_dequantize_rows_q8": [I32, I32, I32, P, P, P],
             "oracle_ffn_row": [I32, I32, I32, I32, P, P, P, P, P],
             "oracle_expert_ffn": [I32, I32, I32, I32, I32, P, P, P, P, P, P],
             "oracle_combine": [I32, I32, I32, I32, P, P, P, P, P, P],
@@ -252,14 +254,44 @@ def bias_update(num_tokens: int, top_k: int, counts, sel_bias, step: float = 1e-
     return b
 
 
+def quantize_rows_q8(dtype: str, x) -> tuple:
+    """Per-row INT8 payload: (q [rows, d] int8, scale [rows] fp32)."""
+    ed = _elem_dtype(dtype)
+    x = _c(x, ed)
+    rows, d = x.shape
+    q = np.empty((rows, d), np.int8)
+    s = np.empty(rows, np.float32)
+    _check(lib().oracle_quantize_rows_q8(int(rows), int(d), DTYPE_CODES[dtype], _ptr(x), _ptr(q),
+                                         _ptr(s)), "oracle_quantize_rows_q8")
+    return q, s
+
+
+def dequantize_rows_q8(dtype: str, q, scale) -> np.ndarray:
+    q = _c(q, np.int8)
+    scale = _c(scale, np.float32)
+    rows, d = q.shape
+    out = np.empty((rows, d), _elem_dtype(dtype))
+    _check(lib().oracle_dequantize_rows_q8(int(rows), int(d), DTYPE_CODES[dtype], _ptr(q),
+                                           _ptr(scale), _ptr(out)), "oracle_dequantize_rows_q8")
+    return out
+
+
 def forward(cfg: dict, x, w_router, router_bias, sel_bias, w1, w3, w2,
             shared=None, residual=True) -> dict:
     """The whole layer: route -> dispatch -> permute -> FFN -> combine.
-    ``shared`` is an optional (w1, w3, w2) triple of one always-on expert."""
+    ``shared`` is an optional (w1, w3, w2) triple of one always-on expert.
+    With cfg["payload"] == "int8" the permuted rows travel as the per-token
+    INT8 payload (quantised once per token, rows copied, dequantised before
+    the FFN); the shared expert and the residual use x itself."""
     r = route(cfg, x, w_router, router_bias, sel_bias)
     dsp = dispatch(cfg, r["topk_idx"])
     M = dsp["num_rows"]
-    x_perm = permute(cfg["dtype"], x, dsp["token_of_row"], M)
+    if cfg.get("payload", "native") == "int8":
+        q, sc = quantize_rows_q8(cfg["dtype"], x)
+        tor = dsp["token_of_row"][:M]
+        x_perm = dequantize_rows_q8(cfg["dtype"], q[tor], sc[tor])
+    else:
+        x_perm = permute(cfg["dtype"], x, dsp["token_of_row"], M)
     y_perm = expert_ffn(cfg["dtype"], cfg["act"], x_perm, dsp["expert_offsets"], w1, w3, w2)
     shared_out = None
     if shared is not None:

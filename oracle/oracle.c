@@ -380,6 +380,62 @@ int oracle_permute(int32_t num_rows, int32_t hidden, int32_t dtype, const void* 
   return 0;
 }
 
+/* ----------------------------------------------------- INT8 payload -- */
+
+/* INT8 payload of the dispatch exchange (EP notes, "深入推导": INT8-quantised
+ * communication halves the exchange volume).  The pages give no scheme; the
+ * reading taken is one symmetric scale per token row, and every decision is an
+ * fp32 IEEE operation rounded to nearest even:
+ *   amax = max_i |x_i|  (exact);  amax == 0: q = 0, s = 0;  otherwise
+ *   inv  = 127 / amax,  q_i = clamp(rint(x_i * inv), -127, 127),  s = amax / 127. */
+int oracle_quantize_rows_q8(int32_t num_rows, int32_t hidden, int32_t dtype, const void* x,
+                            int8_t* q, float* scale) {
+  if (num_rows < 0 || hidden < 1 || !dtype_ok(dtype)) return -1;
+  if (num_rows > 0 && (!x || !q || !scale)) return -1;
+  for (int32_t r = 0; r < num_rows; ++r) {
+    const size_t base = (size_t)r * hidden;
+    float amax = 0.0f;
+    for (int32_t i = 0; i < hidden; ++i) {
+      const float v = fabsf((float)elem(x, dtype, base + i));
+      if (v > amax) amax = v;
+    }
+    if (amax == 0.0f) {
+      for (int32_t i = 0; i < hidden; ++i) q[base + i] = 0;
+      scale[r] = 0.0f;
+      continue;
+    }
+    const float inv = 127.0f / amax;
+    for (int32_t i = 0; i < hidden; ++i) {
+      const float v = (float)elem(x, dtype, base + i) * inv;
+      float c = rintf(v);
+      if (c > 127.0f) c = 127.0f;
+      if (c < -127.0f) c = -127.0f;
+      q[base + i] = (int8_t)c;
+    }
+    scale[r] = amax / 127.0f;
+  }
+  return 0;
+}
+
+/* x'_i = q_i * s as an fp32 product, then rounded to the dtype (bf16: nearest
+ * even; fp32: unchanged). */
+int oracle_dequantize_rows_q8(int32_t num_rows, int32_t hidden, int32_t dtype, const int8_t* q,
+                              const float* scale, void* x) {
+  if (num_rows < 0 || hidden < 1 || !dtype_ok(dtype)) return -1;
+  if (num_rows > 0 && (!x || !q || !scale)) return -1;
+  for (int32_t r = 0; r < num_rows; ++r) {
+    for (int32_t i = 0; i < hidden; ++i) {
+      const size_t k = (size_t)r * hidden + i;
+      const float v = (float)q[k] * scale[r];
+      if (dtype == 0)
+        ((float*)x)[k] = v;
+      else
+        ((uint16_t*)x)[k] = double_to_bf16_bits((double)v);
+    }
+  }
+  return 0;
+}
+
 /* ------------------------------------------------------------ expert FFN -- */
 
 static double act_relu(double u) { return u > 0.0 ? u : 0.0; }

@@ -86,6 +86,19 @@ int oracle_dispatch_ex(const oracle_desc* desc, int32_t admission, const int32_t
 int oracle_permute(int32_t num_rows, int32_t hidden, int32_t dtype, const void* x,
                    const int32_t* token_of_row, void* x_perm);
 
+/* INT8 payload of the dispatch exchange, one symmetric scale per row (EP
+ * notes, "深入推导": INT8-quantised communication halves the exchange volume;
+ * the scheme is a reading).  Each step an fp32 IEEE operation rounded to
+ * nearest even: amax = max |x_i|; inv = 127 / amax; q_i = clamp(rint(x_i * inv),
+ * -127, 127); scale = amax / 127 (a zero row gives q = 0, scale = 0).
+ * q is [num_rows, hidden] int8, scale [num_rows] fp32. */
+int oracle_quantize_rows_q8(int32_t num_rows, int32_t hidden, int32_t dtype, const void* x,
+                            int8_t* q, float* scale);
+
+/* x_i = q_i * scale as an fp32 product, rounded to the dtype (bf16: nearest even). */
+int oracle_dequantize_rows_q8(int32_t num_rows, int32_t hidden, int32_t dtype, const int8_t* q,
+                              const float* scale, void* x);
+
 /* One row of one expert's FFN: y = W2 act(W1 x [, W3 x]).  w1/w3 are [h,d],
  * w2 is [d,h] (row-major, out x in); w3 only for SwiGLU (gate = w1, up = w3). */
 int oracle_ffn_row(int32_t hidden, int32_t ffn_hidden, int32_t act, int32_t dtype,
