@@ -50,6 +50,9 @@ def parse_args():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0,
                     help="target length of the oracle's timed sample")
+    ap.add_argument("--payload", default="native", choices=["native", "int8"],
+                    help="dispatched rows as the layer dtype, or as the INT8 payload "
+                         "(quantised in the permute, dequantised before the FFN)")
     ap.add_argument("--no-clocks", action="store_true",
                     help="skip reading the clocks with rocm-smi (a child process; under a "
                          "profiler that has already initialised the GPU, leave it out)")
@@ -176,6 +179,8 @@ def describe(cfg) -> str:
         s += " +shared"
     if cfg.get("admission", "token") != "token":
         s += f" admission={cfg['admission']}"
+    if cfg.get("payload", "native") != "native":
+        s += f" payload={cfg['payload']}"
     return s
 
 
@@ -257,6 +262,8 @@ def main():
         cfg["cf"] = args.cf
     if args.admission != "token":
         cfg["admission"] = args.admission
+    if args.payload != "native":
+        cfg["payload"] = args.payload
     # Inputs: the glossary snippet's stream for the toy workload (CPU), else
     # drawn on the device.
     gen_dev = "cpu" if args.workload == "toy" else "cuda"

@@ -38,7 +38,8 @@ TORCH_DTYPE = {MOE_F32: torch.float32, MOE_BF16: torch.bfloat16}
 
 EXPORTS = [
     "moe_route_workspace_size", "moe_route", "moe_router_logits",
-    "moe_dispatch_workspace_size", "moe_dispatch", "moe_dispatch_ex",
+    "moe_dispatch_workspace_size", "moe_dispatch", "moe_dispatch_ex", "moe_dispatch_q8",
+    "moe_dequantize_q8",
     "moe_expert_ffn_workspace_size", "moe_expert_ffn", "moe_expert_ffn_plan",
     "moe_expert_ffn_up", "moe_expert_ffn_down", "moe_expert_ffn_pack_weights", "moe_combine",
     "moe_bias_update", "moe_status_string",
@@ -100,6 +101,8 @@ def lib() -> ctypes.CDLL:
             "moe_dispatch_workspace_size": ([D], SZ),
             "moe_dispatch": ([D, P, P, P, P, P, P, P, P, P, P, P, SZ, P], I32),
             "moe_dispatch_ex": ([D, I32, P, P, P, P, P, P, P, P, P, P, P, SZ, P], I32),
+            "moe_dispatch_q8": ([D, I32, P, P, P, P, P, P, P, P, P, P, P, P, SZ, P], I32),
+            "moe_dequantize_q8": ([I32, I32, I32, P, P, P, P, P], I32),
             "moe_expert_ffn_workspace_size": ([I32, I32, I32, I32, I32, I32], SZ),
             "moe_expert_ffn": ([I32, I32, I32, I32, I32, I32, P, P, P, P, P, P, P, SZ, P], I32),
             "moe_expert_ffn_plan": ([I32, I32, I32, I32, I32, I32, P, P, SZ, P], I32),
@@ -218,6 +221,47 @@ def moe_dispatch_ex(desc, admission, x, topk_idx, x_perm, row_of_slot, token_of_
     adm = ADMISSION[admission] if isinstance(admission, str) else int(admission)
     _dispatch("moe_dispatch_ex", desc, adm, x, topk_idx, x_perm, row_of_slot, token_of_row,
               slot_of_row, expert_offsets, admitted, rank_offsets, rank_counts, ws, stream)
+
+
+def moe_dispatch_q8(desc, admission, x, topk_idx, x_perm_q, row_scale, row_of_slot,
+                    token_of_row, slot_of_row, expert_offsets, admitted, rank_offsets,
+                    rank_counts, ws, stream=None):
+    """Dispatch with the INT8 row payload: x_perm_q [N*k, d] int8 codes and
+    row_scale [N*k] fp32 instead of dtype rows."""
+    adm = ADMISSION[admission] if isinstance(admission, str) else int(admission)
+    N, d, E, k, R = desc.num_tokens, desc.hidden, desc.num_experts, desc.top_k, desc.num_ranks
+    dt = TORCH_DTYPE.get(desc.dtype)
+    S = N * k
+    st = lib().moe_dispatch_q8(
+        ctypes.byref(desc), adm, _ptr(x, "x", dt, N * d, N > 0),
+        _ptr(topk_idx, "topk_idx", torch.int32, S, N > 0),
+        _ptr(x_perm_q, "x_perm_q", torch.int8, S * d, N > 0),
+        _ptr(row_scale, "row_scale", torch.float32, S, N > 0),
+        _ptr(row_of_slot, "row_of_slot", torch.int32, S, N > 0),
+        _ptr(token_of_row, "token_of_row", torch.int32, S, N > 0),
+        _ptr(slot_of_row, "slot_of_row", torch.int8, S, N > 0),
+        _ptr(expert_offsets, "expert_offsets", torch.int32, E + 1),
+        _ptr(admitted, "admitted", torch.int32, E),
+        _ptr(rank_offsets, "rank_offsets", torch.int32, R + 1),
+        _ptr(rank_counts, "rank_counts", torch.int32, R),
+        _ptr(ws, "ws", None, None, False), 0 if ws is None else ws.numel() * ws.element_size(),
+        _stream(stream))
+    _raise("moe_dispatch_q8", st)
+
+
+def moe_dequantize_q8(max_rows, hidden, dtype, x_perm_q, row_scale, num_rows, x_perm,
+                      stream=None):
+    """x_perm[r] = dtype(x_perm_q[r] * row_scale[r]) for r < num_rows[0] (a
+    one-element device tensor, e.g. expert_offsets[E:])."""
+    dtype = DTYPE[dtype] if isinstance(dtype, str) else int(dtype)
+    dt = TORCH_DTYPE.get(dtype)
+    M, d = max_rows, hidden
+    st = lib().moe_dequantize_q8(
+        M, d, dtype, _ptr(x_perm_q, "x_perm_q", torch.int8, M * d, M > 0),
+        _ptr(row_scale, "row_scale", torch.float32, M, M > 0),
+        _ptr(num_rows, "num_rows", torch.int32, 1, M > 0),
+        _ptr(x_perm, "x_perm", dt, M * d, M > 0), _stream(stream))
+    _raise("moe_dequantize_q8", st)
 
 
 def _dispatch(name, desc, admission, x, topk_idx, x_perm, row_of_slot, token_of_row,

@@ -118,11 +118,63 @@ int moe_dispatch(const moe_route_desc* desc, const void* x, const int32_t* topk_
                          rank_counts, ws, ws_bytes, stream);
 }
 
+// Shared by moe_dispatch_ex and moe_dispatch_q8: x_perm is the dtype rows or,
+// with xq set, the INT8 payload rows (then x_perm must be NULL).
+static int dispatch_common(const moe_route_desc* desc, int32_t admission, const void* x,
+                           const int32_t* topk_idx, void* x_perm, int8_t* xq, float* row_scale,
+                           int32_t* row_of_slot, int32_t* token_of_row, int8_t* slot_of_row,
+                           int32_t* expert_offsets, int32_t* admitted, int32_t* rank_offsets,
+                           int32_t* rank_counts, void* ws, size_t ws_bytes, void* stream);
+
 int moe_dispatch_ex(const moe_route_desc* desc, int32_t admission, const void* x,
                     const int32_t* topk_idx, void* x_perm, int32_t* row_of_slot,
                     int32_t* token_of_row, int8_t* slot_of_row, int32_t* expert_offsets,
                     int32_t* admitted, int32_t* rank_offsets, int32_t* rank_counts, void* ws,
                     size_t ws_bytes, void* stream) {
+  return dispatch_common(desc, admission, x, topk_idx, x_perm, nullptr, nullptr, row_of_slot,
+                         token_of_row, slot_of_row, expert_offsets, admitted, rank_offsets,
+                         rank_counts, ws, ws_bytes, stream);
+}
+
+int moe_dispatch_q8(const moe_route_desc* desc, int32_t admission, const void* x,
+                    const int32_t* topk_idx, int8_t* x_perm_q, float* row_scale,
+                    int32_t* row_of_slot, int32_t* token_of_row, int8_t* slot_of_row,
+                    int32_t* expert_offsets, int32_t* admitted, int32_t* rank_offsets,
+                    int32_t* rank_counts, void* ws, size_t ws_bytes, void* stream) {
+  if (desc && desc->num_tokens > 0) {
+    if (!x_perm_q || !row_scale) return MOE_ERR_INVALID_ARG;
+    if (!aligned16(x_perm_q) || (reinterpret_cast<uintptr_t>(row_scale) & 3u))
+      return MOE_ERR_INVALID_ARG;
+  }
+  if (desc && (desc->dtype == MOE_F32 || desc->dtype == MOE_BF16) &&
+      desc->hidden > moe::q8_max_hidden(desc->dtype))
+    return MOE_ERR_UNSUPPORTED;
+  return dispatch_common(desc, admission, x, topk_idx, nullptr, x_perm_q, row_scale, row_of_slot,
+                         token_of_row, slot_of_row, expert_offsets, admitted, rank_offsets,
+                         rank_counts, ws, ws_bytes, stream);
+}
+
+int moe_dequantize_q8(int32_t max_rows, int32_t hidden, int32_t dtype, const int8_t* x_perm_q,
+                      const float* row_scale, const int32_t* num_rows, void* x_perm,
+                      void* stream) {
+  if (max_rows < 0 || hidden < 1 || (dtype != MOE_F32 && dtype != MOE_BF16))
+    return MOE_ERR_INVALID_ARG;
+  if (hidden % 8 != 0) return MOE_ERR_UNSUPPORTED;
+  if (max_rows > 0) {
+    if (!x_perm_q || !row_scale || !num_rows || !x_perm) return MOE_ERR_INVALID_ARG;
+    if (!aligned16(x_perm_q) || !aligned16(x_perm) ||
+        (reinterpret_cast<uintptr_t>(row_scale) & 3u) || (reinterpret_cast<uintptr_t>(num_rows) & 3u))
+      return MOE_ERR_INVALID_ARG;
+  }
+  return status_of(moe::launch_dequantize_q8(max_rows, hidden, dtype, x_perm_q, row_scale,
+                                             num_rows, x_perm, static_cast<hipStream_t>(stream)));
+}
+
+static int dispatch_common(const moe_route_desc* desc, int32_t admission, const void* x,
+                           const int32_t* topk_idx, void* x_perm, int8_t* xq, float* row_scale,
+                           int32_t* row_of_slot, int32_t* token_of_row, int8_t* slot_of_row,
+                           int32_t* expert_offsets, int32_t* admitted, int32_t* rank_offsets,
+                           int32_t* rank_counts, void* ws, size_t ws_bytes, void* stream) {
   int st = check_desc(desc);
   if (st != MOE_OK) return st;
   if (admission != MOE_ADMIT_TOKEN_ORDER && admission != MOE_ADMIT_FIRST_CHOICE)
@@ -130,9 +182,9 @@ int moe_dispatch_ex(const moe_route_desc* desc, int32_t admission, const void* x
   if (!expert_offsets || !admitted || !rank_offsets || !rank_counts) return MOE_ERR_INVALID_ARG;
   const int N = desc->num_tokens;
   if (N > 0) {
-    if (!x || !topk_idx || !x_perm || !row_of_slot || !token_of_row || !slot_of_row)
+    if (!x || !topk_idx || !(x_perm || xq) || !row_of_slot || !token_of_row || !slot_of_row)
       return MOE_ERR_INVALID_ARG;
-    if (!aligned16(x) || !aligned16(x_perm)) return MOE_ERR_INVALID_ARG;
+    if (!aligned16(x) || (x_perm && !aligned16(x_perm))) return MOE_ERR_INVALID_ARG;
   }
   const size_t need = moe::dispatch_workspace_bytes(N, desc->top_k, desc->num_experts);
   if (!ws || ws_bytes < need || (reinterpret_cast<uintptr_t>(ws) & 15u)) return MOE_ERR_WORKSPACE;
@@ -140,6 +192,8 @@ int moe_dispatch_ex(const moe_route_desc* desc, int32_t admission, const void* x
                       desc->dtype, capacity_of(desc), x, topk_idx, x_perm, row_of_slot,
                       token_of_row, slot_of_row, expert_offsets, admitted, rank_offsets,
                       rank_counts, ws, admission == MOE_ADMIT_FIRST_CHOICE ? 1 : 0};
+  a.xq = xq;
+  a.row_scale = row_scale;
   return status_of(moe::launch_dispatch(a, static_cast<hipStream_t>(stream)));
 }
 

@@ -312,6 +312,154 @@ __global__ __launch_bounds__(256) void dispatch_permute(const u32x4* __restrict_
   }
 }
 
+// INT8 payload of the dispatch exchange (EP notes, "深入推导": INT8-quantised
+// communication halves the exchange volume): the permuted rows leave as int8
+// codes with one fp32 scale per token.  One wave per token keeps the row in
+// registers (up to kQ8MaxVec 16-byte vectors per lane), takes its absmax with
+// a wave max, and makes every decision as one fp32 IEEE operation rounded to
+// nearest even (hipcc divides correctly rounded by default):
+//   inv = 127 / amax,  q = clamp(rint(x * inv), -127, 127),  scale = amax / 127
+// (a zero row gives q = 0 and scale 0).  Codes and scale go to each of the
+// token's admitted rows: x is read once, d bytes + 4 written per row.
+constexpr int kQ8MaxVec = 16;
+
+__device__ __forceinline__ uint32_t q8_code(float v, float inv) {
+  const float c = fminf(fmaxf(rintf(v * inv), -127.f), 127.f);
+  return static_cast<uint32_t>(static_cast<int32_t>(c)) & 0xffu;
+}
+
+template <int DTYPE>
+__global__ __launch_bounds__(256) void dispatch_permute_q8(const u32x4* __restrict__ x, int N,
+                                                           int vec_per_row, int k,
+                                                           const int32_t* __restrict__ row_of_slot,
+                                                           uint8_t* __restrict__ xq,
+                                                           float* __restrict__ row_scale) {
+  constexpr int EPV = DTYPE == 0 ? 4 : 8;  // elements per 16-byte vector
+  const int lane = threadIdx.x % 64;
+  const int gw = blockIdx.x * 4 + threadIdx.x / 64;
+  const int nw = gridDim.x * 4;
+  const size_t d = (size_t)vec_per_row * EPV;
+  for (int t = gw; t < N; t += nw) {
+    const int my_row = lane < k ? row_of_slot[(size_t)t * k + lane] : -1;
+    int rows[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) rows[j] = __shfl(my_row, j, 64);
+    const u32x4* src = x + (size_t)t * vec_per_row;
+    u32x4 buf[kQ8MaxVec];
+#pragma unroll
+    for (int u = 0; u < kQ8MaxVec; ++u) {
+      const int v = u * 64 + lane;
+      buf[u] = v < vec_per_row ? src[v] : u32x4{0u, 0u, 0u, 0u};
+    }
+    float amax = 0.f;
+#pragma unroll
+    for (int u = 0; u < kQ8MaxVec; ++u) {
+#pragma unroll
+      for (int c = 0; c < 4; ++c) {
+        if constexpr (DTYPE == 0) {
+          amax = fmaxf(amax, fabsf(__uint_as_float(buf[u][c])));
+        } else {
+          amax = fmaxf(amax, fabsf(__uint_as_float(buf[u][c] << 16)));
+          amax = fmaxf(amax, fabsf(__uint_as_float(buf[u][c] & 0xffff0000u)));
+        }
+      }
+    }
+    amax = wave_max(amax);
+    const float inv = amax > 0.f ? 127.f / amax : 0.f;
+    const float scale = amax > 0.f ? amax / 127.f : 0.f;
+#pragma unroll
+    for (int u = 0; u < kQ8MaxVec; ++u) {
+      const int v = u * 64 + lane;
+      if (v >= vec_per_row) continue;
+      uint32_t lo, hi = 0;
+      if constexpr (DTYPE == 0) {
+        lo = q8_code(__uint_as_float(buf[u][0]), inv) | q8_code(__uint_as_float(buf[u][1]), inv) << 8 |
+             q8_code(__uint_as_float(buf[u][2]), inv) << 16 |
+             q8_code(__uint_as_float(buf[u][3]), inv) << 24;
+      } else {
+        uint32_t w[2] = {0u, 0u};
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+          const uint32_t pair = q8_code(__uint_as_float(buf[u][c] << 16), inv) |
+                                q8_code(__uint_as_float(buf[u][c] & 0xffff0000u), inv) << 8;
+          w[c / 2] |= pair << (16 * (c % 2));
+        }
+        lo = w[0];
+        hi = w[1];
+      }
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        if (j < k && rows[j] >= 0) {
+          uint8_t* dst = xq + (size_t)rows[j] * d + (size_t)v * EPV;
+          if constexpr (DTYPE == 0) {
+            *reinterpret_cast<uint32_t*>(dst) = lo;
+          } else {
+            *reinterpret_cast<uint2*>(dst) = make_uint2(lo, hi);
+          }
+        }
+      }
+    }
+    if (lane < k && my_row >= 0) row_scale[my_row] = scale;
+  }
+}
+
+// Receiver side of the INT8 payload: x_perm[r] = dtype(q[r] * scale[r]) (fp32
+// product, then bf16 round-to-nearest-even) for r < *num_rows.  One wave per
+// row; each lane turns 8 (bf16) or 4 (fp32) codes into one 16-byte vector.
+template <int DTYPE>
+__global__ __launch_bounds__(256) void dequantize_q8(const uint8_t* __restrict__ xq,
+                                                     const float* __restrict__ row_scale,
+                                                     const int32_t* __restrict__ num_rows,
+                                                     int max_rows, int vec_per_row,
+                                                     u32x4* __restrict__ out) {
+  constexpr int EPV = DTYPE == 0 ? 4 : 8;
+  const int lane = threadIdx.x % 64;
+  const int gw = blockIdx.x * 4 + threadIdx.x / 64;
+  const int nw = gridDim.x * 4;
+  const int M = min(*num_rows, max_rows);
+  const size_t d = (size_t)vec_per_row * EPV;
+  for (int r = gw; r < M; r += nw) {
+    const float sc = row_scale[r];
+    const uint8_t* src = xq + (size_t)r * d;
+    u32x4* dst = out + (size_t)r * vec_per_row;
+    for (int v = lane; v < vec_per_row; v += 64) {
+      u32x4 o;
+      if constexpr (DTYPE == 0) {
+        const uint32_t c4 = *reinterpret_cast<const uint32_t*>(src + (size_t)v * 4);
+#pragma unroll
+        for (int c = 0; c < 4; ++c)
+          o[c] = __float_as_uint((float)(int8_t)(c4 >> (8 * c)) * sc);
+      } else {
+        const uint2 c8 = *reinterpret_cast<const uint2*>(src + (size_t)v * 8);
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+          const uint32_t word = c < 2 ? c8.x : c8.y;
+          const int sh = 16 * (c % 2);
+          o[c] = pack_bf16x2((float)(int8_t)(word >> sh) * sc, (float)(int8_t)(word >> (sh + 8)) * sc);
+        }
+      }
+      dst[v] = o;
+    }
+  }
+}
+
+int q8_max_hidden(int dtype) { return kQ8MaxVec * 64 * (dtype == 0 ? 4 : 8); }
+
+hipError_t launch_dequantize_q8(int max_rows, int d, int dtype, const void* xq,
+                                const float* row_scale, const int32_t* num_rows, void* out,
+                                hipStream_t st) {
+  if (max_rows <= 0) return hipSuccess;
+  const int vec_per_row = d * (dtype == 0 ? 4 : 2) / 16;
+  const int blocks = std::max(1, std::min((max_rows + 3) / 4, 8192));
+  if (dtype == 0)
+    dequantize_q8<0><<<blocks, 256, 0, st>>>(static_cast<const uint8_t*>(xq), row_scale, num_rows,
+                                              max_rows, vec_per_row, static_cast<u32x4*>(out));
+  else
+    dequantize_q8<1><<<blocks, 256, 0, st>>>(static_cast<const uint8_t*>(xq), row_scale, num_rows,
+                                              max_rows, vec_per_row, static_cast<u32x4*>(out));
+  return hipGetLastError();
+}
+
 size_t dispatch_workspace_bytes(int N, int k, int E) {
   const size_t S = (size_t)N * k;
   const size_t tiles = (S + kTileSlots - 1) / kTileSlots;
@@ -343,8 +491,19 @@ hipError_t launch_dispatch(const DispatchArgs& a, hipStream_t st) {
   const int vec_per_row = a.d * elem / 16;
   const int waves_needed = a.N;
   const int blocks = std::max(1, std::min((waves_needed + 3) / 4, 8192));
-  dispatch_permute<<<blocks, 256, 0, st>>>(static_cast<const u32x4*>(a.x), a.N, vec_per_row, a.k,
-                                           a.row_of_slot, static_cast<u32x4*>(a.x_perm));
+  if (a.xq) {
+    if (a.dtype == 0)
+      dispatch_permute_q8<0><<<blocks, 256, 0, st>>>(static_cast<const u32x4*>(a.x), a.N,
+                                                     vec_per_row, a.k, a.row_of_slot,
+                                                     static_cast<uint8_t*>(a.xq), a.row_scale);
+    else
+      dispatch_permute_q8<1><<<blocks, 256, 0, st>>>(static_cast<const u32x4*>(a.x), a.N,
+                                                     vec_per_row, a.k, a.row_of_slot,
+                                                     static_cast<uint8_t*>(a.xq), a.row_scale);
+  } else {
+    dispatch_permute<<<blocks, 256, 0, st>>>(static_cast<const u32x4*>(a.x), a.N, vec_per_row,
+                                             a.k, a.row_of_slot, static_cast<u32x4*>(a.x_perm));
+  }
   return hipGetLastError();
 }
 

@@ -48,7 +48,16 @@ struct DispatchArgs {
   int32_t* rank_counts;
   void* ws;
   int first_choice;  // 0: token order; 1: every token's slot j before any slot j + 1
+  void* xq = nullptr;          // INT8 payload rows [N*k, d] (x_perm unused when set)
+  float* row_scale = nullptr;  // one scale per payload row
 };
+
+// INT8 payload: the largest hidden size the register-resident quantiser takes,
+// and the receiver-side dequantisation of rows < *num_rows.
+int q8_max_hidden(int dtype);
+hipError_t launch_dequantize_q8(int max_rows, int d, int dtype, const void* xq,
+                                const float* row_scale, const int32_t* num_rows, void* out,
+                                hipStream_t st);
 
 size_t dispatch_workspace_bytes(int N, int k, int E);
 hipError_t launch_dispatch(const DispatchArgs& a, hipStream_t st);

@@ -12,7 +12,8 @@ from __future__ import annotations
 import torch
 
 from . import (ACT, DTYPE, TORCH_DTYPE, desc_from_workload, moe_bias_update, moe_combine,
-               moe_dispatch, moe_dispatch_ex, moe_dispatch_workspace_size, moe_expert_ffn,
+               moe_dequantize_q8, moe_dispatch, moe_dispatch_ex, moe_dispatch_q8,
+               moe_dispatch_workspace_size, moe_expert_ffn,
                moe_expert_ffn_pack_weights, moe_expert_ffn_workspace_size, moe_route,
                moe_route_workspace_size, workspace)
 
@@ -60,6 +61,12 @@ class MoeBuffers:
         self.counts = torch.empty(E, **i32)
         self.ws_route = workspace(moe_route_workspace_size(d), device)
         self.x_perm = torch.empty(max(S, 1), dim, dtype=dt, device=device)
+        # INT8 row payload of the dispatch exchange (workloads with
+        # payload="int8"): codes and one scale per row, dequantised into x_perm.
+        self.x_perm_q = self.row_scale = None
+        if cfg.get("payload", "native") == "int8":
+            self.x_perm_q = torch.empty(max(S, 1), dim, dtype=torch.int8, device=device)
+            self.row_scale = torch.empty(max(S, 1), dtype=torch.float32, device=device)
         self.row_of_slot = torch.empty(N, k, **i32)
         self.token_of_row = torch.empty(max(S, 1), **i32)
         self.slot_of_row = torch.empty(max(S, 1), dtype=torch.int8, device=device)
@@ -92,9 +99,17 @@ def route(buf: MoeBuffers, inp: dict, sel_bias=None, stream=None):
 
 def dispatch(buf: MoeBuffers, inp: dict, stream=None):
     """Admission in token order unless the workload sets ``admission`` to
-    ``"first_choice"``."""
+    ``"first_choice"``.  With ``payload="int8"`` the rows travel as the INT8
+    payload and are dequantised into x_perm (what a receiving rank does)."""
     adm = buf.cfg.get("admission", "token")
-    if adm == "token":
+    if buf.x_perm_q is not None:
+        d = buf.desc
+        moe_dispatch_q8(d, adm, inp["x"], buf.topk_idx, buf.x_perm_q, buf.row_scale,
+                        buf.row_of_slot, buf.token_of_row, buf.slot_of_row, buf.expert_offsets,
+                        buf.admitted, buf.rank_offsets, buf.rank_counts, buf.ws_dispatch, stream)
+        moe_dequantize_q8(d.num_tokens * d.top_k, d.hidden, d.dtype, buf.x_perm_q, buf.row_scale,
+                          buf.expert_offsets[d.num_experts:], buf.x_perm, stream)
+    elif adm == "token":
         moe_dispatch(buf.desc, inp["x"], buf.topk_idx, buf.x_perm, buf.row_of_slot,
                      buf.token_of_row, buf.slot_of_row, buf.expert_offsets, buf.admitted,
                      buf.rank_offsets, buf.rank_counts, buf.ws_dispatch, stream)

@@ -10,7 +10,8 @@
  *                    selection-only bias), combine weights, per-expert counts
  *   moe_dispatch     capacity, token-order admission, expert- and
  *                    rank-contiguous row layout, permuted hidden states
- *                    (moe_dispatch_ex: also first-choice-first admission)
+ *                    (moe_dispatch_ex: also first-choice-first admission;
+ *                    moe_dispatch_q8 / moe_dequantize_q8: INT8 row payload)
  *   moe_expert_ffn   every expert's FFN over its rows as one grouped GEMM pair
  *                    (bf16 weights packed once by moe_expert_ffn_pack_weights)
  *   moe_combine      weighted sum back to token order, plus residual and an
@@ -199,6 +200,35 @@ int moe_dispatch_ex(const moe_route_desc* desc, int32_t admission, const void* x
                     int32_t* token_of_row, int8_t* slot_of_row, int32_t* expert_offsets,
                     int32_t* admitted, int32_t* rank_offsets, int32_t* rank_counts,
                     void* ws, size_t ws_bytes, void* stream);
+
+/* INT8 payload of the dispatch exchange.  EP notes, "深入推导" (DeepSeek-V3's EP
+ * configuration): INT8-quantised communication halves the exchange volume.  The
+ * pages give no scheme; this is one symmetric scale per token row, each
+ * decision an fp32 IEEE operation rounded to nearest even:
+ *   amax = max_i |x_ti|;  inv = 127 / amax;  q_ti = clamp(rint(x_ti * inv), -127, 127);
+ *   scale_t = amax / 127   (a row of zeros: q = 0, scale = 0).
+ * moe_dispatch_q8 is moe_dispatch_ex (same arguments, outputs, workspace and
+ * errors) except that the permuted rows are written as that payload instead of
+ * dtype rows:
+ *  x_perm_q   [N*k, d]  int8   out: row r holds the codes of x[token_of_row[r]]
+ *                              (rows >= M untouched); 16-byte aligned
+ *  row_scale  [N*k]     fp32   out: its scale (entries >= M untouched)
+ * x is read once per token.  Returns MOE_ERR_UNSUPPORTED when d exceeds 8192
+ * (bf16) / 4096 (fp32), the row a wave keeps in registers. */
+int moe_dispatch_q8(const moe_route_desc* desc, int32_t admission, const void* x,
+                    const int32_t* topk_idx, int8_t* x_perm_q, float* row_scale,
+                    int32_t* row_of_slot, int32_t* token_of_row, int8_t* slot_of_row,
+                    int32_t* expert_offsets, int32_t* admitted, int32_t* rank_offsets,
+                    int32_t* rank_counts, void* ws, size_t ws_bytes, void* stream);
+
+/* Receiver side of the INT8 payload: x_perm[r, i] = q[r, i] * row_scale[r] as an
+ * fp32 product, rounded to dtype (bf16: nearest even), for r < min(*num_rows,
+ * max_rows).  num_rows is a DEVICE pointer (for the layer: &expert_offsets[E]),
+ * so the row count never has to reach the host.  x_perm_q and x_perm
+ * 16-byte aligned; d % 8 == 0 (else MOE_ERR_UNSUPPORTED). */
+int moe_dequantize_q8(int32_t max_rows, int32_t hidden, int32_t dtype, const int8_t* x_perm_q,
+                      const float* row_scale, const int32_t* num_rows, void* x_perm,
+                      void* stream);
 
 /* ------------------------------------------------------------- expert FFN -- */
 

@@ -19,7 +19,7 @@ FAKE = ctypes.c_void_p(0x10000)  # aligned, never dereferenced (validation fails
 def declared_functions():
     text = open(HEADER).read()
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-    return sorted(set(re.findall(r"\b(moe_[a-z_]+)\s*\(", text)))
+    return sorted(set(re.findall(r"\b(moe_[a-z0-9_]+)\s*\(", text)))
 
 
 def test_header_declares_the_boundary():
@@ -131,6 +131,47 @@ def test_dispatch_ex_validation():
         args2[2] = None  # x_perm
         assert lib.moe_dispatch_ex(ctypes.byref(d), adm, *args2, FAKE, need,
                                    None) == moe.MOE_ERR_INVALID_ARG
+
+
+def test_dispatch_q8_validation():
+    """moe_dispatch_q8 checks what moe_dispatch_ex checks, plus its payload
+    buffers and the largest row a wave quantises in registers."""
+    lib = moe.lib()
+    d = moe.route_desc(64, 64, 8, 2, R=4, cf=1.25)
+    need = moe.moe_dispatch_workspace_size(d)
+    rest = [FAKE] * 7  # row_of_slot .. rank_counts
+
+    def call(desc, adm=0, xq=FAKE, sc=FAKE, ws_bytes=need):
+        return lib.moe_dispatch_q8(ctypes.byref(desc), adm, FAKE, FAKE, xq, sc, *rest, FAKE,
+                                   ws_bytes, None)
+    assert call(d, xq=None) == moe.MOE_ERR_INVALID_ARG
+    assert call(d, sc=None) == moe.MOE_ERR_INVALID_ARG
+    assert call(d, xq=ctypes.c_void_p(0x10008)) == moe.MOE_ERR_INVALID_ARG       # 16-byte alignment
+    assert call(d, sc=ctypes.c_void_p(0x10002)) == moe.MOE_ERR_INVALID_ARG       # 4-byte alignment
+    assert call(d, adm=5) == moe.MOE_ERR_INVALID_ARG
+    assert call(d, ws_bytes=need - 4) == moe.MOE_ERR_WORKSPACE
+    assert call(moe.route_desc(64, 8200, 8, 2)) == moe.MOE_ERR_UNSUPPORTED  # > 8192 bf16
+    f32 = moe.route_desc(64, 4104, 8, 2)
+    f32.dtype = moe.MOE_F32
+    assert call(f32) == moe.MOE_ERR_UNSUPPORTED                   # > 4096 fp32
+
+
+def test_dequantize_q8_validation():
+    lib = moe.lib()
+    ok = dict(M=16, d=64, dt=moe.MOE_BF16, q=FAKE, s=FAKE, n=FAKE, out=FAKE)
+
+    def call(**kw):
+        a = dict(ok, **kw)
+        return lib.moe_dequantize_q8(a["M"], a["d"], a["dt"], a["q"], a["s"], a["n"], a["out"],
+                                     None)
+    assert call(M=-1) == moe.MOE_ERR_INVALID_ARG
+    assert call(dt=7) == moe.MOE_ERR_INVALID_ARG
+    assert call(d=60) == moe.MOE_ERR_UNSUPPORTED
+    for key in ("q", "s", "n", "out"):
+        assert call(**{key: None}) == moe.MOE_ERR_INVALID_ARG
+    assert call(q=ctypes.c_void_p(0x10008)) == moe.MOE_ERR_INVALID_ARG
+    assert call(out=ctypes.c_void_p(0x10004)) == moe.MOE_ERR_INVALID_ARG
+    assert call(M=0, q=None, s=None, n=None, out=None) == moe.MOE_OK  # nothing to do
 
 
 def test_expert_ffn_validation():

@@ -33,6 +33,9 @@ CASES = {
     "zipf-small-cf2.0": W.with_(W.small("zipf"), cf=2.0),
     # GShard's top-2 router: first choices fill the capacity before second ones.
     "zipf-small-cf1.0-first-choice": W.with_(W.small("zipf"), cf=1.0, admission="first_choice"),
+    # Rows travel as the INT8 payload and are dequantised before the FFN.
+    "switch-small-int8": W.with_(W.small("switch"), payload="int8"),
+    "toy-small-int8": W.with_(W.small("toy"), payload="int8"),
 }
 
 _cache = {}
@@ -331,6 +334,50 @@ def test_dispatch_first_choice_bit_exact(N, E, k, cf):
     if k > 1 and cf > 0:
         assert not np.array_equal(dsp["row_of_slot"], tok["row_of_slot"]), \
             "the case should tell the two walks apart"
+
+
+@pytest.mark.parametrize("N,d,dtype,E,k", [
+    (3001, 1024, "bf16", 64, 1),    # Switch-like rows, 2 vectors per lane
+    (517, 7168, "bf16", 256, 8),    # DeepSeek-like rows, 14 vectors per lane
+    (64, 8192, "bf16", 8, 2),       # the widest bf16 row a wave keeps in registers
+    (1001, 1000, "bf16", 16, 3),    # ragged: 125 vectors per row
+    (1001, 512, "fp32", 8, 2),      # fp32 rows, 4 codes per vector
+    (77, 4096, "fp32", 8, 2),       # the widest fp32 row
+])
+def test_dispatch_q8_codes_bit_exact(N, d, dtype, E, k):
+    """moe_dispatch_q8 and moe_dequantize_q8 against the oracle's INT8 payload:
+    codes, scales and dequantised rows bit for bit, the layout as moe_dispatch.
+    Rows include zeros, a single spike, exact halves of the step and wide
+    dynamic range."""
+    cfg = W.with_(W.small("switch"), N=N, d=d, E=E, k=k, R=min(E, 8), cf=1.25, dtype=dtype,
+                  payload="int8")
+    print(f"[dispatch q8] N={N} d={d} {dtype} E={E} k={k}", flush=True)
+    g = torch.Generator().manual_seed(N + d)
+    x = torch.randn(N, d, generator=g) * torch.exp(torch.randn(N, 1, generator=g) * 3)
+    x[0] = 0.0                                   # zero row: codes 0, scale 0
+    x[1] = 0.0
+    x[1, d // 3] = -5.0                          # one spike: -127 there, 0 elsewhere
+    x[2] = torch.arange(d) % 7 - 3.5             # a coarse grid with amax 3.5
+    x[3, :8] = torch.tensor([127.0, 0.5, 1.5, 2.5, -0.5, -1.5, 126.5, -126.5])
+    x[3, 8:] = 0.0
+    x = x.to(W.torch_dtype(cfg))
+    rng = np.random.default_rng(N)
+    ids = np.stack([rng.choice(E, size=k, replace=False) for _ in range(N)]).astype(np.int32)
+    buf = moe.MoeBuffers(cfg)
+    buf.topk_idx.copy_(torch.from_numpy(ids))
+    layer.dispatch(buf, {"x": x.cuda()})
+    torch.cuda.synchronize()
+    dsp = oracle.dispatch(cfg, ids)
+    for key in ("row_of_slot", "token_of_row", "slot_of_row", "expert_offsets", "admitted"):
+        assert np.array_equal(getattr(buf, key).cpu().numpy(), dsp[key]), key
+    M = dsp["num_rows"]
+    q, sc = oracle.quantize_rows_q8(dtype, n(x))
+    tor = dsp["token_of_row"][:M]
+    assert np.array_equal(buf.x_perm_q[:M].cpu().numpy(), q[tor])
+    assert np.array_equal(bits(buf.row_scale[:M]), sc[tor].view(np.int32))
+    want = oracle.dequantize_rows_q8(dtype, q[tor], sc[tor])
+    assert np.array_equal(bits(buf.x_perm[:M]), bits(as_tensor(want, dtype)))
+    assert (q[1] == 0).sum() == d - 1 and q[1, d // 3] == -127 and sc[0] == 0.0
 
 
 def test_all_tokens_to_one_expert_with_capacity():
