@@ -315,9 +315,10 @@ __global__ __launch_bounds__(256) void dispatch_permute(const u32x4* __restrict_
 // INT8 payload of the dispatch exchange (EP notes, "深入推导": INT8-quantised
 // communication halves the exchange volume): the permuted rows leave as int8
 // codes with one fp32 scale per token.  One wave per token keeps the row in
-// registers (up to kQ8MaxVec 16-byte vectors per lane), takes its absmax with
-// a wave max, and makes every decision as one fp32 IEEE operation rounded to
-// nearest even (hipcc divides correctly rounded by default):
+// registers (VPL 16-byte vectors per lane, a power of two up to kQ8MaxVec,
+// chosen from d), takes its absmax with a wave max, and makes every decision
+// as one fp32 IEEE operation rounded to nearest even (hipcc divides correctly
+// rounded by default):
 //   inv = 127 / amax,  q = clamp(rint(x * inv), -127, 127),  scale = amax / 127
 // (a zero row gives q = 0 and scale 0).  Codes and scale go to each of the
 // token's admitted rows: x is read once, d bytes + 4 written per row.
@@ -328,32 +329,29 @@ __device__ __forceinline__ uint32_t q8_code(float v, float inv) {
   return static_cast<uint32_t>(static_cast<int32_t>(c)) & 0xffu;
 }
 
-template <int DTYPE>
+template <int DTYPE, int VPL>
 __global__ __launch_bounds__(256) void dispatch_permute_q8(const u32x4* __restrict__ x, int N,
                                                            int vec_per_row, int k,
                                                            const int32_t* __restrict__ row_of_slot,
                                                            uint8_t* __restrict__ xq,
                                                            float* __restrict__ row_scale) {
-  constexpr int EPV = DTYPE == 0 ? 4 : 8;  // elements per 16-byte vector
+  constexpr int EPV = DTYPE == 0 ? 4 : 8;  // elements (= code bytes) per 16-byte vector
   const int lane = threadIdx.x % 64;
   const int gw = blockIdx.x * 4 + threadIdx.x / 64;
   const int nw = gridDim.x * 4;
   const size_t d = (size_t)vec_per_row * EPV;
   for (int t = gw; t < N; t += nw) {
     const int my_row = lane < k ? row_of_slot[(size_t)t * k + lane] : -1;
-    int rows[8];
-#pragma unroll
-    for (int j = 0; j < 8; ++j) rows[j] = __shfl(my_row, j, 64);
     const u32x4* src = x + (size_t)t * vec_per_row;
-    u32x4 buf[kQ8MaxVec];
+    u32x4 buf[VPL];
 #pragma unroll
-    for (int u = 0; u < kQ8MaxVec; ++u) {
+    for (int u = 0; u < VPL; ++u) {
       const int v = u * 64 + lane;
       buf[u] = v < vec_per_row ? src[v] : u32x4{0u, 0u, 0u, 0u};
     }
     float amax = 0.f;
 #pragma unroll
-    for (int u = 0; u < kQ8MaxVec; ++u) {
+    for (int u = 0; u < VPL; ++u) {
 #pragma unroll
       for (int c = 0; c < 4; ++c) {
         if constexpr (DTYPE == 0) {
@@ -367,15 +365,16 @@ __global__ __launch_bounds__(256) void dispatch_permute_q8(const u32x4* __restri
     amax = wave_max(amax);
     const float inv = amax > 0.f ? 127.f / amax : 0.f;
     const float scale = amax > 0.f ? amax / 127.f : 0.f;
+    // Codes of this lane's vectors: 4 (fp32) or 8 (bf16) bytes each.
+    uint32_t lo[VPL], hi[VPL];
 #pragma unroll
-    for (int u = 0; u < kQ8MaxVec; ++u) {
-      const int v = u * 64 + lane;
-      if (v >= vec_per_row) continue;
-      uint32_t lo, hi = 0;
+    for (int u = 0; u < VPL; ++u) {
       if constexpr (DTYPE == 0) {
-        lo = q8_code(__uint_as_float(buf[u][0]), inv) | q8_code(__uint_as_float(buf[u][1]), inv) << 8 |
-             q8_code(__uint_as_float(buf[u][2]), inv) << 16 |
-             q8_code(__uint_as_float(buf[u][3]), inv) << 24;
+        lo[u] = q8_code(__uint_as_float(buf[u][0]), inv) |
+                q8_code(__uint_as_float(buf[u][1]), inv) << 8 |
+                q8_code(__uint_as_float(buf[u][2]), inv) << 16 |
+                q8_code(__uint_as_float(buf[u][3]), inv) << 24;
+        hi[u] = 0;
       } else {
         uint32_t w[2] = {0u, 0u};
 #pragma unroll
@@ -384,18 +383,22 @@ __global__ __launch_bounds__(256) void dispatch_permute_q8(const u32x4* __restri
                                 q8_code(__uint_as_float(buf[u][c] & 0xffff0000u), inv) << 8;
           w[c / 2] |= pair << (16 * (c % 2));
         }
-        lo = w[0];
-        hi = w[1];
+        lo[u] = w[0];
+        hi[u] = w[1];
       }
+    }
+    // Each admitted row: one base address, the lane's vectors at fixed offsets.
+    for (int j = 0; j < k; ++j) {
+      const int r = __shfl(my_row, j, 64);  // uniform
+      if (r < 0) continue;
+      uint8_t* base = xq + (size_t)r * d + (size_t)lane * EPV;
 #pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        if (j < k && rows[j] >= 0) {
-          uint8_t* dst = xq + (size_t)rows[j] * d + (size_t)v * EPV;
-          if constexpr (DTYPE == 0) {
-            *reinterpret_cast<uint32_t*>(dst) = lo;
-          } else {
-            *reinterpret_cast<uint2*>(dst) = make_uint2(lo, hi);
-          }
+      for (int u = 0; u < VPL; ++u) {
+        if (u * 64 + lane < vec_per_row) {
+          if constexpr (DTYPE == 0)
+            *reinterpret_cast<uint32_t*>(base + u * 64 * EPV) = lo[u];
+          else
+            *reinterpret_cast<uint2*>(base + u * 64 * EPV) = make_uint2(lo[u], hi[u]);
         }
       }
     }
@@ -492,14 +495,25 @@ hipError_t launch_dispatch(const DispatchArgs& a, hipStream_t st) {
   const int waves_needed = a.N;
   const int blocks = std::max(1, std::min((waves_needed + 3) / 4, 8192));
   if (a.xq) {
-    if (a.dtype == 0)
-      dispatch_permute_q8<0><<<blocks, 256, 0, st>>>(static_cast<const u32x4*>(a.x), a.N,
-                                                     vec_per_row, a.k, a.row_of_slot,
-                                                     static_cast<uint8_t*>(a.xq), a.row_scale);
-    else
-      dispatch_permute_q8<1><<<blocks, 256, 0, st>>>(static_cast<const u32x4*>(a.x), a.N,
-                                                     vec_per_row, a.k, a.row_of_slot,
-                                                     static_cast<uint8_t*>(a.xq), a.row_scale);
+    // Vectors per lane the row needs, rounded up to a power of two (<= kQ8MaxVec).
+    const int vpl = (vec_per_row + 63) / 64;
+    auto go = [&](auto kernel) {
+      kernel<<<blocks, 256, 0, st>>>(static_cast<const u32x4*>(a.x), a.N, vec_per_row, a.k,
+                                     a.row_of_slot, static_cast<uint8_t*>(a.xq), a.row_scale);
+    };
+    if (a.dtype == 0) {
+      if (vpl <= 1) go(dispatch_permute_q8<0, 1>);
+      else if (vpl <= 2) go(dispatch_permute_q8<0, 2>);
+      else if (vpl <= 4) go(dispatch_permute_q8<0, 4>);
+      else if (vpl <= 8) go(dispatch_permute_q8<0, 8>);
+      else go(dispatch_permute_q8<0, 16>);
+    } else {
+      if (vpl <= 1) go(dispatch_permute_q8<1, 1>);
+      else if (vpl <= 2) go(dispatch_permute_q8<1, 2>);
+      else if (vpl <= 4) go(dispatch_permute_q8<1, 4>);
+      else if (vpl <= 8) go(dispatch_permute_q8<1, 8>);
+      else go(dispatch_permute_q8<1, 16>);
+    }
   } else {
     dispatch_permute<<<blocks, 256, 0, st>>>(static_cast<const u32x4*>(a.x), a.N, vec_per_row,
                                              a.k, a.row_of_slot, static_cast<u32x4*>(a.x_perm));
