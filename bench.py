@@ -286,7 +286,13 @@ def main():
     # forked onto a side stream at the start of the step and joined before
     # the combine, as the layer's forward does; it is timed by its own pair
     # of events on that stream.
-    calls = ["route", "dispatch", "ffn_plan", "ffn_up", "ffn_down", "combine", "bias_update"]
+    # Dispatch runs as its two halves (moe_dispatch_layout, then moe_permute or
+    # the INT8 payload's moe_permute_q8 + moe_dequantize_q8): the same kernels
+    # in the same order as one moe_dispatch call, timed apart.
+    q8 = buf.x_perm_q is not None
+    adm = cfg.get("admission", "token")
+    calls = (["route", "dispatch_layout", "permute"] + (["dequantize"] if q8 else [])
+             + ["ffn_plan", "ffn_up", "ffn_down", "combine", "bias_update"])
     fork = layer.has_shared(buf, wts)
     main = torch.cuda.current_stream()
 
@@ -301,26 +307,45 @@ def main():
             layer.shared_ffn(buf, wts, buf.side_stream)
             if shared_events is not None:
                 shared_events[1].record(buf.side_stream)
-        mark(0)
+        i = 0
+        mark(i)
         layer.route(buf, inp)
-        mark(1)
-        layer.dispatch(buf, inp)
-        mark(2)
+        i += 1
+        mark(i)
+        moe.moe_dispatch_layout(d, adm, buf.topk_idx, buf.row_of_slot, buf.token_of_row,
+                                buf.slot_of_row, buf.expert_offsets, buf.admitted,
+                                buf.rank_offsets, buf.rank_counts, buf.ws_dispatch)
+        i += 1
+        mark(i)
+        if q8:
+            moe.moe_permute_q8(d, inp["x"], buf.row_of_slot, buf.x_perm_q, buf.row_scale)
+            i += 1
+            mark(i)
+            moe.moe_dequantize_q8(S, dim, cfg["dtype"], buf.x_perm_q, buf.row_scale,
+                                  buf.expert_offsets[E:], buf.x_perm)
+        else:
+            moe.moe_permute(d, inp["x"], buf.row_of_slot, buf.x_perm)
+        i += 1
+        mark(i)
         moe.moe_expert_ffn_plan(E, S, dim, h, cfg["act"], cfg["dtype"], buf.expert_offsets,
                                 buf.ws_ffn)
-        mark(3)
+        i += 1
+        mark(i)
         moe.moe_expert_ffn_up(E, S, dim, h, cfg["act"], cfg["dtype"], buf.x_perm,
                               buf.expert_offsets, wts["w1"], wts.get("w3"), buf.ws_ffn)
-        mark(4)
+        i += 1
+        mark(i)
         moe.moe_expert_ffn_down(E, S, dim, h, cfg["act"], cfg["dtype"], buf.expert_offsets,
                                 wts["w2"], buf.y_perm, buf.ws_ffn)
-        mark(5)
+        i += 1
+        mark(i)
         if fork:
             main.wait_stream(buf.side_stream)
         layer.combine(buf, inp, residual=True)
-        mark(6)
+        i += 1
+        mark(i)
         layer.bias_update(buf, bias_state, step_bias)
-        mark(7)
+        mark(i + 1)
 
     for _ in range(args.warmup):
         step()
@@ -415,7 +440,13 @@ def main():
     up_bytes = (active * mats_up * h * dim + M * dim + M * h) * es
     down_flops = 2.0 * M * h * dim
     down_bytes = (active * dim * h + M * h + M * dim) * es
-    dispatch_bytes = S * 4 + N * dim * es + M * dim * es + S * 4 + 2 * S * 4 + S
+    # dispatch layout: ids read, row_of_slot + token_of_row + slot_of_row written
+    layout_bytes = S * 4 + S * 4 + S * 4 + S
+    # permute: x read once, every admitted row written (INT8 payload: d bytes + a
+    # 4-byte scale per row), row_of_slot read; dequantisation reads the payload
+    # back and writes dtype rows
+    permute_bytes = N * dim * es + (M * (dim + 4) if q8 else M * dim * es) + S * 4
+    dequant_bytes = M * (dim + 4) + M * dim * es
     combine_bytes = M * dim * es + N * dim * es + N * dim * es + S * 8
     route_bytes = N * dim * es + E * dim * es + N * E * 4 + S * 8
     peak = MFMA_PEAK_TFLOPS[cfg["dtype"]]
@@ -432,18 +463,23 @@ def main():
         "ffn_up": roof("ffn_up", up_flops, up_bytes),
         "ffn_down": roof("ffn_down", down_flops, down_bytes),
     }
-    for name, nbytes in [("route", route_bytes), ("dispatch", dispatch_bytes),
-                         ("combine", combine_bytes)]:
+    hbm_calls = [("route", route_bytes), ("dispatch_layout", layout_bytes),
+                 ("permute", permute_bytes), ("combine", combine_bytes)]
+    if q8:
+        hbm_calls.append(("dequantize", dequant_bytes))
+    for name, nbytes in hbm_calls:
         t = per_call[name] * 1e-6
         kern[name] = {"us": round(per_call[name], 2), "gbs": round(nbytes / t / 1e9, 1),
                       "hbm_frac": round(nbytes / t / (HBM_PEAK_GBS * 1e9), 4)}
+    kern["dispatch"] = {"us": round(sum(per_call[c] for c in
+                                        ("dispatch_layout", "permute", "dequantize")
+                                        if c in per_call), 2)}
     for name in per_call:
         kern.setdefault(name, {"us": round(per_call[name], 2)})
     cold = {"ms_per_step_with_per_call_events": round(cold_step_ms, 4), "steps": n_cold,
             "ffn_up": roof("ffn_up", up_flops, up_bytes, cold_call),
             "ffn_down": roof("ffn_down", down_flops, down_bytes, cold_call)}
-    for name, nbytes in [("route", route_bytes), ("dispatch", dispatch_bytes),
-                         ("combine", combine_bytes)]:
+    for name, nbytes in hbm_calls:
         cold[name] = {"us": round(cold_call[name], 2),
                       "hbm_frac": round(nbytes / (cold_call[name] * 1e-6) / (HBM_PEAK_GBS * 1e9), 4)}
     for name in cold_call:
@@ -481,7 +517,7 @@ def main():
         "roofline": roofline,
         "grouped_gemm_mfma_frac": {"up": kern["ffn_up"]["mfma_frac"],
                                    "down": kern["ffn_down"]["mfma_frac"]},
-        "permute_hbm_frac": kern["dispatch"]["hbm_frac"],
+        "permute_hbm_frac": kern["permute"]["hbm_frac"],
         "kernels": kern,
         "ms_per_step_with_per_call_events": round(instrumented_ms, 4),
         "step_ms_p10_p50_p90": [round(pct(step_ms, q), 4) for q in (0.1, 0.5, 0.9)],

@@ -39,7 +39,7 @@ TORCH_DTYPE = {MOE_F32: torch.float32, MOE_BF16: torch.bfloat16}
 EXPORTS = [
     "moe_route_workspace_size", "moe_route", "moe_router_logits",
     "moe_dispatch_workspace_size", "moe_dispatch", "moe_dispatch_ex", "moe_dispatch_q8",
-    "moe_dequantize_q8",
+    "moe_dequantize_q8", "moe_dispatch_layout", "moe_permute", "moe_permute_q8",
     "moe_expert_ffn_workspace_size", "moe_expert_ffn", "moe_expert_ffn_plan",
     "moe_expert_ffn_up", "moe_expert_ffn_down", "moe_expert_ffn_pack_weights", "moe_combine",
     "moe_bias_update", "moe_status_string",
@@ -103,6 +103,9 @@ def lib() -> ctypes.CDLL:
             "moe_dispatch_ex": ([D, I32, P, P, P, P, P, P, P, P, P, P, P, SZ, P], I32),
             "moe_dispatch_q8": ([D, I32, P, P, P, P, P, P, P, P, P, P, P, P, SZ, P], I32),
             "moe_dequantize_q8": ([I32, I32, I32, P, P, P, P, P], I32),
+            "moe_dispatch_layout": ([D, I32, P, P, P, P, P, P, P, P, P, SZ, P], I32),
+            "moe_permute": ([D, P, P, P, P], I32),
+            "moe_permute_q8": ([D, P, P, P, P, P], I32),
             "moe_expert_ffn_workspace_size": ([I32, I32, I32, I32, I32, I32], SZ),
             "moe_expert_ffn": ([I32, I32, I32, I32, I32, I32, P, P, P, P, P, P, P, SZ, P], I32),
             "moe_expert_ffn_plan": ([I32, I32, I32, I32, I32, I32, P, P, SZ, P], I32),
@@ -247,6 +250,48 @@ def moe_dispatch_q8(desc, admission, x, topk_idx, x_perm_q, row_scale, row_of_sl
         _ptr(ws, "ws", None, None, False), 0 if ws is None else ws.numel() * ws.element_size(),
         _stream(stream))
     _raise("moe_dispatch_q8", st)
+
+
+def moe_dispatch_layout(desc, admission, topk_idx, row_of_slot, token_of_row, slot_of_row,
+                        expert_offsets, admitted, rank_offsets, rank_counts, ws, stream=None):
+    """The layout half of moe_dispatch_ex (no rows are moved)."""
+    adm = ADMISSION[admission] if isinstance(admission, str) else int(admission)
+    N, E, k, R = desc.num_tokens, desc.num_experts, desc.top_k, desc.num_ranks
+    S = N * k
+    st = lib().moe_dispatch_layout(
+        ctypes.byref(desc), adm, _ptr(topk_idx, "topk_idx", torch.int32, S, N > 0),
+        _ptr(row_of_slot, "row_of_slot", torch.int32, S, N > 0),
+        _ptr(token_of_row, "token_of_row", torch.int32, S, N > 0),
+        _ptr(slot_of_row, "slot_of_row", torch.int8, S, N > 0),
+        _ptr(expert_offsets, "expert_offsets", torch.int32, E + 1),
+        _ptr(admitted, "admitted", torch.int32, E),
+        _ptr(rank_offsets, "rank_offsets", torch.int32, R + 1),
+        _ptr(rank_counts, "rank_counts", torch.int32, R),
+        _ptr(ws, "ws", None, None, False), 0 if ws is None else ws.numel() * ws.element_size(),
+        _stream(stream))
+    _raise("moe_dispatch_layout", st)
+
+
+def moe_permute(desc, x, row_of_slot, x_perm, stream=None):
+    """The permute half of moe_dispatch: x_perm[row_of_slot[t, j]] = x[t]."""
+    N, d, k = desc.num_tokens, desc.hidden, desc.top_k
+    dt = TORCH_DTYPE.get(desc.dtype)
+    st = lib().moe_permute(ctypes.byref(desc), _ptr(x, "x", dt, N * d, N > 0),
+                           _ptr(row_of_slot, "row_of_slot", torch.int32, N * k, N > 0),
+                           _ptr(x_perm, "x_perm", dt, N * k * d, N > 0), _stream(stream))
+    _raise("moe_permute", st)
+
+
+def moe_permute_q8(desc, x, row_of_slot, x_perm_q, row_scale, stream=None):
+    """The permute half of moe_dispatch_q8 (INT8 payload rows and scales)."""
+    N, d, k = desc.num_tokens, desc.hidden, desc.top_k
+    dt = TORCH_DTYPE.get(desc.dtype)
+    st = lib().moe_permute_q8(ctypes.byref(desc), _ptr(x, "x", dt, N * d, N > 0),
+                              _ptr(row_of_slot, "row_of_slot", torch.int32, N * k, N > 0),
+                              _ptr(x_perm_q, "x_perm_q", torch.int8, N * k * d, N > 0),
+                              _ptr(row_scale, "row_scale", torch.float32, N * k, N > 0),
+                              _stream(stream))
+    _raise("moe_permute_q8", st)
 
 
 def moe_dequantize_q8(max_rows, hidden, dtype, x_perm_q, row_scale, num_rows, x_perm,

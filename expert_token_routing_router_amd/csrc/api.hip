@@ -124,7 +124,8 @@ static int dispatch_common(const moe_route_desc* desc, int32_t admission, const 
                            const int32_t* topk_idx, void* x_perm, int8_t* xq, float* row_scale,
                            int32_t* row_of_slot, int32_t* token_of_row, int8_t* slot_of_row,
                            int32_t* expert_offsets, int32_t* admitted, int32_t* rank_offsets,
-                           int32_t* rank_counts, void* ws, size_t ws_bytes, void* stream);
+                           int32_t* rank_counts, void* ws, size_t ws_bytes, void* stream,
+                           int stages = moe::kDispatchLayout | moe::kDispatchPermute);
 
 int moe_dispatch_ex(const moe_route_desc* desc, int32_t admission, const void* x,
                     const int32_t* topk_idx, void* x_perm, int32_t* row_of_slot,
@@ -174,27 +175,67 @@ static int dispatch_common(const moe_route_desc* desc, int32_t admission, const 
                            const int32_t* topk_idx, void* x_perm, int8_t* xq, float* row_scale,
                            int32_t* row_of_slot, int32_t* token_of_row, int8_t* slot_of_row,
                            int32_t* expert_offsets, int32_t* admitted, int32_t* rank_offsets,
-                           int32_t* rank_counts, void* ws, size_t ws_bytes, void* stream) {
+                           int32_t* rank_counts, void* ws, size_t ws_bytes, void* stream,
+                           int stages) {
   int st = check_desc(desc);
   if (st != MOE_OK) return st;
-  if (admission != MOE_ADMIT_TOKEN_ORDER && admission != MOE_ADMIT_FIRST_CHOICE)
-    return MOE_ERR_INVALID_ARG;
-  if (!expert_offsets || !admitted || !rank_offsets || !rank_counts) return MOE_ERR_INVALID_ARG;
+  const bool layout = stages & moe::kDispatchLayout, permute = stages & moe::kDispatchPermute;
   const int N = desc->num_tokens;
-  if (N > 0) {
-    if (!x || !topk_idx || !(x_perm || xq) || !row_of_slot || !token_of_row || !slot_of_row)
+  if (layout) {
+    if (admission != MOE_ADMIT_TOKEN_ORDER && admission != MOE_ADMIT_FIRST_CHOICE)
       return MOE_ERR_INVALID_ARG;
+    if (!expert_offsets || !admitted || !rank_offsets || !rank_counts) return MOE_ERR_INVALID_ARG;
+    if (N > 0 && (!topk_idx || !row_of_slot || !token_of_row || !slot_of_row))
+      return MOE_ERR_INVALID_ARG;
+  }
+  if (permute && N > 0) {
+    if (!x || !row_of_slot || !(x_perm || xq)) return MOE_ERR_INVALID_ARG;
     if (!aligned16(x) || (x_perm && !aligned16(x_perm))) return MOE_ERR_INVALID_ARG;
   }
-  const size_t need = moe::dispatch_workspace_bytes(N, desc->top_k, desc->num_experts);
-  if (!ws || ws_bytes < need || (reinterpret_cast<uintptr_t>(ws) & 15u)) return MOE_ERR_WORKSPACE;
+  if (layout) {
+    const size_t need = moe::dispatch_workspace_bytes(N, desc->top_k, desc->num_experts);
+    if (!ws || ws_bytes < need || (reinterpret_cast<uintptr_t>(ws) & 15u))
+      return MOE_ERR_WORKSPACE;
+  }
   moe::DispatchArgs a{N, desc->hidden, desc->num_experts, desc->top_k, desc->num_ranks,
                       desc->dtype, capacity_of(desc), x, topk_idx, x_perm, row_of_slot,
                       token_of_row, slot_of_row, expert_offsets, admitted, rank_offsets,
                       rank_counts, ws, admission == MOE_ADMIT_FIRST_CHOICE ? 1 : 0};
   a.xq = xq;
   a.row_scale = row_scale;
-  return status_of(moe::launch_dispatch(a, static_cast<hipStream_t>(stream)));
+  return status_of(moe::launch_dispatch(a, static_cast<hipStream_t>(stream), stages));
+}
+
+int moe_dispatch_layout(const moe_route_desc* desc, int32_t admission, const int32_t* topk_idx,
+                        int32_t* row_of_slot, int32_t* token_of_row, int8_t* slot_of_row,
+                        int32_t* expert_offsets, int32_t* admitted, int32_t* rank_offsets,
+                        int32_t* rank_counts, void* ws, size_t ws_bytes, void* stream) {
+  return dispatch_common(desc, admission, nullptr, topk_idx, nullptr, nullptr, nullptr,
+                         row_of_slot, token_of_row, slot_of_row, expert_offsets, admitted,
+                         rank_offsets, rank_counts, ws, ws_bytes, stream,
+                         moe::kDispatchLayout);
+}
+
+int moe_permute(const moe_route_desc* desc, const void* x, const int32_t* row_of_slot,
+                void* x_perm, void* stream) {
+  return dispatch_common(desc, MOE_ADMIT_TOKEN_ORDER, x, nullptr, x_perm, nullptr, nullptr,
+                         const_cast<int32_t*>(row_of_slot), nullptr, nullptr, nullptr, nullptr,
+                         nullptr, nullptr, nullptr, 0, stream, moe::kDispatchPermute);
+}
+
+int moe_permute_q8(const moe_route_desc* desc, const void* x, const int32_t* row_of_slot,
+                   int8_t* x_perm_q, float* row_scale, void* stream) {
+  if (desc && desc->num_tokens > 0) {
+    if (!x_perm_q || !row_scale) return MOE_ERR_INVALID_ARG;
+    if (!aligned16(x_perm_q) || (reinterpret_cast<uintptr_t>(row_scale) & 3u))
+      return MOE_ERR_INVALID_ARG;
+  }
+  if (desc && (desc->dtype == MOE_F32 || desc->dtype == MOE_BF16) &&
+      desc->hidden > moe::q8_max_hidden(desc->dtype))
+    return MOE_ERR_UNSUPPORTED;
+  return dispatch_common(desc, MOE_ADMIT_TOKEN_ORDER, x, nullptr, nullptr, x_perm_q, row_scale,
+                         const_cast<int32_t*>(row_of_slot), nullptr, nullptr, nullptr, nullptr,
+                         nullptr, nullptr, nullptr, 0, stream, moe::kDispatchPermute);
 }
 
 static int check_ffn(int32_t E, int32_t max_rows, int32_t d, int32_t h, int32_t act,

@@ -469,27 +469,29 @@ size_t dispatch_workspace_bytes(int N, int k, int E) {
   return std::max<size_t>(tiles, 1) * (size_t)E * sizeof(int32_t);
 }
 
-hipError_t launch_dispatch(const DispatchArgs& a, hipStream_t st) {
+hipError_t launch_dispatch(const DispatchArgs& a, hipStream_t st, int stages) {
   const int S = a.N * a.k;
   const int tiles = (S + kTileSlots - 1) / kTileSlots;
   int32_t* tile_counts = static_cast<int32_t*>(a.ws);
-  if (tiles > 0 && (long long)tiles * a.E <= kCountLds && a.E <= 1024) {
-    dispatch_count<<<1, 1024, 0, st>>>(a.topk_idx, S, a.k, a.first_choice, tiles, a.E, a.R,
-                                       a.cap, tile_counts,
-                                       a.expert_offsets, a.admitted, a.rank_offsets,
-                                       a.rank_counts);
-  } else {
+  if (stages & kDispatchLayout) {
+    if (tiles > 0 && (long long)tiles * a.E <= kCountLds && a.E <= 1024) {
+      dispatch_count<<<1, 1024, 0, st>>>(a.topk_idx, S, a.k, a.first_choice, tiles, a.E, a.R,
+                                         a.cap, tile_counts,
+                                         a.expert_offsets, a.admitted, a.rank_offsets,
+                                         a.rank_counts);
+    } else {
+      if (tiles > 0)
+        dispatch_tile_hist<<<tiles, 256, 0, st>>>(a.topk_idx, S, a.k, a.E, a.first_choice,
+                                                  tile_counts);
+      dispatch_scan<<<1, 256, 0, st>>>(tile_counts, tiles, a.E, a.R, a.cap, a.expert_offsets,
+                                       a.admitted, a.rank_offsets, a.rank_counts);
+    }
     if (tiles > 0)
-      dispatch_tile_hist<<<tiles, 256, 0, st>>>(a.topk_idx, S, a.k, a.E, a.first_choice,
-                                                tile_counts);
-    dispatch_scan<<<1, 256, 0, st>>>(tile_counts, tiles, a.E, a.R, a.cap, a.expert_offsets,
-                                     a.admitted, a.rank_offsets, a.rank_counts);
+      dispatch_assign<<<tiles, 256, 0, st>>>(a.topk_idx, S, a.k, a.first_choice, a.E, a.cap,
+                                             tile_counts, a.expert_offsets, a.row_of_slot,
+                                             a.token_of_row, a.slot_of_row);
   }
-  if (tiles == 0) return hipGetLastError();
-  dispatch_assign<<<tiles, 256, 0, st>>>(a.topk_idx, S, a.k, a.first_choice, a.E, a.cap,
-                                         tile_counts,
-                                         a.expert_offsets, a.row_of_slot, a.token_of_row,
-                                         a.slot_of_row);
+  if (!(stages & kDispatchPermute) || a.N == 0) return hipGetLastError();
   const int elem = a.dtype == 0 ? 4 : 2;
   const int vec_per_row = a.d * elem / 16;
   const int waves_needed = a.N;

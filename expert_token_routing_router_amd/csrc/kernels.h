@@ -60,7 +60,11 @@ hipError_t launch_dequantize_q8(int max_rows, int d, int dtype, const void* xq,
                                 hipStream_t st);
 
 size_t dispatch_workspace_bytes(int N, int k, int E);
-hipError_t launch_dispatch(const DispatchArgs& a, hipStream_t st);
+// Stages of a dispatch: the layout (histograms, capacity, scan, ranks) and the
+// permute of the rows (dtype rows, or the INT8 payload when xq is set).
+enum { kDispatchLayout = 1, kDispatchPermute = 2 };
+hipError_t launch_dispatch(const DispatchArgs& a, hipStream_t st,
+                           int stages = kDispatchLayout | kDispatchPermute);
 
 struct FfnArgs {
   int E, max_rows, d, h, act, dtype;

@@ -201,6 +201,27 @@ int moe_dispatch_ex(const moe_route_desc* desc, int32_t admission, const void* x
                     int32_t* admitted, int32_t* rank_offsets, int32_t* rank_counts,
                     void* ws, size_t ws_bytes, void* stream);
 
+/* The two halves of moe_dispatch_ex / moe_dispatch_q8, for callers that schedule
+ * them apart -- a multi-GPU layer exchanges the rank counts from the layout
+ * before it moves the rows (glossary step 2) -- or time them apart.
+ * moe_dispatch_layout: histograms, capacity, admission walk, scan and ranks --
+ *   every output of moe_dispatch_ex except x_perm (arguments, workspace and
+ *   errors as there; x is not read).
+ * moe_permute: x_perm[row_of_slot[t, j]] = x[t] for every admitted slot (the
+ *   permute of moe_dispatch; row_of_slot from moe_dispatch_layout).
+ * moe_permute_q8: the same rows as the INT8 payload (codes and scales exactly
+ *   as moe_dispatch_q8).
+ * A layout followed by a permute on one stream equals one moe_dispatch_ex /
+ * moe_dispatch_q8 call, bit for bit. */
+int moe_dispatch_layout(const moe_route_desc* desc, int32_t admission, const int32_t* topk_idx,
+                        int32_t* row_of_slot, int32_t* token_of_row, int8_t* slot_of_row,
+                        int32_t* expert_offsets, int32_t* admitted, int32_t* rank_offsets,
+                        int32_t* rank_counts, void* ws, size_t ws_bytes, void* stream);
+int moe_permute(const moe_route_desc* desc, const void* x, const int32_t* row_of_slot,
+                void* x_perm, void* stream);
+int moe_permute_q8(const moe_route_desc* desc, const void* x, const int32_t* row_of_slot,
+                   int8_t* x_perm_q, float* row_scale, void* stream);
+
 /* INT8 payload of the dispatch exchange.  EP notes, "深入推导" (DeepSeek-V3's EP
  * configuration): INT8-quantised communication halves the exchange volume.  The
  * pages give no scheme; this is one symmetric scale per token row, each

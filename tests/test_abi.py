@@ -156,6 +156,36 @@ def test_dispatch_q8_validation():
     assert call(f32) == moe.MOE_ERR_UNSUPPORTED                   # > 4096 fp32
 
 
+def test_dispatch_halves_validation():
+    """moe_dispatch_layout checks the layout arguments and workspace (x is not
+    needed); moe_permute / moe_permute_q8 check rows, x and the output."""
+    lib = moe.lib()
+    d = moe.route_desc(64, 64, 8, 2, R=4, cf=1.25)
+    need = moe.moe_dispatch_workspace_size(d)
+    outs = [FAKE] * 7  # row_of_slot .. rank_counts
+    assert lib.moe_dispatch_layout(ctypes.byref(d), 0, FAKE, *outs, FAKE, need - 4,
+                                   None) == moe.MOE_ERR_WORKSPACE
+    assert lib.moe_dispatch_layout(ctypes.byref(d), 3, FAKE, *outs, FAKE, need,
+                                   None) == moe.MOE_ERR_INVALID_ARG
+    assert lib.moe_dispatch_layout(ctypes.byref(d), 0, None, *outs, FAKE, need,
+                                   None) == moe.MOE_ERR_INVALID_ARG
+    bad = moe.route_desc(64, 64, 8, 2, R=3)
+    assert lib.moe_dispatch_layout(ctypes.byref(bad), 0, FAKE, *outs, FAKE, need,
+                                   None) == moe.MOE_ERR_INVALID_ARG
+    assert lib.moe_permute(ctypes.byref(d), None, FAKE, FAKE, None) == moe.MOE_ERR_INVALID_ARG
+    assert lib.moe_permute(ctypes.byref(d), FAKE, None, FAKE, None) == moe.MOE_ERR_INVALID_ARG
+    assert lib.moe_permute(ctypes.byref(d), FAKE, FAKE, None, None) == moe.MOE_ERR_INVALID_ARG
+    assert lib.moe_permute(ctypes.byref(d), FAKE, FAKE, ctypes.c_void_p(0x10008),
+                           None) == moe.MOE_ERR_INVALID_ARG
+    assert lib.moe_permute_q8(ctypes.byref(d), FAKE, FAKE, None, FAKE,
+                              None) == moe.MOE_ERR_INVALID_ARG
+    assert lib.moe_permute_q8(ctypes.byref(d), FAKE, FAKE, FAKE, None,
+                              None) == moe.MOE_ERR_INVALID_ARG
+    wide = moe.route_desc(64, 8200, 8, 2)
+    assert lib.moe_permute_q8(ctypes.byref(wide), FAKE, FAKE, FAKE, FAKE,
+                              None) == moe.MOE_ERR_UNSUPPORTED
+
+
 def test_dequantize_q8_validation():
     lib = moe.lib()
     ok = dict(M=16, d=64, dt=moe.MOE_BF16, q=FAKE, s=FAKE, n=FAKE, out=FAKE)

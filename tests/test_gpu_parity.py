@@ -380,6 +380,38 @@ def test_dispatch_q8_codes_bit_exact(N, d, dtype, E, k):
     assert (q[1] == 0).sum() == d - 1 and q[1, d // 3] == -127 and sc[0] == 0.0
 
 
+@pytest.mark.parametrize("payload,admission", [("native", "token"), ("native", "first_choice"),
+                                               ("int8", "token")])
+def test_dispatch_halves_equal_one_call(payload, admission):
+    """moe_dispatch_layout then moe_permute (or moe_permute_q8) on one stream
+    writes exactly what one moe_dispatch_ex (or moe_dispatch_q8) call writes."""
+    cfg = W.with_(W.small("zipf"), cf=1.0, admission=admission, payload=payload)
+    print(f"[dispatch halves] {payload} {admission}", flush=True)
+    inp = to_dev(W.make_inputs(cfg, weights=False))
+    one, two = moe.MoeBuffers(cfg), moe.MoeBuffers(cfg)
+    layer.route(one, inp)
+    two.topk_idx.copy_(one.topk_idx)
+    layer.dispatch(one, inp)
+    d = two.desc
+    moe.moe_dispatch_layout(d, admission, two.topk_idx, two.row_of_slot, two.token_of_row,
+                            two.slot_of_row, two.expert_offsets, two.admitted, two.rank_offsets,
+                            two.rank_counts, two.ws_dispatch)
+    if payload == "int8":
+        moe.moe_permute_q8(d, inp["x"], two.row_of_slot, two.x_perm_q, two.row_scale)
+    else:
+        moe.moe_permute(d, inp["x"], two.row_of_slot, two.x_perm)
+    torch.cuda.synchronize()
+    M = int(one.expert_offsets[-1].item())
+    for key in ("row_of_slot", "token_of_row", "slot_of_row", "expert_offsets", "admitted",
+                "rank_offsets", "rank_counts"):
+        assert torch.equal(getattr(one, key), getattr(two, key)), key
+    if payload == "int8":
+        assert torch.equal(one.x_perm_q[:M], two.x_perm_q[:M])
+        assert torch.equal(one.row_scale[:M].view(torch.int32), two.row_scale[:M].view(torch.int32))
+    else:
+        assert torch.equal(one.x_perm[:M].view(torch.int16), two.x_perm[:M].view(torch.int16))
+
+
 def test_all_tokens_to_one_expert_with_capacity():
     """A huge selection bias sends every token to expert 3; capacity 1.25
     admits the first cap tokens; every other token leaves the layer unchanged."""
