@@ -10,6 +10,8 @@
 //
 // Bias update: same page, bias-based balancing bullet (after each step, lower
 // the bias of overloaded experts, raise it for idle ones).
+#include <type_traits>
+
 #include "device.h"
 #include "kernels.h"
 
@@ -20,7 +22,8 @@ namespace moe {
 // d = 4096, 141 -> 134 us for d = 7168, while one vector keeps the
 // occupancy d = 1024 needs), and the next token's row ids and weights are
 // loaded while the current token's rows move.
-template <int DTYPE, int V>  // DTYPE 0 fp32 (4 per vector), 1 bf16 (8 per vector)
+// KM: slots per token the kernel holds rows for (k <= KM).
+template <int DTYPE, int V, int KM>  // DTYPE 0 fp32 (4 per vector), 1 bf16 (8 per vector)
 __global__ __launch_bounds__(256) void combine_rows(const u32x4* __restrict__ y_perm,
                                                     const int32_t* __restrict__ row_of_slot,
                                                     const float* __restrict__ topk_w,
@@ -61,8 +64,25 @@ __global__ __launch_bounds__(256) void combine_rows(const u32x4* __restrict__ y_
     }
     for (int v0 = 0; v0 < vec_per_row; v0 += V * 64) {
       const size_t tv0 = (size_t)t * vec_per_row + v0 + lane;
+      // Every load of this chunk first (residual, shared, the k expert rows),
+      // then the adds in the fixed order: one memory round trip per chunk.
+      u32x4 qr[V], qs[V], qy[KM][V];
+#pragma unroll
+      for (int u = 0; u < V; ++u) {
+        const bool in = v0 + u * 64 + lane < vec_per_row;
+        if (residual && in) qr[u] = residual[tv0 + u * 64];
+        if (shared_out && in) qs[u] = shared_out[tv0 + u * 64];
+      }
+#pragma unroll
+      for (int j = 0; j < KM; ++j) {
+        if (j < k && rows[j] >= 0) {
+          const u32x4* src = y_perm + (size_t)rows[j] * vec_per_row + v0 + lane;
+#pragma unroll
+          for (int u = 0; u < V; ++u)
+            if (v0 + u * 64 + lane < vec_per_row) qy[j][u] = src[u * 64];
+        }
+      }
       float acc[V][VE];
-      u32x4 q[V];
 #pragma unroll
       for (int u = 0; u < V; ++u) {
 #pragma unroll
@@ -70,32 +90,19 @@ __global__ __launch_bounds__(256) void combine_rows(const u32x4* __restrict__ y_
       }
       // residual + shared + sum_j w_j row_j, in that order (a skipped slot
       // adds nothing).
-      if (residual) {
 #pragma unroll
-        for (int u = 0; u < V; ++u)
-          if (v0 + u * 64 + lane < vec_per_row) q[u] = residual[tv0 + u * 64];
-#pragma unroll
-        for (int u = 0; u < V; ++u)
-          if (v0 + u * 64 + lane < vec_per_row) add_vec(acc[u], q[u], 1.f);
-      }
-      if (shared_out) {
-#pragma unroll
-        for (int u = 0; u < V; ++u)
-          if (v0 + u * 64 + lane < vec_per_row) q[u] = shared_out[tv0 + u * 64];
-#pragma unroll
-        for (int u = 0; u < V; ++u)
-          if (v0 + u * 64 + lane < vec_per_row) add_vec(acc[u], q[u], 1.f);
+      for (int u = 0; u < V; ++u) {
+        if (v0 + u * 64 + lane < vec_per_row) {
+          if (residual) add_vec(acc[u], qr[u], 1.f);
+          if (shared_out) add_vec(acc[u], qs[u], 1.f);
+        }
       }
 #pragma unroll
-      for (int j = 0; j < 8; ++j) {
+      for (int j = 0; j < KM; ++j) {
         if (j < k && rows[j] >= 0) {
-          const u32x4* src = y_perm + (size_t)rows[j] * vec_per_row + v0 + lane;
 #pragma unroll
           for (int u = 0; u < V; ++u)
-            if (v0 + u * 64 + lane < vec_per_row) q[u] = src[u * 64];
-#pragma unroll
-          for (int u = 0; u < V; ++u)
-            if (v0 + u * 64 + lane < vec_per_row) add_vec(acc[u], q[u], ws[j]);
+            if (v0 + u * 64 + lane < vec_per_row) add_vec(acc[u], qy[j][u], ws[j]);
         }
       }
 #pragma unroll
@@ -126,18 +133,27 @@ hipError_t launch_combine(const CombineArgs& a, hipStream_t st) {
   auto sh = static_cast<const u32x4*>(a.shared_out);
   auto y = static_cast<u32x4*>(a.y);
   const bool wide = vec_per_row > 128;
-  if (a.dtype == 0 && wide)
-    combine_rows<0, 2><<<blocks, 256, 0, st>>>(yp, a.row_of_slot, a.topk_w, res, sh, y, a.N,
-                                               vec_per_row, a.k);
-  else if (a.dtype == 0)
-    combine_rows<0, 1><<<blocks, 256, 0, st>>>(yp, a.row_of_slot, a.topk_w, res, sh, y, a.N,
-                                               vec_per_row, a.k);
-  else if (wide)
-    combine_rows<1, 2><<<blocks, 256, 0, st>>>(yp, a.row_of_slot, a.topk_w, res, sh, y, a.N,
-                                               vec_per_row, a.k);
-  else
-    combine_rows<1, 1><<<blocks, 256, 0, st>>>(yp, a.row_of_slot, a.topk_w, res, sh, y, a.N,
-                                               vec_per_row, a.k);
+  auto go = [&](auto kernel) {
+    kernel<<<blocks, 256, 0, st>>>(yp, a.row_of_slot, a.topk_w, res, sh, y, a.N, vec_per_row,
+                                   a.k);
+  };
+  // One kernel copy per (dtype, vectors in flight, slots held): registers are
+  // reserved only for the slots a workload has.
+  auto pick = [&](auto dt, auto v) {
+    constexpr int D = decltype(dt)::value, VV = decltype(v)::value;
+    if (a.k <= 1) go(combine_rows<D, VV, 1>);
+    else if (a.k <= 2) go(combine_rows<D, VV, 2>);
+    else if (a.k <= 4) go(combine_rows<D, VV, 4>);
+    else go(combine_rows<D, VV, 8>);
+  };
+  using I0 = std::integral_constant<int, 0>;
+  using I1 = std::integral_constant<int, 1>;
+  using I2 = std::integral_constant<int, 2>;
+  if (a.dtype == 0) {
+    if (wide) pick(I0{}, I2{}); else pick(I0{}, I1{});
+  } else {
+    if (wide) pick(I1{}, I2{}); else pick(I1{}, I1{});
+  }
   return hipGetLastError();
 }
 
