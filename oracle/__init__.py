@@ -172,15 +172,20 @@ ADMISSION = {"token": 0, "first_choice": 1}
 def dispatch(cfg: dict, topk_idx, admission: str | None = None) -> dict:
     """Capacity, admission and layout.  admission: "token" (default; token
     order) or "first_choice" (every token's first choice before any second
-    choice); defaults to cfg.get("admission", "token")."""
+    choice); defaults to cfg.get("admission", "token").  cfg["layout"] ==
+    "padded" asks for GShard-style fixed buffers of cap rows per expert."""
     adm = ADMISSION[admission or cfg.get("admission", "token")]
+    padded = cfg.get("layout", "compact") == "padded"
+    if padded:
+        adm |= 2
     topk_idx = _c(topk_idx, np.int32)
     N, k, E, R = topk_idx.shape[0], cfg["k"], cfg["E"], cfg.get("R", 1)
     S = N * k
+    rows = max(S, E * capacity(dict(cfg, N=N))) if padded else S
     out = {
         "row_of_slot": np.empty((N, k), np.int32),
-        "token_of_row": np.empty(S, np.int32),
-        "slot_of_row": np.empty(S, np.int8),
+        "token_of_row": np.empty(rows, np.int32),
+        "slot_of_row": np.empty(rows, np.int8),
         "expert_offsets": np.empty(E + 1, np.int32),
         "admitted": np.empty(E, np.int32),
         "rank_offsets": np.empty(R + 1, np.int32),
@@ -289,7 +294,11 @@ def forward(cfg: dict, x, w_router, router_bias, sel_bias, w1, w3, w2,
     if cfg.get("payload", "native") == "int8":
         q, sc = quantize_rows_q8(cfg["dtype"], x)
         tor = dsp["token_of_row"][:M]
-        x_perm = dequantize_rows_q8(cfg["dtype"], q[tor], sc[tor])
+        live = tor >= 0  # padding rows of the padded layout carry zero codes
+        qr = np.zeros((M, q.shape[1]), np.int8)
+        sr = np.zeros(M, np.float32)
+        qr[live], sr[live] = q[tor[live]], sc[tor[live]]
+        x_perm = dequantize_rows_q8(cfg["dtype"], qr, sr)
     else:
         x_perm = permute(cfg["dtype"], x, dsp["token_of_row"], M)
     y_perm = expert_ffn(cfg["dtype"], cfg["act"], x_perm, dsp["expert_offsets"], w1, w3, w2)

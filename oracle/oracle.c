@@ -281,7 +281,8 @@ int oracle_dispatch_ex(const oracle_desc* desc, int32_t admission, const int32_t
                        int32_t* expert_offsets, int32_t* admitted,
                        int32_t* rank_offsets, int32_t* rank_counts) {
   if (!desc_ok(desc) || !expert_offsets || !admitted || !rank_offsets || !rank_counts) return -1;
-  if (admission != 0 && admission != 1) return -1;
+  if (admission & ~3) return -1;
+  const int first_choice = admission & 1, padded = (admission >> 1) & 1;
   const int32_t N = desc->num_tokens, E = desc->num_experts, k = desc->top_k;
   const int32_t R = desc->num_ranks;
   const size_t S = (size_t)N * k;
@@ -289,6 +290,9 @@ int oracle_dispatch_ex(const oracle_desc* desc, int32_t admission, const int32_t
   for (size_t i = 0; i < S; ++i)
     if (topk_idx[i] < 0 || topk_idx[i] >= E) return -1;
   const int64_t cap = oracle_capacity(desc);
+  /* The padded layout needs a finite capacity and E * cap rows. */
+  if (padded && (desc->capacity_factor <= 0.0f || (int64_t)E * cap > INT32_MAX)) return -1;
+  const size_t rows_total = padded && (size_t)E * (size_t)cap > S ? (size_t)E * (size_t)cap : S;
 
   int32_t* seen = (int32_t*)calloc((size_t)E, sizeof(int32_t));
   int32_t* rank_in_expert = (int32_t*)malloc(sizeof(int32_t) * (S ? S : 1));
@@ -301,7 +305,7 @@ int oracle_dispatch_ex(const oracle_desc* desc, int32_t admission, const int32_t
   }
   for (size_t i = 0; i < S; ++i) counts[topk_idx[i]] += 1;
 
-  if (admission == 0) {
+  if (!first_choice) {
     /* Admission in token order (t outer, slot inner). */
     for (int32_t t = 0; t < N; ++t) {
       for (int32_t j = 0; j < k; ++j) {
@@ -332,15 +336,18 @@ int oracle_dispatch_ex(const oracle_desc* desc, int32_t admission, const int32_t
     }
   }
 
+  /* Compact layout: expert e's rows follow expert e-1's admitted rows.
+   * Padded layout (GShard's fixed buffers of cap rows per expert): expert e
+   * owns rows [e cap, (e+1) cap); the rows past its admitted ones are padding. */
   int32_t run = 0;
   for (int32_t e = 0; e < E; ++e) {
     admitted[e] = counts[e] < cap ? counts[e] : (int32_t)cap;
-    expert_offsets[e] = run;
+    expert_offsets[e] = padded ? (int32_t)(e * cap) : run;
     run += admitted[e];
   }
-  expert_offsets[E] = run;
+  expert_offsets[E] = padded ? (int32_t)(E * cap) : run;
 
-  for (size_t i = 0; i < S; ++i) {
+  for (size_t i = 0; i < rows_total; ++i) {
     token_of_row[i] = -1;
     slot_of_row[i] = -1;
   }
@@ -375,8 +382,12 @@ int oracle_permute(int32_t num_rows, int32_t hidden, int32_t dtype, const void* 
   if (num_rows < 0 || hidden < 1 || !dtype_ok(dtype)) return -1;
   if (num_rows > 0 && (!x || !token_of_row || !x_perm)) return -1;
   const size_t es = dtype == 0 ? 4 : 2, rb = es * (size_t)hidden;
-  for (int32_t i = 0; i < num_rows; ++i)
-    memcpy((char*)x_perm + (size_t)i * rb, (const char*)x + (size_t)token_of_row[i] * rb, rb);
+  for (int32_t i = 0; i < num_rows; ++i) {
+    if (token_of_row[i] < 0) /* a padding row of the padded layout */
+      memset((char*)x_perm + (size_t)i * rb, 0, rb);
+    else
+      memcpy((char*)x_perm + (size_t)i * rb, (const char*)x + (size_t)token_of_row[i] * rb, rb);
+  }
   return 0;
 }
 

@@ -76,13 +76,22 @@ int oracle_dispatch(const oracle_desc* desc, const int32_t* topk_idx,
  * expert follow that order.  MLSys ch.10, section 10.5 names GShard's top-2
  * router; the pages fix no admission priority, and this is the plainest
  * reading of a router that ranks first choices above second ones.
+ * Bit 1 of admission (value 2, combinable with either order) asks for the
+ * padded layout of GShard-style fixed buffers ("参考答案" answer 2 of the EP
+ * notes sizes each expert's buffer as the mean load times the capacity
+ * factor): expert e owns rows [e cap, (e+1) cap), expert_offsets[e] = e cap,
+ * its admitted rows come first in admission order and the rest are padding
+ * (token_of_row = slot_of_row = -1); rank offsets and counts follow from the
+ * offsets as before.  token_of_row / slot_of_row then hold max(N k, E cap)
+ * entries.  The padded layout needs a finite capacity (cf > 0).
  * Returns -1 for any other admission value. */
 int oracle_dispatch_ex(const oracle_desc* desc, int32_t admission, const int32_t* topk_idx,
                        int32_t* row_of_slot, int32_t* token_of_row, int8_t* slot_of_row,
                        int32_t* expert_offsets, int32_t* admitted,
                        int32_t* rank_offsets, int32_t* rank_counts);
 
-/* x_perm[i] = x[token_of_row[i]] for i < num_rows (a byte copy). */
+/* x_perm[i] = x[token_of_row[i]] for i < num_rows (a byte copy); a row with
+ * token_of_row[i] < 0 (padding of the padded layout) is all zero bytes. */
 int oracle_permute(int32_t num_rows, int32_t hidden, int32_t dtype, const void* x,
                    const int32_t* token_of_row, void* x_perm);
 

@@ -268,6 +268,75 @@ def test_first_choice_invariants_property(N, E_pow, k, R_pow, cf, skew, seed):
     _check_invariants(cfg, idx, dsp, "first_choice")
 
 
+# ---- padded layout (GShard-style fixed buffers of cap rows per expert) ----
+
+
+def test_padded_layout_relocates_the_compact_rows():
+    """Expert e's admitted rows move from the compact offset to row e*cap, in
+    the same order; the rows after them up to (e+1)*cap are padding; offsets
+    and per-rank counts become multiples of cap.  Both admission orders."""
+    rng = np.random.default_rng(34)
+    for trial in range(30):
+        E = int(rng.choice([2, 4, 8, 16]))
+        k = int(rng.integers(1, min(3, E) + 1))
+        N = int(rng.integers(1, 250))
+        R = int(rng.choice([r for r in (1, 2, 4) if E % r == 0]))
+        cf = float(rng.choice([0.25, 0.5, 1.0, 1.25, 2.0]))
+        idx = _random_topk(rng, N, E, k, skew=float(rng.choice([0.0, 1.5])))
+        for adm in ("token", "first_choice"):
+            cfg = _cfg(N=N, E=E, k=k, R=R, cf=cf, admission=adm)
+            cap = oracle.capacity(cfg)
+            com = oracle.dispatch(cfg, idx)
+            pad = oracle.dispatch(dict(cfg, layout="padded"), idx)
+            assert np.array_equal(pad["admitted"], com["admitted"])
+            assert np.array_equal(pad["expert_offsets"], np.arange(E + 1) * cap)
+            assert np.array_equal(pad["rank_counts"], np.full(R, E // R * cap))
+            assert pad["num_rows"] == E * cap
+            ros_c, ros_p = com["row_of_slot"], pad["row_of_slot"]
+            assert np.array_equal(ros_c < 0, ros_p < 0)
+            e_of = idx[ros_c >= 0]
+            off = com["expert_offsets"]
+            assert np.array_equal(ros_p[ros_c >= 0], e_of * cap + ros_c[ros_c >= 0] - off[e_of])
+            for e in range(E):
+                a = com["admitted"][e]
+                seg = slice(e * cap, e * cap + a)
+                assert np.array_equal(pad["token_of_row"][seg], com["token_of_row"][off[e]:off[e] + a])
+                assert np.array_equal(pad["slot_of_row"][seg], com["slot_of_row"][off[e]:off[e] + a])
+                assert np.all(pad["token_of_row"][e * cap + a:(e + 1) * cap] == -1)
+                assert np.all(pad["slot_of_row"][e * cap + a:(e + 1) * cap] == -1)
+
+
+def test_padded_layout_needs_a_capacity():
+    with pytest.raises(ValueError):
+        oracle.dispatch(_cfg(N=8, E=4, k=1, cf=0.0, layout="padded"),
+                        np.zeros((8, 1), np.int32))
+
+
+def test_padding_rows_permute_to_zero():
+    x = np.arange(4 * 8, dtype=np.float32).reshape(4, 8) + 1
+    tor = np.array([2, -1, 0, -1, 3], np.int32)
+    out = oracle.permute("fp32", x, tor, 5)
+    assert np.array_equal(out[[0, 2, 4]], x[[2, 0, 3]])
+    assert np.all(out[[1, 3]] == 0)
+
+
+def test_padded_layer_output_equals_compact():
+    """Each FFN row depends on its input row only and padding rows are zero,
+    so the padded layout changes no output bit (Switch and Zipf, small)."""
+    import moe_workloads as W
+    for name, cf in (("switch", None), ("zipf", 1.0)):
+        cfg = W.small(name) if cf is None else W.with_(W.small(name), cf=cf)
+        inp = W.make_inputs(cfg)
+        n = W.to_numpy
+        args = (n(inp["x"]), n(inp["w_router"]), n(inp["router_bias"]), n(inp["sel_bias"]),
+                n(inp["w1"]), n(inp["w3"]), n(inp["w2"]))
+        com = oracle.forward(cfg, *args)
+        pad = oracle.forward(dict(cfg, layout="padded"), *args)
+        assert np.array_equal(com["y"], pad["y"]), name
+        live = pad["token_of_row"][:pad["num_rows"]] >= 0
+        assert np.all(pad["y_perm"][~live] == 0)
+
+
 def test_permute_is_bitwise_row_copy():
     rng = np.random.default_rng(24)
     N, d, E, k = 100, 32, 4, 2
