@@ -50,6 +50,9 @@ def parse_args():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0,
                     help="target length of the oracle's timed sample")
+    ap.add_argument("--layout", default="compact", choices=["compact", "padded"],
+                    help="dispatch layout: compact rows, or fixed buffers of cap rows per "
+                         "expert (the FFN then runs every row of them)")
     ap.add_argument("--payload", default="native", choices=["native", "int8"],
                     help="dispatched rows as the layer dtype, or as the INT8 payload "
                          "(quantised in the permute, dequantised before the FFN)")
@@ -181,6 +184,8 @@ def describe(cfg) -> str:
         s += f" admission={cfg['admission']}"
     if cfg.get("payload", "native") != "native":
         s += f" payload={cfg['payload']}"
+    if cfg.get("layout", "compact") != "compact":
+        s += f" layout={cfg['layout']}"
     return s
 
 
@@ -264,6 +269,8 @@ def main():
         cfg["admission"] = args.admission
     if args.payload != "native":
         cfg["payload"] = args.payload
+    if args.layout != "compact":
+        cfg["layout"] = args.layout
     # Inputs: the glossary snippet's stream for the toy workload (CPU), else
     # drawn on the device.
     gen_dev = "cpu" if args.workload == "toy" else "cuda"
@@ -290,8 +297,14 @@ def main():
     # the INT8 payload's moe_permute_q8 + moe_dequantize_q8): the same kernels
     # in the same order as one moe_dispatch call, timed apart.
     q8 = buf.x_perm_q is not None
-    adm = cfg.get("admission", "token")
-    calls = (["route", "dispatch_layout", "permute"] + (["dequantize"] if q8 else [])
+    adm = buf.flags
+    padded = cfg.get("layout", "compact") == "padded"
+    R_ffn = buf.rows  # rows the FFN runs over (E*cap with the padded layout)
+    # The padded layout's padding rows are zeroed by the whole-dispatch call,
+    # so that layout runs the dispatch as one call.
+    disp_calls = ["dispatch"] if padded else (["dispatch_layout", "permute"]
+                                              + (["dequantize"] if q8 else []))
+    calls = (["route"] + disp_calls
              + ["ffn_plan", "ffn_up", "ffn_down", "combine", "bias_update"])
     fork = layer.has_shared(buf, wts)
     main = torch.cuda.current_stream()
@@ -312,30 +325,33 @@ def main():
         layer.route(buf, inp)
         i += 1
         mark(i)
-        moe.moe_dispatch_layout(d, adm, buf.topk_idx, buf.row_of_slot, buf.token_of_row,
-                                buf.slot_of_row, buf.expert_offsets, buf.admitted,
-                                buf.rank_offsets, buf.rank_counts, buf.ws_dispatch)
-        i += 1
-        mark(i)
-        if q8:
-            moe.moe_permute_q8(d, inp["x"], buf.row_of_slot, buf.x_perm_q, buf.row_scale)
+        if padded:
+            layer.dispatch(buf, inp)
+        else:
+            moe.moe_dispatch_layout(d, adm, buf.topk_idx, buf.row_of_slot, buf.token_of_row,
+                                    buf.slot_of_row, buf.expert_offsets, buf.admitted,
+                                    buf.rank_offsets, buf.rank_counts, buf.ws_dispatch)
             i += 1
             mark(i)
-            moe.moe_dequantize_q8(S, dim, cfg["dtype"], buf.x_perm_q, buf.row_scale,
-                                  buf.expert_offsets[E:], buf.x_perm)
-        else:
-            moe.moe_permute(d, inp["x"], buf.row_of_slot, buf.x_perm)
+            if q8:
+                moe.moe_permute_q8(d, inp["x"], buf.row_of_slot, buf.x_perm_q, buf.row_scale)
+                i += 1
+                mark(i)
+                moe.moe_dequantize_q8(S, dim, cfg["dtype"], buf.x_perm_q, buf.row_scale,
+                                      buf.expert_offsets[E:], buf.x_perm)
+            else:
+                moe.moe_permute(d, inp["x"], buf.row_of_slot, buf.x_perm)
         i += 1
         mark(i)
-        moe.moe_expert_ffn_plan(E, S, dim, h, cfg["act"], cfg["dtype"], buf.expert_offsets,
+        moe.moe_expert_ffn_plan(E, R_ffn, dim, h, cfg["act"], cfg["dtype"], buf.expert_offsets,
                                 buf.ws_ffn)
         i += 1
         mark(i)
-        moe.moe_expert_ffn_up(E, S, dim, h, cfg["act"], cfg["dtype"], buf.x_perm,
+        moe.moe_expert_ffn_up(E, R_ffn, dim, h, cfg["act"], cfg["dtype"], buf.x_perm,
                               buf.expert_offsets, wts["w1"], wts.get("w3"), buf.ws_ffn)
         i += 1
         mark(i)
-        moe.moe_expert_ffn_down(E, S, dim, h, cfg["act"], cfg["dtype"], buf.expert_offsets,
+        moe.moe_expert_ffn_down(E, R_ffn, dim, h, cfg["act"], cfg["dtype"], buf.expert_offsets,
                                 wts["w2"], buf.y_perm, buf.ws_ffn)
         i += 1
         mark(i)
@@ -431,7 +447,8 @@ def main():
         torch.cuda.synchronize()
 
     # Algorithmic work of this batch (rows actually admitted).
-    M = int(buf.expert_offsets[E].item())
+    M = int(buf.expert_offsets[E].item())  # rows laid out (E*cap when padded)
+    admitted_rows = int(buf.admitted.sum().item())
     counts = buf.admitted.cpu()
     active = int((counts > 0).sum().item())
     es = 2 if cfg["dtype"] == "bf16" else 4
@@ -445,7 +462,8 @@ def main():
     # permute: x read once, every admitted row written (INT8 payload: d bytes + a
     # 4-byte scale per row), row_of_slot read; dequantisation reads the payload
     # back and writes dtype rows
-    permute_bytes = N * dim * es + (M * (dim + 4) if q8 else M * dim * es) + S * 4
+    permute_bytes = (N * dim * es + (admitted_rows * (dim + 4) if q8 else admitted_rows * dim * es)
+                     + S * 4)
     dequant_bytes = M * (dim + 4) + M * dim * es
     combine_bytes = M * dim * es + N * dim * es + N * dim * es + S * 8
     route_bytes = N * dim * es + E * dim * es + N * E * 4 + S * 8
@@ -463,17 +481,25 @@ def main():
         "ffn_up": roof("ffn_up", up_flops, up_bytes),
         "ffn_down": roof("ffn_down", down_flops, down_bytes),
     }
-    hbm_calls = [("route", route_bytes), ("dispatch_layout", layout_bytes),
-                 ("permute", permute_bytes), ("combine", combine_bytes)]
-    if q8:
-        hbm_calls.append(("dequantize", dequant_bytes))
+    if padded:  # one whole-dispatch call; the padding rows are written as zeros
+        hbm_calls = [("route", route_bytes),
+                     ("dispatch", layout_bytes + permute_bytes
+                      + (M - admitted_rows) * (dim + 4 if q8 else dim * es)
+                      + (dequant_bytes if q8 else 0)),
+                     ("combine", combine_bytes)]
+    else:
+        hbm_calls = [("route", route_bytes), ("dispatch_layout", layout_bytes),
+                     ("permute", permute_bytes), ("combine", combine_bytes)]
+        if q8:
+            hbm_calls.append(("dequantize", dequant_bytes))
     for name, nbytes in hbm_calls:
         t = per_call[name] * 1e-6
         kern[name] = {"us": round(per_call[name], 2), "gbs": round(nbytes / t / 1e9, 1),
                       "hbm_frac": round(nbytes / t / (HBM_PEAK_GBS * 1e9), 4)}
-    kern["dispatch"] = {"us": round(sum(per_call[c] for c in
-                                        ("dispatch_layout", "permute", "dequantize")
-                                        if c in per_call), 2)}
+    if not padded:
+        kern["dispatch"] = {"us": round(sum(per_call[c] for c in
+                                            ("dispatch_layout", "permute", "dequantize")
+                                            if c in per_call), 2)}
     for name in per_call:
         kern.setdefault(name, {"us": round(per_call[name], 2)})
     cold = {"ms_per_step_with_per_call_events": round(cold_step_ms, 4), "steps": n_cold,
@@ -512,12 +538,13 @@ def main():
         "vs_baseline": None,
         "dtype": cfg["dtype"],
         "data": "synthetic",
-        "config": {"workload": describe(cfg), "global_batch": N, "rows_admitted": M,
-                   "dropped_slots": S - M, "active_experts": active},
+        "config": {"workload": describe(cfg), "global_batch": N,
+                   "rows_admitted": admitted_rows, "dropped_slots": S - admitted_rows,
+                   "rows_laid_out": M, "active_experts": active},
         "roofline": roofline,
         "grouped_gemm_mfma_frac": {"up": kern["ffn_up"]["mfma_frac"],
                                    "down": kern["ffn_down"]["mfma_frac"]},
-        "permute_hbm_frac": kern["permute"]["hbm_frac"],
+        "permute_hbm_frac": kern["permute" if "permute" in kern else "dispatch"]["hbm_frac"],
         "kernels": kern,
         "ms_per_step_with_per_call_events": round(instrumented_ms, 4),
         "step_ms_p10_p50_p90": [round(pct(step_ms, q), 4) for q in (0.1, 0.5, 0.9)],

@@ -27,7 +27,7 @@ MOE_OK, MOE_ERR_INVALID_ARG, MOE_ERR_UNSUPPORTED, MOE_ERR_HIP, MOE_ERR_WORKSPACE
 MOE_F32, MOE_BF16 = 0, 1
 MOE_SOFTMAX_TOPK, MOE_SOFTMAX_ALL, MOE_SIGMOID_NORM = 0, 1, 2
 MOE_RELU, MOE_GELU, MOE_SWIGLU = 0, 1, 2
-MOE_ADMIT_TOKEN_ORDER, MOE_ADMIT_FIRST_CHOICE = 0, 1
+MOE_ADMIT_TOKEN_ORDER, MOE_ADMIT_FIRST_CHOICE, MOE_LAYOUT_PADDED = 0, 1, 2
 
 SCORE = {"softmax_topk": MOE_SOFTMAX_TOPK, "softmax_all": MOE_SOFTMAX_ALL,
          "sigmoid_norm": MOE_SIGMOID_NORM}
@@ -40,6 +40,7 @@ EXPORTS = [
     "moe_route_workspace_size", "moe_route", "moe_router_logits",
     "moe_dispatch_workspace_size", "moe_dispatch", "moe_dispatch_ex", "moe_dispatch_q8",
     "moe_dequantize_q8", "moe_dispatch_layout", "moe_permute", "moe_permute_q8",
+    "moe_dispatch_rows",
     "moe_expert_ffn_workspace_size", "moe_expert_ffn", "moe_expert_ffn_plan",
     "moe_expert_ffn_up", "moe_expert_ffn_down", "moe_expert_ffn_pack_weights", "moe_combine",
     "moe_bias_update", "moe_status_string",
@@ -106,6 +107,7 @@ def lib() -> ctypes.CDLL:
             "moe_dispatch_layout": ([D, I32, P, P, P, P, P, P, P, P, P, SZ, P], I32),
             "moe_permute": ([D, P, P, P, P], I32),
             "moe_permute_q8": ([D, P, P, P, P, P], I32),
+            "moe_dispatch_rows": ([D, I32], ctypes.c_int64),
             "moe_expert_ffn_workspace_size": ([I32, I32, I32, I32, I32, I32], SZ),
             "moe_expert_ffn": ([I32, I32, I32, I32, I32, I32, P, P, P, P, P, P, P, SZ, P], I32),
             "moe_expert_ffn_plan": ([I32, I32, I32, I32, I32, I32, P, P, SZ, P], I32),
@@ -220,7 +222,8 @@ def moe_dispatch_ex(desc, admission, x, topk_idx, x_perm, row_of_slot, token_of_
                     slot_of_row, expert_offsets, admitted, rank_offsets, rank_counts, ws,
                     stream=None):
     """admission: "token" / MOE_ADMIT_TOKEN_ORDER or "first_choice" /
-    MOE_ADMIT_FIRST_CHOICE."""
+    MOE_ADMIT_FIRST_CHOICE, optionally | MOE_LAYOUT_PADDED (admission_flags());
+    with the padded layout the row buffers need moe_dispatch_rows() rows."""
     adm = ADMISSION[admission] if isinstance(admission, str) else int(admission)
     _dispatch("moe_dispatch_ex", desc, adm, x, topk_idx, x_perm, row_of_slot, token_of_row,
               slot_of_row, expert_offsets, admitted, rank_offsets, rank_counts, ws, stream)
@@ -235,14 +238,15 @@ def moe_dispatch_q8(desc, admission, x, topk_idx, x_perm_q, row_scale, row_of_sl
     N, d, E, k, R = desc.num_tokens, desc.hidden, desc.num_experts, desc.top_k, desc.num_ranks
     dt = TORCH_DTYPE.get(desc.dtype)
     S = N * k
+    rows = S if not adm & MOE_LAYOUT_PADDED else moe_dispatch_rows(desc, adm)
     st = lib().moe_dispatch_q8(
         ctypes.byref(desc), adm, _ptr(x, "x", dt, N * d, N > 0),
         _ptr(topk_idx, "topk_idx", torch.int32, S, N > 0),
-        _ptr(x_perm_q, "x_perm_q", torch.int8, S * d, N > 0),
-        _ptr(row_scale, "row_scale", torch.float32, S, N > 0),
+        _ptr(x_perm_q, "x_perm_q", torch.int8, rows * d, N > 0),
+        _ptr(row_scale, "row_scale", torch.float32, rows, N > 0),
         _ptr(row_of_slot, "row_of_slot", torch.int32, S, N > 0),
-        _ptr(token_of_row, "token_of_row", torch.int32, S, N > 0),
-        _ptr(slot_of_row, "slot_of_row", torch.int8, S, N > 0),
+        _ptr(token_of_row, "token_of_row", torch.int32, rows, N > 0),
+        _ptr(slot_of_row, "slot_of_row", torch.int8, rows, N > 0),
         _ptr(expert_offsets, "expert_offsets", torch.int32, E + 1),
         _ptr(admitted, "admitted", torch.int32, E),
         _ptr(rank_offsets, "rank_offsets", torch.int32, R + 1),
@@ -252,17 +256,32 @@ def moe_dispatch_q8(desc, admission, x, topk_idx, x_perm_q, row_scale, row_of_sl
     _raise("moe_dispatch_q8", st)
 
 
+def admission_flags(admission="token", layout="compact") -> int:
+    """Admission order plus layout as the C flags (strings or ints)."""
+    adm = ADMISSION[admission] if isinstance(admission, str) else int(admission)
+    return adm | (MOE_LAYOUT_PADDED if layout == "padded" else 0)
+
+
+def moe_dispatch_rows(desc, admission) -> int:
+    """Rows the dispatch lays out (N*k, or max(N*k, E*cap) when padded)."""
+    r = int(lib().moe_dispatch_rows(ctypes.byref(desc), int(admission)))
+    if r < 0:
+        raise ValueError("moe_dispatch_rows: invalid descriptor or admission flags")
+    return r
+
+
 def moe_dispatch_layout(desc, admission, topk_idx, row_of_slot, token_of_row, slot_of_row,
                         expert_offsets, admitted, rank_offsets, rank_counts, ws, stream=None):
     """The layout half of moe_dispatch_ex (no rows are moved)."""
     adm = ADMISSION[admission] if isinstance(admission, str) else int(admission)
     N, E, k, R = desc.num_tokens, desc.num_experts, desc.top_k, desc.num_ranks
     S = N * k
+    rows = S if not adm & MOE_LAYOUT_PADDED else moe_dispatch_rows(desc, adm)
     st = lib().moe_dispatch_layout(
         ctypes.byref(desc), adm, _ptr(topk_idx, "topk_idx", torch.int32, S, N > 0),
         _ptr(row_of_slot, "row_of_slot", torch.int32, S, N > 0),
-        _ptr(token_of_row, "token_of_row", torch.int32, S, N > 0),
-        _ptr(slot_of_row, "slot_of_row", torch.int8, S, N > 0),
+        _ptr(token_of_row, "token_of_row", torch.int32, rows, N > 0),
+        _ptr(slot_of_row, "slot_of_row", torch.int8, rows, N > 0),
         _ptr(expert_offsets, "expert_offsets", torch.int32, E + 1),
         _ptr(admitted, "admitted", torch.int32, E),
         _ptr(rank_offsets, "rank_offsets", torch.int32, R + 1),
@@ -314,15 +333,17 @@ def _dispatch(name, desc, admission, x, topk_idx, x_perm, row_of_slot, token_of_
     N, d, E, k, R = desc.num_tokens, desc.hidden, desc.num_experts, desc.top_k, desc.num_ranks
     dt = TORCH_DTYPE.get(desc.dtype)
     S = N * k
+    adm_flags = admission or 0
+    rows = S if not adm_flags & MOE_LAYOUT_PADDED else moe_dispatch_rows(desc, adm_flags)
     fn = getattr(lib(), name)
     head = (ctypes.byref(desc),) if admission is None else (ctypes.byref(desc), admission)
     st = fn(
         *head, _ptr(x, "x", dt, N * d, N > 0),
         _ptr(topk_idx, "topk_idx", torch.int32, S, N > 0),
-        _ptr(x_perm, "x_perm", dt, S * d, N > 0),
+        _ptr(x_perm, "x_perm", dt, rows * d, N > 0),
         _ptr(row_of_slot, "row_of_slot", torch.int32, S, N > 0),
-        _ptr(token_of_row, "token_of_row", torch.int32, S, N > 0),
-        _ptr(slot_of_row, "slot_of_row", torch.int8, S, N > 0),
+        _ptr(token_of_row, "token_of_row", torch.int32, rows, N > 0),
+        _ptr(slot_of_row, "slot_of_row", torch.int8, rows, N > 0),
         _ptr(expert_offsets, "expert_offsets", torch.int32, E + 1),
         _ptr(admitted, "admitted", torch.int32, E),
         _ptr(rank_offsets, "rank_offsets", torch.int32, R + 1),

@@ -118,6 +118,12 @@ int moe_dispatch(const moe_route_desc* desc, const void* x, const int32_t* topk_
                          rank_counts, ws, ws_bytes, stream);
 }
 
+// The padded layout needs a finite capacity and E * cap rows addressable as int32.
+static bool padded_layout_ok(const moe_route_desc* d) {
+  if (!(d->capacity_factor > 0.f)) return false;
+  return (long long)d->num_experts * capacity_of(d) <= 0x7fffffffLL;
+}
+
 // Shared by moe_dispatch_ex and moe_dispatch_q8: x_perm is the dtype rows or,
 // with xq set, the INT8 payload rows (then x_perm must be NULL).
 static int dispatch_common(const moe_route_desc* desc, int32_t admission, const void* x,
@@ -181,9 +187,10 @@ static int dispatch_common(const moe_route_desc* desc, int32_t admission, const 
   if (st != MOE_OK) return st;
   const bool layout = stages & moe::kDispatchLayout, permute = stages & moe::kDispatchPermute;
   const int N = desc->num_tokens;
+  const int padded = (admission & MOE_LAYOUT_PADDED) ? 1 : 0;
   if (layout) {
-    if (admission != MOE_ADMIT_TOKEN_ORDER && admission != MOE_ADMIT_FIRST_CHOICE)
-      return MOE_ERR_INVALID_ARG;
+    if (admission & ~(MOE_ADMIT_FIRST_CHOICE | MOE_LAYOUT_PADDED)) return MOE_ERR_INVALID_ARG;
+    if (padded && !padded_layout_ok(desc)) return MOE_ERR_INVALID_ARG;
     if (!expert_offsets || !admitted || !rank_offsets || !rank_counts) return MOE_ERR_INVALID_ARG;
     if (N > 0 && (!topk_idx || !row_of_slot || !token_of_row || !slot_of_row))
       return MOE_ERR_INVALID_ARG;
@@ -200,10 +207,20 @@ static int dispatch_common(const moe_route_desc* desc, int32_t admission, const 
   moe::DispatchArgs a{N, desc->hidden, desc->num_experts, desc->top_k, desc->num_ranks,
                       desc->dtype, capacity_of(desc), x, topk_idx, x_perm, row_of_slot,
                       token_of_row, slot_of_row, expert_offsets, admitted, rank_offsets,
-                      rank_counts, ws, admission == MOE_ADMIT_FIRST_CHOICE ? 1 : 0};
+                      rank_counts, ws, (admission & MOE_ADMIT_FIRST_CHOICE) ? 1 : 0};
   a.xq = xq;
   a.row_scale = row_scale;
+  a.padded = layout ? padded : 0;
   return status_of(moe::launch_dispatch(a, static_cast<hipStream_t>(stream), stages));
+}
+
+int64_t moe_dispatch_rows(const moe_route_desc* desc, int32_t admission) {
+  if (check_desc(desc) != MOE_OK) return -1;
+  if (admission & ~(MOE_ADMIT_FIRST_CHOICE | MOE_LAYOUT_PADDED)) return -1;
+  const int padded = (admission & MOE_LAYOUT_PADDED) ? 1 : 0;
+  if (padded && !padded_layout_ok(desc)) return -1;
+  return (int64_t)moe::dispatch_rows(desc->num_tokens, desc->top_k, desc->num_experts,
+                                     capacity_of(desc), padded);
 }
 
 int moe_dispatch_layout(const moe_route_desc* desc, int32_t admission, const int32_t* topk_idx,

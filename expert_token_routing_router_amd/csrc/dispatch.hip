@@ -65,6 +65,7 @@ __global__ __launch_bounds__(256) void dispatch_tile_hist(const int32_t* __restr
 // One block of 256 threads; thread e owns expert e.
 __global__ __launch_bounds__(256) void dispatch_scan(int32_t* __restrict__ tile_counts,
                                                      int num_tiles, int E, int R, int32_t cap,
+                                                     int padded,
                                                      int32_t* __restrict__ expert_offsets,
                                                      int32_t* __restrict__ admitted,
                                                      int32_t* __restrict__ rank_offsets,
@@ -92,14 +93,16 @@ __global__ __launch_bounds__(256) void dispatch_scan(int32_t* __restrict__ tile_
     scan[e] += v;
     __syncthreads();
   }
-  const int32_t excl = scan[e] - adm;
+  // Padded layout: expert e owns rows [e cap, (e+1) cap) whatever it admits.
+  const int32_t excl = padded ? e * cap : scan[e] - adm;
+  const int32_t total = padded ? E * cap : scan[e];
   if (e < E) {
     expert_offsets[e] = excl;
     offs[e] = excl;
   }
   if (e == E - 1) {
-    expert_offsets[E] = scan[e];
-    offs[E] = scan[e];
+    expert_offsets[E] = total;
+    offs[E] = total;
   }
   __syncthreads();
   const int per = E / R;
@@ -117,7 +120,7 @@ constexpr int kCountLds = 16384;  // ints
 __global__ __launch_bounds__(1024) void dispatch_count(const int32_t* __restrict__ topk_idx,
                                                        int S, int k, int first_choice,
                                                        int num_tiles, int E, int R,
-                                                       int32_t cap,
+                                                       int32_t cap, int padded,
                                                        int32_t* __restrict__ tile_base,
                                                        int32_t* __restrict__ expert_offsets,
                                                        int32_t* __restrict__ admitted,
@@ -170,7 +173,9 @@ __global__ __launch_bounds__(1024) void dispatch_count(const int32_t* __restrict
   if (lane == 63) scan[wv] = incl;
   __syncthreads();
   for (int w = 0; w < wv; ++w) incl += scan[w];
-  const int32_t excl = incl - adm;
+  // Padded layout: expert e owns rows [e cap, (e+1) cap) whatever it admits.
+  const int32_t excl = padded ? tid * cap : incl - adm;
+  if (padded) incl = E * cap;
   if (tid < E) {
     expert_offsets[tid] = excl;
     offs[tid] = excl;
@@ -463,6 +468,49 @@ hipError_t launch_dequantize_q8(int max_rows, int d, int dtype, const void* xq,
   return hipGetLastError();
 }
 
+// Padded layout: rows e cap + i with i >= admitted[e] are padding.  The index
+// pass marks them (token_of_row = slot_of_row = -1); the row pass zero-fills
+// them (x_perm rows, or the INT8 payload's codes and scale).  Admitted rows
+// are written by dispatch_assign / the permute and never touched here.
+__global__ __launch_bounds__(256) void dispatch_pad_index(const int32_t* __restrict__ admitted,
+                                                          int E, int32_t cap,
+                                                          int32_t* __restrict__ token_of_row,
+                                                          int8_t* __restrict__ slot_of_row) {
+  const long long rows = (long long)E * cap;
+  for (long long r = (long long)blockIdx.x * 256 + threadIdx.x; r < rows;
+       r += (long long)gridDim.x * 256) {
+    const int e = (int)(r / cap);
+    if (r - (long long)e * cap >= admitted[e]) {
+      token_of_row[r] = -1;
+      slot_of_row[r] = -1;
+    }
+  }
+}
+
+__global__ __launch_bounds__(256) void dispatch_pad_rows(const int32_t* __restrict__ admitted,
+                                                         int E, int32_t cap, int row_bytes,
+                                                         u32x4* __restrict__ rows_out,
+                                                         float* __restrict__ row_scale) {
+  const int lane = threadIdx.x % 64;
+  const long long rows = (long long)E * cap;
+  const int vec = row_bytes / 16;
+  for (long long r = (long long)blockIdx.x * 4 + threadIdx.x / 64; r < rows;
+       r += (long long)gridDim.x * 4) {
+    const int e = (int)(r / cap);
+    if (r - (long long)e * cap < admitted[e]) continue;
+    u32x4* dst = rows_out + r * vec;
+    for (int v = lane; v < vec; v += 64) dst[v] = u32x4{0u, 0u, 0u, 0u};
+    if (row_scale && lane == 0) row_scale[r] = 0.f;
+  }
+}
+
+size_t dispatch_rows(int N, int k, int E, int32_t cap, int padded) {
+  const size_t S = (size_t)N * k;
+  if (!padded) return S;
+  const size_t P = (size_t)E * (size_t)cap;
+  return P > S ? P : S;
+}
+
 size_t dispatch_workspace_bytes(int N, int k, int E) {
   const size_t S = (size_t)N * k;
   const size_t tiles = (S + kTileSlots - 1) / kTileSlots;
@@ -476,20 +524,27 @@ hipError_t launch_dispatch(const DispatchArgs& a, hipStream_t st, int stages) {
   if (stages & kDispatchLayout) {
     if (tiles > 0 && (long long)tiles * a.E <= kCountLds && a.E <= 1024) {
       dispatch_count<<<1, 1024, 0, st>>>(a.topk_idx, S, a.k, a.first_choice, tiles, a.E, a.R,
-                                         a.cap, tile_counts,
+                                         a.cap, a.padded, tile_counts,
                                          a.expert_offsets, a.admitted, a.rank_offsets,
                                          a.rank_counts);
     } else {
       if (tiles > 0)
         dispatch_tile_hist<<<tiles, 256, 0, st>>>(a.topk_idx, S, a.k, a.E, a.first_choice,
                                                   tile_counts);
-      dispatch_scan<<<1, 256, 0, st>>>(tile_counts, tiles, a.E, a.R, a.cap, a.expert_offsets,
-                                       a.admitted, a.rank_offsets, a.rank_counts);
+      dispatch_scan<<<1, 256, 0, st>>>(tile_counts, tiles, a.E, a.R, a.cap, a.padded,
+                                       a.expert_offsets, a.admitted, a.rank_offsets,
+                                       a.rank_counts);
     }
     if (tiles > 0)
       dispatch_assign<<<tiles, 256, 0, st>>>(a.topk_idx, S, a.k, a.first_choice, a.E, a.cap,
                                              tile_counts, a.expert_offsets, a.row_of_slot,
                                              a.token_of_row, a.slot_of_row);
+    if (a.padded) {
+      const long long rows = (long long)a.E * a.cap;
+      const int blocks = (int)std::min<long long>((rows + 255) / 256, 4096);
+      dispatch_pad_index<<<std::max(blocks, 1), 256, 0, st>>>(a.admitted, a.E, a.cap,
+                                                              a.token_of_row, a.slot_of_row);
+    }
   }
   if (!(stages & kDispatchPermute) || a.N == 0) return hipGetLastError();
   const int elem = a.dtype == 0 ? 4 : 2;
@@ -519,6 +574,13 @@ hipError_t launch_dispatch(const DispatchArgs& a, hipStream_t st, int stages) {
   } else {
     dispatch_permute<<<blocks, 256, 0, st>>>(static_cast<const u32x4*>(a.x), a.N, vec_per_row,
                                              a.k, a.row_of_slot, static_cast<u32x4*>(a.x_perm));
+  }
+  if (a.padded && a.admitted) {  // padding rows of the padded layout: zeros
+    const long long rows = (long long)a.E * a.cap;
+    const int pblocks = (int)std::max<long long>(1, std::min<long long>((rows + 3) / 4, 8192));
+    dispatch_pad_rows<<<pblocks, 256, 0, st>>>(
+        a.admitted, a.E, a.cap, a.xq ? a.d : a.d * elem,
+        static_cast<u32x4*>(a.xq ? a.xq : a.x_perm), a.xq ? a.row_scale : nullptr);
   }
   return hipGetLastError();
 }

@@ -50,7 +50,11 @@ struct DispatchArgs {
   int first_choice;  // 0: token order; 1: every token's slot j before any slot j + 1
   void* xq = nullptr;          // INT8 payload rows [N*k, d] (x_perm unused when set)
   float* row_scale = nullptr;  // one scale per payload row
+  int padded = 0;              // 1: expert e owns rows [e cap, (e+1) cap) (cap finite)
 };
+
+// Rows a dispatch lays out: N*k, or max(N*k, E*cap) for the padded layout.
+size_t dispatch_rows(int N, int k, int E, int32_t cap, int padded);
 
 // INT8 payload: the largest hidden size the register-resident quantiser takes,
 // and the receiver-side dequantisation of rows < *num_rows.

@@ -12,7 +12,8 @@ from __future__ import annotations
 import torch
 
 from . import (ACT, DTYPE, TORCH_DTYPE, desc_from_workload, moe_bias_update, moe_combine,
-               moe_dequantize_q8, moe_dispatch, moe_dispatch_ex, moe_dispatch_q8,
+               admission_flags, moe_dequantize_q8, moe_dispatch, moe_dispatch_ex,
+               moe_dispatch_q8, moe_dispatch_rows,
                moe_dispatch_workspace_size, moe_expert_ffn,
                moe_expert_ffn_pack_weights, moe_expert_ffn_workspace_size, moe_route,
                moe_route_workspace_size, workspace)
@@ -53,6 +54,11 @@ class MoeBuffers:
         d = self.desc
         N, E, k, R, dim = d.num_tokens, d.num_experts, d.top_k, d.num_ranks, d.hidden
         S = N * k
+        # Admission order and layout as the dispatch's flags; the padded layout
+        # (fixed cap rows per expert) lays out max(N*k, E*cap) rows.
+        self.flags = admission_flags(cfg.get("admission", "token"), cfg.get("layout", "compact"))
+        self.rows = moe_dispatch_rows(d, self.flags)
+        S_rows = max(self.rows, 1)
         dt = TORCH_DTYPE[d.dtype]
         i32 = dict(dtype=torch.int32, device=device)
         self.logits = torch.empty(N, E, dtype=torch.float32, device=device)
@@ -60,24 +66,24 @@ class MoeBuffers:
         self.topk_w = torch.empty(N, k, dtype=torch.float32, device=device)
         self.counts = torch.empty(E, **i32)
         self.ws_route = workspace(moe_route_workspace_size(d), device)
-        self.x_perm = torch.empty(max(S, 1), dim, dtype=dt, device=device)
+        self.x_perm = torch.empty(S_rows, dim, dtype=dt, device=device)
         # INT8 row payload of the dispatch exchange (workloads with
         # payload="int8"): codes and one scale per row, dequantised into x_perm.
         self.x_perm_q = self.row_scale = None
         if cfg.get("payload", "native") == "int8":
-            self.x_perm_q = torch.empty(max(S, 1), dim, dtype=torch.int8, device=device)
-            self.row_scale = torch.empty(max(S, 1), dtype=torch.float32, device=device)
+            self.x_perm_q = torch.empty(S_rows, dim, dtype=torch.int8, device=device)
+            self.row_scale = torch.empty(S_rows, dtype=torch.float32, device=device)
         self.row_of_slot = torch.empty(N, k, **i32)
-        self.token_of_row = torch.empty(max(S, 1), **i32)
-        self.slot_of_row = torch.empty(max(S, 1), dtype=torch.int8, device=device)
+        self.token_of_row = torch.empty(S_rows, **i32)
+        self.slot_of_row = torch.empty(S_rows, dtype=torch.int8, device=device)
         self.expert_offsets = torch.empty(E + 1, **i32)
         self.admitted = torch.empty(E, **i32)
         self.rank_offsets = torch.empty(R + 1, **i32)
         self.rank_counts = torch.empty(R, **i32)
         self.ws_dispatch = workspace(moe_dispatch_workspace_size(d), device)
-        self.y_perm = torch.empty(max(S, 1), dim, dtype=dt, device=device)
+        self.y_perm = torch.empty(S_rows, dim, dtype=dt, device=device)
         h = cfg["h"]
-        self.ws_ffn = workspace(moe_expert_ffn_workspace_size(E, S, dim, h, cfg["act"],
+        self.ws_ffn = workspace(moe_expert_ffn_workspace_size(E, self.rows, dim, h, cfg["act"],
                                                               cfg["dtype"]), device)
         self.shared_out = None
         if cfg.get("shared"):
@@ -99,17 +105,18 @@ def route(buf: MoeBuffers, inp: dict, sel_bias=None, stream=None):
 
 def dispatch(buf: MoeBuffers, inp: dict, stream=None):
     """Admission in token order unless the workload sets ``admission`` to
-    ``"first_choice"``.  With ``payload="int8"`` the rows travel as the INT8
-    payload and are dequantised into x_perm (what a receiving rank does)."""
-    adm = buf.cfg.get("admission", "token")
+    ``"first_choice"``; the compact layout unless it sets ``layout`` to
+    ``"padded"``.  With ``payload="int8"`` the rows travel as the INT8 payload
+    and are dequantised into x_perm (what a receiving rank does)."""
+    adm = buf.flags
     if buf.x_perm_q is not None:
         d = buf.desc
         moe_dispatch_q8(d, adm, inp["x"], buf.topk_idx, buf.x_perm_q, buf.row_scale,
                         buf.row_of_slot, buf.token_of_row, buf.slot_of_row, buf.expert_offsets,
                         buf.admitted, buf.rank_offsets, buf.rank_counts, buf.ws_dispatch, stream)
-        moe_dequantize_q8(d.num_tokens * d.top_k, d.hidden, d.dtype, buf.x_perm_q, buf.row_scale,
+        moe_dequantize_q8(buf.rows, d.hidden, d.dtype, buf.x_perm_q, buf.row_scale,
                           buf.expert_offsets[d.num_experts:], buf.x_perm, stream)
-    elif adm == "token":
+    elif adm == 0:
         moe_dispatch(buf.desc, inp["x"], buf.topk_idx, buf.x_perm, buf.row_of_slot,
                      buf.token_of_row, buf.slot_of_row, buf.expert_offsets, buf.admitted,
                      buf.rank_offsets, buf.rank_counts, buf.ws_dispatch, stream)
@@ -125,8 +132,7 @@ def routed_ffn(buf: MoeBuffers, inp: dict, stream=None):
     d, cfg = buf.desc, buf.cfg
     if not inp.get("weights_packed"):
         raise ValueError("expert_ffn needs the weights from prepare_weights(cfg, inp)")
-    S = d.num_tokens * d.top_k
-    moe_expert_ffn(d.num_experts, S, d.hidden, cfg["h"], cfg["act"], cfg["dtype"], buf.x_perm,
+    moe_expert_ffn(d.num_experts, buf.rows, d.hidden, cfg["h"], cfg["act"], cfg["dtype"], buf.x_perm,
                    buf.expert_offsets, inp["w1"], inp.get("w3"), inp["w2"], buf.y_perm,
                    buf.ws_ffn, stream)
 

@@ -179,9 +179,25 @@ int moe_dispatch(const moe_route_desc* desc, const void* x, const int32_t* topk_
 /* Admission orders of moe_dispatch_ex. */
 typedef enum {
   MOE_ADMIT_TOKEN_ORDER = 0,  /* tokens in order, a token's slots j = 0..k-1 in turn */
-  MOE_ADMIT_FIRST_CHOICE = 1  /* slot 0 of every token (in token order), then slot 1
+  MOE_ADMIT_FIRST_CHOICE = 1, /* slot 0 of every token (in token order), then slot 1
                                  of every token, and so on */
+  MOE_LAYOUT_PADDED = 2       /* flag, with either order: fixed buffers of cap rows per
+                                 expert (see moe_dispatch_rows) */
 } moe_admission;
+
+/* Rows a dispatch with these admission flags lays out: N*k for the compact
+ * layout; max(N*k, E*cap) with MOE_LAYOUT_PADDED.  EP notes, "参考答案" answer 2,
+ * sizes each expert's buffer as the mean load times the capacity factor; the
+ * padded layout is that buffer: expert e owns rows [e*cap, (e+1)*cap),
+ * expert_offsets[e] = e*cap (so moe_expert_ffn runs every row of the buffer,
+ * GShard's static shapes), its admitted rows come first in admission order,
+ * and the rest are padding: token_of_row = slot_of_row = -1 and, from
+ * moe_dispatch_ex / moe_dispatch_q8, zero rows (zero codes, scale 0), whose
+ * FFN output is zero and which moe_combine never reads.  rank_counts are then
+ * (E/R)*cap: an all-to-all of fixed size.  x_perm, token_of_row, slot_of_row
+ * (and x_perm_q, row_scale) need this many rows.  The padded layout needs a
+ * finite capacity (cf > 0).  Returns -1 for an invalid descriptor or flags. */
+int64_t moe_dispatch_rows(const moe_route_desc* desc, int32_t admission);
 
 /* Dispatch with a choice of admission order.  MLSys ch.10, section 10.5 names
  * GShard's top-2 router, whose first choices outrank second choices when an
@@ -194,7 +210,9 @@ typedef enum {
  * admitted = min(count_e, cap), rank offsets, workspace size, errors -- is as
  * for moe_dispatch, which is moe_dispatch_ex with MOE_ADMIT_TOKEN_ORDER.  With
  * k = 1, or with no capacity limit, both orders admit the same slots.
- * Returns MOE_ERR_INVALID_ARG for any other admission value. */
+ * admission may also carry MOE_LAYOUT_PADDED (see moe_dispatch_rows for the
+ * layout and the buffer sizes).  Returns MOE_ERR_INVALID_ARG for any other
+ * admission value, and for MOE_LAYOUT_PADDED without a capacity. */
 int moe_dispatch_ex(const moe_route_desc* desc, int32_t admission, const void* x,
                     const int32_t* topk_idx, void* x_perm, int32_t* row_of_slot,
                     int32_t* token_of_row, int8_t* slot_of_row, int32_t* expert_offsets,
@@ -208,7 +226,9 @@ int moe_dispatch_ex(const moe_route_desc* desc, int32_t admission, const void* x
  *   every output of moe_dispatch_ex except x_perm (arguments, workspace and
  *   errors as there; x is not read).
  * moe_permute: x_perm[row_of_slot[t, j]] = x[t] for every admitted slot (the
- *   permute of moe_dispatch; row_of_slot from moe_dispatch_layout).
+ *   permute of moe_dispatch; row_of_slot from moe_dispatch_layout).  It writes
+ *   admitted rows only: padding rows of a padded layout are left as they are
+ *   (the whole-dispatch calls zero them).
  * moe_permute_q8: the same rows as the INT8 payload (codes and scales exactly
  *   as moe_dispatch_q8).
  * A layout followed by a permute on one stream equals one moe_dispatch_ex /

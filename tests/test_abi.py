@@ -121,9 +121,20 @@ def test_dispatch_ex_validation():
     d = moe.route_desc(64, 64, 8, 2, R=4, cf=1.25)
     need = moe.moe_dispatch_workspace_size(d)
     args = [FAKE] * 10
-    for adm in (-1, 2, 7):
+    for adm in (-1, 4, 7, 8):
         assert lib.moe_dispatch_ex(ctypes.byref(d), adm, *args, FAKE, need,
                                    None) == moe.MOE_ERR_INVALID_ARG
+    # The padded layout needs a capacity.
+    nocap = moe.route_desc(64, 64, 8, 2, R=4, cf=0.0)
+    need0 = moe.moe_dispatch_workspace_size(nocap)
+    for adm in (moe.MOE_LAYOUT_PADDED, moe.MOE_LAYOUT_PADDED | moe.MOE_ADMIT_FIRST_CHOICE):
+        assert lib.moe_dispatch_ex(ctypes.byref(nocap), adm, *args, FAKE, need0,
+                                   None) == moe.MOE_ERR_INVALID_ARG
+        assert lib.moe_dispatch_rows(ctypes.byref(nocap), adm) == -1
+    # Rows: N*k compact, max(N*k, E*cap) padded (cap = ceil(1.25 * 128 / 8) = 20).
+    assert lib.moe_dispatch_rows(ctypes.byref(d), 0) == 128
+    assert lib.moe_dispatch_rows(ctypes.byref(d), moe.MOE_LAYOUT_PADDED) == 160
+    assert lib.moe_dispatch_rows(ctypes.byref(d), 4) == -1
     for adm in (moe.MOE_ADMIT_TOKEN_ORDER, moe.MOE_ADMIT_FIRST_CHOICE):
         assert lib.moe_dispatch_ex(ctypes.byref(d), adm, *args, FAKE, need - 4,
                                    None) == moe.MOE_ERR_WORKSPACE
@@ -165,7 +176,7 @@ def test_dispatch_halves_validation():
     outs = [FAKE] * 7  # row_of_slot .. rank_counts
     assert lib.moe_dispatch_layout(ctypes.byref(d), 0, FAKE, *outs, FAKE, need - 4,
                                    None) == moe.MOE_ERR_WORKSPACE
-    assert lib.moe_dispatch_layout(ctypes.byref(d), 3, FAKE, *outs, FAKE, need,
+    assert lib.moe_dispatch_layout(ctypes.byref(d), 4, FAKE, *outs, FAKE, need,
                                    None) == moe.MOE_ERR_INVALID_ARG
     assert lib.moe_dispatch_layout(ctypes.byref(d), 0, None, *outs, FAKE, need,
                                    None) == moe.MOE_ERR_INVALID_ARG

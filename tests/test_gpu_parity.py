@@ -36,6 +36,9 @@ CASES = {
     # Rows travel as the INT8 payload and are dequantised before the FFN.
     "switch-small-int8": W.with_(W.small("switch"), payload="int8"),
     "toy-small-int8": W.with_(W.small("toy"), payload="int8"),
+    # GShard-style fixed buffers: cap rows per expert, padding rows zero.
+    "zipf-small-cf1.0-padded": W.with_(W.small("zipf"), cf=1.0, layout="padded"),
+    "switch-small-padded-int8": W.with_(W.small("switch"), layout="padded", payload="int8"),
 }
 
 _cache = {}
@@ -410,6 +413,33 @@ def test_dispatch_halves_equal_one_call(payload, admission):
         assert torch.equal(one.row_scale[:M].view(torch.int32), two.row_scale[:M].view(torch.int32))
     else:
         assert torch.equal(one.x_perm[:M].view(torch.int16), two.x_perm[:M].view(torch.int16))
+
+
+@pytest.mark.parametrize("name,kw", [
+    ("switch", {}),
+    ("zipf", dict(cf=1.25, admission="first_choice")),
+    ("switch", dict(payload="int8")),
+])
+def test_padded_layout_output_equals_compact(name, kw):
+    """The layer with the padded layout (the FFN runs every buffer row, padding
+    included) gives the compact layout's y bit for bit: each row's output
+    depends on that row only, and padding rows are never combined."""
+    cfg = W.with_(W.small(name), **kw)
+    print(f"[padded vs compact] {name} {kw}", flush=True)
+    inp = moe.prepare_weights(cfg, to_dev(W.make_inputs(cfg)))
+    com = moe.MoeBuffers(cfg)
+    pad = moe.MoeBuffers(W.with_(cfg, layout="padded"))
+    moe.moe_forward(com, inp)
+    moe.moe_forward(pad, inp)
+    torch.cuda.synchronize()
+    assert pad.rows >= com.rows
+    assert torch.equal(com.y.view(torch.int16), pad.y.view(torch.int16))
+    cap = oracle.capacity(cfg)
+    E = cfg["E"]
+    assert torch.equal(pad.expert_offsets.cpu(), torch.arange(E + 1, dtype=torch.int32) * cap)
+    live = pad.token_of_row[:E * cap] >= 0
+    assert int(live.sum()) == int(com.admitted.sum())
+    assert bool((pad.y_perm[:E * cap][~live].float() == 0).all()), "padding rows must stay zero"
 
 
 def test_all_tokens_to_one_expert_with_capacity():
