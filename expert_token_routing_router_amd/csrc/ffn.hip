@@ -190,7 +190,7 @@ __host__ __device__ __forceinline__ int packed_slab_rows(int N) { return N % 256
 // The epilogue converts to bf16 in registers (v_cvt_pk_bf16_f32), swaps
 // half-rows between lanes l and l+32 (v_permlane32_swap) so each lane owns 8
 // consecutive columns, and stores 16 bytes per lane straight to global memory.
-constexpr int kGemmBM = 320, kGemmWaves = 8;
+constexpr int kGemmBM = 320, kGemmBMSmall = 128, kGemmWaves = 8;
 // Cache-policy bits of the weight loads (nt | sc1 on gfx950): each weight
 // byte is read once per launch, so it is fetched as streaming data.  Measured
 // with the operand stream alone (no MFMA): 0.98 against 1.04 us per K stage.
@@ -205,14 +205,14 @@ constexpr int kWeightCpol = 2 | 16;
 // so a down tile's K stage is one contiguous run.
 enum { kUpGemm = 0, kDownGemm = 1 };
 
-template <int BN, int ACT, int MODE>
+template <int BM, int BN, int ACT, int MODE>
 __global__ __launch_bounds__(kGemmWaves * 64, 1) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void grouped_gemm_bf16(
     const bf16_t* __restrict__ A, const bf16_t* __restrict__ B, const bf16_t* __restrict__ B2,
     bf16_t* __restrict__ C, int K, int N, const int4* __restrict__ tiles,
     const int32_t* __restrict__ tile_count, int n_tiles, int ldg, int gm) {
   constexpr bool DUAL = ACT == ACT_SWIGLU;
-  constexpr int BM = kGemmBM, BK = 32, RB = BK * 2;  // RB: bytes per staged row
+  constexpr int BK = 32, RB = BK * 2;  // RB: bytes per staged row
   constexpr int CH = BK / 8;                         // 16-byte chunks per row
   constexpr int RPL = 1024 / RB;                     // rows per 1-KB load
   constexpr int KK = BK / 16;                        // MFMA K steps per stage
@@ -567,14 +567,22 @@ void grouped_gemm_bf16(
     MOE_EPILOGUE(FA_);                                                                     \
   } while (0)
 
-  static_assert(FM == 5, "one copy per live-fragment count 0..5");
-  switch (fa) {
-    case 0: MOE_TILE(0); break;
-    case 1: MOE_TILE(1); break;
-    case 2: MOE_TILE(2); break;
-    case 3: MOE_TILE(3); break;
-    case 4: MOE_TILE(4); break;
-    default: MOE_TILE(5); break;
+  static_assert(FM == 5 || FM == 2, "one copy per live-fragment count 0..FM");
+  if constexpr (FM == 5) {
+    switch (fa) {
+      case 0: MOE_TILE(0); break;
+      case 1: MOE_TILE(1); break;
+      case 2: MOE_TILE(2); break;
+      case 3: MOE_TILE(3); break;
+      case 4: MOE_TILE(4); break;
+      default: MOE_TILE(5); break;
+    }
+  } else {
+    switch (fa) {
+      case 0: MOE_TILE(0); break;
+      case 1: MOE_TILE(1); break;
+      default: MOE_TILE(2); break;
+    }
   }
 #undef MOE_TILE
 #undef MOE_EPILOGUE
@@ -699,20 +707,33 @@ constexpr int kF32BM = 64, kF32BN = 64;
 
 static size_t align256(size_t x) { return (x + 255) / 256 * 256; }
 
-static int ffn_bm(int dtype) { return dtype == 0 ? kF32BM : kGemmBM; }
+// Row-tile height.  bf16: 320 rows, which take a whole expert at capacity
+// factor 1.25 of 256 rows.  128 rows when experts average at most 32 rows
+// (decode-sized batches): such tiles hold two live fragments per wave instead
+// of five, which leaves the accumulators for twice the columns (half the
+// column tiles, so half the prologues and epilogues) and drops the requests
+// for rows past a 320-row tile.  Only where one tile per expert is all but
+// certain: an expert of more rows than a tile is split, and each of its row
+// tiles streams the expert's weights again (DeepSeek-like layer, 128 rows per
+// expert on average but spread around that: 5.75 -> 6.63 ms per step with
+// 128-row tiles; decode, ~8 rows per expert: 3.77 -> 3.64 ms).
+static int ffn_bm(int dtype, int E, int max_rows) {
+  if (dtype == 0) return kF32BM;
+  return (long long)max_rows <= 32LL * E ? kGemmBMSmall : kGemmBM;
+}
 
 // Upper bound of row tiles: every expert may end in a partial tile.
 static int max_m_tiles(int max_rows, int BM, int E) { return (max_rows + BM - 1) / BM + E; }
 
 static size_t ffn_plan_bytes(int E, int max_rows, int dtype) {
   return align256(sizeof(int32_t)) +
-         align256((size_t)max_m_tiles(max_rows, ffn_bm(dtype), E) * sizeof(int4));
+         align256((size_t)max_m_tiles(max_rows, ffn_bm(dtype, E, max_rows), E) * sizeof(int4));
 }
 
 // 16-row groups of the packed bf16 hidden buffer: each tile rounds its rows up
 // to whole groups, so at most one partial group per tile.
 static int ffn_groups(int E, int max_rows) {
-  return (max_rows + 15) / 16 + max_m_tiles(max_rows, kGemmBM, E);
+  return (max_rows + 15) / 16 + max_m_tiles(max_rows, ffn_bm(1, E, max_rows), E);
 }
 
 size_t ffn_workspace_bytes(int E, int max_rows, int d, int h, int act, int dtype) {
@@ -737,21 +758,22 @@ static int grid_of(int m_tiles, int n_tiles) {
 }
 
 hipError_t launch_ffn_plan(const FfnArgs& a, hipStream_t st) {
-  ffn_plan_tiles<<<1, 1024, 0, st>>>(a.offsets, a.E, ffn_bm(a.dtype), a.max_rows, ffn_tiles(a),
+  ffn_plan_tiles<<<1, 1024, 0, st>>>(a.offsets, a.E, ffn_bm(a.dtype, a.E, a.max_rows), a.max_rows,
+                                     ffn_tiles(a),
                                      ffn_count(a));
   return hipGetLastError();
 }
 
-template <int BN, int ACT, int MODE>
+template <int BM, int BN, int ACT, int MODE>
 static void launch_bf16(const bf16_t* A, const bf16_t* B, const bf16_t* B2, bf16_t* C, int K,
                         int N, const FfnArgs& a, hipStream_t st) {
   const int nt = (N + BN - 1) / BN;
-  const int g = grid_of(max_m_tiles(a.max_rows, kGemmBM, a.E), nt);
+  const int g = grid_of(max_m_tiles(a.max_rows, BM, a.E), nt);
   // Groups of 4 row tiles once experts average two or more row tiles: an XCD's
   // 32 concurrent blocks then cover 4 x 8 tiles, and its L2 misses per K stage
   // fall from 1 A tile + 32 weight slabs to 4 A tiles + 8 weight slabs.
-  const int gm = a.max_rows / a.E >= 2 * kGemmBM ? 4 : 1;
-  grouped_gemm_bf16<BN, ACT, MODE><<<g, kGemmWaves * 64, 0, st>>>(
+  const int gm = a.max_rows / a.E >= 2 * BM ? 4 : 1;
+  grouped_gemm_bf16<BM, BN, ACT, MODE><<<g, kGemmWaves * 64, 0, st>>>(
       A, B, B2, C, K, N, ffn_tiles(a), ffn_count(a), nt, ffn_groups(a.E, a.max_rows), gm);
 }
 
@@ -777,13 +799,27 @@ hipError_t launch_ffn_up(const FfnArgs& a, hipStream_t st) {
     auto W1 = static_cast<const bf16_t*>(a.w1);
     auto W3 = static_cast<const bf16_t*>(a.w3);
     auto H = static_cast<bf16_t*>(ffn_hidden_buf(a));
-    if (a.act == ACT_SWIGLU) launch_bf16<128, ACT_SWIGLU, kUpGemm>(X, W1, W3, H, a.d, a.h, a, st);
-    else if (a.h >= 2048) {
-      if (a.act == ACT_RELU) launch_bf16<256, ACT_RELU, kUpGemm>(X, W1, nullptr, H, a.d, a.h, a, st);
-      else launch_bf16<256, ACT_GELU, kUpGemm>(X, W1, nullptr, H, a.d, a.h, a, st);
+    if (ffn_bm(1, a.E, a.max_rows) == kGemmBMSmall) {
+      // 128-row tiles: twice the columns per tile for the same accumulators.
+      constexpr int S = kGemmBMSmall;
+      if (a.act == ACT_SWIGLU) {
+        if (a.h >= 1024) launch_bf16<S, 256, ACT_SWIGLU, kUpGemm>(X, W1, W3, H, a.d, a.h, a, st);
+        else launch_bf16<S, 128, ACT_SWIGLU, kUpGemm>(X, W1, W3, H, a.d, a.h, a, st);
+      } else if (a.h >= 2048) {
+        if (a.act == ACT_RELU) launch_bf16<S, 512, ACT_RELU, kUpGemm>(X, W1, nullptr, H, a.d, a.h, a, st);
+        else launch_bf16<S, 512, ACT_GELU, kUpGemm>(X, W1, nullptr, H, a.d, a.h, a, st);
+      } else {
+        if (a.act == ACT_RELU) launch_bf16<S, 256, ACT_RELU, kUpGemm>(X, W1, nullptr, H, a.d, a.h, a, st);
+        else launch_bf16<S, 256, ACT_GELU, kUpGemm>(X, W1, nullptr, H, a.d, a.h, a, st);
+      }
+    } else if (a.act == ACT_SWIGLU) {
+      launch_bf16<kGemmBM, 128, ACT_SWIGLU, kUpGemm>(X, W1, W3, H, a.d, a.h, a, st);
+    } else if (a.h >= 2048) {
+      if (a.act == ACT_RELU) launch_bf16<kGemmBM, 256, ACT_RELU, kUpGemm>(X, W1, nullptr, H, a.d, a.h, a, st);
+      else launch_bf16<kGemmBM, 256, ACT_GELU, kUpGemm>(X, W1, nullptr, H, a.d, a.h, a, st);
     } else {
-      if (a.act == ACT_RELU) launch_bf16<128, ACT_RELU, kUpGemm>(X, W1, nullptr, H, a.d, a.h, a, st);
-      else launch_bf16<128, ACT_GELU, kUpGemm>(X, W1, nullptr, H, a.d, a.h, a, st);
+      if (a.act == ACT_RELU) launch_bf16<kGemmBM, 128, ACT_RELU, kUpGemm>(X, W1, nullptr, H, a.d, a.h, a, st);
+      else launch_bf16<kGemmBM, 128, ACT_GELU, kUpGemm>(X, W1, nullptr, H, a.d, a.h, a, st);
     }
   }
   return hipGetLastError();
@@ -798,8 +834,15 @@ hipError_t launch_ffn_down(const FfnArgs& a, hipStream_t st) {
     auto H = static_cast<const bf16_t*>(ffn_hidden_buf(a));
     auto W2 = static_cast<const bf16_t*>(a.w2);
     auto Y = static_cast<bf16_t*>(a.y_rows);
-    if (a.d >= 1024) launch_bf16<256, ACT_NONE, kDownGemm>(H, W2, nullptr, Y, a.h, a.d, a, st);
-    else launch_bf16<128, ACT_NONE, kDownGemm>(H, W2, nullptr, Y, a.h, a.d, a, st);
+    if (ffn_bm(1, a.E, a.max_rows) == kGemmBMSmall) {
+      constexpr int S = kGemmBMSmall;
+      if (a.d >= 2048) launch_bf16<S, 512, ACT_NONE, kDownGemm>(H, W2, nullptr, Y, a.h, a.d, a, st);
+      else launch_bf16<S, 256, ACT_NONE, kDownGemm>(H, W2, nullptr, Y, a.h, a.d, a, st);
+    } else if (a.d >= 1024) {
+      launch_bf16<kGemmBM, 256, ACT_NONE, kDownGemm>(H, W2, nullptr, Y, a.h, a.d, a, st);
+    } else {
+      launch_bf16<kGemmBM, 128, ACT_NONE, kDownGemm>(H, W2, nullptr, Y, a.h, a.d, a, st);
+    }
   }
   return hipGetLastError();
 }

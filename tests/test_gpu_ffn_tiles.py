@@ -7,7 +7,8 @@ per-expert row counts below sit on every one of those edges (0, 1, 31/32/33,
 160/161, 319/320/321, 641), with output widths that are and are not a
 multiple of the column tile.  Experts of many row tiles take the grouped
 block order (4 row tiles walk their column tiles together), with a short last
-group.  Reference: the oracle's grouped FFN on the same
+group; decode-sized batches take 128-row tiles with wider column tiles.
+Reference: the oracle's grouped FFN on the same
 rows (glossary "Expert Parallelism", step 3), per-tensor max relative error
 within 2e-2 (bf16) / 1e-4 (fp32).
 """
@@ -88,6 +89,20 @@ def test_ffn_row_tile_edges(d, h, act, dtype):
 @pytest.mark.parametrize("act", ["gelu", "swiglu"])
 def test_ffn_grouped_row_tiles(act):
     _check_ffn(512, 1024, act, "bf16", [1500, 0, 700, 2100], seed=77)
+
+
+# Decode-sized batches (at most 32 rows per expert on average) take 128-row
+# tiles with twice the columns per tile: experts of 0, 1, 31/32/33, 64, 127,
+# 128, 129 (split in two) and 300 (split in three) rows among many small ones,
+# with output widths that are and are not a multiple of the wider column tile.
+SMALL_COUNTS = [0, 1, 31, 32, 33, 64, 127, 128, 129, 300] + [3, 0, 7, 1] * 24
+
+
+@pytest.mark.parametrize("d,h,act", [(512, 1024, "swiglu"), (512, 2048, "gelu"),
+                                     (2048, 640, "swiglu"), (384, 512, "relu")])
+def test_ffn_small_row_tiles(d, h, act):
+    assert sum(SMALL_COUNTS) + 7 <= 32 * len(SMALL_COUNTS), "must take the 128-row tiles"
+    _check_ffn(d, h, act, "bf16", SMALL_COUNTS, seed=d + 3 * h)
 
 
 def _check_ffn(d, h, act, dtype, counts, seed):
