@@ -268,3 +268,16 @@ def test_binding_requires_device_tensors():
     x = torch.zeros(4, 64, dtype=torch.bfloat16)
     with pytest.raises(ValueError):
         moe.moe_route(desc, x, x, None, None, None, None, None, None, None)
+
+
+def test_bench_refuses_more_than_one_gpu(capsys, monkeypatch):
+    """bench.py --gpus 2 prints why and exits with status 2 before touching a GPU."""
+    import json
+    import sys
+
+    import bench
+    monkeypatch.setattr(sys, "argv", ["bench.py", "--gpus", "2"])
+    with pytest.raises(SystemExit) as ex:
+        bench.main()
+    assert ex.value.code == 2
+    assert "one GPU" in json.loads(capsys.readouterr().out.strip())["error"]
