@@ -79,6 +79,7 @@ def lib():
             "oracle_ffn_row": [I32, I32, I32, I32, P, P, P, P, P],
             "oracle_expert_ffn": [I32, I32, I32, I32, I32, P, P, P, P, P, P],
             "oracle_combine": [I32, I32, I32, I32, P, P, P, P, P, P],
+            "oracle_combine_backward": [I32, I32, I32, I32, P, P, P, P, P, P],
             "oracle_bias_update": [I32, I32, I32, P, F32, P],
         }
         for name, args in sig.items():
@@ -249,6 +250,28 @@ def combine(dtype: str, y_perm, row_of_slot, topk_w, residual=None, shared_out=N
                                 _ptr(topk_w), _ptr(residual), _ptr(shared_out), _ptr(y)),
            "oracle_combine")
     return y
+
+
+def combine_backward(dtype: str, dy, y_perm, row_of_slot, topk_w, num_rows: int) -> tuple:
+    """(dy_perm [num_rows, d], dtopk_w [N, k]); rows no slot maps to are zero."""
+    ed = _elem_dtype(dtype)
+    dy, y_perm = _c(dy, ed), _c(y_perm, ed)
+    row_of_slot, topk_w = _c(row_of_slot, np.int32), _c(topk_w, np.float32)
+    N, k = row_of_slot.shape
+    d = dy.shape[1]
+    dy_perm = np.zeros((max(num_rows, 0), d), ed)
+    dw = np.empty((N, k), np.float32)
+    _check(lib().oracle_combine_backward(N, d, k, DTYPE_CODES[dtype], _ptr(dy), _ptr(y_perm),
+                                         _ptr(row_of_slot), _ptr(topk_w), _ptr(dy_perm),
+                                         _ptr(dw)), "oracle_combine_backward")
+    return dy_perm, dw
+
+
+def permute_backward(dtype: str, dx_perm, row_of_slot) -> np.ndarray:
+    """dx[t] = sum over the token's admitted rows of dx_perm: the combine with
+    unit weights and no residual."""
+    row_of_slot = _c(row_of_slot, np.int32)
+    return combine(dtype, dx_perm, row_of_slot, np.ones(row_of_slot.shape, np.float32))
 
 
 def bias_update(num_tokens: int, top_k: int, counts, sel_bias, step: float = 1e-3):

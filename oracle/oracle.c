@@ -559,6 +559,42 @@ int oracle_combine(int32_t num_tokens, int32_t hidden, int32_t top_k, int32_t dt
   return 0;
 }
 
+/* Backward of the combine's expert terms (the layer's training step reads the
+ * four steps of [EP-glossary] "How tokens travel between GPUs" backwards): for
+ * every admitted slot (t, j) with row r = row_of_slot[t, j] and weight w,
+ *   dy_perm[r]    = w * dy[t]                    (fp64, rounded once to the dtype)
+ *   dtopk_w[t, j] = sum_i dy[t, i] * y_perm[r, i] (fp64, rounded once to fp32)
+ * A dropped slot gets dtopk_w = 0 and writes no row.  The residual and shared
+ * terms pass dy through unchanged (no computation).  The permute's backward is
+ * the combine itself with unit weights and no residual: dx[t] = sum over the
+ * token's admitted rows of dx_perm (oracle_combine). */
+int oracle_combine_backward(int32_t num_tokens, int32_t hidden, int32_t top_k, int32_t dtype,
+                            const void* dy, const void* y_perm, const int32_t* row_of_slot,
+                            const float* topk_w, void* dy_perm, float* dtopk_w) {
+  if (num_tokens < 0 || hidden < 1 || top_k < 1 || !dtype_ok(dtype)) return -1;
+  if (num_tokens > 0 && (!dy || !y_perm || !row_of_slot || !topk_w || !dy_perm || !dtopk_w))
+    return -1;
+  for (int32_t t = 0; t < num_tokens; ++t) {
+    for (int32_t j = 0; j < top_k; ++j) {
+      const size_t slot = (size_t)t * top_k + j;
+      const int32_t row = row_of_slot[slot];
+      if (row < 0) {
+        dtopk_w[slot] = 0.0f;
+        continue;
+      }
+      const double w = (double)topk_w[slot];
+      double dot = 0.0;
+      for (int32_t i = 0; i < hidden; ++i) {
+        const double g = elem(dy, dtype, (size_t)t * hidden + i);
+        dot += g * elem(y_perm, dtype, (size_t)row * hidden + i);
+        store(dy_perm, dtype, (size_t)row * hidden + i, w * g);
+      }
+      dtopk_w[slot] = (float)dot;
+    }
+  }
+  return 0;
+}
+
 /* ------------------------------------------------------------ bias update -- */
 
 /* Bias-based balancing: after each step the bias of overloaded experts goes

@@ -128,6 +128,14 @@ int oracle_combine(int32_t num_tokens, int32_t hidden, int32_t top_k, int32_t dt
                    const void* residual, const void* shared_out, void* y);
 
 /* Selection-bias update from pre-capacity counts. */
+/* Backward of the combine's expert terms: dy_perm[r] = w * dy[t] (rounded to the
+ * dtype) and dtopk_w[t, j] = <dy[t], y_perm[r]> (fp64 sum, rounded to fp32) for
+ * every admitted slot; dropped slots get dtopk_w = 0.  (The permute's backward
+ * is oracle_combine with unit weights and no residual.) */
+int oracle_combine_backward(int32_t num_tokens, int32_t hidden, int32_t top_k, int32_t dtype,
+                            const void* dy, const void* y_perm, const int32_t* row_of_slot,
+                            const float* topk_w, void* dy_perm, float* dtopk_w);
+
 int oracle_bias_update(int32_t num_experts, int32_t num_tokens, int32_t top_k,
                        const int32_t* counts, float step, float* sel_bias);
 
