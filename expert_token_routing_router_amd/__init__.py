@@ -40,7 +40,7 @@ EXPORTS = [
     "moe_route_workspace_size", "moe_route", "moe_router_logits",
     "moe_dispatch_workspace_size", "moe_dispatch", "moe_dispatch_ex", "moe_dispatch_q8",
     "moe_dequantize_q8", "moe_dispatch_layout", "moe_permute", "moe_permute_q8",
-    "moe_dispatch_rows",
+    "moe_dispatch_rows", "moe_combine_backward", "moe_permute_backward",
     "moe_expert_ffn_workspace_size", "moe_expert_ffn", "moe_expert_ffn_plan",
     "moe_expert_ffn_up", "moe_expert_ffn_down", "moe_expert_ffn_pack_weights", "moe_combine",
     "moe_bias_update", "moe_status_string",
@@ -108,6 +108,8 @@ def lib() -> ctypes.CDLL:
             "moe_permute": ([D, P, P, P, P], I32),
             "moe_permute_q8": ([D, P, P, P, P, P], I32),
             "moe_dispatch_rows": ([D, I32], ctypes.c_int64),
+            "moe_combine_backward": ([D, P, P, P, P, P, P, P], I32),
+            "moe_permute_backward": ([D, P, P, P, P], I32),
             "moe_expert_ffn_workspace_size": ([I32, I32, I32, I32, I32, I32], SZ),
             "moe_expert_ffn": ([I32, I32, I32, I32, I32, I32, P, P, P, P, P, P, P, SZ, P], I32),
             "moe_expert_ffn_plan": ([I32, I32, I32, I32, I32, I32, P, P, SZ, P], I32),
@@ -434,6 +436,35 @@ def moe_combine(desc, y_perm, row_of_slot, topk_w, residual, shared_out, y, stre
         _ptr(shared_out, "shared_out", dt, N * d, False),
         _ptr(y, "y", dt, N * d, N > 0), _stream(stream))
     _raise("moe_combine", st)
+
+
+def moe_combine_backward(desc, dy, y_perm, row_of_slot, topk_w, dy_perm, dtopk_w,
+                         num_rows=None, stream=None):
+    """dy_perm[r] = w * dy[t] and dtopk_w[t, j] = <dy[t], y_perm[r]> for every
+    admitted slot (backward of the combine's expert terms)."""
+    N, d, k = desc.num_tokens, desc.hidden, desc.top_k
+    dt = TORCH_DTYPE.get(desc.dtype)
+    rows = N * k if num_rows is None else num_rows
+    st = lib().moe_combine_backward(
+        ctypes.byref(desc), _ptr(dy, "dy", dt, N * d, N > 0),
+        _ptr(y_perm, "y_perm", dt, rows * d, N > 0),
+        _ptr(row_of_slot, "row_of_slot", torch.int32, N * k, N > 0),
+        _ptr(topk_w, "topk_w", torch.float32, N * k, N > 0),
+        _ptr(dy_perm, "dy_perm", dt, rows * d, N > 0),
+        _ptr(dtopk_w, "dtopk_w", torch.float32, N * k, N > 0), _stream(stream))
+    _raise("moe_combine_backward", st)
+
+
+def moe_permute_backward(desc, dx_perm, row_of_slot, dx, num_rows=None, stream=None):
+    """dx[t] = sum of the token's admitted rows of dx_perm (adjoint of the permute)."""
+    N, d, k = desc.num_tokens, desc.hidden, desc.top_k
+    dt = TORCH_DTYPE.get(desc.dtype)
+    rows = N * k if num_rows is None else num_rows
+    st = lib().moe_permute_backward(
+        ctypes.byref(desc), _ptr(dx_perm, "dx_perm", dt, rows * d, N > 0),
+        _ptr(row_of_slot, "row_of_slot", torch.int32, N * k, N > 0),
+        _ptr(dx, "dx", dt, N * d, N > 0), _stream(stream))
+    _raise("moe_permute_backward", st)
 
 
 def moe_bias_update(num_experts, num_tokens, top_k, counts, step, sel_bias, stream=None):

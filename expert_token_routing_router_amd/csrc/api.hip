@@ -372,6 +372,38 @@ int moe_combine(const moe_route_desc* desc, const void* y_perm, const int32_t* r
   return status_of(moe::launch_combine(a, static_cast<hipStream_t>(stream)));
 }
 
+int moe_combine_backward(const moe_route_desc* desc, const void* dy, const void* y_perm,
+                         const int32_t* row_of_slot, const float* topk_w, void* dy_perm,
+                         float* dtopk_w, void* stream) {
+  int st = check_desc(desc);
+  if (st != MOE_OK) return st;
+  const int N = desc->num_tokens;
+  if (N > 0) {
+    if (!dy || !y_perm || !row_of_slot || !topk_w || !dy_perm || !dtopk_w)
+      return MOE_ERR_INVALID_ARG;
+    if (!aligned16(dy) || !aligned16(y_perm) || !aligned16(dy_perm) ||
+        (reinterpret_cast<uintptr_t>(dtopk_w) & 3u))
+      return MOE_ERR_INVALID_ARG;
+  }
+  moe::CombineBackwardArgs a{N, desc->hidden, desc->top_k, desc->dtype, dy, y_perm,
+                             row_of_slot, topk_w, dy_perm, dtopk_w};
+  return status_of(moe::launch_combine_backward(a, static_cast<hipStream_t>(stream)));
+}
+
+int moe_permute_backward(const moe_route_desc* desc, const void* dx_perm,
+                         const int32_t* row_of_slot, void* dx, void* stream) {
+  int st = check_desc(desc);
+  if (st != MOE_OK) return st;
+  const int N = desc->num_tokens;
+  if (N > 0) {
+    if (!dx_perm || !row_of_slot || !dx) return MOE_ERR_INVALID_ARG;
+    if (!aligned16(dx_perm) || !aligned16(dx)) return MOE_ERR_INVALID_ARG;
+  }
+  return status_of(moe::launch_permute_backward(N, desc->hidden, desc->top_k, desc->dtype,
+                                                dx_perm, row_of_slot, dx,
+                                                static_cast<hipStream_t>(stream)));
+}
+
 int moe_bias_update(int32_t num_experts, int32_t num_tokens, int32_t top_k,
                     const int32_t* counts, float step, float* sel_bias, void* stream) {
   if (num_experts < 1 || num_tokens < 0 || top_k < 1 || !counts || !sel_bias)

@@ -99,6 +99,20 @@ struct CombineArgs {
 
 hipError_t launch_combine(const CombineArgs& a, hipStream_t st);
 
+// Backward of the combine's expert terms and of the permute (backward.hip).
+struct CombineBackwardArgs {
+  int N, d, k, dtype;
+  const void* dy;
+  const void* y_perm;
+  const int32_t* row_of_slot;
+  const float* topk_w;
+  void* dy_perm;
+  float* dtopk_w;
+};
+hipError_t launch_combine_backward(const CombineBackwardArgs& a, hipStream_t st);
+hipError_t launch_permute_backward(int N, int d, int k, int dtype, const void* dx_perm,
+                                   const int32_t* row_of_slot, void* dx, hipStream_t st);
+
 hipError_t launch_bias_update(int E, int N, int k, const int32_t* counts, float step,
                               float* sel_bias, hipStream_t st);
 

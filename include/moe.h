@@ -18,6 +18,9 @@
  *                    optional shared-expert output
  *   moe_bias_update  lower the selection bias of overloaded experts, raise it
  *                    for underloaded ones
+ *   moe_combine_backward, moe_permute_backward
+ *                    the data path's backward: gradients of the combine's
+ *                    expert terms (rows and weights) and of the permute
  *
  * Conventions (all entry points):
  *  - Every tensor pointer is a DEVICE pointer owned by the caller; the library
@@ -365,6 +368,32 @@ int moe_expert_ffn_pack_weights(int32_t num_experts, int32_t rows, int32_t cols,
 int moe_combine(const moe_route_desc* desc, const void* y_perm, const int32_t* row_of_slot,
                 const float* topk_w, const void* residual, const void* shared_out,
                 void* y, void* stream);
+
+/* --------------------------------------------------------------- backward -- */
+
+/* Backward of the data path (a training step reads the glossary's four steps
+ * of "How tokens travel between GPUs" in reverse).
+ *
+ * moe_combine_backward: given dy [N, d] (dtype), the forward's y_perm,
+ * row_of_slot and topk_w, for every admitted slot (t, j) with row r:
+ *   dy_perm[r]    = w_tj * dy[t]            fp32 product, rounded once to the dtype
+ *   dtopk_w[t, j] = <dy[t], y_perm[r]>      exact products summed in fp64, then fp32
+ * A dropped slot gets dtopk_w = 0 and writes no row; rows of dy_perm no slot
+ * maps to are left untouched.  The residual and shared terms of moe_combine pass
+ * dy on unchanged, so they need no call.  dy, y_perm, dy_perm 16-byte aligned.
+ *
+ * moe_permute_backward: dx[t] = sum over the token's admitted slots, in slot
+ * order, of dx_perm[row_of_slot[t, j]] (fp32, rounded once to the dtype); a
+ * token with every slot dropped gets zero.  This is the adjoint of the permute
+ * (x_perm[r] = x[token_of_row[r]]).  dx_perm, dx 16-byte aligned.
+ *
+ * Both return MOE_ERR_INVALID_ARG for a bad descriptor, missing or misaligned
+ * buffers. */
+int moe_combine_backward(const moe_route_desc* desc, const void* dy, const void* y_perm,
+                         const int32_t* row_of_slot, const float* topk_w, void* dy_perm,
+                         float* dtopk_w, void* stream);
+int moe_permute_backward(const moe_route_desc* desc, const void* dx_perm,
+                         const int32_t* row_of_slot, void* dx, void* stream);
 
 /* ------------------------------------------------------------ bias update -- */
 

@@ -281,3 +281,23 @@ def test_bench_refuses_more_than_one_gpu(capsys, monkeypatch):
         bench.main()
     assert ex.value.code == 2
     assert "one GPU" in json.loads(capsys.readouterr().out.strip())["error"]
+
+
+def test_backward_validation():
+    lib = moe.lib()
+    d = moe.route_desc(64, 64, 8, 2)
+    args = [FAKE] * 6
+    for i in range(6):
+        bad = list(args)
+        bad[i] = None
+        assert lib.moe_combine_backward(ctypes.byref(d), *bad, None) == moe.MOE_ERR_INVALID_ARG
+    mis = list(args)
+    mis[0] = ctypes.c_void_p(0x10008)  # dy misaligned
+    assert lib.moe_combine_backward(ctypes.byref(d), *mis, None) == moe.MOE_ERR_INVALID_ARG
+    for i in range(3):
+        bad = [FAKE] * 3
+        bad[i] = None
+        assert lib.moe_permute_backward(ctypes.byref(d), *bad, None) == moe.MOE_ERR_INVALID_ARG
+    bad_desc = moe.route_desc(64, 64, 8, 2, R=3)
+    assert lib.moe_permute_backward(ctypes.byref(bad_desc), FAKE, FAKE, FAKE,
+                                    None) == moe.MOE_ERR_INVALID_ARG

@@ -442,6 +442,49 @@ def test_padded_layout_output_equals_compact(name, kw):
     assert bool((pad.y_perm[:E * cap][~live].float() == 0).all()), "padding rows must stay zero"
 
 
+BACKWARD_CASES = ["switch-small", "zipf-small-cf1.0", "deepseek-small", "toy-small"]
+
+
+@pytest.mark.parametrize("name", BACKWARD_CASES)
+def test_combine_and_permute_backward(name):
+    """moe_combine_backward and moe_permute_backward on the forward's own
+    layout against the oracle: dy_perm rows and dx within the layer tolerance,
+    the weight gradients within 1e-5 of the largest, dropped slots exactly 0
+    and tokens with every slot dropped exactly 0 in dx."""
+    cfg, inp_cpu, gpu, ref = run_case(name)
+    dt = cfg["dtype"]
+    N, d, k = cfg["N"], cfg["d"], cfg["k"]
+    M = ref["num_rows"]
+    g = torch.Generator().manual_seed(N + d)
+    dy = torch.randn(N, d, generator=g).to(W.torch_dtype(cfg))
+    dxp = torch.randn(max(M, 1), d, generator=g).to(W.torch_dtype(cfg))
+    buf = moe.MoeBuffers(cfg)
+    rows = buf.rows
+    y_perm = gpu["y_perm"].cuda()
+    ros, tw = gpu["row_of_slot"].cuda(), gpu["topk_w"].cuda()
+    dy_perm = torch.zeros(rows, d, dtype=dy.dtype, device="cuda")
+    dw = torch.full((N, k), 7.0, dtype=torch.float32, device="cuda")
+    dx_perm = torch.zeros(rows, d, dtype=dy.dtype, device="cuda")
+    dx_perm[:M] = dxp[:M].cuda()
+    dx = torch.full((N, d), 5.0, dtype=dy.dtype, device="cuda")
+    print(f"[backward {name}] N={N} d={d} k={k} rows={M}", flush=True)
+    moe.moe_combine_backward(buf.desc, dy.cuda(), y_perm, ros, tw, dy_perm, dw, num_rows=rows)
+    moe.moe_permute_backward(buf.desc, dx_perm, ros, dx, num_rows=rows)
+    torch.cuda.synchronize()
+    r_dyp, r_dw = oracle.combine_backward(dt, n(dy), n(gpu["y_perm"][:M]), n(gpu["row_of_slot"]),
+                                          n(gpu["topk_w"]), M)
+    r_dx = oracle.permute_backward(dt, n(dxp[:M]), n(gpu["row_of_slot"]))
+    err = rel_err(dy_perm[:M].float(), as_tensor(r_dyp, dt).float())
+    assert err <= TOL[dt], f"dy_perm max rel err {err:.3e}"
+    assert rel_err(dw.cpu(), torch.from_numpy(r_dw)) <= 1e-5
+    dropped = gpu["row_of_slot"] < 0
+    assert bool((dw.cpu()[dropped] == 0).all())
+    err = rel_err(dx.float().cpu(), as_tensor(r_dx, dt).float())
+    assert err <= TOL[dt], f"dx max rel err {err:.3e}"
+    none = dropped.all(dim=1)
+    assert bool((dx.cpu()[none].float() == 0).all())
+
+
 def test_all_tokens_to_one_expert_with_capacity():
     """A huge selection bias sends every token to expert 3; capacity 1.25
     admits the first cap tokens; every other token leaves the layer unchanged."""
