@@ -59,6 +59,9 @@ def parse_args():
     ap.add_argument("--no-clocks", action="store_true",
                     help="skip reading the clocks with rocm-smi (a child process; under a "
                          "profiler that has already initialised the GPU, leave it out)")
+    ap.add_argument("--backward", action="store_true",
+                    help="also time the data path's backward (moe_combine_backward, "
+                         "moe_permute_backward) on this workload's layout")
     ap.add_argument("--rank-share", action="store_true",
                     help="also time the expert FFN on one rank's share of the experts at "
                          "its real shape (rows from all R source ranks)")
@@ -169,6 +172,51 @@ def rank_share(moe, torch, cfg, buf, wts, steps: int) -> dict:
             "mfma_frac": round(flops / (us * 1e-6) / (peak * 1e12), 4),
             "hbm_frac": round(nbytes / (us * 1e-6) / (HBM_PEAK_GBS * 1e9), 4),
             "bound": "mfma" if flops / (peak * 1e12) >= nbytes / (HBM_PEAK_GBS * 1e9) else "hbm"}
+
+
+def backward_pass(moe, torch, buf, steps: int) -> dict:
+    """The data path's backward on the layer's last layout: the combine's
+    expert terms (row and weight gradients) and the permute's adjoint, timed
+    with events; per call, the algorithmic bytes over the time."""
+    d = buf.desc
+    N, k, dim = d.num_tokens, d.top_k, d.hidden
+    dev = buf.y.device
+    dt = buf.y.dtype
+    es = buf.y.element_size()
+    M = int(buf.expert_offsets[d.num_experts].item())
+    g = torch.Generator(device=dev).manual_seed(7)
+    dy = torch.randn(N, dim, generator=g, device=dev).to(dt)
+    dy_perm = torch.empty_like(buf.y_perm)
+    dw = torch.empty(N, k, dtype=torch.float32, device=dev)
+    dx = torch.empty(N, dim, dtype=dt, device=dev)
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(3)]
+    cb = pb = 0.0
+
+    def run():
+        moe.moe_combine_backward(d, dy, buf.y_perm, buf.row_of_slot, buf.topk_w, dy_perm, dw,
+                                 num_rows=buf.rows)
+        moe.moe_permute_backward(d, dy_perm, buf.row_of_slot, dx, num_rows=buf.rows)
+
+    for _ in range(3):
+        run()
+    torch.cuda.synchronize()
+    for _ in range(steps):
+        ev[0].record()
+        moe.moe_combine_backward(d, dy, buf.y_perm, buf.row_of_slot, buf.topk_w, dy_perm, dw,
+                                 num_rows=buf.rows)
+        ev[1].record()
+        moe.moe_permute_backward(d, dy_perm, buf.row_of_slot, dx, num_rows=buf.rows)
+        ev[2].record()
+        torch.cuda.synchronize()
+        cb += ev[0].elapsed_time(ev[1])
+        pb += ev[1].elapsed_time(ev[2])
+    cb, pb = cb / steps * 1e3, pb / steps * 1e3
+    S = N * k
+    cb_bytes = N * dim * es + 2 * M * dim * es + S * 12  # dy, y_perm rows, dy_perm rows
+    pb_bytes = M * dim * es + N * dim * es + S * 4       # dx_perm rows, dx
+    frac = lambda nb, us: round(nb / (us * 1e-6) / (HBM_PEAK_GBS * 1e9), 4)
+    return {"combine_backward": {"us": round(cb, 2), "hbm_frac": frac(cb_bytes, cb)},
+            "permute_backward": {"us": round(pb, 2), "hbm_frac": frac(pb_bytes, pb)}}
 
 
 def describe(cfg) -> str:
@@ -556,6 +604,8 @@ def main():
     }
     if args.rank_share:
         out["rank_share"] = rank_share(moe, torch, cfg, buf, wts, max(5, min(args.steps, 30)))
+    if args.backward:
+        out["backward"] = backward_pass(moe, torch, buf, max(5, min(args.steps, 30)))
     if not args.no_cpu_baseline:
         host = {}
         for key, v in inp.items():
