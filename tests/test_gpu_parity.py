@@ -251,6 +251,45 @@ def test_empty_batch():
     assert buf.rank_counts.abs().sum().item() == 0
 
 
+@pytest.mark.parametrize("name", ["switch-small", "deepseek-small", "switch-small-int8",
+                                  "zipf-small-cf1.0-first-choice", "zipf-small-cf1.0-padded",
+                                  "switch-small-padded-int8"])
+def test_empty_batch_whole_layer(name):
+    """N = 0 through every call of the layer (route, either dispatch, the
+    INT8 payload, the padded layout, the shared expert, combine, both backward
+    calls and the bias update): each returns without error and lays out nothing;
+    with no tokens every expert's load equals the mean, so the bias is unchanged."""
+    base = CASES[name]
+    cfg = W.with_(base, N=0)
+    print(f"[empty {name}] E={cfg['E']} k={cfg['k']}", flush=True)
+    inp_cpu = W.make_inputs(base)
+    inp_cpu["x"] = inp_cpu["x"][:0]
+    inp = moe.prepare_weights(cfg, to_dev(inp_cpu))
+    buf = moe.MoeBuffers(cfg)
+    assert buf.rows == 0
+    y = moe.moe_forward(buf, inp)
+    dt = y.dtype
+    d, k = cfg["d"], cfg["k"]
+    dy = torch.empty(0, d, dtype=dt, device="cuda")
+    dy_perm = torch.empty(1, d, dtype=dt, device="cuda")
+    dw = torch.empty(0, k, dtype=torch.float32, device="cuda")
+    moe.moe_combine_backward(buf.desc, dy, buf.y_perm, buf.row_of_slot, buf.topk_w, dy_perm, dw,
+                             num_rows=buf.rows)
+    dx = torch.empty(0, d, dtype=dt, device="cuda")
+    moe.moe_permute_backward(buf.desc, dy_perm, buf.row_of_slot, dx, num_rows=buf.rows)
+    sb = inp["sel_bias"].clone() if inp.get("sel_bias") is not None else torch.zeros(
+        cfg["E"], dtype=torch.float32, device="cuda")
+    sb0 = sb.clone()
+    layer.bias_update(buf, sb, 1e-3)
+    torch.cuda.synchronize()
+    assert tuple(y.shape) == (0, d)
+    assert buf.counts.abs().sum().item() == 0
+    assert buf.expert_offsets.abs().sum().item() == 0
+    assert buf.admitted.abs().sum().item() == 0
+    assert buf.rank_offsets.abs().sum().item() == 0
+    assert torch.equal(sb, sb0)
+
+
 @pytest.mark.parametrize("N", [1, 63, 64, 65, 1023, 1025])
 def test_ragged_token_counts(N):
     base = W.small("deepseek")
