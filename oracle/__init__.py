@@ -78,6 +78,9 @@ def lib():
             "oracle_dequantize_rows_q8": [I32, I32, I32, P, P, P],
             "oracle_ffn_row": [I32, I32, I32, I32, P, P, P, P, P],
             "oracle_expert_ffn": [I32, I32, I32, I32, I32, P, P, P, P, P, P],
+            "oracle_ffn_backward_row": [I32, I32, I32, I32, P, P, P, P, P, P, P, P, P],
+            "oracle_expert_ffn_backward": [I32, I32, I32, I32, I32, P, P, P, P, P, P, P, P, P,
+                                           P],
             "oracle_combine": [I32, I32, I32, I32, P, P, P, P, P, P],
             "oracle_combine_backward": [I32, I32, I32, I32, P, P, P, P, P, P],
             "oracle_bias_update": [I32, I32, I32, P, F32, P],
@@ -235,6 +238,41 @@ def expert_ffn(dtype: str, act: str, x_rows, offsets, w1, w3, w2) -> np.ndarray:
                                    _ptr(offsets), _ptr(w1), _ptr(w3), _ptr(w2), _ptr(y)),
            "oracle_expert_ffn")
     return y
+
+
+def ffn_backward_row(dtype: str, act: str, x_row, w1, w3, w2, dy_row) -> tuple:
+    """Backward of one row through one expert: (dx [d] in the dtype, H, du, dv
+    as fp64 arrays [h] holding the values the dtype rounds them to)."""
+    ed = _elem_dtype(dtype)
+    x_row, dy_row, w1, w2 = _c(x_row, ed), _c(dy_row, ed), _c(w1, ed), _c(w2, ed)
+    w3 = _c(w3, ed)
+    h, d = w1.shape
+    dx = np.empty(d, ed)
+    H, du, dv = np.empty(h), np.empty(h), np.empty(h)
+    _check(lib().oracle_ffn_backward_row(d, h, ACT_CODES[act], DTYPE_CODES[dtype], _ptr(x_row),
+                                         _ptr(w1), _ptr(w3), _ptr(w2), _ptr(dy_row), _ptr(dx),
+                                         _ptr(H), _ptr(du), _ptr(dv)), "oracle_ffn_backward_row")
+    return dx, H, du, dv
+
+
+def expert_ffn_backward(dtype: str, act: str, x_rows, offsets, w1, w3, w2, dy_rows) -> tuple:
+    """Backward of the grouped FFN: (dx_rows in the dtype, rows outside every
+    segment zero; dw1, dw3 [E,h,d] and dw2 [E,d,h] in fp32; dw3 None unless
+    SwiGLU).  Weights are plain row-major."""
+    ed = _elem_dtype(dtype)
+    x_rows, dy_rows, w1, w2 = _c(x_rows, ed), _c(dy_rows, ed), _c(w1, ed), _c(w2, ed)
+    w3 = _c(w3, ed)
+    offsets = _c(offsets, np.int32)
+    E, h, d = w1.shape
+    dx = np.zeros((x_rows.shape[0], d), ed)
+    dw1 = np.empty((E, h, d), np.float32)
+    dw3 = np.empty((E, h, d), np.float32) if act == "swiglu" else None
+    dw2 = np.empty((E, d, h), np.float32)
+    _check(lib().oracle_expert_ffn_backward(E, d, h, ACT_CODES[act], DTYPE_CODES[dtype],
+                                            _ptr(x_rows), _ptr(offsets), _ptr(w1), _ptr(w3),
+                                            _ptr(w2), _ptr(dy_rows), _ptr(dx), _ptr(dw1),
+                                            _ptr(dw3), _ptr(dw2)), "oracle_expert_ffn_backward")
+    return dx, dw1, dw3, dw2
 
 
 def combine(dtype: str, y_perm, row_of_slot, topk_w, residual=None, shared_out=None):

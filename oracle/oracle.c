@@ -528,6 +528,171 @@ int oracle_expert_ffn(int32_t num_experts, int32_t hidden, int32_t ffn_hidden,
   return failed ? -1 : 0;
 }
 
+/* --------------------------------------------------- expert FFN backward -- */
+
+/* Derivatives of the activations (the gradients of the layer's expert
+ * networks, the backward of the layer).  gelu(u) = u Phi(u), so
+ * gelu'(u) = Phi(u) + u phi(u); silu(u) = u s(u) with s the logistic
+ * function, so silu'(u) = s(u) (1 + u (1 - s(u))). */
+static double dact_relu(double u) { return u > 0.0 ? 1.0 : 0.0; }
+static double dact_gelu(double u) {
+  const double pi = 3.14159265358979323846;
+  return 0.5 * (1.0 + erf(u / sqrt(2.0))) + u * exp(-0.5 * u * u) / sqrt(2.0 * pi);
+}
+static double dact_silu(double u) {
+  const double s = 1.0 / (1.0 + exp(-u));
+  return s * (1.0 + u * (1.0 - s));
+}
+static double round_dt(int32_t dtype, double v) {
+  return dtype == 0 ? (double)(float)v : bf16_bits_to_double(double_to_bf16_bits(v));
+}
+
+/* One row through the backward of one expert, by the chain rule through the
+ * forward of oracle_ffn_row (u = x W1^T, v = x W3^T, H = act(u) [* v],
+ * y = H W2^T):
+ *   g  = dy W2                 (gradient at H; fp64 sums)
+ *   du = g * act'(u) [* v]     (gradient at u), rounded to the dtype
+ *   dv = g * silu(u)           (SwiGLU: gradient at v), rounded to the dtype
+ *   dx = du W1 [+ dv W3]       (fp64 sums), rounded to the dtype.
+ * h_out, du_out and dv_out (nullable) receive H (rounded as in the forward),
+ * du and dv: the operands of the weight gradients. */
+int oracle_ffn_backward_row(int32_t hidden, int32_t ffn_hidden, int32_t act, int32_t dtype,
+                            const void* x_row, const void* w1, const void* w3, const void* w2,
+                            const void* dy_row, void* dx_row, double* h_out, double* du_out,
+                            double* dv_out) {
+  if (hidden < 1 || ffn_hidden < 1 || act < 0 || act > 2 || !dtype_ok(dtype)) return -1;
+  if (!x_row || !w1 || !w2 || !dy_row || !dx_row || (act == 2 && !w3)) return -1;
+  const int32_t d = hidden, h = ffn_hidden;
+  double* xd = (double*)malloc(sizeof(double) * d);
+  double* dyd = (double*)malloc(sizeof(double) * d);
+  double* du = (double*)malloc(sizeof(double) * h);
+  double* dv = (double*)malloc(sizeof(double) * h);
+  if (!xd || !dyd || !du || !dv) {
+    free(xd);
+    free(dyd);
+    free(du);
+    free(dv);
+    return -1;
+  }
+  for (int32_t i = 0; i < d; ++i) {
+    xd[i] = elem(x_row, dtype, i);
+    dyd[i] = elem(dy_row, dtype, i);
+  }
+  for (int32_t j = 0; j < h; ++j) {
+    double u = 0.0, v = 0.0, g = 0.0;
+    for (int32_t i = 0; i < d; ++i) u += xd[i] * elem(w1, dtype, (size_t)j * d + i);
+    if (act == 2)
+      for (int32_t i = 0; i < d; ++i) v += xd[i] * elem(w3, dtype, (size_t)j * d + i);
+    for (int32_t i = 0; i < d; ++i) g += dyd[i] * elem(w2, dtype, (size_t)i * h + j);
+    double hv, dgu, dgv = 0.0;
+    if (act == 0) {
+      hv = act_relu(u);
+      dgu = g * dact_relu(u);
+    } else if (act == 1) {
+      hv = act_gelu(u);
+      dgu = g * dact_gelu(u);
+    } else {
+      hv = act_silu(u) * v;
+      dgu = g * dact_silu(u) * v;
+      dgv = g * act_silu(u);
+    }
+    du[j] = round_dt(dtype, dgu);
+    dv[j] = round_dt(dtype, dgv);
+    if (h_out) h_out[j] = round_dt(dtype, hv);
+    if (du_out) du_out[j] = du[j];
+    if (dv_out) dv_out[j] = dv[j];
+  }
+  for (int32_t i = 0; i < d; ++i) {
+    double o = 0.0;
+    for (int32_t j = 0; j < h; ++j) o += du[j] * elem(w1, dtype, (size_t)j * d + i);
+    if (act == 2)
+      for (int32_t j = 0; j < h; ++j) o += dv[j] * elem(w3, dtype, (size_t)j * d + i);
+    store(dx_row, dtype, (size_t)i, o);
+  }
+  free(xd);
+  free(dyd);
+  free(du);
+  free(dv);
+  return 0;
+}
+
+/* Backward of the grouped FFN: rows [offsets[e], offsets[e+1]) of x_rows and
+ * dy_rows belong to expert e.  dx_rows gets every such row's input gradient;
+ * the weight gradients sum over the expert's rows (fp64 sums, stored fp32):
+ *   dw1[e][j][i] = sum_r du[r][j] x[r][i],  dw3[e][j][i] = sum_r dv[r][j] x[r][i],
+ *   dw2[e][i][j] = sum_r dy[r][i] H[r][j].
+ * An expert with no rows gets zero weight gradients; dw3 only for SwiGLU. */
+int oracle_expert_ffn_backward(int32_t num_experts, int32_t hidden, int32_t ffn_hidden,
+                               int32_t act, int32_t dtype, const void* x_rows,
+                               const int32_t* offsets, const void* w1, const void* w3,
+                               const void* w2, const void* dy_rows, void* dx_rows, float* dw1,
+                               float* dw3, float* dw2) {
+  if (num_experts < 1 || hidden < 1 || ffn_hidden < 1 || !dtype_ok(dtype) || !offsets)
+    return -1;
+  if (act < 0 || act > 2 || !dw1 || !dw2 || (act == 2 && (!w3 || !dw3))) return -1;
+  const int32_t d = hidden, h = ffn_hidden;
+  const size_t es = dtype == 0 ? 4 : 2;
+  const size_t wsz = (size_t)d * h * es, rb = (size_t)d * es;
+  for (int32_t e = 0; e < num_experts; ++e)
+    if (offsets[e + 1] < offsets[e] || offsets[e] < 0) return -1;
+  int failed = 0;
+  for (int32_t e = 0; e < num_experts && !failed; ++e) {
+    const int32_t lo = offsets[e], n = offsets[e + 1] - offsets[e];
+    const char* w1e = (const char*)w1 + (size_t)e * wsz;
+    const char* w3e = w3 ? (const char*)w3 + (size_t)e * wsz : NULL;
+    const char* w2e = (const char*)w2 + (size_t)e * wsz;
+    float* g1 = dw1 + (size_t)e * h * d;
+    float* g3 = act == 2 ? dw3 + (size_t)e * h * d : NULL;
+    float* g2 = dw2 + (size_t)e * d * h;
+    const size_t cells = (size_t)(n > 0 ? n : 1) * h;
+    double* H = (double*)malloc(sizeof(double) * cells);
+    double* du = (double*)malloc(sizeof(double) * cells);
+    double* dv = (double*)malloc(sizeof(double) * cells);
+    if (!H || !du || !dv) {
+      free(H);
+      free(du);
+      free(dv);
+      return -1;
+    }
+#pragma omp parallel for num_threads(g_threads) schedule(dynamic, 1)
+    for (int32_t r = 0; r < n; ++r) {
+      if (oracle_ffn_backward_row(d, h, act, dtype, (const char*)x_rows + (size_t)(lo + r) * rb,
+                                  w1e, w3e, w2e, (const char*)dy_rows + (size_t)(lo + r) * rb,
+                                  (char*)dx_rows + (size_t)(lo + r) * rb, H + (size_t)r * h,
+                                  du + (size_t)r * h, dv + (size_t)r * h) != 0) {
+#pragma omp atomic write
+        failed = 1;
+      }
+    }
+#pragma omp parallel for num_threads(g_threads) schedule(static)
+    for (int32_t j = 0; j < h; ++j) {
+      for (int32_t i = 0; i < d; ++i) {
+        double s1 = 0.0, s3 = 0.0;
+        for (int32_t r = 0; r < n; ++r) {
+          const double xv = elem(x_rows, dtype, (size_t)(lo + r) * d + i);
+          s1 += du[(size_t)r * h + j] * xv;
+          s3 += dv[(size_t)r * h + j] * xv;
+        }
+        g1[(size_t)j * d + i] = (float)s1;
+        if (g3) g3[(size_t)j * d + i] = (float)s3;
+      }
+    }
+#pragma omp parallel for num_threads(g_threads) schedule(static)
+    for (int32_t i = 0; i < d; ++i) {
+      for (int32_t j = 0; j < h; ++j) {
+        double s2 = 0.0;
+        for (int32_t r = 0; r < n; ++r)
+          s2 += elem(dy_rows, dtype, (size_t)(lo + r) * d + i) * H[(size_t)r * h + j];
+        g2[(size_t)i * h + j] = (float)s2;
+      }
+    }
+    free(H);
+    free(du);
+    free(dv);
+  }
+  return failed ? -1 : 0;
+}
+
 /* --------------------------------------------------------------- combine -- */
 
 /* Combine: each token's expert outputs come back to it, weighted by the router

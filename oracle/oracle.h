@@ -121,6 +121,24 @@ int oracle_expert_ffn(int32_t num_experts, int32_t hidden, int32_t ffn_hidden,
                       const int32_t* offsets, const void* w1, const void* w3,
                       const void* w2, void* y_rows);
 
+/* Backward of one row through one expert (chain rule through oracle_ffn_row):
+ * g = dy W2, du = g act'(u) [* v], dv = g silu(u) (SwiGLU), dx = du W1 [+ dv W3];
+ * du, dv and dx rounded to the dtype.  h_out/du_out/dv_out (nullable, h doubles
+ * each) receive H as the forward rounds it, du and dv. */
+int oracle_ffn_backward_row(int32_t hidden, int32_t ffn_hidden, int32_t act, int32_t dtype,
+                            const void* x_row, const void* w1, const void* w3, const void* w2,
+                            const void* dy_row, void* dx_row, double* h_out, double* du_out,
+                            double* dv_out);
+
+/* Backward of the grouped FFN: dx_rows for every row of a segment, and fp32
+ * weight gradients dw1/dw3 [E,h,d] (sum over the expert's rows of du x^T,
+ * dv x^T) and dw2 [E,d,h] (sum of dy H^T); zero for an expert with no rows. */
+int oracle_expert_ffn_backward(int32_t num_experts, int32_t hidden, int32_t ffn_hidden,
+                               int32_t act, int32_t dtype, const void* x_rows,
+                               const int32_t* offsets, const void* w1, const void* w3,
+                               const void* w2, const void* dy_rows, void* dx_rows, float* dw1,
+                               float* dw3, float* dw2);
+
 /* y[t] = residual[t] + shared[t] + sum_j w[t,j] y_perm[row_of_slot[t,j]]
  * (residual, shared nullable; dropped slots, row < 0, contribute nothing). */
 int oracle_combine(int32_t num_tokens, int32_t hidden, int32_t top_k, int32_t dtype,
