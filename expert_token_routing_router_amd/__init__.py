@@ -41,6 +41,7 @@ EXPORTS = [
     "moe_dispatch_workspace_size", "moe_dispatch", "moe_dispatch_ex", "moe_dispatch_q8",
     "moe_dequantize_q8", "moe_dispatch_layout", "moe_permute", "moe_permute_q8",
     "moe_dispatch_rows", "moe_combine_backward", "moe_permute_backward",
+    "moe_expert_ffn_backward_workspace_size", "moe_expert_ffn_backward",
     "moe_expert_ffn_workspace_size", "moe_expert_ffn", "moe_expert_ffn_plan",
     "moe_expert_ffn_up", "moe_expert_ffn_down", "moe_expert_ffn_pack_weights", "moe_combine",
     "moe_bias_update", "moe_status_string",
@@ -110,6 +111,9 @@ def lib() -> ctypes.CDLL:
             "moe_dispatch_rows": ([D, I32], ctypes.c_int64),
             "moe_combine_backward": ([D, P, P, P, P, P, P, P], I32),
             "moe_permute_backward": ([D, P, P, P, P], I32),
+            "moe_expert_ffn_backward_workspace_size": ([I32, I32, I32, I32, I32, I32], SZ),
+            "moe_expert_ffn_backward": ([I32, I32, I32, I32, I32, I32, P, P, P, P, P, P, P, P, P,
+                                         P, P, SZ, P], I32),
             "moe_expert_ffn_workspace_size": ([I32, I32, I32, I32, I32, I32], SZ),
             "moe_expert_ffn": ([I32, I32, I32, I32, I32, I32, P, P, P, P, P, P, P, SZ, P], I32),
             "moe_expert_ffn_plan": ([I32, I32, I32, I32, I32, I32, P, P, SZ, P], I32),
@@ -465,6 +469,37 @@ def moe_permute_backward(desc, dx_perm, row_of_slot, dx, num_rows=None, stream=N
         _ptr(row_of_slot, "row_of_slot", torch.int32, N * k, N > 0),
         _ptr(dx, "dx", dt, N * d, N > 0), _stream(stream))
     _raise("moe_permute_backward", st)
+
+
+def moe_expert_ffn_backward_workspace_size(num_experts, max_rows, hidden, ffn_hidden, act,
+                                           dtype) -> int:
+    act = ACT[act] if isinstance(act, str) else int(act)
+    dtype = DTYPE[dtype] if isinstance(dtype, str) else int(dtype)
+    return int(lib().moe_expert_ffn_backward_workspace_size(num_experts, max_rows, hidden,
+                                                             ffn_hidden, act, dtype))
+
+
+def moe_expert_ffn_backward(num_experts, max_rows, hidden, ffn_hidden, act, dtype, x_rows,
+                            group_offsets, w1, w3, w2, dy_rows, dx_rows, dw1, dw3, dw2, ws,
+                            stream=None):
+    """Input gradients dx_rows and fp32 weight gradients dw1/dw3/dw2 of the
+    grouped expert FFN; weights in plain row-major layout (not packed)."""
+    act = ACT[act] if isinstance(act, str) else int(act)
+    dtype = DTYPE[dtype] if isinstance(dtype, str) else int(dtype)
+    dt = TORCH_DTYPE.get(dtype)
+    E, M, d, h = num_experts, max_rows, hidden, ffn_hidden
+    sw = act == MOE_SWIGLU
+    f32 = torch.float32
+    st = lib().moe_expert_ffn_backward(
+        E, M, d, h, act, dtype, _ptr(x_rows, "x_rows", dt, M * d, M > 0),
+        _ptr(group_offsets, "group_offsets", torch.int32, E + 1),
+        _ptr(w1, "w1", dt, E * h * d), _ptr(w3, "w3", dt, E * h * d, sw),
+        _ptr(w2, "w2", dt, E * d * h), _ptr(dy_rows, "dy_rows", dt, M * d, M > 0),
+        _ptr(dx_rows, "dx_rows", dt, M * d, M > 0), _ptr(dw1, "dw1", f32, E * h * d),
+        _ptr(dw3, "dw3", f32, E * h * d, sw), _ptr(dw2, "dw2", f32, E * d * h),
+        _ptr(ws, "ws", None, None, False), 0 if ws is None else ws.numel() * ws.element_size(),
+        _stream(stream))
+    _raise("moe_expert_ffn_backward", st)
 
 
 def moe_bias_update(num_experts, num_tokens, top_k, counts, step, sel_bias, stream=None):

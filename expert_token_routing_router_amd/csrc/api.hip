@@ -307,6 +307,53 @@ int moe_expert_ffn(int32_t num_experts, int32_t max_rows, int32_t hidden, int32_
   return status_of(e);
 }
 
+// Backward of the expert FFN: bf16 only; d and h multiples of 32; at most
+// 1024 experts; the 64-row tile list must fit a grid dimension.
+static int check_ffn_backward(int32_t E, int32_t max_rows, int32_t d, int32_t h, int32_t act,
+                              int32_t dtype) {
+  if (E < 1 || max_rows < 0 || d < 1 || h < 1) return MOE_ERR_INVALID_ARG;
+  if (act < MOE_RELU || act > MOE_SWIGLU) return MOE_ERR_INVALID_ARG;
+  if (dtype != MOE_F32 && dtype != MOE_BF16) return MOE_ERR_INVALID_ARG;
+  if (dtype != MOE_BF16 || E > 1024 || d % 32 != 0 || h % 32 != 0) return MOE_ERR_UNSUPPORTED;
+  if (moe::ffn_backward_max_tiles(E, max_rows) > 65535) return MOE_ERR_UNSUPPORTED;
+  return MOE_OK;
+}
+
+size_t moe_expert_ffn_backward_workspace_size(int32_t num_experts, int32_t max_rows,
+                                              int32_t hidden, int32_t ffn_hidden, int32_t act,
+                                              int32_t dtype) {
+  if (check_ffn_backward(num_experts, max_rows, hidden, ffn_hidden, act, dtype) != MOE_OK)
+    return 0;
+  return moe::ffn_backward_workspace_bytes(num_experts, max_rows, hidden, ffn_hidden, act);
+}
+
+int moe_expert_ffn_backward(int32_t num_experts, int32_t max_rows, int32_t hidden,
+                            int32_t ffn_hidden, int32_t act, int32_t dtype, const void* x_rows,
+                            const int32_t* group_offsets, const void* w1, const void* w3,
+                            const void* w2, const void* dy_rows, void* dx_rows, float* dw1,
+                            float* dw3, float* dw2, void* ws, size_t ws_bytes, void* stream) {
+  int st = check_ffn_backward(num_experts, max_rows, hidden, ffn_hidden, act, dtype);
+  if (st != MOE_OK) return st;
+  const bool swiglu = act == MOE_SWIGLU;
+  if (!group_offsets || !w1 || !w2 || !dw1 || !dw2) return MOE_ERR_INVALID_ARG;
+  if (swiglu != (w3 != nullptr) || swiglu != (dw3 != nullptr)) return MOE_ERR_INVALID_ARG;
+  if ((reinterpret_cast<uintptr_t>(group_offsets) & 3u) || !aligned16(w1) || !aligned16(w2) ||
+      (w3 && !aligned16(w3)) || !aligned16(dw1) || !aligned16(dw2) || (dw3 && !aligned16(dw3)))
+    return MOE_ERR_INVALID_ARG;
+  if (max_rows > 0) {
+    if (!x_rows || !dy_rows || !dx_rows) return MOE_ERR_INVALID_ARG;
+    if (!aligned16(x_rows) || !aligned16(dy_rows) || !aligned16(dx_rows))
+      return MOE_ERR_INVALID_ARG;
+    const size_t need = moe::ffn_backward_workspace_bytes(num_experts, max_rows, hidden,
+                                                          ffn_hidden, act);
+    if (!ws || ws_bytes < need || (reinterpret_cast<uintptr_t>(ws) & 255u))
+      return MOE_ERR_WORKSPACE;
+  }
+  moe::FfnBackwardArgs a{num_experts, max_rows, hidden, ffn_hidden, act, x_rows, group_offsets,
+                         w1, w3, w2, dy_rows, dx_rows, dw1, dw3, dw2, ws};
+  return status_of(moe::launch_ffn_backward(a, static_cast<hipStream_t>(stream)));
+}
+
 int moe_expert_ffn_plan(int32_t num_experts, int32_t max_rows, int32_t hidden,
                         int32_t ffn_hidden, int32_t act, int32_t dtype,
                         const int32_t* group_offsets, void* ws, size_t ws_bytes, void* stream) {

@@ -113,6 +113,26 @@ hipError_t launch_combine_backward(const CombineBackwardArgs& a, hipStream_t st)
 hipError_t launch_permute_backward(int N, int d, int k, int dtype, const void* dx_perm,
                                    const int32_t* row_of_slot, void* dx, hipStream_t st);
 
+// Backward of the expert FFN (backward_ffn.hip), bf16: plain row-major
+// weights w1/w3 [E,h,d] and w2 [E,d,h]; fp32 weight gradients.
+struct FfnBackwardArgs {
+  int E, max_rows, d, h, act;
+  const void* x_rows;
+  const int32_t* offsets;
+  const void* w1;
+  const void* w3;
+  const void* w2;
+  const void* dy_rows;
+  void* dx_rows;
+  float* dw1;
+  float* dw3;
+  float* dw2;
+  void* ws;
+};
+size_t ffn_backward_workspace_bytes(int E, int max_rows, int d, int h, int act);
+int ffn_backward_max_tiles(int E, int max_rows);
+hipError_t launch_ffn_backward(const FfnBackwardArgs& a, hipStream_t st);
+
 hipError_t launch_bias_update(int E, int N, int k, const int32_t* counts, float step,
                               float* sel_bias, hipStream_t st);
 

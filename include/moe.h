@@ -21,6 +21,9 @@
  *   moe_combine_backward, moe_permute_backward
  *                    the data path's backward: gradients of the combine's
  *                    expert terms (rows and weights) and of the permute
+ *   moe_expert_ffn_backward
+ *                    the expert FFN's backward: input gradients of every
+ *                    expert's rows and the experts' weight gradients
  *
  * Conventions (all entry points):
  *  - Every tensor pointer is a DEVICE pointer owned by the caller; the library
@@ -394,6 +397,39 @@ int moe_combine_backward(const moe_route_desc* desc, const void* dy, const void*
                          float* dtopk_w, void* stream);
 int moe_permute_backward(const moe_route_desc* desc, const void* dx_perm,
                          const int32_t* row_of_slot, void* dx, void* stream);
+
+/* Backward of the expert FFN (each expert is an ordinary feed-forward block:
+ * glossary "Expert Parallelism", introduction).  With the forward of
+ * moe_expert_ffn, u = x W1^T, v = x W3^T, H = act(u) [* v], y = H W2^T, over
+ * rows [group_offsets[e], group_offsets[e+1]) (clamped to max_rows) of expert e:
+ *   g   = dy W2                     (gradient at H)
+ *   du  = g * act'(u) [* v]         rounded to bf16
+ *   dv  = g * silu(u)               SwiGLU only, rounded to bf16
+ *   dx  = du W1 [+ dv W3]           rounded to bf16, written to dx_rows
+ *   dw1[e] = sum_r du^T x,  dw3[e] = sum_r dv^T x,  dw2[e] = sum_r dy^T H
+ * u, v and H are recomputed (H rounded to bf16 as in the forward); products
+ * run on bf16 operands with fp32 sums.  GELU is the erf form,
+ * gelu'(u) = Phi(u) + u phi(u).
+ *
+ *  x_rows, dy_rows, dx_rows [max_rows, d] bf16 (dy_rows: the gradient at
+ *      y_rows, e.g. moe_combine_backward's dy_perm; rows outside every
+ *      segment are neither read nor written);
+ *  w1, w3 [E, h, d] and w2 [E, d, h] bf16, PLAIN row-major (not the packed
+ *      layout of moe_expert_ffn); w3 and dw3 only for MOE_SWIGLU (NULL else);
+ *  dw1, dw3 [E, h, d] and dw2 [E, d, h] fp32, fully written (zero for an
+ *      expert with no rows, also when max_rows == 0).
+ * dtype must be MOE_BF16, d and h multiples of 32, E <= 1024 (else
+ * MOE_ERR_UNSUPPORTED).  Workspace from moe_expert_ffn_backward_workspace_size
+ * (H and [du | dv] for every row, about max_rows * 3h * 2 bytes for SwiGLU);
+ * none is needed when max_rows == 0.  All buffers 16-byte aligned. */
+size_t moe_expert_ffn_backward_workspace_size(int32_t num_experts, int32_t max_rows,
+                                              int32_t hidden, int32_t ffn_hidden, int32_t act,
+                                              int32_t dtype);
+int moe_expert_ffn_backward(int32_t num_experts, int32_t max_rows, int32_t hidden,
+                            int32_t ffn_hidden, int32_t act, int32_t dtype, const void* x_rows,
+                            const int32_t* group_offsets, const void* w1, const void* w3,
+                            const void* w2, const void* dy_rows, void* dx_rows, float* dw1,
+                            float* dw3, float* dw2, void* ws, size_t ws_bytes, void* stream);
 
 /* ------------------------------------------------------------ bias update -- */
 

@@ -301,3 +301,40 @@ def test_backward_validation():
     bad_desc = moe.route_desc(64, 64, 8, 2, R=3)
     assert lib.moe_permute_backward(ctypes.byref(bad_desc), FAKE, FAKE, FAKE,
                                     None) == moe.MOE_ERR_INVALID_ARG
+
+
+def test_expert_ffn_backward_validation():
+    """Host-side checks of moe_expert_ffn_backward: every rejected call returns
+    before any launch (no device is touched)."""
+    lib = moe.lib()
+    E, M, d, h = 4, 100, 64, 96
+    need = lib.moe_expert_ffn_backward_workspace_size(E, M, d, h, moe.MOE_SWIGLU, moe.MOE_BF16)
+    assert need > 0
+    # fp32, a d or h off the 32 grid, and too many experts are unsupported.
+    assert lib.moe_expert_ffn_backward_workspace_size(E, M, d, h, moe.MOE_SWIGLU, moe.MOE_F32) == 0
+    assert lib.moe_expert_ffn_backward_workspace_size(E, M, 48, h, moe.MOE_SWIGLU,
+                                                      moe.MOE_BF16) == 0
+    assert lib.moe_expert_ffn_backward_workspace_size(1025, M, d, h, moe.MOE_GELU,
+                                                      moe.MOE_BF16) == 0
+
+    def call(E=E, M=M, d=d, h=h, act=moe.MOE_SWIGLU, dtype=moe.MOE_BF16, x=FAKE, off=FAKE,
+             w3=FAKE, dw3=FAKE, dy=FAKE, ws=FAKE, ws_bytes=need):
+        return lib.moe_expert_ffn_backward(E, M, d, h, act, dtype, x, off, FAKE, w3, FAKE, dy,
+                                           FAKE, FAKE, dw3, FAKE, ws, ws_bytes, None)
+
+    assert call(dtype=moe.MOE_F32) == moe.MOE_ERR_UNSUPPORTED
+    assert call(d=48) == moe.MOE_ERR_UNSUPPORTED
+    assert call(h=80) == moe.MOE_ERR_UNSUPPORTED
+    assert call(E=0) == moe.MOE_ERR_INVALID_ARG
+    assert call(M=-1) == moe.MOE_ERR_INVALID_ARG
+    assert call(act=3) == moe.MOE_ERR_INVALID_ARG
+    assert call(dtype=7) == moe.MOE_ERR_INVALID_ARG
+    assert call(off=None) == moe.MOE_ERR_INVALID_ARG
+    assert call(w3=None) == moe.MOE_ERR_INVALID_ARG          # SwiGLU needs W3 ...
+    assert call(dw3=None) == moe.MOE_ERR_INVALID_ARG         # ... and its gradient
+    assert call(act=moe.MOE_GELU) == moe.MOE_ERR_INVALID_ARG  # GELU takes neither
+    assert call(x=None) == moe.MOE_ERR_INVALID_ARG
+    assert call(dy=ctypes.c_void_p(0x10008)) == moe.MOE_ERR_INVALID_ARG  # misaligned
+    assert call(ws_bytes=need - 1) == moe.MOE_ERR_WORKSPACE
+    assert call(ws=None) == moe.MOE_ERR_WORKSPACE
+    assert call(ws=ctypes.c_void_p(0x10010)) == moe.MOE_ERR_WORKSPACE  # not 256-aligned

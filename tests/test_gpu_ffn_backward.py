@@ -1,0 +1,191 @@
+"""GPU parity of the expert-FFN backward (moe_expert_ffn_backward) against the
+oracle: input gradients and fp32 weight gradients within the bf16 layer
+tolerance (max |gpu - ref| / max |ref| per tensor), on
+
+- seeded ragged segments (an empty expert, a segment of one row, rows after
+  the last segment that must stay untouched) at the reduced shapes of every
+  activation, including an h that is not a multiple of the 128-column tile;
+- the layer's backward chained through the data path (combine backward ->
+  FFN backward -> permute backward) on the oracle forward's own layout;
+- the full Switch shape (16384 rows, d 1024, h 4096, 64 experts), sampled:
+  input gradients of rows across the batch and both weight gradients of one
+  whole expert, each from the oracle's per-row backward.
+"""
+
+import numpy as np
+import pytest
+import torch
+
+import expert_token_routing_router_amd as moe
+import moe_workloads as W
+import oracle
+
+from gpu_util import TOL, as_tensor, n, oracle_reference, rel_err, threads
+
+pytestmark = pytest.mark.gpu
+
+BF16 = torch.bfloat16
+SHAPES = {
+    # name: (workload for d, h, act; experts; rows)
+    "switch-small-gelu": (W.small("switch"), 16, 700),
+    "mixtral-small-swiglu": (W.small("mixtral"), 8, 611),       # h 448: a 64-column tail
+    "deepseek-small-swiglu": (W.small("deepseek"), 24, 523),    # h 192, d 384
+    "toy-small-relu": (W.with_(W.small("toy"), dtype="bf16"), 8, 300),
+}
+
+
+def _segments(E, rows, seed):
+    """Ragged, monotone offsets over the first rows - 37 rows: expert 1 empty,
+    expert 2 a single row; the last 37 rows lie outside every segment."""
+    g = np.random.default_rng(seed)
+    used = rows - 37
+    cuts = np.sort(g.integers(0, used + 1, size=E - 1))
+    off = np.concatenate([[0], cuts, [used]]).astype(np.int32)
+    off[2] = off[1]
+    off[3] = min(off[2] + 1, off[4]) if E > 3 else off[3]
+    return off
+
+
+def _weights(E, d, h, act, seed, scale=0.05):
+    g = torch.Generator().manual_seed(seed)
+    w1 = (torch.randn(E, h, d, generator=g) * scale).to(BF16)
+    w3 = (torch.randn(E, h, d, generator=g) * scale).to(BF16) if act == "swiglu" else None
+    w2 = (torch.randn(E, d, h, generator=g) * scale).to(BF16)
+    return w1, w3, w2
+
+
+def _gpu_backward(E, rows, d, h, act, x, off, w1, w3, w2, dy, sentinel=3.0):
+    dev = lambda t: None if t is None else t.cuda()  # noqa: E731
+    sw = act == "swiglu"
+    dx = torch.full((max(rows, 1), d), sentinel, dtype=BF16, device="cuda")
+    dw1 = torch.full((E, h, d), 9.0, device="cuda")
+    dw3 = torch.full((E, h, d), 9.0, device="cuda") if sw else None
+    dw2 = torch.full((E, d, h), 9.0, device="cuda")
+    ws = moe.workspace(moe.moe_expert_ffn_backward_workspace_size(E, rows, d, h, act, "bf16"))
+    moe.moe_expert_ffn_backward(E, rows, d, h, act, "bf16", dev(x), dev(off), dev(w1), dev(w3),
+                                dev(w2), dev(dy), dx, dw1, dw3, dw2, ws)
+    torch.cuda.synchronize()
+    return dx.cpu(), dw1.cpu(), None if dw3 is None else dw3.cpu(), dw2.cpu()
+
+
+@pytest.mark.parametrize("name", list(SHAPES))
+def test_ffn_backward_ragged_segments(name):
+    cfg, E, rows = SHAPES[name]
+    d, h, act = cfg["d"], cfg["h"], cfg["act"]
+    print(f"[ffn backward {name}] E={E} rows={rows} d={d} h={h} {act}", flush=True)
+    off = _segments(E, rows, seed=rows)
+    g = torch.Generator().manual_seed(d + h)
+    x = torch.randn(rows, d, generator=g).to(BF16)
+    dy = (torch.randn(rows, d, generator=g) * 0.5).to(BF16)
+    w1, w3, w2 = _weights(E, d, h, act, seed=E + d)
+    dx, dw1, dw3, dw2 = _gpu_backward(E, rows, d, h, act, x, torch.from_numpy(off), w1, w3, w2,
+                                      dy)
+    oracle.set_threads(threads())
+    r_dx, r_dw1, r_dw3, r_dw2 = oracle.expert_ffn_backward("bf16", act, n(x), off, n(w1), n(w3),
+                                                           n(w2), n(dy))
+    used = int(off[-1])
+    err = rel_err(dx[:used].float(), as_tensor(r_dx[:used], "bf16").float())
+    assert err <= TOL["bf16"], f"dx max rel err {err:.3e}"
+    assert bool((dx[used:] == 3.0).all()), "rows outside every segment must stay untouched"
+    for got, ref, key in ((dw1, r_dw1, "dw1"), (dw3, r_dw3, "dw3"), (dw2, r_dw2, "dw2")):
+        if ref is None:
+            continue
+        err = rel_err(got, torch.from_numpy(ref))
+        assert err <= TOL["bf16"], f"{key} max rel err {err:.3e}"
+        assert bool((got[1] == 0).all()), f"{key}: an expert with no rows gets zeros"
+
+
+@pytest.mark.parametrize("name", ["switch", "mixtral"])
+def test_layer_backward_chain(name):
+    """combine backward -> FFN backward -> permute backward on the oracle
+    forward's layout, expert outputs and weights (compact layout, drops
+    included), against the same chain of oracle calls."""
+    cfg = W.small(name)
+    dt, act = cfg["dtype"], cfg["act"]
+    N, d, h, E, k = cfg["N"], cfg["d"], cfg["h"], cfg["E"], cfg["k"]
+    print(f"[layer backward {name}] N={N} d={d} h={h} E={E} k={k}", flush=True)
+    inp_cpu = W.make_inputs(cfg)
+    ref = oracle_reference(cfg, inp_cpu)
+    M = ref["num_rows"]
+    buf = moe.MoeBuffers(cfg)
+    rows = buf.rows
+    g = torch.Generator().manual_seed(N)
+    dy = torch.randn(N, d, generator=g).to(BF16)
+
+    def padded(a):
+        t = torch.zeros(max(rows, 1), d, dtype=BF16)
+        t[:M] = as_tensor(a[:M], dt)
+        return t.cuda()
+
+    x_perm, y_perm = padded(ref["x_perm"]), padded(ref["y_perm"])
+    ros = torch.from_numpy(ref["row_of_slot"]).cuda()
+    tw = torch.from_numpy(ref["topk_w"]).cuda()
+    off = torch.from_numpy(ref["expert_offsets"]).cuda()
+    dy_perm = torch.zeros(max(rows, 1), d, dtype=BF16, device="cuda")
+    dtw = torch.empty(N, k, device="cuda")
+    moe.moe_combine_backward(buf.desc, dy.cuda(), y_perm, ros, tw, dy_perm, dtw, num_rows=rows)
+    w1, w3, w2 = inp_cpu["w1"], inp_cpu["w3"], inp_cpu["w2"]
+    dev = lambda t: None if t is None else t.cuda()  # noqa: E731
+    dx_perm = torch.zeros(max(rows, 1), d, dtype=BF16, device="cuda")
+    dw1 = torch.empty(E, h, d, device="cuda")
+    dw3 = torch.empty(E, h, d, device="cuda") if act == "swiglu" else None
+    dw2 = torch.empty(E, d, h, device="cuda")
+    ws = moe.workspace(moe.moe_expert_ffn_backward_workspace_size(E, rows, d, h, act, dt))
+    moe.moe_expert_ffn_backward(E, rows, d, h, act, dt, x_perm, off, dev(w1), dev(w3), dev(w2),
+                                dy_perm, dx_perm, dw1, dw3, dw2, ws)
+    dx = torch.empty(N, d, dtype=BF16, device="cuda")
+    moe.moe_permute_backward(buf.desc, dx_perm, ros, dx, num_rows=rows)
+    torch.cuda.synchronize()
+
+    oracle.set_threads(threads())
+    r_dyp, r_dtw = oracle.combine_backward(dt, n(dy), ref["y_perm"][:M], ref["row_of_slot"],
+                                           ref["topk_w"], M)
+    r_dxp, r_dw1, r_dw3, r_dw2 = oracle.expert_ffn_backward(
+        dt, act, ref["x_perm"][:M], ref["expert_offsets"], n(w1), n(w3), n(w2), r_dyp)
+    r_dx = oracle.permute_backward(dt, r_dxp, ref["row_of_slot"])
+    assert rel_err(dtw.cpu(), torch.from_numpy(r_dtw)) <= 1e-5
+    err = rel_err(dx.cpu().float(), as_tensor(r_dx, dt).float())
+    assert err <= TOL[dt], f"dx max rel err {err:.3e}"
+    for got, r, key in ((dw1, r_dw1, "dw1"), (dw3, r_dw3, "dw3"), (dw2, r_dw2, "dw2")):
+        if r is None:
+            continue
+        err = rel_err(got.cpu(), torch.from_numpy(r))
+        assert err <= TOL[dt], f"{key} max rel err {err:.3e}"
+
+
+def test_ffn_backward_full_switch_sampled():
+    """The full Switch shape in the launch configuration the benchmark's
+    backward pass uses: input gradients of 8 rows spread over the batch, and
+    dw1 / dw2 of one whole expert, from the oracle's per-row backward."""
+    cfg = W.full("switch")
+    N, d, h, E, act = cfg["N"], cfg["d"], cfg["h"], cfg["E"], cfg["act"]
+    print(f"[ffn backward full switch] rows={N} d={d} h={h} E={E}", flush=True)
+    inp = W.make_inputs(cfg)
+    x, w1, w2 = inp["x"], inp["w1"], inp["w2"]
+    g = torch.Generator().manual_seed(7)
+    dy = (torch.randn(N, d, generator=g) * 0.5).to(BF16)
+    counts = np.bincount(np.random.default_rng(3).integers(0, E, N), minlength=E)
+    off = np.concatenate([[0], np.cumsum(counts)]).astype(np.int32)
+    dx, dw1, _, dw2 = _gpu_backward(E, N, d, h, act, x, torch.from_numpy(off), w1, None, w2, dy)
+    xn, dyn, w1n, w2n = n(x), n(dy), n(w1), n(w2)
+    expert_of = np.searchsorted(off, np.arange(N), side="right") - 1
+    for r in np.linspace(0, N - 1, 8).astype(int):
+        e = expert_of[r]
+        r_dx, _, _, _ = oracle.ffn_backward_row("bf16", act, xn[r], w1n[e], None, w2n[e], dyn[r])
+        err = rel_err(dx[r].float(), as_tensor(r_dx, "bf16").float())
+        assert err <= TOL["bf16"], f"dx row {r} max rel err {err:.3e}"
+    e = 5
+    lo, hi = int(off[e]), int(off[e + 1])
+    Hs, dus = [], []
+    for r in range(lo, hi):
+        _, H, du, _ = oracle.ffn_backward_row("bf16", act, xn[r], w1n[e], None, w2n[e], dyn[r])
+        Hs.append(H)
+        dus.append(du)
+    xe = as_tensor(xn[lo:hi], "bf16").double().numpy()
+    dye = as_tensor(dyn[lo:hi], "bf16").double().numpy()
+    r_dw1 = np.array(dus).T @ xe      # sum over the expert's rows of du x^T
+    r_dw2 = dye.T @ np.array(Hs)      # sum over the expert's rows of dy H^T
+    err = rel_err(dw1[e], torch.from_numpy(r_dw1))
+    assert err <= TOL["bf16"], f"dw1[{e}] max rel err {err:.3e}"
+    err = rel_err(dw2[e], torch.from_numpy(r_dw2))
+    assert err <= TOL["bf16"], f"dw2[{e}] max rel err {err:.3e}"

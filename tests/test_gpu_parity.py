@@ -499,8 +499,12 @@ def test_combine_and_permute_backward(name):
     dxp = torch.randn(max(M, 1), d, generator=g).to(W.torch_dtype(cfg))
     buf = moe.MoeBuffers(cfg)
     rows = buf.rows
-    y_perm = gpu["y_perm"].cuda()
-    ros, tw = gpu["row_of_slot"].cuda(), gpu["topk_w"].cuda()
+    # Both sides take the oracle forward's layout, weights and expert outputs.
+    y_perm = torch.zeros(max(rows, 1), d, dtype=dy.dtype)
+    y_perm[:M] = as_tensor(ref["y_perm"][:M], dt)
+    y_perm = y_perm.cuda()
+    ros_cpu, tw_cpu = torch.from_numpy(ref["row_of_slot"]), torch.from_numpy(ref["topk_w"])
+    ros, tw = ros_cpu.cuda(), tw_cpu.cuda()
     dy_perm = torch.zeros(rows, d, dtype=dy.dtype, device="cuda")
     dw = torch.full((N, k), 7.0, dtype=torch.float32, device="cuda")
     dx_perm = torch.zeros(rows, d, dtype=dy.dtype, device="cuda")
@@ -510,13 +514,13 @@ def test_combine_and_permute_backward(name):
     moe.moe_combine_backward(buf.desc, dy.cuda(), y_perm, ros, tw, dy_perm, dw, num_rows=rows)
     moe.moe_permute_backward(buf.desc, dx_perm, ros, dx, num_rows=rows)
     torch.cuda.synchronize()
-    r_dyp, r_dw = oracle.combine_backward(dt, n(dy), n(gpu["y_perm"][:M]), n(gpu["row_of_slot"]),
-                                          n(gpu["topk_w"]), M)
-    r_dx = oracle.permute_backward(dt, n(dxp[:M]), n(gpu["row_of_slot"]))
+    r_dyp, r_dw = oracle.combine_backward(dt, n(dy), ref["y_perm"][:M], ref["row_of_slot"],
+                                          ref["topk_w"], M)
+    r_dx = oracle.permute_backward(dt, n(dxp[:M]), ref["row_of_slot"])
     err = rel_err(dy_perm[:M].float(), as_tensor(r_dyp, dt).float())
     assert err <= TOL[dt], f"dy_perm max rel err {err:.3e}"
     assert rel_err(dw.cpu(), torch.from_numpy(r_dw)) <= 1e-5
-    dropped = gpu["row_of_slot"] < 0
+    dropped = ros_cpu < 0
     assert bool((dw.cpu()[dropped] == 0).all())
     err = rel_err(dx.float().cpu(), as_tensor(r_dx, dt).float())
     assert err <= TOL[dt], f"dx max rel err {err:.3e}"
