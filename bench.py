@@ -174,10 +174,11 @@ def rank_share(moe, torch, cfg, buf, wts, steps: int) -> dict:
             "bound": "mfma" if flops / (peak * 1e12) >= nbytes / (HBM_PEAK_GBS * 1e9) else "hbm"}
 
 
-def backward_pass(moe, torch, buf, steps: int) -> dict:
-    """The data path's backward on the layer's last layout: the combine's
-    expert terms (row and weight gradients) and the permute's adjoint, timed
-    with events; per call, the algorithmic bytes over the time."""
+def backward_pass(moe, torch, buf, inp, steps: int) -> dict:
+    """The layer's backward on its last layout: the combine's expert terms
+    (row and weight gradients), the expert FFN's backward (input and weight
+    gradients, bf16) and the permute's adjoint, timed with events; per call,
+    the algorithmic bytes (data path) or FLOPs (FFN) over the time."""
     d = buf.desc
     N, k, dim = d.num_tokens, d.top_k, d.hidden
     dev = buf.y.device
@@ -215,8 +216,48 @@ def backward_pass(moe, torch, buf, steps: int) -> dict:
     cb_bytes = N * dim * es + 2 * M * dim * es + S * 12  # dy, y_perm rows, dy_perm rows
     pb_bytes = M * dim * es + N * dim * es + S * 4       # dx_perm rows, dx
     frac = lambda nb, us: round(nb / (us * 1e-6) / (HBM_PEAK_GBS * 1e9), 4)
-    return {"combine_backward": {"us": round(cb, 2), "hbm_frac": frac(cb_bytes, cb)},
-            "permute_backward": {"us": round(pb, 2), "hbm_frac": frac(pb_bytes, pb)}}
+    out = {"combine_backward": {"us": round(cb, 2), "hbm_frac": frac(cb_bytes, cb)},
+           "permute_backward": {"us": round(pb, 2), "hbm_frac": frac(pb_bytes, pb)}}
+    cfg = buf.cfg
+    if cfg["dtype"] != "bf16":
+        return out
+    # Expert FFN backward over the admitted rows, plain row-major weights.
+    E, h, act = d.num_experts, cfg["h"], cfg["act"]
+    w1, w3, w2 = inp["w1"], inp.get("w3"), inp["w2"]
+    sw = act == "swiglu"
+    dx_perm = torch.empty_like(buf.x_perm)
+    dw1 = torch.empty(E, h, dim, dtype=torch.float32, device=dev)
+    dw3 = torch.empty(E, h, dim, dtype=torch.float32, device=dev) if sw else None
+    dw2 = torch.empty(E, dim, h, dtype=torch.float32, device=dev)
+    ws = moe.workspace(moe.moe_expert_ffn_backward_workspace_size(E, buf.rows, dim, h, act, "bf16"),
+                       dev)
+
+    def ffn_bwd():
+        moe.moe_expert_ffn_backward(E, buf.rows, dim, h, act, "bf16", buf.x_perm,
+                                    buf.expert_offsets, w1, w3, w2, dy_perm, dx_perm, dw1, dw3,
+                                    dw2, ws)
+
+    for _ in range(2):
+        ffn_bwd()
+    torch.cuda.synchronize()
+    fb = 0.0
+    for _ in range(steps):
+        ev[0].record()
+        ffn_bwd()
+        ev[1].record()
+        torch.cuda.synchronize()
+        fb += ev[0].elapsed_time(ev[1])
+    fb = fb / steps * 1e3
+    # Products per row: u (and v) and g over d, dx over h (2h), the weight
+    # gradients over the rows: 2 d h FLOPs each.
+    n_mm = 7 if sw else 4
+    flops = 2.0 * M * dim * h * n_mm
+    grad_bytes = (3 if sw else 2) * E * h * dim * 4  # fp32 weight gradients written
+    out["ffn_backward"] = {
+        "us": round(fb, 2), "tflops": round(flops / (fb * 1e-6) / 1e12, 1),
+        "mfma_frac": round(flops / (fb * 1e-6) / (MFMA_PEAK_TFLOPS["bf16"] * 1e12), 4),
+        "weight_grad_bytes": grad_bytes}
+    return out
 
 
 def describe(cfg) -> str:
@@ -605,7 +646,7 @@ def main():
     if args.rank_share:
         out["rank_share"] = rank_share(moe, torch, cfg, buf, wts, max(5, min(args.steps, 30)))
     if args.backward:
-        out["backward"] = backward_pass(moe, torch, buf, max(5, min(args.steps, 30)))
+        out["backward"] = backward_pass(moe, torch, buf, inp, max(5, min(args.steps, 30)))
     if not args.no_cpu_baseline:
         host = {}
         for key, v in inp.items():
