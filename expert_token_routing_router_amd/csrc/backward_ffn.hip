@@ -13,18 +13,20 @@
 // u and v are recomputed, not kept from the forward.
 //
 // Three kernels, all on v_mfma_f32_32x32x16_bf16 with fp32 accumulators:
-//   bwd_act    per 64-row tile of an expert, K = d: the three products x W1^T,
+//   bwd_act    per 128-row tile of an expert, K = d: the three products x W1^T,
 //              x W3^T and dy W2 share the tile; the epilogue writes H and
 //              G = [du | dv] (bf16) to the workspace;
 //   bwd_dgrad  dx = G [W1 ; W3], K = h (2h for SwiGLU);
 //   bwd_wgrad  weight gradients, K = the expert's rows: G^T x into dW1 / dW3,
 //              dy^T H into dW2.  An expert with no rows gets zeros.
-// Block tile: 128 output columns x 64 output rows; 4 waves of 64 x 32 (two
-// 32x32 fragments each).  A staged operand tile holds 32 k per row in LDS,
+// Block tile: 128 output columns x 128 output rows; 4 waves of 64 x 64 (2 x 2
+// fragments of 32 x 32).  A staged operand tile holds 32 k per row in LDS,
 // rows padded to 40 elements; operands whose memory runs along the row
 // index instead (W2 in bwd_act, the weights in bwd_dgrad, every operand of
-// bwd_wgrad) are transposed on their way into LDS.  The next K step's global
-// loads are in flight while the current step is multiplied.
+// bwd_wgrad) are transposed on their way into LDS, each thread loading the
+// same 8 rows at two consecutive k and writing them as 8 packed k pairs.
+// The next K step's global loads are in flight while the current step is
+// multiplied.
 #include "device.h"
 #include "kernels.h"
 
@@ -35,7 +37,7 @@ typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 
 constexpr int kBK = 32, kLdk = kBK + 8;  // staged row: 32 k + 8 pad elements (80 bytes)
-constexpr int kTM = 128, kTN = 64;       // block tile: output columns x output rows
+constexpr int kTM = 128, kTN = 128;      // block tile: output columns x output rows
 constexpr int kThreads = 256;
 constexpr int kRelu = 0, kGelu = 1, kSwiglu = 2;
 
@@ -44,6 +46,7 @@ size_t align256(size_t x) { return (x + 255) / 256 * 256; }
 // The 16-byte vectors one thread stages per K step for an R-row tile.
 template <int R>
 struct Stage {
+  static_assert(R == 128, "staged tiles are 128 rows: two vectors per thread");
   u32x4 v[R * (kBK / 8) / kThreads];
 };
 
@@ -72,15 +75,17 @@ __device__ __forceinline__ void put_k(bf16_t* T, const Stage<R>& s) {
 
 // Rows whose memory runs along the row index: element (row, k) at
 // src[(k0 + k) * ld + row0 + row]; k at or past nk, and rows at or past nrow
-// (a multiple of 8), read as zero.
+// (a multiple of 8), read as zero.  Thread i stages rows [8c, 8c + 8) at
+// k = 2kp and 2kp + 1 (kp = i / 16, c = i % 16).
 template <int R>
 __device__ __forceinline__ void fetch_t(Stage<R>& s, const bf16_t* __restrict__ src, size_t ld,
                                         int row0, int nrow, int k0, int nk) {
-  constexpr int VPK = R / 8;  // vectors per k
+  const int kp = threadIdx.x >> 4, c = threadIdx.x & 15;
+  const bool row_ok = 8 * c < nrow;
 #pragma unroll
-  for (int p = 0; p < R * 4 / kThreads; ++p) {
-    const int idx = p * kThreads + threadIdx.x, k = idx / VPK, c = idx % VPK;
-    s.v[p] = (k < nk && 8 * c < nrow)
+  for (int p = 0; p < 2; ++p) {
+    const int k = 2 * kp + p;
+    s.v[p] = (row_ok && k < nk)
                  ? *reinterpret_cast<const u32x4*>(src + (size_t)(k0 + k) * ld + row0 + 8 * c)
                  : u32x4{0u, 0u, 0u, 0u};
   }
@@ -88,49 +93,55 @@ __device__ __forceinline__ void fetch_t(Stage<R>& s, const bf16_t* __restrict__ 
 
 template <int R>
 __device__ __forceinline__ void put_t(bf16_t* T, const Stage<R>& s) {
-  constexpr int VPK = R / 8;
+  const int kp = threadIdx.x >> 4, c = threadIdx.x & 15;
 #pragma unroll
-  for (int p = 0; p < R * 4 / kThreads; ++p) {
-    const int idx = p * kThreads + threadIdx.x, k = idx / VPK, c = idx % VPK;
-#pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      const uint32_t w = s.v[p][q];
-      T[(8 * c + 2 * q) * kLdk + k] = (bf16_t)(w & 0xffffu);
-      T[(8 * c + 2 * q + 1) * kLdk + k] = (bf16_t)(w >> 16);
-    }
+  for (int q = 0; q < 4; ++q) {
+    const uint32_t a = s.v[0][q], b = s.v[1][q];  // rows 8c + 2q, 8c + 2q + 1 at k = 2kp, 2kp + 1
+    *reinterpret_cast<uint32_t*>(T + (8 * c + 2 * q) * kLdk + 2 * kp) = (a & 0xffffu) | (b << 16);
+    *reinterpret_cast<uint32_t*>(T + (8 * c + 2 * q + 1) * kLdk + 2 * kp) =
+        (a >> 16) | (b & 0xffff0000u);
   }
 }
 
-// acc[f] += P rows [wm*64 + 32f, +32) x Q rows [wn*32, +32) over the 32
-// staged k.  Afterwards lane l of fragment f holds, in acc[f][4g + i], output
-// column wm*64 + 32f + 8g + 4(l/32) + i of output row wn*32 + l%32.
-__device__ __forceinline__ void mma(f32x16 (&acc)[2], const bf16_t* P, const bf16_t* Q, int wm,
-                                    int wn, int lane) {
+// acc[f][j] += P rows [wm*64 + 32f, +32) x Q rows [wn*64 + 32j, +32) over
+// the 32 staged k.  Afterwards lane l holds, in acc[f][j][4g + i], output
+// column wm*64 + 32f + 8g + 4(l/32) + i of output row wn*64 + 32j + l%32.
+typedef f32x16 Acc[2][2];
+
+__device__ __forceinline__ void mma(Acc& acc, const bf16_t* P, const bf16_t* Q, int wm, int wn,
+                                    int lane) {
   const int lr = lane & 31, lk = (lane >> 5) * 8;
 #pragma unroll
   for (int kk = 0; kk < kBK; kk += 16) {
-    const bf16x8 q = *reinterpret_cast<const bf16x8*>(Q + (wn * 32 + lr) * kLdk + kk + lk);
+    bf16x8 q[2], p[2];
 #pragma unroll
-    for (int f = 0; f < 2; ++f) {
-      const bf16x8 p =
-          *reinterpret_cast<const bf16x8*>(P + (wm * 64 + f * 32 + lr) * kLdk + kk + lk);
-      acc[f] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(p, q, acc[f], 0, 0, 0);
-    }
+    for (int j = 0; j < 2; ++j)
+      q[j] = *reinterpret_cast<const bf16x8*>(Q + (wn * 64 + j * 32 + lr) * kLdk + kk + lk);
+#pragma unroll
+    for (int f = 0; f < 2; ++f)
+      p[f] = *reinterpret_cast<const bf16x8*>(P + (wm * 64 + f * 32 + lr) * kLdk + kk + lk);
+#pragma unroll
+    for (int f = 0; f < 2; ++f)
+#pragma unroll
+      for (int j = 0; j < 2; ++j)
+        acc[f][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(p[f], q[j], acc[f][j], 0, 0, 0);
   }
 }
 
-__device__ __forceinline__ void zero(f32x16 (&acc)[2]) {
+__device__ __forceinline__ void zero(Acc& acc) {
 #pragma unroll
   for (int f = 0; f < 2; ++f)
 #pragma unroll
-    for (int i = 0; i < 16; ++i) acc[f][i] = 0.f;
+    for (int j = 0; j < 2; ++j)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) acc[f][j][i] = 0.f;
 }
 
 __device__ __forceinline__ void store4_bf16(bf16_t* p, float a, float b, float c, float d) {
   *reinterpret_cast<uint2*>(p) = make_uint2(pack_bf16x2(a, b), pack_bf16x2(c, d));
 }
 
-// 64-row tiles of every expert's segment, in expert order: tiles[q] = (expert,
+// 128-row tiles of every expert's segment, in expert order: tiles[q] = (expert,
 // first row, end row).  At most cap tiles are written (segments that overlap
 // could ask for more); count = the number written.
 __global__ __launch_bounds__(1024) void bwd_plan(const int32_t* __restrict__ offsets, int E,
@@ -158,7 +169,7 @@ __global__ __launch_bounds__(1024) void bwd_plan(const int32_t* __restrict__ off
   if (e == 1023) *count = min(s[1023], cap);
 }
 
-// H and G = [du | dv] for one 64-row tile and 128 columns of h.
+// H and G = [du | dv] for one 128-row tile and 128 columns of h.
 template <int ACT>
 __global__ __launch_bounds__(kThreads) void bwd_act(
     const bf16_t* __restrict__ x, const bf16_t* __restrict__ dy, const bf16_t* __restrict__ w1,
@@ -189,7 +200,7 @@ __global__ __launch_bounds__(kThreads) void bwd_act(
     fetch_k<kTN>(sd, dy, d, r0, nr, k0);
   };
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6, wm = w & 1, wn = w >> 1;
-  f32x16 au[2], av[2], ag[2];
+  Acc au, av, ag;
   zero(au);
   zero(av);
   zero(ag);
@@ -207,45 +218,48 @@ __global__ __launch_bounds__(kThreads) void bwd_act(
     if constexpr (DUAL) mma(av, P3, QX, wm, wn, lane);
     mma(ag, P2, QD, wm, wn, lane);
   }
-  const int n = wn * 32 + (lane & 31);
-  if (n >= nr) return;
-  const size_t row = (size_t)(r0 + n);
   const size_t ldg = DUAL ? 2 * (size_t)h : (size_t)h;
 #pragma unroll
-  for (int f = 0; f < 2; ++f) {
+  for (int j = 0; j < 2; ++j) {
+    const int n = wn * 64 + j * 32 + (lane & 31);
+    if (n >= nr) continue;
+    const size_t row = (size_t)(r0 + n);
 #pragma unroll
-    for (int g = 0; g < 4; ++g) {
-      const int m = wm * 64 + f * 32 + g * 8 + 4 * (lane >> 5);
-      if (m >= nm) continue;
-      float hv[4], gu[4], gv[4];
+    for (int f = 0; f < 2; ++f) {
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const float u = au[f][4 * g + i], gg = ag[f][4 * g + i];
-        if constexpr (ACT == kRelu) {
-          hv[i] = fmaxf(u, 0.f);
-          gu[i] = u > 0.f ? gg : 0.f;
-        } else if constexpr (ACT == kGelu) {
-          const float Phi = 0.5f * (1.f + erff(u * 0.70710678118654752f));
-          const float phi = 0.39894228040143268f * expf(-0.5f * u * u);
-          hv[i] = u * Phi;
-          gu[i] = gg * (Phi + u * phi);
-        } else {
-          const float v = av[f][4 * g + i];
-          const float s = 1.f / (1.f + expf(-u)), si = u * s;
-          hv[i] = si * v;
-          gu[i] = gg * v * (s * (1.f + u * (1.f - s)));
-          gv[i] = gg * si;
+      for (int g = 0; g < 4; ++g) {
+        const int m = wm * 64 + f * 32 + g * 8 + 4 * (lane >> 5);
+        if (m >= nm) continue;
+        float hv[4], gu[4], gv[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const float u = au[f][j][4 * g + i], gg = ag[f][j][4 * g + i];
+          if constexpr (ACT == kRelu) {
+            hv[i] = fmaxf(u, 0.f);
+            gu[i] = u > 0.f ? gg : 0.f;
+          } else if constexpr (ACT == kGelu) {
+            const float Phi = 0.5f * (1.f + erff(u * 0.70710678118654752f));
+            const float phi = 0.39894228040143268f * expf(-0.5f * u * u);
+            hv[i] = u * Phi;
+            gu[i] = gg * (Phi + u * phi);
+          } else {
+            const float v = av[f][j][4 * g + i];
+            const float s = 1.f / (1.f + expf(-u)), si = u * s;
+            hv[i] = si * v;
+            gu[i] = gg * v * (s * (1.f + u * (1.f - s)));
+            gv[i] = gg * si;
+          }
         }
+        const int col = m0 + m;
+        store4_bf16(Hbuf + row * h + col, hv[0], hv[1], hv[2], hv[3]);
+        store4_bf16(G + row * ldg + col, gu[0], gu[1], gu[2], gu[3]);
+        if constexpr (DUAL) store4_bf16(G + row * ldg + h + col, gv[0], gv[1], gv[2], gv[3]);
       }
-      const int col = m0 + m;
-      store4_bf16(Hbuf + row * h + col, hv[0], hv[1], hv[2], hv[3]);
-      store4_bf16(G + row * ldg + col, gu[0], gu[1], gu[2], gu[3]);
-      if constexpr (DUAL) store4_bf16(G + row * ldg + h + col, gv[0], gv[1], gv[2], gv[3]);
     }
   }
 }
 
-// dx for one 64-row tile and 128 columns of d: K runs over [du | dv].
+// dx for one 128-row tile and 128 columns of d: K runs over [du | dv].
 template <bool DUAL>
 __global__ __launch_bounds__(kThreads) void bwd_dgrad(
     const bf16_t* __restrict__ G, const bf16_t* __restrict__ w1, const bf16_t* __restrict__ w3,
@@ -269,7 +283,7 @@ __global__ __launch_bounds__(kThreads) void bwd_dgrad(
     fetch_k<kTN>(sq, G, K, r0, nr, k0);
   };
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6, wm = w & 1, wn = w >> 1;
-  f32x16 acc[2];
+  Acc acc;
   zero(acc);
   fetch(0);
   for (int k0 = 0; k0 < K; k0 += kBK) {
@@ -280,17 +294,20 @@ __global__ __launch_bounds__(kThreads) void bwd_dgrad(
     if (k0 + kBK < K) fetch(k0 + kBK);
     mma(acc, P, Q, wm, wn, lane);
   }
-  const int n = wn * 32 + (lane & 31);
-  if (n >= nr) return;
-  bf16_t* out = dx + (size_t)(r0 + n) * d + m0;
 #pragma unroll
-  for (int f = 0; f < 2; ++f) {
+  for (int j = 0; j < 2; ++j) {
+    const int n = wn * 64 + j * 32 + (lane & 31);
+    if (n >= nr) continue;
+    bf16_t* out = dx + (size_t)(r0 + n) * d + m0;
 #pragma unroll
-    for (int g = 0; g < 4; ++g) {
-      const int m = wm * 64 + f * 32 + g * 8 + 4 * (lane >> 5);
-      if (m < nm)
-        store4_bf16(out + m, acc[f][4 * g], acc[f][4 * g + 1], acc[f][4 * g + 2],
-                    acc[f][4 * g + 3]);
+    for (int f = 0; f < 2; ++f) {
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const int m = wm * 64 + f * 32 + g * 8 + 4 * (lane >> 5);
+        if (m < nm)
+          store4_bf16(out + m, acc[f][j][4 * g], acc[f][j][4 * g + 1], acc[f][j][4 * g + 2],
+                      acc[f][j][4 * g + 3]);
+      }
     }
   }
 }
@@ -319,7 +336,7 @@ __global__ __launch_bounds__(kThreads) void bwd_wgrad(
     fetch_t<kTN>(sq, Qsrc, ldq, n0, nn, lo + k0, nk);
   };
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6, wm = w & 1, wn = w >> 1;
-  f32x16 acc[2];
+  Acc acc;
   zero(acc);
   if (K > 0) fetch(0);
   for (int k0 = 0; k0 < K; k0 += kBK) {
@@ -330,19 +347,22 @@ __global__ __launch_bounds__(kThreads) void bwd_wgrad(
     if (k0 + kBK < K) fetch(k0 + kBK);
     mma(acc, P, Q, wm, wn, lane);
   }
-  const int nl = wn * 32 + (lane & 31);
-  if (nl >= nn) return;
-  const int n = n0 + nl;
-  float* orow = n < split ? outA + ((size_t)e * split + n) * M
-                          : outB + ((size_t)e * (Nn - split) + (n - split)) * M;
 #pragma unroll
-  for (int f = 0; f < 2; ++f) {
+  for (int j = 0; j < 2; ++j) {
+    const int nl = wn * 64 + j * 32 + (lane & 31);
+    if (nl >= nn) continue;
+    const int n = n0 + nl;
+    float* orow = n < split ? outA + ((size_t)e * split + n) * M
+                            : outB + ((size_t)e * (Nn - split) + (n - split)) * M;
 #pragma unroll
-    for (int g = 0; g < 4; ++g) {
-      const int m = wm * 64 + f * 32 + g * 8 + 4 * (lane >> 5);
-      if (m < nm)
-        *reinterpret_cast<float4*>(orow + m0 + m) =
-            make_float4(acc[f][4 * g], acc[f][4 * g + 1], acc[f][4 * g + 2], acc[f][4 * g + 3]);
+    for (int f = 0; f < 2; ++f) {
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const int m = wm * 64 + f * 32 + g * 8 + 4 * (lane >> 5);
+        if (m < nm)
+          *reinterpret_cast<float4*>(orow + m0 + m) = make_float4(
+              acc[f][j][4 * g], acc[f][j][4 * g + 1], acc[f][j][4 * g + 2], acc[f][j][4 * g + 3]);
+      }
     }
   }
 }
