@@ -4,21 +4,26 @@
 One step is one pass of the whole hot path over one batch of synthetic input,
 already resident in HBM: route -> dispatch -> expert FFN (plan, up, down; plus
 the shared expert where the workload has one) -> combine -> selection-bias
-update.  Default workload: Switch-style top-1, N=16384 tokens, d=1024, 64
-experts, softmax over all 64, capacity factor 1.25 (cap 320, token-order
-admission), GELU experts 1024->4096->1024, 8 simulated EP ranks, bf16.
+update.  Default workload: the largest configuration that fits one GPU, the
+DeepSeek-V3-like layer (N=4096 tokens, d=7168, 256 routed experts plus one
+shared expert, sigmoid affinities with a selection-only bias, 8 groups of 32
+keeping 4, top-8, SwiGLU 7168->2048->7168, 64 simulated EP ranks, bf16).
 
-Prints one JSON line.  Every library call inside the timed region is bracketed
-by HIP events on the stream it is launched on; the per-call averages give the
-roofline of the dominant kernel and the per-step breakdown.  Two more passes
-give the step-time percentiles (one event per step) and the cold-cache per-call
-times (a 512 MiB write before each step evicts the Infinity Cache and the L2s).  The CPU oracle is
-timed on a bounded sample of the same workload (``cpu_baseline``).
+Prints one JSON line.  Every library call inside a second pass over the same
+steps is bracketed by HIP events on the stream it is launched on; the per-call
+averages give the roofline of the dominant kernel (algorithmic bytes or FLOPs
+over its average duration) and the per-step breakdown.  Two more passes give
+the step-time percentiles (one event per step) and the cold-cache per-call
+times (a 512 MiB write before each step evicts the Infinity Cache and the
+L2s).  The CPU oracle is timed on a bounded sample of the same workload
+(``cpu_baseline``).  Short passes over other workloads (``--extra-workloads``,
+default the Switch-style and Mixtral-like layers) are reported beside it.
 """
 
 from __future__ import annotations
 
 import argparse
+import glob
 import hashlib
 import json
 import math
@@ -34,15 +39,15 @@ METRIC = "MoE layer tokens/sec at 1 GPU; grouped-GEMM % MFMA peak; permute % HBM
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, published
 MFMA_PEAK_TFLOPS = {"bf16": 2500.0, "fp32": 157.3}  # dense, published
 PROFILE_DIR = os.path.join(ROOT, "profiles")
+WORKLOADS = ["toy", "switch", "mixtral", "deepseek", "zipf", "decode"]
 
 
-def parse_args():
+def parse_args(argv=None):
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=50)
-    ap.add_argument("--workload", default="switch",
-                    choices=["toy", "switch", "mixtral", "deepseek", "zipf", "decode"])
+    ap.add_argument("--workload", default="deepseek", choices=WORKLOADS)
     ap.add_argument("--cf", type=float, default=None, help="override the capacity factor")
     ap.add_argument("--admission", default="token", choices=["token", "first_choice"],
                     help="capacity admission order: token order, or every token's first "
@@ -56,18 +61,23 @@ def parse_args():
     ap.add_argument("--payload", default="native", choices=["native", "int8"],
                     help="dispatched rows as the layer dtype, or as the INT8 payload "
                          "(quantised in the permute, dequantised before the FFN)")
-    ap.add_argument("--no-clocks", action="store_true",
-                    help="skip reading the clocks with rocm-smi (a child process; under a "
-                         "profiler that has already initialised the GPU, leave it out)")
+    ap.add_argument("--combine", default="unfused", choices=["unfused", "fused"],
+                    help="unfused: the down GEMM writes y_perm and moe_combine gathers it; "
+                         "fused: the down GEMM scatter-adds w*O into an fp32 accumulator "
+                         "that moe_combine finishes")
+    ap.add_argument("--no-clocks", action="store_true", help="skip reading the clocks")
     ap.add_argument("--backward", action="store_true",
-                    help="also time the data path's backward (moe_combine_backward, "
-                         "moe_permute_backward) on this workload's layout")
+                    help="also time the layer's backward calls on this workload's layout")
     ap.add_argument("--rank-share", action="store_true",
                     help="also time the expert FFN on one rank's share of the experts at "
                          "its real shape (rows from all R source ranks)")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="also run one device copy of this size (counter calibration)")
-    return ap.parse_args()
+    ap.add_argument("--extra-workloads", default="switch,mixtral",
+                    help="comma-separated workloads timed briefly beside the headline "
+                         "one ('none' for none)")
+    ap.add_argument("--extra-steps", type=int, default=30)
+    return ap.parse_args(argv)
 
 
 def kernel_sources_digest() -> str:
@@ -102,21 +112,336 @@ def read_traffic(kernel: str, workload: str, digest: str):
 
 
 def read_clocks() -> dict:
-    """Current clocks from rocm-smi, if it answers within a few seconds.  Runs
-    before this process initialises the GPU."""
+    """The selected DPM levels of the first AMD GPU the kernel driver exposes in
+    sysfs (pp_dpm_sclk / pp_dpm_mclk; the line marked '*' is the current one).
+    Read in-process: no child process, so nothing is spawned under a profiler."""
     info = {}
-    try:
-        import subprocess
-        r = subprocess.run(["rocm-smi", "--showclocks", "--json"], capture_output=True,
-                           text=True, timeout=20)
-        card = next(iter(json.loads(r.stdout).values()))
-        for key, val in card.items():
-            kl = key.lower()
-            if "sclk" in kl or "mclk" in kl:
-                info[key] = val
-    except Exception as exc:  # clocks are context, never a reason to fail
-        info["clocks"] = f"unavailable ({type(exc).__name__})"
-    return info
+    for dev in sorted(glob.glob("/sys/class/drm/card*/device")):
+        try:
+            with open(os.path.join(dev, "vendor")) as f:
+                if f.read().strip() != "0x1002":
+                    continue
+            for clk in ("sclk", "mclk"):
+                with open(os.path.join(dev, f"pp_dpm_{clk}")) as f:
+                    cur = [l.strip() for l in f if l.strip().endswith("*")]
+                info[clk] = cur[0] if cur else "unknown"
+            info["sysfs"] = dev
+            return info
+        except OSError:
+            continue
+    return {"clocks": "unavailable (no readable pp_dpm_* in sysfs)"}
+
+
+def describe(cfg) -> str:
+    s = (f"{cfg['name']} N={cfg['N']} d={cfg['d']} h={cfg['h']} E={cfg['E']} k={cfg['k']} "
+         f"score={cfg['score']} act={cfg['act']} R={cfg['R']}")
+    if cfg.get("cf"):
+        s += f" cf={cfg['cf']}"
+    if cfg.get("G", 1) > 1:
+        s += f" groups={cfg['G']}/keep{cfg['kg']}"
+    if cfg.get("shared"):
+        s += " +shared"
+    if cfg.get("admission", "token") != "token":
+        s += f" admission={cfg['admission']}"
+    if cfg.get("payload", "native") != "native":
+        s += f" payload={cfg['payload']}"
+    if cfg.get("layout", "compact") != "compact":
+        s += f" layout={cfg['layout']}"
+    if cfg.get("combine", "unfused") != "unfused":
+        s += f" combine={cfg['combine']}"
+    return s
+
+
+class LayerRun:
+    """One workload's inputs (resident in HBM), packed weights, buffers and the
+    step as a sequence of library calls on torch's current stream."""
+
+    def __init__(self, cfg, dev):
+        import torch
+
+        import expert_token_routing_router_amd as moe
+        from expert_token_routing_router_amd import layer
+        import moe_workloads as W
+
+        self.torch, self.moe, self.layer = torch, moe, layer
+        self.cfg = cfg
+        # Inputs: the glossary snippet's stream for the toy workload (CPU),
+        # else drawn on the device.
+        gen_dev = "cpu" if cfg["name"] == "toy" else "cuda"
+        src = W.make_inputs(cfg, device=gen_dev)
+        self.inp = {k: (tuple(None if t is None else t.to(dev) for t in v) if isinstance(v, tuple)
+                        else (v.to(dev) if isinstance(v, torch.Tensor) else v))
+                    for k, v in src.items()}
+        self.buf = moe.MoeBuffers(cfg, dev)
+        # bf16 expert weights are packed once, as a model load would, before any
+        # timed work.
+        self.wts = moe.prepare_weights(cfg, self.inp)
+        d = self.buf.desc
+        self.E = d.num_experts
+        self.bias_state = (self.inp["sel_bias"].clone() if self.inp.get("sel_bias") is not None
+                           else torch.zeros(self.E, dtype=torch.float32, device=dev))
+        self.step_bias = cfg.get("bias_step", 1e-3)
+        self.q8 = self.buf.x_perm_q is not None
+        self.padded = cfg.get("layout", "compact") == "padded"
+        self.fused = cfg.get("combine", "unfused") == "fused"
+        # The padded layout's padding rows are zeroed by the whole-dispatch
+        # call, so that layout runs the dispatch as one call; otherwise the
+        # dispatch runs as its two halves (the same kernels in the same order
+        # as one moe_dispatch call, timed apart).
+        disp = (["dispatch"] if self.padded else
+                ["dispatch_layout", "permute"] + (["dequantize"] if self.q8 else []))
+        self.calls = ["route"] + disp + ["ffn_plan", "ffn_up", "ffn_down", "combine",
+                                         "bias_update"]
+        self.fork = layer.has_shared(self.buf, self.wts)
+        self.main = torch.cuda.current_stream()
+
+    def step(self, events=None, shared_events=None):
+        """One layer step.  A shared expert (needs only x) is forked onto a side
+        stream at the start and joined before the combine, as the layer's
+        forward does, timed by its own pair of events on that stream."""
+        moe, layer, buf, cfg, inp, wts = (self.moe, self.layer, self.buf, self.cfg, self.inp,
+                                          self.wts)
+        d = buf.desc
+        E, dim, h = d.num_experts, d.hidden, cfg["h"]
+        rows = buf.rows
+        main = self.main
+        marks = iter(events or [])
+
+        def mark():
+            if events is not None:
+                next(marks).record(main)
+
+        if self.fork:
+            buf.side_stream.wait_stream(main)
+            if shared_events is not None:
+                shared_events[0].record(buf.side_stream)
+            layer.shared_ffn(buf, wts, buf.side_stream)
+            if shared_events is not None:
+                shared_events[1].record(buf.side_stream)
+        mark()
+        layer.route(buf, inp)
+        mark()
+        if self.padded:
+            layer.dispatch(buf, inp)
+        else:
+            moe.moe_dispatch_layout(d, buf.flags, buf.topk_idx, buf.row_of_slot,
+                                    buf.token_of_row, buf.slot_of_row, buf.expert_offsets,
+                                    buf.admitted, buf.rank_offsets, buf.rank_counts,
+                                    buf.ws_dispatch)
+            mark()
+            if self.q8:
+                moe.moe_permute_q8(d, inp["x"], buf.row_of_slot, buf.x_perm_q, buf.row_scale)
+                mark()
+                moe.moe_dequantize_q8(rows, dim, cfg["dtype"], buf.x_perm_q, buf.row_scale,
+                                      buf.expert_offsets[E:], buf.x_perm)
+            else:
+                moe.moe_permute(d, inp["x"], buf.row_of_slot, buf.x_perm)
+        mark()
+        moe.moe_expert_ffn_plan(E, rows, dim, h, cfg["act"], cfg["dtype"], buf.expert_offsets,
+                                buf.ws_ffn)
+        mark()
+        moe.moe_expert_ffn_up(E, rows, dim, h, cfg["act"], cfg["dtype"], buf.x_perm,
+                              buf.expert_offsets, wts["w1"], wts.get("w3"), buf.ws_ffn)
+        mark()
+        moe.moe_expert_ffn_down(E, rows, dim, h, cfg["act"], cfg["dtype"], buf.expert_offsets,
+                                wts["w2"], None if self.fused else buf.y_perm,
+                                buf.fused_args(), buf.ws_ffn)
+        mark()
+        if self.fork:
+            main.wait_stream(buf.side_stream)
+        layer.combine(buf, inp, residual=True)
+        mark()
+        layer.bias_update(buf, self.bias_state, self.step_bias)
+        mark()
+
+    def n_events(self):
+        return len(self.calls) + 1
+
+    def algorithmic(self) -> dict:
+        """Algorithmic work of this batch per call, from the rows actually
+        admitted and the experts that received any.  The FFN's hidden buffer H
+        is implementation traffic, not algorithmic: it is in no byte count."""
+        buf, cfg = self.buf, self.cfg
+        d = buf.desc
+        N, k, E, dim, h = d.num_tokens, d.top_k, d.num_experts, d.hidden, cfg["h"]
+        S = N * k
+        es = 2 if cfg["dtype"] == "bf16" else 4
+        admitted = buf.admitted.cpu()
+        M = int(admitted.sum().item())               # admitted rows
+        laid = int(buf.expert_offsets[E].item())     # rows laid out (E*cap when padded)
+        active = int((admitted > 0).sum().item())
+        mats_up = 2 if cfg["act"] == "swiglu" else 1
+        shared = buf.shared_out is not None
+        w_up = active * mats_up * h * dim * es
+        w_down = active * dim * h * es
+        out = {
+            "M": M, "laid": laid, "active": active, "es": es, "mats_up": mats_up,
+            "ffn_up": (2.0 * M * dim * h * mats_up, w_up + M * dim * es),
+            "ffn_down": (2.0 * M * h * dim, w_down + M * dim * es),
+            "weight_bytes": w_up + w_down,
+            # route: x and the router weight read, logits and the k choices written
+            "route": (0.0, N * dim * es + E * dim * es + N * E * 4 + S * 8),
+            # layout: ids read; row_of_slot, token_of_row, slot_of_row written
+            "dispatch_layout": (0.0, S * 4 + S * 4 + buf.rows * 5),
+            # permute: x read once, every admitted row written (INT8 payload: d
+            # bytes + a 4-byte scale per row), row_of_slot read
+            "permute": (0.0, N * dim * es + (M * (dim + 4) if self.q8 else M * dim * es) + S * 4),
+            "dequantize": (0.0, laid * (dim + 4) + laid * dim * es),
+            # combine: every admitted row (fused: the fp32 accumulator row per
+            # token instead), the residual and y, the shared output, the weights
+            "combine": (0.0, (N * dim * 4 if self.fused else M * dim * es) + 2 * N * dim * es
+                        + (N * dim * es if shared else 0) + S * 8),
+        }
+        if self.fused:  # the down GEMM adds w*O into the accumulator instead of writing y_perm
+            out["ffn_down"] = (2.0 * M * h * dim, w_down + M * dim * 4)
+        if self.padded:
+            out["dispatch"] = (0.0, out["dispatch_layout"][1] + out["permute"][1]
+                               + (laid - M) * (dim + 4 if self.q8 else dim * es)
+                               + (out["dequantize"][1] if self.q8 else 0))
+        return out
+
+
+def time_steps(run, steps):
+    """Exactly `steps` steps between two synchronisations (one GPU, so no
+    barrier is needed beyond that); the step time is the larger of the HIP-event
+    and the host wall time of the region."""
+    torch = run.torch
+    edge = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    edge[0].record()
+    for _ in range(steps):
+        run.step()
+    edge[1].record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    gpu_ms = edge[0].elapsed_time(edge[1])
+    return max(gpu_ms, wall * 1e3) / steps, gpu_ms, wall
+
+
+def per_call_pass(run, steps):
+    """The same steps with a HIP event at every call boundary on the main
+    stream (every call is launched on it; the shared expert has its own pair on
+    the side stream).  Each event drains the queue for a few microseconds, so
+    this pass gives per-kernel durations, not the step time."""
+    torch = run.torch
+    nev = run.n_events()
+    events = [[torch.cuda.Event(enable_timing=True) for _ in range(nev)] for _ in range(steps)]
+    sh = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(steps)]
+    torch.cuda.synchronize()
+    for s in range(steps):
+        run.step(events[s], sh[s])
+    torch.cuda.synchronize()
+    per = {c: sum(ev[i].elapsed_time(ev[i + 1]) for ev in events) / steps * 1e3
+           for i, c in enumerate(run.calls)}  # microseconds
+    if run.fork:
+        per["shared_ffn"] = sum(a.elapsed_time(b) for a, b in sh) / steps * 1e3
+    inst = sum(ev[0].elapsed_time(ev[-1]) for ev in events) / steps
+    return per, inst
+
+
+def kernel_table(run, alg, per) -> dict:
+    peak = MFMA_PEAK_TFLOPS[run.cfg["dtype"]]
+    kern = {}
+    for name, us in per.items():
+        ent = {"us": round(us, 2)}
+        if name in alg and isinstance(alg[name], tuple):
+            flops, nbytes = alg[name]
+            t = us * 1e-6
+            ent["gbs"] = round(nbytes / t / 1e9, 1)
+            ent["hbm_frac"] = round(nbytes / t / (HBM_PEAK_GBS * 1e9), 4)
+            if flops:
+                t_f, t_b = flops / (peak * 1e12), nbytes / (HBM_PEAK_GBS * 1e9)
+                ent["tflops"] = round(flops / t / 1e12, 2)
+                ent["mfma_frac"] = round(flops / t / (peak * 1e12), 4)
+                ent["bound"] = "mfma" if t_f >= t_b else "hbm"
+        kern[name] = ent
+    if "dispatch_layout" in per:
+        kern["dispatch"] = {"us": round(sum(per[c] for c in ("dispatch_layout", "permute",
+                                                             "dequantize") if c in per), 2)}
+    return kern
+
+
+def routed_ffn_floor(run, alg, per) -> dict:
+    """The routed expert FFN (up + down launches) against its floor: the larger
+    of streaming the active experts' weights at the HBM peak and the FLOPs at
+    the MFMA peak."""
+    peak = MFMA_PEAK_TFLOPS[run.cfg["dtype"]]
+    t = (per["ffn_up"] + per["ffn_down"]) * 1e-6
+    flops = alg["ffn_up"][0] + alg["ffn_down"][0]
+    t_w = alg["weight_bytes"] / (HBM_PEAK_GBS * 1e9)
+    t_f = flops / (peak * 1e12)
+    return {"us": round(t * 1e6, 1), "weight_bytes": alg["weight_bytes"],
+            "weight_floor_us": round(t_w * 1e6, 1), "mfma_floor_us": round(t_f * 1e6, 1),
+            "frac_of_floor": round(max(t_w, t_f) / t, 4),
+            "weight_stream_gbs": round(alg["weight_bytes"] / t / 1e9, 1)}
+
+
+def load_metrics(run) -> dict:
+    """Load the pages measure: assignments per expert and per simulated rank
+    (the layer ends when its busiest GPU ends), and the drop rate.  The Zipf
+    workload also gets its realised popularity: the share of the hottest
+    experts and the exponent fitted to count versus popularity rank, and the
+    drop rate each capacity factor of its sweep would give on these counts."""
+    import numpy as np
+
+    buf, cfg = run.buf, run.cfg
+    d = buf.desc
+    N, k, E, R = d.num_tokens, d.top_k, d.num_experts, d.num_ranks
+    S = N * k
+    counts = buf.counts.cpu().numpy().astype(np.int64)
+    admitted = buf.admitted.cpu().numpy().astype(np.int64)
+    rank_pre = counts.reshape(R, E // R).sum(1)
+    rank_adm = buf.rank_counts.cpu().numpy().astype(np.int64)
+    out = {
+        "expert_count_max_over_mean": round(float(counts.max()) / (S / E), 3) if S else None,
+        "expert_count_min_max": [int(counts.min()), int(counts.max())],
+        "rank_load_max_over_mean": round(float(rank_pre.max()) / (S / R), 3) if S else None,
+        "rank_admitted_max_over_mean": (round(float(rank_adm.max()) / max(rank_adm.mean(), 1e-9), 3)
+                                        if S else None),
+        "rank_admitted_min_max": [int(rank_adm.min()), int(rank_adm.max())],
+        "drop_rate": round(1.0 - admitted.sum() / S, 5) if S else 0.0,
+    }
+    if cfg.get("zipf"):
+        srt = np.sort(counts)[::-1].astype(np.float64)
+        pos = srt > 0
+        r = np.arange(1, E + 1, dtype=np.float64)
+        slope = np.polyfit(np.log(r[pos]), np.log(srt[pos]), 1)[0]
+        out["zipf"] = {"target_s": cfg["zipf"], "fitted_s": round(float(-slope), 3),
+                       "top1_share": round(srt[0] / S, 4), "top8_share": round(srt[:8].sum() / S, 4)}
+        sweep = {}
+        for cf in cfg.get("cf_sweep", ()):
+            cap = math.ceil(cf * S / E)
+            sweep[str(cf)] = round(1.0 - np.minimum(counts, cap).sum() / S, 5)
+        out["zipf"]["drop_rate_by_cf"] = sweep
+    return out
+
+
+def quick_workload(name, steps, warmup, dev) -> dict:
+    """A short pass over another workload: step time and the per-call
+    durations with their roofline fractions (no cold pass, no oracle)."""
+    import moe_workloads as W
+
+    cfg = W.full(name)
+    run = LayerRun(cfg, dev)
+    for _ in range(warmup):
+        run.step()
+    ms, _, _ = time_steps(run, steps)
+    per, _ = per_call_pass(run, steps)
+    alg = run.algorithmic()
+    kern = kernel_table(run, alg, per)
+    out = {"workload": describe(cfg), "ms_per_step": round(ms, 4),
+           "tokens_per_s": round(cfg["N"] / (ms * 1e-3), 1), "steps": steps, "warmup": warmup,
+           "grouped_gemm": {k: kern[k] for k in ("ffn_up", "ffn_down")},
+           "routed_ffn": routed_ffn_floor(run, alg, per),
+           "route_us": kern["route"]["us"], "combine_hbm_frac": kern["combine"]["hbm_frac"],
+           "permute_hbm_frac": kern.get("permute", kern.get("dispatch", {})).get("hbm_frac")}
+    del run
+    run = None
+    import torch
+    torch.cuda.synchronize()
+    torch.cuda.empty_cache()
+    return out
 
 
 def rank_share(moe, torch, cfg, buf, wts, steps: int) -> dict:
@@ -144,7 +469,8 @@ def rank_share(moe, torch, cfg, buf, wts, steps: int) -> dict:
                        device=dev)
 
     def run():
-        moe.moe_expert_ffn(El, M, dim, h, cfg["act"], cfg["dtype"], recv, goff, w1, w3, w2, y, ws)
+        moe.moe_expert_ffn(El, M, dim, h, cfg["act"], cfg["dtype"], recv, goff, w1, w3, w2, y, None,
+                           ws)
 
     for _ in range(3):
         run()
@@ -177,17 +503,20 @@ def rank_share(moe, torch, cfg, buf, wts, steps: int) -> dict:
 def backward_pass(moe, torch, buf, inp, steps: int) -> dict:
     """The layer's backward on its last layout: the combine's expert terms
     (row and weight gradients), the expert FFN's backward (input and weight
-    gradients, bf16) and the permute's adjoint, timed with events; per call,
-    the algorithmic bytes (data path) or FLOPs (FFN) over the time."""
+    gradients, bf16), the permute's adjoint and the router's backward, timed
+    with events; per call, the algorithmic bytes (data path) or FLOPs (FFN)
+    over the time."""
     d = buf.desc
     N, k, dim = d.num_tokens, d.top_k, d.hidden
     dev = buf.y.device
     dt = buf.y.dtype
     es = buf.y.element_size()
-    M = int(buf.expert_offsets[d.num_experts].item())
+    M = int(buf.admitted.sum().item())
     g = torch.Generator(device=dev).manual_seed(7)
     dy = torch.randn(N, dim, generator=g, device=dev).to(dt)
-    dy_perm = torch.empty_like(buf.y_perm)
+    # Rows of dy_perm that no slot maps to (padding rows of a padded layout)
+    # are never written by moe_combine_backward: start from zeros.
+    dy_perm = torch.zeros_like(buf.y_perm)
     dw = torch.empty(N, k, dtype=torch.float32, device=dev)
     dx = torch.empty(N, dim, dtype=dt, device=dev)
     ev = [torch.cuda.Event(enable_timing=True) for _ in range(3)]
@@ -215,13 +544,13 @@ def backward_pass(moe, torch, buf, inp, steps: int) -> dict:
     S = N * k
     cb_bytes = N * dim * es + 2 * M * dim * es + S * 12  # dy, y_perm rows, dy_perm rows
     pb_bytes = M * dim * es + N * dim * es + S * 4       # dx_perm rows, dx
-    frac = lambda nb, us: round(nb / (us * 1e-6) / (HBM_PEAK_GBS * 1e9), 4)
+    frac = lambda nb, us: round(nb / (us * 1e-6) / (HBM_PEAK_GBS * 1e9), 4)  # noqa: E731
     out = {"combine_backward": {"us": round(cb, 2), "hbm_frac": frac(cb_bytes, cb)},
            "permute_backward": {"us": round(pb, 2), "hbm_frac": frac(pb_bytes, pb)}}
     cfg = buf.cfg
     if cfg["dtype"] != "bf16":
         return out
-    # Expert FFN backward over the admitted rows, plain row-major weights.
+    # Expert FFN backward over the laid-out rows, plain row-major weights.
     E, h, act = d.num_experts, cfg["h"], cfg["act"]
     w1, w3, w2 = inp["w1"], inp.get("w3"), inp["w2"]
     sw = act == "swiglu"
@@ -248,40 +577,28 @@ def backward_pass(moe, torch, buf, inp, steps: int) -> dict:
         torch.cuda.synchronize()
         fb += ev[0].elapsed_time(ev[1])
     fb = fb / steps * 1e3
-    # Products per row: u (and v) and g over d, dx over h (2h), the weight
-    # gradients over the rows: 2 d h FLOPs each.
-    n_mm = 7 if sw else 4
-    flops = 2.0 * M * dim * h * n_mm
+    # Algorithmic products per admitted row, 2 d h FLOPs each: g = dy W2, dx
+    # (one product per gate/up matrix), and one weight gradient per weight
+    # matrix: 6 for SwiGLU (g, dx over W1 and W3, dW1, dW3, dW2), 4 otherwise.
+    # The kernels also recompute u (and v): 8 and 5 products executed.
+    n_alg, n_exec = (6, 8) if sw else (4, 5)
+    flops = 2.0 * M * dim * h * n_alg
     grad_bytes = (3 if sw else 2) * E * h * dim * 4  # fp32 weight gradients written
+    pk = MFMA_PEAK_TFLOPS["bf16"] * 1e12
     out["ffn_backward"] = {
         "us": round(fb, 2), "tflops": round(flops / (fb * 1e-6) / 1e12, 1),
-        "mfma_frac": round(flops / (fb * 1e-6) / (MFMA_PEAK_TFLOPS["bf16"] * 1e12), 4),
+        "mfma_frac": round(flops / (fb * 1e-6) / pk, 4),
+        "executed_tflops": round(2.0 * M * dim * h * n_exec / (fb * 1e-6) / 1e12, 1),
         "weight_grad_bytes": grad_bytes}
     return out
-
-
-def describe(cfg) -> str:
-    s = (f"{cfg['name']} N={cfg['N']} d={cfg['d']} h={cfg['h']} E={cfg['E']} k={cfg['k']} "
-         f"score={cfg['score']} act={cfg['act']} R={cfg['R']}")
-    if cfg.get("cf"):
-        s += f" cf={cfg['cf']}"
-    if cfg.get("G", 1) > 1:
-        s += f" groups={cfg['G']}/keep{cfg['kg']}"
-    if cfg.get("shared"):
-        s += " +shared"
-    if cfg.get("admission", "token") != "token":
-        s += f" admission={cfg['admission']}"
-    if cfg.get("payload", "native") != "native":
-        s += f" payload={cfg['payload']}"
-    if cfg.get("layout", "compact") != "compact":
-        s += f" layout={cfg['layout']}"
-    return s
 
 
 def cpu_baseline(cfg, inp, target_s: float) -> dict:
     """Time the oracle (as it stands) on the first T tokens of the workload,
     taken as a batch of T (capacity recomputed for T): route, dispatch, FFN,
-    combine and bias update.  T is chosen so the run lasts about target_s."""
+    combine and bias update.  T is chosen so the run lasts about target_s.  Each
+    token's FFN work is independent of the others, so tokens/s on the sample
+    is the rate the oracle would sustain over the whole batch (extrapolated)."""
     import numpy as np
 
     import moe_workloads as W
@@ -292,7 +609,7 @@ def cpu_baseline(cfg, inp, target_s: float) -> dict:
     n = W.to_numpy
     wr, rb = n(inp["w_router"]), n(inp["router_bias"])
     sb = n(inp["sel_bias"])
-    bias_state = sb if sb is not None else np.zeros(cfg["E"], np.float32)
+    bias_state = sb.copy() if sb is not None else np.zeros(cfg["E"], np.float32)
     w1, w3, w2 = n(inp["w1"]), n(inp["w3"]), n(inp["w2"])
     shared = None
     if inp.get("shared") is not None:
@@ -317,13 +634,15 @@ def cpu_baseline(cfg, inp, target_s: float) -> dict:
             break
         T = int(min(cfg["N"], max(2 * T, T * target_s / max(elapsed, 1e-6))))
         elapsed = run(T)
+    full = T >= cfg["N"]
+    label = "" if full else " (a sample: tokens/s extrapolated to the whole batch)"
     out = {"value": T / elapsed, "unit": "tokens/s", "cores": threads, "kind": "oracle",
            "sample": f"first {T} of {cfg['N']} tokens as one batch (capacity for {T}); "
-                     f"route+dispatch+FFN+combine+bias update; {elapsed:.1f} s"}
+                     f"route+dispatch+FFN+combine+bias update; {elapsed:.1f} s{label}"}
 
     # The same on one thread, the plain loops as written, on a smaller sample.
     oracle.set_threads(1)
-    T1 = min(cfg["N"], 16)
+    T1 = min(cfg["N"], 8)
     e1 = run(T1)
     for _ in range(4):
         if e1 >= target_s / 4 or T1 >= cfg["N"]:
@@ -332,12 +651,13 @@ def cpu_baseline(cfg, inp, target_s: float) -> dict:
         e1 = run(T1)
     oracle.set_threads(threads)
     out["single_thread"] = {"value": T1 / e1, "unit": "tokens/s", "cores": 1,
-                            "sample": f"first {T1} of {cfg['N']} tokens as one batch; {e1:.1f} s"}
+                            "sample": f"first {T1} of {cfg['N']} tokens as one batch; {e1:.1f} s"
+                                      + ("" if T1 >= cfg["N"] else " (extrapolated)")}
     return out
 
 
-def main():
-    args = parse_args()
+def main(argv=None):
+    args = parse_args(argv)
     if args.gpus != 1:
         print(json.dumps({"error": "this build runs on one GPU only; --gpus must be 1",
                           "n_gpus": args.gpus}))
@@ -346,8 +666,6 @@ def main():
     clocks = {} if args.no_clocks else read_clocks()
     import torch
 
-    import expert_token_routing_router_amd as moe
-    from expert_token_routing_router_amd import layer
     import moe_workloads as W
 
     dev = torch.device("cuda:0")
@@ -360,138 +678,19 @@ def main():
         cfg["payload"] = args.payload
     if args.layout != "compact":
         cfg["layout"] = args.layout
-    # Inputs: the glossary snippet's stream for the toy workload (CPU), else
-    # drawn on the device.
-    gen_dev = "cpu" if args.workload == "toy" else "cuda"
-    inp_src = W.make_inputs(cfg, device=gen_dev)
-    inp = {k: (tuple(None if t is None else t.to(dev) for t in v) if isinstance(v, tuple)
-               else (v.to(dev) if isinstance(v, torch.Tensor) else v))
-           for k, v in inp_src.items()}
-    buf = moe.MoeBuffers(cfg, dev)
-    # bf16 expert weights are packed once, as a model load would, before any
-    # timed work.
-    wts = moe.prepare_weights(cfg, inp)
-    d = buf.desc
-    N, E, k, dim, h = d.num_tokens, d.num_experts, d.top_k, d.hidden, cfg["h"]
-    S = N * k
-    bias_state = (inp["sel_bias"].clone() if inp.get("sel_bias") is not None
-                  else torch.zeros(E, dtype=torch.float32, device=dev))
-    step_bias = cfg.get("bias_step", 1e-3)
-
-    # Calls on the main stream, in order.  A shared expert (needs only x) is
-    # forked onto a side stream at the start of the step and joined before
-    # the combine, as the layer's forward does; it is timed by its own pair
-    # of events on that stream.
-    # Dispatch runs as its two halves (moe_dispatch_layout, then moe_permute or
-    # the INT8 payload's moe_permute_q8 + moe_dequantize_q8): the same kernels
-    # in the same order as one moe_dispatch call, timed apart.
-    q8 = buf.x_perm_q is not None
-    adm = buf.flags
-    padded = cfg.get("layout", "compact") == "padded"
-    R_ffn = buf.rows  # rows the FFN runs over (E*cap with the padded layout)
-    # The padded layout's padding rows are zeroed by the whole-dispatch call,
-    # so that layout runs the dispatch as one call.
-    disp_calls = ["dispatch"] if padded else (["dispatch_layout", "permute"]
-                                              + (["dequantize"] if q8 else []))
-    calls = (["route"] + disp_calls
-             + ["ffn_plan", "ffn_up", "ffn_down", "combine", "bias_update"])
-    fork = layer.has_shared(buf, wts)
-    main = torch.cuda.current_stream()
-
-    def step(events=None, shared_events=None):
-        def mark(i):
-            if events is not None:
-                events[i].record(main)
-        if fork:
-            buf.side_stream.wait_stream(main)
-            if shared_events is not None:
-                shared_events[0].record(buf.side_stream)
-            layer.shared_ffn(buf, wts, buf.side_stream)
-            if shared_events is not None:
-                shared_events[1].record(buf.side_stream)
-        i = 0
-        mark(i)
-        layer.route(buf, inp)
-        i += 1
-        mark(i)
-        if padded:
-            layer.dispatch(buf, inp)
-        else:
-            moe.moe_dispatch_layout(d, adm, buf.topk_idx, buf.row_of_slot, buf.token_of_row,
-                                    buf.slot_of_row, buf.expert_offsets, buf.admitted,
-                                    buf.rank_offsets, buf.rank_counts, buf.ws_dispatch)
-            i += 1
-            mark(i)
-            if q8:
-                moe.moe_permute_q8(d, inp["x"], buf.row_of_slot, buf.x_perm_q, buf.row_scale)
-                i += 1
-                mark(i)
-                moe.moe_dequantize_q8(S, dim, cfg["dtype"], buf.x_perm_q, buf.row_scale,
-                                      buf.expert_offsets[E:], buf.x_perm)
-            else:
-                moe.moe_permute(d, inp["x"], buf.row_of_slot, buf.x_perm)
-        i += 1
-        mark(i)
-        moe.moe_expert_ffn_plan(E, R_ffn, dim, h, cfg["act"], cfg["dtype"], buf.expert_offsets,
-                                buf.ws_ffn)
-        i += 1
-        mark(i)
-        moe.moe_expert_ffn_up(E, R_ffn, dim, h, cfg["act"], cfg["dtype"], buf.x_perm,
-                              buf.expert_offsets, wts["w1"], wts.get("w3"), buf.ws_ffn)
-        i += 1
-        mark(i)
-        moe.moe_expert_ffn_down(E, R_ffn, dim, h, cfg["act"], cfg["dtype"], buf.expert_offsets,
-                                wts["w2"], buf.y_perm, buf.ws_ffn)
-        i += 1
-        mark(i)
-        if fork:
-            main.wait_stream(buf.side_stream)
-        layer.combine(buf, inp, residual=True)
-        i += 1
-        mark(i)
-        layer.bias_update(buf, bias_state, step_bias)
-        mark(i + 1)
+    if args.combine != "unfused":
+        cfg["combine"] = args.combine
+    run = LayerRun(cfg, dev)
+    N = cfg["N"]
 
     for _ in range(args.warmup):
-        step()
+        run.step()
     torch.cuda.synchronize()
-
-    # Timed region: exactly K steps, nothing else on the stream, bracketed by
-    # synchronisation (one GPU, so no barrier is needed beyond that).
-    edge = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    edge[0].record()
-    for _ in range(args.steps):
-        step()
-    edge[1].record()
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-    gpu_ms = edge[0].elapsed_time(edge[1])
-    ms_per_step = max(gpu_ms, wall * 1e3) / args.steps
+    # Timed region: exactly K steps.
+    ms_per_step, gpu_ms, wall = time_steps(run, args.steps)
     value = N / (ms_per_step * 1e-3)
 
-    # Per-call pass: the same K steps again with a HIP event at every call
-    # boundary (on torch's current stream, which every call is launched on).
-    # Each event drains the queue for a few microseconds, so this pass gives
-    # the per-kernel durations and the roofline, not the step time.
-    nev = len(calls) + 1
-    events = [[torch.cuda.Event(enable_timing=True) for _ in range(nev)] for _ in range(args.steps)]
-    sh_events = [[torch.cuda.Event(enable_timing=True) for _ in range(2)]
-                 for _ in range(args.steps)]
-    torch.cuda.synchronize()
-    for s in range(args.steps):
-        step(events[s], sh_events[s])
-    torch.cuda.synchronize()
-    per_call = {c: 0.0 for c in calls}
-    for ev in events:
-        for i, c in enumerate(calls):
-            per_call[c] += ev[i].elapsed_time(ev[i + 1])
-    per_call = {c: v / args.steps * 1e3 for c, v in per_call.items()}  # microseconds
-    if fork:
-        per_call["shared_ffn"] = sum(a.elapsed_time(b) for a, b in sh_events) / args.steps * 1e3
-    instrumented_ms = sum(events[s][0].elapsed_time(events[s][-1])
-                          for s in range(args.steps)) / args.steps
+    per_call, instrumented_ms = per_call_pass(run, args.steps)
 
     # Step-time distribution: the same K steps with one event per step
     # boundary only.
@@ -499,7 +698,7 @@ def main():
     torch.cuda.synchronize()
     marks[0].record()
     for s in range(args.steps):
-        step()
+        run.step()
         marks[s + 1].record()
     torch.cuda.synchronize()
     step_ms = sorted(marks[s].elapsed_time(marks[s + 1]) for s in range(args.steps))
@@ -510,17 +709,18 @@ def main():
     # Cold pass: before each step a 512 MiB write evicts the 256 MB Infinity
     # Cache and every XCD's L2, then the step runs with per-call events.
     n_cold = min(args.steps, 20)
+    nev = run.n_events()
     flush = torch.empty(512 << 18, dtype=torch.float32, device=dev)
     cold_ev = [[torch.cuda.Event(enable_timing=True) for _ in range(nev)] for _ in range(n_cold)]
     cold_sh = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(n_cold)]
     torch.cuda.synchronize()
     for s in range(n_cold):
         flush.fill_(float(s))
-        step(cold_ev[s], cold_sh[s])
+        run.step(cold_ev[s], cold_sh[s])
     torch.cuda.synchronize()
     cold_call = {c: sum(ev[i].elapsed_time(ev[i + 1]) for ev in cold_ev) / n_cold * 1e3
-                 for i, c in enumerate(calls)}
-    if fork:
+                 for i, c in enumerate(run.calls)}
+    if run.fork:
         cold_call["shared_ffn"] = sum(a.elapsed_time(b) for a, b in cold_sh) / n_cold * 1e3
     cold_step_ms = sum(ev[0].elapsed_time(ev[-1]) for ev in cold_ev) / n_cold
     del flush
@@ -534,77 +734,19 @@ def main():
         torch.cuda.synchronize()
         torch.add(a, 0.0, out=b)
         torch.cuda.synchronize()
+        del a, b
 
-    # Algorithmic work of this batch (rows actually admitted).
-    M = int(buf.expert_offsets[E].item())  # rows laid out (E*cap when padded)
-    admitted_rows = int(buf.admitted.sum().item())
-    counts = buf.admitted.cpu()
-    active = int((counts > 0).sum().item())
-    es = 2 if cfg["dtype"] == "bf16" else 4
-    mats_up = 2 if cfg["act"] == "swiglu" else 1
-    up_flops = 2.0 * M * dim * h * mats_up
-    up_bytes = (active * mats_up * h * dim + M * dim + M * h) * es
-    down_flops = 2.0 * M * h * dim
-    down_bytes = (active * dim * h + M * h + M * dim) * es
-    # dispatch layout: ids read, row_of_slot + token_of_row + slot_of_row written
-    layout_bytes = S * 4 + S * 4 + S * 4 + S
-    # permute: x read once, every admitted row written (INT8 payload: d bytes + a
-    # 4-byte scale per row), row_of_slot read; dequantisation reads the payload
-    # back and writes dtype rows
-    permute_bytes = (N * dim * es + (admitted_rows * (dim + 4) if q8 else admitted_rows * dim * es)
-                     + S * 4)
-    dequant_bytes = M * (dim + 4) + M * dim * es
-    combine_bytes = M * dim * es + N * dim * es + N * dim * es + S * 8
-    route_bytes = N * dim * es + E * dim * es + N * E * 4 + S * 8
-    peak = MFMA_PEAK_TFLOPS[cfg["dtype"]]
-
-    def roof(name, flops, nbytes, table=per_call):
-        t = table[name] * 1e-6
-        t_f, t_b = flops / (peak * 1e12), nbytes / (HBM_PEAK_GBS * 1e9)
-        return {"us": round(table[name], 2), "tflops": round(flops / t / 1e12, 2),
-                "gbs": round(nbytes / t / 1e9, 1), "mfma_frac": round(flops / t / (peak * 1e12), 4),
-                "hbm_frac": round(nbytes / t / (HBM_PEAK_GBS * 1e9), 4),
-                "bound": "mfma" if t_f >= t_b else "hbm"}
-
-    kern = {
-        "ffn_up": roof("ffn_up", up_flops, up_bytes),
-        "ffn_down": roof("ffn_down", down_flops, down_bytes),
-    }
-    if padded:  # one whole-dispatch call; the padding rows are written as zeros
-        hbm_calls = [("route", route_bytes),
-                     ("dispatch", layout_bytes + permute_bytes
-                      + (M - admitted_rows) * (dim + 4 if q8 else dim * es)
-                      + (dequant_bytes if q8 else 0)),
-                     ("combine", combine_bytes)]
-    else:
-        hbm_calls = [("route", route_bytes), ("dispatch_layout", layout_bytes),
-                     ("permute", permute_bytes), ("combine", combine_bytes)]
-        if q8:
-            hbm_calls.append(("dequantize", dequant_bytes))
-    for name, nbytes in hbm_calls:
-        t = per_call[name] * 1e-6
-        kern[name] = {"us": round(per_call[name], 2), "gbs": round(nbytes / t / 1e9, 1),
-                      "hbm_frac": round(nbytes / t / (HBM_PEAK_GBS * 1e9), 4)}
-    if not padded:
-        kern["dispatch"] = {"us": round(sum(per_call[c] for c in
-                                            ("dispatch_layout", "permute", "dequantize")
-                                            if c in per_call), 2)}
-    for name in per_call:
-        kern.setdefault(name, {"us": round(per_call[name], 2)})
-    cold = {"ms_per_step_with_per_call_events": round(cold_step_ms, 4), "steps": n_cold,
-            "ffn_up": roof("ffn_up", up_flops, up_bytes, cold_call),
-            "ffn_down": roof("ffn_down", down_flops, down_bytes, cold_call)}
-    for name, nbytes in hbm_calls:
-        cold[name] = {"us": round(cold_call[name], 2),
-                      "hbm_frac": round(nbytes / (cold_call[name] * 1e-6) / (HBM_PEAK_GBS * 1e9), 4)}
-    for name in cold_call:
-        cold.setdefault(name, {"us": round(cold_call[name], 2)})
+    alg = run.algorithmic()
+    kern = kernel_table(run, alg, per_call)
+    cold = {"ms_per_step_with_per_call_events": round(cold_step_ms, 4), "steps": n_cold}
+    cold.update(kernel_table(run, alg, cold_call))
 
     dom = "ffn_up" if per_call["ffn_up"] >= per_call["ffn_down"] else "ffn_down"
     dk = kern[dom]
     kernel_name = {"ffn_up": "grouped_gemm_up", "ffn_down": "grouped_gemm_down"}[dom]
     digest = kernel_sources_digest()
     traffic = read_traffic(kernel_name, args.workload, digest)
+    peak = MFMA_PEAK_TFLOPS[cfg["dtype"]]
     if dk["bound"] == "mfma":
         roofline = {"bound": "mfma", "achieved": dk["tflops"], "peak": peak, "unit": "TFLOP/s",
                     "frac": dk["mfma_frac"], "traffic": traffic}
@@ -612,6 +754,10 @@ def main():
         roofline = {"bound": "hbm", "achieved": dk["gbs"], "peak": HBM_PEAK_GBS, "unit": "GB/s",
                     "frac": dk["hbm_frac"], "traffic": traffic}
     roofline["kernel"] = f"{kernel_name} ({dom})"
+    roofline["us_per_launch"] = dk["us"]
+    roofline["algorithmic"] = ("active experts' weights + x_perm rows read"
+                               + (" + y_perm rows written" if dom == "ffn_down" else "")
+                               + "; H excluded")
     roofline["mfma_frac"] = dk["mfma_frac"]
 
     out = {
@@ -628,12 +774,15 @@ def main():
         "dtype": cfg["dtype"],
         "data": "synthetic",
         "config": {"workload": describe(cfg), "global_batch": N,
-                   "rows_admitted": admitted_rows, "dropped_slots": S - admitted_rows,
-                   "rows_laid_out": M, "active_experts": active},
+                   "rows_admitted": alg["M"], "dropped_slots": N * cfg["k"] - alg["M"],
+                   "rows_laid_out": alg["laid"], "active_experts": alg["active"]},
         "roofline": roofline,
+        "routed_ffn": routed_ffn_floor(run, alg, per_call),
         "grouped_gemm_mfma_frac": {"up": kern["ffn_up"]["mfma_frac"],
                                    "down": kern["ffn_down"]["mfma_frac"]},
-        "permute_hbm_frac": kern["permute" if "permute" in kern else "dispatch"]["hbm_frac"],
+        # the permute call with its events; the kernel alone is in profiles/
+        "permute_hbm_frac": kern.get("permute", kern.get("dispatch", {})).get("hbm_frac"),
+        "load": load_metrics(run),
         "kernels": kern,
         "ms_per_step_with_per_call_events": round(instrumented_ms, 4),
         "step_ms_p10_p50_p90": [round(pct(step_ms, q), 4) for q in (0.1, 0.5, 0.9)],
@@ -644,18 +793,33 @@ def main():
         "kernel_sources_digest": digest,
     }
     if args.rank_share:
-        out["rank_share"] = rank_share(moe, torch, cfg, buf, wts, max(5, min(args.steps, 30)))
+        out["rank_share"] = rank_share(run.moe, torch, cfg, run.buf, run.wts,
+                                       max(5, min(args.steps, 30)))
     if args.backward:
-        out["backward"] = backward_pass(moe, torch, buf, inp, max(5, min(args.steps, 30)))
+        out["backward"] = backward_pass(run.moe, torch, run.buf, run.inp,
+                                        max(5, min(args.steps, 30)))
+    host = None
     if not args.no_cpu_baseline:
         host = {}
-        for key, v in inp.items():
+        for key, v in run.inp.items():
             if isinstance(v, tuple):
                 host[key] = tuple(None if t is None else t.cpu() for t in v)
             elif isinstance(v, torch.Tensor):
                 host[key] = v.cpu()
             else:
                 host[key] = v
+    # Free the headline workload's device memory before the other workloads.
+    del run
+    torch.cuda.synchronize()
+    torch.cuda.empty_cache()
+    extras = [w for w in args.extra_workloads.split(",") if w and w != "none"]
+    if extras:
+        out["other_workloads"] = {}
+        for w in extras:
+            if w == args.workload or w not in WORKLOADS:
+                continue
+            out["other_workloads"][w] = quick_workload(w, args.extra_steps, 10, dev)
+    if host is not None:
         cb = cpu_baseline(cfg, host, args.cpu_seconds)
         cb["gpu_speedup"] = round(value / cb["value"], 1)
         cb["single_thread"]["gpu_speedup"] = round(value / cb["single_thread"]["value"], 1)

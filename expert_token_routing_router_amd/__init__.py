@@ -71,6 +71,32 @@ class RouteDesc(ctypes.Structure):
     ]
 
 
+class FusedCombine(ctypes.Structure):
+    """Mirror of ``moe_fused_combine`` (the down GEMM's scatter-add combine)."""
+
+    _fields_ = [
+        ("num_tokens", ctypes.c_int32),
+        ("top_k", ctypes.c_int32),
+        ("topk_w", ctypes.c_void_p),
+        ("token_of_row", ctypes.c_void_p),
+        ("slot_of_row", ctypes.c_void_p),
+        ("y_acc", ctypes.c_void_p),
+    ]
+
+
+def fused_combine(num_tokens, top_k, topk_w, token_of_row, slot_of_row, y_acc) -> FusedCombine:
+    """The fused combine argument of ``moe_expert_ffn`` / ``moe_expert_ffn_down``:
+    topk_w [N, k] fp32, token_of_row / slot_of_row of the dispatch (int32 /
+    int8, one per row), y_acc [N, d] fp32 (zeroed by the FFN call)."""
+    N, k = int(num_tokens), int(top_k)
+    f = FusedCombine(N, k)
+    f.topk_w = _ptr(topk_w, "topk_w", torch.float32, N * k, N > 0)
+    f.token_of_row = _ptr(token_of_row, "token_of_row", torch.int32, None, True)
+    f.slot_of_row = _ptr(slot_of_row, "slot_of_row", torch.int8, None, True)
+    f.y_acc = _ptr(y_acc, "y_acc", torch.float32, None, N > 0)
+    return f
+
+
 def route_desc(N, d, E, k, R=1, cf=0.0, G=1, kg=1, score="softmax_topk", dtype="bf16"):
     return RouteDesc(int(N), int(d), int(E), int(k), int(R), float(cf or 0.0), int(G), int(kg),
                      SCORE[score] if isinstance(score, str) else int(score),
@@ -96,6 +122,7 @@ def lib() -> ctypes.CDLL:
         L = ctypes.CDLL(LIB_PATH)
         P, I32, SZ, F32 = ctypes.c_void_p, ctypes.c_int32, ctypes.c_size_t, ctypes.c_float
         D = ctypes.POINTER(RouteDesc)
+        FC = ctypes.POINTER(FusedCombine)
         sigs = {
             "moe_route_workspace_size": ([D], SZ),
             "moe_route": ([D, P, P, P, P, P, P, P, P, P, SZ, P], I32),
@@ -115,12 +142,13 @@ def lib() -> ctypes.CDLL:
             "moe_expert_ffn_backward": ([I32, I32, I32, I32, I32, I32, P, P, P, P, P, P, P, P, P,
                                          P, P, SZ, P], I32),
             "moe_expert_ffn_workspace_size": ([I32, I32, I32, I32, I32, I32], SZ),
-            "moe_expert_ffn": ([I32, I32, I32, I32, I32, I32, P, P, P, P, P, P, P, SZ, P], I32),
+            "moe_expert_ffn": ([I32, I32, I32, I32, I32, I32, P, P, P, P, P, P, FC, P, SZ, P],
+                               I32),
             "moe_expert_ffn_plan": ([I32, I32, I32, I32, I32, I32, P, P, SZ, P], I32),
             "moe_expert_ffn_up": ([I32, I32, I32, I32, I32, I32, P, P, P, P, P, SZ, P], I32),
-            "moe_expert_ffn_down": ([I32, I32, I32, I32, I32, I32, P, P, P, P, SZ, P], I32),
+            "moe_expert_ffn_down": ([I32, I32, I32, I32, I32, I32, P, P, P, FC, P, SZ, P], I32),
             "moe_expert_ffn_pack_weights": ([I32, I32, I32, I32, P, P, P], I32),
-            "moe_combine": ([D, P, P, P, P, P, P, P], I32),
+            "moe_combine": ([D, P, P, P, P, P, P, P, P], I32),
             "moe_bias_update": ([I32, I32, I32, P, F32, P, P], I32),
             "moe_status_string": ([I32], ctypes.c_char_p),
         }
@@ -359,8 +387,13 @@ def _dispatch(name, desc, admission, x, topk_idx, x_perm, row_of_slot, token_of_
     _raise(name, st)
 
 
+def _fused_ref(fused):
+    return None if fused is None else ctypes.byref(fused)
+
+
 def moe_expert_ffn(num_experts, max_rows, hidden, ffn_hidden, act, dtype, x_rows,
-                   group_offsets, w1, w3, w2, y_rows, ws, stream=None):
+                   group_offsets, w1, w3, w2, y_rows, fused, ws, stream=None):
+    """fused: None, or ``fused_combine(...)`` (then y_rows may be None)."""
     act = ACT[act] if isinstance(act, str) else int(act)
     dtype = DTYPE[dtype] if isinstance(dtype, str) else int(dtype)
     dt = TORCH_DTYPE.get(dtype)
@@ -369,7 +402,8 @@ def moe_expert_ffn(num_experts, max_rows, hidden, ffn_hidden, act, dtype, x_rows
         E, M, d, h, act, dtype, _ptr(x_rows, "x_rows", dt, M * d, M > 0),
         _ptr(group_offsets, "group_offsets", torch.int32, E + 1),
         _ptr(w1, "w1", dt, E * h * d), _ptr(w3, "w3", dt, E * h * d, act == MOE_SWIGLU),
-        _ptr(w2, "w2", dt, E * d * h), _ptr(y_rows, "y_rows", dt, M * d, M > 0),
+        _ptr(w2, "w2", dt, E * d * h),
+        _ptr(y_rows, "y_rows", dt, M * d, M > 0 and fused is None), _fused_ref(fused),
         _ptr(ws, "ws", None, None, False), 0 if ws is None else ws.numel() * ws.element_size(),
         _stream(stream))
     _raise("moe_expert_ffn", st)
@@ -417,27 +451,33 @@ def moe_expert_ffn_up(num_experts, max_rows, hidden, ffn_hidden, act, dtype, x_r
 
 
 def moe_expert_ffn_down(num_experts, max_rows, hidden, ffn_hidden, act, dtype, group_offsets,
-                        w2, y_rows, ws, stream=None):
+                        w2, y_rows, fused, ws, stream=None):
+    """fused: None, or ``fused_combine(...)`` (then y_rows may be None)."""
     act = ACT[act] if isinstance(act, str) else int(act)
     dtype = DTYPE[dtype] if isinstance(dtype, str) else int(dtype)
     dt = TORCH_DTYPE.get(dtype)
     E, M, d, h = num_experts, max_rows, hidden, ffn_hidden
     st = lib().moe_expert_ffn_down(
         E, M, d, h, act, dtype, _ptr(group_offsets, "group_offsets", torch.int32, E + 1),
-        _ptr(w2, "w2", dt, E * d * h), _ptr(y_rows, "y_rows", dt, M * d, M > 0),
+        _ptr(w2, "w2", dt, E * d * h),
+        _ptr(y_rows, "y_rows", dt, M * d, M > 0 and fused is None), _fused_ref(fused),
         *_ws(ws), _stream(stream))
     _raise("moe_expert_ffn_down", st)
 
 
-def moe_combine(desc, y_perm, row_of_slot, topk_w, residual, shared_out, y, stream=None):
+def moe_combine(desc, y_perm, row_of_slot, topk_w, residual, shared_out, y_acc, y, stream=None):
+    """y_acc: None, or the fp32 accumulator a fused down GEMM filled (then
+    y_perm, row_of_slot and topk_w are not read and may be None)."""
     N, d, k = desc.num_tokens, desc.hidden, desc.top_k
     dt = TORCH_DTYPE.get(desc.dtype)
+    unfused = N > 0 and y_acc is None
     st = lib().moe_combine(
-        ctypes.byref(desc), _ptr(y_perm, "y_perm", dt, None, N > 0),
-        _ptr(row_of_slot, "row_of_slot", torch.int32, N * k, N > 0),
-        _ptr(topk_w, "topk_w", torch.float32, N * k, N > 0),
+        ctypes.byref(desc), _ptr(y_perm, "y_perm", dt, None, unfused),
+        _ptr(row_of_slot, "row_of_slot", torch.int32, N * k, unfused),
+        _ptr(topk_w, "topk_w", torch.float32, N * k, unfused),
         _ptr(residual, "residual", dt, N * d, False),
         _ptr(shared_out, "shared_out", dt, N * d, False),
+        _ptr(y_acc, "y_acc", torch.float32, N * d, False),
         _ptr(y, "y", dt, N * d, N > 0), _stream(stream))
     _raise("moe_combine", st)
 

@@ -270,22 +270,35 @@ size_t moe_expert_ffn_workspace_size(int32_t num_experts, int32_t max_rows, int3
   return moe::ffn_workspace_bytes(num_experts, max_rows, hidden, ffn_hidden, act, dtype);
 }
 
+// The fused combine argument of the down GEMM: sizes in range, every array
+// present once there are rows and tokens, the accumulator 16-byte aligned.
+static int check_fused(const moe_fused_combine* f, int32_t max_rows) {
+  if (f->num_tokens < 0 || f->top_k < 1 || f->top_k > kMaxTopK) return MOE_ERR_INVALID_ARG;
+  if (max_rows > 0 && (!f->token_of_row || !f->slot_of_row)) return MOE_ERR_INVALID_ARG;
+  if (f->num_tokens > 0 && (!f->topk_w || !f->y_acc || !aligned16(f->y_acc)))
+    return MOE_ERR_INVALID_ARG;
+  return MOE_OK;
+}
+
 // Validation shared by moe_expert_ffn and its stages.  stage: 0 = all,
 // 1 = plan, 2 = up, 3 = down.
 static int check_ffn_call(int stage, int32_t E, int32_t max_rows, int32_t d, int32_t h,
                           int32_t act, int32_t dtype, const void* x_rows,
                           const int32_t* offsets, const void* w1, const void* w3,
-                          const void* w2, const void* y_rows, const void* ws, size_t ws_bytes) {
+                          const void* w2, const void* y_rows, const void* ws, size_t ws_bytes,
+                          const moe_fused_combine* fused = nullptr) {
   int st = check_ffn(E, max_rows, d, h, act, dtype);
   if (st != MOE_OK) return st;
   if (!offsets) return MOE_ERR_INVALID_ARG;
   const bool up = stage == 0 || stage == 2, down = stage == 0 || stage == 3;
   if (up && (!w1 || (act == MOE_SWIGLU) != (w3 != nullptr))) return MOE_ERR_INVALID_ARG;
   if (down && !w2) return MOE_ERR_INVALID_ARG;
+  if (down && fused && (st = check_fused(fused, max_rows)) != MOE_OK) return st;
   if (max_rows == 0) return MOE_OK;
   if (up && (!x_rows || !aligned16(x_rows) || !aligned16(w1) || (w3 && !aligned16(w3))))
     return MOE_ERR_INVALID_ARG;
-  if (down && (!y_rows || !aligned16(y_rows) || !aligned16(w2))) return MOE_ERR_INVALID_ARG;
+  if (down && (!aligned16(w2) || (!fused && (!y_rows || !aligned16(y_rows)))))
+    return MOE_ERR_INVALID_ARG;
   const size_t need = moe::ffn_workspace_bytes(E, max_rows, d, h, act, dtype);
   if (!ws || ws_bytes < need || (reinterpret_cast<uintptr_t>(ws) & 255u)) return MOE_ERR_WORKSPACE;
   return MOE_OK;
@@ -294,13 +307,23 @@ static int check_ffn_call(int stage, int32_t E, int32_t max_rows, int32_t d, int
 int moe_expert_ffn(int32_t num_experts, int32_t max_rows, int32_t hidden, int32_t ffn_hidden,
                    int32_t act, int32_t dtype, const void* x_rows,
                    const int32_t* group_offsets, const void* w1, const void* w3,
-                   const void* w2, void* y_rows, void* ws, size_t ws_bytes, void* stream) {
+                   const void* w2, void* y_rows, const moe_fused_combine* fused, void* ws,
+                   size_t ws_bytes, void* stream) {
   int st = check_ffn_call(0, num_experts, max_rows, hidden, ffn_hidden, act, dtype, x_rows,
-                          group_offsets, w1, w3, w2, y_rows, ws, ws_bytes);
-  if (st != MOE_OK || max_rows == 0) return st;
-  moe::FfnArgs a{num_experts, max_rows, hidden, ffn_hidden, act, dtype, x_rows,
-                 group_offsets, w1, w3, w2, y_rows, ws};
+                          group_offsets, w1, w3, w2, y_rows, ws, ws_bytes, fused);
+  if (st != MOE_OK) return st;
   hipStream_t s = static_cast<hipStream_t>(stream);
+  moe::FusedCombineArgs fc{};
+  if (fused) fc = {fused->num_tokens, fused->top_k, fused->topk_w, fused->token_of_row,
+                   fused->slot_of_row, fused->y_acc};
+  if (max_rows == 0) {  // nothing to multiply; a fused call still leaves y_acc zeroed
+    if (!fused || fused->num_tokens == 0) return MOE_OK;
+    moe::FfnArgs z{num_experts, 0, hidden, ffn_hidden, act, dtype, nullptr, group_offsets,
+                   nullptr, nullptr, w2, nullptr, nullptr, &fc};
+    return status_of(moe::launch_ffn_zero_acc(z, s));
+  }
+  moe::FfnArgs a{num_experts, max_rows, hidden, ffn_hidden, act, dtype, x_rows,
+                 group_offsets, w1, w3, w2, y_rows, ws, fused ? &fc : nullptr};
   hipError_t e = moe::launch_ffn_plan(a, s);
   if (e == hipSuccess) e = moe::launch_ffn_up(a, s);
   if (e == hipSuccess) e = moe::launch_ffn_down(a, s);
@@ -380,13 +403,22 @@ int moe_expert_ffn_up(int32_t num_experts, int32_t max_rows, int32_t hidden, int
 int moe_expert_ffn_down(int32_t num_experts, int32_t max_rows, int32_t hidden,
                         int32_t ffn_hidden, int32_t act, int32_t dtype,
                         const int32_t* group_offsets, const void* w2, void* y_rows,
-                        void* ws, size_t ws_bytes, void* stream) {
+                        const moe_fused_combine* fused, void* ws, size_t ws_bytes,
+                        void* stream) {
   int st = check_ffn_call(3, num_experts, max_rows, hidden, ffn_hidden, act, dtype, nullptr,
-                          group_offsets, nullptr, nullptr, w2, y_rows, ws, ws_bytes);
-  if (st != MOE_OK || max_rows == 0) return st;
+                          group_offsets, nullptr, nullptr, w2, y_rows, ws, ws_bytes, fused);
+  if (st != MOE_OK) return st;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  moe::FusedCombineArgs fc{};
+  if (fused) fc = {fused->num_tokens, fused->top_k, fused->topk_w, fused->token_of_row,
+                   fused->slot_of_row, fused->y_acc};
   moe::FfnArgs a{num_experts, max_rows, hidden, ffn_hidden, act, dtype, nullptr,
-                 group_offsets, nullptr, nullptr, w2, y_rows, ws};
-  return status_of(moe::launch_ffn_down(a, static_cast<hipStream_t>(stream)));
+                 group_offsets, nullptr, nullptr, w2, y_rows, ws, fused ? &fc : nullptr};
+  if (max_rows == 0) {
+    if (!fused || fused->num_tokens == 0) return MOE_OK;
+    return status_of(moe::launch_ffn_zero_acc(a, s));
+  }
+  return status_of(moe::launch_ffn_down(a, s));
 }
 
 int moe_expert_ffn_pack_weights(int32_t num_experts, int32_t rows, int32_t cols, int32_t dtype,
@@ -404,18 +436,23 @@ int moe_expert_ffn_pack_weights(int32_t num_experts, int32_t rows, int32_t cols,
 }
 
 int moe_combine(const moe_route_desc* desc, const void* y_perm, const int32_t* row_of_slot,
-                const float* topk_w, const void* residual, const void* shared_out, void* y,
-                void* stream) {
+                const float* topk_w, const void* residual, const void* shared_out,
+                const float* y_acc, void* y, void* stream) {
   int st = check_desc(desc);
   if (st != MOE_OK) return st;
   const int N = desc->num_tokens;
   if (N == 0) return MOE_OK;
-  if (!y_perm || !row_of_slot || !topk_w || !y) return MOE_ERR_INVALID_ARG;
-  if (!aligned16(y_perm) || !aligned16(y) || (residual && !aligned16(residual)) ||
+  if (!y) return MOE_ERR_INVALID_ARG;
+  if (y_acc) {
+    if (!aligned16(y_acc)) return MOE_ERR_INVALID_ARG;
+  } else {
+    if (!y_perm || !row_of_slot || !topk_w || !aligned16(y_perm)) return MOE_ERR_INVALID_ARG;
+  }
+  if (!aligned16(y) || (residual && !aligned16(residual)) ||
       (shared_out && !aligned16(shared_out)))
     return MOE_ERR_INVALID_ARG;
   moe::CombineArgs a{N, desc->hidden, desc->top_k, desc->dtype, y_perm, row_of_slot, topk_w,
-                     residual, shared_out, y};
+                     residual, shared_out, y, y_acc};
   return status_of(moe::launch_combine(a, static_cast<hipStream_t>(stream)));
 }
 

@@ -123,8 +123,69 @@ __global__ __launch_bounds__(256) void combine_rows(const u32x4* __restrict__ y_
   }
 }
 
+// Finish of the fused combine: the down GEMM has added sum_j w_j * row_j into
+// the fp32 accumulator y_acc; y = residual + shared + y_acc in fp32 in that
+// order, rounded once.  One thread per 16 bytes of y (4 fp32 / 8 bf16
+// elements), grid-stride.
+template <int DTYPE>
+__global__ __launch_bounds__(256) void combine_finish(const float* __restrict__ y_acc,
+                                                      const u32x4* __restrict__ residual,
+                                                      const u32x4* __restrict__ shared_out,
+                                                      u32x4* __restrict__ y, size_t nvec) {
+  constexpr int VE = DTYPE == 0 ? 4 : 8;
+  const size_t stride = (size_t)gridDim.x * blockDim.x;
+  for (size_t v = (size_t)blockIdx.x * blockDim.x + threadIdx.x; v < nvec; v += stride) {
+    float acc[VE];
+#pragma unroll
+    for (int i = 0; i < VE; ++i) acc[i] = 0.f;
+    auto add = [&](const u32x4 q) {
+      const uint32_t w4[4] = {q.x, q.y, q.z, q.w};
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        if constexpr (DTYPE == 0) {
+          acc[i] += __uint_as_float(w4[i]);
+        } else {
+          acc[2 * i] += bf16_to_f32(w4[i] & 0xffffu);
+          acc[2 * i + 1] += bf16_to_f32(w4[i] >> 16);
+        }
+      }
+    };
+    if (residual) add(residual[v]);
+    if (shared_out) add(shared_out[v]);
+    const u32x4* yv = reinterpret_cast<const u32x4*>(y_acc) + v * (VE / 4);
+#pragma unroll
+    for (int c = 0; c < VE / 4; ++c) {
+      const u32x4 q = yv[c];
+      acc[4 * c] += __uint_as_float(q.x);
+      acc[4 * c + 1] += __uint_as_float(q.y);
+      acc[4 * c + 2] += __uint_as_float(q.z);
+      acc[4 * c + 3] += __uint_as_float(q.w);
+    }
+    u32x4 out;
+    if constexpr (DTYPE == 0) {
+      out = u32x4{__float_as_uint(acc[0]), __float_as_uint(acc[1]), __float_as_uint(acc[2]),
+                  __float_as_uint(acc[3])};
+    } else {
+      out = u32x4{pack_bf16x2(acc[0], acc[1]), pack_bf16x2(acc[2], acc[3]),
+                  pack_bf16x2(acc[4], acc[5]), pack_bf16x2(acc[6], acc[7])};
+    }
+    y[v] = out;
+  }
+}
+
 hipError_t launch_combine(const CombineArgs& a, hipStream_t st) {
   if (a.N == 0) return hipSuccess;
+  if (a.y_acc) {
+    const int elem = a.dtype == 0 ? 4 : 2;
+    const size_t nvec = (size_t)a.N * a.d * elem / 16;
+    const int blocks = (int)std::min<size_t>((nvec + 255) / 256, 8192);
+    auto res = static_cast<const u32x4*>(a.residual);
+    auto sh = static_cast<const u32x4*>(a.shared_out);
+    auto y = static_cast<u32x4*>(a.y);
+    if (a.dtype == 0) combine_finish<0><<<blocks, 256, 0, st>>>(a.y_acc, res, sh, y, nvec);
+    else combine_finish<1><<<blocks, 256, 0, st>>>(a.y_acc, res, sh, y, nvec);
+    return hipGetLastError();
+  }
   const int elem = a.dtype == 0 ? 4 : 2;
   const int vec_per_row = a.d * elem / 16;
   const int blocks = std::max(1, std::min((a.N + 3) / 4, 8192));

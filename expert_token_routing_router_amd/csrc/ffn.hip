@@ -190,7 +190,7 @@ __host__ __device__ __forceinline__ int packed_slab_rows(int N) { return N % 256
 // The epilogue converts to bf16 in registers (v_cvt_pk_bf16_f32), swaps
 // half-rows between lanes l and l+32 (v_permlane32_swap) so each lane owns 8
 // consecutive columns, and stores 16 bytes per lane straight to global memory.
-constexpr int kGemmBM = 320, kGemmBMSmall = 128, kGemmWaves = 8;
+constexpr int kGemmBM = 320, kGemmBMMid = 192, kGemmBMSmall = 128, kGemmWaves = 8;
 // Cache-policy bits of the weight loads (nt | sc1 on gfx950): each weight
 // byte is read once per launch, so it is fetched as streaming data.  Measured
 // with the operand stream alone (no MFMA): 0.98 against 1.04 us per K stage.
@@ -202,18 +202,23 @@ constexpr int kWeightCpol = 2 | 16;
 // 16-row group g (tiles[q].w numbers a tile's groups), one 1-KB block at
 // element offset (t * ldg + g) * 512, laid out as the A stage rows sit in LDS
 // (16-byte position L: row L/4 of the group, logical chunk (L % 4) ^ swz4(L/4)),
-// so a down tile's K stage is one contiguous run.
-enum { kUpGemm = 0, kDownGemm = 1 };
+// so a down tile's K stage is one contiguous run.  MODE kDownFused: the down
+// GEMM with the combine folded in: no C; each output row, rounded to bf16, is
+// scaled by its routing weight and added into the token's fp32 accumulator
+// row with hardware float atomics.  For that epilogue the MFMA operands are
+// swapped (A fragment first), so a lane holds one output column of 16 rows and
+// the 32 lanes of a half-wave cover 32 consecutive columns of one row: each
+// atomic instruction touches two 128-byte runs instead of 64 scattered words.
+enum { kUpGemm = 0, kDownGemm = 1, kDownFused = 2 };
 
 template <int BM, int BN, int ACT, int MODE>
 __global__ __launch_bounds__(kGemmWaves * 64, 1) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void grouped_gemm_bf16(
     const bf16_t* __restrict__ A, const bf16_t* __restrict__ B, const bf16_t* __restrict__ B2,
     bf16_t* __restrict__ C, int K, int N, const int4* __restrict__ tiles,
-    const int32_t* __restrict__ tile_count, int n_tiles, int ldg, int gm) {
+    const int32_t* __restrict__ tile_count, int n_tiles, int ldg, int gm, FusedCombineArgs fc) {
   constexpr bool DUAL = ACT == ACT_SWIGLU;
   constexpr int BK = 32, RB = BK * 2;  // RB: bytes per staged row
-  constexpr int CH = BK / 8;                         // 16-byte chunks per row
   constexpr int RPL = 1024 / RB;                     // rows per 1-KB load
   constexpr int KK = BK / 16;                        // MFMA K steps per stage
   constexpr int BROWS = DUAL ? 2 * BN : BN;          // weight rows per stage
@@ -229,13 +234,14 @@ void grouped_gemm_bf16(
   // stages (full cache lines, half the requests of 64-byte pieces) into two
   // pair slots; the weights keep their own ring of NW single stages.
   constexpr bool AP = MODE == kUpGemm;
+  constexpr bool FUSED = MODE == kDownFused;
   constexpr int ASLOT = BM * 2 * RB;                   // bytes of one A pair slot
   constexpr int WST = BROWS * RB;                      // bytes of one weight stage
   constexpr int NW_ = (kLdsBytes - 2 * ASLOT) / WST;
-  constexpr int NW = AP ? (NW_ < 6 ? NW_ : 6) : NS;    // weight ring depth
+  constexpr int NW = AP ? (NW_ < 8 ? NW_ : 8) : NS;    // weight ring depth
   constexpr int LA2 = BM / 8 / 4;                      // A loads per pair, A waves (0-3)
   constexpr int LDSB = AP ? 2 * ASLOT + NW * WST : NS * STAGE;
-  static_assert(!AP || (NW >= 4 && NW - 2 <= 4 && (NW - 1) * LB < 64 && 2 * LA2 < 64),
+  static_assert(!AP || (NW >= 4 && NW - 2 <= 6 && (NW - 1) * LB < 64 && 2 * LA2 < 64),
                 "pair ring: A pairs two stages ahead, weight waits covered below");
   static_assert(NS >= 3, "the ring needs three stages");
   static_assert(KK == 2, "register sets alternate per K step");
@@ -264,25 +270,29 @@ void grouped_gemm_bf16(
   const bf16_t* src[LMAX];
   int ldst;  // LDS byte offset (within a stage) of this wave's first load
   size_t kstep;
-  int arow = 0, ach0 = 0, ach1 = 0;  // AP A waves: first row, logical chunk offsets
-  if (a_wave && MODE == kDownGemm) {
-    ldst = grp * LA * 1024;
+  int arow = 0, ach0 = 0;  // AP A waves: first row, logical chunk offset
+  // A rows are spread over the four A waves in interleaved units (16-row
+  // groups for the down GEMM, 8-row pieces of a pair for the up GEMM): load i
+  // of wave grp fetches unit 4 i + grp.  A copy of the K loop for FA_ live
+  // fragments issues only the loads of units below 64 FA_ rows (all a tile of
+  // at most 64 FA_ rows holds), so a short tile fetches only its own rows.
+  if (a_wave && MODE != kUpGemm) {
+    ldst = grp * 1024;
     kstep = (size_t)ldg * 512;
     const int last = (r1 - r0 - 1) / RPL;  // the tile's last 16-row group
 #pragma unroll
     for (int i = 0; i < LMAX; ++i) {
-      const int g = min(grp * LA + (i < LA ? i : 0), last);  // groups past the tile: fetched, never used
+      const int g = min(4 * (i < LA ? i : 0) + grp, last);  // past the tile: fetched, never used
       src[i] = A + (size_t)(g0 + g) * 512 + lane * 8;
     }
   } else if (a_wave) {
-    // Load i of a pair: tile rows (grp * LA2 + i) * 8 + lane / 8, physical
-    // 16-byte chunk lane % 8 of the row's 128 bytes, which holds logical chunk
-    // (lane % 8) ^ swz8(row % 16); row % 16 = 8 (i % 2) + lane / 8.
+    // Load i of a pair: tile rows 8 (4 i + grp) + lane / 8, physical 16-byte
+    // chunk lane % 8 of the row's 128 bytes, which holds logical chunk
+    // (lane % 8) ^ swz8(row % 16); row % 16 = 8 (grp % 2) + lane / 8.
     ldst = 0;
     kstep = 0;
-    arow = r0 + grp * LA2 * 8 + lane / 8;
-    ach0 = ((lane & 7) ^ swz8(lane >> 3)) * 8;
-    ach1 = ((lane & 7) ^ swz8(8 + (lane >> 3))) * 8;
+    arow = r0 + grp * 8 + lane / 8;
+    ach0 = ((lane & 7) ^ swz8(8 * (grp & 1) + (lane >> 3))) * 8;
   } else {
     ldst = (AP ? 0 : BM * RB) + grp * LB * 1024;
     const int SR = packed_slab_rows(N);
@@ -296,7 +306,6 @@ void grouped_gemm_bf16(
                (n % SR) / RPL * 512 + lane * 8;
     }
   }
-  const int nl = a_wave ? LA : LB;
 
   // LDS byte offsets (within a stage) of this lane's MFMA fragments; the
   // chunk index of K step kk is (kk * 2 + lane / 32) ^ swizzle(row).
@@ -327,16 +336,17 @@ void grouped_gemm_bf16(
   bf16x8_t xf1[FM], wf1[FN], vf1[FN2];
   const int ktiles = K / BK;
 
-  // Issue the global->LDS loads of K tile kt_ into ring slot slot_.
-#define MOE_RING_ISSUE(kt_, slot_)                                                         \
+  // Issue the global->LDS loads of K tile kt_ into ring slot slot_; the A
+  // waves issue NA_ loads (units 4 i + grp), the weight waves LB.
+#define MOE_RING_ISSUE(kt_, slot_, NA_)                                                    \
   do {                                                                                     \
     char* base_ = smem + (slot_) * STAGE + ldst;                                           \
     if (a_wave) {                                                                          \
-      _Pragma("unroll") for (int i = 0; i < LMAX; ++i) if (LA == LB || i < nl)             \
+      _Pragma("unroll") for (int i = 0; i < LA; ++i) if (i < (NA_))                        \
           __builtin_amdgcn_global_load_lds((void*)(src[i] + (size_t)(kt_) * kstep),        \
-                                           (lds_ptr_t)(base_ + i * 1024), 16, 0, 0);       \
+                                           (lds_ptr_t)(base_ + i * 4096), 16, 0, 0);       \
     } else { /* weights are read once per launch: non-temporal, system scope */            \
-      _Pragma("unroll") for (int i = 0; i < LMAX; ++i) if (LA == LB || i < nl)             \
+      _Pragma("unroll") for (int i = 0; i < LB; ++i)                                       \
           __builtin_amdgcn_global_load_lds((void*)(src[i] + (size_t)(kt_) * kstep),        \
                                            (lds_ptr_t)(base_ + i * 1024), 16, 0, kWeightCpol); \
     }                                                                                      \
@@ -350,14 +360,14 @@ void grouped_gemm_bf16(
         __builtin_amdgcn_global_load_lds((void*)(src[i] + (size_t)(kt_) * kstep),          \
                                          (lds_ptr_t)(base_ + i * 1024), 16, 0, kWeightCpol); \
   } while (0)
-#define MOE_ISSUE_A(p_)                                                                    \
+#define MOE_ISSUE_A(p_, NA_)                                                               \
   do {                                                                                     \
-    char* base_ = smem + ((p_) & 1) * ASLOT + grp * LA2 * 1024;                            \
-    _Pragma("unroll") for (int i = 0; i < LA2; ++i) {                                      \
-      const int row_ = min(arow + 8 * i, r1 - 1); /* rows past the tile: never used */     \
+    char* base_ = smem + ((p_) & 1) * ASLOT + grp * 1024;                                  \
+    _Pragma("unroll") for (int i = 0; i < LA2; ++i) if (i < (NA_)) {                       \
+      const int row_ = min(arow + 32 * i, r1 - 1); /* rows past the tile: never used */    \
       __builtin_amdgcn_global_load_lds(                                                    \
-          (void*)(A + (size_t)row_ * K + ((i & 1) ? ach1 : ach0) + (size_t)(p_) * 2 * BK), \
-          (lds_ptr_t)(base_ + i * 1024), 16, 0, 0);                                        \
+          (void*)(A + (size_t)row_ * K + ach0 + (size_t)(p_) * 2 * BK),                    \
+          (lds_ptr_t)(base_ + i * 4096), 16, 0, 0);                                        \
     }                                                                                      \
   } while (0)
   // Read the fragments of K step kk_ of stage kt_ into set S (FA_ live row
@@ -385,8 +395,12 @@ void grouped_gemm_bf16(
   do {                                                                                     \
     _Pragma("unroll") for (int i = 0; i < (FA_); ++i)                                      \
     _Pragma("unroll") for (int j = 0; j < FN; ++j) {                                       \
-      acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(wf##S[j], xf##S[i], acc[i][j],   \
-                                                          0, 0, 0);                        \
+      if constexpr (FUSED)                                                                 \
+        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(xf##S[i], wf##S[j], acc[i][j], \
+                                                            0, 0, 0);                      \
+      else                                                                                 \
+        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(wf##S[j], xf##S[i], acc[i][j], \
+                                                            0, 0, 0);                      \
       if constexpr (DUAL)                                                                  \
         acc2[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf##S[j], xf##S[i],           \
                                                              acc2[i][j], 0, 0, 0);         \
@@ -394,15 +408,15 @@ void grouped_gemm_bf16(
   } while (0)
   // Wait until the next stage's loads have landed in every wave: at most
   // `later_` younger stages of this wave may still be in flight (vmcnt counts
-  // this wave's 1-KB loads, nl per stage).
-#define MOE_WAIT_STAGE(later_)                                                             \
+  // this wave's 1-KB loads: NA_ per stage for an A wave, LB for a weight wave).
+#define MOE_WAIT_STAGE(later_, NA_)                                                        \
   do {                                                                                     \
     if (a_wave) {                                                                          \
       switch (later_) {                                                                    \
         case 0: wait_vmcnt<0>(); break;                                                    \
-        case 1: wait_vmcnt<LA>(); break;                                                   \
-        case 2: wait_vmcnt<2 * LA>(); break;                                               \
-        default: wait_vmcnt<3 * LA>(); break;                                              \
+        case 1: wait_vmcnt<(NA_)>(); break;                                                \
+        case 2: wait_vmcnt<2 * (NA_)>(); break;                                            \
+        default: wait_vmcnt<3 * (NA_)>(); break;                                           \
       }                                                                                    \
     } else {                                                                               \
       switch (later_) {                                                                    \
@@ -422,7 +436,9 @@ void grouped_gemm_bf16(
       case 1: wait_vmcnt<LB>(); break;                                                     \
       case 2: wait_vmcnt<2 * LB>(); break;                                                 \
       case 3: wait_vmcnt<3 * LB>(); break;                                                 \
-      default: wait_vmcnt<4 * LB>(); break;                                                \
+      case 4: wait_vmcnt<4 * LB>(); break;                                                 \
+      case 5: wait_vmcnt<5 * LB>(); break;                                                 \
+      default: wait_vmcnt<6 * LB>(); break;                                                \
     }                                                                                      \
   } while (0)
   // The whole K loop for FA_ live row fragments.  Every copy issues the same
@@ -438,10 +454,10 @@ void grouped_gemm_bf16(
     if constexpr (AP) {                                                                    \
       /* A pairs 0 and 1, weight stages 0 .. NW-2; stage 0 landed.          */            \
       if (a_wave) {                                                                        \
-        MOE_ISSUE_A(0);                                                                    \
+        MOE_ISSUE_A(0, 2 * (FA_));                                                         \
         if (ktiles > 2) {                                                                  \
-          MOE_ISSUE_A(1);                                                                  \
-          wait_vmcnt<LA2>();                                                               \
+          MOE_ISSUE_A(1, 2 * (FA_));                                                       \
+          wait_vmcnt<2 * (FA_)>();                                                         \
         } else {                                                                           \
           wait_vmcnt<0>();                                                                 \
         }                                                                                  \
@@ -465,7 +481,7 @@ void grouped_gemm_bf16(
         }                                                                                  \
         ring_barrier();                                                                    \
         if (a_wave) {                                                                      \
-          if (kt & 1) MOE_ISSUE_A((kt + 3) >> 1);                                          \
+          if (kt & 1) MOE_ISSUE_A((kt + 3) >> 1, 2 * (FA_));                               \
         } else {                                                                           \
           MOE_ISSUE_W(kt + NW - 1);                                                        \
         }                                                                                  \
@@ -483,7 +499,7 @@ void grouped_gemm_bf16(
           }                                                                                \
           ring_barrier();                                                                  \
           if (a_wave) {                                                                    \
-            if ((kt & 1) && kt + 3 < ktiles) MOE_ISSUE_A((kt + 3) >> 1);                   \
+            if ((kt & 1) && kt + 3 < ktiles) MOE_ISSUE_A((kt + 3) >> 1, 2 * (FA_));        \
           } else if (kt + NW - 1 < ktiles) {                                               \
             MOE_ISSUE_W(kt + NW - 1);                                                      \
           }                                                                                \
@@ -492,17 +508,17 @@ void grouped_gemm_bf16(
         MOE_MFMA_KK(FA_, 1);                                                               \
       }                                                                                    \
     } else {                                                                               \
-      _Pragma("unroll") for (int s = 0; s < NS - 1; ++s) if (s < ktiles) MOE_RING_ISSUE(s, s); \
-      MOE_WAIT_STAGE(min(NS - 2, ktiles - 1));                                             \
+      _Pragma("unroll") for (int s = 0; s < NS - 1; ++s) if (s < ktiles) MOE_RING_ISSUE(s, s, FA_); \
+      MOE_WAIT_STAGE(min(NS - 2, ktiles - 1), FA_);                                        \
       MOE_LOAD_KK(FA_, 0, 0, 0);                                                           \
       /* Steady state: the refill is always in range and the wait count is  */            \
       /* fixed, so the loop body has no branches besides the wave role.     */            \
       for (; kt + NS - 1 < ktiles; ++kt) {                                                 \
         MOE_LOAD_KK(FA_, kt, 1, 1);                                                        \
         MOE_MFMA_KK(FA_, 0);                                                               \
-        if (a_wave) wait_vmcnt<(NS - 3) * LA>(); else wait_vmcnt<(NS - 3) * LB>();         \
+        if (a_wave) wait_vmcnt<(NS - 3) * (FA_)>(); else wait_vmcnt<(NS - 3) * LB>();      \
         ring_barrier();                                                                    \
-        MOE_RING_ISSUE(kt + NS - 1, (kt + NS - 1) % NS);                                   \
+        MOE_RING_ISSUE(kt + NS - 1, (kt + NS - 1) % NS, FA_);                              \
         MOE_LOAD_KK(FA_, kt + 1, 0, 0);                                                    \
         MOE_MFMA_KK(FA_, 1);                                                               \
       }                                                                                    \
@@ -513,8 +529,8 @@ void grouped_gemm_bf16(
         if (kt + 1 < ktiles) {                                                             \
           /* Stage kt+1 visible to all waves; every wave is past its reads of */          \
           /* stage kt-1, so that slot can be refilled.                         */          \
-          MOE_WAIT_STAGE(min(NS - 3, ktiles - kt - 2));                                    \
-          if (kt + NS - 1 < ktiles) MOE_RING_ISSUE(kt + NS - 1, (kt + NS - 1) % NS);       \
+          MOE_WAIT_STAGE(min(NS - 3, ktiles - kt - 2), FA_);                               \
+          if (kt + NS - 1 < ktiles) MOE_RING_ISSUE(kt + NS - 1, (kt + NS - 1) % NS, FA_);  \
           MOE_LOAD_KK(FA_, kt + 1, 0, 0);                                                  \
         }                                                                                  \
         MOE_MFMA_KK(FA_, 1);                                                               \
@@ -557,6 +573,30 @@ void grouped_gemm_bf16(
       }                                                                                    \
     }                                                                                      \
   } while (0)
+  // Fused combine epilogue (operands swapped): accumulator element q of lane l
+  // is output column l & 31 of fragment row 8 (q / 4) + 4 (l >> 5) + q % 4.
+  // Per row: its token and routing weight (rows without a token add nothing),
+  // then w * bf16(O) into y_acc[token] (y_acc rows are N = d wide).
+#define MOE_EPILOGUE_FUSED(FA_)                                                            \
+  do {                                                                                     \
+    _Pragma("unroll") for (int i = 0; i < (FA_); ++i)                                      \
+    _Pragma("unroll") for (int q = 0; q < 16; ++q) {                                       \
+      const int row = r0 + (2 * i + wm) * 32 + 8 * (q >> 2) + 4 * (lane >> 5) + (q & 3);    \
+      int tok = -1;                                                                        \
+      float wt = 0.f;                                                                      \
+      if (row < r1) {                                                                      \
+        tok = fc.token_of_row[row];                                                        \
+        if (tok >= 0) wt = fc.topk_w[(size_t)tok * fc.k + fc.slot_of_row[row]];            \
+      }                                                                                    \
+      _Pragma("unroll") for (int j = 0; j < FN; ++j) {                                     \
+        const int col = n0 + wn * WN + j * 32 + (lane & 31);                               \
+        if (tok >= 0 && col < N) {                                                         \
+          const float o = bf16_to_f32(pack_bf16x2(acc[i][j][q], 0.f) & 0xffffu);           \
+          unsafeAtomicAdd(fc.y_acc + (size_t)tok * N + col, wt * o);                       \
+        }                                                                                  \
+      }                                                                                    \
+    }                                                                                      \
+  } while (0)
   // One self-contained copy (accumulators, K loop, epilogue) per number of
   // live fragments, so no accumulator value crosses from one copy to another.
 #define MOE_TILE(FA_)                                                                      \
@@ -564,28 +604,22 @@ void grouped_gemm_bf16(
     floatx16 acc[(FA_) > 0 ? (FA_) : 1][FN];                                               \
     floatx16 acc2[DUAL && (FA_) > 0 ? (FA_) : 1][FN2];                                     \
     MOE_K_LOOP(FA_);                                                                       \
-    MOE_EPILOGUE(FA_);                                                                     \
+    if constexpr (FUSED) MOE_EPILOGUE_FUSED(FA_);                                          \
+    else MOE_EPILOGUE(FA_);                                                                \
   } while (0)
 
-  static_assert(FM == 5 || FM == 2, "one copy per live-fragment count 0..FM");
-  if constexpr (FM == 5) {
-    switch (fa) {
-      case 0: MOE_TILE(0); break;
-      case 1: MOE_TILE(1); break;
-      case 2: MOE_TILE(2); break;
-      case 3: MOE_TILE(3); break;
-      case 4: MOE_TILE(4); break;
-      default: MOE_TILE(5); break;
-    }
-  } else {
-    switch (fa) {
-      case 0: MOE_TILE(0); break;
-      case 1: MOE_TILE(1); break;
-      default: MOE_TILE(2); break;
-    }
+  static_assert(FM >= 2 && FM <= 5, "one copy per live-fragment count 0..FM");
+  switch (fa) {
+    case 0: MOE_TILE(0); break;
+    case 1: MOE_TILE(1); break;
+    case 2: if constexpr (FM >= 2) MOE_TILE(2); break;
+    case 3: if constexpr (FM >= 3) MOE_TILE(3); break;
+    case 4: if constexpr (FM >= 4) MOE_TILE(4); break;
+    default: if constexpr (FM >= 5) MOE_TILE(5); break;
   }
 #undef MOE_TILE
 #undef MOE_EPILOGUE
+#undef MOE_EPILOGUE_FUSED
 #undef MOE_K_LOOP
 #undef MOE_LOAD_KK
 #undef MOE_MFMA_KK
@@ -631,11 +665,14 @@ hipError_t launch_pack_weights(int E, int N, int K, const void* w, void* wp, hip
 
 // ------------------------------------------------------------- fp32 MFMA ---
 
-template <int ACT>
+// FUSEDC: the down GEMM with the combine folded in (as kDownFused above): each
+// output element, scaled by its row's routing weight, is added into the
+// token's fp32 accumulator row instead of being stored.
+template <int ACT, bool FUSEDC>
 __global__ __launch_bounds__(256) void grouped_gemm_f32(
     const float* __restrict__ A, const float* __restrict__ B, const float* __restrict__ B2,
     float* __restrict__ C, int K, int N, const int4* __restrict__ tiles,
-    const int32_t* __restrict__ tile_count, int n_tiles) {
+    const int32_t* __restrict__ tile_count, int n_tiles, FusedCombineArgs fc) {
   constexpr bool DUAL = ACT == ACT_SWIGLU;
   constexpr int BM = 64, BN = 64, BK = 16, LDK = BK + 1;
   __shared__ float As[BM][LDK], Bs[BN][LDK], B2s[DUAL ? BN : 1][LDK];
@@ -696,7 +733,16 @@ __global__ __launch_bounds__(256) void grouped_gemm_f32(
         float o;
         if constexpr (DUAL) o = silu(acc[i][j][v]) * acc2[i][j][v];
         else o = apply_act(acc[i][j][v], ACT);
-        if (row < r1 && col < N) C[(size_t)row * N + col] = o;
+        if constexpr (FUSEDC) {
+          if (row < r1 && col < N) {
+            const int tok = fc.token_of_row[row];
+            if (tok >= 0)
+              unsafeAtomicAdd(fc.y_acc + (size_t)tok * N + col,
+                              fc.topk_w[(size_t)tok * fc.k + fc.slot_of_row[row]] * o);
+          }
+        } else {
+          if (row < r1 && col < N) C[(size_t)row * N + col] = o;
+        }
       }
     }
 }
@@ -717,9 +763,17 @@ static size_t align256(size_t x) { return (x + 255) / 256 * 256; }
 // tiles streams the expert's weights again (DeepSeek-like layer, 128 rows per
 // expert on average but spread around that: 5.75 -> 6.63 ms per step with
 // 128-row tiles; decode, ~8 rows per expert: 3.77 -> 3.64 ms).
+// 192 rows when experts average at most 128 rows: such a batch is bound by the
+// weight stream, whose rate per CU is the weight bytes the ring keeps in
+// flight over the memory latency; the smaller A slots leave LDS for 7 weight
+// stages instead of 5 (up GEMM) and 5 ring stages instead of 4 (down GEMM),
+// while an expert of up to 192 rows (all but a few at 128 on average) still
+// takes one tile.
 static int ffn_bm(int dtype, int E, int max_rows) {
   if (dtype == 0) return kF32BM;
-  return (long long)max_rows <= 32LL * E ? kGemmBMSmall : kGemmBM;
+  if ((long long)max_rows <= 32LL * E) return kGemmBMSmall;
+  if ((long long)max_rows <= 128LL * E) return kGemmBMMid;
+  return kGemmBM;
 }
 
 // Upper bound of row tiles: every expert may end in a partial tile.
@@ -774,15 +828,17 @@ static void launch_bf16(const bf16_t* A, const bf16_t* B, const bf16_t* B2, bf16
   // fall from 1 A tile + 32 weight slabs to 4 A tiles + 8 weight slabs.
   const int gm = a.max_rows / a.E >= 2 * BM ? 4 : 1;
   grouped_gemm_bf16<BM, BN, ACT, MODE><<<g, kGemmWaves * 64, 0, st>>>(
-      A, B, B2, C, K, N, ffn_tiles(a), ffn_count(a), nt, ffn_groups(a.E, a.max_rows), gm);
+      A, B, B2, C, K, N, ffn_tiles(a), ffn_count(a), nt, ffn_groups(a.E, a.max_rows), gm,
+      MODE == kDownFused ? *a.fused : FusedCombineArgs{});
 }
 
-template <int ACT>
+template <int ACT, bool FUSEDC = false>
 static void launch_f32(const float* A, const float* B, const float* B2, float* C, int K, int N,
                        const FfnArgs& a, hipStream_t st) {
   const int nt = (N + kF32BN - 1) / kF32BN;
   const int g = grid_of(max_m_tiles(a.max_rows, kF32BM, a.E), nt);
-  grouped_gemm_f32<ACT><<<g, 256, 0, st>>>(A, B, B2, C, K, N, ffn_tiles(a), ffn_count(a), nt);
+  grouped_gemm_f32<ACT, FUSEDC><<<g, 256, 0, st>>>(A, B, B2, C, K, N, ffn_tiles(a), ffn_count(a),
+                                                   nt, FUSEDC ? *a.fused : FusedCombineArgs{});
 }
 
 hipError_t launch_ffn_up(const FfnArgs& a, hipStream_t st) {
@@ -799,7 +855,18 @@ hipError_t launch_ffn_up(const FfnArgs& a, hipStream_t st) {
     auto W1 = static_cast<const bf16_t*>(a.w1);
     auto W3 = static_cast<const bf16_t*>(a.w3);
     auto H = static_cast<bf16_t*>(ffn_hidden_buf(a));
-    if (ffn_bm(1, a.E, a.max_rows) == kGemmBMSmall) {
+    const int bm = ffn_bm(1, a.E, a.max_rows);
+    if (bm == kGemmBMMid) {
+      constexpr int S = kGemmBMMid;
+      if (a.act == ACT_SWIGLU) launch_bf16<S, 128, ACT_SWIGLU, kUpGemm>(X, W1, W3, H, a.d, a.h, a, st);
+      else if (a.h >= 2048) {
+        if (a.act == ACT_RELU) launch_bf16<S, 256, ACT_RELU, kUpGemm>(X, W1, nullptr, H, a.d, a.h, a, st);
+        else launch_bf16<S, 256, ACT_GELU, kUpGemm>(X, W1, nullptr, H, a.d, a.h, a, st);
+      } else {
+        if (a.act == ACT_RELU) launch_bf16<S, 128, ACT_RELU, kUpGemm>(X, W1, nullptr, H, a.d, a.h, a, st);
+        else launch_bf16<S, 128, ACT_GELU, kUpGemm>(X, W1, nullptr, H, a.d, a.h, a, st);
+      }
+    } else if (bm == kGemmBMSmall) {
       // 128-row tiles: twice the columns per tile for the same accumulators.
       constexpr int S = kGemmBMSmall;
       if (a.act == ACT_SWIGLU) {
@@ -825,24 +892,58 @@ hipError_t launch_ffn_up(const FfnArgs& a, hipStream_t st) {
   return hipGetLastError();
 }
 
-hipError_t launch_ffn_down(const FfnArgs& a, hipStream_t st) {
-  if (a.dtype == 0) {
-    launch_f32<ACT_NONE>(static_cast<const float*>(ffn_hidden_buf(a)),
-                         static_cast<const float*>(a.w2), nullptr, static_cast<float*>(a.y_rows),
-                         a.h, a.d, a, st);
+// Zero fill of the fused combine's fp32 accumulator (a kernel, not a memset,
+// so a captured graph replays it as a kernel node).
+__global__ __launch_bounds__(256) void zero_f32x4(floatx4* __restrict__ p, size_t n4) {
+  const size_t stride = (size_t)gridDim.x * blockDim.x;
+  for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < n4; i += stride)
+    p[i] = floatx4{0.f, 0.f, 0.f, 0.f};
+}
+
+template <int MODE>
+static void launch_down_bf16(const FfnArgs& a, hipStream_t st) {
+  auto H = static_cast<const bf16_t*>(ffn_hidden_buf(a));
+  auto W2 = static_cast<const bf16_t*>(a.w2);
+  auto Y = static_cast<bf16_t*>(a.y_rows);
+  const int bm = ffn_bm(1, a.E, a.max_rows);
+  if (bm == kGemmBMMid) {
+    if (a.d >= 1024) launch_bf16<kGemmBMMid, 256, ACT_NONE, MODE>(H, W2, nullptr, Y, a.h, a.d, a, st);
+    else launch_bf16<kGemmBMMid, 128, ACT_NONE, MODE>(H, W2, nullptr, Y, a.h, a.d, a, st);
+  } else if (bm == kGemmBMSmall) {
+    constexpr int S = kGemmBMSmall;
+    if (a.d >= 2048) launch_bf16<S, 512, ACT_NONE, MODE>(H, W2, nullptr, Y, a.h, a.d, a, st);
+    else launch_bf16<S, 256, ACT_NONE, MODE>(H, W2, nullptr, Y, a.h, a.d, a, st);
+  } else if (a.d >= 1024) {
+    launch_bf16<kGemmBM, 256, ACT_NONE, MODE>(H, W2, nullptr, Y, a.h, a.d, a, st);
   } else {
-    auto H = static_cast<const bf16_t*>(ffn_hidden_buf(a));
-    auto W2 = static_cast<const bf16_t*>(a.w2);
-    auto Y = static_cast<bf16_t*>(a.y_rows);
-    if (ffn_bm(1, a.E, a.max_rows) == kGemmBMSmall) {
-      constexpr int S = kGemmBMSmall;
-      if (a.d >= 2048) launch_bf16<S, 512, ACT_NONE, kDownGemm>(H, W2, nullptr, Y, a.h, a.d, a, st);
-      else launch_bf16<S, 256, ACT_NONE, kDownGemm>(H, W2, nullptr, Y, a.h, a.d, a, st);
-    } else if (a.d >= 1024) {
-      launch_bf16<kGemmBM, 256, ACT_NONE, kDownGemm>(H, W2, nullptr, Y, a.h, a.d, a, st);
-    } else {
-      launch_bf16<kGemmBM, 128, ACT_NONE, kDownGemm>(H, W2, nullptr, Y, a.h, a.d, a, st);
-    }
+    launch_bf16<kGemmBM, 128, ACT_NONE, MODE>(H, W2, nullptr, Y, a.h, a.d, a, st);
+  }
+}
+
+hipError_t launch_ffn_zero_acc(const FfnArgs& a, hipStream_t st) {
+  const size_t n4 = (size_t)a.fused->N * a.d / 4;  // d is a multiple of 64
+  if (n4 > 0) {
+    const int blocks = (int)std::min<size_t>((n4 + 255) / 256, 4096);
+    zero_f32x4<<<blocks, 256, 0, st>>>(reinterpret_cast<floatx4*>(a.fused->y_acc), n4);
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_ffn_down(const FfnArgs& a, hipStream_t st) {
+  if (a.fused) {
+    const hipError_t e = launch_ffn_zero_acc(a, st);
+    if (e != hipSuccess) return e;
+  }
+  if (a.dtype == 0) {
+    auto H = static_cast<const float*>(ffn_hidden_buf(a));
+    auto W2 = static_cast<const float*>(a.w2);
+    auto Y = static_cast<float*>(a.y_rows);
+    if (a.fused) launch_f32<ACT_NONE, true>(H, W2, nullptr, Y, a.h, a.d, a, st);
+    else launch_f32<ACT_NONE, false>(H, W2, nullptr, Y, a.h, a.d, a, st);
+  } else if (a.fused) {
+    launch_down_bf16<kDownFused>(a, st);
+  } else {
+    launch_down_bf16<kDownGemm>(a, st);
   }
   return hipGetLastError();
 }

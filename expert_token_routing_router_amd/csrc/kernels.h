@@ -70,6 +70,17 @@ enum { kDispatchLayout = 1, kDispatchPermute = 2 };
 hipError_t launch_dispatch(const DispatchArgs& a, hipStream_t st,
                            int stages = kDispatchLayout | kDispatchPermute);
 
+// Fused combine of the down GEMM: expert output row r goes, as
+// topk_w[t, j] * dtype(O[r]), into y_acc[t] (t = token_of_row[r],
+// j = slot_of_row[r]) by fp32 atomic adds instead of into y_rows.
+struct FusedCombineArgs {
+  int N, k;
+  const float* topk_w;
+  const int32_t* token_of_row;
+  const int8_t* slot_of_row;
+  float* y_acc;
+};
+
 struct FfnArgs {
   int E, max_rows, d, h, act, dtype;
   const void* x_rows;
@@ -79,12 +90,15 @@ struct FfnArgs {
   const void* w2;
   void* y_rows;
   void* ws;
+  const FusedCombineArgs* fused = nullptr;  // down GEMM: scatter-add into y_acc
 };
 
 size_t ffn_workspace_bytes(int E, int max_rows, int d, int h, int act, int dtype);
 hipError_t launch_ffn_plan(const FfnArgs& a, hipStream_t st);
 hipError_t launch_ffn_up(const FfnArgs& a, hipStream_t st);
 hipError_t launch_ffn_down(const FfnArgs& a, hipStream_t st);
+// Zero the fused combine's accumulator (a.fused->y_acc, N x d fp32).
+hipError_t launch_ffn_zero_acc(const FfnArgs& a, hipStream_t st);
 hipError_t launch_pack_weights(int E, int N, int K, const void* w, void* wp, hipStream_t st);
 
 struct CombineArgs {
@@ -95,6 +109,7 @@ struct CombineArgs {
   const void* residual;
   const void* shared_out;
   void* y;
+  const float* y_acc = nullptr;  // set: finish a fused down GEMM's accumulator instead
 };
 
 hipError_t launch_combine(const CombineArgs& a, hipStream_t st);

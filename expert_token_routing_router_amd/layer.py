@@ -11,7 +11,8 @@ from __future__ import annotations
 
 import torch
 
-from . import (ACT, DTYPE, TORCH_DTYPE, desc_from_workload, moe_bias_update, moe_combine,
+from . import (ACT, DTYPE, TORCH_DTYPE, desc_from_workload, fused_combine, moe_bias_update,
+               moe_combine,
                admission_flags, moe_dequantize_q8, moe_dispatch, moe_dispatch_ex,
                moe_dispatch_q8, moe_dispatch_rows,
                moe_dispatch_workspace_size, moe_expert_ffn,
@@ -82,6 +83,11 @@ class MoeBuffers:
         self.rank_counts = torch.empty(R, **i32)
         self.ws_dispatch = workspace(moe_dispatch_workspace_size(d), device)
         self.y_perm = torch.empty(S_rows, dim, dtype=dt, device=device)
+        # Fused combine (workloads with combine="fused"): the down GEMM adds
+        # w * O into this fp32 accumulator instead of writing y_perm.
+        self.y_acc = None
+        if cfg.get("combine", "unfused") == "fused":
+            self.y_acc = torch.empty(max(N, 1), dim, dtype=torch.float32, device=device)
         h = cfg["h"]
         self.ws_ffn = workspace(moe_expert_ffn_workspace_size(E, self.rows, dim, h, cfg["act"],
                                                               cfg["dtype"]), device)
@@ -95,6 +101,14 @@ class MoeBuffers:
             self.ws_shared = workspace(moe_expert_ffn_workspace_size(1, N, dim, h, cfg["act"],
                                                                      cfg["dtype"]), device)
         self.y = torch.empty(N, dim, dtype=dt, device=device)
+
+    def fused_args(self):
+        """The down GEMM's fused combine argument (None on the unfused path)."""
+        if self.y_acc is None:
+            return None
+        d = self.desc
+        return fused_combine(d.num_tokens, d.top_k, self.topk_w, self.token_of_row,
+                             self.slot_of_row, self.y_acc)
 
 
 def route(buf: MoeBuffers, inp: dict, sel_bias=None, stream=None):
@@ -132,9 +146,10 @@ def routed_ffn(buf: MoeBuffers, inp: dict, stream=None):
     d, cfg = buf.desc, buf.cfg
     if not inp.get("weights_packed"):
         raise ValueError("expert_ffn needs the weights from prepare_weights(cfg, inp)")
+    fused = buf.fused_args()
     moe_expert_ffn(d.num_experts, buf.rows, d.hidden, cfg["h"], cfg["act"], cfg["dtype"], buf.x_perm,
-                   buf.expert_offsets, inp["w1"], inp.get("w3"), inp["w2"], buf.y_perm,
-                   buf.ws_ffn, stream)
+                   buf.expert_offsets, inp["w1"], inp.get("w3"), inp["w2"],
+                   None if fused is not None else buf.y_perm, fused, buf.ws_ffn, stream)
 
 
 def has_shared(buf: MoeBuffers, inp: dict) -> bool:
@@ -148,7 +163,7 @@ def shared_ffn(buf: MoeBuffers, inp: dict, stream=None):
         raise ValueError("expert_ffn needs the weights from prepare_weights(cfg, inp)")
     sw1, sw3, sw2 = inp["shared"]
     moe_expert_ffn(1, d.num_tokens, d.hidden, cfg["h"], cfg["act"], cfg["dtype"], inp["x"],
-                   buf.shared_offsets, sw1, sw3, sw2, buf.shared_out, buf.ws_shared, stream)
+                   buf.shared_offsets, sw1, sw3, sw2, buf.shared_out, None, buf.ws_shared, stream)
 
 
 def expert_ffn(buf: MoeBuffers, inp: dict, stream=None):
@@ -160,7 +175,7 @@ def expert_ffn(buf: MoeBuffers, inp: dict, stream=None):
 
 def combine(buf: MoeBuffers, inp: dict, residual=True, stream=None):
     moe_combine(buf.desc, buf.y_perm, buf.row_of_slot, buf.topk_w,
-                inp["x"] if residual else None, buf.shared_out, buf.y, stream)
+                inp["x"] if residual else None, buf.shared_out, buf.y_acc, buf.y, stream)
 
 
 def bias_update(buf: MoeBuffers, sel_bias: torch.Tensor, step: float, stream=None):

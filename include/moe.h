@@ -15,7 +15,8 @@
  *   moe_expert_ffn   every expert's FFN over its rows as one grouped GEMM pair
  *                    (bf16 weights packed once by moe_expert_ffn_pack_weights)
  *   moe_combine      weighted sum back to token order, plus residual and an
- *                    optional shared-expert output
+ *                    optional shared-expert output (or, after a fused down
+ *                    GEMM, the finish of its fp32 accumulator)
  *   moe_bias_update  lower the selection bias of overloaded experts, raise it
  *                    for underloaded ones
  *   moe_combine_backward, moe_permute_backward
@@ -279,6 +280,30 @@ int moe_dequantize_q8(int32_t max_rows, int32_t hidden, int32_t dtype, const int
 
 /* ------------------------------------------------------------- expert FFN -- */
 
+/* Fused combine of the down GEMM (glossary step 4 folded into step 3): with
+ * this argument the down GEMM does not write y_rows; each expert output row r
+ * (token t = token_of_row[r], slot j = slot_of_row[r]; rows with t = -1 are
+ * skipped) is rounded to dtype, as the unfused path stores it, multiplied by
+ * topk_w[t, j] in fp32 and added into y_acc[t] with fp32 atomic adds.  The call
+ * first zeroes y_acc (with a kernel: the call stays capturable in a graph).
+ * moe_combine with y_acc then adds the residual and shared output and rounds.
+ * The atomic adds of a token's k rows land in no fixed order, so with k > 1
+ * the result may differ between runs in the last bits; with k = 1 each
+ * element receives one add onto zero and the result is the same on every run.
+ * Either way it matches the unfused path to rounding (within the layer
+ * tolerance), not bit for bit: the unfused combine rounds once per fused
+ * multiply-add, this path rounds the product and the sum apart.  A token whose
+ * every slot was dropped keeps y_acc = 0, so its y is the residual unchanged.
+ * The shared expert never takes this path. */
+typedef struct {
+  int32_t num_tokens;          /* N: rows of y_acc (>= every token_of_row + 1) */
+  int32_t top_k;               /* k: topk_w is [N, k] */
+  const float* topk_w;         /* [N, k] fp32, from moe_route */
+  const int32_t* token_of_row; /* [max_rows] int32, from the dispatch (-1: no token) */
+  const int8_t* slot_of_row;   /* [max_rows] int8, from the dispatch */
+  float* y_acc;                /* [N, d] fp32 out, 16-byte aligned; owned by the caller */
+} moe_fused_combine;
+
 /* Workspace bytes moe_expert_ffn needs for up to max_rows rows. */
 size_t moe_expert_ffn_workspace_size(int32_t num_experts, int32_t max_rows, int32_t hidden,
                                      int32_t ffn_hidden, int32_t act, int32_t dtype);
@@ -301,12 +326,16 @@ size_t moe_expert_ffn_workspace_size(int32_t num_experts, int32_t max_rows, int3
  *                moe_expert_ffn_pack_weights writes (done once, when the
  *                weights are loaded); row-major bf16 weights give wrong
  *                results, which the library cannot detect.
- *  y_rows        [max_rows, d]  dtype out (rows >= offsets[E] untouched)
+ *  y_rows        [max_rows, d]  dtype out (rows >= offsets[E] untouched);
+ *                NULL (and not written) when fused is given
+ *  fused         nullable: the fused combine above (token_of_row and
+ *                slot_of_row then cover max_rows rows)
  *  ws, ws_bytes  workspace >= moe_expert_ffn_workspace_size(...) */
 int moe_expert_ffn(int32_t num_experts, int32_t max_rows, int32_t hidden, int32_t ffn_hidden,
                    int32_t act, int32_t dtype, const void* x_rows,
                    const int32_t* group_offsets, const void* w1, const void* w3,
-                   const void* w2, void* y_rows, void* ws, size_t ws_bytes, void* stream);
+                   const void* w2, void* y_rows, const moe_fused_combine* fused, void* ws,
+                   size_t ws_bytes, void* stream);
 
 /* The three stages of moe_expert_ffn, for callers that time or overlap them.
  * They share one workspace (same size query) and must run in this order on
@@ -314,7 +343,8 @@ int moe_expert_ffn(int32_t num_experts, int32_t max_rows, int32_t hidden, int32_
  *  moe_expert_ffn_plan  per-expert row-tile schedule from group_offsets
  *  moe_expert_ffn_up    H = act(X W1_e^T) (SwiGLU: silu(X W1_e^T)*(X W3_e^T)),
  *                       H kept in ws, one kernel launch
- *  moe_expert_ffn_down  Y = H W2_e^T, one kernel launch
+ *  moe_expert_ffn_down  Y = H W2_e^T, one kernel launch (with fused: a zeroing
+ *                       launch for y_acc, then the GEMM scatter-adding into it)
  * Arguments mean what they mean for moe_expert_ffn; errors likewise. */
 int moe_expert_ffn_plan(int32_t num_experts, int32_t max_rows, int32_t hidden,
                         int32_t ffn_hidden, int32_t act, int32_t dtype,
@@ -326,7 +356,8 @@ int moe_expert_ffn_up(int32_t num_experts, int32_t max_rows, int32_t hidden, int
 int moe_expert_ffn_down(int32_t num_experts, int32_t max_rows, int32_t hidden,
                         int32_t ffn_hidden, int32_t act, int32_t dtype,
                         const int32_t* group_offsets, const void* w2, void* y_rows,
-                        void* ws, size_t ws_bytes, void* stream);
+                        const moe_fused_combine* fused, void* ws, size_t ws_bytes,
+                        void* stream);
 
 /* Pack one bf16 expert weight tensor for the bf16 expert FFN.
  *
@@ -367,10 +398,16 @@ int moe_expert_ffn_pack_weights(int32_t num_experts, int32_t rows, int32_t cols,
  *  topk_w      [N, k]    fp32    from moe_route
  *  residual    [N, d]    dtype   nullable (normally x)
  *  shared_out  [N, d]    dtype   nullable (always-on shared expert output)
+ *  y_acc       [N, d]    fp32    nullable: the accumulator a fused down GEMM
+ *                                (moe_fused_combine) filled; then
+ *                                y[t] = residual[t] + shared_out[t] + y_acc[t]
+ *                                in fp32, rounded once, and y_perm,
+ *                                row_of_slot and topk_w are not read (may be
+ *                                NULL).  16-byte aligned.
  *  y           [N, d]    dtype   out */
 int moe_combine(const moe_route_desc* desc, const void* y_perm, const int32_t* row_of_slot,
                 const float* topk_w, const void* residual, const void* shared_out,
-                void* y, void* stream);
+                const float* y_acc, void* y, void* stream);
 
 /* --------------------------------------------------------------- backward -- */
 

@@ -219,7 +219,7 @@ def test_expert_ffn_validation():
     lib = moe.lib()
     F = FAKE
     call = lambda E, M, d, h, act, dt, w3=None, ws=F, wsb=1 << 30: lib.moe_expert_ffn(  # noqa: E731
-        E, M, d, h, act, dt, F, F, F, w3, F, F, ws, wsb, None)
+        E, M, d, h, act, dt, F, F, F, w3, F, F, None, ws, wsb, None)
     assert call(0, 100, 64, 64, moe.MOE_RELU, moe.MOE_BF16) == moe.MOE_ERR_INVALID_ARG
     assert call(8, -1, 64, 64, moe.MOE_RELU, moe.MOE_BF16) == moe.MOE_ERR_INVALID_ARG
     assert call(8, 100, 96, 64, moe.MOE_RELU, moe.MOE_BF16) == moe.MOE_ERR_UNSUPPORTED
@@ -231,6 +231,39 @@ def test_expert_ffn_validation():
     need = moe.moe_expert_ffn_workspace_size(8, 100, 64, 64, "relu", "bf16")
     assert call(8, 100, 64, 64, moe.MOE_RELU, moe.MOE_BF16, wsb=need - 1) == moe.MOE_ERR_WORKSPACE
     assert call(8, 0, 64, 64, moe.MOE_RELU, moe.MOE_BF16) == moe.MOE_OK  # nothing to do
+
+
+def test_expert_ffn_fused_validation():
+    """The fused combine argument is checked before any launch: its sizes, its
+    arrays and the accumulator's alignment; y_rows is optional only with it."""
+    lib = moe.lib()
+    F = FAKE
+
+    def call(fc, y=None, M=100, stage="all"):
+        ref = ctypes.byref(fc) if fc is not None else None
+        if stage == "down":
+            return lib.moe_expert_ffn_down(8, M, 64, 64, moe.MOE_RELU, moe.MOE_BF16, F, F, y, ref,
+                                           F, 1 << 30, None)
+        return lib.moe_expert_ffn(8, M, 64, 64, moe.MOE_RELU, moe.MOE_BF16, F, F, F, None, F, y,
+                                  ref, F, 1 << 30, None)
+
+    def fc(**kw):
+        a = dict(N=10, k=2, w=0x10000, tor=0x10000, sor=0x10000, acc=0x10000)
+        a.update(kw)
+        return moe.FusedCombine(a["N"], a["k"], a["w"], a["tor"], a["sor"], a["acc"])
+
+    for stage in ("all", "down"):
+        assert call(None, stage=stage) == moe.MOE_ERR_INVALID_ARG  # neither y_rows nor fused
+        assert call(fc(k=0), stage=stage) == moe.MOE_ERR_INVALID_ARG
+        assert call(fc(k=9), stage=stage) == moe.MOE_ERR_INVALID_ARG
+        assert call(fc(N=-1), stage=stage) == moe.MOE_ERR_INVALID_ARG
+        assert call(fc(w=None), stage=stage) == moe.MOE_ERR_INVALID_ARG
+        assert call(fc(tor=None), stage=stage) == moe.MOE_ERR_INVALID_ARG
+        assert call(fc(sor=None), stage=stage) == moe.MOE_ERR_INVALID_ARG
+        assert call(fc(acc=None), stage=stage) == moe.MOE_ERR_INVALID_ARG
+        assert call(fc(acc=0x10008), stage=stage) == moe.MOE_ERR_INVALID_ARG  # misaligned
+        # no rows and no tokens: nothing to do
+        assert call(fc(N=0, tor=None, sor=None, w=None, acc=None), M=0, stage=stage) == moe.MOE_OK
 
 
 def test_pack_weights_validation():
@@ -252,10 +285,16 @@ def test_pack_weights_validation():
 def test_combine_and_bias_validation():
     lib = moe.lib()
     d = moe.route_desc(64, 64, 8, 2)
-    assert lib.moe_combine(ctypes.byref(d), None, FAKE, FAKE, None, None, FAKE, None) == \
+    assert lib.moe_combine(ctypes.byref(d), None, FAKE, FAKE, None, None, None, FAKE, None) == \
         moe.MOE_ERR_INVALID_ARG
     assert lib.moe_combine(ctypes.byref(moe.route_desc(0, 64, 8, 2)), None, None, None, None,
-                           None, None, None) == moe.MOE_OK
+                           None, None, None, None) == moe.MOE_OK
+    # Finishing a fused accumulator needs neither y_perm nor the routing arrays,
+    # but the accumulator must be 16-byte aligned and y present.
+    assert lib.moe_combine(ctypes.byref(d), None, None, None, None, None,
+                           ctypes.c_void_p(0x10004), FAKE, None) == moe.MOE_ERR_INVALID_ARG
+    assert lib.moe_combine(ctypes.byref(d), None, None, None, None, None, FAKE, None,
+                           None) == moe.MOE_ERR_INVALID_ARG
     assert lib.moe_bias_update(0, 10, 1, FAKE, 1e-3, FAKE, None) == moe.MOE_ERR_INVALID_ARG
     assert lib.moe_bias_update(8, 10, 1, None, 1e-3, FAKE, None) == moe.MOE_ERR_INVALID_ARG
     assert lib.moe_bias_update(8, 10, 1, FAKE, float("inf"), FAKE, None) == \

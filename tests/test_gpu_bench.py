@@ -14,7 +14,8 @@ pytestmark = pytest.mark.gpu
 
 def test_bench_json_line(capsys, monkeypatch):
     monkeypatch.setattr(sys, "argv", ["bench.py", "--workload", "toy", "--steps", "3",
-                                      "--warmup", "1", "--cpu-seconds", "0.5", "--no-clocks"])
+                                      "--warmup", "1", "--cpu-seconds", "0.5", "--no-clocks",
+                                      "--extra-workloads", "none"])
     print("[bench] toy, 3 steps", file=sys.stderr, flush=True)
     bench.main()
     lines = [l for l in capsys.readouterr().out.splitlines() if l.startswith("{")]
@@ -36,3 +37,8 @@ def test_bench_json_line(capsys, monkeypatch):
     assert c["single_thread"]["cores"] == 1
     assert set(d["kernels"]) >= {"route", "dispatch_layout", "permute", "ffn_up", "ffn_down",
                                  "combine", "bias_update"}
+    assert "H excluded" in r["algorithmic"]
+    f = d["routed_ffn"]
+    assert 0 < f["frac_of_floor"] <= 1.0 and f["weight_floor_us"] > 0
+    ld = d["load"]
+    assert ld["drop_rate"] == 0.0 and ld["rank_load_max_over_mean"] >= 1.0

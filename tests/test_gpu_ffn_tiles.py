@@ -7,7 +7,8 @@ per-expert row counts below sit on every one of those edges (0, 1, 31/32/33,
 160/161, 319/320/321, 641), with output widths that are and are not a
 multiple of the column tile.  Experts of many row tiles take the grouped
 block order (4 row tiles walk their column tiles together), with a short last
-group; decode-sized batches take 128-row tiles with wider column tiles.
+group; decode-sized batches take 128-row tiles with wider column tiles, and
+batches of at most 128 rows per expert on average 192-row tiles.
 Reference: the oracle's grouped FFN on the same
 rows (glossary "Expert Parallelism", step 3), per-tensor max relative error
 within 2e-2 (bf16) / 1e-4 (fp32).
@@ -105,6 +106,21 @@ def test_ffn_small_row_tiles(d, h, act):
     _check_ffn(d, h, act, "bf16", SMALL_COUNTS, seed=d + 3 * h)
 
 
+# Batches of at most 128 rows per expert on average (the DeepSeek-like layer)
+# take 192-row tiles: experts on the fragment edges of such a tile (0, 1,
+# 31/32/33, 63/64/65, 96, 127/128/129, 160, 191/192), one just past it (193,
+# split in two) and one of three tiles (385), among experts of 100 rows.
+MID_COUNTS = [0, 1, 31, 32, 33, 63, 64, 65, 96, 127, 128, 129, 160, 191, 192, 193, 385] + [100] * 15
+
+
+@pytest.mark.parametrize("d,h,act", [(512, 1024, "swiglu"), (384, 2048, "gelu"),
+                                     (1024, 640, "swiglu"), (256, 512, "relu")])
+def test_ffn_mid_row_tiles(d, h, act):
+    M = sum(MID_COUNTS) + 7
+    assert 32 * len(MID_COUNTS) < M <= 128 * len(MID_COUNTS), "must take the 192-row tiles"
+    _check_ffn(d, h, act, "bf16", MID_COUNTS, seed=d + 5 * h)
+
+
 def _check_ffn(d, h, act, dtype, counts, seed):
     print(f"[ffn tiles] d={d} h={h} act={act} dtype={dtype} counts={counts}", flush=True)
     x, w1, w3, w2, offs = _inputs(d, h, act, dtype, seed=seed, counts=counts)
@@ -115,7 +131,7 @@ def _check_ffn(d, h, act, dtype, counts, seed):
     y = torch.full((M, d), 7.0, dtype=x.dtype, device="cuda")
     ws = moe.workspace(moe.moe_expert_ffn_workspace_size(E, M, d, h, act, dtype))
     moe.moe_expert_ffn(E, M, d, h, act, dtype, x.cuda(), offs.cuda(), wts["w1"], wts["w3"],
-                       wts["w2"], y, ws)
+                       wts["w2"], y, None, ws)
     torch.cuda.synchronize()
     oracle.set_threads(threads())
     ref = oracle.expert_ffn(dtype, act, n(x), n(offs), n(w1), n(w3), n(w2))

@@ -528,6 +528,61 @@ def test_combine_and_permute_backward(name):
     assert bool((dx.cpu()[none].float() == 0).all())
 
 
+# The combine folded into the down GEMM (fp32 atomic scatter-add of w * O into
+# an accumulator that moe_combine finishes), on every workload family and on
+# the padded layout and the INT8 payload.
+FUSED_CASES = ["toy-full", "toy-small", "switch-small", "mixtral-small", "deepseek-small",
+               "decode-small", "zipf-small-cf1.0", "zipf-small-cf1.0-padded", "switch-small-int8"]
+
+
+@pytest.mark.parametrize("name", FUSED_CASES)
+def test_fused_combine_within_tolerance(name):
+    """y of the fused path against the oracle's y (the same definition, summed
+    in another order): within the layer tolerance with the residual and for the
+    branch alone; tokens with every slot dropped pass x through bit for bit;
+    the routing is that of the unfused run.  The accumulator starts as NaN: the
+    FFN call must zero it itself."""
+    cfg, inp_cpu, gpu, ref = run_case(name)
+    fcfg = W.with_(cfg, combine="fused")
+    print(f"[fused combine] {name}", flush=True)
+    inp = moe.prepare_weights(fcfg, to_dev(inp_cpu))
+    buf = moe.MoeBuffers(fcfg)
+    buf.y_acc.fill_(float("nan"))
+    buf.y_perm.fill_(7.0)
+    moe.moe_forward(buf, inp)
+    torch.cuda.synchronize()
+    assert torch.equal(buf.topk_idx.cpu(), gpu["topk_idx"])
+    assert torch.equal(buf.row_of_slot.cpu(), gpu["row_of_slot"])
+    assert bool((buf.y_perm.float() == 7.0).all()), "the fused path must not write y_perm"
+    y = buf.y.cpu()
+    err = rel_err(y, as_tensor(ref["y"], cfg["dtype"]))
+    assert err <= TOL[cfg["dtype"]], f"y max rel err {err:.3e}"
+    dropped = np.all(ref["row_of_slot"] < 0, axis=1)
+    if dropped.any() and ref["shared_out"] is None:
+        d = torch.from_numpy(dropped)
+        assert torch.equal(y[d], inp_cpu["x"][d]), "dropped tokens must pass unchanged"
+    layer.combine(buf, inp, residual=False)
+    torch.cuda.synchronize()
+    err = rel_err(buf.y.cpu(), as_tensor(ref["y_branch"], cfg["dtype"]))
+    assert err <= TOL[cfg["dtype"]], f"branch-only y max rel err {err:.3e}"
+
+
+def test_fused_combine_top1_same_every_run():
+    """With k = 1 every accumulator element receives one add onto zero, so two
+    runs of the fused path give the same y and y_acc bit for bit."""
+    cfg = W.with_(W.small("switch"), combine="fused")
+    inp = moe.prepare_weights(cfg, to_dev(W.make_inputs(cfg)))
+    buf = moe.MoeBuffers(cfg)
+    moe.moe_forward(buf, inp)
+    torch.cuda.synchronize()
+    y0, acc0 = buf.y.clone(), buf.y_acc.clone()
+    buf.y_acc.fill_(float("nan"))
+    moe.moe_forward(buf, inp)
+    torch.cuda.synchronize()
+    assert torch.equal(y0.view(torch.int16), buf.y.view(torch.int16))
+    assert torch.equal(acc0.view(torch.int32), buf.y_acc.view(torch.int32))
+
+
 def test_all_tokens_to_one_expert_with_capacity():
     """A huge selection bias sends every token to expert 3; capacity 1.25
     admits the first cap tokens; every other token leaves the layer unchanged."""
@@ -626,7 +681,7 @@ def test_ffn_stages_equal_single_call():
     moe.moe_expert_ffn_up(E, S, dim, h, cfg["act"], cfg["dtype"], buf.x_perm, buf.expert_offsets,
                           inp["w1"], inp["w3"], buf.ws_ffn)
     moe.moe_expert_ffn_down(E, S, dim, h, cfg["act"], cfg["dtype"], buf.expert_offsets,
-                            inp["w2"], buf.y_perm, buf.ws_ffn)
+                            inp["w2"], buf.y_perm, None, buf.ws_ffn)
     torch.cuda.synchronize()
     M = int(buf.expert_offsets[E].item())
     assert torch.equal(bits_t(buf.y_perm[:M]), bits_t(ref[:M]))
