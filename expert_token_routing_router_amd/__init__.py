@@ -40,7 +40,7 @@ EXPORTS = [
     "moe_route_workspace_size", "moe_route", "moe_router_logits",
     "moe_dispatch_workspace_size", "moe_dispatch", "moe_dispatch_ex", "moe_dispatch_q8",
     "moe_dequantize_q8", "moe_dispatch_layout", "moe_permute", "moe_permute_q8",
-    "moe_dispatch_rows", "moe_combine_backward", "moe_permute_backward",
+    "moe_dispatch_rows", "moe_dispatch_noalloc", "moe_combine_backward", "moe_permute_backward",
     "moe_expert_ffn_backward_workspace_size", "moe_expert_ffn_backward",
     "moe_expert_ffn_workspace_size", "moe_expert_ffn", "moe_expert_ffn_plan",
     "moe_expert_ffn_up", "moe_expert_ffn_down", "moe_expert_ffn_pack_weights", "moe_combine",
@@ -136,6 +136,7 @@ def lib() -> ctypes.CDLL:
             "moe_permute": ([D, P, P, P, P], I32),
             "moe_permute_q8": ([D, P, P, P, P, P], I32),
             "moe_dispatch_rows": ([D, I32], ctypes.c_int64),
+            "moe_dispatch_noalloc": ([D, I32, P, P, P, P, P, P, P, P, P, P, P], I32),
             "moe_combine_backward": ([D, P, P, P, P, P, P, P], I32),
             "moe_permute_backward": ([D, P, P, P, P], I32),
             "moe_expert_ffn_backward_workspace_size": ([I32, I32, I32, I32, I32, I32], SZ),
@@ -288,6 +289,30 @@ def moe_dispatch_q8(desc, admission, x, topk_idx, x_perm_q, row_scale, row_of_sl
         _ptr(ws, "ws", None, None, False), 0 if ws is None else ws.numel() * ws.element_size(),
         _stream(stream))
     _raise("moe_dispatch_q8", st)
+
+
+def moe_dispatch_noalloc(desc, admission, x, topk_idx, x_perm, row_of_slot, token_of_row,
+                         slot_of_row, expert_offsets, admitted, rank_offsets, rank_counts,
+                         stream=None):
+    """moe_dispatch_ex without a workspace: the kernels' scratch is the
+    library's own static device array (calls on one GPU must not overlap)."""
+    adm = ADMISSION[admission] if isinstance(admission, str) else int(admission)
+    N, d, E, k, R = desc.num_tokens, desc.hidden, desc.num_experts, desc.top_k, desc.num_ranks
+    dt = TORCH_DTYPE.get(desc.dtype)
+    S = N * k
+    rows = S if not adm & MOE_LAYOUT_PADDED else moe_dispatch_rows(desc, adm)
+    st = lib().moe_dispatch_noalloc(
+        ctypes.byref(desc), adm, _ptr(x, "x", dt, N * d, N > 0),
+        _ptr(topk_idx, "topk_idx", torch.int32, S, N > 0),
+        _ptr(x_perm, "x_perm", dt, rows * d, N > 0),
+        _ptr(row_of_slot, "row_of_slot", torch.int32, S, N > 0),
+        _ptr(token_of_row, "token_of_row", torch.int32, rows, N > 0),
+        _ptr(slot_of_row, "slot_of_row", torch.int8, rows, N > 0),
+        _ptr(expert_offsets, "expert_offsets", torch.int32, E + 1),
+        _ptr(admitted, "admitted", torch.int32, E),
+        _ptr(rank_offsets, "rank_offsets", torch.int32, R + 1),
+        _ptr(rank_counts, "rank_counts", torch.int32, R), _stream(stream))
+    _raise("moe_dispatch_noalloc", st)
 
 
 def admission_flags(admission="token", layout="compact") -> int:

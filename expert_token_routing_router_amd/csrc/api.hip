@@ -2,6 +2,8 @@
 // the launches.  Nothing here allocates device memory or synchronises.
 #include <math.h>
 
+#include <mutex>
+
 #include "../../include/moe.h"
 #include "kernels.h"
 
@@ -131,7 +133,8 @@ static int dispatch_common(const moe_route_desc* desc, int32_t admission, const 
                            int32_t* row_of_slot, int32_t* token_of_row, int8_t* slot_of_row,
                            int32_t* expert_offsets, int32_t* admitted, int32_t* rank_offsets,
                            int32_t* rank_counts, void* ws, size_t ws_bytes, void* stream,
-                           int stages = moe::kDispatchLayout | moe::kDispatchPermute);
+                           int stages = moe::kDispatchLayout | moe::kDispatchPermute,
+                           bool validate_only = false);
 
 int moe_dispatch_ex(const moe_route_desc* desc, int32_t admission, const void* x,
                     const int32_t* topk_idx, void* x_perm, int32_t* row_of_slot,
@@ -182,7 +185,7 @@ static int dispatch_common(const moe_route_desc* desc, int32_t admission, const 
                            int32_t* row_of_slot, int32_t* token_of_row, int8_t* slot_of_row,
                            int32_t* expert_offsets, int32_t* admitted, int32_t* rank_offsets,
                            int32_t* rank_counts, void* ws, size_t ws_bytes, void* stream,
-                           int stages) {
+                           int stages, bool validate_only) {
   int st = check_desc(desc);
   if (st != MOE_OK) return st;
   const bool layout = stages & moe::kDispatchLayout, permute = stages & moe::kDispatchPermute;
@@ -199,6 +202,7 @@ static int dispatch_common(const moe_route_desc* desc, int32_t admission, const 
     if (!x || !row_of_slot || !(x_perm || xq)) return MOE_ERR_INVALID_ARG;
     if (!aligned16(x) || (x_perm && !aligned16(x_perm))) return MOE_ERR_INVALID_ARG;
   }
+  if (validate_only) return MOE_OK;  // every argument but the workspace checked
   if (layout) {
     const size_t need = moe::dispatch_workspace_bytes(N, desc->top_k, desc->num_experts);
     if (!ws || ws_bytes < need || (reinterpret_cast<uintptr_t>(ws) & 15u))
@@ -212,6 +216,63 @@ static int dispatch_common(const moe_route_desc* desc, int32_t admission, const 
   a.row_scale = row_scale;
   a.padded = layout ? padded : 0;
   return status_of(moe::launch_dispatch(a, static_cast<hipStream_t>(stream), stages));
+}
+
+// ---------------------------------------------------- no-allocation dispatch --
+//
+// moe_dispatch_noalloc runs the dispatch kernels with their scratch (the
+// per-tile, per-expert histograms and tile bases) in this file-scope device
+// array instead of a caller workspace.  Each GPU the library runs on holds its
+// own copy until the process ends.  Host code never passes the array's name
+// to a kernel (on the host it is a stand-in, not a device address): the first
+// call on a device, with that device current, looks its address up once with
+// hipGetSymbolAddress and keeps it per device.  Every call on a device shares
+// that device's array, so calls that overlap on one GPU race; each call
+// writes every entry it reads before reading it, so nothing has to start at
+// zero.
+constexpr size_t kNoAllocScratchBytes = size_t(1) << 20;
+constexpr int kNoAllocMaxDevices = 64;
+static __device__ __align__(256) int32_t scratch[kNoAllocScratchBytes / sizeof(int32_t)];
+
+static std::mutex g_scratch_mutex;
+static void* g_scratch_ptr[kNoAllocMaxDevices];  // guarded by g_scratch_mutex
+
+// This device's address of `scratch` (looked up on its first use), or an error.
+static int noalloc_scratch(void** out) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess) return MOE_ERR_HIP;
+  if (dev < 0 || dev >= kNoAllocMaxDevices) return MOE_ERR_UNSUPPORTED;
+  std::lock_guard<std::mutex> lock(g_scratch_mutex);
+  if (!g_scratch_ptr[dev]) {
+    void* ptr = nullptr;
+    if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) != hipSuccess || !ptr) return MOE_ERR_HIP;
+    g_scratch_ptr[dev] = ptr;
+  }
+  *out = g_scratch_ptr[dev];
+  return MOE_OK;
+}
+
+int moe_dispatch_noalloc(const moe_route_desc* desc, int32_t admission, const void* x,
+                         const int32_t* topk_idx, void* x_perm, int32_t* row_of_slot,
+                         int32_t* token_of_row, int8_t* slot_of_row, int32_t* expert_offsets,
+                         int32_t* admitted, int32_t* rank_offsets, int32_t* rank_counts,
+                         void* stream) {
+  int st = check_desc(desc);
+  if (st != MOE_OK) return st;
+  if (moe::dispatch_workspace_bytes(desc->num_tokens, desc->top_k, desc->num_experts) >
+      kNoAllocScratchBytes)
+    return MOE_ERR_UNSUPPORTED;  // the batch needs more scratch than the static array holds
+  // Everything but the workspace is checked before the device is touched.
+  st = dispatch_common(desc, admission, x, topk_idx, x_perm, nullptr, nullptr, row_of_slot,
+                       token_of_row, slot_of_row, expert_offsets, admitted, rank_offsets,
+                       rank_counts, nullptr, 0, stream,
+                       moe::kDispatchLayout | moe::kDispatchPermute, true);
+  if (st != MOE_OK) return st;
+  void* ws = nullptr;
+  if ((st = noalloc_scratch(&ws)) != MOE_OK) return st;
+  return dispatch_common(desc, admission, x, topk_idx, x_perm, nullptr, nullptr, row_of_slot,
+                         token_of_row, slot_of_row, expert_offsets, admitted, rank_offsets,
+                         rank_counts, ws, kNoAllocScratchBytes, stream);
 }
 
 int64_t moe_dispatch_rows(const moe_route_desc* desc, int32_t admission) {

@@ -226,6 +226,27 @@ int moe_dispatch_ex(const moe_route_desc* desc, int32_t admission, const void* x
                     int32_t* admitted, int32_t* rank_offsets, int32_t* rank_counts,
                     void* ws, size_t ws_bytes, void* stream);
 
+/* Dispatch that allocates nothing and takes no workspace, for callers that
+ * cannot allocate device memory: code under HIP graph capture, tight serving
+ * loops, harnesses that forbid hipMalloc.  Arguments, outputs, layout and
+ * errors are those of moe_dispatch_ex (same kernels, bit-identical results);
+ * the kernels' scratch lives in a 1 MiB device array inside the library
+ * instead of ws, one copy per GPU, kept until the process ends.
+ *  - The call runs on the current device (the one `stream` belongs to); its
+ *    first call on a device looks the array's address up (no allocation).
+ *  - A batch needing more scratch than the array holds -- ceil(N*k / 1024) * E
+ *    * 4 bytes > 1 MiB, i.e. more than about 2^20 slots at E = 256 -- returns
+ *    MOE_ERR_UNSUPPORTED and enqueues nothing.
+ *  - Every call on one GPU shares that GPU's array: calls that overlap on one
+ *    GPU (different streams, or other host threads) race and give wrong
+ *    layouts.  Serialise them.  No state carries over from one call to the
+ *    next: every call writes each scratch entry before reading it. */
+int moe_dispatch_noalloc(const moe_route_desc* desc, int32_t admission, const void* x,
+                         const int32_t* topk_idx, void* x_perm, int32_t* row_of_slot,
+                         int32_t* token_of_row, int8_t* slot_of_row, int32_t* expert_offsets,
+                         int32_t* admitted, int32_t* rank_offsets, int32_t* rank_counts,
+                         void* stream);
+
 /* The two halves of moe_dispatch_ex / moe_dispatch_q8, for callers that schedule
  * them apart -- a multi-GPU layer exchanges the rank counts from the layout
  * before it moves the rows (glossary step 2) -- or time them apart.

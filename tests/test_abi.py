@@ -266,6 +266,28 @@ def test_expert_ffn_fused_validation():
         assert call(fc(N=0, tor=None, sor=None, w=None, acc=None), M=0, stage=stage) == moe.MOE_OK
 
 
+def test_dispatch_noalloc_validation():
+    """The dispatch without a workspace checks its arguments, and that the batch
+    fits its static scratch (1 MiB), before touching any device."""
+    lib = moe.lib()
+    F = FAKE
+
+    def call(desc, adm=0, **null):
+        args = [F] * 10
+        for i in null.get("at", ()):
+            args[i] = None
+        return lib.moe_dispatch_noalloc(ctypes.byref(desc), adm, *args, None)
+
+    # 2^21 slots over 256 experts: 2048 tiles x 256 experts x 4 bytes = 2 MiB
+    assert call(moe.route_desc(1 << 18, 64, 256, 8, 8)) == moe.MOE_ERR_UNSUPPORTED
+    assert call(moe.route_desc(64, 64, 8, 9)) == moe.MOE_ERR_INVALID_ARG       # k > E
+    assert call(moe.route_desc(64, 64, 8, 2), adm=8) == moe.MOE_ERR_INVALID_ARG  # bad flags
+    assert call(moe.route_desc(64, 64, 8, 2), adm=moe.MOE_LAYOUT_PADDED) == \
+        moe.MOE_ERR_INVALID_ARG  # padded layout needs a capacity
+    for i in range(10):  # every array is required for a non-empty batch
+        assert call(moe.route_desc(64, 64, 8, 2), at=(i,)) == moe.MOE_ERR_INVALID_ARG, i
+
+
 def test_pack_weights_validation():
     lib = moe.lib()
     pack = lib.moe_expert_ffn_pack_weights
