@@ -563,8 +563,8 @@ def backward_pass(moe, torch, buf, inp, steps: int) -> dict:
 
     def ffn_bwd():
         moe.moe_expert_ffn_backward(E, buf.rows, dim, h, act, "bf16", buf.x_perm,
-                                    buf.expert_offsets, w1, w3, w2, dy_perm, dx_perm, dw1, dw3,
-                                    dw2, ws)
+                                    buf.expert_offsets, buf.admitted, w1, w3, w2, dy_perm,
+                                    dx_perm, dw1, dw3, dw2, ws)
 
     for _ in range(2):
         ffn_bwd()

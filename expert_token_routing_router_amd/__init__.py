@@ -141,7 +141,7 @@ def lib() -> ctypes.CDLL:
             "moe_permute_backward": ([D, P, P, P, P], I32),
             "moe_expert_ffn_backward_workspace_size": ([I32, I32, I32, I32, I32, I32], SZ),
             "moe_expert_ffn_backward": ([I32, I32, I32, I32, I32, I32, P, P, P, P, P, P, P, P, P,
-                                         P, P, SZ, P], I32),
+                                         P, P, P, SZ, P], I32),
             "moe_expert_ffn_workspace_size": ([I32, I32, I32, I32, I32, I32], SZ),
             "moe_expert_ffn": ([I32, I32, I32, I32, I32, I32, P, P, P, P, P, P, FC, P, SZ, P],
                                I32),
@@ -545,10 +545,12 @@ def moe_expert_ffn_backward_workspace_size(num_experts, max_rows, hidden, ffn_hi
 
 
 def moe_expert_ffn_backward(num_experts, max_rows, hidden, ffn_hidden, act, dtype, x_rows,
-                            group_offsets, w1, w3, w2, dy_rows, dx_rows, dw1, dw3, dw2, ws,
-                            stream=None):
+                            group_offsets, group_rows, w1, w3, w2, dy_rows, dx_rows, dw1, dw3,
+                            dw2, ws, stream=None):
     """Input gradients dx_rows and fp32 weight gradients dw1/dw3/dw2 of the
-    grouped expert FFN; weights in plain row-major layout (not packed)."""
+    grouped expert FFN; weights in plain row-major layout (not packed).
+    group_rows: None, or [E] int32 rows of each segment that hold data (the
+    dispatch's admitted for the padded layout)."""
     act = ACT[act] if isinstance(act, str) else int(act)
     dtype = DTYPE[dtype] if isinstance(dtype, str) else int(dtype)
     dt = TORCH_DTYPE.get(dtype)
@@ -558,6 +560,7 @@ def moe_expert_ffn_backward(num_experts, max_rows, hidden, ffn_hidden, act, dtyp
     st = lib().moe_expert_ffn_backward(
         E, M, d, h, act, dtype, _ptr(x_rows, "x_rows", dt, M * d, M > 0),
         _ptr(group_offsets, "group_offsets", torch.int32, E + 1),
+        _ptr(group_rows, "group_rows", torch.int32, E, False),
         _ptr(w1, "w1", dt, E * h * d), _ptr(w3, "w3", dt, E * h * d, sw),
         _ptr(w2, "w2", dt, E * d * h), _ptr(dy_rows, "dy_rows", dt, M * d, M > 0),
         _ptr(dx_rows, "dx_rows", dt, M * d, M > 0), _ptr(dw1, "dw1", f32, E * h * d),

@@ -141,18 +141,32 @@ __device__ __forceinline__ void store4_bf16(bf16_t* p, float a, float b, float c
   *reinterpret_cast<uint2*>(p) = make_uint2(pack_bf16x2(a, b), pack_bf16x2(c, d));
 }
 
+// Expert e's segment: rows [offsets[e], offsets[e+1]) clamped to max_rows and,
+// when group_rows is given, to its first group_rows[e] rows (the rows that hold
+// data in a padded layout).
+__device__ __forceinline__ int2 segment(const int32_t* __restrict__ offsets,
+                                        const int32_t* __restrict__ group_rows, int e,
+                                        int max_rows) {
+  const int lo = min(offsets[e], max_rows);
+  int hi = min(offsets[e + 1], max_rows);
+  if (group_rows) hi = min(hi, lo + max(group_rows[e], 0));
+  return make_int2(lo, hi);
+}
+
 // 128-row tiles of every expert's segment, in expert order: tiles[q] = (expert,
 // first row, end row).  At most cap tiles are written (segments that overlap
 // could ask for more); count = the number written.
-__global__ __launch_bounds__(1024) void bwd_plan(const int32_t* __restrict__ offsets, int E,
+__global__ __launch_bounds__(1024) void bwd_plan(const int32_t* __restrict__ offsets,
+                                                 const int32_t* __restrict__ group_rows, int E,
                                                  int max_rows, int cap, int4* __restrict__ tiles,
                                                  int32_t* __restrict__ count) {
   __shared__ int32_t s[1024];
   const int e = threadIdx.x;
   int lo = 0, hi = 0, n = 0;
   if (e < E) {
-    lo = min(offsets[e], max_rows);
-    hi = min(offsets[e + 1], max_rows);
+    const int2 sg = segment(offsets, group_rows, e, max_rows);
+    lo = sg.x;
+    hi = sg.y;
     n = hi > lo ? (hi - lo + kTN - 1) / kTN : 0;
   }
   s[e] = n;
@@ -318,14 +332,14 @@ __global__ __launch_bounds__(kThreads) void bwd_dgrad(
 // (fp32, M columns).
 __global__ __launch_bounds__(kThreads) void bwd_wgrad(
     const bf16_t* __restrict__ Psrc, int ldp, const bf16_t* __restrict__ Qsrc, int ldq,
-    const int32_t* __restrict__ offsets, int max_rows, int M, int Nn, int split,
-    float* __restrict__ outA, float* __restrict__ outB) {
+    const int32_t* __restrict__ offsets, const int32_t* __restrict__ group_rows, int max_rows,
+    int M, int Nn, int split, float* __restrict__ outA, float* __restrict__ outB) {
   const int e = blockIdx.y;
   const int mt = (M + kTM - 1) / kTM;
   const int m0 = (blockIdx.x % mt) * kTM, n0 = (blockIdx.x / mt) * kTN;
   const int nm = min(kTM, M - m0), nn = min(kTN, Nn - n0);
-  const int lo = min(offsets[e], max_rows), hi = min(offsets[e + 1], max_rows);
-  const int K = max(hi - lo, 0);
+  const int2 sg = segment(offsets, group_rows, e, max_rows);
+  const int lo = sg.x, K = max(sg.y - sg.x, 0);
   __shared__ __align__(16) bf16_t P[kTM * kLdk];
   __shared__ __align__(16) bf16_t Q[kTN * kLdk];
   Stage<kTM> sp;
@@ -399,7 +413,7 @@ hipError_t launch_ffn_backward(const FfnBackwardArgs& a, hipStream_t st) {
                                      align256((size_t)cap * sizeof(int4)));
     G = reinterpret_cast<bf16_t*>(reinterpret_cast<char*>(Hbuf) +
                                   align256((size_t)a.max_rows * a.h * 2));
-    bwd_plan<<<1, 1024, 0, st>>>(a.offsets, a.E, a.max_rows, cap, tiles, count);
+    bwd_plan<<<1, 1024, 0, st>>>(a.offsets, a.group_rows, a.E, a.max_rows, cap, tiles, count);
     const dim3 ga((a.h + kTM - 1) / kTM, cap);
     switch (a.act) {
       case kRelu:
@@ -423,11 +437,11 @@ hipError_t launch_ffn_backward(const FfnBackwardArgs& a, hipStream_t st) {
   // Weight gradients (zeros for experts without rows, so they run even for
   // an empty batch: no operand is read then).
   const dim3 g13(((a.d + kTM - 1) / kTM) * ((kg + kTN - 1) / kTN), a.E);
-  bwd_wgrad<<<g13, kThreads, 0, st>>>(x, a.d, G, kg, a.offsets, a.max_rows, a.d, kg, a.h, a.dw1,
-                                      a.dw3);
+  bwd_wgrad<<<g13, kThreads, 0, st>>>(x, a.d, G, kg, a.offsets, a.group_rows, a.max_rows, a.d,
+                                      kg, a.h, a.dw1, a.dw3);
   const dim3 g2(((a.h + kTM - 1) / kTM) * ((a.d + kTN - 1) / kTN), a.E);
-  bwd_wgrad<<<g2, kThreads, 0, st>>>(Hbuf, a.h, dy, a.d, a.offsets, a.max_rows, a.h, a.d, a.d,
-                                     a.dw2, nullptr);
+  bwd_wgrad<<<g2, kThreads, 0, st>>>(Hbuf, a.h, dy, a.d, a.offsets, a.group_rows, a.max_rows,
+                                     a.h, a.d, a.d, a.dw2, nullptr);
   return hipGetLastError();
 }
 

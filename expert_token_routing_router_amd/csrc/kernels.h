@@ -134,6 +134,7 @@ struct FfnBackwardArgs {
   int E, max_rows, d, h, act;
   const void* x_rows;
   const int32_t* offsets;
+  const int32_t* group_rows;  // nullable: rows of each segment that hold data
   const void* w1;
   const void* w3;
   const void* w2;

@@ -459,19 +459,27 @@ int moe_permute_backward(const moe_route_desc* desc, const void* dx_perm,
 /* Backward of the expert FFN (each expert is an ordinary feed-forward block:
  * glossary "Expert Parallelism", introduction).  With the forward of
  * moe_expert_ffn, u = x W1^T, v = x W3^T, H = act(u) [* v], y = H W2^T, over
- * rows [group_offsets[e], group_offsets[e+1]) (clamped to max_rows) of expert e:
+ * rows [group_offsets[e], group_offsets[e+1]) (clamped to max_rows and, when
+ * group_rows is given, to the first group_rows[e] of them) of expert e:
  *   g   = dy W2                     (gradient at H)
  *   du  = g * act'(u) [* v]         rounded to bf16
  *   dv  = g * silu(u)               SwiGLU only, rounded to bf16
  *   dx  = du W1 [+ dv W3]           rounded to bf16, written to dx_rows
  *   dw1[e] = sum_r du^T x,  dw3[e] = sum_r dv^T x,  dw2[e] = sum_r dy^T H
- * u, v and H are recomputed (H rounded to bf16 as in the forward); products
- * run on bf16 operands with fp32 sums.  GELU is the erf form,
- * gelu'(u) = Phi(u) + u phi(u).
+ * u, v and H are recomputed and rounded to bf16 at the forward's rounding
+ * point; products run on bf16 operands with fp32 sums.  GELU is the erf form
+ * here, gelu(u) = u Phi(u) and gelu'(u) = Phi(u) + u phi(u), with Phi from the
+ * device erf, whereas the forward evaluates erf by a polynomial: a recomputed
+ * H can differ from the forward's H by one bf16 ulp.
  *
  *  x_rows, dy_rows, dx_rows [max_rows, d] bf16 (dy_rows: the gradient at
  *      y_rows, e.g. moe_combine_backward's dy_perm; rows outside every
  *      segment are neither read nor written);
+ *  group_rows [E] int32 DEVICE array, nullable: rows of each segment that
+ *      hold data.  With the capacity-padded layout pass the dispatch's
+ *      admitted: the padding rows then take no part (moe_combine_backward
+ *      leaves them unwritten in dy_perm, and moe_permute leaves them as they
+ *      were in x_perm) and the gradients equal the compact layout's;
  *  w1, w3 [E, h, d] and w2 [E, d, h] bf16, PLAIN row-major (not the packed
  *      layout of moe_expert_ffn); w3 and dw3 only for MOE_SWIGLU (NULL else);
  *  dw1, dw3 [E, h, d] and dw2 [E, d, h] fp32, fully written (zero for an
@@ -485,9 +493,10 @@ size_t moe_expert_ffn_backward_workspace_size(int32_t num_experts, int32_t max_r
                                               int32_t dtype);
 int moe_expert_ffn_backward(int32_t num_experts, int32_t max_rows, int32_t hidden,
                             int32_t ffn_hidden, int32_t act, int32_t dtype, const void* x_rows,
-                            const int32_t* group_offsets, const void* w1, const void* w3,
-                            const void* w2, const void* dy_rows, void* dx_rows, float* dw1,
-                            float* dw3, float* dw2, void* ws, size_t ws_bytes, void* stream);
+                            const int32_t* group_offsets, const int32_t* group_rows,
+                            const void* w1, const void* w3, const void* w2, const void* dy_rows,
+                            void* dx_rows, float* dw1, float* dw3, float* dw2, void* ws,
+                            size_t ws_bytes, void* stream);
 
 /* ------------------------------------------------------------ bias update -- */
 

@@ -379,9 +379,9 @@ def test_expert_ffn_backward_validation():
                                                       moe.MOE_BF16) == 0
 
     def call(E=E, M=M, d=d, h=h, act=moe.MOE_SWIGLU, dtype=moe.MOE_BF16, x=FAKE, off=FAKE,
-             w3=FAKE, dw3=FAKE, dy=FAKE, ws=FAKE, ws_bytes=need):
-        return lib.moe_expert_ffn_backward(E, M, d, h, act, dtype, x, off, FAKE, w3, FAKE, dy,
-                                           FAKE, FAKE, dw3, FAKE, ws, ws_bytes, None)
+             w3=FAKE, dw3=FAKE, dy=FAKE, ws=FAKE, ws_bytes=need, rows=None):
+        return lib.moe_expert_ffn_backward(E, M, d, h, act, dtype, x, off, rows, FAKE, w3, FAKE,
+                                           dy, FAKE, FAKE, dw3, FAKE, ws, ws_bytes, None)
 
     assert call(dtype=moe.MOE_F32) == moe.MOE_ERR_UNSUPPORTED
     assert call(d=48) == moe.MOE_ERR_UNSUPPORTED
@@ -396,6 +396,7 @@ def test_expert_ffn_backward_validation():
     assert call(act=moe.MOE_GELU) == moe.MOE_ERR_INVALID_ARG  # GELU takes neither
     assert call(x=None) == moe.MOE_ERR_INVALID_ARG
     assert call(dy=ctypes.c_void_p(0x10008)) == moe.MOE_ERR_INVALID_ARG  # misaligned
+    assert call(rows=ctypes.c_void_p(0x10002)) == moe.MOE_ERR_INVALID_ARG  # misaligned int32
     assert call(ws_bytes=need - 1) == moe.MOE_ERR_WORKSPACE
     assert call(ws=None) == moe.MOE_ERR_WORKSPACE
     assert call(ws=ctypes.c_void_p(0x10010)) == moe.MOE_ERR_WORKSPACE  # not 256-aligned

@@ -62,8 +62,8 @@ def _gpu_backward(E, rows, d, h, act, x, off, w1, w3, w2, dy, sentinel=3.0):
     dw3 = torch.full((E, h, d), 9.0, device="cuda") if sw else None
     dw2 = torch.full((E, d, h), 9.0, device="cuda")
     ws = moe.workspace(moe.moe_expert_ffn_backward_workspace_size(E, rows, d, h, act, "bf16"))
-    moe.moe_expert_ffn_backward(E, rows, d, h, act, "bf16", dev(x), dev(off), dev(w1), dev(w3),
-                                dev(w2), dev(dy), dx, dw1, dw3, dw2, ws)
+    moe.moe_expert_ffn_backward(E, rows, d, h, act, "bf16", dev(x), dev(off), None, dev(w1),
+                                dev(w3), dev(w2), dev(dy), dx, dw1, dw3, dw2, ws)
     torch.cuda.synchronize()
     return dx.cpu(), dw1.cpu(), None if dw3 is None else dw3.cpu(), dw2.cpu()
 
@@ -131,8 +131,8 @@ def test_layer_backward_chain(name):
     dw3 = torch.empty(E, h, d, device="cuda") if act == "swiglu" else None
     dw2 = torch.empty(E, d, h, device="cuda")
     ws = moe.workspace(moe.moe_expert_ffn_backward_workspace_size(E, rows, d, h, act, dt))
-    moe.moe_expert_ffn_backward(E, rows, d, h, act, dt, x_perm, off, dev(w1), dev(w3), dev(w2),
-                                dy_perm, dx_perm, dw1, dw3, dw2, ws)
+    moe.moe_expert_ffn_backward(E, rows, d, h, act, dt, x_perm, off, None, dev(w1), dev(w3),
+                                dev(w2), dy_perm, dx_perm, dw1, dw3, dw2, ws)
     dx = torch.empty(N, d, dtype=BF16, device="cuda")
     moe.moe_permute_backward(buf.desc, dx_perm, ros, dx, num_rows=rows)
     torch.cuda.synchronize()
@@ -151,6 +151,59 @@ def test_layer_backward_chain(name):
             continue
         err = rel_err(got.cpu(), torch.from_numpy(r))
         assert err <= TOL[dt], f"{key} max rel err {err:.3e}"
+
+
+@pytest.mark.parametrize("name,kw", [("zipf", dict(cf=1.0)), ("switch", {})])
+def test_ffn_backward_padded_layout_equals_compact(name, kw):
+    """The layer's backward on the capacity-padded layout, with NaN planted in
+    every padding row of x_perm and dy_perm (rows no call is obliged to write):
+    with group_rows = admitted the FFN backward leaves them out, so the weight
+    gradients and every admitted row's dx equal the compact layout's bit for
+    bit (each expert's rows, and their order, are the same in both layouts)."""
+    cfg = W.with_(W.small(name), **kw)
+    print(f"[ffn backward padded vs compact] {name} {kw}", flush=True)
+    dev = lambda t: None if t is None else t.cuda()  # noqa: E731
+    inp_cpu = W.make_inputs(cfg)
+    inp = moe.prepare_weights(cfg, {k: (dev(v) if isinstance(v, torch.Tensor) else v)
+                                    for k, v in inp_cpu.items() if k != "shared"})
+    N, d, h, E, act = cfg["N"], cfg["d"], cfg["h"], cfg["E"], cfg["act"]
+    sw = act == "swiglu"
+    g = torch.Generator().manual_seed(11)
+    dy = torch.randn(N, d, generator=g).to(BF16).cuda()
+    out = {}
+    for layout in ("compact", "padded"):
+        c = W.with_(cfg, layout=layout)
+        buf = moe.MoeBuffers(c)
+        moe.moe_forward(buf, inp)
+        rows = buf.rows
+        dy_perm = torch.full((rows, d), float("nan"), dtype=BF16, device="cuda")
+        if layout == "padded":
+            pad = buf.token_of_row[:rows] < 0
+            buf.x_perm[:rows][pad] = float("nan")
+        moe.moe_combine_backward(buf.desc, dy, buf.y_perm, buf.row_of_slot, buf.topk_w, dy_perm,
+                                 torch.empty(N, cfg["k"], device="cuda"), num_rows=rows)
+        dx_perm = torch.full((rows, d), 5.0, dtype=BF16, device="cuda")
+        dw1 = torch.empty(E, h, d, device="cuda")
+        dw3 = torch.empty(E, h, d, device="cuda") if sw else None
+        dw2 = torch.empty(E, d, h, device="cuda")
+        ws = moe.workspace(moe.moe_expert_ffn_backward_workspace_size(E, rows, d, h, act, "bf16"))
+        moe.moe_expert_ffn_backward(E, rows, d, h, act, "bf16", buf.x_perm, buf.expert_offsets,
+                                    buf.admitted if layout == "padded" else None, inp_cpu["w1"].cuda(),
+                                    dev(inp_cpu["w3"]), inp_cpu["w2"].cuda(), dy_perm, dx_perm,
+                                    dw1, dw3, dw2, ws)
+        dx = torch.empty(N, d, dtype=BF16, device="cuda")
+        moe.moe_permute_backward(buf.desc, dx_perm, buf.row_of_slot, dx, num_rows=rows)
+        torch.cuda.synchronize()
+        out[layout] = (dx.cpu(), dw1.cpu(), None if dw3 is None else dw3.cpu(), dw2.cpu(),
+                       int(buf.admitted.sum()))
+    (cdx, c1, c3, c2, cm), (pdx, p1, p3, p2, pm) = out["compact"], out["padded"]
+    assert cm == pm  # same admitted rows in both layouts
+    for a, b, key in ((c1, p1, "dw1"), (c3, p3, "dw3"), (c2, p2, "dw2")):
+        if a is None:
+            continue
+        assert bool(torch.isfinite(b).all()), f"{key}: padding rows leaked into the gradient"
+        assert torch.equal(a.view(torch.int32), b.view(torch.int32)), f"{key} differs"
+    assert torch.equal(cdx.view(torch.int16), pdx.view(torch.int16))
 
 
 def test_ffn_backward_full_switch_sampled():
