@@ -84,6 +84,7 @@ def lib():
             "oracle_combine": [I32, I32, I32, I32, P, P, P, P, P, P],
             "oracle_combine_backward": [I32, I32, I32, I32, P, P, P, P, P, P],
             "oracle_bias_update": [I32, I32, I32, P, F32, P],
+            "oracle_router_backward": [D, P, P, P, P, P, P, ctypes.c_double, P, P, P, P, P, P],
         }
         for name, args in sig.items():
             fn = getattr(L, name)
@@ -310,6 +311,28 @@ def permute_backward(dtype: str, dx_perm, row_of_slot) -> np.ndarray:
     unit weights and no residual."""
     row_of_slot = _c(row_of_slot, np.int32)
     return combine(dtype, dx_perm, row_of_slot, np.ones(row_of_slot.shape, np.float32))
+
+
+def router_backward(cfg: dict, x, w_router, z, topk_idx, dtopk_w, counts=None,
+                    aux_coef: float = 0.0, dx_in=None) -> dict:
+    """Gradients of the router (and of the auxiliary load-balancing loss with
+    coefficient aux_coef): dz [N,E] fp32, dw_router [E,d] fp32, db [E] fp32,
+    dx [N,d] in the dtype (dx_in added when given), aux_loss (float)."""
+    N, d, E, k = cfg["N"], cfg["d"], cfg["E"], cfg["k"]
+    et = _elem_dtype(cfg["dtype"])
+    desc = _desc(cfg)
+    dz = np.zeros((N, E), np.float32)
+    dw = np.zeros((E, d), np.float32)
+    db = np.zeros(E, np.float32)
+    dx = np.zeros((N, d), et)
+    loss = ctypes.c_double(0.0)
+    cnt = _c(counts, np.int32)
+    _check(lib().oracle_router_backward(
+        ctypes.byref(desc), _ptr(_c(x, et)), _ptr(_c(w_router, et)), _ptr(_c(z, np.float32)),
+        _ptr(_c(topk_idx, np.int32)), _ptr(_c(dtopk_w, np.float32)), _ptr(cnt),
+        float(aux_coef), _ptr(_c(dx_in, et)), _ptr(dz), _ptr(dw), _ptr(db), _ptr(dx),
+        ctypes.byref(loss)), "oracle_router_backward")
+    return {"dz": dz, "dw_router": dw, "db": db, "dx": dx, "aux_loss": loss.value}
 
 
 def bias_update(num_tokens: int, top_k: int, counts, sel_bias, step: float = 1e-3):

@@ -760,6 +760,159 @@ int oracle_combine_backward(int32_t num_tokens, int32_t hidden, int32_t top_k, i
   return 0;
 }
 
+/* ------------------------------------------------------- router backward -- */
+
+/* Backward of the router (the training step reads step 1 of [EP-glossary] "How
+ * tokens travel between GPUs" backwards) plus an auxiliary load-balancing loss
+ * ([EP-glossary] "Load balancing and capacity", auxiliary-loss bullet; [MLSys
+ * ch.10] 10.5 names it for GShard; the pages give no formula).
+ *
+ * Given the router logits z [N,E], the selection topk_idx [N,k] and the
+ * gradient dtopk_w [N,k] of the loss at the combine weights, per token:
+ *  - softmax over the k selected (score_fn 0): w_j = e^{z_j} / sum_sel e^{z};
+ *    dz at selected expert e_j = w_j (g_j - sum_i w_i g_i), 0 elsewhere;
+ *  - softmax over all E (score_fn 1): p = softmax(z), w_j = p_{e_j};
+ *    dz_e = p_e (G_e - sum_j p_{e_j} g_j), G_e = g_j if e = e_j else 0;
+ *  - sigmoid renormalised (score_fn 2): a = 1/(1+e^{-z}), S = sum_sel a,
+ *    w_j = a_j / S; dz at e_j = a_j (1 - a_j) (g_j - sum_i w_i g_i) / S.
+ * The selection (top-k, group limit, selection bias) is piecewise constant in
+ * z: it passes no gradient.  Dropped slots arrive with g = 0.
+ *
+ * Auxiliary loss (reading: the load-balancing loss of the Switch Transformer,
+ * generalised to k slots): L = coef * E * sum_e f_e P_e with f_e = counts_e /
+ * (N k) (the fraction of assignments routed to e, a constant) and P_e the mean
+ * over tokens of the token's router distribution: softmax(z) for the softmax
+ * score functions, a_e / sum_all a for the sigmoid one.  Its gradient adds
+ *   coef E / N * P_e' (f_e' - sum_e f_e P_e)                 (softmax)
+ *   coef E / N * a_e'(1 - a_e') (f_e' - sum_e f_e P_e) / A   (sigmoid, A = sum a)
+ * to dz[t, e'].  coef = 0: no auxiliary loss (aux_loss = 0).
+ *
+ * Through the router z = x W_r^T + b:  dW_r[e] = sum_t dz[t,e] x[t],
+ * db[e] = sum_t dz[t,e], dx[t] = sum_e dz[t,e] W_r[e] (plus dx_in[t] when
+ * given: the rest of the layer's input gradient, so one rounding covers both).
+ * Everything in fp64; dz, dW_r, db rounded once to fp32, dx to the dtype. */
+int oracle_router_backward(const oracle_desc* desc, const void* x, const void* w_router,
+                           const float* z, const int32_t* topk_idx, const float* dtopk_w,
+                           const int32_t* counts, double aux_coef, const void* dx_in,
+                           float* dz_out, float* dw_router, float* db, void* dx,
+                           double* aux_loss) {
+  if (!desc_ok(desc) || !dz_out || !dw_router || !aux_loss) return -1;
+  const int32_t N = desc->num_tokens, d = desc->hidden, E = desc->num_experts;
+  const int32_t k = desc->top_k, sf = desc->score_fn;
+  if (N > 0 && (!x || !w_router || !z || !topk_idx || !dtopk_w || !dx)) return -1;
+  if (aux_coef != 0.0 && !counts) return -1;
+  for (size_t i = 0; i < (size_t)N * k; ++i)
+    if (topk_idx[i] < 0 || topk_idx[i] >= E) return -1;
+  double* dz = (double*)calloc((size_t)N * E + 1, sizeof(double));
+  double* pbar = (double*)calloc((size_t)E + 1, sizeof(double));
+  double* f = (double*)calloc((size_t)E + 1, sizeof(double));
+  double* p = (double*)malloc(sizeof(double) * ((size_t)E + 1));
+  double* w = (double*)malloc(sizeof(double) * ((size_t)k + 1));
+  if (!dz || !pbar || !f || !p || !w) {
+    free(dz); free(pbar); free(f); free(p); free(w);
+    return -1;
+  }
+  if (aux_coef != 0.0 && N > 0)
+    for (int32_t e = 0; e < E; ++e) f[e] = (double)counts[e] / ((double)N * k);
+
+  for (int32_t t = 0; t < N; ++t) {
+    const float* zt = z + (size_t)t * E;
+    const int32_t* idx = topk_idx + (size_t)t * k;
+    const float* g = dtopk_w + (size_t)t * k;
+    double* dzt = dz + (size_t)t * E;
+    /* the token's router distribution over all E (aux loss; softmax-all weights) */
+    double A = 0.0;
+    if (sf == 2) {
+      for (int32_t e = 0; e < E; ++e) {
+        p[e] = 1.0 / (1.0 + exp(-(double)zt[e]));
+        A += p[e];
+      }
+    } else {
+      double zmax = -INFINITY;
+      for (int32_t e = 0; e < E; ++e) zmax = fmax(zmax, (double)zt[e]);
+      for (int32_t e = 0; e < E; ++e) {
+        p[e] = exp((double)zt[e] - zmax);
+        A += p[e];
+      }
+      for (int32_t e = 0; e < E; ++e) p[e] /= A;
+    }
+    /* weights part */
+    if (sf == 0) {
+      double zmax = -INFINITY, sum = 0.0, wg = 0.0;
+      for (int32_t j = 0; j < k; ++j) zmax = fmax(zmax, (double)zt[idx[j]]);
+      for (int32_t j = 0; j < k; ++j) sum += exp((double)zt[idx[j]] - zmax);
+      for (int32_t j = 0; j < k; ++j) {
+        w[j] = exp((double)zt[idx[j]] - zmax) / sum;
+        wg += w[j] * (double)g[j];
+      }
+      for (int32_t j = 0; j < k; ++j) dzt[idx[j]] += w[j] * ((double)g[j] - wg);
+    } else if (sf == 1) {
+      double pg = 0.0;
+      for (int32_t j = 0; j < k; ++j) pg += p[idx[j]] * (double)g[j];
+      for (int32_t e = 0; e < E; ++e) dzt[e] += -p[e] * pg;
+      for (int32_t j = 0; j < k; ++j) dzt[idx[j]] += p[idx[j]] * (double)g[j];
+    } else {
+      double S = 0.0, wg = 0.0;
+      for (int32_t j = 0; j < k; ++j) S += p[idx[j]];
+      for (int32_t j = 0; j < k; ++j) wg += p[idx[j]] / S * (double)g[j];
+      for (int32_t j = 0; j < k; ++j) {
+        const double a = p[idx[j]];
+        dzt[idx[j]] += a * (1.0 - a) * ((double)g[j] - wg) / S;
+      }
+    }
+    /* auxiliary loss part */
+    if (aux_coef != 0.0) {
+      double fp = 0.0;
+      const double scale = aux_coef * (double)E / (double)N;
+      if (sf == 2) {
+        for (int32_t e = 0; e < E; ++e) fp += f[e] * p[e] / A;
+        for (int32_t e = 0; e < E; ++e) {
+          pbar[e] += p[e] / A;
+          dzt[e] += scale * p[e] * (1.0 - p[e]) * (f[e] - fp) / A;
+        }
+      } else {
+        for (int32_t e = 0; e < E; ++e) fp += f[e] * p[e];
+        for (int32_t e = 0; e < E; ++e) {
+          pbar[e] += p[e];
+          dzt[e] += scale * p[e] * (f[e] - fp);
+        }
+      }
+    }
+  }
+  double loss = 0.0;
+  if (aux_coef != 0.0 && N > 0)
+    for (int32_t e = 0; e < E; ++e) loss += f[e] * (pbar[e] / (double)N);
+  *aux_loss = aux_coef * (double)E * loss;
+
+  for (size_t i = 0; i < (size_t)N * E; ++i) dz_out[i] = (float)dz[i];
+  /* dW_r and db: sums over tokens in order */
+  for (int32_t e = 0; e < E; ++e) {
+    double be = 0.0;
+    for (int32_t t = 0; t < N; ++t) be += dz[(size_t)t * E + e];
+    if (db) db[e] = (float)be;
+  }
+#pragma omp parallel for num_threads(g_threads) schedule(static)
+  for (int32_t e = 0; e < E; ++e) {
+    for (int32_t i = 0; i < d; ++i) {
+      double acc = 0.0;
+      for (int32_t t = 0; t < N; ++t)
+        acc += dz[(size_t)t * E + e] * elem(x, desc->dtype, (size_t)t * d + i);
+      dw_router[(size_t)e * d + i] = (float)acc;
+    }
+  }
+#pragma omp parallel for num_threads(g_threads) schedule(static)
+  for (int32_t t = 0; t < N; ++t) {
+    for (int32_t i = 0; i < d; ++i) {
+      double acc = dx_in ? elem(dx_in, desc->dtype, (size_t)t * d + i) : 0.0;
+      for (int32_t e = 0; e < E; ++e)
+        acc += dz[(size_t)t * E + e] * elem(w_router, desc->dtype, (size_t)e * d + i);
+      store(dx, desc->dtype, (size_t)t * d + i, acc);
+    }
+  }
+  free(dz); free(pbar); free(f); free(p); free(w);
+  return 0;
+}
+
 /* ------------------------------------------------------------ bias update -- */
 
 /* Bias-based balancing: after each step the bias of overloaded experts goes

@@ -157,6 +157,17 @@ int oracle_combine_backward(int32_t num_tokens, int32_t hidden, int32_t top_k, i
 int oracle_bias_update(int32_t num_experts, int32_t num_tokens, int32_t top_k,
                        const int32_t* counts, float step, float* sel_bias);
 
+/* Backward of the router and of an auxiliary load-balancing loss (see
+ * oracle.c): from the logits z, the selection and dtopk_w, the gradient dz at
+ * the logits (fp32 out), dW_r [E,d] and db [E] (fp32; db nullable), the
+ * router's input gradient dx [N,d] in the dtype (plus dx_in when not NULL),
+ * and the loss coef * E * sum_e f_e P_e in *aux_loss (coef 0: none). */
+int oracle_router_backward(const oracle_desc* desc, const void* x, const void* w_router,
+                           const float* z, const int32_t* topk_idx, const float* dtopk_w,
+                           const int32_t* counts, double aux_coef, const void* dx_in,
+                           float* dz_out, float* dw_router, float* db, void* dx,
+                           double* aux_loss);
+
 /* Capacity for a descriptor (INT32_MAX when unlimited). */
 int64_t oracle_capacity(const oracle_desc* desc);
 
