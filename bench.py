@@ -547,6 +547,34 @@ def backward_pass(moe, torch, buf, inp, steps: int) -> dict:
     frac = lambda nb, us: round(nb / (us * 1e-6) / (HBM_PEAK_GBS * 1e9), 4)  # noqa: E731
     out = {"combine_backward": {"us": round(cb, 2), "hbm_frac": frac(cb_bytes, cb)},
            "permute_backward": {"us": round(pb, 2), "hbm_frac": frac(pb_bytes, pb)}}
+    # Router backward from the combine backward's weight gradients, with the
+    # auxiliary load-balancing loss, adding the router's term into dx.
+    E = d.num_experts
+    dl = torch.empty(N, E, device=dev)
+    dwr = torch.empty(E, dim, device=dev)
+    dbr = torch.empty(E, device=dev)
+    loss = torch.empty(1, device=dev)
+    rws = moe.workspace(moe.moe_router_backward_workspace_size(d), dev)
+
+    def router_bwd():
+        moe.moe_router_backward(d, inp["x"], inp["w_router"], buf.logits, buf.topk_idx, dw,
+                                buf.counts, 0.01, dl, dwr, dbr, dx, True, loss, rws)
+
+    for _ in range(2):
+        router_bwd()
+    torch.cuda.synchronize()
+    rb = 0.0
+    for _ in range(steps):
+        ev[0].record()
+        router_bwd()
+        ev[1].record()
+        torch.cuda.synchronize()
+        rb += ev[0].elapsed_time(ev[1])
+    rb = rb / steps * 1e3
+    # two contractions of N x E x d (dW_r and dx), plus the logits pass
+    rflops = 2.0 * 2 * N * E * dim
+    out["router_backward"] = {"us": round(rb, 2), "tflops": round(rflops / (rb * 1e-6) / 1e12, 2),
+                              "aux_loss": round(float(loss.item()), 6)}
     cfg = buf.cfg
     if cfg["dtype"] != "bf16":
         return out

@@ -44,7 +44,8 @@ EXPORTS = [
     "moe_expert_ffn_backward_workspace_size", "moe_expert_ffn_backward",
     "moe_expert_ffn_workspace_size", "moe_expert_ffn", "moe_expert_ffn_plan",
     "moe_expert_ffn_up", "moe_expert_ffn_down", "moe_expert_ffn_pack_weights", "moe_combine",
-    "moe_bias_update", "moe_status_string",
+    "moe_bias_update", "moe_status_string", "moe_router_backward_workspace_size",
+    "moe_router_backward",
 ]
 
 
@@ -152,6 +153,8 @@ def lib() -> ctypes.CDLL:
             "moe_combine": ([D, P, P, P, P, P, P, P, P], I32),
             "moe_bias_update": ([I32, I32, I32, P, F32, P, P], I32),
             "moe_status_string": ([I32], ctypes.c_char_p),
+            "moe_router_backward_workspace_size": ([D], SZ),
+            "moe_router_backward": ([D, P, P, P, P, P, P, F32, P, P, P, P, I32, P, P, SZ, P], I32),
         }
         for name, (args, res) in sigs.items():
             fn = getattr(L, name)
@@ -568,6 +571,34 @@ def moe_expert_ffn_backward(num_experts, max_rows, hidden, ffn_hidden, act, dtyp
         _ptr(ws, "ws", None, None, False), 0 if ws is None else ws.numel() * ws.element_size(),
         _stream(stream))
     _raise("moe_expert_ffn_backward", st)
+
+
+def moe_router_backward_workspace_size(desc: RouteDesc) -> int:
+    return int(lib().moe_router_backward_workspace_size(ctypes.byref(desc)))
+
+
+def moe_router_backward(desc, x, w_router, logits, topk_idx, dtopk_w, counts, aux_coef, dlogits,
+                        dw_router, drouter_bias, dx, accumulate_dx, aux_loss, ws, stream=None):
+    """Gradients of the router and of the auxiliary load-balancing loss
+    (include/moe.h): dlogits [N,E] (nullable), dw_router [E,d] fp32,
+    drouter_bias [E] (nullable), dx [N,d] (nullable; added to when
+    accumulate_dx), aux_loss one-element fp32 tensor (nullable)."""
+    N, d, E, k = desc.num_tokens, desc.hidden, desc.num_experts, desc.top_k
+    dt = TORCH_DTYPE.get(desc.dtype)
+    f32 = torch.float32
+    st = lib().moe_router_backward(
+        ctypes.byref(desc), _ptr(x, "x", dt, N * d, N > 0),
+        _ptr(w_router, "w_router", dt, E * d, N > 0),
+        _ptr(logits, "logits", f32, N * E, N > 0),
+        _ptr(topk_idx, "topk_idx", torch.int32, N * k, N > 0),
+        _ptr(dtopk_w, "dtopk_w", f32, N * k, N > 0),
+        _ptr(counts, "counts", torch.int32, E, bool(aux_coef)), float(aux_coef),
+        _ptr(dlogits, "dlogits", f32, N * E, False), _ptr(dw_router, "dw_router", f32, E * d),
+        _ptr(drouter_bias, "drouter_bias", f32, E, False), _ptr(dx, "dx", dt, N * d, False),
+        int(bool(accumulate_dx)), _ptr(aux_loss, "aux_loss", f32, 1, False),
+        _ptr(ws, "ws", None, None, False), 0 if ws is None else ws.numel() * ws.element_size(),
+        _stream(stream))
+    _raise("moe_router_backward", st)
 
 
 def moe_bias_update(num_experts, num_tokens, top_k, counts, step, sel_bias, stream=None):

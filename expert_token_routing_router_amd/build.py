@@ -10,7 +10,7 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(PKG, "csrc")
 LIB = os.path.join(PKG, "libmoe_mi355x.so")
 SOURCES = ["api.hip", "route.hip", "route_mfma.hip", "dispatch.hip", "ffn.hip", "combine.hip",
-           "backward.hip", "backward_ffn.hip"]
+           "backward.hip", "backward_ffn.hip", "router_backward.hip"]
 ARCH = "gfx950"
 
 HIPCC_FLAGS = [

@@ -551,6 +551,38 @@ int moe_permute_backward(const moe_route_desc* desc, const void* dx_perm,
                                                 static_cast<hipStream_t>(stream)));
 }
 
+size_t moe_router_backward_workspace_size(const moe_route_desc* desc) {
+  if (check_desc(desc) != MOE_OK) return 0;
+  return moe::router_backward_workspace_bytes(desc->num_tokens, desc->hidden, desc->num_experts);
+}
+
+int moe_router_backward(const moe_route_desc* desc, const void* x, const void* w_router,
+                        const float* logits, const int32_t* topk_idx, const float* dtopk_w,
+                        const int32_t* counts, float aux_coef, float* dlogits, float* dw_router,
+                        float* drouter_bias, void* dx, int32_t accumulate_dx, float* aux_loss,
+                        void* ws, size_t ws_bytes, void* stream) {
+  int st = check_desc(desc);
+  if (st != MOE_OK) return st;
+  if (!isfinite(aux_coef)) return MOE_ERR_INVALID_ARG;
+  if (!dw_router || (aux_coef != 0.f && !counts)) return MOE_ERR_INVALID_ARG;
+  const int N = desc->num_tokens;
+  const auto al4 = [](const void* p) { return (reinterpret_cast<uintptr_t>(p) & 3u) == 0; };
+  if (!al4(dw_router) || !al4(drouter_bias) || !al4(aux_loss) || !al4(dlogits) || !al4(counts))
+    return MOE_ERR_INVALID_ARG;
+  if (N > 0) {
+    if (!x || !w_router || !logits || !topk_idx || !dtopk_w) return MOE_ERR_INVALID_ARG;
+    if (!al4(logits) || !al4(topk_idx) || !al4(dtopk_w) || (dx && !aligned16(dx)))
+      return MOE_ERR_INVALID_ARG;
+    const size_t need = moe::router_backward_workspace_bytes(N, desc->hidden, desc->num_experts);
+    if (!ws || ws_bytes < need || (reinterpret_cast<uintptr_t>(ws) & 255u)) return MOE_ERR_WORKSPACE;
+  }
+  moe::RouterBackwardArgs a{N, desc->hidden, desc->num_experts, desc->top_k, desc->score_fn,
+                            desc->dtype, x, w_router, logits, topk_idx, dtopk_w, counts,
+                            aux_coef, dlogits, dw_router, drouter_bias, dx,
+                            accumulate_dx ? 1 : 0, aux_loss, ws};
+  return status_of(moe::launch_router_backward(a, static_cast<hipStream_t>(stream)));
+}
+
 int moe_bias_update(int32_t num_experts, int32_t num_tokens, int32_t top_k,
                     const int32_t* counts, float step, float* sel_bias, void* stream) {
   if (num_experts < 1 || num_tokens < 0 || top_k < 1 || !counts || !sel_bias)

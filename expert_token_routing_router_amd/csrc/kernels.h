@@ -152,4 +152,26 @@ hipError_t launch_ffn_backward(const FfnBackwardArgs& a, hipStream_t st);
 hipError_t launch_bias_update(int E, int N, int k, const int32_t* counts, float step,
                               float* sel_bias, hipStream_t st);
 
+// Backward of the router and of the auxiliary load-balancing loss
+// (router_backward.hip).
+struct RouterBackwardArgs {
+  int N, d, E, k, score_fn, dtype;
+  const void* x;
+  const void* w_router;
+  const float* logits;
+  const int32_t* topk_idx;
+  const float* dtopk_w;
+  const int32_t* counts;  // needed when aux_coef != 0
+  float aux_coef;
+  float* dlogits;         // nullable: then dz lives in ws
+  float* dw_router;
+  float* db;              // nullable
+  void* dx;               // nullable
+  int accumulate_dx;
+  float* aux_loss;        // nullable
+  void* ws;
+};
+size_t router_backward_workspace_bytes(int N, int d, int E);
+hipError_t launch_router_backward(const RouterBackwardArgs& a, hipStream_t st);
+
 }  // namespace moe

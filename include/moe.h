@@ -498,6 +498,43 @@ int moe_expert_ffn_backward(int32_t num_experts, int32_t max_rows, int32_t hidde
                             void* dx_rows, float* dw1, float* dw3, float* dw2, void* ws,
                             size_t ws_bytes, void* stream);
 
+/* Backward of the router (glossary "How tokens travel between GPUs", step 1,
+ * read backwards: the router's logits decide the combine weights) and of an
+ * auxiliary load-balancing loss (glossary "Load balancing and capacity",
+ * auxiliary-loss bullet; MLSys ch.10 section 10.5 names it for GShard).  The
+ * pages give the loss no formula; it is taken as the Switch Transformer's,
+ * for k slots:
+ *   L = aux_coef * E * sum_e f_e P_e,  f_e = counts[e] / (N k)  (a constant),
+ *   P_e = mean over tokens of the token's router distribution over all E
+ *         (softmax of z; SIGMOID_NORM: sigmoid(z) / sum over all E of sigmoid(z)).
+ * From the logits z, the selection topk_idx and dtopk_w (the gradient at the
+ * combine weights, moe_combine_backward's output; dropped slots carry 0):
+ *   dz[t, e]  gradient at the logits: through the score function at the
+ *             selected experts (the selection itself, incl. group limit and
+ *             selection bias, passes no gradient) plus the loss's term
+ *   dw_router = dz^T x,  drouter_bias = sum over tokens of dz  (fp32)
+ *   dx[t]     = sum_e dz[t, e] w_router[e]  (+ dx[t] when accumulate_dx: the
+ *             rest of the layer's input gradient; rounded once to dtype)
+ * fp32 arithmetic; the loss is summed in fp64 in a fixed order.
+ *
+ *  x [N, d] dtype, w_router [E, d] dtype, logits [N, E] fp32 (moe_route's, or
+ *  moe_router_logits'), topk_idx [N, k] int32, dtopk_w [N, k] fp32,
+ *  counts [E] int32 (pre-capacity, moe_route's; needed when aux_coef != 0),
+ *  aux_coef  finite; 0 = no auxiliary loss,
+ *  dlogits [N, E] fp32 out, nullable;  dw_router [E, d] fp32 out;
+ *  drouter_bias [E] fp32 out, nullable;  dx [N, d] dtype (in/)out, nullable,
+ *  16-byte aligned;  aux_loss: one fp32 DEVICE value out, nullable;
+ *  ws, ws_bytes >= moe_router_backward_workspace_size (0 when N == 0).
+ * With N == 0 the gradients are zero and the loss 0.  Errors:
+ * MOE_ERR_INVALID_ARG (descriptor, missing or misaligned buffers, counts
+ * missing with aux_coef != 0, a non-finite aux_coef), MOE_ERR_WORKSPACE. */
+size_t moe_router_backward_workspace_size(const moe_route_desc* desc);
+int moe_router_backward(const moe_route_desc* desc, const void* x, const void* w_router,
+                        const float* logits, const int32_t* topk_idx, const float* dtopk_w,
+                        const int32_t* counts, float aux_coef, float* dlogits, float* dw_router,
+                        float* drouter_bias, void* dx, int32_t accumulate_dx, float* aux_loss,
+                        void* ws, size_t ws_bytes, void* stream);
+
 /* ------------------------------------------------------------ bias update -- */
 
 /* Selection-bias update.  Glossary "Load balancing and capacity", bias-based
