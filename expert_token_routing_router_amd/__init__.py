@@ -21,7 +21,9 @@ import os
 import torch
 
 PKG_DIR = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(PKG_DIR, "libmoe_mi355x.so")
+# MOE_MI355X_LIB names another build of the same library (e.g. one whose host
+# code is compiled with sanitizers); the default is the in-tree build.
+LIB_PATH = os.environ.get("MOE_MI355X_LIB") or os.path.join(PKG_DIR, "libmoe_mi355x.so")
 
 MOE_OK, MOE_ERR_INVALID_ARG, MOE_ERR_UNSUPPORTED, MOE_ERR_HIP, MOE_ERR_WORKSPACE = range(5)
 MOE_F32, MOE_BF16 = 0, 1

@@ -26,10 +26,21 @@ def hipcc() -> str:
     return cand if os.path.exists(cand) else "hipcc"
 
 
-def build(verbose: bool = False) -> str:
+# Host code only under AddressSanitizer and UndefinedBehaviorSanitizer (the
+# device code is built as usual); load the result with the sanitizer runtime
+# preloaded (clang's, the one hipcc links against).
+SANITIZE_FLAGS = ["-Xarch_host", "-fsanitize=address", "-Xarch_host", "-fsanitize=undefined",
+                  "-Xarch_host", "-fno-sanitize-recover=all", "-Xarch_host",
+                  "-fno-omit-frame-pointer", "-shared-libsan", "-g"]
+
+
+def build(verbose: bool = False, out: str = LIB, sanitize: bool = False) -> str:
     srcs = [os.path.join(CSRC, s) for s in SOURCES]
-    tmp = LIB + ".tmp"
-    cmd = [hipcc(), *HIPCC_FLAGS, "-I", os.path.join(PKG, "..", "include"), "-o", tmp, *srcs]
+    tmp = out + ".tmp"
+    flags = [f for f in HIPCC_FLAGS if not (sanitize and f == "-O3")]
+    if sanitize:
+        flags = ["-O1", *flags, *SANITIZE_FLAGS]
+    cmd = [hipcc(), *flags, "-I", os.path.join(PKG, "..", "include"), "-o", tmp, *srcs]
     res = subprocess.run(cmd, cwd=CSRC, capture_output=True, text=True)
     noise = "is not a recognized feature for this target"
     err = "\n".join(l for l in res.stderr.splitlines() if noise not in l)
@@ -37,8 +48,8 @@ def build(verbose: bool = False) -> str:
         raise RuntimeError(f"hipcc failed ({res.returncode}):\n{err}")
     if verbose and err.strip():
         print(err, file=sys.stderr)
-    os.replace(tmp, LIB)
-    return LIB
+    os.replace(tmp, out)
+    return out
 
 
 if __name__ == "__main__":

@@ -24,7 +24,10 @@ import subprocess
 import numpy as np
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_HERE, "liboracle.so")
+# ORACLE_LIB names another build of the same C file (e.g. one compiled with
+# sanitizers); the default is the in-tree build.
+DEFAULT_LIB = os.path.join(_HERE, "liboracle.so")
+LIB_PATH = os.environ.get("ORACLE_LIB") or DEFAULT_LIB
 SRC_PATH = os.path.join(_HERE, "oracle.c")
 
 SCORE_CODES = {"softmax_topk": 0, "softmax_all": 1, "sigmoid_norm": 2}
@@ -32,14 +35,18 @@ ACT_CODES = {"relu": 0, "gelu": 1, "swiglu": 2}
 DTYPE_CODES = {"fp32": 0, "bf16": 1}
 
 
-def build() -> str:
-    """Compile ``liboracle.so`` with gcc (strict IEEE: no contraction, no fast-math)."""
+def build(out: str = DEFAULT_LIB, sanitize: bool = False) -> str:
+    """Compile the oracle with gcc (strict IEEE: no contraction, no fast-math)
+    into ``out``; with ``sanitize`` under AddressSanitizer and
+    UndefinedBehaviorSanitizer (abort on the first report)."""
+    san = (["-O1", "-g", "-fsanitize=address,undefined", "-fno-sanitize-recover=all",
+            "-fno-omit-frame-pointer"] if sanitize else ["-O2"])
     cmd = [
-        "gcc", "-O2", "-std=c11", "-Wall", "-Wextra", "-fPIC", "-shared", "-fopenmp",
-        "-ffp-contract=off", "-fno-fast-math", "-o", LIB_PATH, SRC_PATH, "-lm",
+        "gcc", *san, "-std=c11", "-Wall", "-Wextra", "-fPIC", "-shared", "-fopenmp",
+        "-ffp-contract=off", "-fno-fast-math", "-o", out, SRC_PATH, "-lm",
     ]
     subprocess.run(cmd, check=True)
-    return LIB_PATH
+    return out
 
 
 class _Desc(ctypes.Structure):
@@ -64,6 +71,8 @@ def lib():
     global _lib
     if _lib is None:
         if not os.path.exists(LIB_PATH):
+            if LIB_PATH != DEFAULT_LIB:
+                raise RuntimeError(f"{LIB_PATH} (ORACLE_LIB) does not exist")
             build()
         L = ctypes.CDLL(LIB_PATH)
         P, I32, F32 = ctypes.c_void_p, ctypes.c_int32, ctypes.c_float
