@@ -66,6 +66,10 @@ def parse_args(argv=None):
                          "fused: the down GEMM scatter-adds w*O into an fp32 accumulator "
                          "that moe_combine finishes")
     ap.add_argument("--no-clocks", action="store_true", help="skip reading the clocks")
+    ap.add_argument("--graph", action="store_true",
+                    help="replay the step captured once in a HIP graph instead of launching "
+                         "every call from the host (measured: no faster; launches overlap "
+                         "the GPU work either way)")
     ap.add_argument("--backward", action="store_true",
                     help="also time the layer's backward calls on this workload's layout")
     ap.add_argument("--rank-share", action="store_true",
@@ -197,7 +201,7 @@ class LayerRun:
 
     def step(self, events=None, shared_events=None):
         """One layer step.  A shared expert (needs only x) is forked onto a side
-        stream at the start and joined before the combine, as the layer's
+        stream after the route and joined before the combine, as the layer's
         forward does, timed by its own pair of events on that stream."""
         moe, layer, buf, cfg, inp, wts = (self.moe, self.layer, self.buf, self.cfg, self.inp,
                                           self.wts)
@@ -211,6 +215,8 @@ class LayerRun:
             if events is not None:
                 next(marks).record(main)
 
+        mark()
+        layer.route(buf, inp)
         if self.fork:
             buf.side_stream.wait_stream(main)
             if shared_events is not None:
@@ -218,8 +224,6 @@ class LayerRun:
             layer.shared_ffn(buf, wts, buf.side_stream)
             if shared_events is not None:
                 shared_events[1].record(buf.side_stream)
-        mark()
-        layer.route(buf, inp)
         mark()
         if self.padded:
             layer.dispatch(buf, inp)
@@ -256,6 +260,29 @@ class LayerRun:
 
     def n_events(self):
         return len(self.calls) + 1
+
+    def capture(self):
+        """Capture one step (every launch, the shared expert's fork and join)
+        in a HIP graph; afterwards replay() runs that step.  Warm-up on the
+        capture stream first, as torch's capture requires."""
+        torch = self.torch
+        side = torch.cuda.Stream()
+        side.wait_stream(self.main)
+        with torch.cuda.stream(side):
+            self.main = side
+            self.step()
+        self.main = torch.cuda.current_stream()
+        self.main.wait_stream(side)
+        torch.cuda.synchronize()
+        self.graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(self.graph):
+            self.main = torch.cuda.current_stream()
+            self.step()
+        self.main = torch.cuda.current_stream()
+        torch.cuda.synchronize()
+
+    def replay(self):
+        self.graph.replay()
 
     def algorithmic(self) -> dict:
         """Algorithmic work of this batch per call, from the rows actually
@@ -301,17 +328,19 @@ class LayerRun:
         return out
 
 
-def time_steps(run, steps):
+def time_steps(run, steps, graph=False):
     """Exactly `steps` steps between two synchronisations (one GPU, so no
     barrier is needed beyond that); the step time is the larger of the HIP-event
-    and the host wall time of the region."""
+    and the host wall time of the region.  graph: each step is one replay of
+    the captured step."""
     torch = run.torch
     edge = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+    one = run.replay if graph else run.step
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     edge[0].record()
     for _ in range(steps):
-        run.step()
+        one()
     edge[1].record()
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
@@ -417,16 +446,18 @@ def load_metrics(run) -> dict:
     return out
 
 
-def quick_workload(name, steps, warmup, dev) -> dict:
+def quick_workload(name, steps, warmup, dev, graph=False) -> dict:
     """A short pass over another workload: step time and the per-call
     durations with their roofline fractions (no cold pass, no oracle)."""
     import moe_workloads as W
 
     cfg = W.full(name)
     run = LayerRun(cfg, dev)
+    if graph:
+        run.capture()
     for _ in range(warmup):
-        run.step()
-    ms, _, _ = time_steps(run, steps)
+        run.replay() if graph else run.step()
+    ms, _, _ = time_steps(run, steps, graph)
     per, _ = per_call_pass(run, steps)
     alg = run.algorithmic()
     kern = kernel_table(run, alg, per)
@@ -710,12 +741,16 @@ def main(argv=None):
         cfg["combine"] = args.combine
     run = LayerRun(cfg, dev)
     N = cfg["N"]
+    graph = args.graph
+    if graph:
+        run.capture()  # two untimed steps: the capture stream's warm-up and the capture
+    one = run.replay if graph else run.step
 
     for _ in range(args.warmup):
-        run.step()
+        one()
     torch.cuda.synchronize()
     # Timed region: exactly K steps.
-    ms_per_step, gpu_ms, wall = time_steps(run, args.steps)
+    ms_per_step, gpu_ms, wall = time_steps(run, args.steps, graph)
     value = N / (ms_per_step * 1e-3)
 
     per_call, instrumented_ms = per_call_pass(run, args.steps)
@@ -726,7 +761,7 @@ def main(argv=None):
     torch.cuda.synchronize()
     marks[0].record()
     for s in range(args.steps):
-        run.step()
+        one()
         marks[s + 1].record()
     torch.cuda.synchronize()
     step_ms = sorted(marks[s].elapsed_time(marks[s + 1]) for s in range(args.steps))
@@ -817,7 +852,9 @@ def main(argv=None):
         "cold": cold,
         "platform": {"hip": torch.version.hip, "torch": torch.__version__,
                      "device": torch.cuda.get_device_name(0), **clocks},
-        "timed_region": {"gpu_events_ms": round(gpu_ms, 3), "host_wall_ms": round(wall * 1e3, 3)},
+        "timed_region": {"gpu_events_ms": round(gpu_ms, 3), "host_wall_ms": round(wall * 1e3, 3),
+                         "launch": "HIP graph replay of the captured step" if graph
+                         else "eager launches"},
         "kernel_sources_digest": digest,
     }
     if args.rank_share:
@@ -846,7 +883,8 @@ def main(argv=None):
         for w in extras:
             if w == args.workload or w not in WORKLOADS:
                 continue
-            out["other_workloads"][w] = quick_workload(w, args.extra_steps, 10, dev)
+            out["other_workloads"][w] = quick_workload(w, args.extra_steps, 10, dev,
+                                                       args.graph)
     if host is not None:
         cb = cpu_baseline(cfg, host, args.cpu_seconds)
         cb["gpu_speedup"] = round(value / cb["value"], 1)
