@@ -143,6 +143,47 @@ __device__ __forceinline__ void wait_vmcnt() {
   __builtin_amdgcn_s_waitcnt(0x0F70 | (N & 15) | (((N >> 4) & 3) << 14));
 }
 
+// s_waitcnt lgkmcnt(0): this wave's LDS reads (and scalar loads) have
+// returned; vmcnt 63 and expcnt 7 mean "no wait".
+__device__ __forceinline__ void wait_lgkmcnt0() { __builtin_amdgcn_s_waitcnt(0xC07F); }
+
+// Wait until at most `later` groups of PER loads each are still in flight
+// (later <= 7; the ring's static checks keep 7 * PER below the 6-bit limit
+// where it is reached, the clamp only keeps the unused cases compiling).
+template <int PER>
+__device__ __forceinline__ void wait_stages(int later) {
+#define MOE_WS(n) wait_vmcnt<((n) * PER < 63 ? (n) * PER : 63)>()
+  switch (later) {
+    case 0: MOE_WS(0); break;
+    case 1: MOE_WS(1); break;
+    case 2: MOE_WS(2); break;
+    case 3: MOE_WS(3); break;
+    case 4: MOE_WS(4); break;
+    case 5: MOE_WS(5); break;
+    case 6: MOE_WS(6); break;
+    default: MOE_WS(7); break;
+  }
+#undef MOE_WS
+}
+
+// Buffer resource over `bytes` bytes from `base` (gfx9 descriptor: stride 0,
+// so offsets are raw bytes; word 3 = 32-bit data format, which raw dword
+// loads need to be non-zero).  Loads at or past `bytes` return zero.  base
+// must be wave-uniform: the resource lives in scalar registers.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t buffer_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes,
+                                          0x00020000);
+}
+
+// 16 bytes per lane from resource r at byte offset voff (per lane) + soff
+// (uniform) straight into LDS at dst + 16 * lane (dst uniform): one 1-KB
+// buffer_load_dwordx4 ... lds per wave.  CPOL: cache-policy bits.
+template <int CPOL>
+__device__ __forceinline__ void buffer_load_lds16(__amdgpu_buffer_rsrc_t r, char* dst, uint32_t voff,
+                                                  uint32_t soff) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_ptr_t)dst, 16, voff, soff, 0, CPOL);
+}
+
 constexpr int kLdsBytes = 160 * 1024;  // LDS per CU (and per workgroup) on gfx950
 
 // Workgroup barrier for the LDS ring.  Before it, each wave has waited for

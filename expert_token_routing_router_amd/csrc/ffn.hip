@@ -174,17 +174,24 @@ __host__ __device__ __forceinline__ int packed_slab_rows(int N) { return N % 256
 // accumulators, K loop and epilogue, and the wave runs the copy that matches
 // its share.  320-row tiles take a whole expert of up to 320 rows (one tile
 // per expert at capacity factor 1.25 of 256 rows per expert); 160 x 64 wave
-// tiles (160 accumulators) leave room for two waves per SIMD.
+// tiles (160 accumulators) leave room for two waves per SIMD.  192-row tiles
+// go up to 512 weight rows per stage (SwiGLU 256 columns of W1 and of W3, the
+// down GEMM 512 columns): 96 x 128 wave tiles, 192 accumulators, one register
+// set of fragments.  Every column tile re-reads the tile's A rows (from L2),
+// and those reads share each CU's load path with the weight stream, so the
+// wider tile (half the A reads) streams weights faster.
 //
 // MFMA v_mfma_f32_32x32x16_bf16 with the weight fragment as the first operand,
 // so a lane's accumulator holds 4 consecutive output columns of one row.
 // DUAL (SwiGLU): the B stage holds BN rows of W1 (gate) and BN rows of W3
 // (up); the wave keeps both accumulators and combines them in the epilogue.
 //
-// Operands reach LDS by global_load_lds_dwordx4 (16 bytes per lane, 1 KB =
-// 16 rows of 64 bytes per instruction) into a ring of NS stages; waves 0-3
+// Operands reach LDS by buffer_load_dwordx4 ... lds (16 bytes per lane, 1 KB
+// = 16 rows of 64 bytes per instruction) into a ring of NS stages; waves 0-3
 // fetch the A rows (XOR swizzle applied through the choice of source address),
-// waves 4-7 the weight rows.  Weights come packed (moe_expert_ffn_pack_weights)
+// waves 4-7 the weight rows.  A stage's slot is refilled right after the
+// barrier that follows its last LDS reads, so NS - 1 stages are in flight
+// while one is consumed.  Weights come packed (moe_expert_ffn_pack_weights)
 // so that one stage of a slab of 64 or 256 weight rows is one contiguous run
 // already in LDS order: the weight stream reads long sequential runs of HBM.
 // The epilogue converts to bf16 in registers (v_cvt_pk_bf16_f32), swaps
@@ -241,9 +248,18 @@ void grouped_gemm_bf16(
   constexpr int NW = AP ? (NW_ < 8 ? NW_ : 8) : NS;    // weight ring depth
   constexpr int LA2 = BM / 8 / 4;                      // A loads per pair, A waves (0-3)
   constexpr int LDSB = AP ? 2 * ASLOT + NW * WST : NS * STAGE;
-  static_assert(!AP || (NW >= 4 && NW - 2 <= 6 && (NW - 1) * LB < 64 && 2 * LA2 < 64),
+  // Accumulator blocks (16 registers each) of a wave with all FM fragments
+  // live.  Up to 10 (160 registers) the fragments of the two K steps of a
+  // stage sit in two register sets, one refilled while the other feeds the
+  // MFMAs; wider wave tiles (192 accumulators) keep one set, refilled between
+  // the K steps, so the wave fits its 256 registers (two waves per SIMD: the
+  // other wave's MFMAs run while this one waits on its LDS reads).
+  constexpr int ACCB = FM * FN * (DUAL ? 2 : 1);
+  constexpr bool ONESET = ACCB > 10;
+  static_assert(ACCB <= 12, "at most 192 accumulators per wave");
+  static_assert(!AP || (NW >= 3 && NW - 2 <= 6 && (NW - 1) * LB < 64 && 2 * LA2 < 64),
                 "pair ring: A pairs two stages ahead, weight waits covered below");
-  static_assert(NS >= 3, "the ring needs three stages");
+  static_assert(NS >= 3 && NS - 1 <= 7, "the ring needs three stages; waits cover up to 7");
   static_assert(KK == 2, "register sets alternate per K step");
   static_assert(BM % (4 * RPL) == 0 && BROWS % (4 * RPL) == 0, "loads split over 4 waves");
   static_assert(WN % 32 == 0, "wave tile must be whole 32-column MFMA blocks");
@@ -264,13 +280,22 @@ void grouped_gemm_bf16(
   const bool a_wave = wave < 4;
   const int grp = wave % 4;
 
-  // Per-lane source pointers of this wave's loads (16 stage rows each) and the
-  // element step from one K stage to the next: BK along an A row, one slab
-  // stage (SR * BK elements) in the packed weights.
-  const bf16_t* src[LMAX];
+  // Operands are fetched by buffer loads into LDS: a wave-uniform resource
+  // (base address in scalar registers), a per-lane byte offset in one VGPR,
+  // and wave-uniform offsets per load and per stage, so no per-lane 64-bit
+  // pointer stays live across the K loop.  sbase is this wave's stream base
+  // and kstep the elements from one K stage to the next (BK along an A row of
+  // the up GEMM, which is addressed per pair instead; one ldg-group stage of
+  // the packed hidden buffer; one slab stage, SR * BK elements, of the packed
+  // weights); soff[i] is load i's byte offset within a stage.
   int ldst;  // LDS byte offset (within a stage) of this wave's first load
-  size_t kstep;
-  int arow = 0, ach0 = 0;  // AP A waves: first row, logical chunk offset
+  const bf16_t* sbase;
+  size_t kstep = 0;
+  uint32_t soff[LMAX];
+  uint32_t voff;
+  // Up GEMM A waves: the lane's row relative to the tile (first load) and the
+  // tile's last relative row; rows past it are clamped to it.
+  int arel = 0, alast = 0;
   // A rows are spread over the four A waves in interleaved units (16-row
   // groups for the down GEMM, 8-row pieces of a pair for the up GEMM): load i
   // of wave grp fetches unit 4 i + grp.  A copy of the K loop for FA_ live
@@ -278,32 +303,38 @@ void grouped_gemm_bf16(
   // at most 64 FA_ rows holds), so a short tile fetches only its own rows.
   if (a_wave && MODE != kUpGemm) {
     ldst = grp * 1024;
+    sbase = A + (size_t)g0 * 512;
     kstep = (size_t)ldg * 512;
+    voff = lane * 16;
     const int last = (r1 - r0 - 1) / RPL;  // the tile's last 16-row group
 #pragma unroll
-    for (int i = 0; i < LMAX; ++i) {
-      const int g = min(4 * (i < LA ? i : 0) + grp, last);  // past the tile: fetched, never used
-      src[i] = A + (size_t)(g0 + g) * 512 + lane * 8;
-    }
+    for (int i = 0; i < LMAX; ++i)  // past the tile: fetched, never used
+      soff[i] = (uint32_t)min(4 * (i < LA ? i : 0) + grp, last) * 1024u;
   } else if (a_wave) {
     // Load i of a pair: tile rows 8 (4 i + grp) + lane / 8, physical 16-byte
     // chunk lane % 8 of the row's 128 bytes, which holds logical chunk
     // (lane % 8) ^ swz8(row % 16); row % 16 = 8 (grp % 2) + lane / 8.
     ldst = 0;
-    kstep = 0;
-    arow = r0 + grp * 8 + lane / 8;
-    ach0 = ((lane & 7) ^ swz8(8 * (grp & 1) + (lane >> 3))) * 8;
+    sbase = A + (size_t)r0 * K;
+    arel = grp * 8 + lane / 8;
+    alast = r1 - 1 - r0;
+    voff = ((lane & 7) ^ swz8(8 * (grp & 1) + (lane >> 3))) * 16;
+#pragma unroll
+    for (int i = 0; i < LMAX; ++i) soff[i] = 0;
   } else {
     ldst = (AP ? 0 : BM * RB) + grp * LB * 1024;
     const int SR = packed_slab_rows(N);
     kstep = (size_t)SR * BK;
+    voff = lane * 16;
+    // A wave's LB loads are LB consecutive 16-row groups of one matrix
+    // (BROWS / 4 rows; for SwiGLU BN is a multiple of that).
+    const int br0 = grp * LB * RPL;
+    sbase = ((DUAL && br0 >= BN) ? B2 : B) + (size_t)e * N * K;
 #pragma unroll
     for (int i = 0; i < LMAX; ++i) {
       const int br = (grp * LB + (i < LB ? i : 0)) * RPL;  // first weight row in the stage
-      const bf16_t* W = (DUAL && br >= BN) ? B2 : B;
       const int n = min(n0 + (DUAL ? br % BN : br), N - RPL);  // 16-row group, clamped
-      src[i] = W + ((size_t)e * (N / SR) + n / SR) * (size_t)(K / BK) * SR * BK +
-               (n % SR) / RPL * 512 + lane * 8;
+      soff[i] = (uint32_t)(((size_t)(n / SR) * (K / BK) * SR * BK + (n % SR) / RPL * 512) * 2);
     }
   }
 
@@ -336,19 +367,19 @@ void grouped_gemm_bf16(
   bf16x8_t xf1[FM], wf1[FN], vf1[FN2];
   const int ktiles = K / BK;
 
-  // Issue the global->LDS loads of K tile kt_ into ring slot slot_; the A
-  // waves issue NA_ loads (units 4 i + grp), the weight waves LB.
+  // Issue the loads of K tile kt_ into ring slot slot_; the A waves issue
+  // NA_ loads (units 4 i + grp), the weight waves LB.  The stream's resource
+  // is rebased per stage, so the scalar offsets stay within one stage.
 #define MOE_RING_ISSUE(kt_, slot_, NA_)                                                    \
   do {                                                                                     \
     char* base_ = smem + (slot_) * STAGE + ldst;                                           \
+    const auto rs_ = buffer_rsrc(sbase + (size_t)(kt_) * kstep, 0xFFFFFFFFu);              \
     if (a_wave) {                                                                          \
       _Pragma("unroll") for (int i = 0; i < LA; ++i) if (i < (NA_))                        \
-          __builtin_amdgcn_global_load_lds((void*)(src[i] + (size_t)(kt_) * kstep),        \
-                                           (lds_ptr_t)(base_ + i * 4096), 16, 0, 0);       \
+          buffer_load_lds16<0>(rs_, base_ + i * 4096, voff, soff[i]);                      \
     } else { /* weights are read once per launch: non-temporal, system scope */            \
       _Pragma("unroll") for (int i = 0; i < LB; ++i)                                       \
-          __builtin_amdgcn_global_load_lds((void*)(src[i] + (size_t)(kt_) * kstep),        \
-                                           (lds_ptr_t)(base_ + i * 1024), 16, 0, kWeightCpol); \
+          buffer_load_lds16<kWeightCpol>(rs_, base_ + i * 1024, voff, soff[i]);            \
     }                                                                                      \
   } while (0)
   // AP: weight stage kt_ into its ring slot (weight waves), A pair p_ into
@@ -356,18 +387,23 @@ void grouped_gemm_bf16(
 #define MOE_ISSUE_W(kt_)                                                                   \
   do {                                                                                     \
     char* base_ = smem + 2 * ASLOT + ((kt_) % NW) * WST + ldst;                            \
+    const auto rs_ = buffer_rsrc(sbase + (size_t)(kt_) * kstep, 0xFFFFFFFFu);              \
     _Pragma("unroll") for (int i = 0; i < LB; ++i)                                         \
-        __builtin_amdgcn_global_load_lds((void*)(src[i] + (size_t)(kt_) * kstep),          \
-                                         (lds_ptr_t)(base_ + i * 1024), 16, 0, kWeightCpol); \
+        buffer_load_lds16<kWeightCpol>(rs_, base_ + i * 1024, voff, soff[i]);              \
   } while (0)
+  // The A resource spans the tile's rows, every load stays inside it (rows
+  // past the tile are clamped to its last row: fetched, never used).  The
+  // empty asm makes the row offsets be recomputed at each issue (three VALU
+  // operations per load) rather than held in registers across the loop.
 #define MOE_ISSUE_A(p_, NA_)                                                               \
   do {                                                                                     \
     char* base_ = smem + ((p_) & 1) * ASLOT + grp * 1024;                                  \
+    const auto rs_ = buffer_rsrc(sbase, (uint32_t)(alast + 1) * (uint32_t)K * 2u);         \
+    int ar_ = arel;                                                                        \
+    asm volatile("" : "+v"(ar_));                                                          \
     _Pragma("unroll") for (int i = 0; i < LA2; ++i) if (i < (NA_)) {                       \
-      const int row_ = min(arow + 32 * i, r1 - 1); /* rows past the tile: never used */    \
-      __builtin_amdgcn_global_load_lds(                                                    \
-          (void*)(A + (size_t)row_ * K + ach0 + (size_t)(p_) * 2 * BK),                    \
-          (lds_ptr_t)(base_ + i * 4096), 16, 0, 0);                                        \
+      const uint32_t v_ = (uint32_t)min(ar_ + 32 * i, alast) * (uint32_t)K * 2u + voff;    \
+      buffer_load_lds16<0>(rs_, base_ + i * 4096, v_, (uint32_t)(p_) * (2 * BK * 2));      \
     }                                                                                      \
   } while (0)
   // Read the fragments of K step kk_ of stage kt_ into set S (FA_ live row
@@ -406,40 +442,44 @@ void grouped_gemm_bf16(
                                                              acc2[i][j], 0, 0, 0);         \
     }                                                                                      \
   } while (0)
-  // Wait until the next stage's loads have landed in every wave: at most
-  // `later_` younger stages of this wave may still be in flight (vmcnt counts
-  // this wave's 1-KB loads: NA_ per stage for an A wave, LB for a weight wave).
-#define MOE_WAIT_STAGE(later_, NA_)                                                        \
+  // Wait until stage kt_ + 1 has landed in every wave, and let the slot of
+  // stage kt_ be refilled: each wave waits for its own loads of stage kt_ + 1
+  // (vmcnt counts this wave's 1-KB loads, `later_` younger stages may stay in
+  // flight) and for its LDS reads of stage kt_ (lgkmcnt 0), then the barrier
+  // makes both true for the whole block.  The slot a stage was read from is
+  // thus free right after that stage's barrier: a ring of NS slots keeps
+  // NS - 1 stages in flight while one is consumed.
+#define MOE_SYNC_STAGE(later_, NA_)                                                        \
   do {                                                                                     \
-    if (a_wave) {                                                                          \
-      switch (later_) {                                                                    \
-        case 0: wait_vmcnt<0>(); break;                                                    \
-        case 1: wait_vmcnt<(NA_)>(); break;                                                \
-        case 2: wait_vmcnt<2 * (NA_)>(); break;                                            \
-        default: wait_vmcnt<3 * (NA_)>(); break;                                           \
-      }                                                                                    \
-    } else {                                                                               \
-      switch (later_) {                                                                    \
-        case 0: wait_vmcnt<0>(); break;                                                    \
-        case 1: wait_vmcnt<LB>(); break;                                                   \
-        case 2: wait_vmcnt<2 * LB>(); break;                                               \
-        default: wait_vmcnt<3 * LB>(); break;                                              \
-      }                                                                                    \
-    }                                                                                      \
+    if (a_wave) wait_stages<(NA_)>(later_);                                                \
+    else wait_stages<LB>(later_);                                                          \
+    wait_lgkmcnt0();                                                                       \
     ring_barrier();                                                                        \
   } while (0)
-  // AP weight waits: at most later_ younger weight stages of this wave in flight.
-#define MOE_WAIT_W(later_)                                                                 \
+  // Fragments and MFMAs of stage kt_: with two register sets, step 1's reads
+  // were issued before step 0's MFMAs (set 0 holds step 0); with one set the
+  // steps run one after the other.  MOE_STAGE_HEAD runs before the stage's
+  // barrier, MOE_STAGE_TAIL after it (and after the refill): the two-set loop
+  // reads step 0 of stage kt_ + 1 there, while set 1 still feeds the MFMAs.
+#define MOE_STAGE_HEAD(FA_, kt_)                                                           \
   do {                                                                                     \
-    switch (later_) {                                                                      \
-      case 0: wait_vmcnt<0>(); break;                                                      \
-      case 1: wait_vmcnt<LB>(); break;                                                     \
-      case 2: wait_vmcnt<2 * LB>(); break;                                                 \
-      case 3: wait_vmcnt<3 * LB>(); break;                                                 \
-      case 4: wait_vmcnt<4 * LB>(); break;                                                 \
-      case 5: wait_vmcnt<5 * LB>(); break;                                                 \
-      default: wait_vmcnt<6 * LB>(); break;                                                \
+    if constexpr (ONESET) {                                                                \
+      MOE_LOAD_KK(FA_, kt_, 0, 0);                                                         \
+      MOE_MFMA_KK(FA_, 0);                                                                 \
+      MOE_LOAD_KK(FA_, kt_, 1, 0);                                                         \
+      MOE_MFMA_KK(FA_, 0);                                                                 \
+    } else {                                                                               \
+      MOE_LOAD_KK(FA_, kt_, 1, 1);                                                         \
+      MOE_MFMA_KK(FA_, 0);                                                                 \
     }                                                                                      \
+  } while (0)
+#define MOE_STAGE_NEXT(FA_, kt_)                                                           \
+  do {                                                                                     \
+    if constexpr (!ONESET) MOE_LOAD_KK(FA_, (kt_) + 1, 0, 0);                              \
+  } while (0)
+#define MOE_STAGE_TAIL(FA_)                                                                \
+  do {                                                                                     \
+    if constexpr (!ONESET) MOE_MFMA_KK(FA_, 1);                                            \
   } while (0)
   // The whole K loop for FA_ live row fragments.  Every copy issues the same
   // loads and barriers; only the LDS reads and MFMAs differ.
@@ -452,7 +492,7 @@ void grouped_gemm_bf16(
     }                                                                                      \
     int kt = 0;                                                                            \
     if constexpr (AP) {                                                                    \
-      /* A pairs 0 and 1, weight stages 0 .. NW-2; stage 0 landed.          */            \
+      /* A pairs 0 and 1, weight stages 0 .. NW-1; stage 0 landed.          */             \
       if (a_wave) {                                                                        \
         MOE_ISSUE_A(0, 2 * (FA_));                                                         \
         if (ktiles > 2) {                                                                  \
@@ -462,78 +502,71 @@ void grouped_gemm_bf16(
           wait_vmcnt<0>();                                                                 \
         }                                                                                  \
       } else {                                                                             \
-        _Pragma("unroll") for (int s = 0; s < NW - 1; ++s) if (s < ktiles) MOE_ISSUE_W(s); \
-        MOE_WAIT_W(min(NW - 2, ktiles - 1));                                               \
+        _Pragma("unroll") for (int s = 0; s < NW; ++s) if (s < ktiles) MOE_ISSUE_W(s);     \
+        wait_stages<LB>(min(NW - 1, ktiles - 1));                                          \
       }                                                                                    \
       ring_barrier();                                                                      \
-      MOE_LOAD_KK(FA_, 0, 0, 0);                                                           \
-      /* Steady state: the weight refill and the next A pair are in range.  */            \
-      /* The wait at stage kt is for stage kt+1: for the A waves a new pair  */            \
-      /* when kt is odd (issued two stages ago, the only A loads in flight), */            \
-      /* after which pair (kt+3)/2 goes into the slot of stages kt-1 and kt. */            \
-      for (; kt + NW - 1 < ktiles; ++kt) {                                                 \
-        MOE_LOAD_KK(FA_, kt, 1, 1);                                                        \
-        MOE_MFMA_KK(FA_, 0);                                                               \
+      if constexpr (!ONESET) MOE_LOAD_KK(FA_, 0, 0, 0);                                    \
+      /* Steady state: the weight refill (stage kt + NW, into the slot of    */            \
+      /* stage kt) and the next A pair are in range.  For the A waves the    */            \
+      /* wait at stage kt is for a new pair when kt is odd (issued two       */            \
+      /* stages ago, the only A loads in flight), after which pair (kt+3)/2 */             \
+      /* goes into the slot of stages kt-1 and kt.                          */             \
+      for (; kt + NW < ktiles; ++kt) {                                                     \
+        MOE_STAGE_HEAD(FA_, kt);                                                           \
         if (a_wave) {                                                                      \
           if (kt & 1) wait_vmcnt<0>();                                                     \
         } else {                                                                           \
-          wait_vmcnt<(NW - 3) * LB>();                                                     \
+          wait_vmcnt<(NW - 2) * LB>();                                                     \
         }                                                                                  \
+        wait_lgkmcnt0();                                                                   \
         ring_barrier();                                                                    \
         if (a_wave) {                                                                      \
           if (kt & 1) MOE_ISSUE_A((kt + 3) >> 1, 2 * (FA_));                               \
         } else {                                                                           \
-          MOE_ISSUE_W(kt + NW - 1);                                                        \
+          MOE_ISSUE_W(kt + NW);                                                            \
         }                                                                                  \
-        MOE_LOAD_KK(FA_, kt + 1, 0, 0);                                                    \
-        MOE_MFMA_KK(FA_, 1);                                                               \
+        MOE_STAGE_NEXT(FA_, kt);                                                           \
+        MOE_STAGE_TAIL(FA_);                                                               \
       }                                                                                    \
       for (; kt < ktiles; ++kt) {                                                          \
-        MOE_LOAD_KK(FA_, kt, 1, 1);                                                        \
-        MOE_MFMA_KK(FA_, 0);                                                               \
+        MOE_STAGE_HEAD(FA_, kt);                                                           \
         if (kt + 1 < ktiles) {                                                             \
           if (a_wave) {                                                                    \
             if (kt & 1) wait_vmcnt<0>();                                                   \
           } else {                                                                         \
-            MOE_WAIT_W(min(NW - 3, ktiles - kt - 2));                                      \
+            wait_stages<LB>(ktiles - kt - 2);                                              \
           }                                                                                \
+          wait_lgkmcnt0();                                                                 \
           ring_barrier();                                                                  \
-          if (a_wave) {                                                                    \
-            if ((kt & 1) && kt + 3 < ktiles) MOE_ISSUE_A((kt + 3) >> 1, 2 * (FA_));        \
-          } else if (kt + NW - 1 < ktiles) {                                               \
-            MOE_ISSUE_W(kt + NW - 1);                                                      \
-          }                                                                                \
-          MOE_LOAD_KK(FA_, kt + 1, 0, 0);                                                  \
+          if (a_wave && (kt & 1) && kt + 3 < ktiles) MOE_ISSUE_A((kt + 3) >> 1, 2 * (FA_)); \
+          MOE_STAGE_NEXT(FA_, kt);                                                         \
         }                                                                                  \
-        MOE_MFMA_KK(FA_, 1);                                                               \
+        MOE_STAGE_TAIL(FA_);                                                               \
       }                                                                                    \
     } else {                                                                               \
-      _Pragma("unroll") for (int s = 0; s < NS - 1; ++s) if (s < ktiles) MOE_RING_ISSUE(s, s, FA_); \
-      MOE_WAIT_STAGE(min(NS - 2, ktiles - 1), FA_);                                        \
-      MOE_LOAD_KK(FA_, 0, 0, 0);                                                           \
-      /* Steady state: the refill is always in range and the wait count is  */            \
-      /* fixed, so the loop body has no branches besides the wave role.     */            \
-      for (; kt + NS - 1 < ktiles; ++kt) {                                                 \
-        MOE_LOAD_KK(FA_, kt, 1, 1);                                                        \
-        MOE_MFMA_KK(FA_, 0);                                                               \
-        if (a_wave) wait_vmcnt<(NS - 3) * (FA_)>(); else wait_vmcnt<(NS - 3) * LB>();      \
+      _Pragma("unroll") for (int s = 0; s < NS; ++s) if (s < ktiles) MOE_RING_ISSUE(s, s, FA_); \
+      MOE_SYNC_STAGE(min(NS - 1, ktiles - 1), FA_);                                        \
+      if constexpr (!ONESET) MOE_LOAD_KK(FA_, 0, 0, 0);                                    \
+      /* Steady state: the refill (stage kt + NS, into the slot of stage kt) */            \
+      /* is always in range and the wait count is fixed.                    */             \
+      for (; kt + NS < ktiles; ++kt) {                                                     \
+        MOE_STAGE_HEAD(FA_, kt);                                                           \
+        if (a_wave) wait_vmcnt<(NS - 2) * (FA_)>(); else wait_vmcnt<(NS - 2) * LB>();      \
+        wait_lgkmcnt0();                                                                   \
         ring_barrier();                                                                    \
-        MOE_RING_ISSUE(kt + NS - 1, (kt + NS - 1) % NS, FA_);                              \
-        MOE_LOAD_KK(FA_, kt + 1, 0, 0);                                                    \
-        MOE_MFMA_KK(FA_, 1);                                                               \
+        MOE_RING_ISSUE(kt + NS, kt % NS, FA_);                                             \
+        MOE_STAGE_NEXT(FA_, kt);                                                           \
+        MOE_STAGE_TAIL(FA_);                                                               \
       }                                                                                    \
-      /* The last NS - 1 stages: nothing left to issue.                     */            \
+      /* The last NS stages: nothing left to issue.                         */             \
       for (; kt < ktiles; ++kt) {                                                          \
-        MOE_LOAD_KK(FA_, kt, 1, 1);                                                        \
-        MOE_MFMA_KK(FA_, 0);                                                               \
+        MOE_STAGE_HEAD(FA_, kt);                                                           \
         if (kt + 1 < ktiles) {                                                             \
-          /* Stage kt+1 visible to all waves; every wave is past its reads of */          \
-          /* stage kt-1, so that slot can be refilled.                         */          \
-          MOE_WAIT_STAGE(min(NS - 3, ktiles - kt - 2), FA_);                               \
-          if (kt + NS - 1 < ktiles) MOE_RING_ISSUE(kt + NS - 1, (kt + NS - 1) % NS, FA_);  \
-          MOE_LOAD_KK(FA_, kt + 1, 0, 0);                                                  \
+          MOE_SYNC_STAGE(ktiles - kt - 2, FA_);                                            \
+          MOE_STAGE_NEXT(FA_, kt);                                                         \
         }                                                                                  \
-        MOE_MFMA_KK(FA_, 1);                                                               \
+        MOE_STAGE_TAIL(FA_);                                                               \
       }                                                                                    \
     }                                                                                      \
   } while (0)
@@ -623,11 +656,13 @@ void grouped_gemm_bf16(
 #undef MOE_K_LOOP
 #undef MOE_LOAD_KK
 #undef MOE_MFMA_KK
-#undef MOE_WAIT_STAGE
+#undef MOE_SYNC_STAGE
+#undef MOE_STAGE_HEAD
+#undef MOE_STAGE_NEXT
+#undef MOE_STAGE_TAIL
 #undef MOE_RING_ISSUE
 #undef MOE_ISSUE_W
 #undef MOE_ISSUE_A
-#undef MOE_WAIT_W
 }
 
 // Weight packing for the bf16 kernel: W [E, N, K] row-major -> slabs of SR
@@ -763,12 +798,11 @@ static size_t align256(size_t x) { return (x + 255) / 256 * 256; }
 // tiles streams the expert's weights again (DeepSeek-like layer, 128 rows per
 // expert on average but spread around that: 5.75 -> 6.63 ms per step with
 // 128-row tiles; decode, ~8 rows per expert: 3.77 -> 3.64 ms).
-// 192 rows when experts average at most 128 rows: such a batch is bound by the
-// weight stream, whose rate per CU is the weight bytes the ring keeps in
-// flight over the memory latency; the smaller A slots leave LDS for 7 weight
-// stages instead of 5 (up GEMM) and 5 ring stages instead of 4 (down GEMM),
-// while an expert of up to 192 rows (all but a few at 128 on average) still
-// takes one tile.
+// 192 rows when experts average at most 128 rows: an expert of up to 192 rows
+// (all but a few at 128 on average) still takes one tile, and the smaller A
+// slots leave LDS and registers for 512 weight rows per stage where the
+// matrices are wide enough (SwiGLU with h >= 2048, the down GEMM with
+// d >= 4096), which halves the A rows' L2 reads against 256.
 static int ffn_bm(int dtype, int E, int max_rows) {
   if (dtype == 0) return kF32BM;
   if ((long long)max_rows <= 32LL * E) return kGemmBMSmall;
@@ -858,8 +892,10 @@ hipError_t launch_ffn_up(const FfnArgs& a, hipStream_t st) {
     const int bm = ffn_bm(1, a.E, a.max_rows);
     if (bm == kGemmBMMid) {
       constexpr int S = kGemmBMMid;
-      if (a.act == ACT_SWIGLU) launch_bf16<S, 128, ACT_SWIGLU, kUpGemm>(X, W1, W3, H, a.d, a.h, a, st);
-      else if (a.h >= 2048) {
+      if (a.act == ACT_SWIGLU) {
+        if (a.h >= 2048) launch_bf16<S, 256, ACT_SWIGLU, kUpGemm>(X, W1, W3, H, a.d, a.h, a, st);
+        else launch_bf16<S, 128, ACT_SWIGLU, kUpGemm>(X, W1, W3, H, a.d, a.h, a, st);
+      } else if (a.h >= 2048) {
         if (a.act == ACT_RELU) launch_bf16<S, 256, ACT_RELU, kUpGemm>(X, W1, nullptr, H, a.d, a.h, a, st);
         else launch_bf16<S, 256, ACT_GELU, kUpGemm>(X, W1, nullptr, H, a.d, a.h, a, st);
       } else {
@@ -907,7 +943,8 @@ static void launch_down_bf16(const FfnArgs& a, hipStream_t st) {
   auto Y = static_cast<bf16_t*>(a.y_rows);
   const int bm = ffn_bm(1, a.E, a.max_rows);
   if (bm == kGemmBMMid) {
-    if (a.d >= 1024) launch_bf16<kGemmBMMid, 256, ACT_NONE, MODE>(H, W2, nullptr, Y, a.h, a.d, a, st);
+    if (a.d >= 4096) launch_bf16<kGemmBMMid, 512, ACT_NONE, MODE>(H, W2, nullptr, Y, a.h, a.d, a, st);
+    else if (a.d >= 1024) launch_bf16<kGemmBMMid, 256, ACT_NONE, MODE>(H, W2, nullptr, Y, a.h, a.d, a, st);
     else launch_bf16<kGemmBMMid, 128, ACT_NONE, MODE>(H, W2, nullptr, Y, a.h, a.d, a, st);
   } else if (bm == kGemmBMSmall) {
     constexpr int S = kGemmBMSmall;

@@ -121,6 +121,22 @@ def test_ffn_mid_row_tiles(d, h, act):
     _check_ffn(d, h, act, "bf16", MID_COUNTS, seed=d + 5 * h)
 
 
+# Wide 192-row tiles (SwiGLU up: 256 columns of each of W1 and W3; down: 512
+# columns when d >= 4096; one register set per wave): the fragment edges of
+# MID_COUNTS without the fillers, at widths that are multiples of the column
+# tile and at widths that are not (partial last column tile, 64-row weight
+# slabs).
+WIDE_COUNTS = MID_COUNTS[:17]
+
+
+@pytest.mark.parametrize("d,h,act", [(4096, 2048, "swiglu"), (4160, 2112, "swiglu"),
+                                     (4096, 2048, "gelu")])
+def test_ffn_wide_row_tiles(d, h, act):
+    M = sum(WIDE_COUNTS) + 7
+    assert 32 * len(WIDE_COUNTS) < M <= 128 * len(WIDE_COUNTS), "must take the 192-row tiles"
+    _check_ffn(d, h, act, "bf16", WIDE_COUNTS, seed=d + 7 * h)
+
+
 def _check_ffn(d, h, act, dtype, counts, seed):
     print(f"[ffn tiles] d={d} h={h} act={act} dtype={dtype} counts={counts}", flush=True)
     x, w1, w3, w2, offs = _inputs(d, h, act, dtype, seed=seed, counts=counts)
