@@ -69,6 +69,13 @@ __device__ __forceinline__ double lane63(double v) {
   const int hi = __builtin_amdgcn_readlane((int)(b >> 32), 63);
   return __longlong_as_double(((long long)hi << 32) | (unsigned)lo);
 }
+// v of lane ln (wave-uniform ln) in every lane.
+__device__ __forceinline__ double bcast_lane(double v, int ln) {
+  const long long b = __double_as_longlong(v);
+  const int lo = __builtin_amdgcn_readlane((int)b, ln);
+  const int hi = __builtin_amdgcn_readlane((int)(b >> 32), ln);
+  return __longlong_as_double(((long long)hi << 32) | (unsigned)lo);
+}
 
 __device__ __forceinline__ float wave_sum(float v) {
   v += dpp_f<kDppXor1>(0.f, v);

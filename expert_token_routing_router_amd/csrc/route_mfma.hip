@@ -71,6 +71,16 @@ __device__ __forceinline__ float sel_score(float z, int score_fn, float bias) {
   return a + bias;
 }
 
+// Exponent of the lowest set bit of a nonzero finite fp64 value: v is an
+// integer multiple of 2^lowbit_exp(v) (significand m, with the implicit bit
+// for normal values, times 2^(biased exponent - 1075); subnormals 2^-1074).
+__device__ __forceinline__ int lowbit_exp(double v) {
+  const uint64_t b = (uint64_t)__double_as_longlong(v);
+  const int be = (int)((b >> 52) & 0x7ff);
+  const uint64_t m = (b & 0xfffffffffffffull) | (be ? (1ull << 52) : 0ull);
+  return (be ? be : 1) - 1075 + __builtin_ctzll(m);
+}
+
 // Does (sa, a) certainly rank before (sb, b) when only sa >= lower end of a's
 // score and sb <= upper end of b's are known?  Called with lo(a), hi(b).
 __device__ __forceinline__ bool certainly_before(float lo_a, int a, float hi_b, int b) {
@@ -349,51 +359,84 @@ __device__ __forceinline__ void route_tile_tail(
     }
   }
   __syncthreads();
-  // The chain itself for the pairs the test did not settle, one wave per pair:
-  // for each 256 elements the lanes form the exact products (4 each) and store
-  // them to a 2-KB staging buffer of the wave, after the fallback list in the
-  // scratch; then every lane runs the same running fp64 sum over them in
-  // order (broadcast LDS reads), one rounded add each -- the definition's
-  // fma(x, w, acc) with an exact product is the same add.  Conversions,
-  // products and loads stay off the dependency chain.
-  constexpr int kStageBytes = 2048;
-  constexpr int kFbEnd = 2 * kFuseTok * ZW * 2;  // end of the pair and fallback lists
-  constexpr int kStagers = (kFuseRing * kFuseSlot - kFbEnd) / kStageBytes < kFuseWaves
-                               ? (kFuseRing * kFuseSlot - kFbEnd) / kStageBytes
-                               : kFuseWaves;
-  static_assert(kStagers >= 1, "room for one staging buffer");
+  // The chain itself for the pairs the test did not settle, one wave per pair,
+  // walked a segment of `seg` consecutive products at a time.  First every
+  // lane forms the data of up to four segments j: T_j, the fp64 sum of the
+  // segment's exact products in any order; A_j, an upper bound of the sum of
+  // their magnitudes (the fp64 sum of the magnitudes, at most 2^11 terms, so
+  // within a factor 1 + 2^-42; padded by 2^-40); m_j, the least frexp
+  // exponent of its products minus 16 (each product is a multiple of 2^m_j,
+  // a zero product counting as exponent 0 only lowers it).  Then all lanes
+  // walk the segments in order with the chain's running value s, a multiple
+  // of 2^lowbit_exp(s).  With q = min(m_j, that exponent), if
+  // |s| + A_j < 2^(q + 53), every partial sum of the chain inside segment j
+  // is a multiple of 2^q below 2^(q + 53) in magnitude, hence representable:
+  // the chain does not round there, and it leaves the segment at s + T_j
+  // exactly (T_j is then exact as well, by the same bound, and so is the one
+  // add).  Otherwise the chain runs element by element through segment j,
+  // each product broadcast from its lane: the definition's rounded adds in
+  // its order.  Segments hold 64 products up to d = 16384 (at most 256
+  // segments, four per lane).
   const int nfb = nfb_s;
-  if (wave < kStagers) {
-    double* stage = reinterpret_cast<double*>(scratch + kFbEnd + wave * kStageBytes);
-    for (int p = wave; p < nfb; p += kStagers) {
+  {
+    const int seg = 64 * ((d + 64 * 256 - 1) / (64 * 256));
+    const int nseg = (d + seg - 1) / seg;
+    for (int p = wave; p < nfb; p += kFuseWaves) {
       const int v = fb[p];
       const int tl = v >> 8, e = v & 255;
-      const uint2* xr = reinterpret_cast<const uint2*>(x + (size_t)(t0 + tl) * d);
-      const uint2* wr = reinterpret_cast<const uint2*>(w + (size_t)e * d);
-      const int nq = d / 4;  // 4-element pieces per row (d % 32 == 0)
-      double acc = 0.0;
-      uint2 xa = lane < nq ? xr[lane] : uint2{0u, 0u};
-      uint2 wa = lane < nq ? wr[lane] : uint2{0u, 0u};
-      for (int q0 = 0; q0 < nq; q0 += 64) {
-        const double p0 = (double)bf16_to_f32(xa.x & 0xffffu) * (double)bf16_to_f32(wa.x & 0xffffu);
-        const double p1 = (double)bf16_to_f32(xa.x >> 16) * (double)bf16_to_f32(wa.x >> 16);
-        const double p2 = (double)bf16_to_f32(xa.y & 0xffffu) * (double)bf16_to_f32(wa.y & 0xffffu);
-        const double p3 = (double)bf16_to_f32(xa.y >> 16) * (double)bf16_to_f32(wa.y >> 16);
-        if (q0 + 64 + lane < nq) {  // next 256 elements, while these are summed
-          xa = xr[q0 + 64 + lane];
-          wa = wr[q0 + 64 + lane];
+      const bf16_t* xr = x + (size_t)(t0 + tl) * d;
+      const bf16_t* wr = w + (size_t)e * d;
+      double T[4], A[4];
+      int M[4];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        T[u] = 0.0;
+        A[u] = 0.0;
+        M[u] = 0x7fffffff;
+        const int j = lane + 64 * u;
+        if (j < nseg) {
+          const int i1 = min(d, (j + 1) * seg);
+          for (int i = j * seg; i < i1; i += 8) {  // d % 32 == 0: whole 8-element pieces
+            const u32x4 a = *reinterpret_cast<const u32x4*>(xr + i);
+            const u32x4 b = *reinterpret_cast<const u32x4*>(wr + i);
+#pragma unroll
+            for (int h = 0; h < 4; ++h) {
+              const double p0 =
+                  (double)bf16_to_f32(a[h] & 0xffffu) * (double)bf16_to_f32(b[h] & 0xffffu);
+              const double p1 = (double)bf16_to_f32(a[h] >> 16) * (double)bf16_to_f32(b[h] >> 16);
+              T[u] += p0;
+              T[u] += p1;
+              A[u] += fabs(p0);
+              A[u] += fabs(p1);
+              M[u] = min(M[u], min(__builtin_amdgcn_frexp_exp(p0), __builtin_amdgcn_frexp_exp(p1)));
+            }
+          }
+          A[u] *= 1.0 + 0x1p-40;
         }
-        stage[4 * lane] = p0;
-        stage[4 * lane + 1] = p1;
-        stage[4 * lane + 2] = p2;
-        stage[4 * lane + 3] = p3;
-        __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
-        __builtin_amdgcn_wave_barrier();
-        const int n = 4 * min(64, nq - q0);
-#pragma unroll 16
-        for (int i = 0; i < n; ++i) acc = acc + stage[i];
-        __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
-        __builtin_amdgcn_wave_barrier();
+      }
+      double acc = 0.0;
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        for (int ln = 0; ln < 64 && 64 * u + ln < nseg; ++ln) {
+          const double tj = bcast_lane(T[u], ln), aj = bcast_lane(A[u], ln);
+          int q = __builtin_amdgcn_readlane(M[u], ln) - 16;
+          if (acc != 0.0) q = min(q, lowbit_exp(acc));
+          // |s| + A_j rounded up (the fp64 add loses at most 2^-53 of it).
+          const double lhs = (fabs(acc) + aj) * (1.0 + 0x1p-50);
+          if (lhs < ldexp(1.0, min(q + 53, 1023))) {
+            acc = acc + tj;
+          } else {
+            const int j = 64 * u + ln;
+            const int i1 = min(d, (j + 1) * seg);
+            for (int b0 = j * seg; b0 < i1; b0 += 64) {
+              const int i = b0 + lane;
+              double pv = 0.0;
+              if (i < i1) pv = (double)bf16_to_f32(xr[i]) * (double)bf16_to_f32(wr[i]);
+              const int n = min(64, i1 - b0);
+              for (int r = 0; r < n; ++r) acc = acc + bcast_lane(pv, r);
+            }
+          }
+        }
       }
       if (lane == 0) {
         if (router_bias) acc = acc + (double)router_bias[e];
