@@ -140,6 +140,36 @@ def test_route_exact_where_the_chain_rounds():
     assert np.array_equal(buf.counts.cpu().numpy(), r["counts"])
 
 
+@pytest.mark.parametrize("base,d,N", [("deepseek", 2048, 300), ("mixtral", 4096, 200)])
+def test_route_exact_with_a_few_tiny_products(base, d, N):
+    """Rows that fail the whole-row exactness test through a few tiny
+    products only: one element scaled by 2^-40 (every third token, at a
+    moving position) or three elements scaled by 2^-30, 2^-38 and 2^-45.  The
+    chain of such a pair rounds where those products meet a large running
+    value, while most of its 64-product segments cannot round; the selected
+    logits must still be the left-to-right fp64 values bit for bit, on the
+    split launches (256 experts, group limit) and on the one-launch route."""
+    cfg = W.with_(W.small(base), d=d, N=N)
+    inp_cpu = W.make_inputs(cfg, weights=False)
+    x = inp_cpu["x"].float()
+    for t in range(N):
+        if t % 3 == 0:
+            x[t, (37 * t) % d] *= 2.0 ** -40
+        elif t % 3 == 1:
+            for j, s in enumerate((-30, -38, -45)):
+                x[t, (101 * t + 977 * j) % d] *= 2.0 ** s
+    inp_cpu["x"] = x.bfloat16()
+    print(f"[tiny products] {base} N={N} d={d} E={cfg['E']}", flush=True)
+    buf = _route_dispatch(cfg, inp_cpu)
+    r = oracle.route(cfg, n(inp_cpu["x"]), n(inp_cpu["w_router"]), n(inp_cpu["router_bias"]),
+                     n(inp_cpu["sel_bias"]))
+    zr = torch.from_numpy(r["logits"])
+    sel = torch.from_numpy(r["topk_idx"]).long()
+    assert torch.equal(bits_t(buf.logits.cpu().gather(1, sel)), bits_t(zr.gather(1, sel)))
+    assert np.array_equal(buf.topk_idx.cpu().numpy(), r["topk_idx"])
+    assert np.array_equal(buf.counts.cpu().numpy(), r["counts"])
+
+
 @pytest.mark.parametrize("name", list(CASES))
 def test_router_logits_exact_everywhere(name):
     """moe_router_logits gives the defined logit of every pair, bit for bit."""
