@@ -59,6 +59,12 @@ typedef float floatx4 __attribute__((ext_vector_type(4)));
 constexpr int kFuseTok = 32;                     // tokens per block
 constexpr int kFuseWaves = 8;
 constexpr int kFuseRing = 6;  // LDS chunk slots in step 1 (11 measured slower)
+// Pair slots (two chunks each) of step 1: 4 in the one-launch route, 6 in the
+// scoring launch of a split route (it holds no candidate lists or per-token
+// state, so two blocks per CU still fit); the tail launch keeps the ring of
+// kFuseRing chunks as scratch only.
+constexpr int kFusePairs = 4;
+constexpr int kScorePairs = 6;
 constexpr int kFuseSlot = (kFuseTok + 64) * 64;  // bytes: 32 x rows + 64 w rows of 64 B
 
 __device__ __forceinline__ float sigmoid_affinity_v2(float z) {
@@ -583,7 +589,7 @@ __device__ __forceinline__ void route_tile_tail(
 // expert tile (blockIdx.y) per block, writing z~ to `logits` and the squared
 // norms to ws_sx / ws_sw; SPLIT 2 reads them back and runs steps 2-4.
 template <int NJ, int SPLIT>
-__global__ __launch_bounds__(kFuseWaves * 64, 2) void route_fused(
+__global__ __launch_bounds__(kFuseWaves * 64, 4) void route_fused(
     const bf16_t* __restrict__ x, const bf16_t* __restrict__ w, int N, int d, int E, int k,
     int G, int kg, int score_fn, const float* __restrict__ router_bias,
     const float* __restrict__ sel_bias, float* __restrict__ logits,
@@ -592,7 +598,10 @@ __global__ __launch_bounds__(kFuseWaves * 64, 2) void route_fused(
     int ksplit, int tail_tpb) {
   constexpr int ZW = 64 * NJ;
   __shared__ float zs[kFuseTok][ZW];  // z~, then exact values for candidates
-  __shared__ __attribute__((aligned(1024))) char ring[kFuseRing][kFuseSlot];  // step 1; then pairs
+  // Pair slots of step 1 (the tail launch runs no step 1: its ring is scratch).
+  constexpr int RINGP = SPLIT == 1 ? kScorePairs : kFusePairs;
+  constexpr int NSLOT = SPLIT == 2 ? kFuseRing / 2 : RINGP;
+  __shared__ __attribute__((aligned(1024))) char ring[NSLOT][2 * kFuseSlot];  // step 1; then pairs
   __shared__ double sx[kFuseTok], sw[ZW];
   __shared__ uint64_t cand_s[kFuseTok][4], gm_s[kFuseTok][2];
   __shared__ int32_t cnt_s[kFuseTok];
@@ -625,10 +634,17 @@ __global__ __launch_bounds__(kFuseWaves * 64, 2) void route_fused(
   for (int e = tid; e < E; e += kFuseWaves * 64) hist[e] = 0;
 
   // ---- 1. scores --------------------------------------------------------
-  // Six 1-KB loads per chunk: 0-1 x rows 16j.., 2-5 w rows 16(j-2).. of the
-  // expert tile; wave w < 6 issues load w.  Lane L fetches row L/4 of its
-  // load, logical 16-byte chunk (L % 4) ^ swz4(L / 4).
-  const bool loader = wave < 6;
+  // The ring holds pairs of chunks (64 elements) as 128-byte row pieces: 12
+  // loads of 1 KB per pair, j < 4 the x rows 8j.. of the token block, j >= 4
+  // the w rows 8(j - 4).. of the expert tile; wave w issues load w, and waves
+  // 0-3 also load w + 8.  Lane L fetches row 8j' + L/8 of its load, logical
+  // 16-byte chunk (L % 8) ^ swz8(row % 16), into physical chunk L % 8.  The
+  // loads are buffer loads over the block's own x rows and expert rows, so the
+  // second chunk of a last pair past the row end (d an odd number of chunks)
+  // reads zeros instead of past the buffers; every offset that varies sits in
+  // the per-lane offset, which the range check covers.
+  const int nx = min(kFuseTok, N - t0);  // token rows the block may read
+  const int nl = wave < 4 ? 2 : 1;       // loads per pair of this wave
   // Squared norms from the diagonal of X X^T and W W^T, one extra MFMA per
   // chunk on the operands already in registers (waves 0 and 4 for the two
   // token blocks, waves 0-3 for the expert blocks).  In the 16x16 output lane
@@ -640,110 +656,125 @@ __global__ __launch_bounds__(kFuseWaves * 64, 2) void route_fused(
   floatx4 sq32x = floatx4{0.f, 0.f, 0.f, 0.f};
   const int et_begin = SPLIT == 1 ? 64 * (int)blockIdx.y : 0;
   const int et_end = SPLIT == 1 ? et_begin + 64 : (SPLIT == 2 ? 0 : E);
+  const int npair = (nch + 1) / 2;
   for (int et = et_begin; et < et_end; et += 64) {
-    const u32x4* src;
-    {
-      const int j = min(wave, 5);
-      const int r = lane / 4, c = (lane % 4) ^ swz4(r);
-      if (j < 2) {
-        const int t = min(t0 + 16 * j + r, N - 1);
-        src = reinterpret_cast<const u32x4*>(x + (size_t)t * d) + c + 4 * c0;
-      } else {
-        const int e = min(et + 16 * (j - 2) + r, E - 1);
-        src = reinterpret_cast<const u32x4*>(w + (size_t)e * d) + c + 4 * c0;
-      }
+    const int ne = min(64, E - et);
+    const auto rs_x = buffer_rsrc(x + (size_t)t0 * d, (uint32_t)nx * (uint32_t)d * 2u);
+    const auto rs_w = buffer_rsrc(w + (size_t)et * d, (uint32_t)ne * (uint32_t)d * 2u);
+    // Per-lane byte offsets of this wave's loads at pair 0 of the range.
+    uint32_t vo[2];
+    bool isx[2];
+#pragma unroll
+    for (int q = 0; q < 2; ++q) {
+      const int j = wave + 8 * q;
+      const int jj = j < 4 ? j : j - 4;
+      const int r = 8 * jj + lane / 8;
+      isx[q] = j < 4;
+      const int rr = isx[q] ? min(r, nx - 1) : min(r, ne - 1);  // past the end: fetched, unused
+      vo[q] = (uint32_t)rr * (uint32_t)d * 2u + (uint32_t)(((lane & 7) ^ swz8(r & 15)) * 16) +
+              (uint32_t)c0 * 64u;
     }
-#define MOE_FUSE_ISSUE(ch_)                                                                 \
-  do {                                                                                      \
-    if (loader)                                                                             \
-      __builtin_amdgcn_global_load_lds((void*)(src + (size_t)(ch_) * 4),                    \
-                                       (lds_ptr_t)(ring[(ch_) % kFuseRing] + wave * 1024),  \
-                                       16, 0, 0);                                           \
+#define MOE_FUSE_ISSUE(pr_)                                                                  \
+  do {                                                                                       \
+    char* slot_ = ring[(pr_) % RINGP];                                                       \
+    const uint32_t po_ = (uint32_t)(pr_) * 128u;                                             \
+    _Pragma("unroll") for (int q = 0; q < 2; ++q) if (q < nl) {                              \
+      const int j = wave + 8 * q;                                                            \
+      buffer_load_lds16<0>(isx[q] ? rs_x : rs_w, slot_ + j * 1024, vo[q] + po_, 0u);         \
+    }                                                                                        \
   } while (0)
-    // Chunks are consumed in pairs: one wait and one barrier per pair, and the
-    // two chunks' LDS reads and arithmetic overlap.  The prologue issues
-    // kFuseRing - 2 chunks; each pair step refills the two slots the previous
-    // pair used.
-    static_assert(kFuseRing >= 4, "two slots refilled per pair step");
-    for (int c = 0; c < kFuseRing - 2 && c < nch; ++c) MOE_FUSE_ISSUE(c);
+    // Pairs are consumed two per step: one wait and one barrier per two pairs.
+    // The prologue issues RINGP - 2 pairs; each step refills the two slots the
+    // previous step used.
+    static_assert(RINGP >= 4 && 2 * (RINGP - 4) <= 7, "two slots refilled per step");
+    for (int c = 0; c < RINGP - 2 && c < npair; ++c) MOE_FUSE_ISSUE(c);
     double swp = 0.0;  // waves 0-3, diagonal lanes: sum w^2 of expert 16 wave + lane%16
-    floatx4 sq32w = floatx4{0.f, 0.f, 0.f, 0.f};
-    floatx4 acc32 = floatx4{0.f, 0.f, 0.f, 0.f};
+    // fp32 sums of the chunks of a step: chunks 0 and 2 go to the first of
+    // each pair of accumulators, 1 and 3 to the second (at most 64 products
+    // per fp32 sum, and two independent MFMA chains).
+    floatx4 sq32w[2] = {floatx4{0.f, 0.f, 0.f, 0.f}, floatx4{0.f, 0.f, 0.f, 0.f}};
+    floatx4 sq32x[2] = {floatx4{0.f, 0.f, 0.f, 0.f}, floatx4{0.f, 0.f, 0.f, 0.f}};
+    floatx4 acc32[2] = {floatx4{0.f, 0.f, 0.f, 0.f}, floatx4{0.f, 0.f, 0.f, 0.f}};
     double acc[4] = {0.0, 0.0, 0.0, 0.0};
-#define MOE_FUSE_CHUNK(ch_)                                                                 \
+#define MOE_FUSE_CHUNK(pr_, c_, A_)                                                         \
   do {                                                                                      \
-    const char* slot = ring[(ch_) % kFuseRing];                                             \
+    const char* slot = ring[(pr_) % RINGP];                                                 \
     /* MFMA: wave w takes token block w/4 (A = tokens 16(w/4) + (lane & 15)) */            \
     /* and expert block w%4 of the tile (B). */                                             \
     {                                                                                       \
-      const int er = 16 * (wave % 4) + (lane & 15), cc = lane >> 4;                         \
+      const int lc = 4 * (c_) + (lane >> 4), r16 = lane & 15;                               \
+      const int er = 16 * (wave % 4) + r16, tr = 16 * (wave / 4) + r16;                     \
       const bf16x8_t bw = *reinterpret_cast<const bf16x8_t*>(                               \
-          slot + 2048 + (er / 16) * 1024 + ((er % 16) * 4 + (cc ^ swz4(er % 16))) * 16);    \
-      const int tr = lane & 15;                                                             \
+          slot + 4096 + er * 128 + ((lc ^ swz8(r16)) << 4));                                \
       const bf16x8_t ax = *reinterpret_cast<const bf16x8_t*>(                               \
-          slot + (wave / 4) * 1024 + (tr * 4 + (cc ^ swz4(tr))) * 16);                      \
-      acc32 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ax, bw, acc32, 0, 0, 0);              \
-      if (wave < 4) sq32w = __builtin_amdgcn_mfma_f32_16x16x32_bf16(bw, bw, sq32w, 0, 0, 0); \
+          slot + tr * 128 + ((lc ^ swz8(r16)) << 4));                                       \
+      acc32[A_] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ax, bw, acc32[A_], 0, 0, 0);      \
+      if (wave < 4)                                                                          \
+        sq32w[A_] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(bw, bw, sq32w[A_], 0, 0, 0);    \
       if (et == 0 && (wave & 3) == 0)                                                        \
-        sq32x = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ax, ax, sq32x, 0, 0, 0);             \
+        sq32x[A_] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ax, ax, sq32x[A_], 0, 0, 0);    \
     }                                                                                       \
   } while (0)
-    // A pair's fp32 sums of at most 64 exact squares, as upper bounds in fp64:
-    // the rounded sum is at least (1 - 2^-18) of the exact one, and squares
-    // below 2^-126 that the MFMA may flush add at most 64 * 2^-126.
-#define MOE_FUSE_FOLD_SQ()                                                                  \
+    // A step's fp32 sums of at most 64 exact products each, summed in fp64;
+    // its fp32 sums of at most 64 exact squares as upper bounds in fp64: the
+    // rounded sum is at least (1 - 2^-18) of the exact one, and squares below
+    // 2^-126 that the MFMA may flush add at most 64 * 2^-126.
+#define MOE_FUSE_FOLD()                                                                     \
   do {                                                                                      \
-    if (wave < 4) {                                                                         \
-      const float q = diag_v == 0 ? sq32w[0] : diag_v == 1 ? sq32w[1] : diag_v == 2 ? sq32w[2] : sq32w[3]; \
-      if (diag_lane) swp += (double)q * (1.0 + 0x1p-17) + 0x1p-120;                         \
-      sq32w = floatx4{0.f, 0.f, 0.f, 0.f};                                                  \
-    }                                                                                       \
-    if (et == 0 && (wave & 3) == 0) {                                                       \
-      const float q = diag_v == 0 ? sq32x[0] : diag_v == 1 ? sq32x[1] : diag_v == 2 ? sq32x[2] : sq32x[3]; \
-      if (diag_lane) sxp += (double)q * (1.0 + 0x1p-17) + 0x1p-120;                         \
-      sq32x = floatx4{0.f, 0.f, 0.f, 0.f};                                                  \
+    _Pragma("unroll") for (int a_ = 0; a_ < 2; ++a_) {                                      \
+      _Pragma("unroll") for (int v = 0; v < 4; ++v) acc[v] += (double)acc32[a_][v];         \
+      acc32[a_] = floatx4{0.f, 0.f, 0.f, 0.f};                                              \
+      if (wave < 4) {                                                                       \
+        const floatx4 s_ = sq32w[a_];                                                       \
+        const float q = diag_v == 0 ? s_[0] : diag_v == 1 ? s_[1] : diag_v == 2 ? s_[2] : s_[3]; \
+        if (diag_lane) swp += (double)q * (1.0 + 0x1p-17) + 0x1p-120;                       \
+        sq32w[a_] = floatx4{0.f, 0.f, 0.f, 0.f};                                            \
+      }                                                                                     \
+      if (et == 0 && (wave & 3) == 0) {                                                     \
+        const floatx4 s_ = sq32x[a_];                                                       \
+        const float q = diag_v == 0 ? s_[0] : diag_v == 1 ? s_[1] : diag_v == 2 ? s_[2] : s_[3]; \
+        if (diag_lane) sxp += (double)q * (1.0 + 0x1p-17) + 0x1p-120;                       \
+        sq32x[a_] = floatx4{0.f, 0.f, 0.f, 0.f};                                            \
+      }                                                                                     \
     }                                                                                       \
   } while (0)
     // Steady state: both refills of the step are in range, so the wait count
-    // is a constant and the loop body has no branches.
-    int ch = 0;
-    for (; ch + kFuseRing - 1 < nch; ch += 2) {
-      // The pair's last chunk has landed once at most kFuseRing - 4 younger
-      // chunks (one load each per loading wave) are in flight.
-      wait_vmcnt<kFuseRing - 4>();
-      // The pair is visible to all waves; all waves are done with the previous
-      // pair, whose two slots are refilled now.
+    // is a constant and the loop body has no branches besides the wave role.
+    int pr = 0;
+    for (; pr + RINGP - 1 < npair; pr += 2) {
+      // Pairs pr and pr + 1 have landed once at most RINGP - 4 younger pairs
+      // of this wave's loads are in flight.
+      if (nl == 2) wait_vmcnt<2 * (RINGP - 4)>(); else wait_vmcnt<RINGP - 4>();
+      // The pairs are visible to all waves; all waves are done with the
+      // previous step's pairs, whose slots are refilled now.
       ring_barrier();
-      MOE_FUSE_ISSUE(ch + kFuseRing - 2);
-      MOE_FUSE_ISSUE(ch + kFuseRing - 1);
-      MOE_FUSE_CHUNK(ch);
-      MOE_FUSE_CHUNK(ch + 1);
-      // fp32 chunks of at most 64 products, summed in fp64.
-#pragma unroll
-      for (int v = 0; v < 4; ++v) acc[v] += (double)acc32[v];
-      acc32 = floatx4{0.f, 0.f, 0.f, 0.f};
-      MOE_FUSE_FOLD_SQ();
+      MOE_FUSE_ISSUE(pr + RINGP - 2);
+      MOE_FUSE_ISSUE(pr + RINGP - 1);
+      MOE_FUSE_CHUNK(pr, 0, 0);
+      MOE_FUSE_CHUNK(pr, 1, 1);
+      MOE_FUSE_CHUNK(pr + 1, 0, 0);
+      MOE_FUSE_CHUNK(pr + 1, 1, 1);
+      MOE_FUSE_FOLD();
     }
-    // The last pairs: fewer younger chunks in flight, at most one refill.
-    for (; ch < nch; ch += 2) {
-      const bool two = ch + 1 < nch;
-      switch (two ? min(kFuseRing - 4, nch - 2 - ch) : 0) {
-        case 0: wait_vmcnt<0>(); break;
-        case 1: wait_vmcnt<1>(); break;
-        default: wait_vmcnt<2>(); break;
-      }
-      static_assert(kFuseRing - 4 <= 2, "wait counts above cover the ring");
+    // The last steps: fewer younger pairs in flight, refills only in range;
+    // the last step may hold one pair, and the range's last pair one chunk.
+    for (; pr < npair; pr += 2) {
+      const bool two = pr + 1 < npair;
+      const int later = min(npair - 1, pr + RINGP - 3) - (two ? pr + 1 : pr);
+      if (nl == 2) wait_stages<2>(later); else wait_stages<1>(later);
       ring_barrier();
-      if (ch + kFuseRing - 2 < nch) MOE_FUSE_ISSUE(ch + kFuseRing - 2);
-      MOE_FUSE_CHUNK(ch);
-      if (two) MOE_FUSE_CHUNK(ch + 1);
-#pragma unroll
-      for (int v = 0; v < 4; ++v) acc[v] += (double)acc32[v];
-      acc32 = floatx4{0.f, 0.f, 0.f, 0.f};
-      MOE_FUSE_FOLD_SQ();
+      if (pr + RINGP - 2 < npair) MOE_FUSE_ISSUE(pr + RINGP - 2);
+      if (pr + RINGP - 1 < npair) MOE_FUSE_ISSUE(pr + RINGP - 1);
+      MOE_FUSE_CHUNK(pr, 0, 0);
+      if (2 * pr + 1 < nch) MOE_FUSE_CHUNK(pr, 1, 1);
+      if (two) {
+        MOE_FUSE_CHUNK(pr + 1, 0, 0);
+        if (2 * pr + 3 < nch) MOE_FUSE_CHUNK(pr + 1, 1, 1);
+      }
+      MOE_FUSE_FOLD();
     }
 #undef MOE_FUSE_CHUNK
-#undef MOE_FUSE_FOLD_SQ
+#undef MOE_FUSE_FOLD
 #undef MOE_FUSE_ISSUE
     // z~: lane holds expert (lane & 15) of block w%4, tokens 16(w/4) + 4*(lane>>4)+v.
     const int e = et + 16 * (wave % 4) + (lane & 15);
