@@ -891,11 +891,14 @@ hipError_t launch_route_certified(const RouteArgs& a, hipStream_t st) {
   double* ws_sx = split ? static_cast<double*>(a.ws) : nullptr;
   double* ws_sw = split ? ws_sx + (size_t)ks * a.N : nullptr;
   double* ws_part = ks > 1 ? ws_sw + (size_t)ks * a.E : nullptr;
-  // Tail blocks take 16 tokens while that still gives about one block per
-  // CU, fewer for small batches (decode-sized): there the exact sums of a
-  // block's candidate pairs stream each pair's x and w rows from L2, and 16
-  // tokens per block would put all of that on N/16 CUs.
-  const int tail_tpb = std::min(kFuseTok / 2, std::max(1, (a.N + 255) / 256));
+  // Tail blocks take 16 tokens while that still gives about two blocks per
+  // CU (two fit: 128 VGPRs, 75 KB of LDS), fewer for smaller batches: the
+  // phases of a block (certify, exact sums, selection) run one after another,
+  // so a second block on the CU fills the first one's waits, and the exact
+  // sums of a block's candidate pairs stream each pair's x and w rows from
+  // L2, which 16 tokens per block would put on N/16 CUs (decode-sized
+  // batches).  DeepSeek-like layer (4096 tokens): 8 tokens, 227 -> 206 us.
+  const int tail_tpb = std::min(kFuseTok / 2, std::max(1, (a.N + 511) / 512));
   auto launch = [&](auto kernel, dim3 grid) {
     kernel<<<grid, kFuseWaves * 64, 0, st>>>(
         static_cast<const bf16_t*>(a.x), static_cast<const bf16_t*>(a.w_router), a.N, a.d, a.E,
