@@ -649,6 +649,36 @@ def backward_pass(moe, torch, buf, inp, steps: int) -> dict:
         "mfma_frac": round(flops / (fb * 1e-6) / pk, 4),
         "executed_tflops": round(2.0 * M * dim * h * n_exec / (fb * 1e-6) / 1e12, 1),
         "weight_grad_bytes": grad_bytes}
+    # The same backward on the forward's grouped GEMM (packed weights, packed
+    # once per weight update like the forward's, outside the timed region).
+    if dim % 64 == 0 and h % 64 == 0:
+        pw = moe.prepare_backward_weights(cfg, {"w1": w1, "w3": w3, "w2": w2})
+        wsp = moe.workspace(moe.moe_expert_ffn_backward_packed_workspace_size(
+            E, buf.rows, dim, h, act, "bf16"), dev)
+        dx_p = torch.empty_like(buf.x_perm)
+
+        def ffn_bwd_packed():
+            moe.moe_expert_ffn_backward_packed(E, buf.rows, dim, h, act, "bf16", buf.x_perm,
+                                               buf.expert_offsets, buf.admitted, pw["w1"],
+                                               pw["w3"], pw["w2t"], pw["w13t"], dy_perm, dx_p,
+                                               dw1, dw3, dw2, wsp)
+
+        for _ in range(2):
+            ffn_bwd_packed()
+        torch.cuda.synchronize()
+        fp = 0.0
+        for _ in range(steps):
+            ev[0].record()
+            ffn_bwd_packed()
+            ev[1].record()
+            torch.cuda.synchronize()
+            fp += ev[0].elapsed_time(ev[1])
+        fp = fp / steps * 1e3
+        out["ffn_backward_packed"] = {
+            "us": round(fp, 2), "tflops": round(flops / (fp * 1e-6) / 1e12, 1),
+            "mfma_frac": round(flops / (fp * 1e-6) / pk, 4),
+            "executed_tflops": round(2.0 * M * dim * h * n_exec / (fp * 1e-6) / 1e12, 1)}
+        del pw, wsp, dx_p
     return out
 
 

@@ -44,6 +44,8 @@ EXPORTS = [
     "moe_dequantize_q8", "moe_dispatch_layout", "moe_permute", "moe_permute_q8",
     "moe_dispatch_rows", "moe_dispatch_noalloc", "moe_combine_backward", "moe_permute_backward",
     "moe_expert_ffn_backward_workspace_size", "moe_expert_ffn_backward",
+    "moe_expert_ffn_backward_packed_workspace_size", "moe_expert_ffn_backward_packed",
+    "moe_expert_ffn_pack_weights_t",
     "moe_expert_ffn_workspace_size", "moe_expert_ffn", "moe_expert_ffn_plan",
     "moe_expert_ffn_up", "moe_expert_ffn_down", "moe_expert_ffn_pack_weights", "moe_combine",
     "moe_bias_update", "moe_status_string", "moe_router_backward_workspace_size",
@@ -152,6 +154,10 @@ def lib() -> ctypes.CDLL:
             "moe_expert_ffn_up": ([I32, I32, I32, I32, I32, I32, P, P, P, P, P, SZ, P], I32),
             "moe_expert_ffn_down": ([I32, I32, I32, I32, I32, I32, P, P, P, FC, P, SZ, P], I32),
             "moe_expert_ffn_pack_weights": ([I32, I32, I32, I32, P, P, P], I32),
+            "moe_expert_ffn_pack_weights_t": ([I32, I32, I32, I32, I32, P, P, P, P], I32),
+            "moe_expert_ffn_backward_packed_workspace_size": ([I32, I32, I32, I32, I32, I32], SZ),
+            "moe_expert_ffn_backward_packed": ([I32, I32, I32, I32, I32, I32, P, P, P, P, P, P, P,
+                                                P, P, P, P, P, P, SZ, P], I32),
             "moe_combine": ([D, P, P, P, P, P, P, P, P], I32),
             "moe_bias_update": ([I32, I32, I32, P, F32, P, P], I32),
             "moe_status_string": ([I32], ctypes.c_char_p),
@@ -450,6 +456,21 @@ def moe_expert_ffn_pack_weights(num_experts, rows, cols, dtype, w, w_packed, str
     _raise("moe_expert_ffn_pack_weights", st)
 
 
+def moe_expert_ffn_pack_weights_t(num_experts, rows, cols_a, cols, dtype, wa, wb, w_packed,
+                                  stream=None):
+    """Pack the [E, rows, cols] matrix [wa^T | wb^T] (wa [E, cols_a, rows],
+    wb [E, cols - cols_a, rows] or None when cols_a == cols) into ``w_packed``
+    in the expert FFN's packed layout (the backward's W2^T and [W1^T | W3^T])."""
+    dtype = DTYPE[dtype] if isinstance(dtype, str) else int(dtype)
+    dt = TORCH_DTYPE.get(dtype)
+    E = num_experts
+    st = lib().moe_expert_ffn_pack_weights_t(
+        E, rows, cols_a, cols, dtype, _ptr(wa, "wa", dt, E * cols_a * rows),
+        _ptr(wb, "wb", dt, E * (cols - cols_a) * rows, cols_a < cols),
+        _ptr(w_packed, "w_packed", dt, E * rows * cols), _stream(stream))
+    _raise("moe_expert_ffn_pack_weights_t", st)
+
+
 def _ws(ws):
     return (_ptr(ws, "ws", None, None, False),
             0 if ws is None else ws.numel() * ws.element_size())
@@ -575,6 +596,40 @@ def moe_expert_ffn_backward(num_experts, max_rows, hidden, ffn_hidden, act, dtyp
     _raise("moe_expert_ffn_backward", st)
 
 
+def moe_expert_ffn_backward_packed_workspace_size(num_experts, max_rows, hidden, ffn_hidden,
+                                                  act, dtype) -> int:
+    act = ACT[act] if isinstance(act, str) else int(act)
+    dtype = DTYPE[dtype] if isinstance(dtype, str) else int(dtype)
+    return int(lib().moe_expert_ffn_backward_packed_workspace_size(num_experts, max_rows, hidden,
+                                                                    ffn_hidden, act, dtype))
+
+
+def moe_expert_ffn_backward_packed(num_experts, max_rows, hidden, ffn_hidden, act, dtype, x_rows,
+                                   group_offsets, group_rows, w1_packed, w3_packed, w2t_packed,
+                                   w13t_packed, dy_rows, dx_rows, dw1, dw3, dw2, ws,
+                                   stream=None):
+    """moe_expert_ffn_backward on the forward's grouped GEMM: w1/w3 packed as
+    for moe_expert_ffn, w2t_packed and w13t_packed from
+    moe_expert_ffn_pack_weights_t (see prepare_backward_weights)."""
+    act = ACT[act] if isinstance(act, str) else int(act)
+    dtype = DTYPE[dtype] if isinstance(dtype, str) else int(dtype)
+    dt = TORCH_DTYPE.get(dtype)
+    E, M, d, h = num_experts, max_rows, hidden, ffn_hidden
+    sw = act == MOE_SWIGLU
+    kg = 2 * h if sw else h
+    f32 = torch.float32
+    st = lib().moe_expert_ffn_backward_packed(
+        E, M, d, h, act, dtype, _ptr(x_rows, "x_rows", dt, M * d, M > 0),
+        _ptr(group_offsets, "group_offsets", torch.int32, E + 1),
+        _ptr(group_rows, "group_rows", torch.int32, E, False),
+        _ptr(w1_packed, "w1_packed", dt, E * h * d), _ptr(w3_packed, "w3_packed", dt, E * h * d, sw),
+        _ptr(w2t_packed, "w2t_packed", dt, E * h * d), _ptr(w13t_packed, "w13t_packed", dt, E * d * kg),
+        _ptr(dy_rows, "dy_rows", dt, M * d, M > 0), _ptr(dx_rows, "dx_rows", dt, M * d, M > 0),
+        _ptr(dw1, "dw1", f32, E * h * d), _ptr(dw3, "dw3", f32, E * h * d, sw),
+        _ptr(dw2, "dw2", f32, E * d * h), *_ws(ws), _stream(stream))
+    _raise("moe_expert_ffn_backward_packed", st)
+
+
 def moe_router_backward_workspace_size(desc: RouteDesc) -> int:
     return int(lib().moe_router_backward_workspace_size(ctypes.byref(desc)))
 
@@ -611,4 +666,5 @@ def moe_bias_update(num_experts, num_tokens, top_k, counts, step, sel_bias, stre
     _raise("moe_bias_update", st)
 
 
-from .layer import MoeBuffers, moe_forward, prepare_weights  # noqa: E402,F401  (composition of the calls above)
+from .layer import (MoeBuffers, moe_forward, prepare_backward_weights,  # noqa: E402,F401
+                    prepare_weights)  # composition of the calls above

@@ -440,6 +440,59 @@ int moe_expert_ffn_backward(int32_t num_experts, int32_t max_rows, int32_t hidde
   return status_of(moe::launch_ffn_backward(a, static_cast<hipStream_t>(stream)));
 }
 
+// Backward on packed weights: the forward GEMM's shape limits (d, h multiples
+// of 64, E <= 1024) besides the backward's own.
+static int check_ffn_backward_packed(int32_t E, int32_t max_rows, int32_t d, int32_t h,
+                                     int32_t act, int32_t dtype) {
+  const int st = check_ffn_backward(E, max_rows, d, h, act, dtype);
+  if (st != MOE_OK) return st;
+  if (E > kMaxFfnExperts || d % 64 != 0 || h % 64 != 0) return MOE_ERR_UNSUPPORTED;
+  return MOE_OK;
+}
+
+size_t moe_expert_ffn_backward_packed_workspace_size(int32_t num_experts, int32_t max_rows,
+                                                     int32_t hidden, int32_t ffn_hidden,
+                                                     int32_t act, int32_t dtype) {
+  if (check_ffn_backward_packed(num_experts, max_rows, hidden, ffn_hidden, act, dtype) != MOE_OK)
+    return 0;
+  return moe::ffn_bwd_packed_workspace_bytes(num_experts, max_rows, hidden, ffn_hidden, act);
+}
+
+int moe_expert_ffn_backward_packed(int32_t num_experts, int32_t max_rows, int32_t hidden,
+                                   int32_t ffn_hidden, int32_t act, int32_t dtype,
+                                   const void* x_rows, const int32_t* group_offsets,
+                                   const int32_t* group_rows, const void* w1_packed,
+                                   const void* w3_packed, const void* w2t_packed,
+                                   const void* w13t_packed, const void* dy_rows, void* dx_rows,
+                                   float* dw1, float* dw3, float* dw2, void* ws, size_t ws_bytes,
+                                   void* stream) {
+  int st = check_ffn_backward_packed(num_experts, max_rows, hidden, ffn_hidden, act, dtype);
+  if (st != MOE_OK) return st;
+  const bool swiglu = act == MOE_SWIGLU;
+  if (!group_offsets || !w1_packed || !w2t_packed || !w13t_packed || !dw1 || !dw2)
+    return MOE_ERR_INVALID_ARG;
+  if (swiglu != (w3_packed != nullptr) || swiglu != (dw3 != nullptr)) return MOE_ERR_INVALID_ARG;
+  if ((reinterpret_cast<uintptr_t>(group_offsets) & 3u) ||
+      (reinterpret_cast<uintptr_t>(group_rows) & 3u) || !aligned16(w1_packed) ||
+      (w3_packed && !aligned16(w3_packed)) || !aligned16(w2t_packed) ||
+      !aligned16(w13t_packed) || !aligned16(dw1) || !aligned16(dw2) || (dw3 && !aligned16(dw3)))
+    return MOE_ERR_INVALID_ARG;
+  if (max_rows > 0) {
+    if (!x_rows || !dy_rows || !dx_rows) return MOE_ERR_INVALID_ARG;
+    if (!aligned16(x_rows) || !aligned16(dy_rows) || !aligned16(dx_rows))
+      return MOE_ERR_INVALID_ARG;
+    const size_t need = moe::ffn_bwd_packed_workspace_bytes(num_experts, max_rows, hidden,
+                                                            ffn_hidden, act);
+    if (!ws || ws_bytes < need || (reinterpret_cast<uintptr_t>(ws) & 255u))
+      return MOE_ERR_WORKSPACE;
+  }
+  moe::FfnBwdPackedArgs a{num_experts, max_rows, hidden, ffn_hidden, act, x_rows,
+                          group_offsets, group_rows, w1_packed, w3_packed, w2t_packed,
+                          w13t_packed, dy_rows, dx_rows, ws};
+  return status_of(
+      moe::launch_ffn_backward_packed(a, dw1, dw3, dw2, static_cast<hipStream_t>(stream)));
+}
+
 int moe_expert_ffn_plan(int32_t num_experts, int32_t max_rows, int32_t hidden,
                         int32_t ffn_hidden, int32_t act, int32_t dtype,
                         const int32_t* group_offsets, void* ws, size_t ws_bytes, void* stream) {
@@ -496,6 +549,30 @@ int moe_expert_ffn_pack_weights(int32_t num_experts, int32_t rows, int32_t cols,
   if (a0 < b0 + bytes && b0 < a0 + bytes) return MOE_ERR_INVALID_ARG;  // must not overlap
   return status_of(moe::launch_pack_weights(num_experts, rows, cols, w, w_packed,
                                             static_cast<hipStream_t>(stream)));
+}
+
+int moe_expert_ffn_pack_weights_t(int32_t num_experts, int32_t rows, int32_t cols_a,
+                                  int32_t cols, int32_t dtype, const void* wa, const void* wb,
+                                  void* w_packed, void* stream) {
+  if (num_experts < 1 || rows < 1 || cols < 1 || cols_a < 1 || cols_a > cols)
+    return MOE_ERR_INVALID_ARG;
+  if (dtype != MOE_F32 && dtype != MOE_BF16) return MOE_ERR_INVALID_ARG;
+  if (dtype != MOE_BF16 || rows % 64 != 0 || cols % 64 != 0 || cols_a % 8 != 0)
+    return MOE_ERR_UNSUPPORTED;
+  if (!wa || !w_packed || !aligned16(wa) || !aligned16(w_packed)) return MOE_ERR_INVALID_ARG;
+  if ((cols_a < cols) != (wb != nullptr) || (wb && !aligned16(wb))) return MOE_ERR_INVALID_ARG;
+  const size_t bytes = (size_t)num_experts * rows * cols * 2;
+  const char* b0 = static_cast<const char*>(w_packed);
+  const char* a0 = static_cast<const char*>(wa);
+  const size_t abytes = (size_t)num_experts * rows * cols_a * 2;
+  if (a0 < b0 + bytes && b0 < a0 + abytes) return MOE_ERR_INVALID_ARG;  // must not overlap
+  if (wb) {
+    const char* c0 = static_cast<const char*>(wb);
+    const size_t cbytes = (size_t)num_experts * rows * (cols - cols_a) * 2;
+    if (c0 < b0 + bytes && b0 < c0 + cbytes) return MOE_ERR_INVALID_ARG;
+  }
+  return status_of(moe::launch_pack_weights_t(num_experts, rows, cols_a, cols, wa, wb, w_packed,
+                                              static_cast<hipStream_t>(stream)));
 }
 
 int moe_combine(const moe_route_desc* desc, const void* y_perm, const int32_t* row_of_slot,

@@ -69,6 +69,30 @@ __device__ __forceinline__ float apply_act(float u, int act) {
 // g sigmoid(g); v_rcp_f32 (within 2 ulp) in place of an IEEE divide.
 __device__ __forceinline__ float silu(float g) { return g * __builtin_amdgcn_rcpf(1.f + __expf(-g)); }
 
+// H = act(u) [* v], du = g act'(u) [* v], dv = g silu(u) (SwiGLU), all in
+// fp32, for the backward (GELU in the erf form with the device erf and exp:
+// gelu(u) = u Phi(u), gelu'(u) = Phi(u) + u phi(u)).
+template <int ACT>
+__device__ __forceinline__ void bwd_act_grad(float u, float v, float g, float& hv, float& du,
+                                             float& dv) {
+  if constexpr (ACT == ACT_RELU) {
+    hv = fmaxf(u, 0.f);
+    du = u > 0.f ? g : 0.f;
+    dv = 0.f;
+  } else if constexpr (ACT == ACT_GELU) {
+    const float Phi = 0.5f * (1.f + erff(u * 0.70710678118654752f));
+    const float phi = 0.39894228040143268f * expf(-0.5f * u * u);
+    hv = u * Phi;
+    du = g * (Phi + u * phi);
+    dv = 0.f;
+  } else {
+    const float s = 1.f / (1.f + expf(-u)), si = u * s;
+    hv = si * v;
+    du = g * v * (s * (1.f + u * (1.f - s)));
+    dv = g * si;
+  }
+}
+
 // ------------------------------------------------------------- tile plan ---
 
 // One block of 1024 threads (E <= 1024): expert e owns n_e = ceil(rows_e / BM)
@@ -78,7 +102,10 @@ __device__ __forceinline__ float silu(float g) { return g * __builtin_amdgcn_rcp
 // row, row end, first 16-row group}, and *count = number of tiles.  The group
 // numbering gives every tile ceil(rows / 16) groups of its own, in tile order:
 // the packed hidden buffer of the bf16 FFN stores a tile's rows there.  Rows
-// are clamped to max_rows.
+// are clamped to max_rows and, when group_rows is given, each segment to its
+// first group_rows[e] rows.  Nondecreasing offsets need at most cap_tiles
+// tiles and cap_groups groups (the workspace's sizes); a tile past either is
+// not written, and *count stops before the first such tile.
 // Inclusive scan over the 1024 threads of a block: shuffles inside each wave,
 // then the 16 wave totals (two barriers instead of a Hillis-Steele loop).
 __device__ __forceinline__ int32_t block_scan_1024(int32_t v, int32_t* wsum) {
@@ -96,16 +123,19 @@ __device__ __forceinline__ int32_t block_scan_1024(int32_t v, int32_t* wsum) {
 }
 
 __global__ __launch_bounds__(1024) void ffn_plan_tiles(const int32_t* __restrict__ offsets,
-                                                       int E, int BM, int max_rows,
-                                                       int4* __restrict__ tiles,
+                                                       const int32_t* __restrict__ group_rows,
+                                                       int E, int BM, int max_rows, int cap_tiles,
+                                                       int cap_groups, int4* __restrict__ tiles,
                                                        int32_t* __restrict__ count) {
   __shared__ int32_t wsum[16];
-  __shared__ int32_t total_s;
+  __shared__ int32_t total_s, first_bad_s;
   const int e = threadIdx.x;
+  if (e == 0) first_bad_s = 0x7fffffff;
   int32_t lo = 0, hi = 0, n = 0, chunk = BM;
   if (e < E) {
     lo = min(offsets[e], max_rows);
     hi = min(offsets[e + 1], max_rows);
+    if (group_rows) hi = min(hi, lo + max(group_rows[e], 0));
     n = hi > lo ? (hi - lo + BM - 1) / BM : 0;
     if (n > 0) chunk = ((hi - lo + n - 1) / n + 31) / 32 * 32;
   }
@@ -118,10 +148,17 @@ __global__ __launch_bounds__(1024) void ffn_plan_tiles(const int32_t* __restrict
   int32_t g0 = block_scan_1024(ng, wsum) - ng;
   for (int q = 0; q < n; ++q) {
     const int32_t r0 = lo + q * chunk, r1 = min(hi, r0 + chunk);
-    tiles[start + q] = make_int4(e, r0, r1, g0);
-    g0 += (r1 - r0 + 15) / 16;
+    const int32_t g1 = g0 + (r1 - r0 + 15) / 16;
+    if (start + q < cap_tiles && g1 <= cap_groups) {
+      tiles[start + q] = make_int4(e, r0, r1, g0);
+    } else {
+      atomicMin(&first_bad_s, start + q);
+      break;
+    }
+    g0 = g1;
   }
-  if (e == 0) *count = total_s;  // written by thread E-1 before the second scan's barriers
+  __syncthreads();
+  if (e == 0) *count = min(total_s, first_bad_s);
 }
 
 // XCD-aware block order.  The hardware deals blocks round-robin over the 8
@@ -216,15 +253,36 @@ constexpr int kWeightCpol = 2 | 16;
 // swapped (A fragment first), so a lane holds one output column of 16 rows and
 // the 32 lanes of a half-wave cover 32 consecutive columns of one row: each
 // atomic instruction touches two 128-byte runs instead of 64 scattered words.
-enum { kUpGemm = 0, kDownGemm = 1, kDownFused = 2 };
+//
+// Two modes serve the backward of the expert FFN (u = x W1^T, v = x W3^T; the
+// gradient at H is g = dy W2):
+// MODE kUpRawF32: the up GEMM with no activation; u (and for SwiGLU v) go out
+//   as fp32, row-major [rows, N], to be.U and be.V.
+// MODE kBwdG: A = dy rows (row-major [rows, K = d]), B = W2^T packed (N = h):
+//   the product is g; the epilogue reads u (and v) at the same positions and
+//   forms H = act(u) [* v], du = g act'(u) [* v] and, for SwiGLU, dv =
+//   g silu(u) (the activation named by ACT, with a single B operand), each
+//   rounded to bf16: H row-major to be.H ([rows, N]); G = [du | dv] row-major
+//   to be.G ([rows, kg], kg = N or 2N) and in the packed layout to C (K = kg:
+//   dv's columns follow du's), where the dx GEMM reads it as its A.
+enum { kUpGemm = 0, kDownGemm = 1, kDownFused = 2, kUpRawF32 = 3, kBwdG = 4 };
+
+struct BwdEpiArgs {
+  float* U;       // kUpRawF32: written; kBwdG: read
+  float* V;       // SwiGLU only
+  bf16_t* G;      // kBwdG: [du | dv] row-major, kg columns
+  bf16_t* H;      // kBwdG: H row-major, N columns
+  int kg;
+};
 
 template <int BM, int BN, int ACT, int MODE>
 __global__ __launch_bounds__(kGemmWaves * 64, 1) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void grouped_gemm_bf16(
     const bf16_t* __restrict__ A, const bf16_t* __restrict__ B, const bf16_t* __restrict__ B2,
     bf16_t* __restrict__ C, int K, int N, const int4* __restrict__ tiles,
-    const int32_t* __restrict__ tile_count, int n_tiles, int ldg, int gm, FusedCombineArgs fc) {
-  constexpr bool DUAL = ACT == ACT_SWIGLU;
+    const int32_t* __restrict__ tile_count, int n_tiles, int ldg, int gm, FusedCombineArgs fc,
+    BwdEpiArgs be) {
+  constexpr bool DUAL = ACT == ACT_SWIGLU && MODE != kBwdG;  // two B operands
   constexpr int BK = 32, RB = BK * 2;  // RB: bytes per staged row
   constexpr int RPL = 1024 / RB;                     // rows per 1-KB load
   constexpr int KK = BK / 16;                        // MFMA K steps per stage
@@ -240,7 +298,7 @@ void grouped_gemm_bf16(
   // Up GEMM (AP): the A rows are fetched as 128-byte pieces covering two K
   // stages (full cache lines, half the requests of 64-byte pieces) into two
   // pair slots; the weights keep their own ring of NW single stages.
-  constexpr bool AP = MODE == kUpGemm;
+  constexpr bool AP = MODE == kUpGemm || MODE == kUpRawF32 || MODE == kBwdG;
   constexpr bool FUSED = MODE == kDownFused;
   constexpr int ASLOT = BM * 2 * RB;                   // bytes of one A pair slot
   constexpr int WST = BROWS * RB;                      // bytes of one weight stage
@@ -301,7 +359,7 @@ void grouped_gemm_bf16(
   // of wave grp fetches unit 4 i + grp.  A copy of the K loop for FA_ live
   // fragments issues only the loads of units below 64 FA_ rows (all a tile of
   // at most 64 FA_ rows holds), so a short tile fetches only its own rows.
-  if (a_wave && MODE != kUpGemm) {
+  if (a_wave && !AP) {
     ldst = grp * 1024;
     sbase = A + (size_t)g0 * 512;
     kstep = (size_t)ldg * 512;
@@ -630,6 +688,65 @@ void grouped_gemm_bf16(
       }                                                                                    \
     }                                                                                      \
   } while (0)
+  // fp32 epilogue (kUpRawF32): lane l holds columns 8g + 4(l>>5) + 0..3 of
+  // row l&31 for g = 0..3, stored as they are.
+#define MOE_EPILOGUE_RAW(FA_)                                                              \
+  do {                                                                                     \
+    _Pragma("unroll") for (int i = 0; i < (FA_); ++i) {                                    \
+      const int row = r0 + (2 * i + wm) * 32 + (lane & 31);                                \
+      _Pragma("unroll") for (int j = 0; j < FN; ++j)                                       \
+      _Pragma("unroll") for (int g = 0; g < 4; ++g) {                                      \
+        const int col = n0 + wn * WN + j * 32 + 8 * g + 4 * (lane >> 5);                   \
+        if (row < r1 && col < N) {                                                         \
+          const size_t o_ = (size_t)row * N + col;                                         \
+          *reinterpret_cast<floatx4*>(be.U + o_) =                                         \
+              floatx4{acc[i][j][4 * g], acc[i][j][4 * g + 1], acc[i][j][4 * g + 2],        \
+                      acc[i][j][4 * g + 3]};                                               \
+          if constexpr (DUAL)                                                              \
+            *reinterpret_cast<floatx4*>(be.V + o_) =                                       \
+                floatx4{acc2[i][j][4 * g], acc2[i][j][4 * g + 1], acc2[i][j][4 * g + 2],   \
+                        acc2[i][j][4 * g + 3]};                                            \
+        }                                                                                  \
+      }                                                                                    \
+    }                                                                                      \
+  } while (0)
+  // Activation-gradient epilogue (kBwdG), four consecutive columns at a time;
+  // the packed store of 4 elements is half of a 16-byte position: row r16 of
+  // the tile's group, logical chunk (col % 32) / 8, elements col % 8 on.
+#define MOE_EPILOGUE_BWDG(FA_)                                                             \
+  do {                                                                                     \
+    _Pragma("unroll") for (int i = 0; i < (FA_); ++i) {                                    \
+      const int lr = (2 * i + wm) * 32 + (lane & 31);                                      \
+      const int row = r0 + lr;                                                             \
+      const int r16 = lr % 16, grp = g0 + lr / 16;                                         \
+      _Pragma("unroll") for (int j = 0; j < FN; ++j)                                       \
+      _Pragma("unroll") for (int g = 0; g < 4; ++g) {                                      \
+        const int col = n0 + wn * WN + j * 32 + 8 * g + 4 * (lane >> 5);                   \
+        if (row < r1 && col < N) {                                                         \
+          const size_t o_ = (size_t)row * N + col;                                         \
+          const floatx4 uu = *reinterpret_cast<const floatx4*>(be.U + o_);                 \
+          floatx4 vv = floatx4{0.f, 0.f, 0.f, 0.f};                                        \
+          if constexpr (ACT == ACT_SWIGLU) vv = *reinterpret_cast<const floatx4*>(be.V + o_); \
+          float hv[4], gu[4], gv[4];                                                       \
+          _Pragma("unroll") for (int q = 0; q < 4; ++q)                                    \
+            bwd_act_grad<ACT>(uu[q], vv[q], acc[i][j][4 * g + q], hv[q], gu[q], gv[q]);    \
+          const uint2 hb = make_uint2(pack_bf16x2(hv[0], hv[1]), pack_bf16x2(hv[2], hv[3])); \
+          const uint2 ub = make_uint2(pack_bf16x2(gu[0], gu[1]), pack_bf16x2(gu[2], gu[3])); \
+          *reinterpret_cast<uint2*>(be.H + o_) = hb;                                       \
+          *reinterpret_cast<uint2*>(be.G + (size_t)row * be.kg + col) = ub;                \
+          const int pos = 4 * r16 + (((col % 32) / 8) ^ swz4(r16));                        \
+          *reinterpret_cast<uint2*>(C + ((size_t)(col / 32) * ldg + grp) * 512 + pos * 8 + \
+                                    (col % 8)) = ub;                                       \
+          if constexpr (ACT == ACT_SWIGLU) {                                               \
+            const uint2 vb = make_uint2(pack_bf16x2(gv[0], gv[1]), pack_bf16x2(gv[2], gv[3])); \
+            *reinterpret_cast<uint2*>(be.G + (size_t)row * be.kg + N + col) = vb;          \
+            *reinterpret_cast<uint2*>(C + ((size_t)((N + col) / 32) * ldg + grp) * 512 +   \
+                                      pos * 8 + (col % 8)) = vb;                           \
+          }                                                                                \
+        }                                                                                  \
+      }                                                                                    \
+    }                                                                                      \
+  } while (0)
   // One self-contained copy (accumulators, K loop, epilogue) per number of
   // live fragments, so no accumulator value crosses from one copy to another.
 #define MOE_TILE(FA_)                                                                      \
@@ -638,6 +755,8 @@ void grouped_gemm_bf16(
     floatx16 acc2[DUAL && (FA_) > 0 ? (FA_) : 1][FN2];                                     \
     MOE_K_LOOP(FA_);                                                                       \
     if constexpr (FUSED) MOE_EPILOGUE_FUSED(FA_);                                          \
+    else if constexpr (MODE == kUpRawF32) MOE_EPILOGUE_RAW(FA_);                           \
+    else if constexpr (MODE == kBwdG) MOE_EPILOGUE_BWDG(FA_);                              \
     else MOE_EPILOGUE(FA_);                                                                \
   } while (0)
 
@@ -653,6 +772,8 @@ void grouped_gemm_bf16(
 #undef MOE_TILE
 #undef MOE_EPILOGUE
 #undef MOE_EPILOGUE_FUSED
+#undef MOE_EPILOGUE_RAW
+#undef MOE_EPILOGUE_BWDG
 #undef MOE_K_LOOP
 #undef MOE_LOAD_KK
 #undef MOE_MFMA_KK
@@ -695,6 +816,54 @@ hipError_t launch_pack_weights(int E, int N, int K, const void* w, void* wp, hip
   const int blocks = (int)std::min<size_t>((chunks + 255) / 256, 8192);
   pack_weights_bf16<<<blocks, 256, 0, st>>>(static_cast<const bf16_t*>(w),
                                             static_cast<bf16_t*>(wp), N, K, chunks);
+  return hipGetLastError();
+}
+
+// The same packed layout for a matrix given transposed: the [N, K] matrix
+// whose columns k < KA are rows k of wa[e] ([E, KA, N] row-major) and whose
+// columns k >= KA are rows k - KA of wb[e] ([E, K - KA, N]).  The backward
+// takes W2^T (N = h, K = d, from W2 [E, d, h]) and [W1^T | W3^T] (N = d,
+// K = h or 2h, from W1, W3 [E, h, d]) this way.  One thread per 16-byte
+// output chunk, eight gathered elements each (a one-time repacking).
+__global__ __launch_bounds__(256) void pack_weights_t_bf16(const bf16_t* __restrict__ wa,
+                                                           const bf16_t* __restrict__ wb,
+                                                           bf16_t* __restrict__ wp, int N, int KA,
+                                                           int K, size_t chunks) {
+  const int SR = packed_slab_rows(N), kts = K / 32, KB = K - KA;
+  const size_t stride = (size_t)gridDim.x * blockDim.x;
+  for (size_t q = (size_t)blockIdx.x * blockDim.x + threadIdx.x; q < chunks; q += stride) {
+    const int L = (int)(q % 64);
+    const size_t blk = q / 64;
+    const int g = (int)(blk % (SR / 16));
+    const size_t st = blk / (SR / 16);
+    const int kt = (int)(st % kts);
+    const size_t es = st / kts;
+    const int r = L / 4, c = (L % 4) ^ swz4(r);
+    const size_t row = es * SR + g * 16 + r;
+    const size_t e = row / N;
+    const int n = (int)(row % N), k0 = kt * 32 + c * 8;
+    uint32_t v[4];
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+      uint32_t lh[2];
+#pragma unroll
+      for (int b = 0; b < 2; ++b) {
+        const int k = k0 + 2 * t + b;
+        lh[b] = k < KA ? wa[(e * KA + k) * N + n] : wb[(e * KB + (k - KA)) * N + n];
+      }
+      v[t] = lh[0] | (lh[1] << 16);
+    }
+    *reinterpret_cast<u32x4*>(wp + q * 8) = u32x4{v[0], v[1], v[2], v[3]};
+  }
+}
+
+hipError_t launch_pack_weights_t(int E, int N, int KA, int K, const void* wa, const void* wb,
+                                 void* wp, hipStream_t st) {
+  const size_t chunks = (size_t)E * N * K / 8;
+  const int blocks = (int)std::min<size_t>((chunks + 255) / 256, 8192);
+  pack_weights_t_bf16<<<blocks, 256, 0, st>>>(static_cast<const bf16_t*>(wa),
+                                              static_cast<const bf16_t*>(wb),
+                                              static_cast<bf16_t*>(wp), N, KA, K, chunks);
   return hipGetLastError();
 }
 
@@ -846,15 +1015,16 @@ static int grid_of(int m_tiles, int n_tiles) {
 }
 
 hipError_t launch_ffn_plan(const FfnArgs& a, hipStream_t st) {
-  ffn_plan_tiles<<<1, 1024, 0, st>>>(a.offsets, a.E, ffn_bm(a.dtype, a.E, a.max_rows), a.max_rows,
-                                     ffn_tiles(a),
-                                     ffn_count(a));
+  const int bm = ffn_bm(a.dtype, a.E, a.max_rows);
+  ffn_plan_tiles<<<1, 1024, 0, st>>>(a.offsets, nullptr, a.E, bm, a.max_rows,
+                                     max_m_tiles(a.max_rows, bm, a.E), ffn_groups(a.E, a.max_rows),
+                                     ffn_tiles(a), ffn_count(a));
   return hipGetLastError();
 }
 
 template <int BM, int BN, int ACT, int MODE>
 static void launch_bf16(const bf16_t* A, const bf16_t* B, const bf16_t* B2, bf16_t* C, int K,
-                        int N, const FfnArgs& a, hipStream_t st) {
+                        int N, const FfnArgs& a, hipStream_t st, BwdEpiArgs be = {}) {
   const int nt = (N + BN - 1) / BN;
   const int g = grid_of(max_m_tiles(a.max_rows, BM, a.E), nt);
   // Groups of 4 row tiles once experts average two or more row tiles: an XCD's
@@ -863,7 +1033,7 @@ static void launch_bf16(const bf16_t* A, const bf16_t* B, const bf16_t* B2, bf16
   const int gm = a.max_rows / a.E >= 2 * BM ? 4 : 1;
   grouped_gemm_bf16<BM, BN, ACT, MODE><<<g, kGemmWaves * 64, 0, st>>>(
       A, B, B2, C, K, N, ffn_tiles(a), ffn_count(a), nt, ffn_groups(a.E, a.max_rows), gm,
-      MODE == kDownFused ? *a.fused : FusedCombineArgs{});
+      MODE == kDownFused ? *a.fused : FusedCombineArgs{}, be);
 }
 
 template <int ACT, bool FUSEDC = false>
@@ -982,6 +1152,104 @@ hipError_t launch_ffn_down(const FfnArgs& a, hipStream_t st) {
   } else {
     launch_down_bf16<kDownGemm>(a, st);
   }
+  return hipGetLastError();
+}
+
+// ------------------------------------------------------- backward GEMMs ---
+
+// Workspace of the backward on the grouped GEMM: the tile plan (as the
+// forward's), G = [du | dv] in the packed layout (K = kg = h or 2h), u (and v)
+// in fp32, then G and H row-major for the weight gradients.
+namespace {
+struct BwdLayout {
+  size_t gpk, u, v, grm, hrm, total;
+};
+BwdLayout bwd_layout(int E, int max_rows, int h, int act) {
+  const size_t kg = act == ACT_SWIGLU ? 2 * (size_t)h : (size_t)h;
+  BwdLayout l;
+  l.gpk = ffn_plan_bytes(E, max_rows, 1);
+  l.u = l.gpk + align256((size_t)ffn_groups(E, max_rows) * 16 * kg * 2);
+  l.v = l.u + align256((size_t)max_rows * h * 4);
+  l.grm = l.v + (act == ACT_SWIGLU ? align256((size_t)max_rows * h * 4) : 0);
+  l.hrm = l.grm + align256((size_t)max_rows * kg * 2);
+  l.total = l.hrm + align256((size_t)max_rows * h * 2);
+  return l;
+}
+}  // namespace
+
+size_t ffn_bwd_packed_workspace_bytes(int E, int max_rows, int d, int h, int act) {
+  (void)d;
+  return bwd_layout(E, max_rows, h, act).total;
+}
+
+hipError_t launch_ffn_bwd_packed_gemms(const FfnBwdPackedArgs& a, void** g_rm, void** h_rm,
+                                       hipStream_t st) {
+  const BwdLayout l = bwd_layout(a.E, a.max_rows, a.h, a.act);
+  char* ws = static_cast<char*>(a.ws);
+  const bool dual = a.act == ACT_SWIGLU;
+  const int kg = dual ? 2 * a.h : a.h;
+  BwdEpiArgs be{reinterpret_cast<float*>(ws + l.u), dual ? reinterpret_cast<float*>(ws + l.v) : nullptr,
+                reinterpret_cast<bf16_t*>(ws + l.grm), reinterpret_cast<bf16_t*>(ws + l.hrm), kg};
+  *g_rm = be.G;
+  *h_rm = be.H;
+  if (a.max_rows == 0) return hipGetLastError();
+  FfnArgs f{a.E, a.max_rows, a.d, a.h, a.act, 1, a.x_rows, a.offsets, a.w1p, a.w3p, nullptr,
+            nullptr, a.ws};
+  const int bm = ffn_bm(1, a.E, a.max_rows);
+  ffn_plan_tiles<<<1, 1024, 0, st>>>(a.offsets, a.group_rows, a.E, bm, a.max_rows,
+                                     max_m_tiles(a.max_rows, bm, a.E), ffn_groups(a.E, a.max_rows),
+                                     ffn_tiles(f), ffn_count(f));
+  auto X = static_cast<const bf16_t*>(a.x_rows);
+  auto DY = static_cast<const bf16_t*>(a.dy_rows);
+  auto W1 = static_cast<const bf16_t*>(a.w1p);
+  auto W3 = static_cast<const bf16_t*>(a.w3p);
+  auto W2T = static_cast<const bf16_t*>(a.w2tp);
+  auto W13T = static_cast<const bf16_t*>(a.w13tp);
+  auto GP = reinterpret_cast<bf16_t*>(ws + l.gpk);
+  auto DX = static_cast<bf16_t*>(a.dx_rows);
+  // u (v): the forward's up GEMM shape; g: an up GEMM of dy with W2^T, one
+  // B operand; dx: the forward's down GEMM shape over G (K = kg).
+  const bool wide = a.h >= 2048;
+#define MOE_BWD_TILES(S_)                                                                  \
+  do {                                                                                     \
+    constexpr int S = (S_);                                                                \
+    if (dual) {                                                                            \
+      if constexpr (S != kGemmBM) {                                                        \
+        if (wide)                                                                          \
+          launch_bf16<S, 256, ACT_SWIGLU, kUpRawF32>(X, W1, W3, nullptr, a.d, a.h, f, st, be); \
+        else                                                                               \
+          launch_bf16<S, 128, ACT_SWIGLU, kUpRawF32>(X, W1, W3, nullptr, a.d, a.h, f, st, be); \
+      } else {                                                                             \
+        launch_bf16<S, 128, ACT_SWIGLU, kUpRawF32>(X, W1, W3, nullptr, a.d, a.h, f, st, be); \
+      }                                                                                    \
+    } else if (wide) {                                                                     \
+      launch_bf16<S, 256, ACT_NONE, kUpRawF32>(X, W1, nullptr, nullptr, a.d, a.h, f, st, be); \
+    } else {                                                                               \
+      launch_bf16<S, 128, ACT_NONE, kUpRawF32>(X, W1, nullptr, nullptr, a.d, a.h, f, st, be); \
+    }                                                                                      \
+    switch (a.act) {                                                                       \
+      case ACT_RELU:                                                                       \
+        if (wide) launch_bf16<S, 256, ACT_RELU, kBwdG>(DY, W2T, nullptr, GP, a.d, a.h, f, st, be); \
+        else launch_bf16<S, 128, ACT_RELU, kBwdG>(DY, W2T, nullptr, GP, a.d, a.h, f, st, be); \
+        break;                                                                             \
+      case ACT_GELU:                                                                       \
+        if (wide) launch_bf16<S, 256, ACT_GELU, kBwdG>(DY, W2T, nullptr, GP, a.d, a.h, f, st, be); \
+        else launch_bf16<S, 128, ACT_GELU, kBwdG>(DY, W2T, nullptr, GP, a.d, a.h, f, st, be); \
+        break;                                                                             \
+      default:                                                                             \
+        if (wide) launch_bf16<S, 256, ACT_SWIGLU, kBwdG>(DY, W2T, nullptr, GP, a.d, a.h, f, st, be); \
+        else launch_bf16<S, 128, ACT_SWIGLU, kBwdG>(DY, W2T, nullptr, GP, a.d, a.h, f, st, be); \
+        break;                                                                             \
+    }                                                                                      \
+    if (a.d >= 1024)                                                                       \
+      launch_bf16<S, 256, ACT_NONE, kDownGemm>(GP, W13T, nullptr, DX, kg, a.d, f, st);     \
+    else                                                                                   \
+      launch_bf16<S, 128, ACT_NONE, kDownGemm>(GP, W13T, nullptr, DX, kg, a.d, f, st);     \
+  } while (0)
+  if (bm == kGemmBMMid) MOE_BWD_TILES(kGemmBMMid);
+  else if (bm == kGemmBMSmall) MOE_BWD_TILES(kGemmBMSmall);
+  else MOE_BWD_TILES(kGemmBM);
+#undef MOE_BWD_TILES
   return hipGetLastError();
 }
 

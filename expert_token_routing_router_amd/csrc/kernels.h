@@ -100,6 +100,31 @@ hipError_t launch_ffn_down(const FfnArgs& a, hipStream_t st);
 // Zero the fused combine's accumulator (a.fused->y_acc, N x d fp32).
 hipError_t launch_ffn_zero_acc(const FfnArgs& a, hipStream_t st);
 hipError_t launch_pack_weights(int E, int N, int K, const void* w, void* wp, hipStream_t st);
+// The packed layout of the [N, K] matrix [wa^T | wb^T] (wa [E, KA, N], wb
+// [E, K - KA, N] row-major; wb unused when KA == K).
+hipError_t launch_pack_weights_t(int E, int N, int KA, int K, const void* wa, const void* wb,
+                                 void* wp, hipStream_t st);
+
+// Backward of the expert FFN on the grouped GEMM (bf16, packed weights): the
+// tile plan, u (v) recomputed in fp32, g = dy W2 with H, du, dv, and dx.
+struct FfnBwdPackedArgs {
+  int E, max_rows, d, h, act;
+  const void* x_rows;
+  const int32_t* offsets;
+  const int32_t* group_rows;  // nullable
+  const void* w1p;            // forward-packed W1 [E, h, d]
+  const void* w3p;            // forward-packed W3 (SwiGLU)
+  const void* w2tp;           // packed W2^T: N = h, K = d
+  const void* w13tp;          // packed [W1^T | W3^T]: N = d, K = h or 2h
+  const void* dy_rows;
+  void* dx_rows;
+  void* ws;
+};
+size_t ffn_bwd_packed_workspace_bytes(int E, int max_rows, int d, int h, int act);
+// Enqueues the GEMMs; *g_rm and *h_rm receive the workspace's row-major G
+// ([max_rows, kg]) and H ([max_rows, h]) for the weight gradients.
+hipError_t launch_ffn_bwd_packed_gemms(const FfnBwdPackedArgs& a, void** g_rm, void** h_rm,
+                                       hipStream_t st);
 
 struct CombineArgs {
   int N, d, k, dtype;
@@ -148,6 +173,10 @@ struct FfnBackwardArgs {
 size_t ffn_backward_workspace_bytes(int E, int max_rows, int d, int h, int act);
 int ffn_backward_max_tiles(int E, int max_rows);
 hipError_t launch_ffn_backward(const FfnBackwardArgs& a, hipStream_t st);
+// The whole backward on packed weights: the GEMMs above, then the weight
+// gradients from the row-major G and H.
+hipError_t launch_ffn_backward_packed(const FfnBwdPackedArgs& a, float* dw1, float* dw3,
+                                      float* dw2, hipStream_t st);
 
 hipError_t launch_bias_update(int E, int N, int k, const int32_t* counts, float step,
                               float* sel_bias, hipStream_t st);

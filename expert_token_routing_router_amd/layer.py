@@ -16,7 +16,8 @@ from . import (ACT, DTYPE, TORCH_DTYPE, desc_from_workload, fused_combine, moe_b
                admission_flags, moe_dequantize_q8, moe_dispatch, moe_dispatch_ex,
                moe_dispatch_q8, moe_dispatch_rows,
                moe_dispatch_workspace_size, moe_expert_ffn,
-               moe_expert_ffn_pack_weights, moe_expert_ffn_workspace_size, moe_route,
+               moe_expert_ffn_pack_weights, moe_expert_ffn_pack_weights_t,
+               moe_expert_ffn_workspace_size, moe_route,
                moe_route_workspace_size, workspace)
 
 
@@ -43,6 +44,32 @@ def prepare_weights(cfg: dict, inp: dict, stream=None) -> dict:
     if inp.get("shared") is not None:
         sw1, sw3, sw2 = inp["shared"]
         out["shared"] = (pack(sw1, h, d), pack(sw3, h, d), pack(sw2, d, h))
+    return out
+
+
+def prepare_backward_weights(cfg: dict, inp: dict, stream=None) -> dict:
+    """Packed weights of the backward on the grouped GEMM (bf16), from the
+    plain row-major w1, w3 [E, h, d] and w2 [E, d, h] of ``inp``: w1, w3 as
+    the forward packs them, w2t = W2^T (rows h, cols d) and w13t = [W1^T | W3^T]
+    (rows d, cols h or 2h).  Done once per weight update."""
+    if cfg["dtype"] != "bf16":
+        raise ValueError("the packed backward is bf16 only")
+    d, h = cfg["d"], cfg["h"]
+    w1, w3, w2 = inp["w1"], inp.get("w3"), inp["w2"]
+    E = w1.shape[0]
+    out = {}
+    for name, w in (("w1", w1), ("w3", w3)):
+        if w is None:
+            out[name] = None
+            continue
+        wp = torch.empty_like(w)
+        moe_expert_ffn_pack_weights(E, h, d, "bf16", w, wp, stream)
+        out[name] = wp
+    out["w2t"] = torch.empty(E, h, d, dtype=w2.dtype, device=w2.device)
+    moe_expert_ffn_pack_weights_t(E, h, d, d, "bf16", w2, None, out["w2t"], stream)
+    kg = 2 * h if w3 is not None else h
+    out["w13t"] = torch.empty(E, d, kg, dtype=w1.dtype, device=w1.device)
+    moe_expert_ffn_pack_weights_t(E, d, h, kg, "bf16", w1, w3, out["w13t"], stream)
     return out
 
 

@@ -22,7 +22,8 @@
  *   moe_combine_backward, moe_permute_backward
  *                    the data path's backward: gradients of the combine's
  *                    expert terms (rows and weights) and of the permute
- *   moe_expert_ffn_backward
+ *   moe_expert_ffn_backward (moe_expert_ffn_backward_packed: on the forward's
+ *                    grouped GEMM, with weights packed once)
  *                    the expert FFN's backward: input gradients of every
  *                    expert's rows and the experts' weight gradients
  *
@@ -405,6 +406,23 @@ int moe_expert_ffn_down(int32_t num_experts, int32_t max_rows, int32_t hidden,
 int moe_expert_ffn_pack_weights(int32_t num_experts, int32_t rows, int32_t cols, int32_t dtype,
                                 const void* w, void* w_packed, void* stream);
 
+/* The same packed layout for a matrix given transposed, as the backward on
+ * the grouped GEMM needs it (moe_expert_ffn_backward_packed): per expert e the
+ * [rows, cols] matrix M_e whose columns j < cols_a are row j of wa[e] and
+ * whose columns j >= cols_a are row j - cols_a of wb[e]:
+ *   wa [E, cols_a, rows], wb [E, cols - cols_a, rows] bf16 row-major (wb
+ *   NULL exactly when cols_a == cols); w_packed [E, rows, cols] bf16.
+ * The backward takes W2^T (rows = h, cols = cols_a = d, wa = w2 [E, d, h]) and
+ * [W1^T | W3^T] (rows = d, cols_a = h, cols = 2h for SwiGLU with wa = w1, wb =
+ * w3, both [E, h, d]; cols = h and wb = NULL otherwise).  Like the forward's
+ * packing it is done once per weight update, not per step.  A permutation of
+ * the values.  Errors: MOE_ERR_INVALID_ARG (sizes, cols_a > cols, wb given or
+ * missing wrongly, null/misaligned/overlapping pointers), MOE_ERR_UNSUPPORTED
+ * (fp32; rows or cols not a multiple of 64, cols_a not of 8), MOE_ERR_HIP. */
+int moe_expert_ffn_pack_weights_t(int32_t num_experts, int32_t rows, int32_t cols_a,
+                                  int32_t cols, int32_t dtype, const void* wa, const void* wb,
+                                  void* w_packed, void* stream);
+
 /* ---------------------------------------------------------------- combine -- */
 
 /* Combine.  Glossary step 4 (outputs return to each token and are weighted by
@@ -497,6 +515,36 @@ int moe_expert_ffn_backward(int32_t num_experts, int32_t max_rows, int32_t hidde
                             const void* w1, const void* w3, const void* w2, const void* dy_rows,
                             void* dx_rows, float* dw1, float* dw3, float* dw2, void* ws,
                             size_t ws_bytes, void* stream);
+
+/* The same backward with every product on the forward's grouped GEMM
+ * (moe_expert_ffn's kernel: operands streamed into LDS, packed weights) and
+ * the same definitions, rounding points and outputs as moe_expert_ffn_backward:
+ * u (and v) are recomputed as an fp32 GEMM, g = dy W2 runs as a GEMM whose
+ * epilogue forms H, du, dv from u, v and g, and dx = [du | dv] [W1 ; W3] as
+ * the forward's down GEMM over G; the weight gradients then run as in
+ * moe_expert_ffn_backward.  Weights come packed:
+ *   w1_packed, w3_packed  moe_expert_ffn_pack_weights of w1, w3 (rows h,
+ *                         cols d), as the forward uses them;
+ *   w2t_packed            moe_expert_ffn_pack_weights_t of w2 (rows h,
+ *                         cols_a = cols = d);
+ *   w13t_packed           moe_expert_ffn_pack_weights_t of w1 (and w3):
+ *                         rows d, cols_a h, cols h (2h for SwiGLU).
+ * Other arguments as in moe_expert_ffn_backward (group_rows included); d and h
+ * must be multiples of 64.  The workspace (moe_expert_ffn_backward_packed_
+ * workspace_size: the tile plan, G in the packed layout, u and v in fp32, G
+ * and H row-major -- about max_rows * 9h * 2 bytes for SwiGLU) is needed only
+ * when max_rows > 0.  Errors as moe_expert_ffn_backward's. */
+size_t moe_expert_ffn_backward_packed_workspace_size(int32_t num_experts, int32_t max_rows,
+                                                     int32_t hidden, int32_t ffn_hidden,
+                                                     int32_t act, int32_t dtype);
+int moe_expert_ffn_backward_packed(int32_t num_experts, int32_t max_rows, int32_t hidden,
+                                   int32_t ffn_hidden, int32_t act, int32_t dtype,
+                                   const void* x_rows, const int32_t* group_offsets,
+                                   const int32_t* group_rows, const void* w1_packed,
+                                   const void* w3_packed, const void* w2t_packed,
+                                   const void* w13t_packed, const void* dy_rows, void* dx_rows,
+                                   float* dw1, float* dw3, float* dw2, void* ws, size_t ws_bytes,
+                                   void* stream);
 
 /* Backward of the router (glossary "How tokens travel between GPUs", step 1,
  * read backwards: the router's logits decide the combine weights) and of an

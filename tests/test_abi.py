@@ -400,3 +400,58 @@ def test_expert_ffn_backward_validation():
     assert call(ws_bytes=need - 1) == moe.MOE_ERR_WORKSPACE
     assert call(ws=None) == moe.MOE_ERR_WORKSPACE
     assert call(ws=ctypes.c_void_p(0x10010)) == moe.MOE_ERR_WORKSPACE  # not 256-aligned
+
+
+def test_expert_ffn_backward_packed_validation():
+    """Host-side checks of moe_expert_ffn_backward_packed (the backward's own
+    checks plus the forward GEMM's 64-grid for d and h) and of
+    moe_expert_ffn_pack_weights_t: every rejected call returns before any
+    launch."""
+    lib = moe.lib()
+    E, M, d, h = 4, 100, 64, 128
+    need = lib.moe_expert_ffn_backward_packed_workspace_size(E, M, d, h, moe.MOE_SWIGLU,
+                                                             moe.MOE_BF16)
+    assert need > lib.moe_expert_ffn_backward_workspace_size(E, M, d, h, moe.MOE_SWIGLU,
+                                                             moe.MOE_BF16)
+    for args in ((E, M, 96, h, moe.MOE_SWIGLU, moe.MOE_BF16),     # d on the 32 grid only
+                 (E, M, d, 96, moe.MOE_GELU, moe.MOE_BF16),       # h likewise
+                 (E, M, d, h, moe.MOE_SWIGLU, moe.MOE_F32),
+                 (1025, M, d, h, moe.MOE_RELU, moe.MOE_BF16)):
+        assert lib.moe_expert_ffn_backward_packed_workspace_size(*args) == 0, args
+
+    def call(E=E, M=M, d=d, h=h, act=moe.MOE_SWIGLU, dtype=moe.MOE_BF16, x=FAKE, off=FAKE,
+             w1=FAKE, w3=FAKE, w2t=FAKE, w13t=FAKE, dw3=FAKE, dy=FAKE, ws=FAKE, ws_bytes=need,
+             rows=None):
+        return lib.moe_expert_ffn_backward_packed(E, M, d, h, act, dtype, x, off, rows, w1, w3,
+                                                  w2t, w13t, dy, FAKE, FAKE, dw3, FAKE, ws,
+                                                  ws_bytes, None)
+
+    assert call(d=96) == moe.MOE_ERR_UNSUPPORTED
+    assert call(h=96) == moe.MOE_ERR_UNSUPPORTED
+    assert call(dtype=moe.MOE_F32) == moe.MOE_ERR_UNSUPPORTED
+    assert call(E=0) == moe.MOE_ERR_INVALID_ARG
+    assert call(act=3) == moe.MOE_ERR_INVALID_ARG
+    assert call(off=None) == moe.MOE_ERR_INVALID_ARG
+    for key in ("w1", "w2t", "w13t"):
+        assert call(**{key: None}) == moe.MOE_ERR_INVALID_ARG, key
+        assert call(**{key: ctypes.c_void_p(0x10008)}) == moe.MOE_ERR_INVALID_ARG, key
+    assert call(w3=None) == moe.MOE_ERR_INVALID_ARG          # SwiGLU needs W3 ...
+    assert call(dw3=None) == moe.MOE_ERR_INVALID_ARG         # ... and its gradient
+    assert call(act=moe.MOE_GELU) == moe.MOE_ERR_INVALID_ARG  # GELU takes neither
+    assert call(x=None) == moe.MOE_ERR_INVALID_ARG
+    assert call(rows=ctypes.c_void_p(0x10002)) == moe.MOE_ERR_INVALID_ARG
+    assert call(ws_bytes=need - 1) == moe.MOE_ERR_WORKSPACE
+    assert call(ws=ctypes.c_void_p(0x10010)) == moe.MOE_ERR_WORKSPACE
+
+    pack = lib.moe_expert_ffn_pack_weights_t
+    A, B, C = (ctypes.c_void_p(0x10000), ctypes.c_void_p(0x10000 + (1 << 30)),
+               ctypes.c_void_p(0x10000 + (2 << 30)))
+    assert pack(0, 64, 64, 64, moe.MOE_BF16, A, None, B, None) == moe.MOE_ERR_INVALID_ARG
+    assert pack(2, 64, 128, 64, moe.MOE_BF16, A, None, B, None) == moe.MOE_ERR_INVALID_ARG
+    assert pack(2, 64, 64, 64, moe.MOE_F32, A, None, B, None) == moe.MOE_ERR_UNSUPPORTED
+    assert pack(2, 96, 64, 64, moe.MOE_BF16, A, None, B, None) == moe.MOE_ERR_UNSUPPORTED
+    assert pack(2, 64, 60, 128, moe.MOE_BF16, A, C, B, None) == moe.MOE_ERR_UNSUPPORTED
+    assert pack(2, 64, 64, 128, moe.MOE_BF16, A, None, B, None) == moe.MOE_ERR_INVALID_ARG
+    assert pack(2, 64, 64, 64, moe.MOE_BF16, A, C, B, None) == moe.MOE_ERR_INVALID_ARG
+    assert pack(2, 64, 64, 128, moe.MOE_BF16, A, C, ctypes.c_void_p(0x10000 + 4096), None) == \
+        moe.MOE_ERR_INVALID_ARG  # overlaps wa

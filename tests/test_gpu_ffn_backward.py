@@ -54,32 +54,54 @@ def _weights(E, d, h, act, seed, scale=0.05):
     return w1, w3, w2
 
 
-def _gpu_backward(E, rows, d, h, act, x, off, w1, w3, w2, dy, sentinel=3.0):
+def _backward_call(path, E, rows, d, h, act, x, off, group_rows, w1, w3, w2, dy, dx, dw1, dw3,
+                   dw2):
+    """One FFN backward on device tensors: ``plain`` (moe_expert_ffn_backward,
+    row-major weights) or ``packed`` (moe_expert_ffn_backward_packed on the
+    forward's grouped GEMM, weights from prepare_backward_weights)."""
+    if path == "plain":
+        ws = moe.workspace(moe.moe_expert_ffn_backward_workspace_size(E, rows, d, h, act, "bf16"))
+        moe.moe_expert_ffn_backward(E, rows, d, h, act, "bf16", x, off, group_rows, w1, w3, w2,
+                                    dy, dx, dw1, dw3, dw2, ws)
+    else:
+        pw = moe.prepare_backward_weights({"dtype": "bf16", "d": d, "h": h},
+                                          {"w1": w1, "w3": w3, "w2": w2})
+        ws = moe.workspace(moe.moe_expert_ffn_backward_packed_workspace_size(E, rows, d, h, act,
+                                                                              "bf16"))
+        moe.moe_expert_ffn_backward_packed(E, rows, d, h, act, "bf16", x, off, group_rows,
+                                           pw["w1"], pw["w3"], pw["w2t"], pw["w13t"], dy, dx,
+                                           dw1, dw3, dw2, ws)
+
+
+def _gpu_backward(E, rows, d, h, act, x, off, w1, w3, w2, dy, sentinel=3.0, path="plain"):
     dev = lambda t: None if t is None else t.cuda()  # noqa: E731
     sw = act == "swiglu"
     dx = torch.full((max(rows, 1), d), sentinel, dtype=BF16, device="cuda")
     dw1 = torch.full((E, h, d), 9.0, device="cuda")
     dw3 = torch.full((E, h, d), 9.0, device="cuda") if sw else None
     dw2 = torch.full((E, d, h), 9.0, device="cuda")
-    ws = moe.workspace(moe.moe_expert_ffn_backward_workspace_size(E, rows, d, h, act, "bf16"))
-    moe.moe_expert_ffn_backward(E, rows, d, h, act, "bf16", dev(x), dev(off), None, dev(w1),
-                                dev(w3), dev(w2), dev(dy), dx, dw1, dw3, dw2, ws)
+    _backward_call(path, E, rows, d, h, act, dev(x), dev(off), None, dev(w1), dev(w3), dev(w2),
+                   dev(dy), dx, dw1, dw3, dw2)
     torch.cuda.synchronize()
     return dx.cpu(), dw1.cpu(), None if dw3 is None else dw3.cpu(), dw2.cpu()
 
 
+PATHS = ["plain", "packed"]
+
+
+@pytest.mark.parametrize("path", PATHS)
 @pytest.mark.parametrize("name", list(SHAPES))
-def test_ffn_backward_ragged_segments(name):
+def test_ffn_backward_ragged_segments(name, path):
     cfg, E, rows = SHAPES[name]
     d, h, act = cfg["d"], cfg["h"], cfg["act"]
-    print(f"[ffn backward {name}] E={E} rows={rows} d={d} h={h} {act}", flush=True)
+    print(f"[ffn backward {name} {path}] E={E} rows={rows} d={d} h={h} {act}", flush=True)
     off = _segments(E, rows, seed=rows)
     g = torch.Generator().manual_seed(d + h)
     x = torch.randn(rows, d, generator=g).to(BF16)
     dy = (torch.randn(rows, d, generator=g) * 0.5).to(BF16)
     w1, w3, w2 = _weights(E, d, h, act, seed=E + d)
     dx, dw1, dw3, dw2 = _gpu_backward(E, rows, d, h, act, x, torch.from_numpy(off), w1, w3, w2,
-                                      dy)
+                                      dy, path=path)
     oracle.set_threads(threads())
     r_dx, r_dw1, r_dw3, r_dw2 = oracle.expert_ffn_backward("bf16", act, n(x), off, n(w1), n(w3),
                                                            n(w2), n(dy))
@@ -153,15 +175,16 @@ def test_layer_backward_chain(name):
         assert err <= TOL[dt], f"{key} max rel err {err:.3e}"
 
 
+@pytest.mark.parametrize("path", PATHS)
 @pytest.mark.parametrize("name,kw", [("zipf", dict(cf=1.0)), ("switch", {})])
-def test_ffn_backward_padded_layout_equals_compact(name, kw):
+def test_ffn_backward_padded_layout_equals_compact(name, kw, path):
     """The layer's backward on the capacity-padded layout, with NaN planted in
     every padding row of x_perm and dy_perm (rows no call is obliged to write):
     with group_rows = admitted the FFN backward leaves them out, so the weight
     gradients and every admitted row's dx equal the compact layout's bit for
     bit (each expert's rows, and their order, are the same in both layouts)."""
     cfg = W.with_(W.small(name), **kw)
-    print(f"[ffn backward padded vs compact] {name} {kw}", flush=True)
+    print(f"[ffn backward padded vs compact] {name} {kw} {path}", flush=True)
     dev = lambda t: None if t is None else t.cuda()  # noqa: E731
     inp_cpu = W.make_inputs(cfg)
     inp = moe.prepare_weights(cfg, {k: (dev(v) if isinstance(v, torch.Tensor) else v)
@@ -186,11 +209,10 @@ def test_ffn_backward_padded_layout_equals_compact(name, kw):
         dw1 = torch.empty(E, h, d, device="cuda")
         dw3 = torch.empty(E, h, d, device="cuda") if sw else None
         dw2 = torch.empty(E, d, h, device="cuda")
-        ws = moe.workspace(moe.moe_expert_ffn_backward_workspace_size(E, rows, d, h, act, "bf16"))
-        moe.moe_expert_ffn_backward(E, rows, d, h, act, "bf16", buf.x_perm, buf.expert_offsets,
-                                    buf.admitted if layout == "padded" else None, inp_cpu["w1"].cuda(),
-                                    dev(inp_cpu["w3"]), inp_cpu["w2"].cuda(), dy_perm, dx_perm,
-                                    dw1, dw3, dw2, ws)
+        _backward_call(path, E, rows, d, h, act, buf.x_perm, buf.expert_offsets,
+                       buf.admitted if layout == "padded" else None, inp_cpu["w1"].cuda(),
+                       dev(inp_cpu["w3"]), inp_cpu["w2"].cuda(), dy_perm, dx_perm, dw1, dw3,
+                       dw2)
         dx = torch.empty(N, d, dtype=BF16, device="cuda")
         moe.moe_permute_backward(buf.desc, dx_perm, buf.row_of_slot, dx, num_rows=rows)
         torch.cuda.synchronize()
@@ -206,20 +228,22 @@ def test_ffn_backward_padded_layout_equals_compact(name, kw):
     assert torch.equal(cdx.view(torch.int16), pdx.view(torch.int16))
 
 
-def test_ffn_backward_full_switch_sampled():
+@pytest.mark.parametrize("path", PATHS)
+def test_ffn_backward_full_switch_sampled(path):
     """The full Switch shape in the launch configuration the benchmark's
     backward pass uses: input gradients of 8 rows spread over the batch, and
     dw1 / dw2 of one whole expert, from the oracle's per-row backward."""
     cfg = W.full("switch")
     N, d, h, E, act = cfg["N"], cfg["d"], cfg["h"], cfg["E"], cfg["act"]
-    print(f"[ffn backward full switch] rows={N} d={d} h={h} E={E}", flush=True)
+    print(f"[ffn backward full switch {path}] rows={N} d={d} h={h} E={E}", flush=True)
     inp = W.make_inputs(cfg)
     x, w1, w2 = inp["x"], inp["w1"], inp["w2"]
     g = torch.Generator().manual_seed(7)
     dy = (torch.randn(N, d, generator=g) * 0.5).to(BF16)
     counts = np.bincount(np.random.default_rng(3).integers(0, E, N), minlength=E)
     off = np.concatenate([[0], np.cumsum(counts)]).astype(np.int32)
-    dx, dw1, _, dw2 = _gpu_backward(E, N, d, h, act, x, torch.from_numpy(off), w1, None, w2, dy)
+    dx, dw1, _, dw2 = _gpu_backward(E, N, d, h, act, x, torch.from_numpy(off), w1, None, w2, dy,
+                                    path=path)
     xn, dyn, w1n, w2n = n(x), n(dy), n(w1), n(w2)
     expert_of = np.searchsorted(off, np.arange(N), side="right") - 1
     for r in np.linspace(0, N - 1, 8).astype(int):
@@ -242,3 +266,43 @@ def test_ffn_backward_full_switch_sampled():
     assert err <= TOL["bf16"], f"dw1[{e}] max rel err {err:.3e}"
     err = rel_err(dw2[e], torch.from_numpy(r_dw2))
     assert err <= TOL["bf16"], f"dw2[{e}] max rel err {err:.3e}"
+
+
+# The packed backward on 192-row tiles: h = 2048 takes the wide recompute and
+# g GEMMs (256 columns per tile; SwiGLU 256 of W1 and of W3), d = 1024 the
+# 256-column dx GEMM; experts on the fragment edges of a 192-row tile, one
+# past it (split in two), 37 rows outside every segment.
+WIDE_COUNTS = [0, 1, 31, 32, 33, 63, 64, 65, 96, 127, 128, 129, 160, 191, 192, 193]
+
+
+@pytest.mark.parametrize("act", ["swiglu", "gelu"])
+def test_ffn_backward_packed_wide_tiles(act):
+    E, d, h = len(WIDE_COUNTS), 1024, 2048
+    used = sum(WIDE_COUNTS)
+    rows = used + 37
+    assert 32 * E < rows <= 128 * E, "must take the 192-row tiles"
+    print(f"[ffn backward packed wide] E={E} rows={rows} d={d} h={h} {act}", flush=True)
+    off = np.concatenate([[0], np.cumsum(WIDE_COUNTS)]).astype(np.int32)
+    g = torch.Generator().manual_seed(h + E)
+    x = torch.randn(rows, d, generator=g).to(BF16)
+    dy = (torch.randn(rows, d, generator=g) * 0.5).to(BF16)
+    w1, w3, w2 = _weights(E, d, h, act, seed=d, scale=0.03)
+    dx, dw1, dw3, dw2 = _gpu_backward(E, rows, d, h, act, x, torch.from_numpy(off), w1, w3, w2,
+                                      dy, path="packed")
+    oracle.set_threads(threads())
+    r_dx, r_dw1, r_dw3, r_dw2 = oracle.expert_ffn_backward("bf16", act, n(x), off, n(w1), n(w3),
+                                                           n(w2), n(dy))
+    err = rel_err(dx[:used].float(), as_tensor(r_dx[:used], "bf16").float())
+    assert err <= TOL["bf16"], f"dx max rel err {err:.3e}"
+    assert bool((dx[used:] == 3.0).all()), "rows outside every segment must stay untouched"
+    for e in range(E):
+        a, b = int(off[e]), int(off[e + 1])
+        if b > a:
+            ee = rel_err(dx[a:b].float(), as_tensor(r_dx[a:b], "bf16").float())
+            assert ee <= TOL["bf16"], f"dx of expert {e} ({b - a} rows): {ee:.3e}"
+    for got, ref, key in ((dw1, r_dw1, "dw1"), (dw3, r_dw3, "dw3"), (dw2, r_dw2, "dw2")):
+        if ref is None:
+            continue
+        err = rel_err(got, torch.from_numpy(ref))
+        assert err <= TOL["bf16"], f"{key} max rel err {err:.3e}"
+        assert bool((got[0] == 0).all()), f"{key}: an expert with no rows gets zeros"
