@@ -446,26 +446,25 @@ hipError_t launch_ffn_backward(const FfnBackwardArgs& a, hipStream_t st) {
 }
 
 // The backward on packed weights: u (v), g and dx on the forward's grouped
-// GEMM (LDS-DMA ring, packed weights), then the weight gradients as above from
-// the row-major G and H those GEMMs leave in the workspace.
+// GEMM (LDS-DMA ring, packed weights), then the weight gradients on the same
+// GEMM from G, H, x and dy transposed per expert (ffn.hip).  An empty batch
+// only zeroes the weight gradients.
 hipError_t launch_ffn_backward_packed(const FfnBwdPackedArgs& a, float* dw1, float* dw3,
                                       float* dw2, hipStream_t st) {
+  if (a.max_rows == 0) {
+    const size_t hd = (size_t)a.E * a.h * a.d;
+    hipError_t err = launch_zero_f32(dw1, hd, st);
+    if (err == hipSuccess && dw3) err = launch_zero_f32(dw3, hd, st);
+    if (err == hipSuccess) err = launch_zero_f32(dw2, hd, st);
+    return err;
+  }
   void* gv = nullptr;
   void* hv = nullptr;
   const hipError_t err = launch_ffn_bwd_packed_gemms(a, &gv, &hv, st);
   if (err != hipSuccess) return err;
-  const int kg = a.act == kSwiglu ? 2 * a.h : a.h;
-  const bf16_t* x = static_cast<const bf16_t*>(a.x_rows);
-  const bf16_t* dy = static_cast<const bf16_t*>(a.dy_rows);
-  const bf16_t* G = static_cast<const bf16_t*>(gv);
-  const bf16_t* Hbuf = static_cast<const bf16_t*>(hv);
-  const dim3 g13(((a.d + kTM - 1) / kTM) * ((kg + kTN - 1) / kTN), a.E);
-  bwd_wgrad<<<g13, kThreads, 0, st>>>(x, a.d, G, kg, a.offsets, a.group_rows, a.max_rows, a.d,
-                                      kg, a.h, dw1, dw3);
-  const dim3 g2(((a.h + kTM - 1) / kTM) * ((a.d + kTN - 1) / kTN), a.E);
-  bwd_wgrad<<<g2, kThreads, 0, st>>>(Hbuf, a.h, dy, a.d, a.offsets, a.group_rows, a.max_rows,
-                                     a.h, a.d, a.d, dw2, nullptr);
-  return hipGetLastError();
+  char* wg = static_cast<char*>(a.ws) +
+             ffn_bwd_gemms_workspace_bytes(a.E, a.max_rows, a.d, a.h, a.act);
+  return launch_ffn_bwd_wgrad(a, gv, hv, wg, dw1, dw3, dw2, st);
 }
 
 }  // namespace moe

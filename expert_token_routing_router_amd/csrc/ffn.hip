@@ -265,14 +265,25 @@ constexpr int kWeightCpol = 2 | 16;
 //   rounded to bf16: H row-major to be.H ([rows, N]); G = [du | dv] row-major
 //   to be.G ([rows, kg], kg = N or 2N) and in the packed layout to C (K = kg:
 //   dv's columns follow du's), where the dx GEMM reads it as its A.
-enum { kUpGemm = 0, kDownGemm = 1, kDownFused = 2, kUpRawF32 = 3, kBwdG = 4 };
+// MODE kWgrad: the weight gradients, C[m, n] = sum over an expert's rows r of
+//   A[r][m] B[r][n] (dW1 | dW3 from G and x, dW2 from dy and H): per expert a
+//   GEMM whose reduction runs over its rows, padded to kst[e+1] - kst[e]
+//   stages of 32 rows (zero rows past the segment).  A comes transposed in the
+//   packed-A layout (block (kst[e] + t) * M/16 + m/16, as the down GEMM's A with
+//   groups over m), B transposed in the weights' slab layout from element
+//   kst[e] * 32 * N on (slab s of the expert at s * kt_e * SR * 32).  Output
+//   rows m < split go to U ([E, split, N] fp32), the others to V ([E, M -
+//   split, N]); an expert without rows gets zeros.
+enum { kUpGemm = 0, kDownGemm = 1, kDownFused = 2, kUpRawF32 = 3, kBwdG = 4, kWgrad = 5 };
 
 struct BwdEpiArgs {
-  float* U;       // kUpRawF32: written; kBwdG: read
-  float* V;       // SwiGLU only
+  float* U;       // kUpRawF32: written; kBwdG: read; kWgrad: the first output
+  float* V;       // SwiGLU only; kWgrad: the second output
   bf16_t* G;      // kBwdG: [du | dv] row-major, kg columns
   bf16_t* H;      // kBwdG: H row-major, N columns
-  int kg;
+  int kg;         // kBwdG: columns of G; kWgrad: rows of the first output
+  int M;          // kWgrad: rows of C
+  const int32_t* kst;  // kWgrad: stage offset of each expert, [E + 1]
 };
 
 template <int BM, int BN, int ACT, int MODE>
@@ -332,6 +343,8 @@ void grouped_gemm_bf16(
   const int4 tile = tiles[mt];
   const int e = tile.x, r0 = tile.y, r1 = tile.z, g0 = tile.w;
   const int n0 = nt * BN;
+  // K stages of this tile: fixed, or (kWgrad) the expert's own.
+  const int ktiles = MODE == kWgrad ? be.kst[e + 1] - be.kst[e] : K / BK;
   // wave is uniform: readfirstlane lets every per-wave index live in SGPRs.
   const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wm = wave / 4, wn = wave % 4;
@@ -387,12 +400,13 @@ void grouped_gemm_bf16(
     // A wave's LB loads are LB consecutive 16-row groups of one matrix
     // (BROWS / 4 rows; for SwiGLU BN is a multiple of that).
     const int br0 = grp * LB * RPL;
-    sbase = ((DUAL && br0 >= BN) ? B2 : B) + (size_t)e * N * K;
+    sbase = ((DUAL && br0 >= BN) ? B2 : B) +
+            (MODE == kWgrad ? (size_t)be.kst[e] * BK * N : (size_t)e * N * K);
 #pragma unroll
     for (int i = 0; i < LMAX; ++i) {
       const int br = (grp * LB + (i < LB ? i : 0)) * RPL;  // first weight row in the stage
       const int n = min(n0 + (DUAL ? br % BN : br), N - RPL);  // 16-row group, clamped
-      soff[i] = (uint32_t)(((size_t)(n / SR) * (K / BK) * SR * BK + (n % SR) / RPL * 512) * 2);
+      soff[i] = (uint32_t)(((size_t)(n / SR) * ktiles * SR * BK + (n % SR) / RPL * 512) * 2);
     }
   }
 
@@ -423,7 +437,6 @@ void grouped_gemm_bf16(
   // set 1 step 1.  Each set is refilled while the other one feeds the MFMAs.
   bf16x8_t xf0[FM], wf0[FN], vf0[FN2];
   bf16x8_t xf1[FM], wf1[FN], vf1[FN2];
-  const int ktiles = K / BK;
 
   // Issue the loads of K tile kt_ into ring slot slot_; the A waves issue
   // NA_ loads (units 4 i + grp), the weight waves LB.  The stream's resource
@@ -747,6 +760,23 @@ void grouped_gemm_bf16(
       }                                                                                    \
     }                                                                                      \
   } while (0)
+  // Weight-gradient epilogue (kWgrad): fp32, rows split between the outputs.
+#define MOE_EPILOGUE_WG(FA_)                                                               \
+  do {                                                                                     \
+    _Pragma("unroll") for (int i = 0; i < (FA_); ++i) {                                    \
+      const int m = r0 + (2 * i + wm) * 32 + (lane & 31);                                  \
+      float* orow_ = m < be.kg ? be.U + ((size_t)e * be.kg + m) * N                        \
+                               : be.V + ((size_t)e * (be.M - be.kg) + (m - be.kg)) * N;     \
+      _Pragma("unroll") for (int j = 0; j < FN; ++j)                                       \
+      _Pragma("unroll") for (int g = 0; g < 4; ++g) {                                      \
+        const int col = n0 + wn * WN + j * 32 + 8 * g + 4 * (lane >> 5);                   \
+        if (m < r1 && col < N)                                                             \
+          *reinterpret_cast<floatx4*>(orow_ + col) =                                       \
+              floatx4{acc[i][j][4 * g], acc[i][j][4 * g + 1], acc[i][j][4 * g + 2],        \
+                      acc[i][j][4 * g + 3]};                                               \
+      }                                                                                    \
+    }                                                                                      \
+  } while (0)
   // One self-contained copy (accumulators, K loop, epilogue) per number of
   // live fragments, so no accumulator value crosses from one copy to another.
 #define MOE_TILE(FA_)                                                                      \
@@ -757,6 +787,7 @@ void grouped_gemm_bf16(
     if constexpr (FUSED) MOE_EPILOGUE_FUSED(FA_);                                          \
     else if constexpr (MODE == kUpRawF32) MOE_EPILOGUE_RAW(FA_);                           \
     else if constexpr (MODE == kBwdG) MOE_EPILOGUE_BWDG(FA_);                              \
+    else if constexpr (MODE == kWgrad) MOE_EPILOGUE_WG(FA_);                               \
     else MOE_EPILOGUE(FA_);                                                                \
   } while (0)
 
@@ -774,6 +805,7 @@ void grouped_gemm_bf16(
 #undef MOE_EPILOGUE_FUSED
 #undef MOE_EPILOGUE_RAW
 #undef MOE_EPILOGUE_BWDG
+#undef MOE_EPILOGUE_WG
 #undef MOE_K_LOOP
 #undef MOE_LOAD_KK
 #undef MOE_MFMA_KK
@@ -1177,9 +1209,23 @@ BwdLayout bwd_layout(int E, int max_rows, int h, int act) {
 }
 }  // namespace
 
-size_t ffn_bwd_packed_workspace_bytes(int E, int max_rows, int d, int h, int act) {
+size_t ffn_bwd_gemms_workspace_bytes(int E, int max_rows, int d, int h, int act) {
   (void)d;
   return bwd_layout(E, max_rows, h, act).total;
+}
+
+size_t ffn_bwd_packed_workspace_bytes(int E, int max_rows, int d, int h, int act) {
+  return ffn_bwd_gemms_workspace_bytes(E, max_rows, d, h, act) +
+         ffn_bwd_wgrad_workspace_bytes(E, max_rows, d, h, act);
+}
+
+hipError_t launch_zero_f32(float* p, size_t n, hipStream_t st) {
+  const size_t n4 = n / 4;  // n is a multiple of 64 here
+  if (n4 > 0) {
+    const int blocks = (int)std::min<size_t>((n4 + 255) / 256, 4096);
+    zero_f32x4<<<blocks, 256, 0, st>>>(reinterpret_cast<floatx4*>(p), n4);
+  }
+  return hipGetLastError();
 }
 
 hipError_t launch_ffn_bwd_packed_gemms(const FfnBwdPackedArgs& a, void** g_rm, void** h_rm,
@@ -1241,6 +1287,12 @@ hipError_t launch_ffn_bwd_packed_gemms(const FfnBwdPackedArgs& a, void** g_rm, v
         else launch_bf16<S, 128, ACT_SWIGLU, kBwdG>(DY, W2T, nullptr, GP, a.d, a.h, f, st, be); \
         break;                                                                             \
     }                                                                                      \
+    if constexpr (S == kGemmBMMid) {                                                       \
+      if (a.d >= 4096) {                                                                   \
+        launch_bf16<S, 512, ACT_NONE, kDownGemm>(GP, W13T, nullptr, DX, kg, a.d, f, st);   \
+        break;                                                                             \
+      }                                                                                    \
+    }                                                                                      \
     if (a.d >= 1024)                                                                       \
       launch_bf16<S, 256, ACT_NONE, kDownGemm>(GP, W13T, nullptr, DX, kg, a.d, f, st);     \
     else                                                                                   \
@@ -1250,6 +1302,180 @@ hipError_t launch_ffn_bwd_packed_gemms(const FfnBwdPackedArgs& a, void** g_rm, v
   else if (bm == kGemmBMSmall) MOE_BWD_TILES(kGemmBMSmall);
   else MOE_BWD_TILES(kGemmBM);
 #undef MOE_BWD_TILES
+  return hipGetLastError();
+}
+
+// ------------------------------------------------- weight gradients ---
+
+// Segments as the backward clamps them (to max_rows and, when given, to the
+// first group_rows[e] rows), their stage offsets kst[e] (sum of ceil(rows /
+// 32) before e; kst[E] = the total), and the tiles of the two weight-gradient
+// GEMMs: BM rows of M1 (= kg) or M2 (= d) for every expert, {e, m0, m1,
+// kst[e] M / 16 + m0 / 16}.
+__global__ __launch_bounds__(1024) void wgrad_plan(const int32_t* __restrict__ offsets,
+                                                   const int32_t* __restrict__ group_rows, int E,
+                                                   int max_rows, int BM, int M1, int M2,
+                                                   int2* __restrict__ seg, int32_t* __restrict__ kst,
+                                                   int4* __restrict__ tiles1,
+                                                   int4* __restrict__ tiles2,
+                                                   int32_t* __restrict__ counts) {
+  __shared__ int32_t wsum[16];
+  const int e = threadIdx.x;
+  int lo = 0, hi = 0;
+  if (e < E) {
+    lo = min(offsets[e], max_rows);
+    hi = min(offsets[e + 1], max_rows);
+    if (group_rows) hi = min(hi, lo + max(group_rows[e], 0));
+    hi = max(hi, lo);
+  }
+  const int n = (hi - lo + 31) / 32;
+  const int incl = block_scan_1024(n, wsum);
+  if (e < E) {
+    seg[e] = make_int2(lo, hi);
+    kst[e] = incl - n;
+    if (e == E - 1) kst[E] = incl;
+    const int mt1 = (M1 + BM - 1) / BM, mt2 = (M2 + BM - 1) / BM;
+    for (int i = 0; i < mt1; ++i)
+      tiles1[e * mt1 + i] = make_int4(e, i * BM, min(M1, (i + 1) * BM),
+                                      (incl - n) * (M1 / 16) + i * BM / 16);
+    for (int i = 0; i < mt2; ++i)
+      tiles2[e * mt2 + i] = make_int4(e, i * BM, min(M2, (i + 1) * BM),
+                                      (incl - n) * (M2 / 16) + i * BM / 16);
+    if (e == 0) {
+      counts[0] = E * mt1;
+      counts[1] = E * mt2;
+    }
+  }
+}
+
+// Row-major activations src [rows, C] (bf16) of every expert's segment, in
+// stages of 32 rows (zero past the segment), transposed into 1-KB blocks of
+// 16 columns x 32 rows laid out as the GEMM stages them (16-byte position L:
+// column 16q + L/4, logical chunk (L % 4) ^ swz4(L/4) of the 32 rows): the
+// packed-A order (block (kst[e] + t) C/16 + q) or, with layoutB, the weights'
+// slab order (slab s = q / (SR/16) of the expert at s kt_e SR/16 blocks, then
+// stage t, then the block in the slab).  One block of 256 threads per stage
+// and 256 columns, through an LDS tile.
+__global__ __launch_bounds__(256) void pack_rows_t_bf16(const bf16_t* __restrict__ src, int C,
+                                                        const int2* __restrict__ seg,
+                                                        const int32_t* __restrict__ kst, int E,
+                                                        int layoutB, bf16_t* __restrict__ out) {
+  __shared__ __attribute__((aligned(16))) bf16_t tile[32][256 + 8];
+  const int sg = blockIdx.x;
+  if (sg >= kst[E]) return;
+  int lo = 0, hi = E - 1;  // the expert e with kst[e] <= sg < kst[e + 1]
+  while (lo < hi) {
+    const int mid = (lo + hi + 1) / 2;
+    if (kst[mid] <= sg) lo = mid; else hi = mid - 1;
+  }
+  const int e = lo, t = sg - kst[e], kte = kst[e + 1] - kst[e];
+  const int2 sgm = seg[e];
+  const int r0 = sgm.x + 32 * t;
+  const int c0 = blockIdx.y * 256;
+  const int tid = threadIdx.x;
+#pragma unroll
+  for (int u = 0; u < 4; ++u) {
+    const int id = tid + 256 * u, row = id / 32, cc = id % 32, col = c0 + cc * 8;
+    u32x4 v = {0u, 0u, 0u, 0u};
+    if (r0 + row < sgm.y && col < C) v = *reinterpret_cast<const u32x4*>(src + (size_t)(r0 + row) * C + col);
+    *reinterpret_cast<u32x4*>(&tile[row][cc * 8]) = v;
+  }
+  __syncthreads();
+  const int SR = packed_slab_rows(C), bps = SR / 16;
+#pragma unroll
+  for (int u = 0; u < 4; ++u) {
+    const int id = tid + 256 * u, ql = id / 64, L = id % 64;
+    const int cl = 16 * ql + L / 4;
+    if (c0 + 16 * ql >= C) continue;
+    const int k0 = 8 * ((L % 4) ^ swz4(L / 4));
+    uint32_t w4[4];
+#pragma unroll
+    for (int q2 = 0; q2 < 4; ++q2)
+      w4[q2] = (uint32_t)tile[k0 + 2 * q2][cl] | ((uint32_t)tile[k0 + 2 * q2 + 1][cl] << 16);
+    const int q = (c0 >> 4) + ql;
+    const size_t blk = layoutB ? (size_t)kst[e] * (C / 16) + (size_t)(q / bps) * kte * bps +
+                                     (size_t)t * bps + (q % bps)
+                               : ((size_t)kst[e] + t) * (C / 16) + q;
+    *reinterpret_cast<u32x4*>(out + blk * 512 + L * 8) = u32x4{w4[0], w4[1], w4[2], w4[3]};
+  }
+}
+
+namespace {
+constexpr int kWgBM = 128;
+struct WgLayout {
+  size_t seg, kst, counts, tiles1, tiles2, gt, xt, dyt, ht, total;
+};
+WgLayout wg_layout(size_t base, int E, int max_rows, int d, int h, int act) {
+  const int kg = act == ACT_SWIGLU ? 2 * h : h;
+  const size_t stages = (size_t)(max_rows + 31) / 32 + E;
+  WgLayout l;
+  l.seg = base;
+  l.kst = l.seg + align256((size_t)E * sizeof(int2));
+  l.counts = l.kst + align256((size_t)(E + 1) * sizeof(int32_t));
+  l.tiles1 = l.counts + align256(2 * sizeof(int32_t));
+  l.tiles2 = l.tiles1 + align256((size_t)E * ((kg + kWgBM - 1) / kWgBM) * sizeof(int4));
+  l.gt = l.tiles2 + align256((size_t)E * ((d + kWgBM - 1) / kWgBM) * sizeof(int4));
+  l.xt = l.gt + align256(stages * 32 * kg * 2);
+  l.dyt = l.xt + align256(stages * 32 * d * 2);
+  l.ht = l.dyt + align256(stages * 32 * d * 2);
+  l.total = l.ht + align256(stages * 32 * h * 2);
+  return l;
+}
+
+template <int BN>
+void launch_wgrad_gemm(const bf16_t* A, const bf16_t* B, int N, const int4* tiles,
+                       const int32_t* count, int m_tiles_max, int ldg, BwdEpiArgs be,
+                       hipStream_t st) {
+  const int nt = (N + BN - 1) / BN;
+  grouped_gemm_bf16<kWgBM, BN, ACT_NONE, kWgrad><<<grid_of(m_tiles_max, nt), kGemmWaves * 64, 0,
+                                                   st>>>(A, B, nullptr, nullptr, 0, N, tiles,
+                                                         count, nt, ldg, 1, FusedCombineArgs{}, be);
+}
+}  // namespace
+
+size_t ffn_bwd_wgrad_workspace_bytes(int E, int max_rows, int d, int h, int act) {
+  return wg_layout(0, E, max_rows, d, h, act).total;
+}
+
+hipError_t launch_ffn_bwd_wgrad(const FfnBwdPackedArgs& a, const void* g_rm, const void* h_rm,
+                                void* ws, float* dw1, float* dw3, float* dw2, hipStream_t st) {
+  const int kg = a.act == ACT_SWIGLU ? 2 * a.h : a.h;
+  const WgLayout l = wg_layout(0, a.E, a.max_rows, a.d, a.h, a.act);
+  char* w = static_cast<char*>(ws);
+  int2* seg = reinterpret_cast<int2*>(w + l.seg);
+  int32_t* kst = reinterpret_cast<int32_t*>(w + l.kst);
+  int32_t* counts = reinterpret_cast<int32_t*>(w + l.counts);
+  int4* tiles1 = reinterpret_cast<int4*>(w + l.tiles1);
+  int4* tiles2 = reinterpret_cast<int4*>(w + l.tiles2);
+  bf16_t* GT = reinterpret_cast<bf16_t*>(w + l.gt);
+  bf16_t* XT = reinterpret_cast<bf16_t*>(w + l.xt);
+  bf16_t* DYT = reinterpret_cast<bf16_t*>(w + l.dyt);
+  bf16_t* HT = reinterpret_cast<bf16_t*>(w + l.ht);
+  wgrad_plan<<<1, 1024, 0, st>>>(a.offsets, a.group_rows, a.E, a.max_rows, kWgBM, kg, a.d, seg,
+                                 kst, tiles1, tiles2, counts);
+  if (a.max_rows > 0) {
+    const int stages = (a.max_rows + 31) / 32 + a.E;
+    auto pack = [&](const void* src, int C, int layoutB, bf16_t* out) {
+      pack_rows_t_bf16<<<dim3(stages, (C + 255) / 256), 256, 0, st>>>(
+          static_cast<const bf16_t*>(src), C, seg, kst, a.E, layoutB, out);
+    };
+    pack(g_rm, kg, 0, GT);
+    pack(a.x_rows, a.d, 1, XT);
+    pack(a.dy_rows, a.d, 0, DYT);
+    pack(h_rm, a.h, 1, HT);
+  }
+  const int mt1 = (kg + kWgBM - 1) / kWgBM, mt2 = (a.d + kWgBM - 1) / kWgBM;
+  // dW1 | dW3 [kg, d] = G^T x; dW2 [d, h] = dy^T H.
+  BwdEpiArgs b1{dw1, dw3, nullptr, nullptr, a.h, kg, kst};
+  BwdEpiArgs b2{dw2, nullptr, nullptr, nullptr, a.d, a.d, kst};
+  if (a.d >= 1024)
+    launch_wgrad_gemm<512>(GT, XT, a.d, tiles1, counts, a.E * mt1, kg / 16, b1, st);
+  else
+    launch_wgrad_gemm<256>(GT, XT, a.d, tiles1, counts, a.E * mt1, kg / 16, b1, st);
+  if (a.h >= 1024)
+    launch_wgrad_gemm<512>(DYT, HT, a.h, tiles2, counts + 1, a.E * mt2, a.d / 16, b2, st);
+  else
+    launch_wgrad_gemm<256>(DYT, HT, a.h, tiles2, counts + 1, a.E * mt2, a.d / 16, b2, st);
   return hipGetLastError();
 }
 

@@ -121,10 +121,19 @@ struct FfnBwdPackedArgs {
   void* ws;
 };
 size_t ffn_bwd_packed_workspace_bytes(int E, int max_rows, int d, int h, int act);
+// The GEMMs' share of it (the weight gradients' workspace follows).
+size_t ffn_bwd_gemms_workspace_bytes(int E, int max_rows, int d, int h, int act);
+hipError_t launch_zero_f32(float* p, size_t n, hipStream_t st);
 // Enqueues the GEMMs; *g_rm and *h_rm receive the workspace's row-major G
 // ([max_rows, kg]) and H ([max_rows, h]) for the weight gradients.
 hipError_t launch_ffn_bwd_packed_gemms(const FfnBwdPackedArgs& a, void** g_rm, void** h_rm,
                                        hipStream_t st);
+// The weight gradients on the grouped GEMM from the row-major G and H (and
+// x, dy): transposed per expert into the GEMM's operand layouts, in a
+// workspace of ffn_bwd_wgrad_workspace_bytes (256-aligned).
+size_t ffn_bwd_wgrad_workspace_bytes(int E, int max_rows, int d, int h, int act);
+hipError_t launch_ffn_bwd_wgrad(const FfnBwdPackedArgs& a, const void* g_rm, const void* h_rm,
+                                void* ws, float* dw1, float* dw3, float* dw2, hipStream_t st);
 
 struct CombineArgs {
   int N, d, k, dtype;

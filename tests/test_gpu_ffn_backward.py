@@ -306,3 +306,26 @@ def test_ffn_backward_packed_wide_tiles(act):
         err = rel_err(got, torch.from_numpy(ref))
         assert err <= TOL["bf16"], f"{key} max rel err {err:.3e}"
         assert bool((got[0] == 0).all()), f"{key}: an expert with no rows gets zeros"
+
+
+@pytest.mark.parametrize("act", ["swiglu", "gelu"])
+def test_ffn_backward_packed_empty_batch(act):
+    """No rows: every weight gradient is written as zeros, nothing else read
+    (no workspace, no activations)."""
+    E, d, h = 3, 64, 128
+    sw = act == "swiglu"
+    w1, w3, w2 = _weights(E, d, h, act, seed=5)
+    pw = moe.prepare_backward_weights({"dtype": "bf16", "d": d, "h": h},
+                                      {"w1": w1.cuda(), "w3": None if w3 is None else w3.cuda(),
+                                       "w2": w2.cuda()})
+    off = torch.zeros(E + 1, dtype=torch.int32, device="cuda")
+    dw1 = torch.full((E, h, d), 9.0, device="cuda")
+    dw3 = torch.full((E, h, d), 9.0, device="cuda") if sw else None
+    dw2 = torch.full((E, d, h), 9.0, device="cuda")
+    moe.moe_expert_ffn_backward_packed(E, 0, d, h, act, "bf16", None, off, None, pw["w1"],
+                                       pw["w3"], pw["w2t"], pw["w13t"], None, None, dw1, dw3, dw2,
+                                       None)
+    torch.cuda.synchronize()
+    for t in (dw1, dw3, dw2):
+        if t is not None:
+            assert bool((t == 0).all())
