@@ -136,6 +136,55 @@ def read_clocks() -> dict:
     return {"clocks": "unavailable (no readable pp_dpm_* in sysfs)"}
 
 
+class ClockSampler:
+    """Samples the current gfx clock (the marked line of pp_dpm_sclk, in MHz)
+    from a thread while the GPU works: under load the chip runs below its
+    2.4 GHz peak clock, and the MFMA peak scales with it.  In-process sysfs
+    reads only; a no-op when the file is missing."""
+
+    def __init__(self, sysfs, period_s=0.004):
+        import threading
+        self.path = os.path.join(sysfs, "pp_dpm_sclk") if sysfs else None
+        self.period, self.mhz = period_s, []
+        self.stop_ev = threading.Event()
+        self.thread = threading.Thread(target=self._loop, daemon=True)
+
+    def _read(self):
+        with open(self.path) as f:
+            for line in f:
+                line = line.strip()
+                if line.endswith("*"):
+                    num = "".join(ch for ch in line.split(":", 1)[-1] if ch.isdigit())
+                    return int(num) if num else None
+        return None
+
+    def _loop(self):
+        while not self.stop_ev.is_set():
+            try:
+                v = self._read()
+            except OSError:
+                return
+            if v:
+                self.mhz.append(v)
+            self.stop_ev.wait(self.period)
+
+    def __enter__(self):
+        if self.path and os.path.exists(self.path):
+            self.thread.start()
+        return self
+
+    def __exit__(self, *exc):
+        self.stop_ev.set()
+        if self.thread.is_alive():
+            self.thread.join()
+
+    def summary(self):
+        if not self.mhz:
+            return None
+        v = sorted(self.mhz)
+        return {"samples": len(v), "median": v[len(v) // 2], "min": v[0], "max": v[-1]}
+
+
 def describe(cfg) -> str:
     s = (f"{cfg['name']} N={cfg['N']} d={cfg['d']} h={cfg['h']} E={cfg['E']} k={cfg['k']} "
          f"score={cfg['score']} act={cfg['act']} R={cfg['R']}")
@@ -446,9 +495,10 @@ def load_metrics(run) -> dict:
     return out
 
 
-def quick_workload(name, steps, warmup, dev, graph=False) -> dict:
+def quick_workload(name, steps, warmup, dev, graph=False, sysfs=None) -> dict:
     """A short pass over another workload: step time and the per-call
-    durations with their roofline fractions (no cold pass, no oracle)."""
+    durations with their roofline fractions (no cold pass, no oracle), and the
+    gfx clock sampled during the per-call pass."""
     import moe_workloads as W
 
     cfg = W.full(name)
@@ -458,10 +508,15 @@ def quick_workload(name, steps, warmup, dev, graph=False) -> dict:
     for _ in range(warmup):
         run.replay() if graph else run.step()
     ms, _, _ = time_steps(run, steps, graph)
-    per, _ = per_call_pass(run, steps)
+    with ClockSampler(sysfs) as sampler:
+        per, _ = per_call_pass(run, steps)
+    sclk = sampler.summary()
     alg = run.algorithmic()
     kern = kernel_table(run, alg, per)
-    out = {"workload": describe(cfg), "ms_per_step": round(ms, 4),
+    if sclk:
+        for k in ("ffn_up", "ffn_down"):
+            kern[k]["mfma_frac_at_sampled_clock"] = round(kern[k]["mfma_frac"] * 2400.0 / sclk["median"], 4)
+    out = {"workload": describe(cfg), "ms_per_step": round(ms, 4), "sclk_mhz_sampled": sclk,
            "tokens_per_s": round(cfg["N"] / (ms * 1e-3), 1), "steps": steps, "warmup": warmup,
            "grouped_gemm": {k: kern[k] for k in ("ffn_up", "ffn_down")},
            "routed_ffn": routed_ffn_floor(run, alg, per),
@@ -783,7 +838,11 @@ def main(argv=None):
     ms_per_step, gpu_ms, wall = time_steps(run, args.steps, graph)
     value = N / (ms_per_step * 1e-3)
 
-    per_call, instrumented_ms = per_call_pass(run, args.steps)
+    # The per-call pass, with the gfx clock sampled beside it (the clock the
+    # kernels' durations were taken at).
+    with ClockSampler(clocks.get("sysfs")) as sampler:
+        per_call, instrumented_ms = per_call_pass(run, args.steps)
+    sclk = sampler.summary()
 
     # Step-time distribution: the same K steps with one event per step
     # boundary only.
@@ -852,6 +911,10 @@ def main(argv=None):
                                + (" + y_perm rows written" if dom == "ffn_down" else "")
                                + "; H excluded")
     roofline["mfma_frac"] = dk["mfma_frac"]
+    if sclk:
+        # The same product against the MFMA peak at the sampled clock
+        # (the 2.5 PFLOP/s figure assumes 2.4 GHz).
+        roofline["mfma_frac_at_sampled_clock"] = round(dk["mfma_frac"] * 2400.0 / sclk["median"], 4)
 
     out = {
         "metric": METRIC,
@@ -881,7 +944,8 @@ def main(argv=None):
         "step_ms_p10_p50_p90": [round(pct(step_ms, q), 4) for q in (0.1, 0.5, 0.9)],
         "cold": cold,
         "platform": {"hip": torch.version.hip, "torch": torch.__version__,
-                     "device": torch.cuda.get_device_name(0), **clocks},
+                     "device": torch.cuda.get_device_name(0), **clocks,
+                     "sclk_mhz_sampled_in_per_call_pass": sclk},
         "timed_region": {"gpu_events_ms": round(gpu_ms, 3), "host_wall_ms": round(wall * 1e3, 3),
                          "launch": "HIP graph replay of the captured step" if graph
                          else "eager launches"},
@@ -914,7 +978,7 @@ def main(argv=None):
             if w == args.workload or w not in WORKLOADS:
                 continue
             out["other_workloads"][w] = quick_workload(w, args.extra_steps, 10, dev,
-                                                       args.graph)
+                                                       args.graph, clocks.get("sysfs"))
     if host is not None:
         cb = cpu_baseline(cfg, host, args.cpu_seconds)
         cb["gpu_speedup"] = round(value / cb["value"], 1)
