@@ -307,6 +307,37 @@ class LayerRun:
         layer.bias_update(buf, self.bias_state, self.step_bias)
         mark()
 
+    def single_calls(self) -> dict:
+        """Each call of a step (compact native-payload layout) as a closure
+        that repeats it on the main stream with the step's own buffers, for
+        timing one call with nothing else running: every one rewrites the same
+        outputs from the same inputs (the bias update, which changes the next
+        route, is left out)."""
+        moe, layer, buf, cfg, inp, wts = (self.moe, self.layer, self.buf, self.cfg, self.inp,
+                                          self.wts)
+        if self.padded or self.q8 or self.fused:
+            return {}
+        d = buf.desc
+        E, dim, h, rows = d.num_experts, d.hidden, cfg["h"], buf.rows
+        calls = {
+            "route": lambda: layer.route(buf, inp),
+            "dispatch_layout": lambda: moe.moe_dispatch_layout(
+                d, buf.flags, buf.topk_idx, buf.row_of_slot, buf.token_of_row, buf.slot_of_row,
+                buf.expert_offsets, buf.admitted, buf.rank_offsets, buf.rank_counts,
+                buf.ws_dispatch),
+            "permute": lambda: moe.moe_permute(d, inp["x"], buf.row_of_slot, buf.x_perm),
+            "ffn_up": lambda: moe.moe_expert_ffn_up(E, rows, dim, h, cfg["act"], cfg["dtype"],
+                                                    buf.x_perm, buf.expert_offsets, wts["w1"],
+                                                    wts.get("w3"), buf.ws_ffn),
+            "ffn_down": lambda: moe.moe_expert_ffn_down(E, rows, dim, h, cfg["act"],
+                                                        cfg["dtype"], buf.expert_offsets,
+                                                        wts["w2"], buf.y_perm, None, buf.ws_ffn),
+            "combine": lambda: layer.combine(buf, inp, residual=True),
+        }
+        if self.fork:
+            calls["shared_ffn"] = lambda: layer.shared_ffn(buf, wts, self.main)
+        return calls
+
     def n_events(self):
         return len(self.calls) + 1
 
@@ -418,6 +449,30 @@ def per_call_pass(run, steps):
     return per, inst
 
 
+def isolated_pass(run, reps) -> dict:
+    """Each call of the step timed alone after a full step: 3 untimed calls,
+    then `reps` back to back between two events on the main stream, nothing
+    on any other stream.  Inside the step a call can share the GPU with the
+    shared expert's side stream; this is the call's own rate."""
+    torch = run.torch
+    out = {}
+    for name, fn in run.single_calls().items():
+        for _ in range(3):
+            fn()
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+        torch.cuda.synchronize()
+        ev[0].record(run.main)
+        for _ in range(reps):
+            fn()
+        ev[1].record(run.main)
+        torch.cuda.synchronize()
+        out[name] = ev[0].elapsed_time(ev[1]) / reps * 1e3
+    # Leave the step's state as a step leaves it.
+    run.step()
+    torch.cuda.synchronize()
+    return out
+
+
 def kernel_table(run, alg, per) -> dict:
     peak = MFMA_PEAK_TFLOPS[run.cfg["dtype"]]
     kern = {}
@@ -511,6 +566,7 @@ def quick_workload(name, steps, warmup, dev, graph=False, sysfs=None) -> dict:
     with ClockSampler(sysfs) as sampler:
         per, _ = per_call_pass(run, steps)
     sclk = sampler.summary()
+    iso = isolated_pass(run, max(3, min(steps, 10)))
     alg = run.algorithmic()
     kern = kernel_table(run, alg, per)
     if sclk:
@@ -521,7 +577,8 @@ def quick_workload(name, steps, warmup, dev, graph=False, sysfs=None) -> dict:
            "grouped_gemm": {k: kern[k] for k in ("ffn_up", "ffn_down")},
            "routed_ffn": routed_ffn_floor(run, alg, per),
            "route_us": kern["route"]["us"], "combine_hbm_frac": kern["combine"]["hbm_frac"],
-           "permute_hbm_frac": kern.get("permute", kern.get("dispatch", {})).get("hbm_frac")}
+           "permute_hbm_frac": kern.get("permute", kern.get("dispatch", {})).get("hbm_frac"),
+           "isolated": kernel_table(run, alg, iso)}
     del run
     run = None
     import torch
@@ -843,6 +900,7 @@ def main(argv=None):
     with ClockSampler(clocks.get("sysfs")) as sampler:
         per_call, instrumented_ms = per_call_pass(run, args.steps)
     sclk = sampler.summary()
+    iso_call = isolated_pass(run, max(3, min(args.steps, 10)))
 
     # Step-time distribution: the same K steps with one event per step
     # boundary only.
@@ -890,6 +948,7 @@ def main(argv=None):
 
     alg = run.algorithmic()
     kern = kernel_table(run, alg, per_call)
+    iso = kernel_table(run, alg, iso_call)
     cold = {"ms_per_step_with_per_call_events": round(cold_step_ms, 4), "steps": n_cold}
     cold.update(kernel_table(run, alg, cold_call))
 
@@ -936,8 +995,12 @@ def main(argv=None):
         "routed_ffn": routed_ffn_floor(run, alg, per_call),
         "grouped_gemm_mfma_frac": {"up": kern["ffn_up"]["mfma_frac"],
                                    "down": kern["ffn_down"]["mfma_frac"]},
-        # the permute call with its events; the kernel alone is in profiles/
+        # the permute call with its events inside the step (where the shared
+        # expert's side stream may share the GPU), and the call timed alone
         "permute_hbm_frac": kern.get("permute", kern.get("dispatch", {})).get("hbm_frac"),
+        "permute_hbm_frac_isolated": iso.get("permute", {}).get("hbm_frac"),
+        "combine_hbm_frac_isolated": iso.get("combine", {}).get("hbm_frac"),
+        "isolated": iso,
         "load": load_metrics(run),
         "kernels": kern,
         "ms_per_step_with_per_call_events": round(instrumented_ms, 4),
