@@ -105,7 +105,8 @@ __device__ __forceinline__ void bwd_act_grad(float u, float v, float g, float& h
 // are clamped to max_rows and, when group_rows is given, each segment to its
 // first group_rows[e] rows.  Nondecreasing offsets need at most cap_tiles
 // tiles and cap_groups groups (the workspace's sizes); a tile past either is
-// not written, and *count stops before the first such tile.
+// not written, and count[0] stops before the first such tile.  count[1] is
+// the row-tile group size of the GEMMs' block order (see tile_of).
 // Inclusive scan over the 1024 threads of a block: shuffles inside each wave,
 // then the 16 wave totals (two barriers instead of a Hillis-Steele loop).
 __device__ __forceinline__ int32_t block_scan_1024(int32_t v, int32_t* wsum) {
@@ -128,9 +129,12 @@ __global__ __launch_bounds__(1024) void ffn_plan_tiles(const int32_t* __restrict
                                                        int cap_groups, int4* __restrict__ tiles,
                                                        int32_t* __restrict__ count) {
   __shared__ int32_t wsum[16];
-  __shared__ int32_t total_s, first_bad_s;
+  __shared__ int32_t total_s, first_bad_s, multi_s;
   const int e = threadIdx.x;
-  if (e == 0) first_bad_s = 0x7fffffff;
+  if (e == 0) {
+    first_bad_s = 0x7fffffff;
+    multi_s = 0;
+  }
   int32_t lo = 0, hi = 0, n = 0, chunk = BM;
   if (e < E) {
     lo = min(offsets[e], max_rows);
@@ -139,7 +143,8 @@ __global__ __launch_bounds__(1024) void ffn_plan_tiles(const int32_t* __restrict
     n = hi > lo ? (hi - lo + BM - 1) / BM : 0;
     if (n > 0) chunk = ((hi - lo + n - 1) / n + 31) / 32 * 32;
   }
-  const int32_t n_incl = block_scan_1024(n, wsum);
+  const int32_t n_incl = block_scan_1024(n, wsum);  // its first barrier orders multi_s = 0
+  if (n >= 2) atomicAdd(&multi_s, n);
   const int32_t start = n_incl - n;
   if (e == E - 1) total_s = n_incl;
   // 16-row groups of this expert's tiles, then their exclusive prefix.
@@ -158,7 +163,12 @@ __global__ __launch_bounds__(1024) void ffn_plan_tiles(const int32_t* __restrict
     g0 = g1;
   }
   __syncthreads();
-  if (e == 0) *count = min(total_s, first_bad_s);
+  if (e == 0) {
+    count[0] = min(total_s, first_bad_s);
+    // Block order of the GEMMs (tile_of): groups of 4 row tiles once a quarter
+    // of the row tiles belong to experts of two or more.
+    count[1] = total_s > 0 && 4 * multi_s >= total_s ? 4 : 1;
+  }
 }
 
 // XCD-aware block order.  The hardware deals blocks round-robin over the 8
@@ -339,7 +349,7 @@ void grouped_gemm_bf16(
   const int logical = xcd_logical(blockIdx.x, m_tiles * n_tiles);
   if (logical < 0) return;
   int mt, nt;
-  tile_of(logical, n_tiles, m_tiles, gm, mt, nt);
+  tile_of(logical, n_tiles, m_tiles, gm > 0 ? gm : tile_count[1], mt, nt);
   const int4 tile = tiles[mt];
   const int e = tile.x, r0 = tile.y, r1 = tile.z, g0 = tile.w;
   const int n0 = nt * BN;
@@ -1059,12 +1069,13 @@ static void launch_bf16(const bf16_t* A, const bf16_t* B, const bf16_t* B2, bf16
                         int N, const FfnArgs& a, hipStream_t st, BwdEpiArgs be = {}) {
   const int nt = (N + BN - 1) / BN;
   const int g = grid_of(max_m_tiles(a.max_rows, BM, a.E), nt);
-  // Groups of 4 row tiles once experts average two or more row tiles: an XCD's
-  // 32 concurrent blocks then cover 4 x 8 tiles, and its L2 misses per K stage
-  // fall from 1 A tile + 32 weight slabs to 4 A tiles + 8 weight slabs.
-  const int gm = a.max_rows / a.E >= 2 * BM ? 4 : 1;
+  // Block order from the plan (gm 0): groups of 4 row tiles once a quarter of
+  // the row tiles belong to experts of two or more; an XCD's 32 concurrent
+  // blocks then cover 4 x 8 tiles, so an expert's row tiles read its weight
+  // slabs from that XCD's L2, and its L2 misses per K stage fall from 1 A tile
+  // + 32 weight slabs to 4 A tiles + 8 weight slabs.
   grouped_gemm_bf16<BM, BN, ACT, MODE><<<g, kGemmWaves * 64, 0, st>>>(
-      A, B, B2, C, K, N, ffn_tiles(a), ffn_count(a), nt, ffn_groups(a.E, a.max_rows), gm,
+      A, B, B2, C, K, N, ffn_tiles(a), ffn_count(a), nt, ffn_groups(a.E, a.max_rows), 0,
       MODE == kDownFused ? *a.fused : FusedCombineArgs{}, be);
 }
 
