@@ -106,7 +106,8 @@ __device__ __forceinline__ void bwd_act_grad(float u, float v, float g, float& h
 // first group_rows[e] rows.  Nondecreasing offsets need at most cap_tiles
 // tiles and cap_groups groups (the workspace's sizes); a tile past either is
 // not written, and count[0] stops before the first such tile.  count[1] is
-// the row-tile group size of the GEMMs' block order (see tile_of).
+// the row-tile group size of the GEMMs' block order (see tile_of), count[2]
+// the row tile height BM.
 // Inclusive scan over the 1024 threads of a block: shuffles inside each wave,
 // then the 16 wave totals (two barriers instead of a Hillis-Steele loop).
 __device__ __forceinline__ int32_t block_scan_1024(int32_t v, int32_t* wsum) {
@@ -123,24 +124,39 @@ __device__ __forceinline__ int32_t block_scan_1024(int32_t v, int32_t* wsum) {
   return v;
 }
 
+// Experts averaging at most this many rows take the 192-row tiles.
+constexpr int kMidRowsPerExpert = 128;
+
+// BMalt > 0: the plan picks its row tile height itself, BMalt when the
+// segments hold at most kMidRowsPerExpert rows per expert on average, else BM,
+// and stores it in count[2] (the GEMMs that serve both read it there).
 __global__ __launch_bounds__(1024) void ffn_plan_tiles(const int32_t* __restrict__ offsets,
                                                        const int32_t* __restrict__ group_rows,
-                                                       int E, int BM, int max_rows, int cap_tiles,
-                                                       int cap_groups, int4* __restrict__ tiles,
+                                                       int E, int BM, int BMalt, int max_rows,
+                                                       int cap_tiles, int cap_groups,
+                                                       int4* __restrict__ tiles,
                                                        int32_t* __restrict__ count) {
   __shared__ int32_t wsum[16];
-  __shared__ int32_t total_s, first_bad_s, multi_s;
+  __shared__ int32_t total_s, first_bad_s, multi_s, rows_s;
   const int e = threadIdx.x;
   if (e == 0) {
     first_bad_s = 0x7fffffff;
     multi_s = 0;
+    rows_s = 0;
   }
-  int32_t lo = 0, hi = 0, n = 0, chunk = BM;
+  int32_t lo = 0, hi = 0, n = 0;
   if (e < E) {
     lo = min(offsets[e], max_rows);
     hi = min(offsets[e + 1], max_rows);
     if (group_rows) hi = min(hi, lo + max(group_rows[e], 0));
-    n = hi > lo ? (hi - lo + BM - 1) / BM : 0;
+  }
+  __syncthreads();
+  if (hi > lo) atomicAdd(&rows_s, hi - lo);
+  __syncthreads();
+  const int bm = BMalt > 0 && (long long)rows_s <= (long long)kMidRowsPerExpert * E ? BMalt : BM;
+  int32_t chunk = bm;
+  if (e < E) {
+    n = hi > lo ? (hi - lo + bm - 1) / bm : 0;
     if (n > 0) chunk = ((hi - lo + n - 1) / n + 31) / 32 * 32;
   }
   const int32_t n_incl = block_scan_1024(n, wsum);  // its first barrier orders multi_s = 0
@@ -168,6 +184,7 @@ __global__ __launch_bounds__(1024) void ffn_plan_tiles(const int32_t* __restrict
     // Block order of the GEMMs (tile_of): groups of 4 row tiles once a quarter
     // of the row tiles belong to experts of two or more.
     count[1] = total_s > 0 && 4 * multi_s >= total_s ? 4 : 1;
+    count[2] = bm;
   }
 }
 
@@ -296,12 +313,27 @@ struct BwdEpiArgs {
   const int32_t* kst;  // kWgrad: stage offset of each expert, [E + 1]
 };
 
+// LDS bytes of one tile configuration (the ring the body below lays out).
 template <int BM, int BN, int ACT, int MODE>
-__global__ __launch_bounds__(kGemmWaves * 64, 1) __attribute__((amdgpu_waves_per_eu(2, 2)))
-void grouped_gemm_bf16(
-    const bf16_t* __restrict__ A, const bf16_t* __restrict__ B, const bf16_t* __restrict__ B2,
-    bf16_t* __restrict__ C, int K, int N, const int4* __restrict__ tiles,
-    const int32_t* __restrict__ tile_count, int n_tiles, int ldg, int gm, FusedCombineArgs fc,
+struct GemmLds {
+  static constexpr bool DUAL = ACT == ACT_SWIGLU && MODE != kBwdG;
+  static constexpr int RB = 64, BROWS = DUAL ? 2 * BN : BN, STAGE = (BM + BROWS) * RB;
+  static constexpr int NS = kLdsBytes / STAGE < 6 ? kLdsBytes / STAGE : 6;
+  static constexpr bool AP = MODE == kUpGemm || MODE == kUpRawF32 || MODE == kBwdG;
+  static constexpr int ASLOT = BM * 2 * RB, WST = BROWS * RB;
+  static constexpr int NW_ = (kLdsBytes - 2 * ASLOT) / WST;
+  static constexpr int NW = AP ? (NW_ < 8 ? NW_ : 8) : NS;
+  static constexpr int bytes = AP ? 2 * ASLOT + NW * WST : NS * STAGE;
+};
+
+// The kernel body, inlined into the kernels below; smem is the block's LDS
+// array (GemmLds<...>::bytes at least, 1-KB aligned), m_tiles the plan's row
+// tile count and gm its block-order group size.
+template <int BM, int BN, int ACT, int MODE>
+__device__ __forceinline__ void gemm_bf16_body(
+    char* smem, const bf16_t* __restrict__ A, const bf16_t* __restrict__ B,
+    const bf16_t* __restrict__ B2, bf16_t* __restrict__ C, int K, int N,
+    const int4* __restrict__ tiles, int m_tiles, int n_tiles, int ldg, int gm, FusedCombineArgs fc,
     BwdEpiArgs be) {
   constexpr bool DUAL = ACT == ACT_SWIGLU && MODE != kBwdG;  // two B operands
   constexpr int BK = 32, RB = BK * 2;  // RB: bytes per staged row
@@ -343,13 +375,12 @@ void grouped_gemm_bf16(
   static_assert(BM % (4 * RPL) == 0 && BROWS % (4 * RPL) == 0, "loads split over 4 waves");
   static_assert(WN % 32 == 0, "wave tile must be whole 32-column MFMA blocks");
   static_assert((NS - 1) * LMAX < 64, "loads in flight must fit the 6-bit vmcnt");
-  __shared__ __attribute__((aligned(1024))) char smem[LDSB];
+  static_assert(LDSB == GemmLds<BM, BN, ACT, MODE>::bytes, "LDS size of the configuration");
 
-  const int m_tiles = *tile_count;
   const int logical = xcd_logical(blockIdx.x, m_tiles * n_tiles);
   if (logical < 0) return;
   int mt, nt;
-  tile_of(logical, n_tiles, m_tiles, gm > 0 ? gm : tile_count[1], mt, nt);
+  tile_of(logical, n_tiles, m_tiles, gm, mt, nt);
   const int4 tile = tiles[mt];
   const int e = tile.x, r0 = tile.y, r1 = tile.z, g0 = tile.w;
   const int n0 = nt * BN;
@@ -828,6 +859,42 @@ void grouped_gemm_bf16(
 #undef MOE_ISSUE_A
 }
 
+template <int BM, int BN, int ACT, int MODE>
+__global__ __launch_bounds__(kGemmWaves * 64, 1) __attribute__((amdgpu_waves_per_eu(2, 2)))
+void grouped_gemm_bf16(
+    const bf16_t* __restrict__ A, const bf16_t* __restrict__ B, const bf16_t* __restrict__ B2,
+    bf16_t* __restrict__ C, int K, int N, const int4* __restrict__ tiles,
+    const int32_t* __restrict__ tile_count, int n_tiles, int ldg, int gm, FusedCombineArgs fc,
+    BwdEpiArgs be) {
+  __shared__ __attribute__((aligned(1024))) char smem[GemmLds<BM, BN, ACT, MODE>::bytes];
+  gemm_bf16_body<BM, BN, ACT, MODE>(smem, A, B, B2, C, K, N, tiles, tile_count[0], n_tiles, ldg,
+                                    gm > 0 ? gm : tile_count[1], fc, be);
+}
+
+// Two tile configurations in one kernel: the tile plan has chosen the row
+// tile height from the batch's row counts (tile_count[2]), so the block runs
+// BM1 x BN1 tiles (n_tiles1 column tiles) when it is BM1, else BM2 x BN2.
+// The LDS array is the larger ring; registers are those of the larger body.
+template <int BM1, int BN1, int BM2, int BN2, int ACT, int MODE>
+__global__ __launch_bounds__(kGemmWaves * 64, 1) __attribute__((amdgpu_waves_per_eu(2, 2)))
+void grouped_gemm_bf16_pick(
+    const bf16_t* __restrict__ A, const bf16_t* __restrict__ B, const bf16_t* __restrict__ B2,
+    bf16_t* __restrict__ C, int K, int N, const int4* __restrict__ tiles,
+    const int32_t* __restrict__ tile_count, int n_tiles1, int n_tiles2, int ldg,
+    FusedCombineArgs fc) {
+  constexpr int L1 = GemmLds<BM1, BN1, ACT, MODE>::bytes, L2 = GemmLds<BM2, BN2, ACT, MODE>::bytes;
+  __shared__ __attribute__((aligned(1024))) char smem[L1 > L2 ? L1 : L2];
+  // The plan's tile count, group size and row tile height in one load (the
+  // plan sits at the 256-aligned start of the workspace).
+  const int4 plan = *reinterpret_cast<const int4*>(tile_count);
+  if (plan.z == BM1)
+    gemm_bf16_body<BM1, BN1, ACT, MODE>(smem, A, B, B2, C, K, N, tiles, plan.x, n_tiles1, ldg,
+                                        plan.y, fc, BwdEpiArgs{});
+  else
+    gemm_bf16_body<BM2, BN2, ACT, MODE>(smem, A, B, B2, C, K, N, tiles, plan.x, n_tiles2, ldg,
+                                        plan.y, fc, BwdEpiArgs{});
+}
+
 // Weight packing for the bf16 kernel: W [E, N, K] row-major -> slabs of SR
 // rows (SR = packed_slab_rows(N)); slab (e, s) holds K/32 stages of SR*32
 // elements, each stage SR/16 blocks of 1 KB laid out exactly as
@@ -1017,8 +1084,29 @@ static size_t align256(size_t x) { return (x + 255) / 256 * 256; }
 static int ffn_bm(int dtype, int E, int max_rows) {
   if (dtype == 0) return kF32BM;
   if ((long long)max_rows <= 32LL * E) return kGemmBMSmall;
-  if ((long long)max_rows <= 128LL * E) return kGemmBMMid;
+  if ((long long)max_rows <= (long long)kMidRowsPerExpert * E) return kGemmBMMid;
   return kGemmBM;
+}
+
+// Where the bound max_rows asks for 320-row tiles but is within 4x of the
+// 192-row threshold, the batch may still hold few enough rows for 192-row
+// tiles (a capacity-bound layer whose hot experts drop most of their slots):
+// the forward's tile plan then picks the height from the real counts
+// (ffn_plan_tiles, BMalt) and the GEMMs serve both (grouped_gemm_bf16_pick).
+// Skewed-load layer (15.6 k of 65.5 k slots admitted, 640-row cap): FFN 709 ->
+// 567 us.  Far above it (Mixtral-like: 2048 rows per expert) the two-height
+// kernel cost 1.3% against the 320-row one and the choice is not offered.
+// 0 when there is no choice.
+static int ffn_bm_alt(int dtype, int E, int max_rows) {
+  return dtype == 1 && ffn_bm(dtype, E, max_rows) == kGemmBM &&
+                 (long long)max_rows <= 4LL * kMidRowsPerExpert * E
+             ? kGemmBMMid
+             : 0;
+}
+// The smallest row tile a plan may use (it sizes the plan and the groups).
+static int ffn_bm_min(int dtype, int E, int max_rows) {
+  const int alt = ffn_bm_alt(dtype, E, max_rows);
+  return alt ? alt : ffn_bm(dtype, E, max_rows);
 }
 
 // Upper bound of row tiles: every expert may end in a partial tile.
@@ -1026,13 +1114,14 @@ static int max_m_tiles(int max_rows, int BM, int E) { return (max_rows + BM - 1)
 
 static size_t ffn_plan_bytes(int E, int max_rows, int dtype) {
   return align256(sizeof(int32_t)) +
-         align256((size_t)max_m_tiles(max_rows, ffn_bm(dtype, E, max_rows), E) * sizeof(int4));
+         align256((size_t)max_m_tiles(max_rows, ffn_bm_min(dtype, E, max_rows), E) *
+                  sizeof(int4));
 }
 
 // 16-row groups of the packed bf16 hidden buffer: each tile rounds its rows up
 // to whole groups, so at most one partial group per tile.
 static int ffn_groups(int E, int max_rows) {
-  return (max_rows + 15) / 16 + max_m_tiles(max_rows, ffn_bm(1, E, max_rows), E);
+  return (max_rows + 15) / 16 + max_m_tiles(max_rows, ffn_bm_min(1, E, max_rows), E);
 }
 
 size_t ffn_workspace_bytes(int E, int max_rows, int d, int h, int act, int dtype) {
@@ -1058,9 +1147,11 @@ static int grid_of(int m_tiles, int n_tiles) {
 
 hipError_t launch_ffn_plan(const FfnArgs& a, hipStream_t st) {
   const int bm = ffn_bm(a.dtype, a.E, a.max_rows);
-  ffn_plan_tiles<<<1, 1024, 0, st>>>(a.offsets, nullptr, a.E, bm, a.max_rows,
-                                     max_m_tiles(a.max_rows, bm, a.E), ffn_groups(a.E, a.max_rows),
-                                     ffn_tiles(a), ffn_count(a));
+  ffn_plan_tiles<<<1, 1024, 0, st>>>(a.offsets, nullptr, a.E, bm,
+                                     ffn_bm_alt(a.dtype, a.E, a.max_rows), a.max_rows,
+                                     max_m_tiles(a.max_rows, ffn_bm_min(a.dtype, a.E, a.max_rows),
+                                                 a.E),
+                                     ffn_groups(a.E, a.max_rows), ffn_tiles(a), ffn_count(a));
   return hipGetLastError();
 }
 
@@ -1077,6 +1168,19 @@ static void launch_bf16(const bf16_t* A, const bf16_t* B, const bf16_t* B2, bf16
   grouped_gemm_bf16<BM, BN, ACT, MODE><<<g, kGemmWaves * 64, 0, st>>>(
       A, B, B2, C, K, N, ffn_tiles(a), ffn_count(a), nt, ffn_groups(a.E, a.max_rows), 0,
       MODE == kDownFused ? *a.fused : FusedCombineArgs{}, be);
+}
+
+// The forward GEMMs where the plan picks the row tile height (ffn_bm_alt):
+// BM1 x BN1 (192-row tiles) or BM2 x BN2 (320-row tiles).
+template <int BM1, int BN1, int BM2, int BN2, int ACT, int MODE>
+static void launch_bf16_pick(const bf16_t* A, const bf16_t* B, const bf16_t* B2, bf16_t* C,
+                             int K, int N, const FfnArgs& a, hipStream_t st) {
+  const int nt1 = (N + BN1 - 1) / BN1, nt2 = (N + BN2 - 1) / BN2;
+  const int g = std::max(grid_of(max_m_tiles(a.max_rows, BM1, a.E), nt1),
+                         grid_of(max_m_tiles(a.max_rows, BM2, a.E), nt2));
+  grouped_gemm_bf16_pick<BM1, BN1, BM2, BN2, ACT, MODE><<<g, kGemmWaves * 64, 0, st>>>(
+      A, B, B2, C, K, N, ffn_tiles(a), ffn_count(a), nt1, nt2, ffn_groups(a.E, a.max_rows),
+      MODE == kDownFused ? *a.fused : FusedCombineArgs{});
 }
 
 template <int ACT, bool FUSEDC = false>
@@ -1128,14 +1232,29 @@ hipError_t launch_ffn_up(const FfnArgs& a, hipStream_t st) {
         if (a.act == ACT_RELU) launch_bf16<S, 256, ACT_RELU, kUpGemm>(X, W1, nullptr, H, a.d, a.h, a, st);
         else launch_bf16<S, 256, ACT_GELU, kUpGemm>(X, W1, nullptr, H, a.d, a.h, a, st);
       }
+    } else if (ffn_bm_alt(1, a.E, a.max_rows) == 0) {
+      if (a.act == ACT_SWIGLU) {
+        launch_bf16<kGemmBM, 128, ACT_SWIGLU, kUpGemm>(X, W1, W3, H, a.d, a.h, a, st);
+      } else if (a.h >= 2048) {
+        if (a.act == ACT_RELU) launch_bf16<kGemmBM, 256, ACT_RELU, kUpGemm>(X, W1, nullptr, H, a.d, a.h, a, st);
+        else launch_bf16<kGemmBM, 256, ACT_GELU, kUpGemm>(X, W1, nullptr, H, a.d, a.h, a, st);
+      } else {
+        if (a.act == ACT_RELU) launch_bf16<kGemmBM, 128, ACT_RELU, kUpGemm>(X, W1, nullptr, H, a.d, a.h, a, st);
+        else launch_bf16<kGemmBM, 128, ACT_GELU, kUpGemm>(X, W1, nullptr, H, a.d, a.h, a, st);
+      }
     } else if (a.act == ACT_SWIGLU) {
-      launch_bf16<kGemmBM, 128, ACT_SWIGLU, kUpGemm>(X, W1, W3, H, a.d, a.h, a, st);
+      // 320-row tiles, or the 192-row ones the mid branch above would take.
+      constexpr int M = kGemmBMMid, L = kGemmBM;
+      if (a.h >= 2048) launch_bf16_pick<M, 256, L, 128, ACT_SWIGLU, kUpGemm>(X, W1, W3, H, a.d, a.h, a, st);
+      else launch_bf16_pick<M, 128, L, 128, ACT_SWIGLU, kUpGemm>(X, W1, W3, H, a.d, a.h, a, st);
     } else if (a.h >= 2048) {
-      if (a.act == ACT_RELU) launch_bf16<kGemmBM, 256, ACT_RELU, kUpGemm>(X, W1, nullptr, H, a.d, a.h, a, st);
-      else launch_bf16<kGemmBM, 256, ACT_GELU, kUpGemm>(X, W1, nullptr, H, a.d, a.h, a, st);
+      constexpr int M = kGemmBMMid, L = kGemmBM;
+      if (a.act == ACT_RELU) launch_bf16_pick<M, 256, L, 256, ACT_RELU, kUpGemm>(X, W1, nullptr, H, a.d, a.h, a, st);
+      else launch_bf16_pick<M, 256, L, 256, ACT_GELU, kUpGemm>(X, W1, nullptr, H, a.d, a.h, a, st);
     } else {
-      if (a.act == ACT_RELU) launch_bf16<kGemmBM, 128, ACT_RELU, kUpGemm>(X, W1, nullptr, H, a.d, a.h, a, st);
-      else launch_bf16<kGemmBM, 128, ACT_GELU, kUpGemm>(X, W1, nullptr, H, a.d, a.h, a, st);
+      constexpr int M = kGemmBMMid, L = kGemmBM;
+      if (a.act == ACT_RELU) launch_bf16_pick<M, 128, L, 128, ACT_RELU, kUpGemm>(X, W1, nullptr, H, a.d, a.h, a, st);
+      else launch_bf16_pick<M, 128, L, 128, ACT_GELU, kUpGemm>(X, W1, nullptr, H, a.d, a.h, a, st);
     }
   }
   return hipGetLastError();
@@ -1163,10 +1282,15 @@ static void launch_down_bf16(const FfnArgs& a, hipStream_t st) {
     constexpr int S = kGemmBMSmall;
     if (a.d >= 2048) launch_bf16<S, 512, ACT_NONE, MODE>(H, W2, nullptr, Y, a.h, a.d, a, st);
     else launch_bf16<S, 256, ACT_NONE, MODE>(H, W2, nullptr, Y, a.h, a.d, a, st);
-  } else if (a.d >= 1024) {
-    launch_bf16<kGemmBM, 256, ACT_NONE, MODE>(H, W2, nullptr, Y, a.h, a.d, a, st);
+  } else if (ffn_bm_alt(1, a.E, a.max_rows) == 0) {
+    if (a.d >= 1024) launch_bf16<kGemmBM, 256, ACT_NONE, MODE>(H, W2, nullptr, Y, a.h, a.d, a, st);
+    else launch_bf16<kGemmBM, 128, ACT_NONE, MODE>(H, W2, nullptr, Y, a.h, a.d, a, st);
   } else {
-    launch_bf16<kGemmBM, 128, ACT_NONE, MODE>(H, W2, nullptr, Y, a.h, a.d, a, st);
+    // 320-row tiles, or the 192-row ones the mid branch above would take.
+    constexpr int M = kGemmBMMid, L = kGemmBM;
+    if (a.d >= 4096) launch_bf16_pick<M, 512, L, 256, ACT_NONE, MODE>(H, W2, nullptr, Y, a.h, a.d, a, st);
+    else if (a.d >= 1024) launch_bf16_pick<M, 256, L, 256, ACT_NONE, MODE>(H, W2, nullptr, Y, a.h, a.d, a, st);
+    else launch_bf16_pick<M, 128, L, 128, ACT_NONE, MODE>(H, W2, nullptr, Y, a.h, a.d, a, st);
   }
 }
 
@@ -1253,7 +1377,7 @@ hipError_t launch_ffn_bwd_packed_gemms(const FfnBwdPackedArgs& a, void** g_rm, v
   FfnArgs f{a.E, a.max_rows, a.d, a.h, a.act, 1, a.x_rows, a.offsets, a.w1p, a.w3p, nullptr,
             nullptr, a.ws};
   const int bm = ffn_bm(1, a.E, a.max_rows);
-  ffn_plan_tiles<<<1, 1024, 0, st>>>(a.offsets, a.group_rows, a.E, bm, a.max_rows,
+  ffn_plan_tiles<<<1, 1024, 0, st>>>(a.offsets, a.group_rows, a.E, bm, 0, a.max_rows,
                                      max_m_tiles(a.max_rows, bm, a.E), ffn_groups(a.E, a.max_rows),
                                      ffn_tiles(f), ffn_count(f));
   auto X = static_cast<const bf16_t*>(a.x_rows);

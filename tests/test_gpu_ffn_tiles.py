@@ -61,11 +61,11 @@ def test_pack_weights_is_the_documented_permutation(E, R, C):
     assert torch.equal(wd.cpu().view(torch.int16), w.view(torch.int16))  # source untouched
 
 
-def _inputs(d, h, act, dtype, seed, counts=COUNTS):
+def _inputs(d, h, act, dtype, seed, counts=COUNTS, spare=7):
     g = torch.Generator().manual_seed(seed)
     E, M = len(counts), sum(counts)
     tdt = torch.bfloat16 if dtype == "bf16" else torch.float32
-    x = torch.randn(M + 7, d, generator=g).to(tdt)
+    x = torch.randn(M + spare, d, generator=g).to(tdt)
     w1 = (torch.randn(E, h, d, generator=g) / d ** 0.5).to(tdt)
     w3 = (torch.randn(E, h, d, generator=g) / d ** 0.5).to(tdt) if act == "swiglu" else None
     w2 = (torch.randn(E, d, h, generator=g) / h ** 0.5).to(tdt)
@@ -137,9 +137,25 @@ def test_ffn_wide_row_tiles(d, h, act):
     _check_ffn(d, h, act, "bf16", WIDE_COUNTS, seed=d + 7 * h)
 
 
-def _check_ffn(d, h, act, dtype, counts, seed):
-    print(f"[ffn tiles] d={d} h={h} act={act} dtype={dtype} counts={counts}", flush=True)
-    x, w1, w3, w2, offs = _inputs(d, h, act, dtype, seed=seed, counts=counts)
+# A bound far above the rows the batch holds (a capacity-bound layer whose hot
+# experts dropped most of their slots): the bound alone asks for 320-row
+# tiles, the plan sees at most 128 rows per expert and picks the 192-row ones,
+# and both GEMMs follow its choice.  The same experts at a bound that keeps
+# 320-row tiles give the same outputs to the tolerance.
+@pytest.mark.parametrize("d,h,act", [(512, 1024, "swiglu"), (384, 2048, "gelu"),
+                                     (4096, 2048, "swiglu"), (256, 512, "relu")])
+def test_ffn_plan_picks_the_row_tile_height(d, h, act):
+    counts = WIDE_COUNTS if d >= 4096 else MID_COUNTS  # d >= 4096: 512-column down tiles
+    spare = 3 * sum(counts)
+    M = sum(counts) + spare
+    assert M > 128 * len(counts) >= sum(counts), "bound: 320 rows; batch: 192"
+    _check_ffn(d, h, act, "bf16", counts, seed=d + 11 * h, spare=spare)
+
+
+def _check_ffn(d, h, act, dtype, counts, seed, spare=7):
+    print(f"[ffn tiles] d={d} h={h} act={act} dtype={dtype} counts={counts} spare={spare}",
+          flush=True)
+    x, w1, w3, w2, offs = _inputs(d, h, act, dtype, seed=seed, counts=counts, spare=spare)
     E, M = len(counts), x.shape[0]
     cfg = {"dtype": dtype, "d": d, "h": h}
     wts = moe.prepare_weights(cfg, {"w1": w1.cuda(), "w3": None if w3 is None else w3.cuda(),
