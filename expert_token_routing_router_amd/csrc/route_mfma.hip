@@ -632,6 +632,10 @@ __global__ __launch_bounds__(kFuseWaves * 64, 4) void route_fused(
     nch = c1 - c0;
   }
   for (int e = tid; e < E; e += kFuseWaves * 64) hist[e] = 0;
+  // The scoring launch of the split route clears the counts its tail launch
+  // adds to (stream order runs the whole tail after it).
+  if (SPLIT == 1 && blockIdx.x == 0 && blockIdx.y == 0 && blockIdx.z == 0)
+    for (int e = tid; e < E; e += kFuseWaves * 64) counts[e] = 0;
 
   // ---- 1. scores --------------------------------------------------------
   // The ring holds pairs of chunks (64 elements) as 128-byte row pieces: 12
@@ -884,9 +888,11 @@ size_t route_certified_workspace_bytes(int N, int d, int E) {
 }
 
 hipError_t launch_route_certified(const RouteArgs& a, hipStream_t st) {
-  launch_zero_i32(a.counts, a.E, st);
   const int blocks = (a.N + kFuseTok - 1) / kFuseTok;
   const bool split = route_split(a.N, a.E);
+  // The counts start at zero: the split route's scoring launch clears them
+  // (its tail launch adds), the one-launch route needs a launch before it.
+  if (!split) launch_zero_i32(a.counts, a.E, st);
   const int ks = route_ksplit(a.N, a.d, a.E);
   double* ws_sx = split ? static_cast<double*>(a.ws) : nullptr;
   double* ws_sw = split ? ws_sx + (size_t)ks * a.N : nullptr;
