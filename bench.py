@@ -66,6 +66,9 @@ def parse_args(argv=None):
                          "fused: the down GEMM scatter-adds w*O into an fp32 accumulator "
                          "that moe_combine finishes")
     ap.add_argument("--no-clocks", action="store_true", help="skip reading the clocks")
+    ap.add_argument("--no-isolated", action="store_true",
+                    help="skip timing each call alone (profiler runs: every launch in the trace "
+                         "is then one of a step, so its per-launch averages are the step's)")
     ap.add_argument("--graph", action="store_true",
                     help="replay the step captured once in a HIP graph instead of launching "
                          "every call from the host (measured: no faster; launches overlap "
@@ -550,7 +553,7 @@ def load_metrics(run) -> dict:
     return out
 
 
-def quick_workload(name, steps, warmup, dev, graph=False, sysfs=None) -> dict:
+def quick_workload(name, steps, warmup, dev, graph=False, sysfs=None, isolated=True) -> dict:
     """A short pass over another workload: step time and the per-call
     durations with their roofline fractions (no cold pass, no oracle), and the
     gfx clock sampled during the per-call pass."""
@@ -566,7 +569,7 @@ def quick_workload(name, steps, warmup, dev, graph=False, sysfs=None) -> dict:
     with ClockSampler(sysfs) as sampler:
         per, _ = per_call_pass(run, steps)
     sclk = sampler.summary()
-    iso = isolated_pass(run, max(3, min(steps, 10)))
+    iso = isolated_pass(run, max(3, min(steps, 10))) if isolated else {}
     alg = run.algorithmic()
     kern = kernel_table(run, alg, per)
     if sclk:
@@ -900,7 +903,7 @@ def main(argv=None):
     with ClockSampler(clocks.get("sysfs")) as sampler:
         per_call, instrumented_ms = per_call_pass(run, args.steps)
     sclk = sampler.summary()
-    iso_call = isolated_pass(run, max(3, min(args.steps, 10)))
+    iso_call = {} if args.no_isolated else isolated_pass(run, max(3, min(args.steps, 10)))
 
     # Step-time distribution: the same K steps with one event per step
     # boundary only.
@@ -1041,7 +1044,8 @@ def main(argv=None):
             if w == args.workload or w not in WORKLOADS:
                 continue
             out["other_workloads"][w] = quick_workload(w, args.extra_steps, 10, dev,
-                                                       args.graph, clocks.get("sysfs"))
+                                                       args.graph, clocks.get("sysfs"),
+                                                       not args.no_isolated)
     if host is not None:
         cb = cpu_baseline(cfg, host, args.cpu_seconds)
         cb["gpu_speedup"] = round(value / cb["value"], 1)
