@@ -98,9 +98,10 @@ __device__ __forceinline__ void bwd_act_grad(float u, float v, float g, float& h
 // One block of 1024 threads (E <= 1024): expert e owns n_e = ceil(rows_e / BM)
 // row tiles of equal height, rounded up to whole 32-row MFMA fragments
 // (chunk_e = 32 ceil(ceil(rows_e / n_e) / 32) <= BM; since (n_e - 1) BM <
-// rows_e, no tile is empty).  Tile q of the batch is tiles[q] = {e, first
-// row, row end, first 16-row group}, and *count = number of tiles.  The group
-// numbering gives every tile ceil(rows / 16) groups of its own, in tile order:
+// rows_e, no tile is empty).  The tiles are {e, first row, row end, first
+// 16-row group}, numbered in expert order, and *count = number of tiles; the
+// list may then be reordered (longest first, below).  The group
+// numbering gives every tile ceil(rows / 16) groups of its own, in expert order:
 // the packed hidden buffer of the bf16 FFN stores a tile's rows there.  Rows
 // are clamped to max_rows and, when group_rows is given, each segment to its
 // first group_rows[e] rows.  Nondecreasing offsets need at most cap_tiles
@@ -138,6 +139,8 @@ __global__ __launch_bounds__(1024) void ffn_plan_tiles(const int32_t* __restrict
                                                        int32_t* __restrict__ count) {
   __shared__ int32_t wsum[16];
   __shared__ int32_t total_s, first_bad_s, multi_s, rows_s;
+  __shared__ __align__(16) int32_t keys_l[1024];
+  __shared__ int32_t rank_l[1024];
   const int e = threadIdx.x;
   if (e == 0) {
     first_bad_s = 0x7fffffff;
@@ -179,12 +182,59 @@ __global__ __launch_bounds__(1024) void ffn_plan_tiles(const int32_t* __restrict
     g0 = g1;
   }
   __syncthreads();
+  const int T = total_s;
+  const bool grouped = T > 0 && 4 * multi_s >= T;
   if (e == 0) {
-    count[0] = min(total_s, first_bad_s);
+    count[0] = min(T, first_bad_s);
     // Block order of the GEMMs (tile_of): groups of 4 row tiles once a quarter
     // of the row tiles belong to experts of two or more.
-    count[1] = total_s > 0 && 4 * multi_s >= total_s ? 4 : 1;
+    count[1] = grouped ? 4 : 1;
     count[2] = bm;
+  }
+  // Longest tiles first.  With one row tile per group the GEMMs hand XCD x
+  // the x-th eighth of the logical tiles, and an XCD's blocks start in order
+  // as its CUs free up: the row tiles are stored by decreasing row count
+  // (ties by position), dealt round-robin to the eight XCD ranges, so every
+  // XCD gets an equal mix and runs its shortest tiles last (a greedy
+  // longest-first schedule; experts of 50 to 232 rows give tiles whose time
+  // differs by their A rows and live fragments).  Batches of short tiles
+  // (under 64 rows on average: decode-sized) keep expert order, which
+  // measured faster there.  Only a tile's place in the list changes, never
+  // its contents, so no output depends on the order.
+  if (!grouped && T > 8 && T <= 1024 && first_bad_s >= T && rows_s >= 64 * T) {
+    // Unique keys (row count, then earlier position first); a tile's rank is
+    // the number of larger keys.  sub threads share a tile, each counting
+    // over a quarter (or third, half) of the keys, four per LDS read.
+    const int T4 = (T + 3) / 4;
+    const int sub = min(4, 1024 / T);
+    int4 mine = make_int4(0, 0, 0, 0);
+    if (e < T) {
+      mine = tiles[e];
+      rank_l[e] = 0;
+    }
+    if (e < 4 * T4) keys_l[e] = e < T ? (mine.z - mine.y) * 1024 + (1023 - e) : -1;
+    __syncthreads();
+    const int t = e / sub, part = e % sub;
+    if (t < T) {
+      const int key = keys_l[t];
+      const int4* keys4 = reinterpret_cast<const int4*>(keys_l);
+      const int b0 = part * T4 / sub, b1 = (part + 1) * T4 / sub;
+      int rank = 0;
+#pragma unroll 4
+      for (int q4 = b0; q4 < b1; ++q4) {
+        const int4 o = keys4[q4];
+        rank += (o.x > key) + (o.y > key) + (o.z > key) + (o.w > key);
+      }
+      atomicAdd(&rank_l[t], rank);
+    }
+    __syncthreads();
+    if (e < T) {
+      const int rank = rank_l[e];
+      const int x = rank & 7;
+      int pos = rank >> 3;
+      for (int y = 0; y < x; ++y) pos += (T - y + 7) >> 3;
+      tiles[pos] = mine;
+    }
   }
 }
 
