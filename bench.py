@@ -75,6 +75,9 @@ def parse_args(argv=None):
                          "the GPU work either way)")
     ap.add_argument("--backward", action="store_true",
                     help="also time the layer's backward calls on this workload's layout")
+    ap.add_argument("--library-gemm", action="store_true",
+                    help="also time the FFN's up and down launches on a uniform batch against "
+                         "the vendor library's batched GEMM (torch.bmm) on the same shapes")
     ap.add_argument("--rank-share", action="store_true",
                     help="also time the expert FFN on one rank's share of the experts at "
                          "its real shape (rows from all R source ranks)")
@@ -646,6 +649,71 @@ def rank_share(moe, torch, cfg, buf, wts, steps: int) -> dict:
             "bound": "mfma" if flops / (peak * 1e12) >= nbytes / (HBM_PEAK_GBS * 1e9) else "hbm"}
 
 
+def library_gemm(moe, torch, cfg, wts, inp, steps: int) -> dict:
+    """The expert FFN's two GEMM launches on a uniform batch (every expert
+    N*k/E rows) against the vendor library on the same shapes: torch.bmm
+    (hipBLASLt) of X [E, rows, d] with [W1^T | W3^T] (or W1^T) as one
+    [E, d, n_up] operand, and of H [E, rows, h] with W2^T [E, h, d], both
+    operands contiguous.  The library computes the plain products; the up
+    launch here also applies the activation (and the SwiGLU product) and
+    writes H, the down launch reads that H.  For scale, not a step."""
+    E, dim, h, act, k, N = cfg["E"], cfg["d"], cfg["h"], cfg["act"], cfg["k"], cfg["N"]
+    if cfg["dtype"] != "bf16":
+        return {}
+    dev = wts["w2"].device
+    per = max(1, (N * k) // E)
+    M = E * per
+    g = torch.Generator(device=dev)
+    g.manual_seed(7)
+    x = torch.randn(M, dim, generator=g, device=dev, dtype=torch.float32).to(torch.bfloat16)
+    off = (torch.arange(E + 1, dtype=torch.int32) * per).to(dev)
+    ws = moe.workspace(moe.moe_expert_ffn_workspace_size(E, M, dim, h, act, "bf16"), device=dev)
+    y = torch.empty_like(x)
+    moe.moe_expert_ffn_plan(E, M, dim, h, act, "bf16", off, ws)
+
+    def timed(fn):
+        for _ in range(3):
+            fn()
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+        torch.cuda.synchronize()
+        ev[0].record()
+        for _ in range(steps):
+            fn()
+        ev[1].record()
+        torch.cuda.synchronize()
+        return ev[0].elapsed_time(ev[1]) / steps * 1e3
+
+    up = timed(lambda: moe.moe_expert_ffn_up(E, M, dim, h, act, "bf16", x, off, wts["w1"],
+                                             wts.get("w3"), ws))
+    down = timed(lambda: moe.moe_expert_ffn_down(E, M, dim, h, act, "bf16", off, wts["w2"], y,
+                                                 None, ws))
+    del ws, y
+    w1, w3, w2 = inp["w1"], inp.get("w3"), inp["w2"]
+    bt = torch.cat([w1, w3], 1) if w3 is not None else w1  # [E, n_up, d]
+    b_up = bt.transpose(1, 2).contiguous()                  # [E, d, n_up]
+    del bt
+    x3 = x.view(E, per, dim)
+    lib_up = timed(lambda: torch.bmm(x3, b_up))
+    del b_up
+    b_dn = w2.transpose(1, 2).contiguous()                  # [E, h, d]
+    hh = torch.randn(E, per, h, generator=g, device=dev, dtype=torch.float32).to(torch.bfloat16)
+    lib_down = timed(lambda: torch.bmm(hh, b_dn))
+    del b_dn, hh, x
+    torch.cuda.empty_cache()
+    n_up = 2 * h if w3 is not None else h
+    f_up, f_dn = 2.0 * M * dim * n_up, 2.0 * M * h * dim
+    peak = MFMA_PEAK_TFLOPS["bf16"] * 1e12
+
+    def rate(f, us):
+        return {"us": round(us, 1), "tflops": round(f / (us * 1e-6) / 1e12, 1),
+                "mfma_frac": round(f / (us * 1e-6) / peak, 4)}
+
+    return {"rows_per_expert": per, "experts": E,
+            "up": {"ours": rate(f_up, up), "library": rate(f_up, lib_up)},
+            "down": {"ours": rate(f_dn, down), "library": rate(f_dn, lib_down)},
+            "library": f"torch.bmm (hipBLASLt) {torch.version.hip}"}
+
+
 def backward_pass(moe, torch, buf, inp, steps: int) -> dict:
     """The layer's backward on its last layout: the combine's expert terms
     (row and weight gradients), the expert FFN's backward (input and weight
@@ -1017,6 +1085,9 @@ def main(argv=None):
                          else "eager launches"},
         "kernel_sources_digest": digest,
     }
+    if args.library_gemm:
+        out["library_gemm"] = library_gemm(run.moe, torch, cfg, run.wts, run.inp,
+                                           max(5, min(args.steps, 20)))
     if args.rank_share:
         out["rank_share"] = rank_share(run.moe, torch, cfg, run.buf, run.wts,
                                        max(5, min(args.steps, 30)))
