@@ -597,16 +597,39 @@ __global__ __launch_bounds__(kFuseWaves * 64, 4) void route_fused(
     double* __restrict__ ws_sx, double* __restrict__ ws_sw, double* __restrict__ ws_part,
     int ksplit, int tail_tpb) {
   constexpr int ZW = 64 * NJ;
-  __shared__ float zs[kFuseTok][ZW];  // z~, then exact values for candidates
   // Pair slots of step 1 (the tail launch runs no step 1: its ring is scratch).
   constexpr int RINGP = SPLIT == 1 ? kScorePairs : kFusePairs;
   constexpr int NSLOT = SPLIT == 2 ? kFuseRing / 2 : RINGP;
-  __shared__ __attribute__((aligned(1024))) char ring[NSLOT][2 * kFuseSlot];  // step 1; then pairs
-  __shared__ double sx[kFuseTok], sw[ZW];
-  __shared__ uint64_t cand_s[kFuseTok][4], gm_s[kFuseTok][2];
-  __shared__ int32_t cnt_s[kFuseTok];
-  __shared__ int32_t hist[ZW];
-  __shared__ int32_t npairs_s, nfb_s;
+  // The block's LDS is one object, carved at fixed offsets: the ring first
+  // (1-KB aligned), then the 8-byte and the 4-byte arrays.  With several LDS
+  // objects the compiler tags each with its own alias scope, and before every
+  // read of the ring it then waits for all of the ring's direct-to-LDS loads,
+  // the refills just issued included (s_waitcnt vmcnt(0)), so no load
+  // overlapped the arithmetic.  As one object the reads are ordered only by
+  // the ring's own waits and barriers (each wave waits for its loads of the
+  // pairs it is about to read, then the barrier), as in the grouped GEMM.
+  // The scoring launch (SPLIT == 1) uses the ring alone.
+  constexpr bool TAIL = SPLIT != 1;
+  constexpr int kRingB = NSLOT * 2 * kFuseSlot;
+  constexpr int kSxO = kRingB, kSwO = kSxO + (TAIL ? kFuseTok * 8 : 0);
+  constexpr int kCandO = kSwO + (TAIL ? ZW * 8 : 0);
+  constexpr int kGmO = kCandO + (TAIL ? kFuseTok * 4 * 8 : 0);
+  constexpr int kZsO = kGmO + (TAIL ? kFuseTok * 2 * 8 : 0);
+  constexpr int kCntO = kZsO + (TAIL ? kFuseTok * ZW * 4 : 0);
+  constexpr int kHistO = kCntO + (TAIL ? kFuseTok * 4 : 0);
+  constexpr int kNpO = kHistO + (TAIL ? ZW * 4 : 0);
+  constexpr int kLdsB = kNpO + (TAIL ? 8 : 0);
+  __shared__ __attribute__((aligned(1024))) char lds[kLdsB];
+  auto& ring = *reinterpret_cast<char (*)[NSLOT][2 * kFuseSlot]>(lds);  // step 1; then pairs
+  auto& zs = *reinterpret_cast<float (*)[kFuseTok][ZW]>(lds + kZsO);  // z~, then exact values
+  auto& sx = *reinterpret_cast<double (*)[kFuseTok]>(lds + kSxO);
+  auto& sw = *reinterpret_cast<double (*)[ZW]>(lds + kSwO);
+  auto& cand_s = *reinterpret_cast<uint64_t (*)[kFuseTok][4]>(lds + kCandO);
+  auto& gm_s = *reinterpret_cast<uint64_t (*)[kFuseTok][2]>(lds + kGmO);
+  auto& cnt_s = *reinterpret_cast<int32_t (*)[kFuseTok]>(lds + kCntO);
+  auto& hist = *reinterpret_cast<int32_t (*)[ZW]>(lds + kHistO);
+  int32_t& npairs_s = *reinterpret_cast<int32_t*>(lds + kNpO);
+  int32_t& nfb_s = *reinterpret_cast<int32_t*>(lds + kNpO + 4);
   // After step 1 the ring holds, at different times, the per-wave scratch of
   // the group limit (steps 2 and 4) and the pair lists (end of 2, step 3).
   static_assert(2 * kFuseTok * ZW * 2 <= kFuseRing * kFuseSlot,
@@ -631,7 +654,8 @@ __global__ __launch_bounds__(kFuseWaves * 64, 4) void route_fused(
     const int c1 = z + 1 == ksplit ? nch : 2 * (pairs * (z + 1) / ksplit);
     nch = c1 - c0;
   }
-  for (int e = tid; e < E; e += kFuseWaves * 64) hist[e] = 0;
+  if constexpr (TAIL)
+    for (int e = tid; e < E; e += kFuseWaves * 64) hist[e] = 0;
   // The scoring launch of the split route clears the counts its tail launch
   // adds to (stream order runs the whole tail after it).
   if (SPLIT == 1 && blockIdx.x == 0 && blockIdx.y == 0 && blockIdx.z == 0)
@@ -813,8 +837,7 @@ __global__ __launch_bounds__(kFuseWaves * 64, 4) void route_fused(
     const int tl = 16 * (wave >> 2) + (lane & 15);
     if (blockIdx.y == 0 && (wave & 3) == 0 && diag_lane && tl < nt)
       ws_sx[(size_t)blockIdx.z * N + t0 + tl] = sxp;
-    return;
-  }
+  } else {
   if constexpr (SPLIT == 2) {
     // The tile's z~ and norms from the scoring launch; after a K split, the
     // sum of the splits' fp64 partials in split order (each partial obeys the
@@ -855,6 +878,7 @@ __global__ __launch_bounds__(kFuseWaves * 64, 4) void route_fused(
   __syncthreads();
   for (int e = tid; e < E; e += kFuseWaves * 64)
     if (hist[e]) atomicAdd(&counts[e], hist[e]);
+  }
 }
 
 // ---------------------------------------------------------------- launch ---
