@@ -49,15 +49,24 @@ enum { ACT_RELU = 0, ACT_GELU = 1, ACT_SWIGLU = 2, ACT_NONE = 3 };
 // into p and the 0.5 into the a_i, and takes e as 2^(-u^2 log2(e) / 2) on
 // v_exp_f32.  t comes from v_rcp_f32 (within 2 ulp on gfx950); the fp32
 // evaluation adds a few ulp, all far below the bf16 rounding H goes through.
-__device__ __forceinline__ float gelu_as7126(float u) {
+// The same evaluation with its parts kept for the backward: h = GELU(u), and
+// tqe = t q e = P(t) e / 2, so that Phi(u) = 1 - tqe (u >= 0) or tqe (u < 0).
+__device__ __forceinline__ void gelu_as7126_parts(float u, float& h, float& tqe, float& e) {
   const float a = fabsf(u);
   const float t = __builtin_amdgcn_rcpf(fmaf(0.3275911f * 0.70710678118654752440f, a, 1.0f));
   float q = fmaf(0.5f * 1.061405429f, t, 0.5f * -1.453152027f);
   q = fmaf(q, t, 0.5f * 1.421413741f);
   q = fmaf(q, t, 0.5f * -0.284496736f);
   q = fmaf(q, t, 0.5f * 0.254829592f);
-  const float e = __builtin_amdgcn_exp2f(u * u * -0.72134752044448170368f);
-  return fmaf(-(a * t), q * e, fmaxf(u, 0.f));
+  e = __builtin_amdgcn_exp2f(u * u * -0.72134752044448170368f);
+  h = fmaf(-(a * t), q * e, fmaxf(u, 0.f));
+  tqe = t * (q * e);
+}
+
+__device__ __forceinline__ float gelu_as7126(float u) {
+  float h, tqe, e;
+  gelu_as7126_parts(u, h, tqe, e);
+  return h;
 }
 
 __device__ __forceinline__ float apply_act(float u, int act) {
@@ -70,8 +79,10 @@ __device__ __forceinline__ float apply_act(float u, int act) {
 __device__ __forceinline__ float silu(float g) { return g * __builtin_amdgcn_rcpf(1.f + __expf(-g)); }
 
 // H = act(u) [* v], du = g act'(u) [* v], dv = g silu(u) (SwiGLU), all in
-// fp32, for the backward (GELU in the erf form with the device erf and exp:
-// gelu(u) = u Phi(u), gelu'(u) = Phi(u) + u phi(u)).
+// fp32, for the backward.  H comes from the forward's own expressions
+// (gelu_as7126, silu).  GELU: gelu(u) = u Phi(u) and gelu'(u) = Phi(u) +
+// u phi(u), with Phi from the same formula 7.1.26 evaluation (its absolute
+// error 1.5e-7 / 2) and phi(u) = e / sqrt(2 pi) from the same e = exp(-u^2/2).
 template <int ACT>
 __device__ __forceinline__ void bwd_act_grad(float u, float v, float g, float& hv, float& du,
                                              float& dv) {
@@ -80,13 +91,13 @@ __device__ __forceinline__ void bwd_act_grad(float u, float v, float g, float& h
     du = u > 0.f ? g : 0.f;
     dv = 0.f;
   } else if constexpr (ACT == ACT_GELU) {
-    const float Phi = 0.5f * (1.f + erff(u * 0.70710678118654752f));
-    const float phi = 0.39894228040143268f * expf(-0.5f * u * u);
-    hv = u * Phi;
-    du = g * (Phi + u * phi);
+    float tqe, e;
+    gelu_as7126_parts(u, hv, tqe, e);
+    const float Phi = u >= 0.f ? 1.f - tqe : tqe;
+    du = g * fmaf(u * 0.39894228040143268f, e, Phi);
     dv = 0.f;
   } else {
-    const float s = 1.f / (1.f + expf(-u)), si = u * s;
+    const float s = __builtin_amdgcn_rcpf(1.f + __expf(-u)), si = u * s;
     hv = si * v;
     du = g * v * (s * (1.f + u * (1.f - s)));
     dv = g * si;

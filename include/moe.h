@@ -485,10 +485,12 @@ int moe_permute_backward(const moe_route_desc* desc, const void* dx_perm,
  *   dx  = du W1 [+ dv W3]           rounded to bf16, written to dx_rows
  *   dw1[e] = sum_r du^T x,  dw3[e] = sum_r dv^T x,  dw2[e] = sum_r dy^T H
  * u, v and H are recomputed and rounded to bf16 at the forward's rounding
- * point; products run on bf16 operands with fp32 sums.  GELU is the erf form
- * here, gelu(u) = u Phi(u) and gelu'(u) = Phi(u) + u phi(u), with Phi from the
- * device erf, whereas the forward evaluates erf by a polynomial: a recomputed
- * H can differ from the forward's H by one bf16 ulp.
+ * point; products run on bf16 operands with fp32 sums.  GELU is the erf form,
+ * gelu(u) = u Phi(u) and gelu'(u) = Phi(u) + u phi(u).  This entry point takes
+ * Phi from the device erf, whereas the forward evaluates erf by a polynomial,
+ * so its recomputed H can differ from the forward's H by one bf16 ulp;
+ * moe_expert_ffn_backward_packed recomputes u (v) on the forward's grouped
+ * GEMM and forms H, Phi and silu with the forward's own expressions.
  *
  *  x_rows, dy_rows, dx_rows [max_rows, d] bf16 (dy_rows: the gradient at
  *      y_rows, e.g. moe_combine_backward's dy_perm; rows outside every
