@@ -37,6 +37,7 @@ namespace moe {
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef float floatx16 __attribute__((ext_vector_type(16)));
 typedef float floatx4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
 enum { ACT_RELU = 0, ACT_GELU = 1, ACT_SWIGLU = 2, ACT_NONE = 3 };
 
@@ -828,36 +829,75 @@ __device__ __forceinline__ void gemm_bf16_body(
   // Activation-gradient epilogue (kBwdG), four consecutive columns at a time;
   // the packed store of 4 elements is half of a 16-byte position: row r16 of
   // the tile's group, logical chunk (col % 32) / 8, elements col % 8 on.
+  // Units (i, j) of four column groups run as a two-stage pipeline: the u (v)
+  // loads of the next unit are issued before this unit's arithmetic and
+  // stores.  The vector memory counter retires loads and stores in issue
+  // order, and a wait after a branch must assume the fewest operations in
+  // flight of any path into it, so the epilogue has no branches: u, v, H and
+  // G go through buffer resources based at the tile's first row (rows past
+  // the tile fall outside the range), the packed G through one based at the
+  // tile's first group of the column block, and a lane outside the tile or
+  // the matrix takes an offset past every range, which the hardware answers
+  // with zeros (loads) or drops (stores).  Each wait then leaves the previous
+  // unit's stores and the next unit's loads in flight.
+#define MOE_BWDG_LOAD(n_, b_)                                                              \
+  do {                                                                                     \
+    const int i_ = (n_) / FN, j_ = (n_) % FN;                                              \
+    const int lr_ = (2 * i_ + wm) * 32 + (lane & 31);                                      \
+    const int cb_ = n0 + wn * WN + j_ * 32;                                                \
+    const bool ok_ = lr_ < rows_t && cb_ < N;                                              \
+    _Pragma("unroll") for (int g = 0; g < 4; ++g) {                                        \
+      const int col_ = cb_ + 8 * g + 4 * (lane >> 5);                                      \
+      const uint32_t o_ = ok_ ? (uint32_t)(lr_ * N + col_) * 4u : kBwdOut;                 \
+      ub_[b_][g] = __builtin_bit_cast(floatx4, __builtin_amdgcn_raw_buffer_load_b128(rs_u, o_, 0, 0)); \
+      if constexpr (ACT == ACT_SWIGLU)                                                     \
+        vb_[b_][g] = __builtin_bit_cast(floatx4, __builtin_amdgcn_raw_buffer_load_b128(rs_v, o_, 0, 0)); \
+    }                                                                                      \
+  } while (0)
 #define MOE_EPILOGUE_BWDG(FA_)                                                             \
   do {                                                                                     \
-    _Pragma("unroll") for (int i = 0; i < (FA_); ++i) {                                    \
+    constexpr int NU_ = (FA_) * FN;                                                        \
+    constexpr uint32_t kBwdOut = 0x80000000u;                                              \
+    const int rows_t = r1 - r0;                                                            \
+    const auto rs_u = buffer_rsrc(be.U + (size_t)r0 * N, (uint32_t)rows_t * (uint32_t)N * 4u); \
+    const auto rs_v = buffer_rsrc(be.V + (size_t)r0 * N, (uint32_t)rows_t * (uint32_t)N * 4u); \
+    const auto rs_h = buffer_rsrc(be.H + (size_t)r0 * N, (uint32_t)rows_t * (uint32_t)N * 2u); \
+    const auto rs_g = buffer_rsrc(be.G + (size_t)r0 * be.kg,                               \
+                                  (uint32_t)rows_t * (uint32_t)be.kg * 2u);                \
+    floatx4 ub_[2][4], vb_[2][4];                                                          \
+    if constexpr (NU_ > 0) MOE_BWDG_LOAD(0, 0);                                            \
+    _Pragma("unroll") for (int n = 0; n < NU_; ++n) {                                      \
+      if (n + 1 < NU_) MOE_BWDG_LOAD(n + 1, (n + 1) & 1);                                  \
+      const int i = n / FN, j = n % FN;                                                    \
       const int lr = (2 * i + wm) * 32 + (lane & 31);                                      \
-      const int row = r0 + lr;                                                             \
-      const int r16 = lr % 16, grp = g0 + lr / 16;                                         \
-      _Pragma("unroll") for (int j = 0; j < FN; ++j)                                       \
+      const int r16 = lr % 16;                                                             \
+      const int cb = n0 + wn * WN + j * 32;                                                \
+      const bool ok = lr < rows_t && cb < N;                                               \
+      /* packed G: column block cb (du) and N + cb (dv), from the tile's first group */    \
+      const auto rs_c = buffer_rsrc(C + ((size_t)(cb / 32) * ldg + g0) * 512, 0x7fffffffu); \
+      const auto rs_c2 = buffer_rsrc(C + ((size_t)((N + cb) / 32) * ldg + g0) * 512, 0x7fffffffu); \
       _Pragma("unroll") for (int g = 0; g < 4; ++g) {                                      \
-        const int col = n0 + wn * WN + j * 32 + 8 * g + 4 * (lane >> 5);                   \
-        if (row < r1 && col < N) {                                                         \
-          const size_t o_ = (size_t)row * N + col;                                         \
-          const floatx4 uu = *reinterpret_cast<const floatx4*>(be.U + o_);                 \
-          floatx4 vv = floatx4{0.f, 0.f, 0.f, 0.f};                                        \
-          if constexpr (ACT == ACT_SWIGLU) vv = *reinterpret_cast<const floatx4*>(be.V + o_); \
-          float hv[4], gu[4], gv[4];                                                       \
-          _Pragma("unroll") for (int q = 0; q < 4; ++q)                                    \
-            bwd_act_grad<ACT>(uu[q], vv[q], acc[i][j][4 * g + q], hv[q], gu[q], gv[q]);    \
-          const uint2 hb = make_uint2(pack_bf16x2(hv[0], hv[1]), pack_bf16x2(hv[2], hv[3])); \
-          const uint2 ub = make_uint2(pack_bf16x2(gu[0], gu[1]), pack_bf16x2(gu[2], gu[3])); \
-          *reinterpret_cast<uint2*>(be.H + o_) = hb;                                       \
-          *reinterpret_cast<uint2*>(be.G + (size_t)row * be.kg + col) = ub;                \
-          const int pos = 4 * r16 + (((col % 32) / 8) ^ swz4(r16));                        \
-          *reinterpret_cast<uint2*>(C + ((size_t)(col / 32) * ldg + grp) * 512 + pos * 8 + \
-                                    (col % 8)) = ub;                                       \
-          if constexpr (ACT == ACT_SWIGLU) {                                               \
-            const uint2 vb = make_uint2(pack_bf16x2(gv[0], gv[1]), pack_bf16x2(gv[2], gv[3])); \
-            *reinterpret_cast<uint2*>(be.G + (size_t)row * be.kg + N + col) = vb;          \
-            *reinterpret_cast<uint2*>(C + ((size_t)((N + col) / 32) * ldg + grp) * 512 +   \
-                                      pos * 8 + (col % 8)) = vb;                           \
-          }                                                                                \
+        const int col = cb + 8 * g + 4 * (lane >> 5);                                      \
+        const floatx4 uu = ub_[n & 1][g];                                                  \
+        floatx4 vv = floatx4{0.f, 0.f, 0.f, 0.f};                                          \
+        if constexpr (ACT == ACT_SWIGLU) vv = vb_[n & 1][g];                               \
+        float hv[4], gu[4], gv[4];                                                         \
+        _Pragma("unroll") for (int q = 0; q < 4; ++q)                                      \
+          bwd_act_grad<ACT>(uu[q], vv[q], acc[i][j][4 * g + q], hv[q], gu[q], gv[q]);      \
+        const u32x2 hb = {pack_bf16x2(hv[0], hv[1]), pack_bf16x2(hv[2], hv[3])};           \
+        const u32x2 ubv = {pack_bf16x2(gu[0], gu[1]), pack_bf16x2(gu[2], gu[3])};          \
+        const int pos = 4 * r16 + (((col % 32) / 8) ^ swz4(r16));                          \
+        const uint32_t oh = ok ? (uint32_t)(lr * N + col) * 2u : kBwdOut;                  \
+        const uint32_t og = ok ? (uint32_t)(lr * be.kg + col) * 2u : kBwdOut;              \
+        const uint32_t oc = ok ? (uint32_t)((lr / 16) * 512 + pos * 8 + col % 8) * 2u : kBwdOut; \
+        __builtin_amdgcn_raw_buffer_store_b64(hb, rs_h, oh, 0, 0);                         \
+        __builtin_amdgcn_raw_buffer_store_b64(ubv, rs_g, og, 0, 0);                        \
+        __builtin_amdgcn_raw_buffer_store_b64(ubv, rs_c, oc, 0, 0);                        \
+        if constexpr (ACT == ACT_SWIGLU) {                                                 \
+          const u32x2 vbv = {pack_bf16x2(gv[0], gv[1]), pack_bf16x2(gv[2], gv[3])};        \
+          const uint32_t og2 = ok ? (uint32_t)(lr * be.kg + N + col) * 2u : kBwdOut;       \
+          __builtin_amdgcn_raw_buffer_store_b64(vbv, rs_g, og2, 0, 0);                     \
+          __builtin_amdgcn_raw_buffer_store_b64(vbv, rs_c2, oc, 0, 0);                     \
         }                                                                                  \
       }                                                                                    \
     }                                                                                      \
@@ -907,6 +947,7 @@ __device__ __forceinline__ void gemm_bf16_body(
 #undef MOE_EPILOGUE_FUSED
 #undef MOE_EPILOGUE_RAW
 #undef MOE_EPILOGUE_BWDG
+#undef MOE_BWDG_LOAD
 #undef MOE_EPILOGUE_WG
 #undef MOE_K_LOOP
 #undef MOE_LOAD_KK
