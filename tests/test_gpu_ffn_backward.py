@@ -308,6 +308,45 @@ def test_ffn_backward_packed_wide_tiles(act):
         assert bool((got[0] == 0).all()), f"{key}: an expert with no rows gets zeros"
 
 
+# The packed backward on 320-row tiles (more than 128 rows per expert on
+# average) with h = 2048: the wide recompute and the activation-gradient
+# epilogue (branch-free loads and stores) at their largest tile, experts on
+# the fragment edges of a 320-row tile and one past it (split in two).
+TALL_COUNTS = [0, 1, 33, 64, 95, 160, 255, 319, 320, 321]
+
+
+@pytest.mark.parametrize("act", ["swiglu", "relu"])
+def test_ffn_backward_packed_tall_tiles(act):
+    E, d, h = len(TALL_COUNTS), 256, 2048
+    used = sum(TALL_COUNTS)
+    rows = used + 37
+    assert rows > 128 * E, "must take the 320-row tiles"
+    print(f"[ffn backward packed tall] E={E} rows={rows} d={d} h={h} {act}", flush=True)
+    off = np.concatenate([[0], np.cumsum(TALL_COUNTS)]).astype(np.int32)
+    g = torch.Generator().manual_seed(h + E + 1)
+    x = torch.randn(rows, d, generator=g).to(BF16)
+    dy = (torch.randn(rows, d, generator=g) * 0.5).to(BF16)
+    w1, w3, w2 = _weights(E, d, h, act, seed=d + 1, scale=0.05)
+    dx, dw1, dw3, dw2 = _gpu_backward(E, rows, d, h, act, x, torch.from_numpy(off), w1, w3, w2,
+                                      dy, path="packed")
+    oracle.set_threads(threads())
+    r_dx, r_dw1, r_dw3, r_dw2 = oracle.expert_ffn_backward("bf16", act, n(x), off, n(w1), n(w3),
+                                                           n(w2), n(dy))
+    assert bool((dx[used:] == 3.0).all()), "rows outside every segment must stay untouched"
+    for e in range(E):
+        a, b = int(off[e]), int(off[e + 1])
+        if b > a:
+            ee = rel_err(dx[a:b].float(), as_tensor(r_dx[a:b], "bf16").float())
+            assert ee <= TOL["bf16"], f"dx of expert {e} ({b - a} rows): {ee:.3e}"
+    for got, ref, key in ((dw1, r_dw1, "dw1"), (dw3, r_dw3, "dw3"), (dw2, r_dw2, "dw2")):
+        if ref is None:
+            continue
+        for e in range(E):
+            ee = rel_err(got[e], torch.from_numpy(ref[e])) if TALL_COUNTS[e] else 0.0
+            assert ee <= TOL["bf16"], f"{key}[{e}] ({TALL_COUNTS[e]} rows) max rel err {ee:.3e}"
+        assert bool((got[0] == 0).all()), f"{key}: an expert with no rows gets zeros"
+
+
 @pytest.mark.parametrize("act", ["swiglu", "gelu"])
 def test_ffn_backward_packed_empty_batch(act):
     """No rows: every weight gradient is written as zeros, nothing else read
