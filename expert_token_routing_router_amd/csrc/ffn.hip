@@ -860,7 +860,8 @@ __device__ __forceinline__ void gemm_bf16_body(
     constexpr uint32_t kBwdOut = 0x80000000u;                                              \
     const int rows_t = r1 - r0;                                                            \
     const auto rs_u = buffer_rsrc(be.U + (size_t)r0 * N, (uint32_t)rows_t * (uint32_t)N * 4u); \
-    const auto rs_v = buffer_rsrc(be.V + (size_t)r0 * N, (uint32_t)rows_t * (uint32_t)N * 4u); \
+    const auto rs_v = buffer_rsrc((ACT == ACT_SWIGLU ? be.V : be.U) + (size_t)r0 * N,        \
+                                  (uint32_t)rows_t * (uint32_t)N * 4u);                    \
     const auto rs_h = buffer_rsrc(be.H + (size_t)r0 * N, (uint32_t)rows_t * (uint32_t)N * 2u); \
     const auto rs_g = buffer_rsrc(be.G + (size_t)r0 * be.kg,                               \
                                   (uint32_t)rows_t * (uint32_t)be.kg * 2u);                \
@@ -875,7 +876,8 @@ __device__ __forceinline__ void gemm_bf16_body(
       const bool ok = lr < rows_t && cb < N;                                               \
       /* packed G: column block cb (du) and N + cb (dv), from the tile's first group */    \
       const auto rs_c = buffer_rsrc(C + ((size_t)(cb / 32) * ldg + g0) * 512, 0x7fffffffu); \
-      const auto rs_c2 = buffer_rsrc(C + ((size_t)((N + cb) / 32) * ldg + g0) * 512, 0x7fffffffu); \
+      const int cb2 = ACT == ACT_SWIGLU ? N + cb : cb; /* dv's column block (SwiGLU) */     \
+      const auto rs_c2 = buffer_rsrc(C + ((size_t)(cb2 / 32) * ldg + g0) * 512, 0x7fffffffu); \
       _Pragma("unroll") for (int g = 0; g < 4; ++g) {                                      \
         const int col = cb + 8 * g + 4 * (lane >> 5);                                      \
         const floatx4 uu = ub_[n & 1][g];                                                  \
