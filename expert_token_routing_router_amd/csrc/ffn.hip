@@ -1191,13 +1191,17 @@ static size_t align256(size_t x) { return (x + 255) / 256 * 256; }
 // live against 91%), and the wide 96 x 128 wave tile reads fewer LDS bytes
 // per MFMA (3 + 4 fragments for 12 MFMAs against 5 + 2 for 10).  Same-box
 // A/B on the Mixtral-like layer (2048 rows per expert): up GEMM 3607 ->
-// 3427 us, down unchanged (1724 us), step 5.50 -> 5.34 ms.
-constexpr int kLargeRowsPerExpert = 1024;
+// 3427 us, down unchanged (1724 us), step 5.50 -> 5.34 ms.  Only with at least
+// kLargeMinRows rows in all: fewer give too few blocks to fill the chip (one
+// expert of 4096 rows, the DeepSeek-like shared expert: 176 up blocks for 256
+// CUs, 420 against 372 us alone, and the layer's step ~30 us slower).
+constexpr int kLargeRowsPerExpert = 1024, kLargeMinRows = 8192;
 static int ffn_bm(int dtype, int E, int max_rows) {
   if (dtype == 0) return kF32BM;
   if ((long long)max_rows <= 32LL * E) return kGemmBMSmall;
   if ((long long)max_rows <= (long long)kMidRowsPerExpert * E) return kGemmBMMid;
-  if ((long long)max_rows >= (long long)kLargeRowsPerExpert * E) return kGemmBMMid;
+  if ((long long)max_rows >= (long long)kLargeRowsPerExpert * E && max_rows >= kLargeMinRows)
+    return kGemmBMMid;
   return kGemmBM;
 }
 
