@@ -8,7 +8,8 @@ per-expert row counts below sit on every one of those edges (0, 1, 31/32/33,
 multiple of the column tile.  Experts of many row tiles take the grouped
 block order (4 row tiles walk their column tiles together), with a short last
 group; decode-sized batches take 128-row tiles with wider column tiles, and
-batches of at most 128 rows per expert on average 192-row tiles.
+batches of at most 128 rows per expert on average 192-row tiles, as do
+batches of at least 1024 rows per expert on average and 8192 in all.
 Reference: the oracle's grouped FFN on the same
 rows (glossary "Expert Parallelism", step 3), per-tensor max relative error
 within 2e-2 (bf16) / 1e-4 (fp32).
@@ -90,6 +91,19 @@ def test_ffn_row_tile_edges(d, h, act, dtype):
 @pytest.mark.parametrize("act", ["gelu", "swiglu"])
 def test_ffn_grouped_row_tiles(act):
     _check_ffn(512, 1024, act, "bf16", [1500, 0, 700, 2100], seed=77)
+
+
+# At least 1024 rows per expert on average and 8192 in all: the 192-row tiles
+# (the wide form where h >= 2048), every expert split into several of them
+# with a shorter last tile, in the grouped block order; every row checked.
+LARGE_COUNTS = [2100, 0, 2500, 1999, 3001]
+
+
+@pytest.mark.parametrize("d,h,act", [(256, 2048, "swiglu"), (512, 1024, "gelu")])
+def test_ffn_large_expert_row_tiles(d, h, act):
+    M = sum(LARGE_COUNTS) + 7
+    assert M >= 1024 * len(LARGE_COUNTS) and M >= 8192, "must take the 192-row tiles"
+    _check_ffn(d, h, act, "bf16", LARGE_COUNTS, seed=d + 11 * h)
 
 
 # Decode-sized batches (at most 32 rows per expert on average) take 128-row
