@@ -347,6 +347,45 @@ def test_ffn_backward_packed_tall_tiles(act):
         assert bool((got[0] == 0).all()), f"{key}: an expert with no rows gets zeros"
 
 
+# The packed backward on large-expert batches (at least 1024 rows per expert on
+# average and 8192 in all) takes the 192-row tiles too: every expert with rows
+# spans several of them with a shorter last one, in the grouped block order;
+# h = 2048 with SwiGLU takes the wide recompute, h = 1024 with GELU the narrow.
+LARGE_COUNTS = [2100, 0, 2500, 1999, 1600]
+
+
+@pytest.mark.parametrize("h,act", [(2048, "swiglu"), (1024, "gelu")])
+def test_ffn_backward_packed_large_expert_tiles(h, act):
+    E, d = len(LARGE_COUNTS), 256
+    used = sum(LARGE_COUNTS)
+    rows = used + 7
+    assert rows >= 1024 * E and rows >= 8192, "must take the large-expert 192-row tiles"
+    print(f"[ffn backward packed large] E={E} rows={rows} d={d} h={h} {act}", flush=True)
+    off = np.concatenate([[0], np.cumsum(LARGE_COUNTS)]).astype(np.int32)
+    g = torch.Generator().manual_seed(h + E + 2)
+    x = torch.randn(rows, d, generator=g).to(BF16)
+    dy = (torch.randn(rows, d, generator=g) * 0.5).to(BF16)
+    w1, w3, w2 = _weights(E, d, h, act, seed=d + 2, scale=0.05)
+    dx, dw1, dw3, dw2 = _gpu_backward(E, rows, d, h, act, x, torch.from_numpy(off), w1, w3, w2,
+                                      dy, path="packed")
+    oracle.set_threads(threads())
+    r_dx, r_dw1, r_dw3, r_dw2 = oracle.expert_ffn_backward("bf16", act, n(x), off, n(w1), n(w3),
+                                                           n(w2), n(dy))
+    assert bool((dx[used:] == 3.0).all()), "rows outside every segment must stay untouched"
+    for e in range(E):
+        a, b = int(off[e]), int(off[e + 1])
+        if b > a:
+            ee = rel_err(dx[a:b].float(), as_tensor(r_dx[a:b], "bf16").float())
+            assert ee <= TOL["bf16"], f"dx of expert {e} ({b - a} rows): {ee:.3e}"
+    for got, ref, key in ((dw1, r_dw1, "dw1"), (dw3, r_dw3, "dw3"), (dw2, r_dw2, "dw2")):
+        if ref is None:
+            continue
+        for e in range(E):
+            ee = rel_err(got[e], torch.from_numpy(ref[e])) if LARGE_COUNTS[e] else 0.0
+            assert ee <= TOL["bf16"], f"{key}[{e}] ({LARGE_COUNTS[e]} rows) max rel err {ee:.3e}"
+        assert bool((got[1] == 0).all()), f"{key}: an expert with no rows gets zeros"
+
+
 @pytest.mark.parametrize("act", ["swiglu", "gelu"])
 def test_ffn_backward_packed_empty_batch(act):
     """No rows: every weight gradient is written as zeros, nothing else read
