@@ -282,6 +282,10 @@ __global__ __launch_bounds__(256) void dispatch_assign(
 }
 
 // Token-major permute: one wave per token (grid-stride), 16-byte vectors.
+// NT: the row stores carry the non-temporal cache policy, for layouts larger
+// than the last-level cache (the expert FFN then reads them back from HBM
+// either way, and plain stores would only evict other data on their way out).
+template <bool NT>
 __global__ __launch_bounds__(256) void dispatch_permute(const u32x4* __restrict__ x, int N,
                                                         int vec_per_row, int k,
                                                         const int32_t* __restrict__ row_of_slot,
@@ -309,7 +313,10 @@ __global__ __launch_bounds__(256) void dispatch_permute(const u32x4* __restrict_
 #pragma unroll
           for (int u = 0; u < 4; ++u) {
             const int v = v0 + u * 64 + lane;
-            if (v < vec_per_row) dst[v] = buf[u];
+            if (v < vec_per_row) {
+              if constexpr (NT) __builtin_nontemporal_store(buf[u], &dst[v]);
+              else dst[v] = buf[u];
+            }
           }
         }
       }
@@ -572,8 +579,19 @@ hipError_t launch_dispatch(const DispatchArgs& a, hipStream_t st, int stages) {
       else go(dispatch_permute_q8<1, 16>);
     }
   } else {
-    dispatch_permute<<<blocks, 256, 0, st>>>(static_cast<const u32x4*>(a.x), a.N, vec_per_row,
-                                             a.k, a.row_of_slot, static_cast<u32x4*>(a.x_perm));
+    // Non-temporal row stores once the rows written (at most N k) exceed the
+    // 256 MiB last-level cache.  Measured on MI355X (same-box A/B): DeepSeek-like
+    // layer, 470 MB of rows: permute 109 -> 95 us alone and the up GEMM that
+    // follows 3011 -> 2896 us in the step; rows that fit the cache (Switch 34 MB,
+    // Mixtral-like 134 MB) are read back from it by the up GEMM, and there
+    // non-temporal stores cost 3 to 5 us (permute or up GEMM).
+    const bool nt = (unsigned long long)a.N * a.k * vec_per_row * 16ull > (256ull << 20);
+    auto go = [&](auto kernel) {
+      kernel<<<blocks, 256, 0, st>>>(static_cast<const u32x4*>(a.x), a.N, vec_per_row, a.k,
+                                     a.row_of_slot, static_cast<u32x4*>(a.x_perm));
+    };
+    if (nt) go(dispatch_permute<true>);
+    else go(dispatch_permute<false>);
   }
   if (a.padded && a.admitted) {  // padding rows of the padded layout: zeros
     const long long rows = (long long)a.E * a.cap;
